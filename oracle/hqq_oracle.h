@@ -1,0 +1,64 @@
+/*
+ * HQQ oracle: plain, single-threaded fp64 reference of the quantizer, the
+ * bit-packing, the dequantisation and the dequantised GEMV.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load it.  The product path (the HIP
+ * library) shares no code with it.
+ *
+ * Source: the page "HQQ 算法解读：不用校准数据，怎样把大模型权重压到 4 bit"
+ * (ludovicoyin.github.io), sections "量化公式" (the affine map and its inverse),
+ * "为什么一定要分组" (groups, bit-packing, 4.5 bpw), "第一拍" (min-max start),
+ * "第二拍" (the proximal loop), "为什么 zero 是这个均值" (the zero update),
+ * "shrink 不是删除极值" (the shrink), "axis 不是一个无关紧要的开关" (grouping by
+ * axis) and "从压缩文件到一次前向" (dequantise then x @ W_hat^T).
+ *
+ * Conventions: W is row-major [rows, cols], N = rows*cols, g = group size,
+ * G = N/g groups.  axis=1: group j holds flat elements j*g + i.  axis=0: group
+ * j holds flat elements i*(N/g) + j.  i = 0..g-1 is the in-group order of
+ * every sum.  s is "codes per unit" (q = W*s + z), delta = 1/s is the stored
+ * step, z is the zero point in code units.  Codes are one byte per weight in
+ * flat row-major order.
+ */
+#ifndef HQQ_ORACLE_H
+#define HQQ_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+double hqq_oracle_half_to_double(uint16_t h);
+uint16_t hqq_oracle_double_to_half(double x);
+void hqq_oracle_doubles_to_halves(const double* x, int64_t n, uint16_t* out);
+
+int64_t hqq_oracle_group_elem(int64_t rows, int64_t cols, int g, int axis, int64_t j, int i);
+
+void hqq_oracle_init_group(const double* w, int g, int nbits, double tiny, double* s, double* delta,
+                           double* z0);
+double hqq_oracle_shrink(double r, double beta, double p);
+void hqq_oracle_round_group(const double* w, int g, int nbits, double s, double delta, double z, double beta,
+                            double p, double* err_sum, double* z_next, double* q_out, double* e_out);
+int hqq_oracle_stop_check(int k, double mae_k, double best);
+int hqq_oracle_stop_iter(const double* mae, int n, int iters, int* rounds_out);
+
+int hqq_oracle_quantize(const double* W, int64_t rows, int64_t cols, int nbits, int g, int axis, int iters,
+                        double p, double beta0, double kappa, double tiny, uint8_t* codes, double* s_out,
+                        double* delta_out, double* z_out, double* mae_out, int* rounds_out, int* kout_out);
+int hqq_oracle_quantize_groups(const double* Wg, int64_t n, int g, int nbits, int kout, double p, double beta0,
+                               double kappa, double tiny, uint8_t* codes, double* s_out, double* delta_out,
+                               double* z_out, double* z_traj, double* err_traj);
+
+int64_t hqq_oracle_packed_bytes(int64_t N, int nbits);
+int hqq_oracle_pack(const uint8_t* codes, int64_t N, int nbits, uint8_t* out);
+int hqq_oracle_unpack(const uint8_t* packed, int64_t N, int nbits, uint8_t* codes);
+
+int hqq_oracle_dequant(const uint8_t* packed, const double* delta, const double* zero, int64_t rows, int64_t cols,
+                       int nbits, int g, int axis, double* out_f64, uint16_t* out_f16);
+int hqq_oracle_gemv(const uint8_t* packed, const double* delta, const double* zero, int64_t N, int64_t K, int g,
+                    const double* x, int64_t batch, const int64_t* rows_sel, int64_t n_sel, double* y);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
