@@ -1,0 +1,170 @@
+/*
+ * hqq.h - C ABI of the HQQ weight-only quantization library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * HQQ (half-quadratic quantization) is a calibration-free, group-wise,
+ * asymmetric affine weight quantizer.  The operations below follow the page
+ * "HQQ 算法解读：不用校准数据，怎样把大模型权重压到 4 bit"
+ * (ludovicoyin.github.io/blog/posts/hqq-half-quadratic-quantization):
+ *   - "量化公式": q = clip(round(W*s + z), 0, 2^b-1), W_hat = (q - z) * delta,
+ *     delta = 1/s is the stored step ("scale"), z the zero in code units;
+ *   - "第一拍": min-max start s0 = (2^b-1)/(max-min), z0 = -min*s0, s = 1 when the
+ *     range is tiny, s limited to at most 2e4;
+ *   - "第二拍" and "为什么 zero 是这个均值": up to `iters` proximal rounds that move
+ *     only the zero, z <- mean(q - (W - e)*s) with e = shrink(W - W_hat) (lp
+ *     shrink, p, beta growing by kappa per round), stopping when the
+ *     whole-tensor reconstruction MAE no longer improves and going back to the
+ *     zero that reached the best MAE; then one final quantisation of W;
+ *   - "为什么一定要分组": bit-packing, two 4-bit codes per byte, four 2-bit codes
+ *     per byte, ten 3-bit codes per 32-bit word;
+ *   - "axis 不是一个无关紧要的开关": groups are reshape([-1, g]) rows (axis=1) or
+ *     reshape([g, -1]) columns (axis=0) of the row-major [rows, cols] weight;
+ *   - "从压缩文件到一次前向": unpack, (q - zero) * scale, x @ W_hat^T.
+ *
+ * Shrink reading (the page names the operator but prints no formula):
+ *   e = sign(r) * max(|r| - |r|^(p-1) / beta, 0), e = 0 at r = 0.
+ * Stop reading: round k's MAE measures z_k; the loop stops at the first k >= 1
+ * whose MAE is not below the best so far, and keeps z_(k-1); when no round
+ * stops it, z_iters (the last update) is kept.
+ *
+ * Data layout (all buffers are device memory, caller-owned):
+ *   W          fp16 [rows, cols], row-major.
+ *   packed     codes in flat row-major order (the same order for both axes),
+ *              little-endian inside each container:
+ *                4-bit: byte j = c[2j] | c[2j+1] << 4            (rows*cols/2 bytes)
+ *                2-bit: byte j = sum_t c[4j+t] << 2t             (rows*cols/4 bytes)
+ *                3-bit: uint32 j = sum_t c[10j+t] << 3t, bits 30-31 zero, the last
+ *                       word padded with code 0          (4*ceil(rows*cols/10) bytes)
+ *   delta/zero one value per group, group j in the order of the group view:
+ *                axis=1: group j = flat elements j*g .. j*g+g-1  ([rows, cols/g]);
+ *                axis=0: group j = flat elements i*(N/g) + j     ([rows/g, cols]).
+ *
+ * Conventions:
+ *   - Ownership: every pointer is caller-owned device memory (workspace
+ *     included).  The library allocates, frees and retains nothing.
+ *   - Asynchrony: every compute call only enqueues work on `stream` (a
+ *     hipStream_t, NULL = the default stream) and returns; nothing is
+ *     synchronised.  Outputs are valid once the stream has reached that point.
+ *   - Alignment: W, packed, delta, zero, x, y and the workspace must be 16-byte
+ *     aligned (torch allocations are 256-byte aligned).
+ *   - Inputs are read only; outputs are fully overwritten; inputs and outputs
+ *     must not overlap.  Inputs must be finite.
+ *   - Errors: arguments are checked before anything is enqueued; a non-zero
+ *     status means nothing was launched (HQQ_ERR_DEVICE: a launch failed; the
+ *     message is in hqq_last_error()).  No exception crosses the ABI.
+ *   - State: the library keeps no mutable global state, so calls on different
+ *     streams may run concurrently (with distinct workspaces).
+ */
+#ifndef HQQ_H
+#define HQQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define HQQ_OK 0
+#define HQQ_ERR_INVALID_ARGUMENT 1 /* a pointer, size or parameter is outside the contract */
+#define HQQ_ERR_UNSUPPORTED 2      /* valid HQQ, but a shape/format this build has no kernel for */
+#define HQQ_ERR_WORKSPACE 3        /* workspace missing or smaller than hqq_quantize_workspace_bytes */
+#define HQQ_ERR_DEVICE 4           /* a HIP call or kernel launch failed */
+
+/* Metadata element types (delta and zero share one type). */
+#define HQQ_META_F16 0 /* the stored format: fp16 scale + fp16 zero, 4.5 bits/weight at 4-bit g64 */
+#define HQQ_META_F32 1
+#define HQQ_META_F64 2 /* the solver's own precision (quantize only) */
+
+/* GEMV / GEMM output types. */
+#define HQQ_OUT_F16 0
+#define HQQ_OUT_F32 1
+
+/* Range max-min at or below which s = 1 ("第一拍": the page says "when the
+ * denominator is too small" without a number; this library uses 1e-4). */
+#define HQQ_TINY_RANGE 1e-4
+/* s is limited to at most this value ("第一拍"). */
+#define HQQ_MAX_SCALE 2.0e4
+/* Largest accepted `iters`. */
+#define HQQ_MAX_ITERS 64
+
+/* Bytes of the packed code buffer for rows*cols codes of `nbits` (2, 3 or 4), or 0
+ * when the arguments are invalid. */
+size_t hqq_packed_bytes(int64_t rows, int64_t cols, int nbits);
+
+/* Number of groups rows*cols/group_size, or -1 when group_size does not divide it. */
+int64_t hqq_num_groups(int64_t rows, int64_t cols, int group_size);
+
+/* Workspace bytes hqq_quantize needs for these arguments, or 0 when they are invalid. */
+size_t hqq_quantize_workspace_bytes(int64_t rows, int64_t cols, int nbits, int group_size, int axis, int iters);
+
+/*
+ * HQQ quantisation of one weight tensor ("第一拍", "第二拍", "为什么一定要分组").
+ *   W_fp16     in   fp16 [rows, cols] row-major.
+ *   nbits      2, 3 or 4.
+ *   group_size 8, 16, 32, 64, 128 or 256; it must divide cols (axis=1) or rows (axis=0);
+ *              axis=0 also needs (rows/group_size)*cols to be a multiple of 8.
+ *   axis       1 (groups along a row) or 0 (groups down a column, row stride rows/g).
+ *   iters      0 .. HQQ_MAX_ITERS proximal rounds at most (20 on the page).
+ *   p          lp exponent of the shrink, 0 < p <= 1 (0.7 on the page).
+ *   beta0      shrink beta of round 0, > 0 (10 on the page).
+ *   kappa      beta growth per round, > 0 (1.01 on the page).
+ *   packed     out  hqq_packed_bytes(rows, cols, nbits) bytes.
+ *   delta      out  one step (1/s) per group, type meta_dtype.
+ *   zero       out  one zero per group (code units), type meta_dtype.
+ *   meta_dtype HQQ_META_F16, HQQ_META_F32 or HQQ_META_F64; values are rounded to
+ *              nearest-even from the solver's fp64 values.
+ *   workspace  device scratch of at least hqq_quantize_workspace_bytes(...) bytes;
+ *              its contents on entry do not matter.
+ *   stop_iter_dev  out (nullable) device int32: index k_out of the kept zero
+ *              (iters when the loop ran to the end).
+ *   mae_trace_dev  out (nullable) device double[iters]: the whole-tensor MAE of each
+ *              round the method evaluates; entries past the stop are NaN.
+ *   stream     hipStream_t or NULL.
+ * The solver runs in fp64 on the GPU; the stop decision stays on the device (no
+ * host round trip).
+ */
+int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int group_size, int axis, int iters,
+                 double p, double beta0, double kappa, void* packed, void* delta, void* zero, int meta_dtype,
+                 void* workspace, size_t workspace_bytes, int32_t* stop_iter_dev, double* mae_trace_dev,
+                 void* stream);
+
+/*
+ * Standalone dequantisation ("量化公式", "从压缩文件到一次前向"):
+ * W_out[i] = fp16((q_i - zero[j]) * delta[j]), j the group of flat element i.
+ *   packed, delta, zero  in  the buffers hqq_quantize wrote (same rows, cols, nbits,
+ *                        group_size, axis); meta_dtype HQQ_META_F16 or HQQ_META_F32.
+ *   W_out_fp16           out fp16 [rows, cols] row-major.
+ * The product is formed exactly and rounded once to nearest-even fp16 (for a zero
+ * of magnitude below 2^-10 the difference q - z may carry one fp32 rounding).
+ */
+int hqq_dequantize(const void* packed, const void* delta, const void* zero, int meta_dtype, int64_t rows,
+                   int64_t cols, int nbits, int group_size, int axis, void* W_out_fp16, void* stream);
+
+/*
+ * Fused dequantise + matrix product with 4-bit weights and fp16 activations
+ * ("从压缩文件到一次前向": y = x @ W_hat^T, W_hat = (q - zero) * scale):
+ *   y[b, n] = sum_k x[b, k] * (q[n, k] - zero[n, k/g]) * delta[n, k/g].
+ *   packed      in  4-bit codes of W [N, K] (axis=1 groups along K).
+ *   delta_fp16, zero_fp16  in  fp16 [N, K/group_size].
+ *   group_size  64 or 128.
+ *   x_fp16      in  fp16 [batch, K] row-major.
+ *   y           out [batch, N] row-major, y_dtype HQQ_OUT_F16 or HQQ_OUT_F32.
+ * N must be a multiple of 16 and K of 128.  batch <= 8 uses a streaming kernel that
+ * keeps q exact and applies delta and zero per group on fp32 partial sums; larger
+ * batches use an MFMA GEMM on fp16 W_hat tiles.  Accumulation is fp32 in both.
+ */
+int hqq_gemv_w4a16(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K,
+                   int group_size, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* stream);
+
+/* Static description of a status code. */
+const char* hqq_status_string(int status);
+
+/* Message of the last HQQ_ERR_* returned on the calling thread ("" if none). */
+const char* hqq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HQQ_H */

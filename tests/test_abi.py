@@ -1,0 +1,109 @@
+"""C-ABI library on the CPU: it loads, exports every symbol the header declares, and its
+host-side logic (sizes, argument checks, status strings) behaves; no kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import weight_only_quantization_amd as hq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hq.LIB_PATH):
+        from weight_only_quantization_amd import build
+        build.build()
+    return hq.load()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hqq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hqq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(hq.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_packed_bytes_match_oracle(lib):
+    o = oracle.get()
+    for nbits in (2, 3, 4):
+        for rows, cols in [(1, 16), (3, 80), (16, 64), (7, 96), (1024, 1024), (11008, 4096)]:
+            assert hq.hqq_packed_bytes(rows, cols, nbits) == o.packed_bytes(rows * cols, nbits)
+    assert hq.hqq_packed_bytes(4, 4, 5) == 0 and hq.hqq_packed_bytes(0, 4, 4) == 0
+
+
+def test_num_groups(lib):
+    assert hq.hqq_num_groups(4096, 4096, 64) == 262144
+    assert hq.hqq_num_groups(28672, 8192, 128) == 1835008
+    assert hq.hqq_num_groups(3, 5, 4) == -1
+
+
+def test_workspace_bytes(lib):
+    assert hq.hqq_quantize_workspace_bytes(1024, 1024, 4, 64, 1, 20) > 0
+    # 3-bit keeps one byte per code in the workspace
+    assert hq.hqq_quantize_workspace_bytes(64, 640, 3, 64, 1, 20) >= 64 * 640
+    assert hq.hqq_quantize_workspace_bytes(1024, 1024, 4, 48, 1, 20) == 0      # g does not divide
+    assert hq.hqq_quantize_workspace_bytes(1024, 1024, 4, 64, 1, 65) == 0      # iters too large
+    assert hq.hqq_quantize_workspace_bytes(1024, 1024, 5, 64, 1, 20) == 0      # nbits
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: every case below fails validation
+
+
+def quantize(lib, rows=64, cols=64, nbits=4, g=64, axis=1, iters=20, p=0.7, b=10.0, k=1.01, meta=0,
+             W=FAKE, ws=FAKE, wsb=1 << 30, out=FAKE):
+    return lib.hqq_quantize(W, rows, cols, nbits, g, axis, iters, p, b, k, out, out, out, meta, ws, wsb, None,
+                            None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nbits=5), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(nbits=1), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(axis=2), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(g=48), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(cols=96, g=48), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(rows=0), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(iters=-1), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(iters=65), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(p=0.0), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(p=1.5), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(b=0.0), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(k=-1.0), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(meta=7), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(W=None), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(W=ctypes.c_void_p((1 << 20) + 2)), hq.HQQ_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), hq.HQQ_ERR_WORKSPACE),
+    (dict(wsb=16), hq.HQQ_ERR_WORKSPACE),
+    (dict(rows=16, cols=4, g=16, axis=0, nbits=4), hq.HQQ_ERR_UNSUPPORTED),
+])
+def test_quantize_rejects_before_launch(lib, kw, status):
+    assert quantize(lib, **kw) == status
+    assert hq.last_error() != ""
+
+
+def test_dequantize_and_gemv_reject(lib):
+    d = lib.hqq_dequantize
+    assert d(FAKE, FAKE, FAKE, 2, 64, 64, 4, 64, 1, FAKE, None) == hq.HQQ_ERR_INVALID_ARGUMENT  # f64 meta
+    assert d(None, FAKE, FAKE, 0, 64, 64, 4, 64, 1, FAKE, None) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert d(FAKE, FAKE, FAKE, 0, 64, 96, 4, 24, 1, FAKE, None) == hq.HQQ_ERR_UNSUPPORTED
+    gv = lib.hqq_gemv_w4a16
+    assert gv(FAKE, FAKE, FAKE, 64, 256, 32, FAKE, 1, FAKE, 0, None) == hq.HQQ_ERR_UNSUPPORTED
+    assert gv(FAKE, FAKE, FAKE, 64, 200, 64, FAKE, 1, FAKE, 0, None) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert gv(FAKE, FAKE, FAKE, 24, 256, 64, FAKE, 1, FAKE, 0, None) == hq.HQQ_ERR_UNSUPPORTED
+    assert gv(FAKE, FAKE, FAKE, 64, 256, 64, FAKE, 0, FAKE, 0, None) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert gv(FAKE, FAKE, FAKE, 64, 256, 64, FAKE, 1, FAKE, 9, None) == hq.HQQ_ERR_INVALID_ARGUMENT
+
+
+def test_status_strings(lib):
+    assert hq.status_string(0) == "HQQ_OK"
+    assert hq.status_string(3) == "HQQ_ERR_WORKSPACE"
+    assert hq.status_string(99) == "HQQ_ERR_UNKNOWN"

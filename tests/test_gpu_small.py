@@ -1,0 +1,229 @@
+"""GPU parity at small sizes: the HIP path through the C ABI against the fp64 oracle, element by
+element, for every format, both axes, several tiles with a ragged tail, and the edge cases."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import (GEMV_TOL, assert_zero_close, compare_quant, gpu_quantize, say, torch_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def weights(rows, cols, seed, sigma=0.02, frac=0.001, k=10.0):
+    return synth.weight_normal(rows, cols, sigma, seed, frac, k)
+
+
+# shapes: several solve blocks and a partial last block (axis=1: 32 groups per block at g=64;
+# axis=0: 64 groups per block)
+CASES = [
+    # nbits, g, axis, rows, cols
+    (4, 64, 1, 37, 192),
+    (4, 16, 1, 29, 96),
+    (4, 32, 1, 33, 160),
+    (4, 128, 1, 17, 384),
+    (4, 256, 1, 9, 512),
+    (3, 64, 1, 37, 192),
+    (3, 16, 1, 23, 80),
+    (2, 16, 1, 37, 192),
+    (2, 64, 1, 21, 128),
+    (4, 128, 0, 256, 200),
+    (4, 64, 0, 192, 136),
+    (4, 16, 0, 48, 120),
+    (2, 16, 0, 64, 72),
+    (3, 128, 0, 256, 104),
+    (3, 32, 0, 96, 88),
+    (2, 256, 0, 256, 64),
+]
+
+
+@pytest.mark.parametrize("nbits,g,axis,rows,cols", CASES)
+def test_quantize_parity(nbits, g, axis, rows, cols):
+    say("quantize parity", nbits, g, axis, rows, cols)
+    W = weights(rows, cols, seed=1000 + rows + cols + nbits)
+    ref = oracle.get().quantize(W.astype(np.float64), nbits=nbits, group_size=g, axis=axis, iters=20)
+    gq = gpu_quantize(W, nbits, g, axis, 20, meta="f64")
+    compare_quant(W, ref, gq, nbits, g, axis)
+
+
+@pytest.mark.parametrize("meta", ["f16", "f32"])
+def test_stored_metadata_rounding(meta):
+    """fp16 / fp32 metadata are the nearest-even roundings of the solver's fp64 values."""
+    say("metadata rounding", meta)
+    W = weights(64, 256, seed=77)
+    g64 = gpu_quantize(W, 4, 64, 1, 20, meta="f64")
+    gm = gpu_quantize(W, 4, 64, 1, 20, meta=meta)
+    if meta == "f16":
+        o = oracle.get()
+        assert np.array_equal(gm["zero"].view(np.uint16), o.to_half_bits(g64["zero"]))
+        assert np.array_equal(gm["delta"].view(np.uint16), o.to_half_bits(g64["delta"]))
+    else:
+        assert np.array_equal(gm["zero"], g64["zero"].astype(np.float32))
+        assert np.array_equal(gm["delta"], g64["delta"].astype(np.float32))
+    assert np.array_equal(gm["packed"], g64["packed"])
+
+
+def edge_tensor():
+    """Groups of 64 (axis=1) with: constants, zeros, a tiny range (s = 1), a range that hits
+    the 2e4 limit, sigma-1 values (shrink active at 2 bits), single outliers, exact ties."""
+    r = np.random.default_rng(5)
+    rows, cols = 16, 128
+    W = r.normal(0, 0.02, (rows, cols))
+    W[0, :64] = 0.375
+    W[0, 64:] = 0.0
+    W[1, :64] = 0.01 + r.uniform(0, 5e-5, 64)
+    W[1, 64:] = 0.5 + r.uniform(0, 3e-4, 64)
+    W[2:6] = r.normal(0, 1.0, (4, cols))
+    W[6, 5] = 0.9
+    W[7, 70] = -1.3
+    W[8, :64] = np.arange(64) / 4.0
+    return W.astype(np.float16)
+
+
+@pytest.mark.parametrize("nbits", [2, 3, 4])
+@pytest.mark.parametrize("iters", [0, 1, 2, 20])
+def test_edge_cases(nbits, iters):
+    say("edge cases", nbits, iters)
+    W = edge_tensor()
+    ref = oracle.get().quantize(W.astype(np.float64), nbits=nbits, group_size=64, axis=1, iters=iters)
+    gq = gpu_quantize(W, nbits, 64, 1, iters, meta="f64")
+    compare_quant(W, ref, gq, nbits, 64, 1)
+
+
+def test_shrink_active_parity():
+    """sigma = 1 weights at 2 bits: residuals above the shrink threshold in every round."""
+    say("shrink active")
+    W = synth.weight_normal(48, 256, 1.0, seed=9)
+    ref = oracle.get().quantize(W.astype(np.float64), nbits=2, group_size=64, axis=1, iters=20)
+    gq = gpu_quantize(W, 2, 64, 1, 20, meta="f64")
+    compare_quant(W, ref, gq, 2, 64, 1)
+
+
+def test_other_solver_parameters():
+    say("other p / beta / kappa")
+    W = synth.weight_normal(40, 128, 0.5, seed=10)
+    for p, b0, k in [(1.0, 10.0, 1.01), (0.5, 3.0, 1.2), (0.9, 50.0, 0.95)]:
+        ref = oracle.get().quantize(W.astype(np.float64), nbits=3, group_size=32, axis=1, iters=12, p=p, beta0=b0,
+                                    kappa=k)
+        gq = gpu_quantize(W, 3, 32, 1, 12, p=p, beta0=b0, kappa=k, meta="f64")
+        compare_quant(W, ref, gq, 3, 32, 1)
+
+
+def test_repeat_calls_deterministic():
+    say("determinism")
+    W = weights(64, 512, seed=12)
+    a = gpu_quantize(W, 4, 64, 1, 20, meta="f64")
+    b = gpu_quantize(W, 4, 64, 1, 20, meta="f64")
+    for k in ("packed", "delta", "zero"):
+        assert np.array_equal(a[k], b[k])
+    assert np.array_equal(a["mae"], b["mae"], equal_nan=True) and a["stop"] == b["stop"]
+
+
+# ---------------------------------------------------------------------------- dequantisation
+
+DQ_CASES = [(4, 64, 1, 37, 192), (4, 128, 0, 256, 200), (3, 64, 1, 37, 192), (3, 16, 0, 48, 120),
+            (2, 16, 1, 37, 192), (2, 32, 0, 96, 88), (4, 16, 1, 13, 48)]
+
+
+@pytest.mark.parametrize("nbits,g,axis,rows,cols", DQ_CASES)
+@pytest.mark.parametrize("meta", ["f16", "f32"])
+def test_dequant_bit_exact(nbits, g, axis, rows, cols, meta):
+    """GPU dequantisation of the oracle's packed codes and stored metadata equals the oracle's
+    nearest-even fp16 of the exact (q - z) * delta."""
+    import weight_only_quantization_amd as hq
+    torch = torch_dev()
+    say("dequant", nbits, g, axis, rows, cols, meta)
+    o = oracle.get()
+    W = weights(rows, cols, seed=2000 + rows)
+    ref = o.quantize(W.astype(np.float64), nbits=nbits, group_size=g, axis=axis, iters=20)
+    packed = o.pack(ref["codes"], nbits)
+    if meta == "f16":
+        d = ref["delta16"].view(np.float16)
+        z = ref["zero16"].view(np.float16)
+    else:
+        d = ref["delta"].astype(np.float32)
+        z = ref["z"].astype(np.float32)
+    _, w16 = o.dequant(packed, d, z, rows, cols, nbits, g, axis)
+    out = hq.hqq_dequantize(torch.from_numpy(packed).cuda(), torch.from_numpy(d).cuda(), torch.from_numpy(z).cuda(),
+                            rows, cols, nbits, g, axis)
+    got = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, w16), int((got != w16).sum())
+
+
+def test_dequant_synthetic_extremes():
+    """Random codes with metadata across fp16's range (subnormal steps, large and negative
+    zeros): still the nearest-even fp16 of the exact product."""
+    import weight_only_quantization_amd as hq
+    torch = torch_dev()
+    say("dequant extremes")
+    o = oracle.get()
+    r = np.random.default_rng(3)
+    rows, cols, g = 64, 256, 64
+    G = rows * cols // g
+    codes = r.integers(0, 16, (rows, cols)).astype(np.uint8)
+    d = np.concatenate([r.uniform(5e-5, 6e-5, G // 4), r.uniform(1e-3, 0.1, G // 4), r.uniform(1, 30, G // 4),
+                        r.uniform(1e-7, 5e-6, G - 3 * (G // 4))]).astype(np.float16)
+    z = np.concatenate([r.uniform(-100, 100, G // 2), r.uniform(0, 15, G - G // 2)]).astype(np.float16)
+    packed = o.pack(codes, 4)
+    _, w16 = o.dequant(packed, d, z, rows, cols, 4, g, 1)
+    out = hq.hqq_dequantize(torch.from_numpy(packed).cuda(), torch.from_numpy(d).cuda(), torch.from_numpy(z).cuda(),
+                            rows, cols, 4, g, 1)
+    got = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, w16), int((got != w16).sum())
+
+
+# ---------------------------------------------------------------------------- fused product
+
+def gemv_inputs(N, K, g, seed):
+    o = oracle.get()
+    W = weights(N, K, seed=seed, frac=0.0)
+    ref = o.quantize(W.astype(np.float64), nbits=4, group_size=g, axis=1, iters=20)
+    return o.pack(ref["codes"], 4), ref["delta16"].view(np.float16), ref["zero16"].view(np.float16)
+
+
+def check_gemv(packed, d16, z16, N, K, g, x, out_f32, rows_sel=None):
+    import weight_only_quantization_amd as hq
+    torch = torch_dev()
+    o = oracle.get()
+    y = hq.hqq_gemv_w4a16(torch.from_numpy(packed).cuda(), torch.from_numpy(d16).cuda(),
+                          torch.from_numpy(z16).cuda(), N, K, g, torch.from_numpy(x).cuda(),
+                          out_dtype=torch.float32 if out_f32 else torch.float16)
+    yg = y.float().cpu().numpy().astype(np.float64)
+    yr = o.gemv(packed, d16, z16, N, K, g, x.astype(np.float64), rows_sel=rows_sel)
+    if rows_sel is not None:
+        yg = yg[:, rows_sel]
+    scale = np.maximum(np.abs(yr), np.sqrt(np.mean(yr ** 2)))
+    err = np.abs(yg - yr) / scale
+    assert err.max() <= GEMV_TOL, "max rel err %.3g" % err.max()
+    return float(err.max())
+
+
+@pytest.mark.parametrize("g", [64, 128])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 7, 8, 9, 16, 33, 130])
+def test_gemv_parity(g, batch):
+    say("gemv", g, batch)
+    N, K = 96, 1152  # 9 chunks of 128 codes: uneven over the 8 waves of a block
+    packed, d16, z16 = gemv_inputs(N, K, g, seed=3000 + g)
+    x = synth.activations(batch, K, seed=11)
+    check_gemv(packed, d16, z16, N, K, g, x, out_f32=True)
+    check_gemv(packed, d16, z16, N, K, g, x, out_f32=False)
+
+
+def test_gemv_onehot_columns():
+    """A one-hot activation row returns one column of W_hat (to fp32 rounding)."""
+    import weight_only_quantization_amd as hq
+    torch = torch_dev()
+    say("gemv one-hot")
+    o = oracle.get()
+    N, K, g = 64, 512, 64
+    packed, d16, z16 = gemv_inputs(N, K, g, seed=55)
+    w64, _ = o.dequant(packed, d16, z16, N, K, 4, g, 1)
+    for batch in (1, 8, 24):
+        ks = np.arange(batch) * 37 % K
+        x = np.zeros((batch, K), np.float16)
+        x[np.arange(batch), ks] = 1.0
+        y = hq.hqq_gemv_w4a16(torch.from_numpy(packed).cuda(), torch.from_numpy(d16).cuda(),
+                              torch.from_numpy(z16).cuda(), N, K, g, torch.from_numpy(x).cuda(),
+                              out_dtype=torch.float32).cpu().numpy()
+        ref = w64[:, ks].T
+        assert np.allclose(y, ref, rtol=2e-3, atol=2e-3 * np.abs(ref).max())

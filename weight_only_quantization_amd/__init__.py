@@ -1,0 +1,193 @@
+"""Python binding of the HQQ C-ABI library (``libhqq.so``, HIP kernels for gfx950).
+
+The functions here only marshal arguments: torch tensors provide device memory and the
+current HIP stream; every step of the quantizer, the dequantisation and the fused
+product runs in the library's kernels.  There is no fallback: when the library is missing
+the import of a compute function raises.
+
+Names follow the C ABI (``include/hqq.h``): ``hqq_quantize``, ``hqq_dequantize``,
+``hqq_gemv_w4a16``, plus the size queries.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhqq.so")
+
+HQQ_OK = 0
+HQQ_ERR_INVALID_ARGUMENT = 1
+HQQ_ERR_UNSUPPORTED = 2
+HQQ_ERR_WORKSPACE = 3
+HQQ_ERR_DEVICE = 4
+HQQ_META_F16, HQQ_META_F32, HQQ_META_F64 = 0, 1, 2
+HQQ_OUT_F16, HQQ_OUT_F32 = 0, 1
+HQQ_MAX_ITERS = 64
+
+# Every symbol the header declares.
+EXPORTS = ("hqq_packed_bytes", "hqq_num_groups", "hqq_quantize_workspace_bytes", "hqq_quantize",
+           "hqq_dequantize", "hqq_gemv_w4a16", "hqq_status_string", "hqq_last_error")
+
+_lib = None
+
+
+class HQQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (status_string(status) if _lib else status, message))
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libhqq.so (raises OSError when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError("libhqq.so not built (run `python -m weight_only_quantization_amd.build`): %s" % path)
+    lib = ctypes.CDLL(path)
+    i64, i32, dbl, p, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t
+    lib.hqq_packed_bytes.argtypes = [i64, i64, i32]
+    lib.hqq_packed_bytes.restype = sz
+    lib.hqq_num_groups.argtypes = [i64, i64, i32]
+    lib.hqq_num_groups.restype = i64
+    lib.hqq_quantize_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+    lib.hqq_quantize_workspace_bytes.restype = sz
+    lib.hqq_quantize.argtypes = [p, i64, i64, i32, i32, i32, i32, dbl, dbl, dbl, p, p, p, i32, p, sz, p, p, p]
+    lib.hqq_quantize.restype = i32
+    lib.hqq_dequantize.argtypes = [p, p, p, i32, i64, i64, i32, i32, i32, p, p]
+    lib.hqq_dequantize.restype = i32
+    lib.hqq_gemv_w4a16.argtypes = [p, p, p, i64, i64, i32, p, i64, p, i32, p]
+    lib.hqq_gemv_w4a16.restype = i32
+    lib.hqq_status_string.argtypes = [i32]
+    lib.hqq_status_string.restype = ctypes.c_char_p
+    lib.hqq_last_error.argtypes = []
+    lib.hqq_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().hqq_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().hqq_last_error().decode()
+
+
+def _check(status: int):
+    if status != HQQ_OK:
+        raise HQQError(status, last_error())
+
+
+# ------------------------------------------------------------------------------ size queries
+
+def hqq_packed_bytes(rows: int, cols: int, nbits: int) -> int:
+    return load().hqq_packed_bytes(rows, cols, nbits)
+
+
+def hqq_num_groups(rows: int, cols: int, group_size: int) -> int:
+    return load().hqq_num_groups(rows, cols, group_size)
+
+
+def hqq_quantize_workspace_bytes(rows, cols, nbits, group_size, axis, iters) -> int:
+    return load().hqq_quantize_workspace_bytes(rows, cols, nbits, group_size, axis, iters)
+
+
+# ------------------------------------------------------------------------------ compute calls
+
+def _stream_ptr(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_META = {}
+
+
+def _meta_code(dtype) -> int:
+    import torch
+    if not _META:
+        _META.update({torch.float16: HQQ_META_F16, torch.float32: HQQ_META_F32, torch.float64: HQQ_META_F64})
+    return _META[dtype]
+
+
+@dataclass
+class Quantized:
+    """Result of hqq_quantize: packed codes plus per-group step and zero, and the solver's
+    device-side stop index and MAE trace."""
+    packed: "object"
+    delta: "object"
+    zero: "object"
+    rows: int
+    cols: int
+    nbits: int
+    group_size: int
+    axis: int
+    stop_iter: "object"
+    mae_trace: "object"
+
+
+def hqq_quantize(W, nbits: int = 4, group_size: int = 64, axis: int = 1, iters: int = 20, p: float = 0.7,
+                 beta0: float = 10.0, kappa: float = 1.01, meta_dtype=None, workspace=None, out=None,
+                 stream=None) -> Quantized:
+    """HQQ quantisation of a 2-D fp16 CUDA tensor.  Output buffers are torch tensors (or the
+    ones passed in `out` as (packed, delta, zero, stop_iter, mae_trace))."""
+    import torch
+    lib = load()
+    assert W.dtype == torch.float16 and W.is_cuda and W.dim() == 2 and W.is_contiguous()
+    rows, cols = W.shape
+    meta_dtype = meta_dtype or torch.float16
+    G = lib.hqq_num_groups(rows, cols, group_size)
+    dev = W.device
+    if out is None:
+        packed = torch.empty(max(lib.hqq_packed_bytes(rows, cols, nbits), 1), dtype=torch.uint8, device=dev)
+        delta = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
+        zero = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
+        stop_iter = torch.empty(1, dtype=torch.int32, device=dev)
+        mae_trace = torch.empty(max(iters, 1), dtype=torch.float64, device=dev)
+    else:
+        packed, delta, zero, stop_iter, mae_trace = out
+    ws_bytes = lib.hqq_quantize_workspace_bytes(rows, cols, nbits, group_size, axis, iters)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    st = lib.hqq_quantize(ctypes.c_void_p(W.data_ptr()), rows, cols, nbits, group_size, axis, iters, p, beta0, kappa,
+                          ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                          ctypes.c_void_p(zero.data_ptr()), _meta_code(meta_dtype),
+                          ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+                          ctypes.c_void_p(stop_iter.data_ptr()), ctypes.c_void_p(mae_trace.data_ptr()),
+                          _stream_ptr(stream))
+    _check(st)
+    return Quantized(packed, delta, zero, rows, cols, nbits, group_size, axis, stop_iter, mae_trace)
+
+
+def hqq_dequantize(packed, delta, zero, rows: int, cols: int, nbits: int, group_size: int, axis: int, out=None,
+                   stream=None):
+    """fp16 [rows, cols] W_hat = (q - zero) * delta."""
+    import torch
+    lib = load()
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float16, device=packed.device)
+    st = lib.hqq_dequantize(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                            ctypes.c_void_p(zero.data_ptr()), _meta_code(delta.dtype), rows, cols, nbits, group_size,
+                            axis, ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream))
+    _check(st)
+    return out
+
+
+def hqq_gemv_w4a16(packed, delta, zero, N: int, K: int, group_size: int, x, out_dtype=None, out=None,
+                   stream=None):
+    """y [batch, N] = x [batch, K] @ W_hat^T for a 4-bit axis=1 weight W [N, K]."""
+    import torch
+    lib = load()
+    out_dtype = out_dtype or torch.float16
+    batch = x.shape[0]
+    if out is None:
+        out = torch.empty((batch, N), dtype=out_dtype, device=x.device)
+    code = HQQ_OUT_F16 if out.dtype == torch.float16 else HQQ_OUT_F32
+    st = lib.hqq_gemv_w4a16(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                            ctypes.c_void_p(zero.data_ptr()), N, K, group_size, ctypes.c_void_p(x.data_ptr()), batch,
+                            ctypes.c_void_p(out.data_ptr()), code, _stream_ptr(stream))
+    _check(st)
+    return out

@@ -1,0 +1,213 @@
+// C ABI of the HQQ library: argument checks, workspace layout, kernel dispatch.
+// Every check happens before anything is enqueued; no exception crosses the boundary.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "hqq_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int device_fail(hipError_t e, const char* what) {
+  return fail(HQQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2_group(int g) { return g == 16 || g == 32 || g == 64 || g == 128 || g == 256; }
+
+// Shared shape checks of quantize / dequantize.  Returns HQQ_OK or an error (message set).
+int check_shape(int64_t rows, int64_t cols, int nbits, int g, int axis) {
+  if (rows <= 0 || cols <= 0) return fail(HQQ_ERR_INVALID_ARGUMENT, "rows and cols must be positive");
+  if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31) || rows * cols > (int64_t(1) << 40))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "tensor too large");
+  if (nbits != 2 && nbits != 3 && nbits != 4) return fail(HQQ_ERR_INVALID_ARGUMENT, "nbits must be 2, 3 or 4");
+  if (axis != 0 && axis != 1) return fail(HQQ_ERR_INVALID_ARGUMENT, "axis must be 0 or 1");
+  if (g <= 0) return fail(HQQ_ERR_INVALID_ARGUMENT, "group_size must be positive");
+  if ((axis == 1 ? cols : rows) % g != 0)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "group_size %d does not divide %s", g, axis == 1 ? "cols" : "rows");
+  if (!pow2_group(g)) return fail(HQQ_ERR_UNSUPPORTED, "group_size must be 16, 32, 64, 128 or 256");
+  if (axis == 0 && ((rows / g) * cols) % 8 != 0)
+    return fail(HQQ_ERR_UNSUPPORTED, "axis=0 needs (rows/group_size)*cols to be a multiple of 8");
+  return HQQ_OK;
+}
+
+struct QuantLayout {
+  int64_t G, nblocks;
+  int threads;
+  size_t lds;
+  size_t off_partials, off_codes, total;
+};
+
+bool quant_layout(int64_t rows, int64_t cols, int nbits, int g, int axis, int iters, QuantLayout* q) {
+  q->G = rows * cols / g;
+  if (!hqq::quant_geometry(q->G, g, axis, iters, &q->nblocks, &q->threads, &q->lds)) return false;
+  auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
+  q->off_partials = 256;
+  q->off_codes = up(q->off_partials + (size_t)iters * q->nblocks * sizeof(double));
+  q->total = q->off_codes + (nbits == 3 ? up((size_t)(rows * cols)) : 0);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hqq_packed_bytes(int64_t rows, int64_t cols, int nbits) {
+  if (rows <= 0 || cols <= 0) return 0;
+  const int64_t N = rows * cols;
+  if (nbits == 4) return (size_t)((N + 1) / 2);
+  if (nbits == 2) return (size_t)((N + 3) / 4);
+  if (nbits == 3) return (size_t)(4 * ((N + 9) / 10));
+  return 0;
+}
+
+int64_t hqq_num_groups(int64_t rows, int64_t cols, int group_size) {
+  if (rows <= 0 || cols <= 0 || group_size <= 0) return -1;
+  const int64_t N = rows * cols;
+  return N % group_size == 0 ? N / group_size : -1;
+}
+
+size_t hqq_quantize_workspace_bytes(int64_t rows, int64_t cols, int nbits, int group_size, int axis, int iters) {
+  if (check_shape(rows, cols, nbits, group_size, axis) != HQQ_OK || iters < 0 || iters > HQQ_MAX_ITERS) return 0;
+  QuantLayout q;
+  if (!quant_layout(rows, cols, nbits, group_size, axis, iters, &q)) return 0;
+  return q.total;
+}
+
+int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int group_size, int axis, int iters,
+                 double p, double beta0, double kappa, void* packed, void* delta, void* zero, int meta_dtype,
+                 void* workspace, size_t workspace_bytes, int32_t* stop_iter_dev, double* mae_trace_dev,
+                 void* stream) {
+  g_last_error[0] = 0;
+  int st = check_shape(rows, cols, nbits, group_size, axis);
+  if (st != HQQ_OK) return st;
+  if (iters < 0 || iters > HQQ_MAX_ITERS) return fail(HQQ_ERR_INVALID_ARGUMENT, "iters must be in [0, %d]", HQQ_MAX_ITERS);
+  if (!(p > 0.0 && p <= 1.0)) return fail(HQQ_ERR_INVALID_ARGUMENT, "p must be in (0, 1]");
+  if (!(beta0 > 0.0) || !isfinite(beta0)) return fail(HQQ_ERR_INVALID_ARGUMENT, "beta0 must be positive");
+  if (!(kappa > 0.0) || !isfinite(kappa)) return fail(HQQ_ERR_INVALID_ARGUMENT, "kappa must be positive");
+  if (meta_dtype != HQQ_META_F16 && meta_dtype != HQQ_META_F32 && meta_dtype != HQQ_META_F64)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "meta_dtype must be HQQ_META_F16, _F32 or _F64");
+  if (!W_fp16 || !packed || !delta || !zero) return fail(HQQ_ERR_INVALID_ARGUMENT, "null buffer");
+  if (!aligned16(W_fp16) || !aligned16(packed) || !aligned16(delta) || !aligned16(zero))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(stop_iter_dev) & 3u) || (reinterpret_cast<uintptr_t>(mae_trace_dev) & 7u))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "stop_iter_dev / mae_trace_dev misaligned");
+  QuantLayout q;
+  if (!quant_layout(rows, cols, nbits, group_size, axis, iters, &q))
+    return fail(HQQ_ERR_UNSUPPORTED, "configuration needs more LDS than one block may use");
+  if (!workspace || workspace_bytes < q.total)
+    return fail(HQQ_ERR_WORKSPACE, "workspace of %zu bytes needed", q.total);
+  if (!aligned16(workspace)) return fail(HQQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+
+  hqq::SolveArgs a;
+  memset(&a, 0, sizeof(a));
+  a.W = reinterpret_cast<const __half*>(W_fp16);
+  a.packed = reinterpret_cast<uint8_t*>(packed);
+  a.delta = delta;
+  a.zero = zero;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  a.ctrl = reinterpret_cast<int32_t*>(ws);
+  a.partials = reinterpret_cast<double*>(ws + q.off_partials);
+  a.codes_ws = nbits == 3 ? ws + q.off_codes : nullptr;
+  a.G = q.G;
+  a.nblocks = q.nblocks;
+  a.iters = iters;
+  a.meta_dtype = meta_dtype;
+  a.qmax = (double)((1 << nbits) - 1);
+  a.tiny = HQQ_TINY_RANGE;
+  a.pm1 = p - 1.0;
+  // beta_k by repeated products (beta grows by kappa after every round); thresholds of the
+  // shrink: e = 0 exactly for |r| <= beta^(-1/(2-p)); a 1e-6 relative margin keeps the fast
+  // path strictly inside that region.
+  double beta = beta0;
+  for (int k = 0; k < iters; ++k) {
+    a.beta[k] = beta;
+    a.thr[k] = pow(beta, -1.0 / (2.0 - p)) * (1.0 - 1e-6);
+    beta = beta * kappa;
+  }
+  double m = INFINITY;
+  for (int k = iters - 1; k >= 0; --k) {
+    m = fmin(m, a.thr[k]);
+    a.thr_frozen[k] = m;
+  }
+  hipError_t e = hqq::launch_quantize(a, nbits, group_size, axis, q.lds, rows * cols, mae_trace_dev, stop_iter_dev,
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "hqq_quantize launch");
+  return HQQ_OK;
+}
+
+int hqq_dequantize(const void* packed, const void* delta, const void* zero, int meta_dtype, int64_t rows,
+                   int64_t cols, int nbits, int group_size, int axis, void* W_out_fp16, void* stream) {
+  g_last_error[0] = 0;
+  int st = check_shape(rows, cols, nbits, group_size, axis);
+  if (st != HQQ_OK) return st;
+  if (meta_dtype != HQQ_META_F16 && meta_dtype != HQQ_META_F32)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "meta_dtype must be HQQ_META_F16 or HQQ_META_F32");
+  if (!packed || !delta || !zero || !W_out_fp16) return fail(HQQ_ERR_INVALID_ARGUMENT, "null buffer");
+  if (!aligned16(packed) || !aligned16(delta) || !aligned16(zero) || !aligned16(W_out_fp16))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
+  hipError_t e = hqq::launch_dequant(reinterpret_cast<const uint8_t*>(packed), delta, zero, meta_dtype, rows, cols,
+                                     nbits, group_size, axis, reinterpret_cast<__half*>(W_out_fp16),
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "hqq_dequantize launch");
+  return HQQ_OK;
+}
+
+int hqq_gemv_w4a16(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K,
+                   int group_size, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* stream) {
+  g_last_error[0] = 0;
+  if (N <= 0 || K <= 0 || batch <= 0) return fail(HQQ_ERR_INVALID_ARGUMENT, "N, K and batch must be positive");
+  if (N > (int64_t(1) << 31) || K > (int64_t(1) << 31) || batch > (int64_t(1) << 24))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "shape too large");
+  if (group_size <= 0 || K % group_size != 0) return fail(HQQ_ERR_INVALID_ARGUMENT, "group_size must divide K");
+  if (group_size != 64 && group_size != 128) return fail(HQQ_ERR_UNSUPPORTED, "group_size must be 64 or 128");
+  if (N % 16 != 0 || K % 128 != 0) return fail(HQQ_ERR_UNSUPPORTED, "N must be a multiple of 16 and K of 128");
+  if (y_dtype != HQQ_OUT_F16 && y_dtype != HQQ_OUT_F32)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "y_dtype must be HQQ_OUT_F16 or HQQ_OUT_F32");
+  if (!packed || !delta_fp16 || !zero_fp16 || !x_fp16 || !y) return fail(HQQ_ERR_INVALID_ARGUMENT, "null buffer");
+  if (!aligned16(packed) || !aligned16(delta_fp16) || !aligned16(zero_fp16) || !aligned16(x_fp16) || !aligned16(y))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* pk = reinterpret_cast<const uint8_t*>(packed);
+  const __half* dl = reinterpret_cast<const __half*>(delta_fp16);
+  const __half* zr = reinterpret_cast<const __half*>(zero_fp16);
+  const __half* xx = reinterpret_cast<const __half*>(x_fp16);
+  hipError_t e;
+  if (batch <= 8) {
+    if (hqq::gemv_lds_bytes(K, group_size, batch) > 64 * 1024) return fail(HQQ_ERR_UNSUPPORTED, "LDS too large");
+    e = hqq::launch_gemv(pk, dl, zr, N, K, group_size, xx, batch, y, y_dtype, st);
+  } else {
+    e = hqq::launch_gemm(pk, dl, zr, N, K, group_size, xx, batch, y, y_dtype, st);
+  }
+  if (e != hipSuccess) return device_fail(e, "hqq_gemv_w4a16 launch");
+  return HQQ_OK;
+}
+
+const char* hqq_status_string(int status) {
+  switch (status) {
+    case HQQ_OK: return "HQQ_OK";
+    case HQQ_ERR_INVALID_ARGUMENT: return "HQQ_ERR_INVALID_ARGUMENT";
+    case HQQ_ERR_UNSUPPORTED: return "HQQ_ERR_UNSUPPORTED";
+    case HQQ_ERR_WORKSPACE: return "HQQ_ERR_WORKSPACE";
+    case HQQ_ERR_DEVICE: return "HQQ_ERR_DEVICE";
+    default: return "HQQ_ERR_UNKNOWN";
+  }
+}
+
+const char* hqq_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/hqq.h"
+
+namespace hqq {
+
+// Arguments of the quantizer kernels (passed by value in the kernel argument segment).
+struct SolveArgs {
+  const __half* W;     // [rows, cols] fp16
+  uint8_t* packed;     // packed output (2/4-bit written directly)
+  void* delta;         // [G] meta_dtype
+  void* zero;          // [G] meta_dtype
+  uint8_t* codes_ws;   // 3-bit: one byte per code, packed afterwards; else nullptr
+  double* partials;    // [iters][nblocks] per-block sums of |W - W_hat| per round
+  int32_t* ctrl;       // [0] = index of the kept zero, [1] = rounds evaluated
+  int64_t G;           // number of groups (= M for axis 0)
+  int64_t nblocks;     // blocks of the solve kernel
+  int iters;
+  int meta_dtype;
+  double qmax;         // 2^b - 1
+  double tiny;         // range at or below which s = 1
+  double pm1;          // p - 1 (exponent of the shrink)
+  double beta[HQQ_MAX_ITERS];        // beta_k = beta0 * kappa^k (repeated products)
+  double thr[HQQ_MAX_ITERS];         // |r| below which round k's shrink is exactly 0
+  double thr_frozen[HQQ_MAX_ITERS];  // min over rounds j >= k of thr[j]
+};
+
+// Quantizer: one solve pass (speculates that the loop runs all rounds), the device-side stop
+// decision, a fix-up pass that redoes the groups when the loop stopped early, 3-bit packing.
+hipError_t launch_quantize(const SolveArgs& a, int nbits, int group_size, int axis, size_t lds_bytes,
+                           int64_t N, double* mae_trace, int32_t* stop_iter, hipStream_t stream);
+// Geometry of the solve kernel for a configuration: blocks, threads, dynamic LDS bytes.
+bool quant_geometry(int64_t G, int group_size, int axis, int iters, int64_t* nblocks, int* threads,
+                    size_t* lds_bytes);
+
+hipError_t launch_dequant(const uint8_t* packed, const void* delta, const void* zero, int meta_dtype,
+                          int64_t rows, int64_t cols, int nbits, int group_size, int axis, __half* out,
+                          hipStream_t stream);
+
+hipError_t launch_gemv(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                       int group_size, const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t stream);
+size_t gemv_lds_bytes(int64_t K, int group_size, int64_t batch);
+
+hipError_t launch_gemm(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                       int group_size, const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t stream);
+
+}  // namespace hqq

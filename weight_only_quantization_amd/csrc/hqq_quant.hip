@@ -1,0 +1,529 @@
+// HQQ quantizer kernels for gfx950 (CDNA4).
+//
+// Method (page "HQQ 算法解读", sections "第一拍", "第二拍", "为什么 zero 是这个均值",
+// "shrink 不是删除极值", "axis 不是一个无关紧要的开关", "为什么一定要分组"):
+//   per group: min-max start s = (2^b-1)/(max-min) (1 when the range is tiny, at most 2e4),
+//   z0 = -min*s, delta = 1/s; then rounds k = 0..: q = clip(rint(W*s + z_k)), W_hat =
+//   (q - z_k)*delta, r = W - W_hat, err_k = sum|r|, e = shrink(r; beta_k, p),
+//   z_(k+1) = mean(q - (W - e)*s); the whole-tensor MAE of round k decides the stop;
+//   final codes q = clip(rint(W*s + z_kept)).
+//
+// Mapping: a group of g weights is held by L lanes of one 64-wide wave, E = g/L weights per
+// lane in VGPRs (fp64 W and W*s, both formed once), so the whole iteration runs out of
+// registers.  Group sums (|r| and the zero update) and the min/max start are reduced over
+// the L lanes with DPP row permutations (quad_perm, row_half_mirror, row_mirror), which give
+// every lane of the group the bit-identical result.  All solver arithmetic is fp64 with no
+// contraction (the library is built with -ffp-contract=off), in the operation order of the
+// method; only the summation order inside a group differs from a sequential sum.
+//
+// Global early stop without host round trips: each block writes, per round, the sum of its
+// groups' |r| sums (fixed order) to the workspace; a one-block kernel adds the block sums in
+// a fixed order, forms MAE_k, applies the stop rule and stores the index of the kept zero
+// on the device.  The solve pass speculates that the loop runs all rounds and writes the
+// final codes for z_iters directly; a fix-up pass (same kernel, reading the index from
+// device memory) redoes the groups only when the loop stopped early.
+//
+// Frozen groups: when a round leaves the zero unchanged (z_(k+1) == z_k bit for bit) and
+// every residual is below the smallest shrink threshold of the remaining rounds, every later
+// round repeats this one exactly (same q, same r, e = 0, same zero), so the wave stops
+// computing once all its groups are frozen and fills the remaining rounds' |r| sums with the
+// last value.  The results are identical to running every round.
+//
+// Shrink fast path: e = 0 exactly when |r| <= beta^(-1/(2-p)); the kernel takes e = 0 for
+// |r| below that threshold times (1 - 1e-6) (a margin far above the rounding of the
+// expression) and evaluates the shrink with pow() otherwise.
+
+#include "hqq_internal.h"
+
+namespace hqq {
+namespace {
+
+// ------------------------------------------------------------------------------------------
+// Cross-lane reductions inside aligned segments of L lanes (L in 1, 2, 4, 8, 16), by DPP.
+// ------------------------------------------------------------------------------------------
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+  return __builtin_amdgcn_update_dpp(0.0, v, CTRL, 0xF, 0xF, false);
+}
+
+template <int L>
+__device__ __forceinline__ double seg_sum(double v) {
+  if constexpr (L >= 2) v = v + dpp<kDppXor1>(v);
+  if constexpr (L >= 4) v = v + dpp<kDppXor2>(v);
+  if constexpr (L >= 8) v = v + dpp<kDppHalfMirror>(v);
+  if constexpr (L >= 16) v = v + dpp<kDppMirror>(v);
+  return v;
+}
+template <int L>
+__device__ __forceinline__ double seg_min(double v) {
+  if constexpr (L >= 2) v = fmin(v, dpp<kDppXor1>(v));
+  if constexpr (L >= 4) v = fmin(v, dpp<kDppXor2>(v));
+  if constexpr (L >= 8) v = fmin(v, dpp<kDppHalfMirror>(v));
+  if constexpr (L >= 16) v = fmin(v, dpp<kDppMirror>(v));
+  return v;
+}
+template <int L>
+__device__ __forceinline__ double seg_max(double v) {
+  if constexpr (L >= 2) v = fmax(v, dpp<kDppXor1>(v));
+  if constexpr (L >= 4) v = fmax(v, dpp<kDppXor2>(v));
+  if constexpr (L >= 8) v = fmax(v, dpp<kDppHalfMirror>(v));
+  if constexpr (L >= 16) v = fmax(v, dpp<kDppMirror>(v));
+  return v;
+}
+
+// fp64 -> fp16 bits, round to nearest even: round to odd into fp32 (24 >= 11 + 2 bits, so the
+// second rounding is exact), then the hardware fp32 -> fp16 conversion.
+__device__ __forceinline__ unsigned short f64_to_f16_bits(double x) {
+  const float f = (float)x;
+  unsigned u = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != x && !__builtin_isinf(f)) {
+    if (fabs(back) > fabs(x)) u -= 1u;
+    u |= 1u;
+  }
+  return __half_as_ushort(__float2half_rn(__uint_as_float(u)));
+}
+
+__device__ __forceinline__ void store_meta(void* p, int dtype, int64_t j, double v) {
+  if (dtype == HQQ_META_F16)
+    reinterpret_cast<unsigned short*>(p)[j] = f64_to_f16_bits(v);
+  else if (dtype == HQQ_META_F32)
+    reinterpret_cast<float*>(p)[j] = (float)v;
+  else
+    reinterpret_cast<double*>(p)[j] = v;
+}
+
+// |r| - |r|^(p-1)/beta for the shrink's rare slow path; kept out of line so that pow's
+// temporaries do not raise the register count of the whole solver.
+__device__ __noinline__ double shrink_mag(double a, double pm1, double beta) { return a - pow(a, pm1) / beta; }
+
+// Lanes per group (L) and weights per lane (E) for a group size.
+template <int G>
+struct Shape {
+  static constexpr int E = (G == 16) ? 4 : (G >= 256 ? 16 : 8);
+  static constexpr int L = G / E;
+  static constexpr int GPW = 64 / L;  // groups per wave
+  static_assert(L >= 1 && L <= 16 && E * L == G, "group size");
+};
+
+// ------------------------------------------------------------------------------------------
+// One proximal round of one group (per lane: E weights).  Returns the group's sum of |r|,
+// the next zero and this lane's largest |r|.
+// ------------------------------------------------------------------------------------------
+template <int E, int L>
+__device__ __forceinline__ void hqq_round(const double (&w)[E], const double (&ws)[E], double s, double delta,
+                                          double z, double qmax, double beta, double pm1, double thr,
+                                          double inv_g, double& err_o, double& zn_o, double& maxr_o) {
+  double err = 0.0, acc = 0.0, maxr = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const double t = ws[e] + z;
+    double qq = __builtin_rint(t);
+    qq = fmax(qq, 0.0);
+    qq = fmin(qq, qmax);
+    const double wh = (qq - z) * delta;
+    const double rr = w[e] - wh;
+    err += fabs(rr);
+    maxr = fmax(maxr, fabs(rr));
+    acc += qq - ws[e];  // e = 0: (W - e)*s is W*s
+  }
+  if (__any(maxr >= thr)) {
+    // Some residual of the wave may pass the shrink: redo the zero sum with the shrink
+    // evaluated wherever it can be non-zero (q and r recomputed identically).
+    acc = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const double t = ws[e] + z;
+      double qq = __builtin_rint(t);
+      qq = fmax(qq, 0.0);
+      qq = fmin(qq, qmax);
+      const double wh = (qq - z) * delta;
+      const double rr = w[e] - wh;
+      const double a = fabs(rr);
+      double ee = 0.0;
+      if (a >= thr) {
+        const double v = shrink_mag(a, pm1, beta);
+        if (v > 0.0) ee = (rr < 0.0) ? -v : v;
+      }
+      acc += (ee == 0.0) ? (qq - ws[e]) : (qq - (w[e] - ee) * s);
+    }
+  }
+  err_o = seg_sum<L>(err);
+  zn_o = seg_sum<L>(acc) * inv_g;
+  maxr_o = maxr;
+}
+
+// Start of a group from its weights (min-max), then the rounds.  Returns the final zero.
+// err_lds (nullptr in the fix-up pass) receives the group's |r| sum per round at
+// err_lds[k * stride]; rounds after the wave froze get the frozen value.
+template <int E, int L>
+__device__ __forceinline__ double solve_group(const SolveArgs& a, const double (&w)[E], double (&ws)[E],
+                                              bool valid, int kmax, double* err_lds, int stride, bool write_err,
+                                              double& s_o, double& delta_o) {
+  double mn = w[0], mx = w[0];
+#pragma unroll
+  for (int e = 1; e < E; ++e) {
+    mn = fmin(mn, w[e]);
+    mx = fmax(mx, w[e]);
+  }
+  mn = seg_min<L>(mn);
+  mx = seg_max<L>(mx);
+  const double d = mx - mn;
+  double s = (d <= a.tiny) ? 1.0 : a.qmax / d;
+  s = fmin(s, HQQ_MAX_SCALE);
+  const double delta = 1.0 / s;
+  double z = -mn * s;
+#pragma unroll
+  for (int e = 0; e < E; ++e) ws[e] = w[e] * s;
+
+  const double inv_g = 1.0 / (double)(E * L);
+  for (int k = 0; k < kmax; ++k) {
+    double err, zn, maxr;
+    hqq_round<E, L>(w, ws, s, delta, z, a.qmax, a.beta[k], a.pm1, a.thr[k], inv_g, err, zn, maxr);
+    if (write_err) err_lds[k * stride] = valid ? err : 0.0;
+    const bool frozen = !valid || (zn == z && maxr <= a.thr_frozen[k]);
+    z = zn;
+    if (__all(frozen)) {
+      if (write_err)
+        for (int kk = k + 1; kk < a.iters; ++kk) err_lds[kk * stride] = valid ? err : 0.0;
+      break;
+    }
+  }
+  s_o = s;
+  delta_o = delta;
+  return z;
+}
+
+template <int E>
+__device__ __forceinline__ void final_codes(const double (&ws)[E], double z, double qmax, unsigned (&c)[E]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    double qq = __builtin_rint(ws[e] + z);
+    qq = fmax(qq, 0.0);
+    qq = fmin(qq, qmax);
+    c[e] = (unsigned)qq;
+  }
+}
+
+// Sum of the per-group round errors of the block, in a fixed order, to the workspace.
+__device__ __forceinline__ void write_partials(const SolveArgs& a, const double* err_lds, int ngroups_block) {
+  __syncthreads();
+  for (int k = threadIdx.x; k < a.iters; k += blockDim.x) {
+    double sum = 0.0;
+    for (int j = 0; j < ngroups_block; ++j) sum += err_lds[k * ngroups_block + j];
+    a.partials[(int64_t)k * a.nblocks + blockIdx.x] = sum;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// axis = 1: group j = 64-bit-aligned run of g consecutive weights.  Block = 4 waves.
+// ------------------------------------------------------------------------------------------
+template <int NBITS, int G, bool FIX>
+__global__ void __launch_bounds__(256) k_quant_ax1(const SolveArgs a) {
+  using S = Shape<G>;
+  constexpr int E = S::E, L = S::L, GPW = S::GPW;
+  constexpr int GPB = 4 * GPW;
+  extern __shared__ double err_lds[];  // [iters][GPB]
+  int kmax = a.iters;
+  if (FIX) {
+    kmax = a.ctrl[0];
+    if (kmax >= a.iters) return;  // the loop ran to the end: the solve pass wrote the result
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / L, slot = lane % L;
+  const int gblock = wave * GPW + sub;
+  const int64_t gidx = (int64_t)blockIdx.x * GPB + gblock;
+  const bool valid = gidx < a.G;
+  const int64_t e0 = (valid ? gidx : 0) * G + slot * E;
+
+  double w[E], ws[E];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.W + e0);
+    if constexpr (E == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(a.W + e0);
+      const unsigned u[2] = {v.x, v.y};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (double)__half2float(__ushort_as_half((unsigned short)(u[e >> 1] >> (16 * (e & 1)))));
+    } else {
+#pragma unroll
+      for (int c = 0; c < E / 8; ++c) {
+        const uint4 v = src[c];
+        const unsigned u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          w[8 * c + e] = (double)__half2float(__ushort_as_half((unsigned short)(u[e >> 1] >> (16 * (e & 1)))));
+      }
+    }
+    if (!valid)
+#pragma unroll
+      for (int e = 0; e < E; ++e) w[e] = 0.0;
+  }
+
+  double s, delta;
+  const double z = solve_group<E, L>(a, w, ws, valid, kmax, err_lds + gblock, GPB, !FIX && slot == 0, s, delta);
+
+  unsigned c[E];
+  final_codes<E>(ws, z, a.qmax, c);
+  if (valid) {
+    if constexpr (NBITS == 4) {
+      if constexpr (E == 4) {
+        reinterpret_cast<unsigned short*>(a.packed)[e0 / 4] =
+            (unsigned short)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12));
+      } else {
+#pragma unroll
+        for (int h = 0; h < E / 8; ++h) {
+          unsigned word = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) word |= c[8 * h + e] << (4 * e);
+          reinterpret_cast<unsigned*>(a.packed)[e0 / 8 + h] = word;
+        }
+      }
+    } else if constexpr (NBITS == 2) {
+      if constexpr (E == 4) {
+        a.packed[e0 / 4] = (uint8_t)(c[0] | (c[1] << 2) | (c[2] << 4) | (c[3] << 6));
+      } else {
+#pragma unroll
+        for (int h = 0; h < E / 8; ++h) {
+          unsigned v = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v |= c[8 * h + e] << (2 * e);
+          reinterpret_cast<unsigned short*>(a.packed)[e0 / 8 + h] = (unsigned short)v;
+        }
+      }
+    } else {  // 3-bit: one byte per code, packed by k_pack3
+      if constexpr (E == 4) {
+        reinterpret_cast<unsigned*>(a.codes_ws + e0)[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      } else {
+#pragma unroll
+        for (int h = 0; h < E / 4; ++h)
+          reinterpret_cast<unsigned*>(a.codes_ws + e0)[h] =
+              c[4 * h] | (c[4 * h + 1] << 8) | (c[4 * h + 2] << 16) | (c[4 * h + 3] << 24);
+      }
+    }
+    if (slot == 0) {
+      store_meta(a.delta, a.meta_dtype, gidx, delta);
+      store_meta(a.zero, a.meta_dtype, gidx, z);
+    }
+  }
+  if (!FIX) write_partials(a, err_lds, GPB);
+}
+
+// ------------------------------------------------------------------------------------------
+// axis = 0: group j = {i*M + j}, a column of the [g, M] view.  A block owns 64 adjacent
+// groups: it loads the g x 64 fp16 tile with 16-byte row loads into LDS, each lane then takes
+// E weights of one group from LDS; the codes go back through LDS for row-wise packed stores.
+// Block = L waves (64*L threads).
+// ------------------------------------------------------------------------------------------
+template <int NBITS, int G, bool FIX>
+__global__ void __launch_bounds__(1024) k_quant_ax0(const SolveArgs a) {
+  using S = Shape<G>;
+  constexpr int E = S::E, L = S::L, GPW = S::GPW;
+  constexpr int TW = 64;          // groups per block
+  constexpr int ROW = TW + 8;     // LDS row stride in halves (16-byte aligned rows)
+  constexpr int NT = 64 * L;      // threads
+  extern __shared__ double smem[];
+  double* err_lds = smem;  // [iters][TW]
+  __half* wt = reinterpret_cast<__half*>(smem + (size_t)a.iters * TW);  // [G][ROW]
+  uint8_t* ct = reinterpret_cast<uint8_t*>(wt);                         // [G][TW] after the loads
+
+  int kmax = a.iters;
+  if (FIX) {
+    kmax = a.ctrl[0];
+    if (kmax >= a.iters) return;
+  }
+  const int64_t M = a.G;
+  const int64_t j0 = (int64_t)blockIdx.x * TW;
+  const int tid = threadIdx.x;
+  for (int task = tid; task < G * 8; task += NT) {
+    const int i = task >> 3, c = task & 7;
+    const int64_t col = j0 + 8 * c;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (col < M) v = *reinterpret_cast<const uint4*>(a.W + (int64_t)i * M + col);
+    *reinterpret_cast<uint4*>(wt + i * ROW + 8 * c) = v;
+  }
+  __syncthreads();
+
+  const int lane = tid & 63, wave = tid >> 6;
+  const int sub = lane / L, slot = lane % L;
+  const int acol = wave * GPW + sub;
+  const int64_t gidx = j0 + acol;
+  const bool valid = gidx < M;
+  double w[E], ws[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) w[e] = (double)__half2float(wt[(slot * E + e) * ROW + acol]);
+  __syncthreads();  // the tile is reused for the codes below
+
+  double s, delta;
+  const double z = solve_group<E, L>(a, w, ws, valid, kmax, err_lds + acol, TW, !FIX && slot == 0, s, delta);
+
+  unsigned c[E];
+  final_codes<E>(ws, z, a.qmax, c);
+#pragma unroll
+  for (int e = 0; e < E; ++e) ct[(slot * E + e) * TW + acol] = (uint8_t)c[e];
+  if (valid && slot == 0) {
+    store_meta(a.delta, a.meta_dtype, gidx, delta);
+    store_meta(a.zero, a.meta_dtype, gidx, z);
+  }
+  __syncthreads();
+  // Rows of 64 codes, 8 codes per task: flat index i*M + j0 + 8c (a multiple of 8).
+  for (int task = tid; task < G * 8; task += NT) {
+    const int i = task >> 3, cc = task & 7;
+    if (j0 + 8 * cc >= M) continue;
+    const uint8_t* cr = ct + i * TW + 8 * cc;
+    const int64_t f = (int64_t)i * M + j0 + 8 * cc;
+    if constexpr (NBITS == 4) {
+      unsigned word = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) word |= (unsigned)cr[e] << (4 * e);
+      reinterpret_cast<unsigned*>(a.packed)[f / 8] = word;
+    } else if constexpr (NBITS == 2) {
+      unsigned v = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v |= (unsigned)cr[e] << (2 * e);
+      reinterpret_cast<unsigned short*>(a.packed)[f / 8] = (unsigned short)v;
+    } else {
+      *reinterpret_cast<uint2*>(a.codes_ws + f) = *reinterpret_cast<const uint2*>(cr);
+    }
+  }
+  if (!FIX) write_partials(a, err_lds, TW);
+}
+
+// ------------------------------------------------------------------------------------------
+// Stop decision ("第二拍"): MAE_k = (sum of the block sums, fixed order) / N; the loop stops
+// at the first k >= 1 with MAE_k not below the best so far and keeps z_(k-1); otherwise it
+// keeps z_iters.  One block of 256 threads.
+// ------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_decide(const double* partials, int64_t nblocks, int iters, double N,
+                                                int32_t* ctrl, int32_t* stop_iter, double* mae_trace) {
+  __shared__ double red[256];
+  __shared__ double mae[HQQ_MAX_ITERS];
+  for (int k = 0; k < iters; ++k) {
+    double sum = 0.0;
+    for (int64_t b = threadIdx.x; b < nblocks; b += 256) sum += partials[(int64_t)k * nblocks + b];
+    red[threadIdx.x] = sum;
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+      if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) mae[k] = red[0] / N;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double best = __builtin_inf();
+    int kout = iters, rounds = iters;
+    for (int k = 0; k < iters; ++k) {
+      if (k >= 1 && !(mae[k] < best)) {
+        kout = k - 1;
+        rounds = k + 1;
+        break;
+      }
+      best = mae[k];
+    }
+    ctrl[0] = kout;
+    ctrl[1] = rounds;
+    if (stop_iter) *stop_iter = kout;
+    if (mae_trace)
+      for (int k = 0; k < iters; ++k) mae_trace[k] = (k < rounds) ? mae[k] : __builtin_nan("");
+  }
+}
+
+// Ten 3-bit codes per 32-bit word, bits 3t, the last word padded with code 0.
+__global__ void __launch_bounds__(256) k_pack3(const uint8_t* codes, int64_t N, uint32_t* out, int64_t nwords) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= nwords) return;
+  uint32_t word = 0;
+  const int64_t base = 10 * j;
+#pragma unroll
+  for (int t = 0; t < 10; ++t)
+    if (base + t < N) word |= (uint32_t)codes[base + t] << (3 * t);
+  out[j] = word;
+}
+
+template <int NBITS, int G>
+hipError_t launch_cfg(const SolveArgs& a, int axis, int64_t nblocks, int threads, size_t lds, hipStream_t st,
+                      bool fix) {
+  if (axis == 1) {
+    if (fix)
+      hipLaunchKernelGGL((k_quant_ax1<NBITS, G, true>), dim3(nblocks), dim3(threads), lds, st, a);
+    else
+      hipLaunchKernelGGL((k_quant_ax1<NBITS, G, false>), dim3(nblocks), dim3(threads), lds, st, a);
+  } else {
+    if (fix)
+      hipLaunchKernelGGL((k_quant_ax0<NBITS, G, true>), dim3(nblocks), dim3(threads), lds, st, a);
+    else
+      hipLaunchKernelGGL((k_quant_ax0<NBITS, G, false>), dim3(nblocks), dim3(threads), lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int NBITS>
+hipError_t launch_bits(const SolveArgs& a, int g, int axis, int64_t nblocks, int threads, size_t lds,
+                       hipStream_t st, bool fix) {
+  switch (g) {
+    case 16: return launch_cfg<NBITS, 16>(a, axis, nblocks, threads, lds, st, fix);
+    case 32: return launch_cfg<NBITS, 32>(a, axis, nblocks, threads, lds, st, fix);
+    case 64: return launch_cfg<NBITS, 64>(a, axis, nblocks, threads, lds, st, fix);
+    case 128: return launch_cfg<NBITS, 128>(a, axis, nblocks, threads, lds, st, fix);
+    case 256: return launch_cfg<NBITS, 256>(a, axis, nblocks, threads, lds, st, fix);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int lanes_per_group(int g) { return g == 16 ? 4 : (g >= 256 ? 16 : g / 8); }
+
+}  // namespace
+
+bool quant_geometry(int64_t G, int g, int axis, int iters, int64_t* nblocks, int* threads, size_t* lds) {
+  if (g != 16 && g != 32 && g != 64 && g != 128 && g != 256) return false;
+  const int L = lanes_per_group(g);
+  const int gpw = 64 / L;
+  if (axis == 1) {
+    const int gpb = 4 * gpw;
+    *nblocks = (G + gpb - 1) / gpb;
+    *threads = 256;
+    *lds = (size_t)iters * gpb * sizeof(double);
+  } else {
+    *nblocks = (G + 63) / 64;
+    *threads = 64 * L;
+    const size_t tile = (size_t)g * (64 + 8) * sizeof(__half);
+    *lds = (size_t)iters * 64 * sizeof(double) + tile;
+  }
+  return *lds <= 64 * 1024;
+}
+
+hipError_t launch_quantize(const SolveArgs& a, int nbits, int g, int axis, size_t lds, int64_t N, double* mae_trace,
+                           int32_t* stop_iter, hipStream_t st) {
+  const int64_t nblocks = a.nblocks;
+  const int threads = axis == 1 ? 256 : 64 * lanes_per_group(g);
+  hipError_t err = hipSuccess;
+  for (int pass = 0; pass < 2 && err == hipSuccess; ++pass) {
+    const bool fix = pass == 1;
+    if (nbits == 4)
+      err = launch_bits<4>(a, g, axis, nblocks, threads, lds, st, fix);
+    else if (nbits == 3)
+      err = launch_bits<3>(a, g, axis, nblocks, threads, lds, st, fix);
+    else
+      err = launch_bits<2>(a, g, axis, nblocks, threads, lds, st, fix);
+    if (err == hipSuccess && pass == 0) {
+      hipLaunchKernelGGL(k_decide, dim3(1), dim3(256), 0, st, a.partials, nblocks, a.iters, (double)N, a.ctrl,
+                         stop_iter, mae_trace);
+      err = hipGetLastError();
+    }
+  }
+  if (err == hipSuccess && nbits == 3) {
+    const int64_t nwords = (N + 9) / 10;
+    hipLaunchKernelGGL(k_pack3, dim3((nwords + 255) / 256), dim3(256), 0, st, a.codes_ws, N,
+                       reinterpret_cast<uint32_t*>(a.packed), nwords);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+}  // namespace hqq
