@@ -1,0 +1,260 @@
+"""Benchmark of the HQQ hot path on one MI355X.
+
+One step = one pass of the whole path over the Llama-7B-shaped layer set (q/k/v/o 4096x4096 and
+three 11008x4096 fp16 weights, N(0, 0.02) with 0.1 % +/-10 sigma outliers):
+  * hqq_quantize of every layer (4-bit, group 64, axis 1, up to 20 rounds, p 0.7, beta 10 x1.01):
+    min-max start, proximal rounds with the whole-tensor early stop, final codes, packing, fp16
+    step and zero;
+  * hqq_dequantize of every layer back to fp16 (the round trip);
+  * hqq_gemv_w4a16 on an 8192x8192 4-bit g64 weight at batch 1 and 8 (GEMV) and 256 (MFMA GEMM).
+Inputs are resident in HBM before the timed region; the GEMV operands rotate over enough
+copies (> 1 GB) that the 256 MB last-level cache cannot hold them.
+
+Prints one JSON line.  `value` is the step's throughput in quantized weights per second
+(all legs inside the step time); the per-leg rates and the roofline of the dominant kernel
+(the quantizer) are reported beside it, with the single-threaded fp64 oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HQQ quantize Gweights/s + dequant-GEMV GB/s (4-bit g64), % of roofline"
+PEAK_HBM = 8.0e12            # B/s
+PEAK_FP16_MFMA = 2.5e15      # FLOP/s dense
+# fp64 VALU: 256 CUs x 64 lanes x 2.4 GHz, one fp64 add/mul/min/max/round per lane per clock
+PEAK_FP64_ALU = 256 * 64 * 2.4e9
+# algorithmic fp64 operations of the method per weight and round:
+# W*s, +z, round, 2 clip, q-z, *delta, W-W_hat, |r| sum, shrink test, W-e, *s, q-(.), sum
+OPS_PER_ROUND = 14
+OPS_FIXED = 6                # min, max, final W*s+z, round, 2 clip
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_only_quantization_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(layer_tensor, q):
+    """The fp64 oracle as it stands, single-threaded on the host, on one 4096x4096 layer."""
+    import numpy as np
+
+    import oracle
+    o = oracle.get()
+    W = layer_tensor.make().astype(np.float64)
+    t0 = time.perf_counter()
+    r = o.quantize(W, nbits=q.nbits, group_size=q.group_size, axis=q.axis, iters=q.iters, p=q.p, beta0=q.beta0,
+                   kappa=q.kappa)
+    dt = time.perf_counter() - t0
+    return {"value": W.size / dt / 1e9, "unit": "Gweights/s", "cores": 1, "kind": "oracle",
+            "sample": "oracle quantize of one %dx%d layer (%s), 4-bit g64 axis=1, %d rounds evaluated, %.1f s"
+                      % (layer_tensor.rows, layer_tensor.cols, layer_tensor.name, r["rounds"], dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import weight_only_quantization_amd as hq
+
+    assert torch.cuda.is_available(), "no GPU"
+    hq.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = synth.WORKLOADS["llama7b_layers"]
+    qp = spec["quant"][0]
+    gspec = synth.WORKLOADS["gemv8192"]
+    gq = gspec["quant"][0]
+
+    # ---------------------------------------------------------------- inputs resident in HBM
+    log("generating inputs")
+    layers = []
+    for t in spec["tensors"]:
+        W = torch.from_numpy(t.make()).to(dev)
+        G = t.rows * t.cols // qp.group_size
+        ws = torch.empty(hq.hqq_quantize_workspace_bytes(t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, qp.iters),
+                         dtype=torch.uint8, device=dev)
+        out = (torch.empty(hq.hqq_packed_bytes(t.rows, t.cols, qp.nbits), dtype=torch.uint8, device=dev),
+               torch.empty(G, dtype=torch.float16, device=dev), torch.empty(G, dtype=torch.float16, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev), torch.empty(qp.iters, dtype=torch.float64, device=dev))
+        What = torch.empty((t.rows, t.cols), dtype=torch.float16, device=dev)
+        layers.append((t, W, ws, out, What))
+    n_weights = sum(t.rows * t.cols for t, *_ in layers)
+
+    gt = gspec["tensors"][0]
+    GN, GK = gt.rows, gt.cols
+    Wg = torch.from_numpy(gt.make()).to(dev)
+    q0 = hq.hqq_quantize(Wg, nbits=gq.nbits, group_size=gq.group_size, axis=gq.axis, iters=gq.iters)
+    gemv_bytes_w = q0.packed.numel() + 4 * q0.delta.numel()
+    ncopy = max(4, int(np.ceil(1.1e9 / gemv_bytes_w)))
+    copies = [(q0.packed.clone(), q0.delta.clone(), q0.zero.clone()) for _ in range(ncopy)]
+    del Wg
+    X = torch.from_numpy(synth.activations(256, GK, gspec["x_seed"])).to(dev)
+    Y = {b: torch.empty((b, GN), dtype=torch.float16, device=dev) for b in (1, 8, 256)}
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        for li, (t, W, ws, out, What) in enumerate(layers):
+            if ev is not None:
+                ev["q"][li][0].record(stream)
+            hq.hqq_quantize(W, nbits=qp.nbits, group_size=qp.group_size, axis=qp.axis, iters=qp.iters, p=qp.p,
+                            beta0=qp.beta0, kappa=qp.kappa, workspace=ws, out=out)
+            if ev is not None:
+                ev["q"][li][1].record(stream)
+        for li, (t, W, ws, out, What) in enumerate(layers):
+            hq.hqq_dequantize(out[0], out[1], out[2], t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=What)
+        for j, b in enumerate((1, 8, 256)):
+            pk, d, z = copies[(3 * i + j) % ncopy]
+            hq.hqq_gemv_w4a16(pk, d, z, GN, GK, gq.group_size, X[:b], out=Y[b])
+
+    # ---------------------------------------------------------------- warmup + timed steps
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = {"q": [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in layers] for _ in range(a.steps)]}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    qtimes = []
+    for i in range(a.steps):
+        evs = {"q": ev["q"][i]}
+        step(i, evs)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = start.elapsed_time(end) / a.steps
+    for i in range(a.steps):
+        qtimes.append([s.elapsed_time(e) for s, e in ev["q"][i]])
+    qtimes = np.array(qtimes)  # [steps, layers] ms per hqq_quantize call
+    q_ms_step = float(qtimes.sum(axis=1).mean())
+
+    stops = [int(out[3].item()) for _, _, _, out, _ in layers]
+    rounds = [min(s + 2, qp.iters) if s < qp.iters else qp.iters for s in stops]
+
+    # ---------------------------------------------------------------- per-leg timing loops
+    def timed(fn, reps):
+        """Mean GPU time of one call: an event pair around every call on the launch stream
+        (host gaps between calls fall outside the pairs)."""
+        fn(0)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for r in range(reps):
+            evs[r][0].record(stream)
+            fn(r)
+            evs[r][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([s.elapsed_time(e) for s, e in evs])) * 1e-3  # s per call
+
+    def dq_all(r):
+        for t, W, ws, out, What in layers:
+            hq.hqq_dequantize(out[0], out[1], out[2], t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=What)
+
+    legs = {}
+    t_dq = timed(dq_all, 10)
+    dq_bytes = sum(t.rows * t.cols * (qp.nbits / 8 + 2) + 4 * t.rows * t.cols / qp.group_size
+                   for t, *_ in layers)
+    legs["dequant"] = {"s_per_layer_set": t_dq, "GB/s": dq_bytes / t_dq / 1e9,
+                       "frac_hbm": dq_bytes / t_dq / PEAK_HBM, "bytes": dq_bytes}
+    for b in (1, 8, 256):
+        def gv(r, b=b):
+            pk, d, z = copies[r % ncopy]
+            hq.hqq_gemv_w4a16(pk, d, z, GN, GK, gq.group_size, X[:b], out=Y[b])
+        tg = timed(gv, 2 * ncopy)
+        byt = GN * GK / 2 + 4 * GN * GK / gq.group_size + 2 * b * GK + 2 * b * GN
+        flops = 2.0 * b * GN * GK
+        legs["gemv_b%d" % b] = {"us": tg * 1e6, "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM,
+                                "TFLOP/s": flops / tg / 1e12, "frac_mfma_f16": flops / tg / PEAK_FP16_MFMA,
+                                "bytes": byt}
+
+    if a.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---------------------------------------------------------------- roofline of the quantizer
+    q_s_per_call = qtimes.mean(axis=0) * 1e-3  # per layer
+    ops = sum((OPS_PER_ROUND * r + OPS_FIXED) * t.rows * t.cols for (t, *_), r in zip(layers, rounds))
+    q_s_total = float(q_s_per_call.sum())
+    achieved = ops / q_s_total
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_sha") == source_digest():
+            traffic = tr.get("bytes_per_layer_set")
+    roof = {"bound": "alu", "achieved": achieved / 1e12, "peak": PEAK_FP64_ALU / 1e12, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP64_ALU, "traffic": traffic,
+            "kernel": "hqq_quantize (solve + stop decision + fix-up), 7 layers",
+            "ops_per_weight": "%d per evaluated round + %d" % (OPS_PER_ROUND, OPS_FIXED),
+            "rounds_evaluated": rounds, "seconds_per_layer_set": q_s_total}
+    alg_bytes_q = sum(t.rows * t.cols * (2 + qp.nbits / 8) + 4 * t.rows * t.cols / qp.group_size
+                      for t, *_ in layers)
+
+    res = {
+        "metric": METRIC,
+        "value": n_weights / (step_ms * 1e-3) / 1e9,
+        "unit": "Gweights/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic (seeded; N(0,0.02) + 0.1% +/-10 sigma outliers; activations N(0,1))",
+        "config": {"workload": "llama7b_layers quantize+pack+dequant (4x4096x4096 + 3x11008x4096, 4-bit g64 "
+                               "axis=1, 20 rounds) + fused W4A16 8192x8192 at batch 1/8/256",
+                   "weights": n_weights, "nbits": qp.nbits, "group_size": qp.group_size, "axis": qp.axis,
+                   "iters": qp.iters, "gemv_copies_rotated": ncopy},
+        "quantize_gweights_per_s": n_weights / q_s_total / 1e9,
+        "quantize_hbm_frac": alg_bytes_q / q_s_total / PEAK_HBM,
+        "stop_index_per_layer": stops,
+        "legs": legs,
+        "roofline": roof,
+        "wall_s": wall,
+    }
+    if not a.no_cpu_baseline:
+        log("timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(spec["tensors"][0], qp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,6 +51,7 @@ def _declare(lib):
         "hqq_oracle_double_to_half": (ctypes.c_uint16, [dbl]),
         "hqq_oracle_doubles_to_halves": (None, [p, i64, p]),
         "hqq_oracle_group_elem": (i64, [i64, i64, i32, i32, i64, i32]),
+        "hqq_oracle_sum": (dbl, [p, i64]),
         "hqq_oracle_init_group": (None, [p, i32, i32, dbl, p, p, p]),
         "hqq_oracle_shrink": (dbl, [dbl, dbl, dbl]),
         "hqq_oracle_round_group": (None, [p, i32, i32, dbl, dbl, dbl, dbl, dbl, p, p, p, p]),
@@ -89,6 +90,10 @@ class Oracle:
         out = np.empty(x.shape, dtype=np.uint16)
         self.lib.hqq_oracle_doubles_to_halves(x.ctypes.data, x.size, out.ctypes.data)
         return out
+
+    def sum(self, v) -> float:
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        return self.lib.hqq_oracle_sum(v.ctypes.data, v.size)
 
     def group_elem(self, rows, cols, g, axis, j, i) -> int:
         return self.lib.hqq_oracle_group_elem(rows, cols, g, axis, j, i)

@@ -22,6 +22,31 @@
 #define PLANT(n) (HQQ_ORACLE_PLANT == (n))
 
 /* ------------------------------------------------------------------------------------------
+ * Summation order.  The pages fix no order for the group mean or for the whole-tensor MAE;
+ * every sum here is the balanced pairwise sum in index order (Higham, "The accuracy of
+ * floating point summation", 1993), over the values zero-padded to the next power of two:
+ * sum(v[lo .. lo+size)) = sum(first half) + sum(second half), a zero-padded half adds 0.
+ * ---------------------------------------------------------------------------------------- */
+
+static double pairwise(const double* v, int64_t lo, int64_t size, int64_t n) {
+  if (lo >= n) return 0.0;
+  if (size == 1) return v[lo];
+  int64_t h = size / 2;
+  return pairwise(v, lo, h, n) + pairwise(v, lo + h, h, n);
+}
+
+double hqq_oracle_sum(const double* v, int64_t n) {
+  int64_t p = 1;
+  while (p < n) p *= 2;
+  if (PLANT(16)) {
+    double s = 0.0;
+    for (int64_t i = 0; i < n; i++) s = s + v[i];
+    return s;
+  }
+  return pairwise(v, 0, p, n);
+}
+
+/* ------------------------------------------------------------------------------------------
  * IEEE binary16 <-> binary64
  * ---------------------------------------------------------------------------------------- */
 
@@ -123,7 +148,7 @@ double hqq_oracle_shrink(double r, double beta, double p) {
 void hqq_oracle_round_group(const double* w, int g, int nbits, double s, double delta, double z, double beta,
                             double p, double* err_sum, double* z_next, double* q_out, double* e_out) {
   double qmax = (double)((1 << nbits) - 1);
-  double err = 0.0, acc = 0.0;
+  double absr[g], term[g];
   for (int i = 0; i < g; i++) {
     double t = w[i] * s;
     t = t + z;
@@ -132,15 +157,15 @@ void hqq_oracle_round_group(const double* w, int g, int nbits, double s, double 
     if (q > qmax && !PLANT(8)) q = qmax;
     double what = (q - z) * delta;
     double r = w[i] - what;
-    err = err + fabs(r);
+    absr[i] = fabs(r);
     double e = hqq_oracle_shrink(r, beta, p);
     double u = PLANT(3) ? w[i] * s : (w[i] - e) * s;
-    acc = acc + (q - u);
+    term[i] = q - u;
     if (q_out) q_out[i] = q;
     if (e_out) e_out[i] = e;
   }
-  *err_sum = err;
-  *z_next = acc / (double)(PLANT(12) ? g - 1 : g);
+  *err_sum = hqq_oracle_sum(absr, g);
+  *z_next = hqq_oracle_sum(term, g) / (double)(PLANT(12) ? g - 1 : g);
 }
 
 /* ------------------------------------------------------------------------------------------
@@ -201,6 +226,12 @@ int hqq_oracle_quantize(const double* W, int64_t rows, int64_t cols, int nbits, 
   for (int64_t j = 0; j < G; j++)
     for (int i = 0; i < g; i++) Wg[j * g + i] = W[hqq_oracle_group_elem(rows, cols, g, axis, j, i)];
 
+  double* gerr = (double*)malloc((size_t)G * sizeof(double));
+  if (!gerr) {
+    free(Wg);
+    free(zbuf);
+    return -2;
+  }
   double* z_prev = zbuf;
   double* z_cur = zbuf + G;
   double* z_next = zbuf + 2 * G;
@@ -210,14 +241,10 @@ int hqq_oracle_quantize(const double* W, int64_t rows, int64_t cols, int nbits, 
   double beta = beta0;
   int kout = iters, rounds = 0, stopped = 0;
   for (int k = 0; k < iters; k++) {
-    double S = 0.0;
-    for (int64_t j = 0; j < G; j++) {
-      double err;
-      hqq_oracle_round_group(Wg + j * g, g, nbits, s_out[j], delta_out[j], z_cur[j], beta, p, &err, &z_next[j],
+    for (int64_t j = 0; j < G; j++)
+      hqq_oracle_round_group(Wg + j * g, g, nbits, s_out[j], delta_out[j], z_cur[j], beta, p, &gerr[j], &z_next[j],
                              NULL, NULL);
-      S = S + err;
-    }
-    double mae = S / (double)N;
+    double mae = hqq_oracle_sum(gerr, G) / (double)N;
     mae_out[k] = mae;
     rounds = k + 1;
     if (hqq_oracle_stop_check(k, mae, best)) {
@@ -251,6 +278,7 @@ int hqq_oracle_quantize(const double* W, int64_t rows, int64_t cols, int nbits, 
   if (kout_out) *kout_out = kout;
   free(Wg);
   free(zbuf);
+  free(gerr);
   return 0;
 }
 

@@ -18,7 +18,8 @@
  * j holds flat elements i*(N/g) + j.  i = 0..g-1 is the in-group order of
  * every sum.  s is "codes per unit" (q = W*s + z), delta = 1/s is the stored
  * step, z is the zero point in code units.  Codes are one byte per weight in
- * flat row-major order.
+ * flat row-major order.  Every sum (group sums, the whole-tensor MAE) is the balanced
+ * pairwise sum in index order, zero-padded to a power of two (hqq_oracle_sum).
  */
 #ifndef HQQ_ORACLE_H
 #define HQQ_ORACLE_H
@@ -31,6 +32,8 @@ extern "C" {
 double hqq_oracle_half_to_double(uint16_t h);
 uint16_t hqq_oracle_double_to_half(double x);
 void hqq_oracle_doubles_to_halves(const double* x, int64_t n, uint16_t* out);
+
+double hqq_oracle_sum(const double* v, int64_t n);
 
 int64_t hqq_oracle_group_elem(int64_t rows, int64_t cols, int g, int axis, int64_t j, int i);
 

@@ -71,8 +71,10 @@ def assert_zero_close(z_gpu, z_ref, what="zero"):
     return float(err.max())
 
 
-def compare_quant(W16, ref, gq, nbits, g, axis, exact_codes=True):
-    """Full comparison of a GPU quantisation with the whole-tensor oracle result."""
+def compare_quant(W16, ref, gq, nbits, g, axis, exact_codes=True, exact=True):
+    """Full comparison of a GPU quantisation with the whole-tensor oracle result.  With
+    `exact`, the MAE trace, zeros and steps must also be bit-identical (both sides use the same
+    summation order; only pow() in an active shrink may differ in its last bit)."""
     o = oracle.get()
     rows, cols = W16.shape
     N = rows * cols
@@ -94,4 +96,8 @@ def compare_quant(W16, ref, gq, nbits, g, axis, exact_codes=True):
     assert np.array_equal(gq["delta"], ref["delta"]) or \
         np.max(np.abs(gq["delta"] - ref["delta"]) / ref["delta"]) <= Z_TOL
     assert_zero_close(gq["zero"], ref["z"])
+    if exact:
+        assert np.array_equal(gq["mae"][:R], ref["mae"]), "MAE trace not bit-identical"
+        assert np.array_equal(gq["zero"], ref["z"]), "zeros not bit-identical"
+        assert np.array_equal(gq["delta"], ref["delta"]), "steps not bit-identical"
     return agree

@@ -59,6 +59,25 @@ def pin_double_to_half_matches_numpy(o):
     assert (got == ref).all(), "double->half differs at %s" % x[got != ref][:5]
 
 
+# ----------------------------------------------------------------------------- summation
+
+def pin_pairwise_sum(o):
+    """Every sum is the balanced pairwise sum in index order (the reading of the unstated
+    order): exact on integers, within the pairwise error bound of the exact sum (math.fsum),
+    and [1, u, u, u] with u = 2^-53 sums to 1 + 2u (a sequential sum would give 1)."""
+    import math
+    u = 2.0 ** -53
+    assert o.sum([1.0, u, u, u]) == 1.0 + 2 * u
+    assert o.sum([]) == 0.0 and o.sum([3.5]) == 3.5
+    r = _rng(2)
+    for n in (1, 2, 3, 7, 64, 100, 1000, 4097):
+        ints = r.integers(-1000, 1000, n).astype(np.float64)
+        assert o.sum(ints) == ints.sum()
+        v = r.normal(0, 1, n)
+        bound = (np.ceil(np.log2(max(n, 2))) + 1) * 2.0 ** -53 * np.abs(v).sum()
+        assert abs(o.sum(v) - math.fsum(v)) <= bound
+
+
 # ----------------------------------------------------------------------------- min-max start
 
 def pin_worked_example(o):

@@ -21,6 +21,7 @@ PLANTS = {
     13: "qmax = 2^b",
     14: "3-bit slots shifted by one bit",
     15: "scale not limited to 2e4",
+    16: "sums accumulated sequentially instead of pairwise",
 }
 
 

@@ -49,7 +49,7 @@ struct QuantLayout {
   int64_t G, nblocks;
   int threads;
   size_t lds;
-  size_t off_partials, off_codes, total;
+  size_t off_partials, off_reduce, off_codes, total;
 };
 
 bool quant_layout(int64_t rows, int64_t cols, int nbits, int g, int axis, int iters, QuantLayout* q) {
@@ -57,7 +57,8 @@ bool quant_layout(int64_t rows, int64_t cols, int nbits, int g, int axis, int it
   if (!hqq::quant_geometry(q->G, g, axis, iters, &q->nblocks, &q->threads, &q->lds)) return false;
   auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
   q->off_partials = 256;
-  q->off_codes = up(q->off_partials + (size_t)iters * q->nblocks * sizeof(double));
+  q->off_reduce = up(q->off_partials + (size_t)iters * q->nblocks * sizeof(double));
+  q->off_codes = up(q->off_reduce + (size_t)iters * hqq::reduce_scratch_entries(q->nblocks, iters) * sizeof(double));
   q->total = q->off_codes + (nbits == 3 ? up((size_t)(rows * cols)) : 0);
   return true;
 }
@@ -145,6 +146,7 @@ int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int 
     a.thr_frozen[k] = m;
   }
   hipError_t e = hqq::launch_quantize(a, nbits, group_size, axis, q.lds, rows * cols, mae_trace_dev, stop_iter_dev,
+                                      reinterpret_cast<double*>(ws + q.off_reduce),
                                       reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "hqq_quantize launch");
   return HQQ_OK;

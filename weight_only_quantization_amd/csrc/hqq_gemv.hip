@@ -32,22 +32,52 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load of packed codes (read once: non-temporal).
+__device__ __forceinline__ uint4 ld_stream16(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 __device__ __forceinline__ f16x2 as_h2(unsigned u) { return __builtin_bit_cast(f16x2, u); }
 __device__ __forceinline__ unsigned as_u(f16x2 h) { return __builtin_bit_cast(unsigned, h); }
 
+// (d & mask) | magic as one v_and_or_b32: the compiler splits it in two when both constants
+// are literals (VOP3 takes no literal here, and at most one scalar operand), so the mask is
+// passed in an SGPR and the magic constant in a VGPR.
+struct Masks {
+  unsigned lo, hi;  // SGPR
+  unsigned magic;   // VGPR
+};
+__device__ __forceinline__ Masks make_masks() {
+  Masks m;
+  asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(m.lo));
+  asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(m.hi));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m.magic));
+  return m;
+}
+__device__ __forceinline__ unsigned and_or(unsigned a, unsigned mask, unsigned magic) {
+  unsigned r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+  return r;
+}
+
 // Eight 4-bit codes -> exact fp16 in the order [c0, c4, 16c1, 16c5, c2, c6, 16c3, 16c7].
-__device__ __forceinline__ void unpack8(unsigned d, f16x2 (&p)[4]) {
+__device__ __forceinline__ f16x8 unpack8(unsigned d, const Masks& mk) {
   const unsigned d8 = d >> 8;
   const f16x2 off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  p[0] = as_h2((d & 0x000F000Fu) | 0x64006400u) + off;
-  p[1] = as_h2((d & 0x00F000F0u) | 0x64006400u) + off;
-  p[2] = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + off;
-  p[3] = as_h2((d8 & 0x00F000F0u) | 0x64006400u) + off;
+  u32x4 r;
+  r[0] = as_u(as_h2(and_or(d, mk.lo, mk.magic)) + off);
+  r[1] = as_u(as_h2(and_or(d, mk.hi, mk.magic)) + off);
+  r[2] = as_u(as_h2(and_or(d8, mk.lo, mk.magic)) + off);
+  r[3] = as_u(as_h2(and_or(d8, mk.hi, mk.magic)) + off);
+  return __builtin_bit_cast(f16x8, r);
 }
 
 __device__ __forceinline__ f16x8 cat(const f16x2 (&p)[4]) {
-  return f16x8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+  const u32x4 r = {as_u(p[0]), as_u(p[1]), as_u(p[2]), as_u(p[3])};
+  return __builtin_bit_cast(f16x8, r);
 }
 
 // Natural order x[0..7] (as 4 dwords of fp16 pairs) -> [x0, x4, x1, x5, x2, x6, x3, x7].
@@ -103,7 +133,8 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
   float* red = sx + B * GPS;                                     // [8][B][16]
   _Float16* xs = reinterpret_cast<_Float16*>(red + 8 * B * 16);  // [B][KS]
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 4, nl = lane & 15;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int64_t n = n0 + nl;
@@ -112,19 +143,36 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
   const __half* drow = delta + n * gpr;
   const __half* zrow = zero + n * gpr;
   const int qh = quarter_of(h);
+  const Masks mk = make_masks();
+  // A-operand row of this lane: batch rows >= B read row 0; they only feed output rows >= B,
+  // which are never stored.
+  const int arow = nl < B ? nl : 0;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int64_t nchunks = K / 128;
+  constexpr int XR = (B * (KS / 8) + 511) / 512;  // 8-element blocks of x staged per thread
   for (int64_t kbase = 0; kbase < K; kbase += KS) {
     const int64_t cbase = kbase / 128;
-    // issue this wave's weight loads for the segment first
+    const int64_t klen = (K - kbase < KS) ? (K - kbase) : KS;
+    const int nb = (int)(klen / 8);
+    // 1. this thread's blocks of x (small, cache-resident) first, so that staging them below
+    //    does not wait for the weight stream
+    uint4 xr[XR];
+#pragma unroll
+    for (int j = 0; j < XR; ++j) {
+      const int idx = tid + 512 * j;
+      const int m = idx / (KS / 8), kb = idx % (KS / 8);
+      xr[j] = make_uint4(0, 0, 0, 0);
+      if (idx < B * (KS / 8) && kb < nb) xr[j] = *reinterpret_cast<const uint4*>(x + m * K + kbase + 8 * kb);
+    }
+    // 2. the wave's weight chunks for the segment (all in flight at once)
     uint4 v[CPW];
     unsigned dm[CPW], zm[CPW];
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int64_t c = cbase + wave + 8 * i;
       if (c < nchunks) {
-        v[i] = *reinterpret_cast<const uint4*>(wrow + c * 64 + h * 16);
+        v[i] = ld_stream16(wrow + c * 64 + h * 16);
         if constexpr (GS == 64) {
           dm[i] = *reinterpret_cast<const unsigned*>(drow + 2 * c);
           zm[i] = *reinterpret_cast<const unsigned*>(zrow + 2 * c);
@@ -134,29 +182,24 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
         }
       }
     }
-    // stage x for the segment: 8-element blocks, operand order, 1/16 on the odd codes
-    const int64_t klen = (K - kbase < KS) ? (K - kbase) : KS;
-    const int nb = (int)(klen / 8);
-    for (int idx = tid; idx < B * (KS / 8); idx += 512) {
-      const int m = idx / (KS / 8), kb = idx % (KS / 8);
-      uint4 o = make_uint4(0, 0, 0, 0);
-      float part = 0.f;
-      if (kb < nb) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(x + m * K + kbase + 8 * kb);
+    // 3. stage x in operand order (1/16 on the odd codes) with the per-group sums of x
+#pragma unroll
+    for (int j = 0; j < XR; ++j) {
+      const int idx = tid + 512 * j;
+      if (idx < B * (KS / 8)) {  // uniform per 256-lane run: segments of GS/8 lanes stay whole
+        const int m = idx / (KS / 8), kb = idx % (KS / 8);
+        const uint4 raw = xr[j];
         const unsigned r4[4] = {raw.x, raw.y, raw.z, raw.w};
+        float part = 0.f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) part += (float)as_h2(r4[t])[0] + (float)as_h2(r4[t])[1];
-        o = perm_slots(raw);
-        const f16x2 sc = {(_Float16)1.0f, (_Float16)0.0625f};
-        // pairs (x0,x4),(x2,x6) keep scale 1; (x1,x5),(x3,x7) get 1/16
+        uint4 o = perm_slots(raw);
         o.y = as_u(as_h2(o.y) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
         o.w = as_u(as_h2(o.w) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
-        (void)sc;
+        *reinterpret_cast<uint4*>(xs + m * KS + 8 * kb) = o;
+        part = seg_sum_f<GS / 8>(part);
+        if ((kb % (GS / 8)) == 0) sx[m * GPS + kb / (GS / 8)] = part;
       }
-      *reinterpret_cast<uint4*>(xs + m * KS + 8 * kb) = o;
-      // group sums of the unscaled x: GS/8 consecutive blocks belong to one group
-      part = seg_sum_f<GS / 8>(part);
-      if ((kb % (GS / 8)) == 0) sx[m * GPS + kb / (GS / 8)] = part;
     }
     __syncthreads();
 
@@ -166,43 +209,40 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
       if (c >= nchunks) break;
       const int cl = (int)(c - cbase);  // chunk within the segment
       if constexpr (GS == 64) {
-        // regroup: lanes 0-31 get the other half's first quarter pair, lanes 32-63 ours
+        // regroup: lane group h then holds quarter pi(h) of both 64-code groups of the chunk
         const auto s0 = __builtin_amdgcn_permlane32_swap(v[i].x, v[i].z, false, false);
         const auto s1 = __builtin_amdgcn_permlane32_swap(v[i].y, v[i].w, false, false);
-        const unsigned grp_d[2][2] = {{s0[0], s1[0]}, {s0[1], s1[1]}};
+        const int kl = cl * 128 + qh * 16;
+        const f16x8 a00 = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl);
+        const f16x8 a01 = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl + 8);
+        const f16x8 a10 = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl + 64);
+        const f16x8 a11 = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl + 72);
+        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+        // the two groups' products interleaved (no back-to-back dependent MFMA)
+        f32x4 P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a00, unpack8(s0[0], mk), zero4, 0, 0, 0);
+        f32x4 P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a10, unpack8(s0[1], mk), zero4, 0, 0, 0);
+        P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a01, unpack8(s1[0], mk), P0, 0, 0, 0);
+        P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a11, unpack8(s1[1], mk), P1, 0, 0, 0);
+        const float dl0 = __half2float(__ushort_as_half((unsigned short)dm[i]));
+        const float dl1 = __half2float(__ushort_as_half((unsigned short)(dm[i] >> 16)));
+        const float zz0 = __half2float(__ushort_as_half((unsigned short)zm[i]));
+        const float zz1 = __half2float(__ushort_as_half((unsigned short)(zm[i] >> 16)));
 #pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {
-          f32x4 P = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            f16x2 p[4];
-            unpack8(grp_d[gg][s], p);
-            const int kl = cl * 128 + gg * 64 + qh * 16 + s * 8;
-            f16x8 A = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (nl < B) A = *reinterpret_cast<const f16x8*>(xs + nl * KS + kl);
-            P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, cat(p), P, 0, 0, 0);
-          }
-          const float dl = __half2float(__ushort_as_half((unsigned short)(dm[i] >> (16 * gg))));
-          const float zz = __half2float(__ushort_as_half((unsigned short)(zm[i] >> (16 * gg))));
-          const int gl = cl * 2 + gg;
-#pragma unroll
-          for (int r = 0; r < (B < 4 ? B : 4); ++r) {
-            const int m = 4 * h + r;
-            const float sxv = (m < B) ? sx[m * GPS + gl] : 0.f;
-            acc[r] = fmaf(dl, fmaf(-zz, sxv, P[r]), acc[r]);
-          }
+        for (int r = 0; r < (B < 4 ? B : 4); ++r) {
+          const int m = 4 * h + r;
+          const float sx0 = (m < B) ? sx[m * GPS + cl * 2] : 0.f;
+          const float sx1 = (m < B) ? sx[m * GPS + cl * 2 + 1] : 0.f;
+          acc[r] = fmaf(dl0, fmaf(-zz0, sx0, P0[r]), acc[r]);
+          acc[r] = fmaf(dl1, fmaf(-zz1, sx1, P1[r]), acc[r]);
         }
       } else {  // GS == 128: the 128-code chunk is one group; lane group h holds codes 32h..32h+31
         const unsigned dd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
         f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          f16x2 p[4];
-          unpack8(dd[s], p);
           const int kl = cl * 128 + h * 32 + s * 8;
-          f16x8 A = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (nl < B) A = *reinterpret_cast<const f16x8*>(xs + nl * KS + kl);
-          P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, cat(p), P, 0, 0, 0);
+          const f16x8 A = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl);
+          P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, unpack8(dd[s], mk), P, 0, 0, 0);
         }
         const float dl = __half2float(__ushort_as_half((unsigned short)dm[i]));
         const float zz = __half2float(__ushort_as_half((unsigned short)zm[i]));
@@ -233,12 +273,26 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
 
 // ------------------------------------------------------------------------------------------
 // GEMM, batch > 8.  Block = 4 waves, tile 128 batch rows x 64 output rows; wave w owns the
-// output rows n0 + 16w .. +15 and all eight 16-row batch tiles.  Per 128-code chunk the block
-// stages x (operand order) in LDS; each wave unpacks and dequantises its own weight rows to
-// fp16 W_hat directly in the B-operand layout.
+// output rows n0 + 16w .. +15 and all eight 16-row batch tiles.  The 128-code chunks of K are
+// software-pipelined: the block's x tile for chunk c+1 is loaded into registers while chunk c
+// is multiplied out of LDS, and each wave's packed weights run one chunk ahead.  Each wave
+// dequantises its own weight rows to fp16 W_hat straight into the B-operand layout, with the
+// codes unpacked in natural k order, so x is staged unchanged.
 // ------------------------------------------------------------------------------------------
 constexpr int kGemmM = 128;
 constexpr int kXRow = 128 + 8;  // LDS row stride (halves) of the x tile
+
+// Eight 4-bit codes -> fp16 pairs (c0,c1), (c2,c3), (c4,c5), (c6,c7), exact.
+__device__ __forceinline__ void unpack8_natural(unsigned d, const Masks& mk, f16x2 (&p)[4]) {
+  const unsigned d4 = d >> 4;  // high nibbles moved to the low nibble of each byte
+  const f16x2 off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  // v_perm_b32: bytes 0-3 of the 64-bit {d4:d} pick d, 4-7 pick d4; byte b of d holds
+  // c(2b) in its low nibble, byte b of d4 holds c(2b+1)
+  p[0] = as_h2(and_or(__builtin_amdgcn_perm(d4, d, 0x0C040C00u), mk.lo, mk.magic)) + off;
+  p[1] = as_h2(and_or(__builtin_amdgcn_perm(d4, d, 0x0C050C01u), mk.lo, mk.magic)) + off;
+  p[2] = as_h2(and_or(__builtin_amdgcn_perm(d4, d, 0x0C060C02u), mk.lo, mk.magic)) + off;
+  p[3] = as_h2(and_or(__builtin_amdgcn_perm(d4, d, 0x0C070C03u), mk.lo, mk.magic)) + off;
+}
 
 template <int GS, int OUT>
 __global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ packed, const __half* __restrict__ delta,
@@ -258,24 +312,36 @@ __global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ packed
   const __half* drow = delta + n * gpr;
   const __half* zrow = zero + n * gpr;
   const int qh = quarter_of(h);
+  const Masks mk = make_masks();
 
   f32x4 acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t nchunks = K / 128;
-  uint4 vnext = *reinterpret_cast<const uint4*>(wrow + h * 16);
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const uint4 v = vnext;
-    if (c + 1 < nchunks) vnext = *reinterpret_cast<const uint4*>(wrow + (c + 1) * 64 + h * 16);
-    // stage x[m0 .. m0+127][128c .. 128c+127]
-    for (int idx = tid; idx < kGemmM * 16; idx += 256) {
-      const int mr = idx >> 4, kb = idx & 15;
-      uint4 o = make_uint4(0, 0, 0, 0);
-      if (m0 + mr < batch) o = perm_slots(*reinterpret_cast<const uint4*>(x + (m0 + mr) * K + c * 128 + 8 * kb));
-      *reinterpret_cast<uint4*>(xt + mr * kXRow + 8 * kb) = o;
+  // x tile staging: thread -> 8 blocks of 8 halves (rows tid/16 + 16j, block tid%16)
+  const int xr_row = tid >> 4, xr_kb = tid & 15;
+  auto load_x = [&](int64_t c, uint4 (&buf)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t mr = m0 + xr_row + 16 * j;
+      buf[j] = make_uint4(0, 0, 0, 0);
+      if (mr < batch) buf[j] = *reinterpret_cast<const uint4*>(x + mr * K + c * 128 + 8 * xr_kb);
     }
-    // weights of this chunk -> fp16 W_hat in operand order, per 64-code group
+  };
+  const int64_t nchunks = K / 128;
+  uint4 xbuf[8];
+  load_x(0, xbuf);
+  uint4 vcur = ld_stream16(wrow + h * 16);
+  for (int64_t c = 0; c < nchunks; ++c) {
+    // publish chunk c's x tile
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(xt + (xr_row + 16 * j) * kXRow + 8 * xr_kb) = xbuf[j];
+    const uint4 v = vcur;
+    if (c + 1 < nchunks) {
+      load_x(c + 1, xbuf);
+      vcur = ld_stream16(wrow + (c + 1) * 64 + h * 16);
+    }
+    // weights of chunk c -> fp16 W_hat in the B-operand layout (natural k order)
     f16x8 Bop[4];
     int kofs[4];
     if constexpr (GS == 64) {
@@ -290,14 +356,10 @@ __global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ packed
         const _Float16 dl = __builtin_bit_cast(_Float16, (unsigned short)(dmw >> (16 * gg)));
         const _Float16 zz = __builtin_bit_cast(_Float16, (unsigned short)(zmw >> (16 * gg)));
         const f16x2 z1 = {zz, zz}, d1 = {dl, dl};
-        const f16x2 z16 = z1 * f16x2{(_Float16)16.0f, (_Float16)16.0f};
-        const f16x2 d16 = d1 * f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
         f16x2 p[4];
-        unpack8(gd[j], p);
-        p[0] = (p[0] - z1) * d1;
-        p[1] = (p[1] - z16) * d16;
-        p[2] = (p[2] - z1) * d1;
-        p[3] = (p[3] - z16) * d16;
+        unpack8_natural(gd[j], mk, p);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p[u] = (p[u] - z1) * d1;
         Bop[j] = cat(p);
         kofs[j] = gg * 64 + qh * 16 + s * 8;
       }
@@ -306,16 +368,12 @@ __global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ packed
       const _Float16 dl = __builtin_bit_cast(_Float16, __half_as_ushort(drow[c]));
       const _Float16 zz = __builtin_bit_cast(_Float16, __half_as_ushort(zrow[c]));
       const f16x2 z1 = {zz, zz}, d1 = {dl, dl};
-      const f16x2 z16 = z1 * f16x2{(_Float16)16.0f, (_Float16)16.0f};
-      const f16x2 d16 = d1 * f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f16x2 p[4];
-        unpack8(dd[j], p);
-        p[0] = (p[0] - z1) * d1;
-        p[1] = (p[1] - z16) * d16;
-        p[2] = (p[2] - z1) * d1;
-        p[3] = (p[3] - z16) * d16;
+        unpack8_natural(dd[j], mk, p);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p[u] = (p[u] - z1) * d1;
         Bop[j] = cat(p);
         kofs[j] = h * 32 + j * 8;
       }

@@ -76,6 +76,17 @@ __device__ __forceinline__ double seg_max(double v) {
   return v;
 }
 
+// Balanced pairwise sum of v[LO .. LO+N) (N a power of two), left half + right half.  With the
+// lane-level DPP tree below this makes every group sum the balanced pairwise sum in index
+// order over the whole group, the summation order fixed for every sum of the method.
+template <int LO, int N, int E>
+__device__ __forceinline__ double tree_sum(const double (&v)[E]) {
+  if constexpr (N == 1)
+    return v[LO];
+  else
+    return tree_sum<LO, N / 2, E>(v) + tree_sum<LO + N / 2, N / 2, E>(v);
+}
+
 // fp64 -> fp16 bits, round to nearest even: round to odd into fp32 (24 >= 11 + 2 bits, so the
 // second rounding is exact), then the hardware fp32 -> fp16 conversion.
 __device__ __forceinline__ unsigned short f64_to_f16_bits(double x) {
@@ -119,7 +130,8 @@ template <int E, int L>
 __device__ __forceinline__ void hqq_round(const double (&w)[E], const double (&ws)[E], double s, double delta,
                                           double z, double qmax, double beta, double pm1, double thr,
                                           double inv_g, double& err_o, double& zn_o, double& maxr_o) {
-  double err = 0.0, acc = 0.0, maxr = 0.0;
+  double ar[E], tm[E];
+  double maxr = 0.0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const double t = ws[e] + z;
@@ -128,14 +140,13 @@ __device__ __forceinline__ void hqq_round(const double (&w)[E], const double (&w
     qq = fmin(qq, qmax);
     const double wh = (qq - z) * delta;
     const double rr = w[e] - wh;
-    err += fabs(rr);
-    maxr = fmax(maxr, fabs(rr));
-    acc += qq - ws[e];  // e = 0: (W - e)*s is W*s
+    ar[e] = fabs(rr);
+    maxr = fmax(maxr, ar[e]);
+    tm[e] = qq - ws[e];  // e = 0: (W - e)*s is W*s
   }
   if (__any(maxr >= thr)) {
-    // Some residual of the wave may pass the shrink: redo the zero sum with the shrink
-    // evaluated wherever it can be non-zero (q and r recomputed identically).
-    acc = 0.0;
+    // Some residual of the wave may pass the shrink: redo the terms with the shrink evaluated
+    // wherever it can be non-zero (q and r recomputed identically).
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const double t = ws[e] + z;
@@ -150,9 +161,11 @@ __device__ __forceinline__ void hqq_round(const double (&w)[E], const double (&w
         const double v = shrink_mag(a, pm1, beta);
         if (v > 0.0) ee = (rr < 0.0) ? -v : v;
       }
-      acc += (ee == 0.0) ? (qq - ws[e]) : (qq - (w[e] - ee) * s);
+      tm[e] = (ee == 0.0) ? (qq - ws[e]) : (qq - (w[e] - ee) * s);
     }
   }
+  const double err = tree_sum<0, E, E>(ar);
+  const double acc = tree_sum<0, E, E>(tm);
   err_o = seg_sum<L>(err);
   zn_o = seg_sum<L>(acc) * inv_g;
   maxr_o = maxr;
@@ -210,34 +223,34 @@ __device__ __forceinline__ void final_codes(const double (&ws)[E], double z, dou
   }
 }
 
-// Sum of the per-group round errors of the block, in a fixed order, to the workspace.
-__device__ __forceinline__ void write_partials(const SolveArgs& a, const double* err_lds, int ngroups_block) {
-  __syncthreads();
-  for (int k = threadIdx.x; k < a.iters; k += blockDim.x) {
-    double sum = 0.0;
-    for (int j = 0; j < ngroups_block; ++j) sum += err_lds[k * ngroups_block + j];
-    a.partials[(int64_t)k * a.nblocks + blockIdx.x] = sum;
+// Sum of the per-group round errors of the block (pairwise, in group order, NG a power of
+// two) to the workspace.
+__device__ __forceinline__ void write_partials(const SolveArgs& a, double* err_lds, int ng, int64_t tile) {
+  for (int st = 1; st < ng; st <<= 1) {
+    __syncthreads();
+    const int pairs = ng / (2 * st);
+    for (int idx = threadIdx.x; idx < a.iters * pairs; idx += blockDim.x) {
+      const int k = idx / pairs, i = idx % pairs;
+      double* row = err_lds + k * ng;
+      row[2 * st * i] = row[2 * st * i] + row[2 * st * i + st];
+    }
   }
+  __syncthreads();
+  for (int k = threadIdx.x; k < a.iters; k += blockDim.x) a.partials[(int64_t)k * a.nblocks + tile] = err_lds[k * ng];
 }
 
 // ------------------------------------------------------------------------------------------
 // axis = 1: group j = 64-bit-aligned run of g consecutive weights.  Block = 4 waves.
 // ------------------------------------------------------------------------------------------
 template <int NBITS, int G, bool FIX>
-__global__ void __launch_bounds__(256) k_quant_ax1(const SolveArgs a) {
+__device__ __forceinline__ void ax1_tile(const SolveArgs& a, int64_t tile, int kmax, double* err_lds) {
   using S = Shape<G>;
   constexpr int E = S::E, L = S::L, GPW = S::GPW;
   constexpr int GPB = 4 * GPW;
-  extern __shared__ double err_lds[];  // [iters][GPB]
-  int kmax = a.iters;
-  if (FIX) {
-    kmax = a.ctrl[0];
-    if (kmax >= a.iters) return;  // the loop ran to the end: the solve pass wrote the result
-  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / L, slot = lane % L;
   const int gblock = wave * GPW + sub;
-  const int64_t gidx = (int64_t)blockIdx.x * GPB + gblock;
+  const int64_t gidx = tile * GPB + gblock;
   const bool valid = gidx < a.G;
   const int64_t e0 = (valid ? gidx : 0) * G + slot * E;
 
@@ -311,7 +324,21 @@ __global__ void __launch_bounds__(256) k_quant_ax1(const SolveArgs a) {
       store_meta(a.zero, a.meta_dtype, gidx, z);
     }
   }
-  if (!FIX) write_partials(a, err_lds, GPB);
+  if (!FIX) write_partials(a, err_lds, GPB, tile);
+}
+
+template <int NBITS, int G, bool FIX>
+__global__ void __launch_bounds__(256) k_quant_ax1(const SolveArgs a) {
+  extern __shared__ double err_lds[];  // [iters][groups per block]
+  int kmax = a.iters;
+  if (FIX) {
+    kmax = a.ctrl[0];
+    if (kmax >= a.iters) return;  // the loop ran to the end: the solve pass wrote the result
+  }
+  for (int64_t tile = blockIdx.x; tile < a.nblocks; tile += gridDim.x) {
+    ax1_tile<NBITS, G, FIX>(a, tile, kmax, err_lds);
+    if (FIX) __syncthreads();
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -321,24 +348,18 @@ __global__ void __launch_bounds__(256) k_quant_ax1(const SolveArgs a) {
 // Block = L waves (64*L threads).
 // ------------------------------------------------------------------------------------------
 template <int NBITS, int G, bool FIX>
-__global__ void __launch_bounds__(1024) k_quant_ax0(const SolveArgs a) {
+__device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int kmax, double* smem) {
   using S = Shape<G>;
   constexpr int E = S::E, L = S::L, GPW = S::GPW;
   constexpr int TW = 64;          // groups per block
   constexpr int ROW = TW + 8;     // LDS row stride in halves (16-byte aligned rows)
   constexpr int NT = 64 * L;      // threads
-  extern __shared__ double smem[];
   double* err_lds = smem;  // [iters][TW]
   __half* wt = reinterpret_cast<__half*>(smem + (size_t)a.iters * TW);  // [G][ROW]
   uint8_t* ct = reinterpret_cast<uint8_t*>(wt);                         // [G][TW] after the loads
 
-  int kmax = a.iters;
-  if (FIX) {
-    kmax = a.ctrl[0];
-    if (kmax >= a.iters) return;
-  }
   const int64_t M = a.G;
-  const int64_t j0 = (int64_t)blockIdx.x * TW;
+  const int64_t j0 = tile * TW;
   const int tid = threadIdx.x;
   for (int task = tid; task < G * 8; task += NT) {
     const int i = task >> 3, c = task & 7;
@@ -391,7 +412,21 @@ __global__ void __launch_bounds__(1024) k_quant_ax0(const SolveArgs a) {
       *reinterpret_cast<uint2*>(a.codes_ws + f) = *reinterpret_cast<const uint2*>(cr);
     }
   }
-  if (!FIX) write_partials(a, err_lds, TW);
+  if (!FIX) write_partials(a, err_lds, TW, tile);
+}
+
+template <int NBITS, int G, bool FIX>
+__global__ void __launch_bounds__(1024) k_quant_ax0(const SolveArgs a) {
+  extern __shared__ double smem[];
+  int kmax = a.iters;
+  if (FIX) {
+    kmax = a.ctrl[0];
+    if (kmax >= a.iters) return;
+  }
+  for (int64_t tile = blockIdx.x; tile < a.nblocks; tile += gridDim.x) {
+    ax0_tile<NBITS, G, FIX>(a, tile, kmax, smem);
+    __syncthreads();
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -399,38 +434,74 @@ __global__ void __launch_bounds__(1024) k_quant_ax0(const SolveArgs a) {
 // at the first k >= 1 with MAE_k not below the best so far and keeps z_(k-1); otherwise it
 // keeps z_iters.  One block of 256 threads.
 // ------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_decide(const double* partials, int64_t nblocks, int iters, double N,
-                                                int32_t* ctrl, int32_t* stop_iter, double* mae_trace) {
-  __shared__ double red[256];
-  __shared__ double mae[HQQ_MAX_ITERS];
-  for (int k = 0; k < iters; ++k) {
-    double sum = 0.0;
-    for (int64_t b = threadIdx.x; b < nblocks; b += 256) sum += partials[(int64_t)k * nblocks + b];
-    red[threadIdx.x] = sum;
+// Block sums of round k are combined as a balanced pairwise tree over the blocks in index
+// order, zero-padded to a power of two.  That tree splits into aligned subtrees of W leaves
+// (W a power of two): k_reduce turns each run of W entries, for every round at once, into one
+// entry, until at most W remain; k_decide forms the last tree, MAE_k = sum / N, and applies
+// the stop rule.  All rounds share each tree level, so a level costs one barrier.
+constexpr int kRedThreads = 1024;
+constexpr int kRedLds = 6144;  // doubles of LDS for the trees (48 KiB)
+
+// Width of the subtrees for `iters` rounds: the largest power of two <= 1024 with
+// iters * W doubles in LDS.
+__host__ __device__ inline int reduce_width(int iters) {
+  int w = 1024;
+  while (w > 1 && (int64_t)w * (iters > 0 ? iters : 1) > kRedLds) w >>= 1;
+  return w;
+}
+
+// red[k * W + i] for k < iters, i < W: pairwise tree over i, in place; result at red[k * W].
+__device__ __forceinline__ void lds_trees(double* red, int iters, int W) {
+  for (int st = 1; st < W; st <<= 1) {
     __syncthreads();
-    for (int st = 128; st > 0; st >>= 1) {
-      if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
-      __syncthreads();
+    const int pairs = W / (2 * st);
+    for (int idx = threadIdx.x; idx < iters * pairs; idx += blockDim.x) {
+      const int k = idx / pairs, j = idx % pairs;
+      red[k * W + 2 * st * j] = red[k * W + 2 * st * j] + red[k * W + 2 * st * j + st];
     }
-    if (threadIdx.x == 0) mae[k] = red[0] / N;
-    __syncthreads();
   }
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(kRedThreads) k_reduce(const double* in, int64_t n_in, double* out, int64_t n_out,
+                                                        int iters) {
+  __shared__ double red[kRedLds];
+  const int W = reduce_width(iters);
+  const int64_t base = (int64_t)blockIdx.x * W;
+  for (int idx = threadIdx.x; idx < iters * W; idx += blockDim.x) {
+    const int k = idx / W, i = idx % W;
+    red[idx] = (base + i < n_in) ? in[(int64_t)k * n_in + base + i] : 0.0;
+  }
+  lds_trees(red, iters, W);
+  for (int k = threadIdx.x; k < iters; k += blockDim.x) out[(int64_t)k * n_out + blockIdx.x] = red[k * W];
+}
+
+__global__ void __launch_bounds__(kRedThreads) k_decide(const double* partials, int64_t n, int iters, double N,
+                                                        int32_t* ctrl, int32_t* stop_iter, double* mae_trace) {
+  __shared__ double red[kRedLds];
+  const int W = reduce_width(iters);
+  for (int idx = threadIdx.x; idx < iters * W; idx += blockDim.x) {
+    const int k = idx / W, i = idx % W;
+    red[idx] = (i < n) ? partials[(int64_t)k * n + i] : 0.0;
+  }
+  lds_trees(red, iters, W);
   if (threadIdx.x == 0) {
     double best = __builtin_inf();
     int kout = iters, rounds = iters;
     for (int k = 0; k < iters; ++k) {
-      if (k >= 1 && !(mae[k] < best)) {
+      const double mae = red[k * W] / N;
+      if (k >= 1 && !(mae < best)) {
         kout = k - 1;
         rounds = k + 1;
         break;
       }
-      best = mae[k];
+      best = mae;
     }
     ctrl[0] = kout;
     ctrl[1] = rounds;
     if (stop_iter) *stop_iter = kout;
     if (mae_trace)
-      for (int k = 0; k < iters; ++k) mae_trace[k] = (k < rounds) ? mae[k] : __builtin_nan("");
+      for (int k = 0; k < iters; ++k) mae_trace[k] = (k < rounds) ? red[k * W] / N : __builtin_nan("");
   }
 }
 
@@ -498,26 +569,48 @@ bool quant_geometry(int64_t G, int g, int axis, int iters, int64_t* nblocks, int
   return *lds <= 64 * 1024;
 }
 
+int64_t reduce_scratch_entries(int64_t nblocks, int iters) {
+  // entries of the intermediate k_reduce levels (per round)
+  const int W = reduce_width(iters);
+  int64_t total = 0, n = nblocks;
+  while (n > W) {
+    n = (n + W - 1) / W;
+    total += n;
+  }
+  return total;
+}
+
 hipError_t launch_quantize(const SolveArgs& a, int nbits, int g, int axis, size_t lds, int64_t N, double* mae_trace,
-                           int32_t* stop_iter, hipStream_t st) {
+                           int32_t* stop_iter, double* reduce_ws, hipStream_t st) {
   const int64_t nblocks = a.nblocks;
   const int threads = axis == 1 ? 256 : 64 * lanes_per_group(g);
   hipError_t err = hipSuccess;
-  for (int pass = 0; pass < 2 && err == hipSuccess; ++pass) {
-    const bool fix = pass == 1;
-    if (nbits == 4)
-      err = launch_bits<4>(a, g, axis, nblocks, threads, lds, st, fix);
-    else if (nbits == 3)
-      err = launch_bits<3>(a, g, axis, nblocks, threads, lds, st, fix);
-    else
-      err = launch_bits<2>(a, g, axis, nblocks, threads, lds, st, fix);
-    if (err == hipSuccess && pass == 0) {
-      hipLaunchKernelGGL(k_decide, dim3(1), dim3(256), 0, st, a.partials, nblocks, a.iters, (double)N, a.ctrl,
-                         stop_iter, mae_trace);
-      err = hipGetLastError();
-    }
+  auto solve = [&](bool fix, int64_t grid) {
+    if (nbits == 4) return launch_bits<4>(a, g, axis, grid, threads, lds, st, fix);
+    if (nbits == 3) return launch_bits<3>(a, g, axis, grid, threads, lds, st, fix);
+    return launch_bits<2>(a, g, axis, grid, threads, lds, st, fix);
+  };
+  err = solve(false, nblocks);
+  if (err != hipSuccess) return err;
+  const double* level = a.partials;
+  int64_t n = nblocks;
+  double* next = reduce_ws;
+  const int W = reduce_width(a.iters);
+  while (n > W) {
+    const int64_t n_out = (n + W - 1) / W;
+    hipLaunchKernelGGL(k_reduce, dim3((unsigned)n_out), dim3(kRedThreads), 0, st, level, n, next, n_out, a.iters);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    level = next;
+    next += n_out * a.iters;
+    n = n_out;
   }
-  if (err == hipSuccess && nbits == 3) {
+  hipLaunchKernelGGL(k_decide, dim3(1), dim3(kRedThreads), 0, st, level, n, a.iters, (double)N, a.ctrl, stop_iter,
+                     mae_trace);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // fix-up pass: a small grid (tiles in a loop), which returns at once when the loop ran to the end
+  err = solve(true, nblocks < 1024 ? nblocks : 1024);
+  if (err != hipSuccess) return err;
+  if (nbits == 3) {
     const int64_t nwords = (N + 9) / 10;
     hipLaunchKernelGGL(k_pack3, dim3((nwords + 255) / 256), dim3(256), 0, st, a.codes_ws, N,
                        reinterpret_cast<uint32_t*>(a.packed), nwords);
