@@ -43,25 +43,13 @@ __device__ __forceinline__ uint4 ld_stream16(const uint8_t* p) {
 __device__ __forceinline__ f16x2 as_h2(unsigned u) { return __builtin_bit_cast(f16x2, u); }
 __device__ __forceinline__ unsigned as_u(f16x2 h) { return __builtin_bit_cast(unsigned, h); }
 
-// (d & mask) | magic as one v_and_or_b32: the compiler splits it in two when both constants
-// are literals (VOP3 takes no literal here, and at most one scalar operand), so the mask is
-// passed in an SGPR and the magic constant in a VGPR.
+// Unpack masks.  Kept as plain constants: ALU inline assembly would hide its register writes
+// from the compiler's hazard tracking (an in-flight MFMA still reads its source VGPRs).
 struct Masks {
-  unsigned lo, hi;  // SGPR
-  unsigned magic;   // VGPR
+  unsigned lo, hi, magic;
 };
-__device__ __forceinline__ Masks make_masks() {
-  Masks m;
-  asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(m.lo));
-  asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(m.hi));
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m.magic));
-  return m;
-}
-__device__ __forceinline__ unsigned and_or(unsigned a, unsigned mask, unsigned magic) {
-  unsigned r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
-  return r;
-}
+__device__ __forceinline__ Masks make_masks() { return Masks{0x000F000Fu, 0x00F000F0u, 0x64006400u}; }
+__device__ __forceinline__ unsigned and_or(unsigned a, unsigned mask, unsigned magic) { return (a & mask) | magic; }
 
 // Eight 4-bit codes -> exact fp16 in the order [c0, c4, 16c1, 16c5, c2, c6, 16c3, 16c7].
 __device__ __forceinline__ f16x8 unpack8(unsigned d, const Masks& mk) {
