@@ -211,6 +211,17 @@ def test_gemv_parity(g, batch):
     check_gemv(packed, d16, z16, N, K, g, x, out_f32=False)
 
 
+@pytest.mark.parametrize("K", [2048, 4224, 8192, 16384])
+@pytest.mark.parametrize("batch", [1, 2, 8])
+def test_gemv_parity_long_rows(K, batch):
+    """Long rows: several chunks per lane in the row-streaming kernel, ragged last chunk set."""
+    say("gemv long rows", K, batch)
+    N = 48
+    packed, d16, z16 = gemv_inputs(N, K, 64, seed=4000 + K)
+    x = synth.activations(batch, K, seed=13)
+    check_gemv(packed, d16, z16, N, K, 64, x, out_f32=True)
+
+
 def test_gemv_onehot_columns():
     """A one-hot activation row returns one column of W_hat (to fp32 rounding)."""
     import weight_only_quantization_amd as hq

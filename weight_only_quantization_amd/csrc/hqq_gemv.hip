@@ -51,15 +51,16 @@ struct Masks {
 __device__ __forceinline__ Masks make_masks() { return Masks{0x000F000Fu, 0x00F000F0u, 0x64006400u}; }
 __device__ __forceinline__ unsigned and_or(unsigned a, unsigned mask, unsigned magic) { return (a & mask) | magic; }
 
-// Eight 4-bit codes -> exact fp16 in the order [c0, c4, 16c1, 16c5, c2, c6, 16c3, 16c7].
-__device__ __forceinline__ f16x8 unpack8(unsigned d, const Masks& mk) {
+// Eight 4-bit codes -> fp16 subnormals in the order [c0, c4, 16c1, 16c5, c2, c6, 16c3, 16c7],
+// each scaled by 2^-24: a masked nibble in the low mantissa bits of a binary16 with a zero
+// exponent field is exactly c * 2^-24 (c * 2^-20 for the high nibble of a byte).  One AND per
+// pair; the dot-product units and the MFMA keep subnormal inputs, products and sums stay in
+// fp32, and the 2^24 is applied once per group.
+constexpr float kSubScale = 16777216.0f;       // 2^24
+constexpr float kSubScaleInv = 5.9604645e-08f;  // 2^-24
+__device__ __forceinline__ f16x8 unpack8_sub(unsigned d) {
   const unsigned d8 = d >> 8;
-  const f16x2 off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  u32x4 r;
-  r[0] = as_u(as_h2(and_or(d, mk.lo, mk.magic)) + off);
-  r[1] = as_u(as_h2(and_or(d, mk.hi, mk.magic)) + off);
-  r[2] = as_u(as_h2(and_or(d8, mk.lo, mk.magic)) + off);
-  r[3] = as_u(as_h2(and_or(d8, mk.hi, mk.magic)) + off);
+  const u32x4 r = {d & 0x000F000Fu, d & 0x00F000F0u, d8 & 0x000F000Fu, d8 & 0x00F000F0u};
   return __builtin_bit_cast(f16x8, r);
 }
 
@@ -131,7 +132,6 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
   const __half* drow = delta + n * gpr;
   const __half* zrow = zero + n * gpr;
   const int qh = quarter_of(h);
-  const Masks mk = make_masks();
   // A-operand row of this lane: batch rows >= B read row 0; they only feed output rows >= B,
   // which are never stored.
   const int arow = nl < B ? nl : 0;
@@ -207,14 +207,15 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
         const f16x8 a11 = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl + 72);
         const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
         // the two groups' products interleaved (no back-to-back dependent MFMA)
-        f32x4 P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a00, unpack8(s0[0], mk), zero4, 0, 0, 0);
-        f32x4 P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a10, unpack8(s0[1], mk), zero4, 0, 0, 0);
-        P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a01, unpack8(s1[0], mk), P0, 0, 0, 0);
-        P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a11, unpack8(s1[1], mk), P1, 0, 0, 0);
-        const float dl0 = __half2float(__ushort_as_half((unsigned short)dm[i]));
-        const float dl1 = __half2float(__ushort_as_half((unsigned short)(dm[i] >> 16)));
-        const float zz0 = __half2float(__ushort_as_half((unsigned short)zm[i]));
-        const float zz1 = __half2float(__ushort_as_half((unsigned short)(zm[i] >> 16)));
+        f32x4 P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a00, unpack8_sub(s0[0]), zero4, 0, 0, 0);
+        f32x4 P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a10, unpack8_sub(s0[1]), zero4, 0, 0, 0);
+        P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a01, unpack8_sub(s1[0]), P0, 0, 0, 0);
+        P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a11, unpack8_sub(s1[1]), P1, 0, 0, 0);
+        // P = 2^-24 sum x q: scale the step up and the zero down by 2^24 (exact)
+        const float dl0 = __half2float(__ushort_as_half((unsigned short)dm[i])) * kSubScale;
+        const float dl1 = __half2float(__ushort_as_half((unsigned short)(dm[i] >> 16))) * kSubScale;
+        const float zz0 = __half2float(__ushort_as_half((unsigned short)zm[i])) * kSubScaleInv;
+        const float zz1 = __half2float(__ushort_as_half((unsigned short)(zm[i] >> 16))) * kSubScaleInv;
 #pragma unroll
         for (int r = 0; r < (B < 4 ? B : 4); ++r) {
           const int m = 4 * h + r;
@@ -230,10 +231,10 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
         for (int s = 0; s < 4; ++s) {
           const int kl = cl * 128 + h * 32 + s * 8;
           const f16x8 A = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl);
-          P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, unpack8(dd[s], mk), P, 0, 0, 0);
+          P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, unpack8_sub(dd[s]), P, 0, 0, 0);
         }
-        const float dl = __half2float(__ushort_as_half((unsigned short)dm[i]));
-        const float zz = __half2float(__ushort_as_half((unsigned short)zm[i]));
+        const float dl = __half2float(__ushort_as_half((unsigned short)dm[i])) * kSubScale;
+        const float zz = __half2float(__ushort_as_half((unsigned short)zm[i])) * kSubScaleInv;
 #pragma unroll
         for (int r = 0; r < (B < 4 ? B : 4); ++r) {
           const int m = 4 * h + r;
@@ -256,6 +257,135 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
 #pragma unroll
     for (int w = 0; w < 8; ++w) sum += red[(w * B + m) * 16 + col];
     store_y<OUT>(y, (int64_t)m * N + n0 + col, sum);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// GEMV on the vector ALUs, batch B <= 2.  Each wave streams whole rows: lane l takes the
+// 32-code chunks c = l + 64 j of a row, so one load instruction reads 1 KB of one row.  The
+// activations are staged once per block in LDS in the unpack order (1/16 on the odd codes),
+// chunk-interleaved so that each read instruction of the wave is contiguous; per chunk the
+// lane forms P = sum x_k q_k with v_dot2_f32_f16 on exact codes and applies the group's step
+// and zero on the fp32 partial, acc += delta * (P - z * sum_k x_k).  Row results are reduced
+// over the wave's lanes with a fixed tree.
+// ------------------------------------------------------------------------------------------
+constexpr int kVRows = 2;  // rows per wave in the VALU GEMV (block: 8 waves, 16 rows)
+
+// Sum over the 64 lanes of a wave (every lane gets the total): DPP inside rows of 16 lanes,
+// then the rows pairwise (lane xor 16, xor 32).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = seg_sum_f<16>(v);
+  v = v + __shfl_xor(v, 16, 64);
+  v = v + __shfl_xor(v, 32, 64);
+  return v;
+}
+
+template <int B, int GS, int OUT, int JMAX>
+__global__ void __launch_bounds__(512) k_gemv_valu(const uint8_t* __restrict__ packed, const __half* __restrict__ delta,
+                                                   const __half* __restrict__ zero, int64_t N, int64_t K,
+                                                   const __half* __restrict__ x, void* __restrict__ y) {
+  extern __shared__ float lds[];
+  const int64_t nch = K / 32;                       // 32-code chunks per row
+  float* sxc = lds;                                  // [B][nch] sum of x over each chunk
+  uint4* xs = reinterpret_cast<uint4*>(sxc + ((B * nch + 3) & ~int64_t(3)));  // [B][4][nch] 16-byte blocks
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t gpr = K / GS;
+
+  // 1. this thread's 16-byte blocks of x first (small, cache-resident), so that staging them
+  //    does not wait behind the weight stream
+  constexpr int XR = (B * 64 * 32 * JMAX / 8 + 511) / 512;  // blocks per thread (K <= 2048 JMAX)
+  const int64_t nxb = B * nch * 4;                           // 16-byte blocks of x
+  uint4 xr[XR];
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const int64_t idx = tid + 512 * (int64_t)i;
+    xr[i] = make_uint4(0, 0, 0, 0);
+    if (idx < nxb) {
+      const int64_t m = idx / (nch * 4), rem = idx % (nch * 4);
+      xr[i] = *reinterpret_cast<const uint4*>(x + m * K + rem * 8);
+    }
+  }
+  // 2. weight rows of this wave, all in flight
+  uint4 wv[kVRows][JMAX];
+  unsigned short dmv[kVRows][JMAX], zmv[kVRows][JMAX];
+#pragma unroll
+  for (int r = 0; r < kVRows; ++r) {
+    const int64_t n = (int64_t)blockIdx.x * 16 + wave + 8 * r;
+    const uint8_t* wrow = packed + n * (K / 2);
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j) {
+      const int64_t c = lane + 64 * j;
+      if (c < nch) {
+        wv[r][j] = ld_stream16(wrow + 16 * c);
+        const int64_t gi = n * gpr + (c * 32) / GS;
+        dmv[r][j] = __half_as_ushort(delta[gi]);
+        zmv[r][j] = __half_as_ushort(zero[gi]);
+      }
+    }
+  }
+  // 3. stage x: 16-byte block t of chunk c of row m at xs[(m * 4 + t) * nch + c], unpack order,
+  //    1/16 on the odd codes; chunk sums of the unscaled x
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const int64_t idx = tid + 512 * (int64_t)i;
+    if (idx < nxb) {  // nxb is a multiple of 4: the 4 lanes of a chunk are active together
+      const int64_t m = idx / (nch * 4), rem = idx % (nch * 4), c = rem / 4, t = rem % 4;
+      const uint4 raw = xr[i];
+      const unsigned r4[4] = {raw.x, raw.y, raw.z, raw.w};
+      float part = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) part += (float)as_h2(r4[q])[0] + (float)as_h2(r4[q])[1];
+      uint4 o = perm_slots(raw);
+      o.y = as_u(as_h2(o.y) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
+      o.w = as_u(as_h2(o.w) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
+      xs[(m * 4 + t) * nch + c] = o;
+      part = seg_sum_f<4>(part);
+      if (t == 0) sxc[m * nch + c] = part;
+    }
+  }
+  __syncthreads();
+
+  // 4. rows
+#pragma unroll
+  for (int r = 0; r < kVRows; ++r) {
+    const int64_t n = (int64_t)blockIdx.x * 16 + wave + 8 * r;
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j) {
+      const int64_t c = lane + 64 * j;
+      if (c < nch) {
+        const unsigned dw[4] = {wv[r][j].x, wv[r][j].y, wv[r][j].z, wv[r][j].w};
+        f16x2 q[4][4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const u32x4 u = __builtin_bit_cast(u32x4, unpack8_sub(dw[t]));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q[t][e] = as_h2(u[e]);
+        }
+        const float dl = __half2float(__ushort_as_half(dmv[r][j])) * kSubScale;
+        const float zz = __half2float(__ushort_as_half(zmv[r][j])) * kSubScaleInv;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          float P = 0.f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint4 xv = xs[(b * 4 + t) * nch + c];
+            const unsigned xu[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) P = __builtin_amdgcn_fdot2(as_h2(xu[e]), q[t][e], P, false);
+          }
+          acc[b] = fmaf(dl, fmaf(-zz, sxc[b * nch + c], P), acc[b]);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float v = wave_sum(acc[b]);
+      if (lane == 0) store_y<OUT>(y, (int64_t)b * N + n, v);
+    }
   }
 }
 
@@ -386,6 +516,29 @@ __global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ packed
     }
 }
 
+template <int B, int GS, int JMAX>
+hipError_t gemv_valu_j(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                       const __half* x, void* y, int y_dtype, hipStream_t st) {
+  const int64_t nch = K / 32;
+  const size_t lds = (size_t)((B * nch + 3) & ~int64_t(3)) * 4 + (size_t)B * K * 2;
+  const dim3 grid((unsigned)(N / 16));
+  if (y_dtype == HQQ_OUT_F16)
+    hipLaunchKernelGGL((k_gemv_valu<B, GS, HQQ_OUT_F16, JMAX>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
+  else
+    hipLaunchKernelGGL((k_gemv_valu<B, GS, HQQ_OUT_F32, JMAX>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
+  return hipGetLastError();
+}
+
+template <int B, int GS>
+hipError_t gemv_valu(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                     const __half* x, void* y, int y_dtype, hipStream_t st) {
+  const int64_t per_lane = (K / 32 + 63) / 64;  // chunks per lane
+  if (per_lane <= 1) return gemv_valu_j<B, GS, 1>(packed, delta, zero, N, K, x, y, y_dtype, st);
+  if (per_lane <= 2) return gemv_valu_j<B, GS, 2>(packed, delta, zero, N, K, x, y, y_dtype, st);
+  if (per_lane <= 4) return gemv_valu_j<B, GS, 4>(packed, delta, zero, N, K, x, y, y_dtype, st);
+  return gemv_valu_j<B, GS, 8>(packed, delta, zero, N, K, x, y, y_dtype, st);
+}
+
 template <int B, int GS>
 hipError_t gemv_b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                   const __half* x, void* y, int y_dtype, hipStream_t st) {
@@ -401,9 +554,14 @@ hipError_t gemv_b(const uint8_t* packed, const __half* delta, const __half* zero
 template <int GS>
 hipError_t gemv_gs(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                    const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t st) {
+  const bool valu = K <= 64 * 32 * 8;
   switch (batch) {
-    case 1: return gemv_b<1, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
-    case 2: return gemv_b<2, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    case 1:
+      return valu ? gemv_valu<1, GS>(packed, delta, zero, N, K, x, y, y_dtype, st)
+                  : gemv_b<1, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    case 2:
+      return valu ? gemv_valu<2, GS>(packed, delta, zero, N, K, x, y, y_dtype, st)
+                  : gemv_b<2, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
     case 3: return gemv_b<3, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
     case 4: return gemv_b<4, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
     case 5: return gemv_b<5, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
