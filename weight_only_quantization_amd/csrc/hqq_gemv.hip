@@ -262,14 +262,23 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
 
 // ------------------------------------------------------------------------------------------
 // GEMV on the vector ALUs, batch B <= 2.  Each wave streams whole rows: lane l takes the
-// 32-code chunks c = l + 64 j of a row, so one load instruction reads 1 KB of one row.  The
-// activations are staged once per block in LDS in the unpack order (1/16 on the odd codes),
-// chunk-interleaved so that each read instruction of the wave is contiguous; per chunk the
-// lane forms P = sum x_k q_k with v_dot2_f32_f16 on exact codes and applies the group's step
-// and zero on the fp32 partial, acc += delta * (P - z * sum_k x_k).  Row results are reduced
-// over the wave's lanes with a fixed tree.
+// 32-code chunks c = l + 64 j of a row, so one load instruction reads 1 KB of one row.  Per
+// chunk the lane forms P = sum x_k q_k with v_dot2_f32_f16 on exact codes and applies the
+// group's step and zero on the fp32 partial, acc += delta * (P - z * sum_k x_k); row results
+// are reduced over the wave's lanes with a fixed tree.
+//
+// Pipelining: wave gw of the grid takes exactly R rows, n = gw + k * (N / R), so at any time
+// the waves of the chip stream one contiguous band of rows.  D rows are in flight per wave:
+// row k + D is requested as soon as row k has been multiplied.  Everything a wave does is
+// straight-line code: loads are unconditional (a chunk index past the row's end is clamped
+// and its contribution selected away), so the compiler's memory-counter waits only ever wait
+// for the row about to be used, never for the whole pipeline.
+//
+// The activations are staged once per block in LDS in the unpack order (1/16 on the odd
+// codes) with the per-chunk sums of x; with XREG the lane then keeps its own chunks of x in
+// registers for all its rows (no LDS traffic in the row loop).
 // ------------------------------------------------------------------------------------------
-constexpr int kVRows = 2;  // rows per wave in the VALU GEMV (block: 8 waves, 16 rows)
+constexpr int kVWaves = 4;  // waves per block of the VALU GEMV
 
 // Sum over the 64 lanes of a wave (every lane gets the total): DPP inside rows of 16 lanes,
 // then the rows pairwise (lane xor 16, xor 32).
@@ -280,111 +289,150 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int B, int GS, int OUT, int JMAX>
-__global__ void __launch_bounds__(512) k_gemv_valu(const uint8_t* __restrict__ packed, const __half* __restrict__ delta,
-                                                   const __half* __restrict__ zero, int64_t N, int64_t K,
-                                                   const __half* __restrict__ x, void* __restrict__ y) {
+// LDS bytes of the VALU GEMV: per-chunk sums of x, then x in 16-byte blocks.
+__host__ __device__ constexpr int64_t valu_lds_bytes(int B, int64_t K) {
+  return ((B * (K / 32) + 3) & ~int64_t(3)) * 4 + (int64_t)B * K * 2;
+}
+
+template <int B, int JMAX, int R>
+__global__ void __launch_bounds__(64 * kVWaves) k_gemv_valu(const uint8_t* __restrict__ packed,
+                                                           const __half* __restrict__ delta,
+                                                           const __half* __restrict__ zero, int64_t N, int64_t K,
+                                                           int gs_log2, int out_dtype, const __half* __restrict__ x,
+                                                           void* __restrict__ y) {
+  constexpr int D = R < 2 ? R : 2;             // rows in flight per wave
+  constexpr bool XREG = B * JMAX <= 4;         // x chunks held in registers
+  constexpr int NT = 64 * kVWaves;
   extern __shared__ float lds[];
-  const int64_t nch = K / 32;                       // 32-code chunks per row
-  float* sxc = lds;                                  // [B][nch] sum of x over each chunk
-  uint4* xs = reinterpret_cast<uint4*>(sxc + ((B * nch + 3) & ~int64_t(3)));  // [B][4][nch] 16-byte blocks
+  const int nch = (int)(K / 32);               // 32-code chunks per row
+  float* sxc = lds;                            // [B][nch] sum of x over each chunk
+  uint4* xs = reinterpret_cast<uint4*>(sxc + ((B * nch + 3) & ~3));  // [B][4][nch] 16-byte blocks
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t gpr = K / GS;
+  const int64_t gpr = K >> gs_log2;            // groups per row
+  const int cshift = gs_log2 - 5;              // chunk -> group within the row
+  const int64_t TW = N / R;                    // waves in the grid
+  const int64_t gw = (int64_t)blockIdx.x * kVWaves + wave;
 
-  // 1. this thread's 16-byte blocks of x first (small, cache-resident), so that staging them
-  //    does not wait behind the weight stream
-  constexpr int XR = (B * 64 * 32 * JMAX / 8 + 511) / 512;  // blocks per thread (K <= 2048 JMAX)
-  const int64_t nxb = B * nch * 4;                           // 16-byte blocks of x
+  // 1. this thread's 16-byte blocks of x (a block past the end re-reads the last one)
+  constexpr int XR = (B * 64 * JMAX * 4 + NT - 1) / NT;
+  const int nxb = B * nch * 4;
   uint4 xr[XR];
 #pragma unroll
   for (int i = 0; i < XR; ++i) {
-    const int64_t idx = tid + 512 * (int64_t)i;
-    xr[i] = make_uint4(0, 0, 0, 0);
-    if (idx < nxb) {
-      const int64_t m = idx / (nch * 4), rem = idx % (nch * 4);
-      xr[i] = *reinterpret_cast<const uint4*>(x + m * K + rem * 8);
-    }
+    const int idx = min(tid + NT * i, nxb - 1);
+    xr[i] = *reinterpret_cast<const uint4*>(x + 8 * idx);  // x is [B][K] contiguous
   }
-  // 2. weight rows of this wave, all in flight
-  uint4 wv[kVRows][JMAX];
-  unsigned short dmv[kVRows][JMAX], zmv[kVRows][JMAX];
-#pragma unroll
-  for (int r = 0; r < kVRows; ++r) {
-    const int64_t n = (int64_t)blockIdx.x * 16 + wave + 8 * r;
+  __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the weight stream
+
+  // 2. the first D rows of this wave, in flight
+  uint4 wv[D][JMAX];
+  unsigned dmv[D][JMAX], zmv[D][JMAX];  // 32 bits each: two loads never share a register
+  auto issue = [&](int s, int64_t n) {
     const uint8_t* wrow = packed + n * (K / 2);
 #pragma unroll
     for (int j = 0; j < JMAX; ++j) {
-      const int64_t c = lane + 64 * j;
-      if (c < nch) {
-        wv[r][j] = ld_stream16(wrow + 16 * c);
-        const int64_t gi = n * gpr + (c * 32) / GS;
-        dmv[r][j] = __half_as_ushort(delta[gi]);
-        zmv[r][j] = __half_as_ushort(zero[gi]);
-      }
+      const int c = min(lane + 64 * j, nch - 1);
+      wv[s][j] = ld_stream16(wrow + 16 * c);
+      const int64_t gi = n * gpr + (c >> cshift);
+      dmv[s][j] = __half_as_ushort(delta[gi]);
+      zmv[s][j] = __half_as_ushort(zero[gi]);
     }
-  }
-  // 3. stage x: 16-byte block t of chunk c of row m at xs[(m * 4 + t) * nch + c], unpack order,
-  //    1/16 on the odd codes; chunk sums of the unscaled x
+  };
+#pragma unroll
+  for (int s = 0; s < D; ++s) issue(s, gw + s * TW);
+
+  // 3. stage x: 16-byte block t of chunk c of batch row m at xs[(m * 4 + t) * nch + c], unpack
+  //    order, 1/16 on the odd codes; chunk sums of the unscaled x.  Clamped indexes rewrite the
+  //    last block with the same value.
 #pragma unroll
   for (int i = 0; i < XR; ++i) {
-    const int64_t idx = tid + 512 * (int64_t)i;
-    if (idx < nxb) {  // nxb is a multiple of 4: the 4 lanes of a chunk are active together
-      const int64_t m = idx / (nch * 4), rem = idx % (nch * 4), c = rem / 4, t = rem % 4;
-      const uint4 raw = xr[i];
-      const unsigned r4[4] = {raw.x, raw.y, raw.z, raw.w};
-      float part = 0.f;
+    const int idx = min(tid + NT * i, nxb - 1);
+    const int m = idx / (nch * 4), rem = idx % (nch * 4), c = rem / 4, t = rem % 4;
+    const uint4 raw = xr[i];
+    const unsigned r4[4] = {raw.x, raw.y, raw.z, raw.w};
+    float part = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) part += (float)as_h2(r4[q])[0] + (float)as_h2(r4[q])[1];
-      uint4 o = perm_slots(raw);
-      o.y = as_u(as_h2(o.y) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
-      o.w = as_u(as_h2(o.w) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
-      xs[(m * 4 + t) * nch + c] = o;
-      part = seg_sum_f<4>(part);
-      if (t == 0) sxc[m * nch + c] = part;
-    }
+    for (int q = 0; q < 4; ++q) part += (float)as_h2(r4[q])[0] + (float)as_h2(r4[q])[1];
+    uint4 o = perm_slots(raw);
+    o.y = as_u(as_h2(o.y) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
+    o.w = as_u(as_h2(o.w) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
+    xs[(m * 4 + t) * nch + c] = o;
+    part = seg_sum_f<4>(part);  // the 4 lanes of a chunk are consecutive and active together
+    if (t == 0) sxc[m * nch + c] = part;
   }
   __syncthreads();
-
-  // 4. rows
+  f16x2 xq[XREG ? B : 1][XREG ? JMAX : 1][16];
+  float sxr[B][JMAX];
 #pragma unroll
-  for (int r = 0; r < kVRows; ++r) {
-    const int64_t n = (int64_t)blockIdx.x * 16 + wave + 8 * r;
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j) {
+      const int c = min(lane + 64 * j, nch - 1);
+      if constexpr (XREG) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint4 v = xs[(b * 4 + t) * nch + c];
+          xq[b][j][4 * t + 0] = as_h2(v.x);
+          xq[b][j][4 * t + 1] = as_h2(v.y);
+          xq[b][j][4 * t + 2] = as_h2(v.z);
+          xq[b][j][4 * t + 3] = as_h2(v.w);
+        }
+      }
+      sxr[b][j] = sxc[b * nch + c];
+    }
+
+  // 4. rows: multiply row k, then request row k + D into the freed slot
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int s = k % D;
+    const int64_t n = gw + k * TW;
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.f;
 #pragma unroll
     for (int j = 0; j < JMAX; ++j) {
-      const int64_t c = lane + 64 * j;
-      if (c < nch) {
-        const unsigned dw[4] = {wv[r][j].x, wv[r][j].y, wv[r][j].z, wv[r][j].w};
-        f16x2 q[4][4];
+      const int c = min(lane + 64 * j, nch - 1);
+      const bool valid = lane + 64 * j < nch;
+      const unsigned dw[4] = {wv[s][j].x, wv[s][j].y, wv[s][j].z, wv[s][j].w};
+      f16x2 q[16];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const u32x4 u = __builtin_bit_cast(u32x4, unpack8_sub(dw[t]));
+      for (int t = 0; t < 4; ++t) {
+        const u32x4 u = __builtin_bit_cast(u32x4, unpack8_sub(dw[t]));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) q[t][e] = as_h2(u[e]);
-        }
-        const float dl = __half2float(__ushort_as_half(dmv[r][j])) * kSubScale;
-        const float zz = __half2float(__ushort_as_half(zmv[r][j])) * kSubScaleInv;
+        for (int e = 0; e < 4; ++e) q[4 * t + e] = as_h2(u[e]);
+      }
+      // codes are 2^-24 * q (subnormal unpack): the step is scaled up and the zero down
+      const float dl = valid ? __half2float(__ushort_as_half((unsigned short)dmv[s][j])) * kSubScale : 0.f;
+      const float zz = __half2float(__ushort_as_half((unsigned short)zmv[s][j])) * kSubScaleInv;
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-          float P = 0.f;
+      for (int b = 0; b < B; ++b) {
+        float P = 0.f;
+        if constexpr (XREG) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) P = __builtin_amdgcn_fdot2(xq[b][j][e], q[e], P, false);
+        } else {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const uint4 xv = xs[(b * 4 + t) * nch + c];
             const unsigned xu[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) P = __builtin_amdgcn_fdot2(as_h2(xu[e]), q[t][e], P, false);
+            for (int e = 0; e < 4; ++e) P = __builtin_amdgcn_fdot2(as_h2(xu[e]), q[4 * t + e], P, false);
           }
-          acc[b] = fmaf(dl, fmaf(-zz, sxc[b * nch + c], P), acc[b]);
         }
+        acc[b] = fmaf(dl, fmaf(-zz, sxr[b][j], P), acc[b]);
       }
     }
+    if (k + D < R) issue(s, gw + (k + D) * TW);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const float v = wave_sum(acc[b]);
-      if (lane == 0) store_y<OUT>(y, (int64_t)b * N + n, v);
+      if (lane == 0) {
+        if (out_dtype == HQQ_OUT_F16)
+          store_y<HQQ_OUT_F16>(y, (int64_t)b * N + n, v);
+        else
+          store_y<HQQ_OUT_F32>(y, (int64_t)b * N + n, v);
+      }
     }
   }
 }
@@ -516,27 +564,42 @@ __global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ packed
     }
 }
 
-template <int B, int GS, int JMAX>
-hipError_t gemv_valu_j(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+// Rows per wave of the VALU GEMV: as many as keep >= 256 blocks (one per compute unit).
+inline int valu_rows_per_wave(int64_t N) {
+  if (N % (8 * kVWaves) == 0 && N / (8 * kVWaves) >= 256) return 8;
+  if (N / (4 * kVWaves) >= 256) return 4;  // N % 16 == 0
+  return 2;
+}
+
+template <int B, int JMAX>
+hipError_t gemv_valu_j(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int gs,
                        const __half* x, void* y, int y_dtype, hipStream_t st) {
-  const int64_t nch = K / 32;
-  const size_t lds = (size_t)((B * nch + 3) & ~int64_t(3)) * 4 + (size_t)B * K * 2;
-  const dim3 grid((unsigned)(N / 16));
-  if (y_dtype == HQQ_OUT_F16)
-    hipLaunchKernelGGL((k_gemv_valu<B, GS, HQQ_OUT_F16, JMAX>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
+  const size_t lds = (size_t)valu_lds_bytes(B, K);
+  const int gl = gs == 64 ? 6 : 7;
+  const int R = valu_rows_per_wave(N);
+  const dim3 grid((unsigned)(N / (R * kVWaves))), block(64 * kVWaves);
+  if (R == 8)
+    hipLaunchKernelGGL((k_gemv_valu<B, JMAX, 8>), grid, block, lds, st, packed, delta, zero, N, K, gl, y_dtype, x, y);
+  else if (R == 4)
+    hipLaunchKernelGGL((k_gemv_valu<B, JMAX, 4>), grid, block, lds, st, packed, delta, zero, N, K, gl, y_dtype, x, y);
   else
-    hipLaunchKernelGGL((k_gemv_valu<B, GS, HQQ_OUT_F32, JMAX>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
+    hipLaunchKernelGGL((k_gemv_valu<B, JMAX, 2>), grid, block, lds, st, packed, delta, zero, N, K, gl, y_dtype, x, y);
   return hipGetLastError();
 }
 
-template <int B, int GS>
-hipError_t gemv_valu(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+template <int B>
+hipError_t gemv_valu(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int gs,
                      const __half* x, void* y, int y_dtype, hipStream_t st) {
   const int64_t per_lane = (K / 32 + 63) / 64;  // chunks per lane
-  if (per_lane <= 1) return gemv_valu_j<B, GS, 1>(packed, delta, zero, N, K, x, y, y_dtype, st);
-  if (per_lane <= 2) return gemv_valu_j<B, GS, 2>(packed, delta, zero, N, K, x, y, y_dtype, st);
-  if (per_lane <= 4) return gemv_valu_j<B, GS, 4>(packed, delta, zero, N, K, x, y, y_dtype, st);
-  return gemv_valu_j<B, GS, 8>(packed, delta, zero, N, K, x, y, y_dtype, st);
+  switch (per_lane) {
+    case 1: return gemv_valu_j<B, 1>(packed, delta, zero, N, K, gs, x, y, y_dtype, st);
+    case 2: return gemv_valu_j<B, 2>(packed, delta, zero, N, K, gs, x, y, y_dtype, st);
+    case 3: return gemv_valu_j<B, 3>(packed, delta, zero, N, K, gs, x, y, y_dtype, st);
+    case 4: return gemv_valu_j<B, 4>(packed, delta, zero, N, K, gs, x, y, y_dtype, st);
+    case 5:
+    case 6: return gemv_valu_j<B, 6>(packed, delta, zero, N, K, gs, x, y, y_dtype, st);
+    default: return gemv_valu_j<B, 8>(packed, delta, zero, N, K, gs, x, y, y_dtype, st);
+  }
 }
 
 template <int B, int GS>
@@ -557,10 +620,10 @@ hipError_t gemv_gs(const uint8_t* packed, const __half* delta, const __half* zer
   const bool valu = K <= 64 * 32 * 8;
   switch (batch) {
     case 1:
-      return valu ? gemv_valu<1, GS>(packed, delta, zero, N, K, x, y, y_dtype, st)
+      return valu ? gemv_valu<1>(packed, delta, zero, N, K, GS, x, y, y_dtype, st)
                   : gemv_b<1, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
     case 2:
-      return valu ? gemv_valu<2, GS>(packed, delta, zero, N, K, x, y, y_dtype, st)
+      return valu ? gemv_valu<2>(packed, delta, zero, N, K, GS, x, y, y_dtype, st)
                   : gemv_b<2, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
     case 3: return gemv_b<3, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
     case 4: return gemv_b<4, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
