@@ -190,7 +190,7 @@ int hqq_gemv_w4a16(const void* packed, const void* delta_fp16, const void* zero_
   const __half* xx = reinterpret_cast<const __half*>(x_fp16);
   hipError_t e;
   if (batch <= 8) {
-    if (hqq::gemv_lds_bytes(K, group_size, batch) > 64 * 1024) return fail(HQQ_ERR_UNSUPPORTED, "LDS too large");
+    if (hqq::gemv_lds_bytes(K, group_size, batch) > 160 * 1024) return fail(HQQ_ERR_UNSUPPORTED, "LDS too large");  // 160 KB per workgroup on gfx950
     e = hqq::launch_gemv(pk, dl, zr, N, K, group_size, xx, batch, y, y_dtype, st);
   } else {
     e = hqq::launch_gemm(pk, dl, zr, N, K, group_size, xx, batch, y, y_dtype, st);

@@ -100,10 +100,12 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
 }
 
 // ------------------------------------------------------------------------------------------
-// GEMV, batch B <= 8.  Block = 8 waves on one 16-row strip; wave w takes the 128-code chunks
-// c = w, w + 8, ... of each K segment.  Per segment the activations are staged in LDS in the
-// operand order (x, with 1/16 on odd codes) together with the per-group sums of x; the eight
-// waves' partial results are added in a fixed order at the end.
+// GEMV, batch B <= 8.  Block = 8 waves on SPB 16-row strips; wave w takes the 128-code chunks
+// c = w, w + 8, ... of each K segment, for every strip of the block.  Per segment the
+// activations are staged in LDS in the operand order (x, with 1/16 on odd codes) together with
+// the per-group sums of x (staged once for all SPB strips); the next segment's loads are in
+// flight while the current one is multiplied.  The eight waves' partial results are added in a
+// fixed order at the end.
 // ------------------------------------------------------------------------------------------
 template <int B>
 struct GemvCfg {
@@ -111,66 +113,78 @@ struct GemvCfg {
   static constexpr int KS = 128 * 8 * CPW;                       // K per segment
 };
 
-template <int B, int GS, int OUT>
+// Sum of the eight fp16 values of a 16-byte block (fp32 accumulation of x * 1).
+__device__ __forceinline__ float block_sum8(const unsigned (&r4)[4]) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  float part = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) part = __builtin_amdgcn_fdot2(as_h2(r4[t]), one, part, false);
+  return part;
+}
+
+template <int B, int GS, int OUT, int SPB>
 __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed, const __half* __restrict__ delta,
                                               const __half* __restrict__ zero, int64_t N, int64_t K,
                                               const __half* __restrict__ x, void* __restrict__ y) {
   constexpr int CPW = GemvCfg<B>::CPW, KS = GemvCfg<B>::KS;
   constexpr int GPS = KS / GS;  // groups per segment
+  constexpr int KSP = KS + 8;   // LDS row stride of x: padded so that rows fall in different banks
   extern __shared__ float lds[];
-  float* sx = lds;                                               // [B][GPS]
-  float* red = sx + B * GPS;                                     // [8][B][16]
-  _Float16* xs = reinterpret_cast<_Float16*>(red + 8 * B * 16);  // [B][KS]
+  float* sx = lds;                                                     // [B][GPS]
+  float* red = sx + B * GPS;                                           // [SPB][8][B][16]
+  _Float16* xs = reinterpret_cast<_Float16*>(red + SPB * 8 * B * 16);  // [B][KSP]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 4, nl = lane & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t n = n0 + nl;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * SPB;
   const int64_t gpr = K / GS;  // groups per row
-  const uint8_t* wrow = packed + n * (K / 2);
-  const __half* drow = delta + n * gpr;
-  const __half* zrow = zero + n * gpr;
   const int qh = quarter_of(h);
   // A-operand row of this lane: batch rows >= B read row 0; they only feed output rows >= B,
   // which are never stored.
   const int arow = nl < B ? nl : 0;
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[SPB];
+#pragma unroll
+  for (int sp = 0; sp < SPB; ++sp) acc[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int64_t nchunks = K / 128;
   constexpr int XR = (B * (KS / 8) + 511) / 512;  // 8-element blocks of x staged per thread
-  for (int64_t kbase = 0; kbase < K; kbase += KS) {
-    const int64_t cbase = kbase / 128;
-    const int64_t klen = (K - kbase < KS) ? (K - kbase) : KS;
-    const int nb = (int)(klen / 8);
-    // 1. this thread's blocks of x (small, cache-resident) first, so that staging them below
-    //    does not wait for the weight stream
-    uint4 xr[XR];
+  // Loads of one segment: this thread's blocks of x (small, cache-resident) first, so that
+  // staging them does not wait for the weight stream, then the wave's weight chunks.  All loads
+  // are unconditional (clamped indexes): a load under a branch makes the compiler wait for it
+  // before the branch joins; blocks and chunks past the end are never staged or never used.
+  uint4 xr[XR];
+  uint4 v[SPB][CPW], vn[SPB][CPW];
+  unsigned dm[SPB][CPW], zm[SPB][CPW], dmn[SPB][CPW], zmn[SPB][CPW];
+  auto load_segment = [&](int64_t kb0, uint4 (&w)[SPB][CPW], unsigned (&d)[SPB][CPW], unsigned (&z)[SPB][CPW]) {
+    const int nbs = (int)(((K - kb0 < KS) ? (K - kb0) : KS) / 8);
 #pragma unroll
     for (int j = 0; j < XR; ++j) {
       const int idx = tid + 512 * j;
-      const int m = idx / (KS / 8), kb = idx % (KS / 8);
-      xr[j] = make_uint4(0, 0, 0, 0);
-      if (idx < B * (KS / 8) && kb < nb) xr[j] = *reinterpret_cast<const uint4*>(x + m * K + kbase + 8 * kb);
+      const int m = min(idx / (KS / 8), B - 1), kb = min(idx % (KS / 8), nbs - 1);
+      xr[j] = *reinterpret_cast<const uint4*>(x + m * K + kb0 + 8 * kb);
     }
-    // 2. the wave's weight chunks for the segment (all in flight at once)
-    uint4 v[CPW];
-    unsigned dm[CPW], zm[CPW];
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int64_t c = cbase + wave + 8 * i;
-      if (c < nchunks) {
-        v[i] = ld_stream16(wrow + c * 64 + h * 16);
+    for (int sp = 0; sp < SPB; ++sp) {
+      const int64_t n = n0 + 16 * sp + nl;
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const int64_t c = min(kb0 / 128 + wave + 8 * i, nchunks - 1);
+        w[sp][i] = ld_stream16(packed + n * (K / 2) + c * 64 + h * 16);
         if constexpr (GS == 64) {
-          dm[i] = *reinterpret_cast<const unsigned*>(drow + 2 * c);
-          zm[i] = *reinterpret_cast<const unsigned*>(zrow + 2 * c);
+          d[sp][i] = *reinterpret_cast<const unsigned*>(delta + n * gpr + 2 * c);
+          z[sp][i] = *reinterpret_cast<const unsigned*>(zero + n * gpr + 2 * c);
         } else {
-          dm[i] = __half_as_ushort(drow[c]);
-          zm[i] = __half_as_ushort(zrow[c]);
+          d[sp][i] = __half_as_ushort(delta[n * gpr + c]);
+          z[sp][i] = __half_as_ushort(zero[n * gpr + c]);
         }
       }
     }
-    // 3. stage x in operand order (1/16 on the odd codes) with the per-group sums of x
+  };
+  load_segment(0, v, dm, zm);
+  for (int64_t kbase = 0; kbase < K; kbase += KS) {
+    const int64_t cbase = kbase / 128;
+    // 1. stage x in operand order (1/16 on the odd codes) with the per-group sums of x
 #pragma unroll
     for (int j = 0; j < XR; ++j) {
       const int idx = tid + 512 * j;
@@ -178,18 +192,19 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
         const int m = idx / (KS / 8), kb = idx % (KS / 8);
         const uint4 raw = xr[j];
         const unsigned r4[4] = {raw.x, raw.y, raw.z, raw.w};
-        float part = 0.f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) part += (float)as_h2(r4[t])[0] + (float)as_h2(r4[t])[1];
+        float part = block_sum8(r4);
         uint4 o = perm_slots(raw);
         o.y = as_u(as_h2(o.y) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
         o.w = as_u(as_h2(o.w) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
-        *reinterpret_cast<uint4*>(xs + m * KS + 8 * kb) = o;
+        *reinterpret_cast<uint4*>(xs + m * KSP + 8 * kb) = o;
         part = seg_sum_f<GS / 8>(part);
         if ((kb % (GS / 8)) == 0) sx[m * GPS + kb / (GS / 8)] = part;
       }
     }
     __syncthreads();
+    // 2. the next segment's loads go out before this one is multiplied
+    const bool more = kbase + KS < K;
+    if (more) load_segment(kbase + KS, vn, dmn, zmn);
 
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
@@ -197,66 +212,89 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
       if (c >= nchunks) break;
       const int cl = (int)(c - cbase);  // chunk within the segment
       if constexpr (GS == 64) {
-        // regroup: lane group h then holds quarter pi(h) of both 64-code groups of the chunk
-        const auto s0 = __builtin_amdgcn_permlane32_swap(v[i].x, v[i].z, false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(v[i].y, v[i].w, false, false);
         const int kl = cl * 128 + qh * 16;
-        const f16x8 a00 = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl);
-        const f16x8 a01 = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl + 8);
-        const f16x8 a10 = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl + 64);
-        const f16x8 a11 = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl + 72);
-        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-        // the two groups' products interleaved (no back-to-back dependent MFMA)
-        f32x4 P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a00, unpack8_sub(s0[0]), zero4, 0, 0, 0);
-        f32x4 P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a10, unpack8_sub(s0[1]), zero4, 0, 0, 0);
-        P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a01, unpack8_sub(s1[0]), P0, 0, 0, 0);
-        P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a11, unpack8_sub(s1[1]), P1, 0, 0, 0);
-        // P = 2^-24 sum x q: scale the step up and the zero down by 2^24 (exact)
-        const float dl0 = __half2float(__ushort_as_half((unsigned short)dm[i])) * kSubScale;
-        const float dl1 = __half2float(__ushort_as_half((unsigned short)(dm[i] >> 16))) * kSubScale;
-        const float zz0 = __half2float(__ushort_as_half((unsigned short)zm[i])) * kSubScaleInv;
-        const float zz1 = __half2float(__ushort_as_half((unsigned short)(zm[i] >> 16))) * kSubScaleInv;
+        const f16x8 a00 = *reinterpret_cast<const f16x8*>(xs + arow * KSP + kl);
+        const f16x8 a01 = *reinterpret_cast<const f16x8*>(xs + arow * KSP + kl + 8);
+        const f16x8 a10 = *reinterpret_cast<const f16x8*>(xs + arow * KSP + kl + 64);
+        const f16x8 a11 = *reinterpret_cast<const f16x8*>(xs + arow * KSP + kl + 72);
+        float sx0[4], sx1[4];
 #pragma unroll
         for (int r = 0; r < (B < 4 ? B : 4); ++r) {
           const int m = 4 * h + r;
-          const float sx0 = (m < B) ? sx[m * GPS + cl * 2] : 0.f;
-          const float sx1 = (m < B) ? sx[m * GPS + cl * 2 + 1] : 0.f;
-          acc[r] = fmaf(dl0, fmaf(-zz0, sx0, P0[r]), acc[r]);
-          acc[r] = fmaf(dl1, fmaf(-zz1, sx1, P1[r]), acc[r]);
+          sx0[r] = (m < B) ? sx[m * GPS + cl * 2] : 0.f;
+          sx1[r] = (m < B) ? sx[m * GPS + cl * 2 + 1] : 0.f;
+        }
+#pragma unroll
+        for (int sp = 0; sp < SPB; ++sp) {
+          // regroup: lane group h then holds quarter pi(h) of both 64-code groups of the chunk
+          const auto s0 = __builtin_amdgcn_permlane32_swap(v[sp][i].x, v[sp][i].z, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(v[sp][i].y, v[sp][i].w, false, false);
+          const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+          // the two groups' products interleaved (no back-to-back dependent MFMA)
+          f32x4 P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a00, unpack8_sub(s0[0]), zero4, 0, 0, 0);
+          f32x4 P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a10, unpack8_sub(s0[1]), zero4, 0, 0, 0);
+          P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a01, unpack8_sub(s1[0]), P0, 0, 0, 0);
+          P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a11, unpack8_sub(s1[1]), P1, 0, 0, 0);
+          // P = 2^-24 sum x q: scale the step up and the zero down by 2^24 (exact)
+          const float dl0 = __half2float(__ushort_as_half((unsigned short)dm[sp][i])) * kSubScale;
+          const float dl1 = __half2float(__ushort_as_half((unsigned short)(dm[sp][i] >> 16))) * kSubScale;
+          const float zz0 = __half2float(__ushort_as_half((unsigned short)zm[sp][i])) * kSubScaleInv;
+          const float zz1 = __half2float(__ushort_as_half((unsigned short)(zm[sp][i] >> 16))) * kSubScaleInv;
+#pragma unroll
+          for (int r = 0; r < (B < 4 ? B : 4); ++r) {
+            acc[sp][r] = fmaf(dl0, fmaf(-zz0, sx0[r], P0[r]), acc[sp][r]);
+            acc[sp][r] = fmaf(dl1, fmaf(-zz1, sx1[r], P1[r]), acc[sp][r]);
+          }
         }
       } else {  // GS == 128: the 128-code chunk is one group; lane group h holds codes 32h..32h+31
-        const unsigned dd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+        f16x8 A[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int kl = cl * 128 + h * 32 + s * 8;
-          const f16x8 A = *reinterpret_cast<const f16x8*>(xs + arow * KS + kl);
-          P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, unpack8_sub(dd[s]), P, 0, 0, 0);
-        }
-        const float dl = __half2float(__ushort_as_half((unsigned short)dm[i])) * kSubScale;
-        const float zz = __half2float(__ushort_as_half((unsigned short)zm[i])) * kSubScaleInv;
+        for (int t = 0; t < 4; ++t) A[t] = *reinterpret_cast<const f16x8*>(xs + arow * KSP + cl * 128 + h * 32 + t * 8);
+        float sxv[4];
 #pragma unroll
         for (int r = 0; r < (B < 4 ? B : 4); ++r) {
           const int m = 4 * h + r;
-          const float sxv = (m < B) ? sx[m * GPS + cl] : 0.f;
-          acc[r] = fmaf(dl, fmaf(-zz, sxv, P[r]), acc[r]);
+          sxv[r] = (m < B) ? sx[m * GPS + cl] : 0.f;
+        }
+#pragma unroll
+        for (int sp = 0; sp < SPB; ++sp) {
+          const unsigned dd[4] = {v[sp][i].x, v[sp][i].y, v[sp][i].z, v[sp][i].w};
+          f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t], unpack8_sub(dd[t]), P, 0, 0, 0);
+          const float dl = __half2float(__ushort_as_half((unsigned short)dm[sp][i])) * kSubScale;
+          const float zz = __half2float(__ushort_as_half((unsigned short)zm[sp][i])) * kSubScaleInv;
+#pragma unroll
+          for (int r = 0; r < (B < 4 ? B : 4); ++r) acc[sp][r] = fmaf(dl, fmaf(-zz, sxv[r], P[r]), acc[sp][r]);
         }
       }
     }
     __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int sp = 0; sp < SPB; ++sp)
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+          v[sp][i] = vn[sp][i];
+          dm[sp][i] = dmn[sp][i];
+          zm[sp][i] = zmn[sp][i];
+        }
+    }
   }
 #pragma unroll
-  for (int r = 0; r < (B < 4 ? B : 4); ++r) {
-    const int m = 4 * h + r;
-    if (m < B) red[(wave * B + m) * 16 + nl] = acc[r];
-  }
+  for (int sp = 0; sp < SPB; ++sp)
+#pragma unroll
+    for (int r = 0; r < (B < 4 ? B : 4); ++r) {
+      const int m = 4 * h + r;
+      if (m < B) red[((sp * 8 + wave) * B + m) * 16 + nl] = acc[sp][r];
+    }
   __syncthreads();
-  if (tid < B * 16) {
-    const int m = tid / 16, col = tid % 16;
+  if (tid < SPB * B * 16) {
+    const int sp = tid / (B * 16), m = (tid / 16) % B, col = tid % 16;
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) sum += red[(w * B + m) * 16 + col];
-    store_y<OUT>(y, (int64_t)m * N + n0 + col, sum);
+    for (int w = 0; w < 8; ++w) sum += red[((sp * 8 + w) * B + m) * 16 + col];
+    store_y<OUT>(y, (int64_t)m * N + n0 + 16 * sp + col, sum);
   }
 }
 
@@ -351,9 +389,7 @@ __global__ void __launch_bounds__(64 * kVWaves) k_gemv_valu(const uint8_t* __res
     const int m = idx / (nch * 4), rem = idx % (nch * 4), c = rem / 4, t = rem % 4;
     const uint4 raw = xr[i];
     const unsigned r4[4] = {raw.x, raw.y, raw.z, raw.w};
-    float part = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) part += (float)as_h2(r4[q])[0] + (float)as_h2(r4[q])[1];
+    float part = block_sum8(r4);
     uint4 o = perm_slots(raw);
     o.y = as_u(as_h2(o.y) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
     o.w = as_u(as_h2(o.w) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
@@ -602,22 +638,42 @@ hipError_t gemv_valu(const uint8_t* packed, const __half* delta, const __half* z
   }
 }
 
+template <int B>
+size_t gemv_lds_b(int gs, int spb) {
+  constexpr int KS = GemvCfg<B>::KS;
+  return (size_t)B * (KS / gs) * 4 + (size_t)spb * 8 * B * 16 * 4 + (size_t)B * (KS + 8) * 2;
+}
+
+// Strips per block of the batched GEMV: two when that still leaves >= 256 blocks.
+inline int gemv_strips_per_block(int64_t N) { return (N % 32 == 0 && N / 32 >= 256) ? 2 : 1; }
+
 template <int B, int GS>
 hipError_t gemv_b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                   const __half* x, void* y, int y_dtype, hipStream_t st) {
-  const size_t lds = gemv_lds_bytes(K, GS, B);
-  const dim3 grid((unsigned)(N / 16));
-  if (y_dtype == HQQ_OUT_F16)
-    hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F16>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
-  else
-    hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F32>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
+  const int spb = gemv_strips_per_block(N);
+  const size_t lds = gemv_lds_b<B>(GS, spb);
+  const dim3 grid((unsigned)(N / (16 * spb)));
+  if (spb == 2) {
+    if (y_dtype == HQQ_OUT_F16)
+      hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F16, 2>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
+    else
+      hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F32, 2>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
+  } else {
+    if (y_dtype == HQQ_OUT_F16)
+      hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F16, 1>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
+    else
+      hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F32, 1>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
+  }
   return hipGetLastError();
 }
+
+// Batch 1-2 with rows of at most 16384 codes run on the vector ALUs.
+inline bool gemv_uses_valu(int64_t K, int64_t batch) { return batch <= 2 && K <= 64 * 32 * 8; }
 
 template <int GS>
 hipError_t gemv_gs(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                    const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t st) {
-  const bool valu = K <= 64 * 32 * 8;
+  const bool valu = gemv_uses_valu(K, batch);
   switch (batch) {
     case 1:
       return valu ? gemv_valu<1>(packed, delta, zero, N, K, GS, x, y, y_dtype, st)
@@ -635,25 +691,19 @@ hipError_t gemv_gs(const uint8_t* packed, const __half* delta, const __half* zer
   }
 }
 
-template <int B>
-size_t gemv_lds_b(int64_t K, int gs) {
-  (void)K;
-  constexpr int KS = GemvCfg<B>::KS;
-  return (size_t)B * (KS / gs) * 4 + (size_t)8 * B * 16 * 4 + (size_t)B * KS * 2;
-}
-
 }  // namespace
 
 size_t gemv_lds_bytes(int64_t K, int gs, int64_t batch) {
-  switch (batch) {
-    case 1: return gemv_lds_b<1>(K, gs);
-    case 2: return gemv_lds_b<2>(K, gs);
-    case 3: return gemv_lds_b<3>(K, gs);
-    case 4: return gemv_lds_b<4>(K, gs);
-    case 5: return gemv_lds_b<5>(K, gs);
-    case 6: return gemv_lds_b<6>(K, gs);
-    case 7: return gemv_lds_b<7>(K, gs);
-    case 8: return gemv_lds_b<8>(K, gs);
+  if (gemv_uses_valu(K, batch)) return (size_t)valu_lds_bytes((int)batch, K);
+  switch (batch) {  // the larger of the one- and two-strip layouts
+    case 1: return gemv_lds_b<1>(gs, 2);
+    case 2: return gemv_lds_b<2>(gs, 2);
+    case 3: return gemv_lds_b<3>(gs, 2);
+    case 4: return gemv_lds_b<4>(gs, 2);
+    case 5: return gemv_lds_b<5>(gs, 2);
+    case 6: return gemv_lds_b<6>(gs, 2);
+    case 7: return gemv_lds_b<7>(gs, 2);
+    case 8: return gemv_lds_b<8>(gs, 2);
     default: return 0;
   }
 }
