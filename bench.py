@@ -29,12 +29,15 @@ sys.path.insert(0, ROOT)
 METRIC = "HQQ quantize Gweights/s + dequant-GEMV GB/s (4-bit g64), % of roofline"
 PEAK_HBM = 8.0e12            # B/s
 PEAK_FP16_MFMA = 2.5e15      # FLOP/s dense
-# fp64 VALU: 256 CUs x 64 lanes x 2.4 GHz, one fp64 add/mul/min/max/round per lane per clock
-PEAK_FP64_ALU = 256 * 64 * 2.4e9
-# algorithmic fp64 operations of the method per weight and round:
-# W*s, +z, round, 2 clip, q-z, *delta, W-W_hat, |r| sum, shrink test, W-e, *s, q-(.), sum
-OPS_PER_ROUND = 14
-OPS_FIXED = 6                # min, max, final W*s+z, round, 2 clip
+# fp64 vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 3.93e13 lane-operations/s
+# (one fp64 add/mul/min/max/round per lane per clock; 78.6 TFLOP/s counts an FMA as two)
+PEAK_FP64_ALU = 256 * 4 * 16 * 2.4e9
+# algorithmic operations per weight: c per evaluated round + a fixed part.  c = 6 is the
+# minimum a round needs when the shrink is exactly zero (the case on these inputs):
+# t = W*s + z, round, clip, t - q, accumulate |.|, accumulate q - W*s; fixed = min, max,
+# W*s, final t, round, two clip compares, pack (8).
+OPS_PER_ROUND = 6
+OPS_FIXED = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_traffic.json")
 
 

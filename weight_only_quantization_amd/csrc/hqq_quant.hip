@@ -236,14 +236,27 @@ __device__ __forceinline__ void write_partials(const SolveArgs& a, double* err_l
     }
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < a.iters; k += blockDim.x) a.partials[(int64_t)k * a.nblocks + tile] = err_lds[k * ng];
+  // block-major [nblocks][iters]: one contiguous run per block
+  for (int k = threadIdx.x; k < a.iters; k += blockDim.x) a.partials[tile * a.iters + k] = err_lds[k * ng];
+}
+
+// The block's step and zero, staged in LDS by one lane per group, go out as one contiguous
+// run per array (small scattered stores would each cost a whole memory burst).
+__device__ __forceinline__ void store_block_meta(const SolveArgs& a, const double* meta_lds, int ng, int64_t g0) {
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 2 * ng) {
+    const int i = t < ng ? t : t - ng;
+    if (g0 + i < a.G) store_meta(t < ng ? a.delta : a.zero, a.meta_dtype, g0 + i, meta_lds[t]);
+  }
 }
 
 // ------------------------------------------------------------------------------------------
 // axis = 1: group j = 64-bit-aligned run of g consecutive weights.  Block = 4 waves.
 // ------------------------------------------------------------------------------------------
 template <int NBITS, int G, bool FIX>
-__device__ __forceinline__ void ax1_tile(const SolveArgs& a, int64_t tile, int kmax, double* err_lds) {
+__device__ __forceinline__ void ax1_tile(const SolveArgs& a, int64_t tile, int kmax, double* err_lds,
+                                         double* meta_lds) {
   using S = Shape<G>;
   constexpr int E = S::E, L = S::L, GPW = S::GPW;
   constexpr int GPB = 4 * GPW;
@@ -320,23 +333,26 @@ __device__ __forceinline__ void ax1_tile(const SolveArgs& a, int64_t tile, int k
       }
     }
     if (slot == 0) {
-      store_meta(a.delta, a.meta_dtype, gidx, delta);
-      store_meta(a.zero, a.meta_dtype, gidx, z);
+      meta_lds[gblock] = delta;
+      meta_lds[GPB + gblock] = z;
     }
   }
+  store_block_meta(a, meta_lds, GPB, tile * GPB);
   if (!FIX) write_partials(a, err_lds, GPB, tile);
 }
 
 template <int NBITS, int G, bool FIX>
 __global__ void __launch_bounds__(256) k_quant_ax1(const SolveArgs a) {
-  extern __shared__ double err_lds[];  // [iters][groups per block]
+  extern __shared__ double err_lds[];  // [iters][groups per block], then [2][groups per block]
+  constexpr int GPB = 4 * Shape<G>::GPW;
+  double* meta_lds = err_lds + a.iters * GPB;
   int kmax = a.iters;
   if (FIX) {
     kmax = a.ctrl[0];
     if (kmax >= a.iters) return;  // the loop ran to the end: the solve pass wrote the result
   }
   for (int64_t tile = blockIdx.x; tile < a.nblocks; tile += gridDim.x) {
-    ax1_tile<NBITS, G, FIX>(a, tile, kmax, err_lds);
+    ax1_tile<NBITS, G, FIX>(a, tile, kmax, err_lds, meta_lds);
     if (FIX) __syncthreads();
   }
 }
@@ -354,8 +370,9 @@ __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int k
   constexpr int TW = 64;          // groups per block
   constexpr int ROW = TW + 8;     // LDS row stride in halves (16-byte aligned rows)
   constexpr int NT = 64 * L;      // threads
-  double* err_lds = smem;  // [iters][TW]
-  __half* wt = reinterpret_cast<__half*>(smem + (size_t)a.iters * TW);  // [G][ROW]
+  double* meta_lds = smem;  // [2][TW]
+  double* err_lds = smem + 2 * TW;  // [iters][TW]
+  __half* wt = reinterpret_cast<__half*>(err_lds + (size_t)a.iters * TW);  // [G][ROW]
   uint8_t* ct = reinterpret_cast<uint8_t*>(wt);                         // [G][TW] after the loads
 
   const int64_t M = a.G;
@@ -388,10 +405,10 @@ __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int k
 #pragma unroll
   for (int e = 0; e < E; ++e) ct[(slot * E + e) * TW + acol] = (uint8_t)c[e];
   if (valid && slot == 0) {
-    store_meta(a.delta, a.meta_dtype, gidx, delta);
-    store_meta(a.zero, a.meta_dtype, gidx, z);
+    meta_lds[acol] = delta;
+    meta_lds[TW + acol] = z;
   }
-  __syncthreads();
+  store_block_meta(a, meta_lds, TW, j0);  // its barrier also publishes the code tile
   // Rows of 64 codes, 8 codes per task: flat index i*M + j0 + 8c (a multiple of 8).
   for (int task = tid; task < G * 8; task += NT) {
     const int i = task >> 3, cc = task & 7;
@@ -463,27 +480,40 @@ __device__ __forceinline__ void lds_trees(double* red, int iters, int W) {
   __syncthreads();
 }
 
+// Entry i of round k of a level: block-major [n][iters] for the solver's per-block sums,
+// round-major [iters][n] for the intermediate levels.  Loads run along memory either way.
+__device__ __forceinline__ void load_level(double* red, const double* in, int64_t n_in, int64_t base, int iters,
+                                           int W, bool block_major) {
+  for (int idx = threadIdx.x; idx < iters * W; idx += blockDim.x) {
+    int k, i;
+    if (block_major) {
+      i = idx / iters;
+      k = idx % iters;
+    } else {
+      k = idx / W;
+      i = idx % W;
+    }
+    const int64_t e = block_major ? (base + i) * iters + k : (int64_t)k * n_in + base + i;
+    red[k * W + i] = (base + i < n_in) ? in[e] : 0.0;
+  }
+}
+
 __global__ void __launch_bounds__(kRedThreads) k_reduce(const double* in, int64_t n_in, double* out, int64_t n_out,
-                                                        int iters) {
+                                                        int iters, int block_major) {
   __shared__ double red[kRedLds];
   const int W = reduce_width(iters);
   const int64_t base = (int64_t)blockIdx.x * W;
-  for (int idx = threadIdx.x; idx < iters * W; idx += blockDim.x) {
-    const int k = idx / W, i = idx % W;
-    red[idx] = (base + i < n_in) ? in[(int64_t)k * n_in + base + i] : 0.0;
-  }
+  load_level(red, in, n_in, base, iters, W, block_major != 0);
   lds_trees(red, iters, W);
   for (int k = threadIdx.x; k < iters; k += blockDim.x) out[(int64_t)k * n_out + blockIdx.x] = red[k * W];
 }
 
 __global__ void __launch_bounds__(kRedThreads) k_decide(const double* partials, int64_t n, int iters, double N,
-                                                        int32_t* ctrl, int32_t* stop_iter, double* mae_trace) {
+                                                        int block_major, int32_t* ctrl, int32_t* stop_iter,
+                                                        double* mae_trace) {
   __shared__ double red[kRedLds];
   const int W = reduce_width(iters);
-  for (int idx = threadIdx.x; idx < iters * W; idx += blockDim.x) {
-    const int k = idx / W, i = idx % W;
-    red[idx] = (i < n) ? partials[(int64_t)k * n + i] : 0.0;
-  }
+  load_level(red, partials, n, 0, iters, W, block_major != 0);
   lds_trees(red, iters, W);
   if (threadIdx.x == 0) {
     double best = __builtin_inf();
@@ -559,12 +589,12 @@ bool quant_geometry(int64_t G, int g, int axis, int iters, int64_t* nblocks, int
     const int gpb = 4 * gpw;
     *nblocks = (G + gpb - 1) / gpb;
     *threads = 256;
-    *lds = (size_t)iters * gpb * sizeof(double);
+    *lds = (size_t)(iters + 2) * gpb * sizeof(double);
   } else {
     *nblocks = (G + 63) / 64;
     *threads = 64 * L;
     const size_t tile = (size_t)g * (64 + 8) * sizeof(__half);
-    *lds = (size_t)iters * 64 * sizeof(double) + tile;
+    *lds = (size_t)(iters + 2) * 64 * sizeof(double) + tile;
   }
   return *lds <= 64 * 1024;
 }
@@ -596,16 +626,19 @@ hipError_t launch_quantize(const SolveArgs& a, int nbits, int g, int axis, size_
   int64_t n = nblocks;
   double* next = reduce_ws;
   const int W = reduce_width(a.iters);
+  int block_major = 1;  // the solver's per-block sums; later levels are round-major
   while (n > W) {
     const int64_t n_out = (n + W - 1) / W;
-    hipLaunchKernelGGL(k_reduce, dim3((unsigned)n_out), dim3(kRedThreads), 0, st, level, n, next, n_out, a.iters);
+    hipLaunchKernelGGL(k_reduce, dim3((unsigned)n_out), dim3(kRedThreads), 0, st, level, n, next, n_out, a.iters,
+                       block_major);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     level = next;
     next += n_out * a.iters;
     n = n_out;
+    block_major = 0;
   }
-  hipLaunchKernelGGL(k_decide, dim3(1), dim3(kRedThreads), 0, st, level, n, a.iters, (double)N, a.ctrl, stop_iter,
-                     mae_trace);
+  hipLaunchKernelGGL(k_decide, dim3(1), dim3(kRedThreads), 0, st, level, n, a.iters, (double)N, block_major, a.ctrl,
+                     stop_iter, mae_trace);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // fix-up pass: a small grid (tiles in a loop), which returns at once when the loop ran to the end
   err = solve(true, nblocks < 1024 ? nblocks : 1024);
