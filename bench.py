@@ -45,10 +45,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+QUANT_SOURCES = ("hqq_quant.hip", "hqq_internal.h")  # the quantizer kernels and their arguments
+
+
 def source_digest() -> str:
+    """Digest of the quantizer's kernel sources: stored counter readings apply only to them."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "weight_only_quantization_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in QUANT_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()

@@ -81,8 +81,8 @@ extern "C" {
 #define HQQ_OUT_F16 0
 #define HQQ_OUT_F32 1
 
-/* Range max-min at or below which s = 1 ("第一拍": the page says "when the
- * denominator is too small" without a number; this library uses 1e-4). */
+/* Range max-min at or below which s = 1 ("第一拍" sets s = 1 for a tiny range but
+ * gives no threshold; this library uses 1e-4). */
 #define HQQ_TINY_RANGE 1e-4
 /* s is limited to at most this value ("第一拍"). */
 #define HQQ_MAX_SCALE 2.0e4

@@ -20,6 +20,17 @@
  * step, z is the zero point in code units.  Codes are one byte per weight in
  * flat row-major order.  Every sum (group sums, the whole-tensor MAE) is the balanced
  * pairwise sum in index order, zero-padded to a power of two (hqq_oracle_sum).
+ *
+ * Pins (tests/oracle_pins.py, each a fact fixed by the page or by the mathematics):
+ * the worked example [-0.8, 0.7] (s0 = 10, z0 = 8, codes 0/8/15) through init, the
+ * rounds and the solver; min-max RTN at iters = 0 with the Delta/2 error bound; ties to
+ * even; degenerate groups; the zero update as the least-squares minimiser (brute force);
+ * L2 monotonicity without the shrink; pack/unpack exhaustively and the 4.5 bpw size;
+ * dequantisation and the GEMV through one-hot and linearity checks; binary16
+ * conversions exhaustively against numpy.  Parity unpinned (readings, no value on the
+ * page to check against): the shrink formula itself, the stop rule's rollback target
+ * and tie handling, the summation order, and the solver's values on the full-size
+ * synthetic tensors.
  */
 #ifndef HQQ_ORACLE_H
 #define HQQ_ORACLE_H
