@@ -482,6 +482,7 @@ __global__ void __launch_bounds__(64 * kVWaves) k_gemv_valu(const uint8_t* __res
 // codes unpacked in natural k order, so x is staged unchanged.
 // ------------------------------------------------------------------------------------------
 constexpr int kGemmM = 128;
+constexpr int kGemmDepth = 4;  // chunks of 128 codes in flight per wave
 constexpr int kXRow = 128 + 8;  // LDS row stride (halves) of the x tile
 
 // Eight 4-bit codes -> fp16 pairs (c0,c1), (c2,c3), (c4,c5), (c6,c7), exact.
@@ -520,76 +521,102 @@ __global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ packed
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // x tile staging: thread -> 8 blocks of 8 halves (rows tid/16 + 16j, block tid%16)
+  // x tile staging: thread -> 8 blocks of 8 halves (rows tid/16 + 16j, block tid%16).  Batch
+  // rows past the end read the last row (unconditional loads: a load under a branch makes the
+  // compiler wait for it at the join); their outputs are never stored.
   const int xr_row = tid >> 4, xr_kb = tid & 15;
-  auto load_x = [&](int64_t c, uint4 (&buf)[8]) {
+  const __half* xrow[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t mr = m0 + xr_row + 16 * j;
-      buf[j] = make_uint4(0, 0, 0, 0);
-      if (mr < batch) buf[j] = *reinterpret_cast<const uint4*>(x + mr * K + c * 128 + 8 * xr_kb);
+  for (int j = 0; j < 8; ++j) xrow[j] = x + min(m0 + xr_row + 16 * j, batch - 1) * K + 8 * xr_kb;
+  // the chunk's packed codes and its groups' step and zero (two groups per chunk at g = 64)
+  auto load_meta = [&](int64_t c, unsigned& dmw, unsigned& zmw) {
+    if constexpr (GS == 64) {
+      dmw = *reinterpret_cast<const unsigned*>(drow + 2 * c);
+      zmw = *reinterpret_cast<const unsigned*>(zrow + 2 * c);
+    } else {
+      dmw = __half_as_ushort(drow[c]);
+      zmw = __half_as_ushort(zrow[c]);
     }
   };
   const int64_t nchunks = K / 128;
-  uint4 xbuf[8];
-  load_x(0, xbuf);
-  uint4 vcur = ld_stream16(wrow + h * 16);
-  for (int64_t c = 0; c < nchunks; ++c) {
-    // publish chunk c's x tile
+  // Chunks c + 1 .. c + kGemmDepth - 1 are in flight (registers) while chunk c is multiplied:
+  // the loop is unrolled by the depth so that every slot index is a constant.  Loads are
+  // unconditional; chunk indexes past the end are clamped (the tail reloads the last chunk).
+  u32x4 xb[kGemmDepth][8];  // native vector type: an array of the uint4 struct went to scratch
+  u32x4 vb[kGemmDepth];
+  unsigned db[kGemmDepth], zb[kGemmDepth];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(xt + (xr_row + 16 * j) * kXRow + 8 * xr_kb) = xbuf[j];
-    const uint4 v = vcur;
-    if (c + 1 < nchunks) {
-      load_x(c + 1, xbuf);
-      vcur = ld_stream16(wrow + (c + 1) * 64 + h * 16);
-    }
-    // weights of chunk c -> fp16 W_hat in the B-operand layout (natural k order)
-    f16x8 Bop[4];
-    int kofs[4];
-    if constexpr (GS == 64) {
-      const auto s0 = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
-      const auto s1 = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
-      const unsigned gd[4] = {s0[0], s1[0], s0[1], s1[1]};
-      const unsigned dmw = *reinterpret_cast<const unsigned*>(drow + 2 * c);
-      const unsigned zmw = *reinterpret_cast<const unsigned*>(zrow + 2 * c);
+  for (int sl = 0; sl < kGemmDepth; ++sl) {
+    const int64_t c = sl < nchunks ? sl : nchunks - 1;
+    vb[sl] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + c * 64 + h * 16));
+    load_meta(c, db[sl], zb[sl]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gg = j >> 1, s = j & 1;
-        const _Float16 dl = __builtin_bit_cast(_Float16, (unsigned short)(dmw >> (16 * gg)));
-        const _Float16 zz = __builtin_bit_cast(_Float16, (unsigned short)(zmw >> (16 * gg)));
+    for (int j = 0; j < 8; ++j) xb[sl][j] = *reinterpret_cast<const u32x4*>(xrow[j] + c * 128);
+  }
+  for (int64_t cb = 0; cb < nchunks; cb += kGemmDepth) {
+#pragma unroll
+    for (int sl = 0; sl < kGemmDepth; ++sl) {
+      const int64_t c = cb + sl;
+      // publish chunk c's x tile, take its codes and metadata, refill the slot with c + depth.
+      // A chunk past the end (the last round of the unrolled loop) gets a zero step, so its
+      // W_hat is 0 and it adds nothing: no branch, so the memory-counter waits stay exact.
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(xt + (xr_row + 16 * j) * kXRow + 8 * xr_kb) = xb[sl][j];
+      const uint4 v = make_uint4(vb[sl][0], vb[sl][1], vb[sl][2], vb[sl][3]);
+      const unsigned dmw = c < nchunks ? db[sl] : 0u, zmw = zb[sl];
+      {
+        const int64_t cn = c + kGemmDepth < nchunks ? c + kGemmDepth : nchunks - 1;
+        vb[sl] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + cn * 64 + h * 16));
+        load_meta(cn, db[sl], zb[sl]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xb[sl][j] = *reinterpret_cast<const u32x4*>(xrow[j] + cn * 128);
+      }
+      // weights of chunk c -> fp16 W_hat in the B-operand layout (natural k order)
+      f16x8 Bop[4];
+      int kofs[4];
+      if constexpr (GS == 64) {
+        const auto s0 = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+        const unsigned gd[4] = {s0[0], s1[0], s0[1], s1[1]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int gg = j >> 1, s = j & 1;
+          const _Float16 dl = __builtin_bit_cast(_Float16, (unsigned short)(dmw >> (16 * gg)));
+          const _Float16 zz = __builtin_bit_cast(_Float16, (unsigned short)(zmw >> (16 * gg)));
+          const f16x2 z1 = {zz, zz}, d1 = {dl, dl};
+          f16x2 p[4];
+          unpack8_natural(gd[j], mk, p);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) p[u] = (p[u] - z1) * d1;
+          Bop[j] = cat(p);
+          kofs[j] = gg * 64 + qh * 16 + s * 8;
+        }
+      } else {
+        const unsigned dd[4] = {v.x, v.y, v.z, v.w};
+        const _Float16 dl = __builtin_bit_cast(_Float16, (unsigned short)dmw);
+        const _Float16 zz = __builtin_bit_cast(_Float16, (unsigned short)zmw);
         const f16x2 z1 = {zz, zz}, d1 = {dl, dl};
-        f16x2 p[4];
-        unpack8_natural(gd[j], mk, p);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) p[u] = (p[u] - z1) * d1;
-        Bop[j] = cat(p);
-        kofs[j] = gg * 64 + qh * 16 + s * 8;
+        for (int j = 0; j < 4; ++j) {
+          f16x2 p[4];
+          unpack8_natural(dd[j], mk, p);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) p[u] = (p[u] - z1) * d1;
+          Bop[j] = cat(p);
+          kofs[j] = h * 32 + j * 8;
+        }
       }
-    } else {
-      const unsigned dd[4] = {v.x, v.y, v.z, v.w};
-      const _Float16 dl = __builtin_bit_cast(_Float16, __half_as_ushort(drow[c]));
-      const _Float16 zz = __builtin_bit_cast(_Float16, __half_as_ushort(zrow[c]));
-      const f16x2 z1 = {zz, zz}, d1 = {dl, dl};
+      __syncthreads();
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f16x2 p[4];
-        unpack8_natural(dd[j], mk, p);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) p[u] = (p[u] - z1) * d1;
-        Bop[j] = cat(p);
-        kofs[j] = h * 32 + j * 8;
+        for (int t = 0; t < 8; ++t) {
+          const f16x8 A = *reinterpret_cast<const f16x8*>(xt + (16 * t + nl) * kXRow + kofs[j]);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bop[j], acc[t], 0, 0, 0);
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const f16x8 A = *reinterpret_cast<const f16x8*>(xt + (16 * t + nl) * kXRow + kofs[j]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bop[j], acc[t], 0, 0, 0);
-      }
-    }
-    __syncthreads();
   }
 #pragma unroll
   for (int t = 0; t < 8; ++t)
@@ -645,20 +672,26 @@ size_t gemv_lds_b(int gs, int spb) {
 }
 
 // Strips per block of the batched GEMV: two when that still leaves >= 256 blocks.
-inline int gemv_strips_per_block(int64_t N) { return (N % 32 == 0 && N / 32 >= 256) ? 2 : 1; }
+inline int gemv_strips_per_block(int64_t N, int64_t batch) {
+  return (batch >= 3 && N % 32 == 0 && N / 32 >= 256) ? 2 : 1;  // batch <= 2 holds 8 chunks per strip
+}
 
 template <int B, int GS>
 hipError_t gemv_b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                   const __half* x, void* y, int y_dtype, hipStream_t st) {
-  const int spb = gemv_strips_per_block(N);
+  const int spb = gemv_strips_per_block(N, B);
   const size_t lds = gemv_lds_b<B>(GS, spb);
   const dim3 grid((unsigned)(N / (16 * spb)));
-  if (spb == 2) {
-    if (y_dtype == HQQ_OUT_F16)
-      hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F16, 2>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
-    else
-      hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F32, 2>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
-  } else {
+  if constexpr (B >= 3) {
+    if (spb == 2) {
+      if (y_dtype == HQQ_OUT_F16)
+        hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F16, 2>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
+      else
+        hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F32, 2>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
+      return hipGetLastError();
+    }
+  }
+  {
     if (y_dtype == HQQ_OUT_F16)
       hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F16, 1>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
     else
