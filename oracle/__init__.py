@@ -64,6 +64,7 @@ def _declare(lib):
         "hqq_oracle_unpack": (i32, [p, i64, i32, p]),
         "hqq_oracle_dequant": (i32, [p, p, p, i64, i64, i32, i32, i32, p, p]),
         "hqq_oracle_gemv": (i32, [p, p, p, i64, i64, i32, p, i64, p, i64, p]),
+        "hqq_oracle_gemv_fmt": (i32, [p, p, p, i64, i64, i32, i32, i32, p, i64, p, i64, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -220,6 +221,26 @@ class Oracle:
                                       y.ctypes.data)
         if rc != 0:
             raise ValueError("oracle gemv rejected the arguments (rc=%d)" % rc)
+        return y
+
+    def gemv_fmt(self, packed, delta, zero, N, K, nbits, group_size, axis, x, rows_sel=None) -> np.ndarray:
+        """y = x @ W_hat^T in fp64 for any stored format (2/3/4-bit, axis 0 or 1)."""
+        pk = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1)
+        dl = np.ascontiguousarray(delta, dtype=np.float64).reshape(-1)
+        zr = np.ascontiguousarray(zero, dtype=np.float64).reshape(-1)
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        B = x.shape[0]
+        if rows_sel is None:
+            sel, nsel = None, N
+        else:
+            sel = np.ascontiguousarray(rows_sel, dtype=np.int64)
+            nsel = sel.size
+        y = np.empty((B, nsel), dtype=np.float64)
+        rc = self.lib.hqq_oracle_gemv_fmt(pk.ctypes.data, dl.ctypes.data, zr.ctypes.data, N, K, nbits, group_size,
+                                          axis, x.ctypes.data, B, None if sel is None else sel.ctypes.data, nsel,
+                                          y.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle gemv_fmt rejected the arguments (rc=%d)" % rc)
         return y
 
 

@@ -450,6 +450,51 @@ int hqq_oracle_gemv(const uint8_t* packed, const double* delta, const double* ze
   return 0;
 }
 
+/* ------------------------------------------------------------------------------------------
+ * The same product for every stored format ("从压缩文件到一次前向": unpack, (q - zero) * scale,
+ * x @ W_hat^T): W [N, K] with nbits in {2, 3, 4}, groups of g along K (axis 1) or the strided
+ * column groups of reshape([g, -1]) (axis 0, "axis 不是一个无关紧要的开关").  Code e of the flat
+ * row-major order is read straight from its container (layout reading R16), its group from the
+ * group view, and the sum over k runs in k order in fp64.
+ * ---------------------------------------------------------------------------------------- */
+
+static int code_at(const uint8_t* packed, int64_t e, int nbits) {
+  if (nbits == 4) return (packed[e / 2] >> ((e % 2) ? 4 : 0)) & 15;
+  if (nbits == 2) return (packed[e / 4] >> (2 * (e % 4))) & 3;
+  int64_t w = e / 10;
+  uint32_t word = (uint32_t)packed[4 * w] | ((uint32_t)packed[4 * w + 1] << 8) | ((uint32_t)packed[4 * w + 2] << 16) |
+                  ((uint32_t)packed[4 * w + 3] << 24);
+  return (int)((word >> (3 * (e % 10))) & 7);
+}
+
+int hqq_oracle_gemv_fmt(const uint8_t* packed, const double* delta, const double* zero, int64_t N, int64_t K,
+                        int nbits, int g, int axis, const double* x, int64_t batch, const int64_t* rows_sel,
+                        int64_t n_sel, double* y) {
+  if (!valid_shape(N, K, nbits, g, axis) || nbits < 2 || nbits > 4 || batch < 0) return -1;
+  if (!rows_sel && n_sel != N) return -1;
+  double* wrow = (double*)malloc((size_t)K * sizeof(double));
+  if (!wrow) return -2;
+  for (int64_t c = 0; c < n_sel; c++) {
+    int64_t n = rows_sel ? rows_sel[c] : c;
+    if (n < 0 || n >= N) {
+      free(wrow);
+      return -1;
+    }
+    for (int64_t k = 0; k < K; k++) {
+      int64_t e = n * K + k;
+      int64_t j = PLANT(17) ? e / g : group_of(e, N, K, g, axis);
+      wrow[k] = ((double)code_at(packed, e, nbits) - zero[j]) * delta[j];
+    }
+    for (int64_t b = 0; b < batch; b++) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; k++) acc = acc + x[b * K + k] * wrow[k];
+      y[b * n_sel + c] = acc;
+    }
+  }
+  free(wrow);
+  return 0;
+}
+
 /* Array form of the fp16 rounding, for convenience. */
 void hqq_oracle_doubles_to_halves(const double* x, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; i++) out[i] = hqq_oracle_double_to_half(x[i]);

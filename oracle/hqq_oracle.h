@@ -71,6 +71,9 @@ int hqq_oracle_dequant(const uint8_t* packed, const double* delta, const double*
                        int nbits, int g, int axis, double* out_f64, uint16_t* out_f16);
 int hqq_oracle_gemv(const uint8_t* packed, const double* delta, const double* zero, int64_t N, int64_t K, int g,
                     const double* x, int64_t batch, const int64_t* rows_sel, int64_t n_sel, double* y);
+int hqq_oracle_gemv_fmt(const uint8_t* packed, const double* delta, const double* zero, int64_t N, int64_t K,
+                        int nbits, int g, int axis, const double* x, int64_t batch, const int64_t* rows_sel,
+                        int64_t n_sel, double* y);
 
 #ifdef __cplusplus
 }

@@ -421,6 +421,33 @@ def pin_gemv(o):
     assert np.array_equal(o.gemv(pk, delta, zero, N, K, g, x1, rows_sel=sel), y1[:, sel])
 
 
+def pin_gemv_formats(o):
+    """The product for every stored format (2-, 3-, 4-bit; axis 1 and axis 0): it equals the
+    plain matmul of the dequantised weight, a one-hot x returns a column of W_hat exactly, and
+    at 4 bits axis 1 it equals the 4-bit product above.  Shapes where the 3-bit rows start
+    inside a word (K not a multiple of 10) and where axis-0 groups stride over rows."""
+    r = _rng(47)
+    cases = [(4, 64, 1, 16, 256), (4, 128, 0, 256, 96), (4, 16, 0, 32, 64), (2, 16, 1, 12, 128), (2, 32, 0, 64, 32),
+             (3, 64, 1, 9, 192), (3, 16, 0, 48, 40)]
+    for nbits, g, axis, N, K in cases:
+        G = N * K // g
+        codes = r.integers(0, 2 ** nbits, (N, K)).astype(np.uint8)
+        delta = r.uniform(1e-3, 0.05, G).astype(np.float16).astype(np.float64)
+        zero = r.uniform(0, 2 ** nbits - 1, G).astype(np.float16).astype(np.float64)
+        pk = o.pack(codes, nbits)
+        w64, _ = o.dequant(pk, delta, zero, N, K, nbits, g, axis)
+        w64 = w64.reshape(N, K)
+        x = r.normal(0, 1, (3, K)).astype(np.float16).astype(np.float64)
+        y = o.gemv_fmt(pk, delta, zero, N, K, nbits, g, axis, x)
+        assert np.allclose(y, x @ w64.T, rtol=1e-12, atol=1e-12), (nbits, g, axis)
+        onehot = np.zeros((2, K))
+        onehot[0, 0] = onehot[1, K - 1] = 1.0
+        y1 = o.gemv_fmt(pk, delta, zero, N, K, nbits, g, axis, onehot)
+        assert (y1 == w64[:, [0, K - 1]].T).all(), (nbits, g, axis)
+        if nbits == 4 and axis == 1:
+            assert np.array_equal(y, o.gemv(pk, delta, zero, N, K, g, x))
+
+
 def pin_mae_definition(o):
     """Round 0's MAE is the mean |W - W_hat| of the min-max start (the dequantisation of the
     iters=0 codes with fp64 metadata)."""

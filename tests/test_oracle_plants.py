@@ -22,6 +22,7 @@ PLANTS = {
     14: "3-bit slots shifted by one bit",
     15: "scale not limited to 2e4",
     16: "sums accumulated sequentially instead of pairwise",
+    17: "product for all formats takes axis-0 groups as axis-1 runs",
 }
 
 
