@@ -103,7 +103,7 @@ size_t hqq_quantize_workspace_bytes(int64_t rows, int64_t cols, int nbits, int g
  * HQQ quantisation of one weight tensor ("第一拍", "第二拍", "为什么一定要分组").
  *   W_fp16     in   fp16 [rows, cols] row-major.
  *   nbits      2, 3 or 4.
- *   group_size 8, 16, 32, 64, 128 or 256; it must divide cols (axis=1) or rows (axis=0);
+ *   group_size 16, 32, 64, 128 or 256; it must divide cols (axis=1) or rows (axis=0);
  *              axis=0 also needs (rows/group_size)*cols to be a multiple of 8.
  *   axis       1 (groups along a row) or 0 (groups down a column, row stride rows/g).
  *   iters      0 .. HQQ_MAX_ITERS proximal rounds at most (20 on the page).
@@ -157,6 +157,23 @@ int hqq_dequantize(const void* packed, const void* delta, const void* zero, int 
  */
 int hqq_gemv_w4a16(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K,
                    int group_size, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* stream);
+
+/*
+ * The same fused product for the other stored formats ("从压缩文件到一次前向";
+ * "axis 不是一个无关紧要的开关" for axis 0; "为什么一定要分组" for the containers):
+ *   y[b, n] = sum_k x[b, k] * (q[n, k] - zero[j]) * delta[j],  j the group of code (n, k)
+ *   in the group view of W [N, K] (axis=1: j = (n*K + k)/g; axis=0: j = (n*K + k) mod (N*K/g),
+ *   i.e. metadata row n mod (N/g), column k).
+ *   packed      in  codes of W [N, K] as hqq_quantize wrote them (nbits, group_size, axis).
+ *   delta_fp16, zero_fp16  in  fp16, one per group in group-view order.
+ *   x_fp16      in  fp16 [batch, K];  y out [batch, N], y_dtype HQQ_OUT_F16 or HQQ_OUT_F32.
+ * Supported: nbits=4 axis=1 (as hqq_gemv_w4a16); nbits=4 axis=0 with group_size 16..256,
+ * K a multiple of 32, batch 1 or 2, K <= 16384; nbits=2 axis=1 group_size 16 with N a
+ * multiple of 16, K a multiple of 64, batch 1 or 2, K <= 16384.  Other combinations return
+ * HQQ_ERR_UNSUPPORTED.  Codes stay exact (fp16 subnormals into v_dot2_f32_f16); fp32 sums.
+ */
+int hqq_gemv(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K, int nbits,
+             int group_size, int axis, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* stream);
 
 /* Static description of a status code. */
 const char* hqq_status_string(int status);

@@ -6,7 +6,7 @@ product runs in the library's kernels.  There is no fallback: when the library i
 the import of a compute function raises.
 
 Names follow the C ABI (``include/hqq.h``): ``hqq_quantize``, ``hqq_dequantize``,
-``hqq_gemv_w4a16``, plus the size queries.
+``hqq_gemv_w4a16``, ``hqq_gemv`` (the other stored formats), plus the size queries.
 """
 from __future__ import annotations
 
@@ -28,7 +28,7 @@ HQQ_MAX_ITERS = 64
 
 # Every symbol the header declares.
 EXPORTS = ("hqq_packed_bytes", "hqq_num_groups", "hqq_quantize_workspace_bytes", "hqq_quantize",
-           "hqq_dequantize", "hqq_gemv_w4a16", "hqq_status_string", "hqq_last_error")
+           "hqq_dequantize", "hqq_gemv_w4a16", "hqq_gemv", "hqq_status_string", "hqq_last_error")
 
 _lib = None
 
@@ -60,6 +60,8 @@ def load(path: str = LIB_PATH):
     lib.hqq_dequantize.restype = i32
     lib.hqq_gemv_w4a16.argtypes = [p, p, p, i64, i64, i32, p, i64, p, i32, p]
     lib.hqq_gemv_w4a16.restype = i32
+    lib.hqq_gemv.argtypes = [p, p, p, i64, i64, i32, i32, i32, p, i64, p, i32, p]
+    lib.hqq_gemv.restype = i32
     lib.hqq_status_string.argtypes = [i32]
     lib.hqq_status_string.restype = ctypes.c_char_p
     lib.hqq_last_error.argtypes = []
@@ -189,5 +191,23 @@ def hqq_gemv_w4a16(packed, delta, zero, N: int, K: int, group_size: int, x, out_
     st = lib.hqq_gemv_w4a16(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
                             ctypes.c_void_p(zero.data_ptr()), N, K, group_size, ctypes.c_void_p(x.data_ptr()), batch,
                             ctypes.c_void_p(out.data_ptr()), code, _stream_ptr(stream))
+    _check(st)
+    return out
+
+
+def hqq_gemv(packed, delta, zero, N: int, K: int, nbits: int, group_size: int, axis: int, x, out_dtype=None,
+             out=None, stream=None):
+    """y [batch, N] = x [batch, K] @ W_hat^T for any stored format the library fuses
+    (4-bit axis 1 or 0, 2-bit axis 1 with groups of 16)."""
+    import torch
+    lib = load()
+    out_dtype = out_dtype or torch.float16
+    batch = x.shape[0]
+    if out is None:
+        out = torch.empty((batch, N), dtype=out_dtype, device=x.device)
+    code = HQQ_OUT_F16 if out.dtype == torch.float16 else HQQ_OUT_F32
+    st = lib.hqq_gemv(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                      ctypes.c_void_p(zero.data_ptr()), N, K, nbits, group_size, axis, ctypes.c_void_p(x.data_ptr()),
+                      batch, ctypes.c_void_p(out.data_ptr()), code, _stream_ptr(stream))
     _check(st)
     return out

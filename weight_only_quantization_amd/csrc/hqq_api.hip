@@ -199,6 +199,44 @@ int hqq_gemv_w4a16(const void* packed, const void* delta_fp16, const void* zero_
   return HQQ_OK;
 }
 
+int hqq_gemv(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K, int nbits,
+             int group_size, int axis, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* stream) {
+  g_last_error[0] = 0;
+  if (nbits == 4 && axis == 1)
+    return hqq_gemv_w4a16(packed, delta_fp16, zero_fp16, N, K, group_size, x_fp16, batch, y, y_dtype, stream);
+  if (N <= 0 || K <= 0 || batch <= 0) return fail(HQQ_ERR_INVALID_ARGUMENT, "N, K and batch must be positive");
+  if (N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) return fail(HQQ_ERR_INVALID_ARGUMENT, "shape too large");
+  if (nbits != 2 && nbits != 3 && nbits != 4) return fail(HQQ_ERR_INVALID_ARGUMENT, "nbits must be 2, 3 or 4");
+  if (axis != 0 && axis != 1) return fail(HQQ_ERR_INVALID_ARGUMENT, "axis must be 0 or 1");
+  if (group_size <= 0 || (axis == 1 ? K : N) % group_size != 0)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "group_size must divide %s", axis == 1 ? "K" : "N");
+  if (y_dtype != HQQ_OUT_F16 && y_dtype != HQQ_OUT_F32)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "y_dtype must be HQQ_OUT_F16 or HQQ_OUT_F32");
+  if (!packed || !delta_fp16 || !zero_fp16 || !x_fp16 || !y) return fail(HQQ_ERR_INVALID_ARGUMENT, "null buffer");
+  if (!aligned16(packed) || !aligned16(delta_fp16) || !aligned16(zero_fp16) || !aligned16(x_fp16) || !aligned16(y))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
+  if (batch > 2) return fail(HQQ_ERR_UNSUPPORTED, "batch must be 1 or 2 for this format");
+  if (K > 16384) return fail(HQQ_ERR_UNSUPPORTED, "K must be at most 16384 for this format");
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* pk = reinterpret_cast<const uint8_t*>(packed);
+  const __half* dl = reinterpret_cast<const __half*>(delta_fp16);
+  const __half* zr = reinterpret_cast<const __half*>(zero_fp16);
+  const __half* xx = reinterpret_cast<const __half*>(x_fp16);
+  hipError_t e;
+  if (nbits == 4 && axis == 0) {
+    if (!pow2_group(group_size)) return fail(HQQ_ERR_UNSUPPORTED, "group_size must be 16, 32, 64, 128 or 256");
+    if (K % 32 != 0) return fail(HQQ_ERR_UNSUPPORTED, "K must be a multiple of 32");
+    e = hqq::launch_gemv_ax0(pk, dl, zr, N, K, group_size, xx, batch, y, y_dtype, st);
+  } else if (nbits == 2 && axis == 1 && group_size == 16) {
+    if (N % 16 != 0 || K % 64 != 0) return fail(HQQ_ERR_UNSUPPORTED, "N must be a multiple of 16 and K of 64");
+    e = hqq::launch_gemv_2b(pk, dl, zr, N, K, xx, batch, y, y_dtype, st);
+  } else {
+    return fail(HQQ_ERR_UNSUPPORTED, "no fused product for nbits=%d group_size=%d axis=%d", nbits, group_size, axis);
+  }
+  if (e != hipSuccess) return device_fail(e, "hqq_gemv launch");
+  return HQQ_OK;
+}
+
 const char* hqq_status_string(int status) {
   switch (status) {
     case HQQ_OK: return "HQQ_OK";

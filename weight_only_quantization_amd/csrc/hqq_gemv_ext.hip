@@ -1,0 +1,449 @@
+// Fused dequantise + product for the other stored formats (page "HQQ 算法解读", sections
+// "从压缩文件到一次前向": unpack, (q - zero) * scale, x @ W_hat^T; "`axis` 不是一个无关紧要的开关"
+// for the axis-0 groups; "为什么一定要分组" for the 2-bit container):
+//   * 4-bit codes with axis-0 groups (a group is a column of reshape([g, -1]): weight row n
+//     uses metadata row r0 = n mod (N/g), one step and zero per column k);
+//   * 2-bit codes with axis-1 groups of 16 (four codes per byte, one group per 32-bit word).
+// Both run on the vector ALUs with v_dot2_f32_f16 on exact codes (fp16 subnormals, as in the
+// 4-bit kernels) and stream whole weight rows, 1 KB per load instruction.
+
+#include "hqq_gemv_common.h"
+
+namespace hqq {
+namespace {
+
+// ------------------------------------------------------------------------------------------
+// Axis 0, 4-bit.  For metadata row r0 the product is
+//   y[b, n] = sum_k a[b, k] q[n, k] - sum_k a[b, k] z[r0, k],   a[b, k] = x[b, k] delta[r0, k],
+// so a block takes one r0 (and a share of its g weight rows n = r0 + (N/g) i): it forms a in
+// fp16 (the product of two fp16 values, rounded once), staged in the unpack slot order with
+// 1/16 on the odd codes, and the zero term from the same staged values (so both terms use the
+// same weights); every weight row is then one fp16-dot-product pass over exact codes.
+// ------------------------------------------------------------------------------------------
+constexpr int kAx0Waves = 4;
+
+template <int B, int JMAX, int RPW>
+__global__ void __launch_bounds__(64 * kAx0Waves) k_gemv_ax0(const uint8_t* __restrict__ packed,
+                                                            const __half* __restrict__ delta,
+                                                            const __half* __restrict__ zero, int64_t N, int64_t K,
+                                                            int g, int subsets, int out_dtype,
+                                                            const __half* __restrict__ x, void* __restrict__ y) {
+  constexpr int D = 2;                      // rows in flight per wave
+  constexpr bool XREG = B * JMAX <= 4;      // a chunks held in registers
+  constexpr int NT = 64 * kAx0Waves;
+  extern __shared__ float lds[];
+  const int nch = (int)(K / 32);            // 32-code chunks per row
+  float* red = lds;                         // [waves][B] partial zero terms
+  uint4* as = reinterpret_cast<uint4*>(red + 4 * B);  // [B][4][nch] 16-byte blocks of a
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t R0 = N / g;
+  const int64_t r0 = blockIdx.x / subsets;
+  const int sub = blockIdx.x % subsets;
+  const __half* drow = delta + r0 * K;
+  const __half* zrow = zero + r0 * K;
+  // rows of this wave: i = sub * 4 * RPW + wave * RPW + t, n = r0 + R0 * i
+  const int64_t i0 = (int64_t)sub * kAx0Waves * RPW + wave * RPW;
+
+  // 1. x, delta and zero blocks of this thread (a block past the end re-reads the last one)
+  constexpr int XR = (B * 64 * JMAX * 4 + NT - 1) / NT;
+  const int nxb = B * nch * 4;
+  uint4 xr[XR], dr[XR], zr[XR];
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const int idx = min(tid + NT * i, nxb - 1);
+    const int kb = idx % (nch * 4);
+    xr[i] = *reinterpret_cast<const uint4*>(x + 8 * idx);  // x is [B][K] contiguous
+    dr[i] = *reinterpret_cast<const uint4*>(drow + 8 * kb);
+    zr[i] = *reinterpret_cast<const uint4*>(zrow + 8 * kb);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // these loads go out ahead of the weight stream
+
+  // 2. the first D rows of this wave, in flight
+  uint4 wv[D][JMAX];
+  auto issue = [&](int s, int64_t i) {
+    const uint8_t* wrow = packed + (r0 + R0 * i) * (K / 2);
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j) wv[s][j] = ld_stream16(wrow + 16 * min(lane + 64 * j, nch - 1));
+  };
+#pragma unroll
+  for (int s = 0; s < D; ++s) issue(s, i0 + s);
+
+  // 3. stage a = x * delta (fp16) in the unpack order, 1/16 on the odd codes, and the zero term
+  float zpart[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) zpart[b] = 0.f;
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const int idx_raw = tid + NT * i;
+    const int idx = min(idx_raw, nxb - 1);
+    const int m = idx / (nch * 4), rem = idx % (nch * 4), c = rem / 4, t = rem % 4;
+    const unsigned xu[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+    const unsigned du[4] = {dr[i].x, dr[i].y, dr[i].z, dr[i].w};
+    const unsigned zu[4] = {zr[i].x, zr[i].y, zr[i].z, zr[i].w};
+    unsigned au[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f16x2 xv = as_h2(xu[q]), dv = as_h2(du[q]);
+      const f16x2 av = {(_Float16)((float)xv[0] * (float)dv[0]), (_Float16)((float)xv[1] * (float)dv[1])};
+      au[q] = as_u(av);
+    }
+    uint4 o = perm_slots(make_uint4(au[0], au[1], au[2], au[3]));
+    o.y = as_u(as_h2(o.y) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
+    o.w = as_u(as_h2(o.w) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
+    as[(m * 4 + t) * nch + c] = o;
+    // zero term from the staged values: slot order [k0, k4, k1, k5, k2, k6, k3, k7], odd x 16
+    const uint4 zp = perm_slots(make_uint4(zu[0], zu[1], zu[2], zu[3]));
+    const unsigned ou[4] = {o.x, o.y, o.z, o.w}, zq[4] = {zp.x, zp.y, zp.z, zp.w};
+    float zt = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float sc = (q & 1) ? 16.f : 1.f;
+      zt = fmaf((float)as_h2(ou[q])[0] * sc, (float)as_h2(zq[q])[0], zt);
+      zt = fmaf((float)as_h2(ou[q])[1] * sc, (float)as_h2(zq[q])[1], zt);
+    }
+    if (idx_raw < nxb) {
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        if (m == b) zpart[b] += zt;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const float v = wave_sum(zpart[b]);
+    if (lane == 0) red[wave * B + b] = v;
+  }
+  __syncthreads();
+  float zb[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAx0Waves; ++w) v += red[w * B + b];
+    zb[b] = v;
+  }
+  f16x2 aq[XREG ? B : 1][XREG ? JMAX : 1][16];
+  if constexpr (XREG) {
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int j = 0; j < JMAX; ++j) {
+        const int c = min(lane + 64 * j, nch - 1);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint4 v = as[(b * 4 + t) * nch + c];
+          aq[b][j][4 * t + 0] = as_h2(v.x);
+          aq[b][j][4 * t + 1] = as_h2(v.y);
+          aq[b][j][4 * t + 2] = as_h2(v.z);
+          aq[b][j][4 * t + 3] = as_h2(v.w);
+        }
+      }
+  }
+
+  // 4. rows: multiply row t, then request row t + D into the freed slot
+#pragma unroll
+  for (int t = 0; t < RPW; ++t) {
+    const int s = t % D;
+    const int64_t n = r0 + R0 * (i0 + t);
+    float P[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) P[b] = 0.f;
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j) {
+      const int c = min(lane + 64 * j, nch - 1);
+      const bool valid = lane + 64 * j < nch;
+      const unsigned dw[4] = {wv[s][j].x, wv[s][j].y, wv[s][j].z, wv[s][j].w};
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        float p = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 u = __builtin_bit_cast(u32x4, unpack8_sub(dw[q]));
+          if constexpr (XREG) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p = __builtin_amdgcn_fdot2(aq[b][j][4 * q + e], as_h2(u[e]), p, false);
+          } else {
+            const uint4 av = as[(b * 4 + q) * nch + c];
+            const unsigned au[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p = __builtin_amdgcn_fdot2(as_h2(au[e]), as_h2(u[e]), p, false);
+          }
+        }
+        P[b] += valid ? p : 0.f;
+      }
+    }
+    if (t + D < RPW) issue(s, i0 + t + D);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float v = wave_sum(P[b]) * kSubScale - zb[b];
+      if (lane == 0) {
+        if (out_dtype == HQQ_OUT_F16)
+          store_y<HQQ_OUT_F16>(y, (int64_t)b * N + n, v);
+        else
+          store_y<HQQ_OUT_F32>(y, (int64_t)b * N + n, v);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Axis 1, 2-bit, groups of 16 (one group per 32-bit word).  Lane l takes the 16-byte chunks
+// c = l + 64 j of a row (64 codes, four groups).  A word d gives its 16 codes as fp16
+// subnormals with one AND each pair: d & 0x00030003 = (c0, c8), d & 0x000C000C = (4c1, 4c9),
+// d & 0x00300030 = (16c2, 16c10), d & 0x00C000C0 = (64c3, 64c11), and the same on d >> 8 for
+// c4..c7 / c12..c15; x is staged in that pair order with 1, 1/4, 1/16, 1/64 on the four
+// positions.  Per group: acc += delta * (P - z * sum_k x_k), the 2^24 folded into delta and z.
+// Waves take R rows n = gw + k N / R with two rows in flight, as the 4-bit kernel.
+// ------------------------------------------------------------------------------------------
+constexpr int k2Waves = 4;
+
+__device__ __forceinline__ void stage_group2(const uint4 (&raw)[2], uint4 (&o)[2], float& sum) {
+  // raw: x of the group, natural order x0..x15 as 8 fp16 pairs
+  const unsigned r[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+  sum = block_sum8({r[0], r[1], r[2], r[3]}) + block_sum8({r[4], r[5], r[6], r[7]});
+  // pair p (0..7) = (x_p, x_{p+8}) scaled by 4^-(p%4)
+  unsigned pr[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const unsigned lo = r[p >> 1], hi = r[4 + (p >> 1)];
+    // x_p is the low (p even) or high (p odd) half of r[p/2]; x_{p+8} likewise of r[4 + p/2]
+    pr[p] = __builtin_amdgcn_perm(hi, lo, (p & 1) ? 0x07060302u : 0x05040100u);
+    const _Float16 sc = (p % 4 == 0) ? (_Float16)1.0f : ((p % 4 == 1) ? (_Float16)0.25f
+                                                        : ((p % 4 == 2) ? (_Float16)0.0625f : (_Float16)0.015625f));
+    if (p % 4) pr[p] = as_u(as_h2(pr[p]) * f16x2{sc, sc});
+  }
+  o[0] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+  o[1] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+}
+
+// Sixteen 2-bit codes of a word -> 8 fp16 subnormal pairs in the order of stage_group2.
+__device__ __forceinline__ void unpack16_2b(unsigned d, unsigned (&u)[8]) {
+  const unsigned d8 = d >> 8;
+  u[0] = d & 0x00030003u;
+  u[1] = d & 0x000C000Cu;
+  u[2] = d & 0x00300030u;
+  u[3] = d & 0x00C000C0u;
+  u[4] = d8 & 0x00030003u;
+  u[5] = d8 & 0x000C000Cu;
+  u[6] = d8 & 0x00300030u;
+  u[7] = d8 & 0x00C000C0u;
+}
+
+template <int B, int JMAX, int R>
+__global__ void __launch_bounds__(64 * k2Waves) k_gemv_2b(const uint8_t* __restrict__ packed,
+                                                         const __half* __restrict__ delta,
+                                                         const __half* __restrict__ zero, int64_t N, int64_t K,
+                                                         int out_dtype, const __half* __restrict__ x,
+                                                         void* __restrict__ y) {
+  constexpr int D = R < 2 ? R : 2;
+  constexpr bool XREG = B * JMAX <= 3;
+  constexpr int NT = 64 * k2Waves;
+  extern __shared__ float lds[];
+  const int nch = (int)(K / 64);              // 64-code chunks per row
+  const int ngr = (int)(K / 16);              // groups per row
+  float* sg = lds;                            // [B][ngr] group sums of x
+  uint4* xs = reinterpret_cast<uint4*>(sg + ((B * ngr + 3) & ~3));  // [B][8][nch] staged x
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t TW = N / R;
+  const int64_t gw = (int64_t)blockIdx.x * k2Waves + wave;
+
+  // 1. x: one group (32 bytes) per task
+  constexpr int XR = (B * 64 * JMAX * 4 + NT - 1) / NT;
+  const int ntask = B * ngr;
+  uint4 xr[XR][2];
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const int idx = min(tid + NT * i, ntask - 1);
+    xr[i][0] = *reinterpret_cast<const uint4*>(x + 16 * idx);
+    xr[i][1] = *reinterpret_cast<const uint4*>(x + 16 * idx + 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. the first D rows: codes (16 B per chunk) and the four groups' steps and zeros (8 B each)
+  uint4 wv[D][JMAX];
+  uint2 dmv[D][JMAX], zmv[D][JMAX];
+  auto issue = [&](int s, int64_t n) {
+    const uint8_t* wrow = packed + n * (K / 4);
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j) {
+      const int c = min(lane + 64 * j, nch - 1);
+      wv[s][j] = ld_stream16(wrow + 16 * c);
+      dmv[s][j] = *reinterpret_cast<const uint2*>(delta + n * ngr + 4 * c);
+      zmv[s][j] = *reinterpret_cast<const uint2*>(zero + n * ngr + 4 * c);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < D; ++s) issue(s, gw + s * TW);
+
+  // 3. stage x: group gi of row m -> pieces xs[(m * 8 + 2 (gi % 4) + h) * nch + gi / 4]
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const int idx = min(tid + NT * i, ntask - 1);  // past the end: the last task again (same values)
+    const int m = idx / ngr, gi = idx % ngr, c = gi / 4, t = gi % 4;
+    uint4 o[2];
+    float sum;
+    stage_group2(xr[i], o, sum);
+    xs[(m * 8 + 2 * t) * nch + c] = o[0];
+    xs[(m * 8 + 2 * t + 1) * nch + c] = o[1];
+    sg[m * ngr + gi] = sum;
+  }
+  __syncthreads();
+  uint4 xq[XREG ? B : 1][XREG ? JMAX : 1][8];
+  float sxr[B][JMAX][4];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j) {
+      const int c = min(lane + 64 * j, nch - 1);
+      if constexpr (XREG) {
+#pragma unroll
+        for (int pc = 0; pc < 8; ++pc) xq[b][j][pc] = xs[(b * 8 + pc) * nch + c];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sxr[b][j][t] = sg[b * ngr + 4 * c + t];
+    }
+
+  // 4. rows
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int s = k % D;
+    const int64_t n = gw + k * TW;
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j) {
+      const int c = min(lane + 64 * j, nch - 1);
+      const bool valid = lane + 64 * j < nch;
+      const unsigned dw[4] = {wv[s][j].x, wv[s][j].y, wv[s][j].z, wv[s][j].w};
+      const unsigned dmw[2] = {dmv[s][j].x, dmv[s][j].y}, zmw[2] = {zmv[s][j].x, zmv[s][j].y};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {  // group t of the chunk = word t
+        unsigned u[8];
+        unpack16_2b(dw[t], u);
+        const unsigned short dh = (unsigned short)(dmw[t >> 1] >> (16 * (t & 1)));
+        const unsigned short zh = (unsigned short)(zmw[t >> 1] >> (16 * (t & 1)));
+        const float dl = valid ? __half2float(__ushort_as_half(dh)) * kSubScale : 0.f;
+        const float zz = __half2float(__ushort_as_half(zh)) * kSubScaleInv;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          float P = 0.f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            uint4 xv;
+            if constexpr (XREG)
+              xv = xq[b][j][2 * t + h];
+            else
+              xv = xs[(b * 8 + 2 * t + h) * nch + c];
+            const unsigned xu[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) P = __builtin_amdgcn_fdot2(as_h2(xu[e]), as_h2(u[4 * h + e]), P, false);
+          }
+          acc[b] = fmaf(dl, fmaf(-zz, sxr[b][j][t], P), acc[b]);
+        }
+      }
+    }
+    if (k + D < R) issue(s, gw + (k + D) * TW);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float v = wave_sum(acc[b]);
+      if (lane == 0) {
+        if (out_dtype == HQQ_OUT_F16)
+          store_y<HQQ_OUT_F16>(y, (int64_t)b * N + n, v);
+        else
+          store_y<HQQ_OUT_F32>(y, (int64_t)b * N + n, v);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------------
+size_t ax0_lds_bytes(int B, int64_t K) { return (size_t)4 * B * 4 + (size_t)B * K * 2; }
+
+template <int B, int JMAX, int RPW>
+hipError_t ax0_launch(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
+                      const __half* x, void* y, int y_dtype, hipStream_t st) {
+  const int subsets = g / (kAx0Waves * RPW);
+  const dim3 grid((unsigned)((N / g) * subsets));
+  hipLaunchKernelGGL((k_gemv_ax0<B, JMAX, RPW>), grid, dim3(64 * kAx0Waves), ax0_lds_bytes(B, K), st, packed, delta,
+                     zero, N, K, g, subsets, y_dtype, x, y);
+  return hipGetLastError();
+}
+
+template <int B, int JMAX>
+hipError_t ax0_rpw(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
+                   const __half* x, void* y, int y_dtype, hipStream_t st) {
+  if (g >= 64) return ax0_launch<B, JMAX, 16>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+  if (g == 32) return ax0_launch<B, JMAX, 8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+  return ax0_launch<B, JMAX, 4>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+}
+
+template <int B>
+hipError_t ax0_b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
+                 const __half* x, void* y, int y_dtype, hipStream_t st) {
+  switch ((K / 32 + 63) / 64) {
+    case 1: return ax0_rpw<B, 1>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 2: return ax0_rpw<B, 2>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 3: return ax0_rpw<B, 3>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 4: return ax0_rpw<B, 4>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 5:
+    case 6: return ax0_rpw<B, 6>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    default: return ax0_rpw<B, 8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+  }
+}
+
+inline int rows_per_wave_2b(int64_t N) {
+  if (N % (8 * k2Waves) == 0 && N / (8 * k2Waves) >= 256) return 8;
+  if (N / (4 * k2Waves) >= 256) return 4;
+  return 2;
+}
+
+size_t lds_2b(int B, int64_t K) { return (size_t)((B * (K / 16) + 3) & ~int64_t(3)) * 4 + (size_t)B * K * 2; }
+
+template <int B, int JMAX>
+hipError_t b2_j(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                const __half* x, void* y, int y_dtype, hipStream_t st) {
+  const int R = rows_per_wave_2b(N);
+  const dim3 grid((unsigned)(N / (R * k2Waves))), block(64 * k2Waves);
+  const size_t lds = lds_2b(B, K);
+  if (R == 8)
+    hipLaunchKernelGGL((k_gemv_2b<B, JMAX, 8>), grid, block, lds, st, packed, delta, zero, N, K, y_dtype, x, y);
+  else if (R == 4)
+    hipLaunchKernelGGL((k_gemv_2b<B, JMAX, 4>), grid, block, lds, st, packed, delta, zero, N, K, y_dtype, x, y);
+  else
+    hipLaunchKernelGGL((k_gemv_2b<B, JMAX, 2>), grid, block, lds, st, packed, delta, zero, N, K, y_dtype, x, y);
+  return hipGetLastError();
+}
+
+template <int B>
+hipError_t b2_b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                const __half* x, void* y, int y_dtype, hipStream_t st) {
+  switch ((K / 64 + 63) / 64) {
+    case 1: return b2_j<B, 1>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    case 2: return b2_j<B, 2>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    case 3: return b2_j<B, 3>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    default: return b2_j<B, 4>(packed, delta, zero, N, K, x, y, y_dtype, st);
+  }
+}
+
+}  // namespace
+
+size_t gemv_ax0_lds_bytes(int64_t K, int64_t batch) { return ax0_lds_bytes((int)batch, K); }
+size_t gemv_2b_lds_bytes(int64_t K, int64_t batch) { return lds_2b((int)batch, K); }
+
+hipError_t launch_gemv_ax0(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                           int g, const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t st) {
+  return batch == 1 ? ax0_b<1>(packed, delta, zero, N, K, g, x, y, y_dtype, st)
+                    : ax0_b<2>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+}
+
+hipError_t launch_gemv_2b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                          const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t st) {
+  return batch == 1 ? b2_b<1>(packed, delta, zero, N, K, x, y, y_dtype, st)
+                    : b2_b<2>(packed, delta, zero, N, K, x, y, y_dtype, st);
+}
+
+}  // namespace hqq

@@ -48,6 +48,14 @@ hipError_t launch_gemv(const uint8_t* packed, const __half* delta, const __half*
                        int group_size, const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t stream);
 size_t gemv_lds_bytes(int64_t K, int group_size, int64_t batch);
 
+// Other stored formats (batch 1 or 2): 4-bit with axis-0 groups; 2-bit with axis-1 groups of 16.
+hipError_t launch_gemv_ax0(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                           int group_size, const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t stream);
+size_t gemv_ax0_lds_bytes(int64_t K, int64_t batch);
+hipError_t launch_gemv_2b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                          const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t stream);
+size_t gemv_2b_lds_bytes(int64_t K, int64_t batch);
+
 hipError_t launch_gemm(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                        int group_size, const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t stream);
 
