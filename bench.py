@@ -7,6 +7,9 @@ three 11008x4096 fp16 weights, N(0, 0.02) with 0.1 % +/-10 sigma outliers):
     step and zero;
   * hqq_dequantize of every layer back to fp16 (the round trip);
   * hqq_gemv_w4a16 on an 8192x8192 4-bit g64 weight at batch 1 and 8 (GEMV) and 256 (MFMA GEMM).
+Beside the step (in "legs", not in `value`): the same layer shapes on Laplace weights at 3-bit
+g64 and 2-bit g16, the 28672x8192 weight with axis-0 groups of 128, and the fused products over
+the 2-bit and axis-0 formats.
 Inputs are resident in HBM before the timed region; the GEMV operands rotate over enough
 copies (> 1 GB) that the 256 MB last-level cache cannot hold them.
 
@@ -74,12 +77,96 @@ def cpu_baseline(layer_tensor, q):
                       % (layer_tensor.rows, layer_tensor.cols, layer_tensor.name, r["rounds"], dt)}
 
 
+def config_legs(a, timed, stream, dev):
+    """Legs outside the step, one per remaining configuration: the 7B-shaped layer set at 3-bit
+    g64 and 2-bit g16 (Laplace weights), the 28672x8192 axis-0 g128 weight, and the fused
+    products over the 2-bit and axis-0 formats (batch 1 and 2, operands rotated over > 1 GB)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import weight_only_quantization_amd as hq
+
+    legs = {}
+
+    def quant_leg(tensors, qp, reps):
+        Ws = [torch.from_numpy(t.make()).to(dev) for t in tensors]
+        wss = [torch.empty(hq.hqq_quantize_workspace_bytes(t.rows, t.cols, qp.nbits, qp.group_size, qp.axis,
+                                                           qp.iters), dtype=torch.uint8, device=dev)
+               for t in tensors]
+        outs = [hq.hqq_quantize(W, nbits=qp.nbits, group_size=qp.group_size, axis=qp.axis, iters=qp.iters, p=qp.p,
+                                beta0=qp.beta0, kappa=qp.kappa, workspace=ws) for W, ws in zip(Ws, wss)]
+
+        def qall(r):
+            for W, ws, q in zip(Ws, wss, outs):
+                hq.hqq_quantize(W, nbits=qp.nbits, group_size=qp.group_size, axis=qp.axis, iters=qp.iters, p=qp.p,
+                                beta0=qp.beta0, kappa=qp.kappa, workspace=ws,
+                                out=(q.packed, q.delta, q.zero, q.stop_iter, q.mae_trace))
+
+        Wh = [torch.empty_like(W) for W in Ws]
+
+        def dqall(r):
+            for t, q, o in zip(tensors, outs, Wh):
+                hq.hqq_dequantize(q.packed, q.delta, q.zero, t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=o)
+
+        tq = timed(qall, reps)
+        td = timed(dqall, reps)
+        n = sum(t.rows * t.cols for t in tensors)
+        wb = 3.2 if qp.nbits == 3 else qp.nbits
+        byt = sum(t.rows * t.cols * (wb / 8 + 4 / qp.group_size) for t in tensors)
+        leg = {"quantize_s": tq, "quantize_gweights_per_s": n / tq / 1e9,
+               "stop_index_per_layer": [int(q.stop_iter.item()) for q in outs],
+               "dequant_s": td, "dequant_GB/s": (byt + 2 * n) / td / 1e9,
+               "dequant_frac_hbm": (byt + 2 * n) / td / PEAK_HBM}
+        del Ws, wss, Wh
+        return leg, outs
+
+    def gemv_leg(name, q, N, K, nbits, g, axis, byt_w):
+        ncopy = max(4, int(np.ceil(1.1e9 / byt_w)))
+        copies = [(q.packed.clone(), q.delta.clone(), q.zero.clone()) for _ in range(ncopy)]
+        X = torch.from_numpy(synth.activations(2, K, 402)).to(dev)
+        for b in (1, 2):
+            Y = torch.empty((b, N), dtype=torch.float16, device=dev)
+
+            def gv(r, b=b, Y=Y):
+                pk, d, z = copies[r % ncopy]
+                hq.hqq_gemv(pk, d, z, N, K, nbits, g, axis, X[:b], out=Y)
+            tg = timed(gv, 2 * ncopy)
+            byt = byt_w + 2 * b * K + 2 * b * N
+            legs["%s_b%d" % (name, b)] = {"us": tg * 1e6, "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM,
+                                          "bytes": byt, "shape": [N, K], "copies_rotated": ncopy}
+        del copies
+
+    log("config legs: 3-bit and 2-bit layer sets")
+    lap = synth.WORKLOADS["llama7b_laplace"]
+    for qp in lap["quant"]:
+        leg, outs = quant_leg(lap["tensors"], qp, 3)
+        legs["layers_laplace_%dbit_g%d" % (qp.nbits, qp.group_size)] = leg
+        if qp.nbits == 2:
+            t = lap["tensors"][4]
+            gemv_leg("gemv_2bit_g16", outs[4], t.rows, t.cols, 2, 16, 1, t.rows * t.cols * (2 / 8 + 4 / 16))
+        del outs
+        torch.cuda.empty_cache()
+    log("config legs: 28672x8192 axis 0")
+    m70 = synth.WORKLOADS["mlp70b"]
+    qp = m70["quant"][0]
+    leg, outs = quant_leg(m70["tensors"], qp, 3)
+    legs["mlp70b_axis0_4bit_g128"] = leg
+    t = m70["tensors"][0]
+    gemv_leg("gemv_axis0_g128", outs[0], t.rows, t.cols, 4, 128, 0, t.rows * t.cols * (4 / 8 + 4 / 128))
+    del outs
+    torch.cuda.empty_cache()
+    return legs
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-legs", action="store_true",
+                    help="skip the 3-/2-bit, axis-0 and other-format legs outside the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     a = ap.parse_args()
@@ -206,6 +293,9 @@ def main():
         legs["gemv_b%d" % b] = {"us": tg * 1e6, "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM,
                                 "TFLOP/s": flops / tg / 1e12, "frac_mfma_f16": flops / tg / PEAK_FP16_MFMA,
                                 "bytes": byt}
+
+    if not a.no_extra_legs:
+        legs.update(config_legs(a, timed, stream, dev))
 
     if a.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -136,8 +136,10 @@ int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int 
  *   packed, delta, zero  in  the buffers hqq_quantize wrote (same rows, cols, nbits,
  *                        group_size, axis); meta_dtype HQQ_META_F16 or HQQ_META_F32.
  *   W_out_fp16           out fp16 [rows, cols] row-major.
- * The product is formed exactly and rounded once to nearest-even fp16 (for a zero
- * of magnitude below 2^-10 the difference q - z may carry one fp32 rounding).
+ * The product is formed exactly and rounded once to nearest-even fp16.  With fp16
+ * metadata this holds for every value (a zero result is +0 where a step <= 0 would
+ * give -0; quantizer steps are positive); with fp32 metadata the difference q - z
+ * may carry one fp32 rounding when 0 < |zero| < 2^-10.
  */
 int hqq_dequantize(const void* packed, const void* delta, const void* zero, int meta_dtype, int64_t rows,
                    int64_t cols, int nbits, int group_size, int axis, void* W_out_fp16, void* stream);

@@ -123,8 +123,12 @@ def test_repeat_calls_deterministic():
 
 # ---------------------------------------------------------------------------- dequantisation
 
+# every fused form: 4-/2-bit axis 1, 4-bit axis 0, 2-bit axis 0 with (rows/g) cols a multiple of 16
+# (and the general kernel when it is not), 3-bit axis 1 with two or three groups per 40 codes and
+# a ragged end, and the general 3-bit axis-0 kernel
 DQ_CASES = [(4, 64, 1, 37, 192), (4, 128, 0, 256, 200), (3, 64, 1, 37, 192), (3, 16, 0, 48, 120),
-            (2, 16, 1, 37, 192), (2, 32, 0, 96, 88), (4, 16, 1, 13, 48)]
+            (2, 16, 1, 37, 192), (2, 32, 0, 96, 88), (4, 16, 1, 13, 48), (2, 32, 0, 64, 96),
+            (4, 16, 0, 32, 40), (3, 16, 1, 13, 48), (3, 32, 1, 7, 96), (3, 256, 1, 5, 256), (2, 64, 1, 9, 320)]
 
 
 @pytest.mark.parametrize("nbits,g,axis,rows,cols", DQ_CASES)
