@@ -77,6 +77,18 @@ def cpu_baseline(layer_tensor, q):
                       % (layer_tensor.rows, layer_tensor.cols, layer_tensor.name, r["rounds"], dt)}
 
 
+def sleep_rate(stream):
+    """Clock rate of torch's spin kernel in cycles per millisecond (measured)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    e0.record(stream)
+    torch.cuda._sleep(2_000_000)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 2_000_000 / max(e0.elapsed_time(e1), 1e-3)
+
+
 def config_legs(a, timed, stream, dev):
     """Legs outside the step, one per remaining configuration: the 7B-shaped layer set at 3-bit
     g64 and 2-bit g16 (Laplace weights), the 28672x8192 axis-0 g128 weight, and the fused
@@ -260,18 +272,27 @@ def main():
     rounds = [min(s + 2, qp.iters) if s < qp.iters else qp.iters for s in stops]
 
     # ---------------------------------------------------------------- per-leg timing loops
+    cycles_per_ms = sleep_rate(stream)
+
     def timed(fn, reps):
-        """Mean GPU time of one call: an event pair around every call on the launch stream
-        (host gaps between calls fall outside the pairs)."""
+        """Mean GPU time of one call over `reps` back-to-back calls on the launch stream.  A spin
+        kernel holds the stream while the host enqueues the calls (so that host launch overhead
+        never leaves the GPU idle between them); one event pair brackets the calls."""
         fn(0)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        h0 = time.perf_counter()
         for r in range(reps):
-            evs[r][0].record(stream)
             fn(r)
-            evs[r][1].record(stream)
+        host_ms = (time.perf_counter() - h0) * 1e3
         torch.cuda.synchronize()
-        return float(np.mean([s.elapsed_time(e) for s, e in evs])) * 1e-3  # s per call
+        torch.cuda._sleep(int(cycles_per_ms * (2.0 * host_ms + 1.0)))
+        t0_ev, t1_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0_ev.record(stream)
+        for r in range(reps):
+            fn(r)
+        t1_ev.record(stream)
+        torch.cuda.synchronize()
+        return t0_ev.elapsed_time(t1_ev) * 1e-3 / reps  # s per call
 
     def dq_all(r):
         for t, W, ws, out, What in layers:

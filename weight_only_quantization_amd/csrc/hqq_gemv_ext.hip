@@ -22,13 +22,13 @@ namespace {
 // ------------------------------------------------------------------------------------------
 constexpr int kAx0Waves = 4;
 
-template <int B, int JMAX, int RPW>
+template <int B, int JMAX, int RPW, int D>
 __global__ void __launch_bounds__(64 * kAx0Waves) k_gemv_ax0(const uint8_t* __restrict__ packed,
                                                             const __half* __restrict__ delta,
                                                             const __half* __restrict__ zero, int64_t N, int64_t K,
                                                             int g, int subsets, int out_dtype,
                                                             const __half* __restrict__ x, void* __restrict__ y) {
-  constexpr int D = 2;                      // rows in flight per wave
+  static_assert(D >= 1 && D <= RPW, "rows in flight must be within the wave's rows");  // D: rows in flight
   constexpr bool XREG = B * JMAX <= 4;      // a chunks held in registers
   constexpr int NT = 64 * kAx0Waves;
   extern __shared__ float lds[];
@@ -229,13 +229,13 @@ __device__ __forceinline__ void unpack16_2b(unsigned d, unsigned (&u)[8]) {
   u[7] = d8 & 0x00C000C0u;
 }
 
-template <int B, int JMAX, int R>
+template <int B, int JMAX, int R, int D>
 __global__ void __launch_bounds__(64 * k2Waves) k_gemv_2b(const uint8_t* __restrict__ packed,
                                                          const __half* __restrict__ delta,
                                                          const __half* __restrict__ zero, int64_t N, int64_t K,
                                                          int out_dtype, const __half* __restrict__ x,
                                                          void* __restrict__ y) {
-  constexpr int D = R < 2 ? R : 2;
+  static_assert(D >= 1 && D <= R, "rows in flight must be within the wave's rows");  // D: rows in flight
   constexpr bool XREG = B * JMAX <= 3;
   constexpr int NT = 64 * k2Waves;
   extern __shared__ float lds[];
@@ -368,14 +368,17 @@ hipError_t ax0_launch(const uint8_t* packed, const __half* delta, const __half* 
                       const __half* x, void* y, int y_dtype, hipStream_t st) {
   const int subsets = g / (kAx0Waves * RPW);
   const dim3 grid((unsigned)((N / g) * subsets));
-  hipLaunchKernelGGL((k_gemv_ax0<B, JMAX, RPW>), grid, dim3(64 * kAx0Waves), ax0_lds_bytes(B, K), st, packed, delta,
+  hipLaunchKernelGGL((k_gemv_ax0<B, JMAX, RPW, 2>), grid, dim3(64 * kAx0Waves), ax0_lds_bytes(B, K), st, packed, delta,
                      zero, N, K, g, subsets, y_dtype, x, y);
   return hipGetLastError();
 }
 
+// rows per wave: a whole group's g rows per block where g allows (fewer blocks re-staging a)
 template <int B, int JMAX>
 hipError_t ax0_rpw(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
                    const __half* x, void* y, int y_dtype, hipStream_t st) {
+  if constexpr (B == 1 || JMAX <= 4)  // 32 unrolled rows of B = 2, K > 8192 run out of registers
+    if (g >= 128) return ax0_launch<B, JMAX, 32>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
   if (g >= 64) return ax0_launch<B, JMAX, 16>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
   if (g == 32) return ax0_launch<B, JMAX, 8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
   return ax0_launch<B, JMAX, 4>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
@@ -395,11 +398,9 @@ hipError_t ax0_b(const uint8_t* packed, const __half* delta, const __half* zero,
   }
 }
 
-inline int rows_per_wave_2b(int64_t N) {
-  if (N % (8 * k2Waves) == 0 && N / (8 * k2Waves) >= 256) return 8;
-  if (N / (4 * k2Waves) >= 256) return 4;
-  return 2;
-}
+// two rows per wave, both in flight from the start (more rows per wave measured slower: the
+// rows of a wave then queue behind each other's memory latency)
+inline int rows_per_wave_2b(int64_t N) { return N % (2 * k2Waves) == 0 ? 2 : 1; }
 
 size_t lds_2b(int B, int64_t K) { return (size_t)((B * (K / 16) + 3) & ~int64_t(3)) * 4 + (size_t)B * K * 2; }
 
@@ -409,12 +410,10 @@ hipError_t b2_j(const uint8_t* packed, const __half* delta, const __half* zero, 
   const int R = rows_per_wave_2b(N);
   const dim3 grid((unsigned)(N / (R * k2Waves))), block(64 * k2Waves);
   const size_t lds = lds_2b(B, K);
-  if (R == 8)
-    hipLaunchKernelGGL((k_gemv_2b<B, JMAX, 8>), grid, block, lds, st, packed, delta, zero, N, K, y_dtype, x, y);
-  else if (R == 4)
-    hipLaunchKernelGGL((k_gemv_2b<B, JMAX, 4>), grid, block, lds, st, packed, delta, zero, N, K, y_dtype, x, y);
+  if (R == 2)
+    hipLaunchKernelGGL((k_gemv_2b<B, JMAX, 2, 2>), grid, block, lds, st, packed, delta, zero, N, K, y_dtype, x, y);
   else
-    hipLaunchKernelGGL((k_gemv_2b<B, JMAX, 2>), grid, block, lds, st, packed, delta, zero, N, K, y_dtype, x, y);
+    hipLaunchKernelGGL((k_gemv_2b<B, JMAX, 1, 1>), grid, block, lds, st, packed, delta, zero, N, K, y_dtype, x, y);
   return hipGetLastError();
 }
 
