@@ -6,7 +6,8 @@ three 11008x4096 fp16 weights, N(0, 0.02) with 0.1 % +/-10 sigma outliers):
     min-max start, proximal rounds with the whole-tensor early stop, final codes, packing, fp16
     step and zero;
   * hqq_dequantize of every layer back to fp16 (the round trip);
-  * hqq_gemv_w4a16 on an 8192x8192 4-bit g64 weight at batch 1 and 8 (GEMV) and 256 (MFMA GEMM).
+  * the fused product on an 8192x8192 4-bit g64 weight: hqq_gemv_w4a16 at batch 1 and 8 (GEMV),
+    hqq_gemm_w4a16 (split-K MFMA GEMM, workspace preallocated) at batch 256.
 Beside the step (in "legs", not in `value`): the same layer shapes on Laplace weights at 3-bit
 g64 and 2-bit g16, the 28672x8192 weight with axis-0 groups of 128, and the fused products over
 the 2-bit and axis-0 formats.
@@ -230,6 +231,14 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    gemm_ws = torch.empty(max(hq.hqq_gemm_workspace_bytes(GN, GK, 256), 16), dtype=torch.uint8, device=dev)
+
+    def product(pk, d, z, b):
+        """Batch <= 8: the streaming GEMV; larger: the split-K GEMM with its workspace."""
+        if b <= 8:
+            hq.hqq_gemv_w4a16(pk, d, z, GN, GK, gq.group_size, X[:b], out=Y[b])
+        else:
+            hq.hqq_gemm_w4a16(pk, d, z, GN, GK, gq.group_size, X[:b], out=Y[b], workspace=gemm_ws)
 
     def step(i, ev=None):
         for li, (t, W, ws, out, What) in enumerate(layers):
@@ -243,7 +252,7 @@ def main():
             hq.hqq_dequantize(out[0], out[1], out[2], t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=What)
         for j, b in enumerate((1, 8, 256)):
             pk, d, z = copies[(3 * i + j) % ncopy]
-            hq.hqq_gemv_w4a16(pk, d, z, GN, GK, gq.group_size, X[:b], out=Y[b])
+            product(pk, d, z, b)
 
     # ---------------------------------------------------------------- warmup + timed steps
     for i in range(a.warmup):
@@ -307,7 +316,7 @@ def main():
     for b in (1, 8, 256):
         def gv(r, b=b):
             pk, d, z = copies[r % ncopy]
-            hq.hqq_gemv_w4a16(pk, d, z, GN, GK, gq.group_size, X[:b], out=Y[b])
+            product(pk, d, z, b)
         tg = timed(gv, 2 * ncopy)
         byt = GN * GK / 2 + 4 * GN * GK / gq.group_size + 2 * b * GK + 2 * b * GN
         flops = 2.0 * b * GN * GK

@@ -161,6 +161,24 @@ int hqq_gemv_w4a16(const void* packed, const void* delta_fp16, const void* zero_
                    int group_size, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* stream);
 
 /*
+ * Batched fused product with a caller-provided workspace (same operation, operands and
+ * output layout as hqq_gemv_w4a16; "从压缩文件到一次前向": y = x @ W_hat^T).  For large
+ * batches: each block of the GPU computes a 256 (batch) x 128 (weight rows) tile over a
+ * share of K, the weight tile dequantised once into LDS, fp16 MFMA with fp32 accumulation;
+ * the K shares' fp32 partial sums are added in a fixed order (deterministic).
+ *   workspace        device memory of at least hqq_gemm_workspace_bytes(N, K, batch) bytes,
+ *                    16-byte aligned, owned by the caller; overwritten (a tiled copy of x and
+ *                    the partial sums); calls that share a workspace must not overlap.
+ * N must be a multiple of 128 and K of 512; group_size 64 or 128; any batch >= 1 (rows are
+ * processed in blocks of 256).  Returns HQQ_ERR_UNSUPPORTED for other shapes and
+ * HQQ_ERR_WORKSPACE when the workspace is too small.
+ */
+size_t hqq_gemm_workspace_bytes(int64_t N, int64_t K, int64_t batch);
+int hqq_gemm_w4a16(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K,
+                   int group_size, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
  * The same fused product for the other stored formats ("从压缩文件到一次前向";
  * "axis 不是一个无关紧要的开关" for axis 0; "为什么一定要分组" for the containers):
  *   y[b, n] = sum_k x[b, k] * (q[n, k] - zero[j]) * delta[j],  j the group of code (n, k)

@@ -244,3 +244,50 @@ def test_gemv_onehot_columns():
                               out_dtype=torch.float32).cpu().numpy()
         ref = w64[:, ks].T
         assert np.allclose(y, ref, rtol=2e-3, atol=2e-3 * np.abs(ref).max())
+
+
+# ---------------------------------------------------------------------------- split-K GEMM
+
+def check_gemm(packed, d16, z16, N, K, g, x, out_f32, rows_sel=None, workspace=None):
+    import weight_only_quantization_amd as hq
+    torch = torch_dev()
+    o = oracle.get()
+    y = hq.hqq_gemm_w4a16(torch.from_numpy(packed).cuda(), torch.from_numpy(d16).cuda(),
+                          torch.from_numpy(z16).cuda(), N, K, g, torch.from_numpy(x).cuda(),
+                          out_dtype=torch.float32 if out_f32 else torch.float16, workspace=workspace)
+    yg = y.float().cpu().numpy().astype(np.float64)
+    yr = o.gemv(packed, d16, z16, N, K, g, x.astype(np.float64), rows_sel=rows_sel)
+    if rows_sel is not None:
+        yg = yg[:, rows_sel]
+    scale = np.maximum(np.abs(yr), np.sqrt(np.mean(yr ** 2)))
+    err = np.abs(yg - yr) / scale
+    assert err.max() <= GEMV_TOL, "max rel err %.3g" % err.max()
+    return float(err.max())
+
+
+@pytest.mark.parametrize("g", [64, 128])
+@pytest.mark.parametrize("N,K,batch", [(128, 512, 9), (256, 1024, 100), (384, 2048, 256), (128, 4096, 300),
+                                       (1024, 512, 37), (128, 1536, 513)])
+def test_gemm_split_parity(g, N, K, batch):
+    """Split-K GEMM: one or several K splits (the split count depends on the tile count), a
+    ragged batch inside one 256-row block and over two and three blocks."""
+    say("gemm split", g, N, K, batch)
+    packed, d16, z16 = gemv_inputs(N, K, g, seed=5000 + N + K)
+    x = synth.activations(batch, K, seed=17)
+    check_gemm(packed, d16, z16, N, K, g, x, out_f32=True)
+    check_gemm(packed, d16, z16, N, K, g, x, out_f32=False)
+
+
+def test_gemm_split_errors():
+    import weight_only_quantization_amd as hq
+    torch = torch_dev()
+    pk = torch.zeros(128 * 512 // 2, dtype=torch.uint8, device="cuda")
+    md = torch.zeros(128 * 512 // 64, dtype=torch.float16, device="cuda")
+    x = torch.zeros((16, 512), dtype=torch.float16, device="cuda")
+    need = hq.hqq_gemm_workspace_bytes(128, 512, 16)
+    assert need > 0 and hq.hqq_gemm_workspace_bytes(120, 512, 16) == 0 and hq.hqq_gemm_workspace_bytes(128, 384, 16) == 0
+    with pytest.raises(hq.HQQError):  # workspace too small
+        hq.hqq_gemm_w4a16(pk, md, md, 128, 512, 64, x, workspace=torch.empty(need - 256, dtype=torch.uint8,
+                                                                                  device="cuda"))
+    with pytest.raises(hq.HQQError):  # N not a multiple of 128
+        hq.hqq_gemm_w4a16(pk, md, md, 64, 512, 64, x)

@@ -136,3 +136,9 @@ def test_workload_gemv():
             err = float(np.max(np.abs(yg - yr) / scale))
             say("    %s max rel err %.3g" % (out_dtype, err))
             assert err <= GEMV_TOL
+            if B > 8:  # the split-K GEMM entry point on the same operands
+                y = hq.hqq_gemm_w4a16(pk_d, d_d, z_d, N, K, q.group_size, torch.from_numpy(x).cuda(),
+                                      out_dtype=out_dtype).float().cpu().numpy().astype(np.float64)
+                err = float(np.max(np.abs(y[:, sel] - yr) / scale))
+                say("    split GEMM %s max rel err %.3g" % (out_dtype, err))
+                assert err <= GEMV_TOL

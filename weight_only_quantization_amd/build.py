@@ -23,7 +23,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-ffp-contract=
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-I" + os.path.join(HERE, "..", "include")]
 
-SOURCES = ["hqq_api.hip", "hqq_quant.hip", "hqq_dequant.hip", "hqq_gemv.hip", "hqq_gemv_ext.hip"]
+SOURCES = ["hqq_api.hip", "hqq_quant.hip", "hqq_dequant.hip", "hqq_gemv.hip", "hqq_gemv_ext.hip", "hqq_gemm.hip"]
 
 
 def _compile(src: str) -> str:

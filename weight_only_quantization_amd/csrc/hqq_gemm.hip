@@ -1,0 +1,329 @@
+// Fused dequantise + matrix product for large batches, split along K (page "HQQ 算法解读",
+// section "从压缩文件到一次前向": unpack, (q - zero) * scale, x @ W_hat^T, with fp32
+// accumulation).
+//
+// A batch of 256 against an 8192-row weight gives only 2M outputs: one block per compute
+// unit then owns an 8192-output tile, too small to feed the matrix cores from LDS and L2 (the
+// activations would be re-read 128 times).  Here a block owns a 256 (batch) x 128 (weight
+// rows) tile over a quarter of K (whatever split brings the grid to >= 256 blocks), so every
+// weight is dequantised once and the activations are read N / 128 times; the splits' fp32
+// partial sums go to a caller-provided workspace and a second kernel adds them in split order
+// (deterministic) into y.
+//
+// Block = 4 waves; wave w owns batch rows 64w .. 64w + 63 of the tile and all 128 weight rows
+// (4 x 8 tiles of v_mfma_f32_16x16x32_f16).  Per 128-code chunk:
+//   * W_hat of the block's 128 rows is dequantised once into LDS (double buffered): thread t
+//     takes row t / 2, 64 codes, and forms fp16(c 2^-24 * (d 2^24) - z d) with the mixed
+//     fp16/fp32 FMA (the code is a masked fp16 subnormal; z d is exact in fp32), one rounding
+//     to fp32 and one to fp16;
+//   * the activations go straight from global memory (L2) into the A operand registers (no
+//     other wave reads them), one chunk ahead;
+//   * the packed codes of chunk c + 2 are loaded while chunk c is multiplied.
+// One barrier per chunk.
+
+#include "hqq_gemv_common.h"
+
+namespace hqq {
+namespace {
+
+constexpr int kSkBM = 256;          // batch rows per block
+constexpr int kSkBN = 128;          // weight rows per block
+constexpr int kSkBK = 128;          // codes per chunk
+constexpr int kSkRow = kSkBK + 8;   // LDS row stride of the W_hat tile (halves)
+constexpr size_t kSkLds = 2 * kSkBN * kSkRow * sizeof(_Float16);
+constexpr int kSkThreads = 256;     // 4 waves, each 64 batch rows x all 128 weight rows
+
+// Eight 4-bit codes of a word (natural order) -> fp16 W_hat pairs (c0,c1), (c2,c3), (c4,c5), (c6,c7).
+// t0 = (c0, c4), t1 = 16 (c1, c5), t2 = (c2, c6), t3 = 16 (c3, c7) as fp16 subnormals.
+__device__ __forceinline__ u32x4 wq8(unsigned w, float ds24, float ds20, float zd) {
+  const unsigned u = w >> 8;
+  const f16x2 h0 = as_h2(w & 0x000F000Fu), h1 = as_h2(w & 0x00F000F0u);
+  const f16x2 h2 = as_h2(u & 0x000F000Fu), h3 = as_h2(u & 0x00F000F0u);
+  const f16x2 p0 = {(_Float16)__builtin_fmaf((float)h0[0], ds24, -zd), (_Float16)__builtin_fmaf((float)h1[0], ds20, -zd)};
+  const f16x2 p1 = {(_Float16)__builtin_fmaf((float)h2[0], ds24, -zd), (_Float16)__builtin_fmaf((float)h3[0], ds20, -zd)};
+  const f16x2 p2 = {(_Float16)__builtin_fmaf((float)h0[1], ds24, -zd), (_Float16)__builtin_fmaf((float)h1[1], ds20, -zd)};
+  const f16x2 p3 = {(_Float16)__builtin_fmaf((float)h2[1], ds24, -zd), (_Float16)__builtin_fmaf((float)h3[1], ds20, -zd)};
+  return u32x4{as_u(p0), as_u(p1), as_u(p2), as_u(p3)};
+}
+
+// Workgroup barrier for LDS hand-over only: waits for this wave's LDS operations, not for its
+// global loads (the prefetched operands stay in flight; __syncthreads would drain them).  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int GS, bool DIRECT>
+__global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restrict__ packed, const __half* __restrict__ delta,
+                                                 const __half* __restrict__ zero, int64_t N, int64_t K, int64_t ks,
+                                                 const u32x4* __restrict__ xt, int64_t MG, int64_t batch,
+                                                 float* __restrict__ part, void* __restrict__ y, int out_dtype,
+                                                 int xcd_map) {
+  extern __shared__ _Float16 wt[];  // [2][kSkBN][kSkRow]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // Block b of a row of the grid runs on XCD b mod 8 (round-robin dispatch).  With xcd_map,
+  // the S splits get 8 / S XCDs each (S <= 8) or each XCD gets S / 8 splits, so one XCD's L2
+  // holds only its splits' columns of x.
+  int tile, split;
+  {
+    const int b = blockIdx.x, nb = gridDim.x, S = (int)(K / ks);
+    if (xcd_map) {
+      const int xcd = b & 7, r = b >> 3;
+      if (S <= 8) {
+        const int per = 8 / S;
+        split = xcd / per;
+        tile = r * per + xcd % per;
+      } else {
+        const int per = S / 8;
+        split = xcd * per + r % per;
+        tile = r / per;
+      }
+    } else {
+      tile = b % (nb / S);
+      split = b / (nb / S);
+    }
+  }
+  const int64_t n0 = (int64_t)tile * kSkBN, m0 = (int64_t)blockIdx.y * kSkBM, k0 = (int64_t)split * ks;
+  const int nch = (int)(ks / kSkBK);
+
+  // W staging: thread -> weight rows wr and 64 + wr, codes 32 wq .. 32 wq + 31 of each chunk
+  // (16 bytes each): one load instruction of a wave spans 16 rows (each row of a 4-bit weight
+  // with K = 8192 is its own 4 KB page, and an instruction's distinct pages are translated one
+  // after another)
+  const int wr = tid >> 2, wq = tid & 3;
+  const uint8_t* wsrc = packed + (n0 + wr) * (K / 2) + k0 / 2 + 16 * wq;
+  const int64_t wstride = 64 * (K / 2);  // second row pass
+  const __half* dsrc = delta + (n0 + wr) * (K / GS);
+  const __half* zsrc = zero + (n0 + wr) * (K / GS);
+  const int64_t mstride = 64 * (K / GS);
+  _Float16* wdst = wt + wr * kSkRow + 32 * wq;
+
+  // A operand from the tiled copy of x: the 16 x 32 fragment of row group mg and k-step q is
+  // 1 KB at xt[(q MG + mg) 64 ..], already in lane order (lane l: row l & 15, codes
+  // 8 (l >> 4) .. +7), so every A load instruction reads one contiguous 1 KB
+  const u32x4* xa[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) xa[t] = xt + ((k0 / 32) * MG + (m0 + 64 * wave + 16 * t) / 16) * 64 + lane;
+
+  auto load_w = [&](int c, u32x4 (&wv)[2], unsigned (&dm)[2], unsigned (&zm)[2]) {
+    const int cc = min(c, nch - 1);  // past the end: reload the last chunk (never used)
+    const int64_t gi = (k0 + (int64_t)kSkBK * cc + 32 * wq) / GS;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      wv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + p * wstride + 64 * cc));
+      dm[p] = __half_as_ushort(dsrc[p * mstride + gi]);
+      zm[p] = __half_as_ushort(zsrc[p * mstride + gi]);
+    }
+  };
+  // A operand of k-step q (32 codes) into one of four register slots
+  const int nsteps = 4 * nch;
+  auto load_a = [&](int q, u32x4 (&av)[4]) {
+    const int qq = min(q, nsteps - 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) av[t] = xa[t][(int64_t)qq * MG * 64];
+  };
+  // per-chunk dequantisation constants of a row's group: z d and d 2^24, d 2^20 (all exact)
+  struct WConst {
+    float zd, ds24, ds20;
+  };
+  auto wconst = [&](unsigned dm, unsigned zm) {
+    const float d = __half2float(__ushort_as_half((unsigned short)dm));
+    const float z = __half2float(__ushort_as_half((unsigned short)zm));
+    return WConst{z * d, d * 16777216.0f, d * 1048576.0f};
+  };
+  // words 2 h, 2 h + 1 of row pass p -> W_hat into LDS buffer `buf`
+  auto stage2 = [&](int buf, const u32x4 (&wv)[2], const WConst (&k)[2], int p, int h) {
+    _Float16* dst = wdst + buf * (kSkBN * kSkRow) + p * 64 * kSkRow;
+#pragma unroll
+    for (int i = 2 * h; i < 2 * h + 2; ++i)
+      *reinterpret_cast<u32x4*>(dst + 8 * i) = wq8(wv[p][i], k[p].ds24, k[p].ds20, k[p].zd);
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One chunk c from LDS buffer `buf`, with the staging of chunk c + 1 (codes in wp, loaded one
+  // chunk ago) into the other buffer and the loads of chunk c + 2's codes into wq spread over
+  // its four k-steps.  k-step s: MFMAs in fragment order j (four batch tiles each); fragment j's
+  // registers are refilled from LDS with k-step s + 1 right after its four MFMAs; words 2s and
+  // 2s + 1 of the thread's next-chunk codes are dequantised and stored; A slot s is refilled
+  // with k-step s of chunk c + 1 after its last MFMA (A runs three k-steps ahead).  The group
+  // scheduling barriers keep the loads where they are written (the compiler would otherwise
+  // sink them to the loop end and wait for them there).
+  u32x4 as[4][4];
+  auto chunk = [&](int buf, int c, const u32x4 (&wp)[2], const unsigned (&dmp)[2], const unsigned (&zmp)[2],
+                   u32x4 (&wn)[2], unsigned (&dmn)[2], unsigned (&zmn)[2]) {
+    load_w(c + 2, wn, dmn, zmn);
+    const WConst k[2] = {wconst(dmp[0], zmp[0]), wconst(dmp[1], zmp[1])};
+    const _Float16* src = wt + buf * (kSkBN * kSkRow) + (lane & 15) * kSkRow + 8 * (lane >> 4);
+    f16x8 B[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) B[j] = *reinterpret_cast<const f16x8*>(src + 16 * j * kSkRow);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      stage2(buf ^ 1, wp, k, s >> 1, s & 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, as[s][t]), B[j], acc[t][j], 0, 0, 0);
+        if (s < 3) B[j] = *reinterpret_cast<const f16x8*>(src + 16 * j * kSkRow + 32 * (s + 1));
+      }
+      load_a(4 * c + s + 4, as[s]);  // into the registers just read: no copy at the loop edge
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // two chunks per iteration, so that the two code register sets keep fixed names; the loads
+  // outstanding at the loop head are issued in the same order as in the loop (codes of the
+  // next chunk, then the A slots), so the head waits only for the former
+  u32x4 wa[2], wb[2];
+  unsigned dma[2], zma[2], dmb[2], zmb[2];
+  load_w(0, wa, dma, zma);
+  {
+    const WConst k[2] = {wconst(dma[0], zma[0]), wconst(dma[1], zma[1])};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) stage2(0, wa, k, s4 >> 1, s4 & 1);
+  }
+  load_w(1, wa, dma, zma);
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) load_a(s4, as[s4]);
+  lds_barrier();
+  for (int c = 0; c < nch; c += 2) {
+    chunk(0, c, wa, dma, zma, wb, dmb, zmb);
+    lds_barrier();
+    chunk(1, c + 1, wb, dmb, zmb, wa, dma, zma);
+    lds_barrier();
+  }
+
+  // D layout: acc[t][j][r] is batch row 64 wave + 16 t + 4 (lane >> 4) + r, weight row
+  // 16 j + (lane & 15)
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = m0 + 64 * wave + 16 * t + 4 * (lane >> 4) + r;
+      if (m >= batch) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t n = n0 + 16 * j + (lane & 15);
+        if constexpr (DIRECT) {
+          if (out_dtype == HQQ_OUT_F16)
+            store_y<HQQ_OUT_F16>(y, m * N + n, acc[t][j][r]);
+          else
+            store_y<HQQ_OUT_F32>(y, m * N + n, acc[t][j][r]);
+        } else {
+          part[((int64_t)split * batch + m) * N + n] = acc[t][j][r];
+        }
+      }
+    }
+}
+
+
+// y = sum over the splits of the partial sums, in split order; 4 outputs per thread.
+__global__ void __launch_bounds__(256) k_splitk_sum(const float* __restrict__ part, int S, int64_t MN,
+                                                    void* __restrict__ y, int out_dtype) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + i);
+  for (int k = 1; k < S; ++k) s += *reinterpret_cast<const f32x4*>(part + (int64_t)k * MN + i);
+  if (out_dtype == HQQ_OUT_F16) {
+    const f16x2 a = {(_Float16)s[0], (_Float16)s[1]}, b = {(_Float16)s[2], (_Float16)s[3]};
+    *reinterpret_cast<uint2*>(reinterpret_cast<__half*>(y) + i) = make_uint2(as_u(a), as_u(b));
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(y) + i) = s;
+  }
+}
+
+// x [batch, K] -> xt: for k-step q (32 codes) and row group mg (16 rows), 64 lanes x 16 bytes,
+// lane l holding row 16 mg + (l & 15) (rows past the batch repeat the last row), codes
+// 32 q + 8 (l >> 4) .. +7.  A block moves a 16-row x 512-code tile through LDS: it reads
+// 1 KB row pieces and writes sixteen whole 1 KB fragments.
+constexpr int kTileCols = 512;
+__global__ void __launch_bounds__(256) k_tile_x(const __half* __restrict__ x, int64_t batch, int64_t K, int64_t MG,
+                                                u32x4* __restrict__ xt) {
+  __shared__ u32x4 tile[16][kTileCols / 8 + 1];
+  const int tid = threadIdx.x;
+  const int64_t mg = blockIdx.y, c0 = (int64_t)blockIdx.x * kTileCols;
+  {
+    const int r = tid >> 4, cp = (tid & 15) * 4;  // row, first 16-byte piece of four
+    const int64_t src_row = min(16 * mg + r, batch - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + src_row * K + c0) + cp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tile[r][cp + i] = src[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i, qb = e >> 6, l = e & 63;
+    xt[((c0 / 32 + qb) * MG + mg) * 64 + l] = tile[l & 15][4 * qb + (l >> 4)];
+  }
+}
+
+}  // namespace
+
+// Splits of K for the split GEMM: the smallest power of two that brings the grid to >= 256
+// blocks, keeping >= 2 chunks of 128 codes (an even number) per split.  0 = not applicable.
+int gemm_splits(int64_t N, int64_t K, int64_t batch) {
+  if (N % kSkBN != 0 || K % kTileCols != 0 || batch <= 0) return 0;
+  const int64_t tiles = (N / kSkBN) * ((batch + kSkBM - 1) / kSkBM);
+  int S = 1;
+  while (tiles * S < 256 && K % (2 * kSkBK * 2 * S) == 0) S *= 2;
+  return S;
+}
+
+namespace {
+size_t tiled_x_bytes(int64_t K, int64_t batch) {
+  const int64_t MG = (batch + kSkBM - 1) / kSkBM * (kSkBM / 16);  // whole blocks of batch rows
+  return ((size_t)MG * 16 * (size_t)K * 2 + 255) & ~size_t(255);
+}
+}  // namespace
+
+size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t batch) {
+  const int S = gemm_splits(N, K, batch);
+  if (S == 0) return 0;
+  return tiled_x_bytes(K, batch) + (S > 1 ? (size_t)S * (size_t)batch * (size_t)N * sizeof(float) : 0);
+}
+
+hipError_t launch_gemm_split(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                             int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
+                             hipStream_t st) {
+  const int S = gemm_splits(N, K, batch);
+  const int64_t MG = (batch + kSkBM - 1) / kSkBM * (kSkBM / 16);
+  u32x4* xt = reinterpret_cast<u32x4*>(workspace);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + tiled_x_bytes(K, batch));
+  {
+    hipLaunchKernelGGL(k_tile_x, dim3((unsigned)(K / kTileCols), (unsigned)MG), dim3(256), 0, st, x, batch, K, MG, xt);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t nb = (N / kSkBN) * S;  // blocks in a row of the grid: weight-row tiles x splits
+  const int xcd_map = nb % 8 == 0 && (S <= 8 ? (N / kSkBN) % (8 / S) == 0 : S % 8 == 0);
+  const dim3 grid((unsigned)nb, (unsigned)((batch + kSkBM - 1) / kSkBM));
+  const int64_t ks = K / S;
+  if (S == 1) {
+    if (gs == 64)
+      hipLaunchKernelGGL((k_gemm_sk<64, true>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks, xt, MG,
+                         batch, nullptr, y, y_dtype, xcd_map);
+    else
+      hipLaunchKernelGGL((k_gemm_sk<128, true>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks, xt, MG,
+                         batch, nullptr, y, y_dtype, xcd_map);
+    return hipGetLastError();
+  }
+  if (gs == 64)
+    hipLaunchKernelGGL((k_gemm_sk<64, false>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks, xt, MG,
+                       batch, part, nullptr, y_dtype, xcd_map);
+  else
+    hipLaunchKernelGGL((k_gemm_sk<128, false>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks, xt, MG,
+                       batch, part, nullptr, y_dtype, xcd_map);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t MN = batch * N;
+  hipLaunchKernelGGL(k_splitk_sum, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, st, part, S, MN, y,
+                     y_dtype);
+  return hipGetLastError();
+}
+
+}  // namespace hqq

@@ -244,15 +244,15 @@ __host__ __device__ constexpr int64_t valu_lds_bytes(int B, int64_t K) {
   return ((B * (K / 32) + 3) & ~int64_t(3)) * 4 + (int64_t)B * K * 2;
 }
 
-template <int B, int JMAX, int R>
-__global__ void __launch_bounds__(64 * kVWaves) k_gemv_valu(const uint8_t* __restrict__ packed,
+template <int B, int JMAX, int R, int D = (R < 2 ? R : 2), int W = kVWaves>
+__global__ void __launch_bounds__(64 * W) k_gemv_valu(const uint8_t* __restrict__ packed,
                                                            const __half* __restrict__ delta,
                                                            const __half* __restrict__ zero, int64_t N, int64_t K,
                                                            int gs_log2, int out_dtype, const __half* __restrict__ x,
                                                            void* __restrict__ y) {
-  constexpr int D = R < 2 ? R : 2;             // rows in flight per wave
+  static_assert(D >= 1 && D <= R, "rows in flight (D) must be within the wave's R rows");
   constexpr bool XREG = B * JMAX <= 4;         // x chunks held in registers
-  constexpr int NT = 64 * kVWaves;
+  constexpr int NT = 64 * W;                   // W waves per block
   extern __shared__ float lds[];
   const int nch = (int)(K / 32);               // 32-code chunks per row
   float* sxc = lds;                            // [B][nch] sum of x over each chunk
@@ -262,7 +262,7 @@ __global__ void __launch_bounds__(64 * kVWaves) k_gemv_valu(const uint8_t* __res
   const int64_t gpr = K >> gs_log2;            // groups per row
   const int cshift = gs_log2 - 5;              // chunk -> group within the row
   const int64_t TW = N / R;                    // waves in the grid
-  const int64_t gw = (int64_t)blockIdx.x * kVWaves + wave;
+  const int64_t gw = (int64_t)blockIdx.x * W + wave;
 
   // 1. this thread's 16-byte blocks of x (a block past the end re-reads the last one)
   constexpr int XR = (B * 64 * JMAX * 4 + NT - 1) / NT;
@@ -539,9 +539,10 @@ __global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ packed
     }
 }
 
-// Rows per wave of the VALU GEMV: as many as keep >= 256 blocks (one per compute unit).
-inline int valu_rows_per_wave(int64_t N) {
-  if (N % (8 * kVWaves) == 0 && N / (8 * kVWaves) >= 256) return 8;
+// Rows per wave of the VALU GEMV: batch 1 as many as keep >= 256 blocks (one per compute
+// unit); batch 2 at most 4 (measured: twice the VALU work per row wants more waves).
+inline int valu_rows_per_wave(int64_t N, int B) {
+  if (B == 1 && N % (8 * kVWaves) == 0 && N / (8 * kVWaves) >= 256) return 8;
   if (N / (4 * kVWaves) >= 256) return 4;  // N % 16 == 0
   return 2;
 }
@@ -551,7 +552,7 @@ hipError_t gemv_valu_j(const uint8_t* packed, const __half* delta, const __half*
                        const __half* x, void* y, int y_dtype, hipStream_t st) {
   const size_t lds = (size_t)valu_lds_bytes(B, K);
   const int gl = gs == 64 ? 6 : 7;
-  const int R = valu_rows_per_wave(N);
+  const int R = valu_rows_per_wave(N, B);
   const dim3 grid((unsigned)(N / (R * kVWaves))), block(64 * kVWaves);
   if (R == 8)
     hipLaunchKernelGGL((k_gemv_valu<B, JMAX, 8>), grid, block, lds, st, packed, delta, zero, N, K, gl, y_dtype, x, y);

@@ -49,6 +49,13 @@ hipError_t launch_gemv(const uint8_t* packed, const __half* delta, const __half*
 size_t gemv_lds_bytes(int64_t K, int group_size, int64_t batch);
 
 // Other stored formats (batch 1 or 2): 4-bit with axis-0 groups; 2-bit with axis-1 groups of 16.
+// Split-K fused GEMM (batched product): K splits for a shape (0 = not supported), the
+// workspace it needs (tiled x + fp32 partial sums), and the launch (tiling pass, GEMM, sum).
+int gemm_splits(int64_t N, int64_t K, int64_t batch);
+size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t batch);
+hipError_t launch_gemm_split(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                             int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
+                             hipStream_t st);
 hipError_t launch_gemv_ax0(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                            int group_size, const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t stream);
 size_t gemv_ax0_lds_bytes(int64_t K, int64_t batch);
