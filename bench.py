@@ -10,7 +10,7 @@ three 11008x4096 fp16 weights, N(0, 0.02) with 0.1 % +/-10 sigma outliers):
     hqq_gemm_w4a16 (split-K MFMA GEMM, workspace preallocated) at batch 256.
 Beside the step (in "legs", not in `value`): the same layer shapes on Laplace weights at 3-bit
 g64 and 2-bit g16, the 28672x8192 weight with axis-0 groups of 128, and the fused products over
-the 2-bit and axis-0 formats.
+the 3-bit, 2-bit and axis-0 formats.
 Inputs are resident in HBM before the timed region; the GEMV operands rotate over enough
 copies (> 1 GB) that the 256 MB last-level cache cannot hold them.
 
@@ -155,9 +155,12 @@ def config_legs(a, timed, stream, dev):
     for qp in lap["quant"]:
         leg, outs = quant_leg(lap["tensors"], qp, 3)
         legs["layers_laplace_%dbit_g%d" % (qp.nbits, qp.group_size)] = leg
+        t = lap["tensors"][4]
         if qp.nbits == 2:
-            t = lap["tensors"][4]
             gemv_leg("gemv_2bit_g16", outs[4], t.rows, t.cols, 2, 16, 1, t.rows * t.cols * (2 / 8 + 4 / 16))
+        else:
+            gemv_leg("gemv_3bit_g%d" % qp.group_size, outs[4], t.rows, t.cols, 3, qp.group_size, 1,
+                     4 * ((t.rows * t.cols + 9) // 10) + 4 * t.rows * t.cols / qp.group_size)
         del outs
         torch.cuda.empty_cache()
     log("config legs: 28672x8192 axis 0")

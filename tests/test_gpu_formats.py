@@ -1,6 +1,7 @@
 """GPU parity of the fused product for the other stored formats (hqq_gemv): 4-bit with
-axis-0 groups and 2-bit with axis-1 groups of 16, against the oracle's fp64 product of the
-same stored codes and fp16 metadata.
+axis-0 groups, 3-bit (ten codes per 32-bit word, rows starting inside words) and 2-bit with
+axis-1 groups of 16, against the oracle's fp64 product of the same stored codes and fp16
+metadata.
 
 Inputs are seeded synthetic codes and metadata (steps U(1e-3, 5e-2), zeros U(0, 2^b - 1),
 activations N(0, 1), all fp16), packed by the oracle; sizes span several lanes' chunks, a
@@ -64,6 +65,24 @@ def test_2bit_g16(N, K):
     _check(N, K, 2, 16, 1, (1, 2), seed=2000 + N + K)
 
 
+# 3-bit: every supported g; K with every residue of a row's start inside a word (K mod 10),
+# one and two rows per wave (N mod 8), K up to the largest span
+CASES_3B = [(16, 12, 208), (32, 64, 800), (64, 40, 4096), (64, 20, 1216), (128, 48, 1152), (64, 16, 5056),
+            (16, 100, 96)]
+
+
+@pytest.mark.parametrize("g,N,K", CASES_3B, ids=lambda v: str(v))
+def test_3bit(g, N, K):
+    _check(N, K, 3, g, 1, (1, 2), seed=2500 + g + N + K)
+
+
+def test_3bit_full_shape():
+    """The 11008 x 4096 projection of the 3-bit layer set (g = 64)."""
+    N, K = 11008, 4096
+    sel = np.sort(np.random.default_rng(9).choice(N, 512, replace=False))
+    _check(N, K, 3, 64, 1, (1, 2), seed=3003, rows_sel=sel)
+
+
 def test_axis0_full_shape():
     """The 70B-MLP shape of the axis-0 quantizer workload: 28672 x 8192, g = 128."""
     N, K = 28672, 8192
@@ -84,7 +103,7 @@ def test_unsupported_formats_rejected():
     pk = torch.zeros(4096, dtype=torch.uint8, device="cuda")
     md = torch.zeros(1024, dtype=torch.float16, device="cuda")
     x = torch.zeros((1, 128), dtype=torch.float16, device="cuda")
-    for nbits, g, axis in ((3, 64, 1), (2, 32, 1), (2, 16, 0)):
+    for nbits, g, axis in ((3, 32, 0), (2, 32, 1), (2, 16, 0)):
         with pytest.raises(hq.HQQError):
             hq.hqq_gemv(pk, md, md, 64, 128, nbits, g, axis, x)
     with pytest.raises(hq.HQQError):  # batch 3 is not fused for these formats
