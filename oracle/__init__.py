@@ -65,6 +65,7 @@ def _declare(lib):
         "hqq_oracle_dequant": (i32, [p, p, p, i64, i64, i32, i32, i32, p, p]),
         "hqq_oracle_gemv": (i32, [p, p, p, i64, i64, i32, p, i64, p, i64, p]),
         "hqq_oracle_gemv_fmt": (i32, [p, p, p, i64, i64, i32, i32, i32, p, i64, p, i64, p]),
+        "hqq_oracle_gemv_t": (i32, [p, p, p, i64, i64, i32, i32, i32, p, i64, p, i64, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -242,6 +243,27 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle gemv_fmt rejected the arguments (rc=%d)" % rc)
         return y
+
+    def gemv_t(self, packed, delta, zero, N, K, nbits, group_size, axis, dy, cols_sel=None) -> np.ndarray:
+        """dX = dY @ W_hat in fp64 (the input gradient of the product).  dy: [batch, N].
+        Returns [batch, n_sel] for the columns cols_sel (all K by default)."""
+        pk = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1)
+        dl = np.ascontiguousarray(delta, dtype=np.float64).reshape(-1)
+        zr = np.ascontiguousarray(zero, dtype=np.float64).reshape(-1)
+        dy = np.ascontiguousarray(dy, dtype=np.float64)
+        B = dy.shape[0]
+        if cols_sel is None:
+            sel, nsel = None, K
+        else:
+            sel = np.ascontiguousarray(cols_sel, dtype=np.int64)
+            nsel = sel.size
+        dx = np.empty((B, nsel), dtype=np.float64)
+        rc = self.lib.hqq_oracle_gemv_t(pk.ctypes.data, dl.ctypes.data, zr.ctypes.data, N, K, nbits, group_size, axis,
+                                        dy.ctypes.data, B, None if sel is None else sel.ctypes.data, nsel,
+                                        dx.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle gemv_t rejected the arguments (rc=%d)" % rc)
+        return dx
 
 
 _default: Oracle | None = None

@@ -495,6 +495,38 @@ int hqq_oracle_gemv_fmt(const uint8_t* packed, const double* delta, const double
   return 0;
 }
 
+/* O9: the input gradient of the forward product, dX = dY @ W_hat ("从压缩文件到一次前向": the
+ * forward is x @ W_hat^T; its gradient with respect to x multiplies by W_hat untransposed):
+ * dX[b, k] = sum over n in order of dY[b, n] * (q[n, k] - z_j) * delta_j, W_hat exact in fp64,
+ * for the columns k in cols_sel (all K when cols_sel is NULL; dX is [batch][n_sel]). */
+int hqq_oracle_gemv_t(const uint8_t* packed, const double* delta, const double* zero, int64_t N, int64_t K,
+                      int nbits, int g, int axis, const double* dy, int64_t batch, const int64_t* cols_sel,
+                      int64_t n_sel, double* dx) {
+  if (!valid_shape(N, K, nbits, g, axis) || nbits < 2 || nbits > 4 || batch < 0) return -1;
+  if (!cols_sel && n_sel != K) return -1;
+  double* wcol = (double*)malloc((size_t)N * sizeof(double));
+  if (!wcol) return -2;
+  for (int64_t c = 0; c < n_sel; c++) {
+    int64_t k = cols_sel ? cols_sel[c] : c;
+    if (k < 0 || k >= K) {
+      free(wcol);
+      return -1;
+    }
+    for (int64_t n = 0; n < N; n++) {
+      int64_t e = PLANT(18) ? (k * N + n) : (n * K + k);
+      int64_t j = group_of(e, N, K, g, axis);
+      wcol[n] = ((double)code_at(packed, e, nbits) - zero[j]) * delta[j];
+    }
+    for (int64_t b = 0; b < batch; b++) {
+      double acc = 0.0;
+      for (int64_t n = 0; n < N; n++) acc = acc + dy[b * N + n] * wcol[n];
+      dx[b * n_sel + c] = acc;
+    }
+  }
+  free(wcol);
+  return 0;
+}
+
 /* Array form of the fp16 rounding, for convenience. */
 void hqq_oracle_doubles_to_halves(const double* x, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; i++) out[i] = hqq_oracle_double_to_half(x[i]);

@@ -26,7 +26,8 @@
  * rounds and the solver; min-max RTN at iters = 0 with the Delta/2 error bound; ties to
  * even; degenerate groups; the zero update as the least-squares minimiser (brute force);
  * L2 monotonicity without the shrink; pack/unpack exhaustively and the 4.5 bpw size;
- * dequantisation and the GEMV through one-hot and linearity checks; binary16
+ * dequantisation and the GEMV through one-hot and linearity checks; the input
+ * gradient through the adjoint identity with the forward product and one-hot rows; binary16
  * conversions exhaustively against numpy.  Parity unpinned (readings, no value on the
  * page to check against): the shrink formula itself, the stop rule's rollback target
  * and tie handling, the summation order, and the solver's values on the full-size
@@ -74,6 +75,11 @@ int hqq_oracle_gemv(const uint8_t* packed, const double* delta, const double* ze
 int hqq_oracle_gemv_fmt(const uint8_t* packed, const double* delta, const double* zero, int64_t N, int64_t K,
                         int nbits, int g, int axis, const double* x, int64_t batch, const int64_t* rows_sel,
                         int64_t n_sel, double* y);
+/* O9: dX [batch][n_sel] = dY [batch][N] @ W_hat [N][K] for the selected columns (the input
+ * gradient of the forward product). */
+int hqq_oracle_gemv_t(const uint8_t* packed, const double* delta, const double* zero, int64_t N, int64_t K,
+                      int nbits, int g, int axis, const double* dy, int64_t batch, const int64_t* cols_sel,
+                      int64_t n_sel, double* dx);
 
 #ifdef __cplusplus
 }

@@ -448,6 +448,35 @@ def pin_gemv_formats(o):
             assert np.array_equal(y, o.gemv(pk, delta, zero, N, K, g, x))
 
 
+def pin_gemv_transposed(o):
+    """The input gradient dX = dY W_hat (every stored format): the adjoint of the forward
+    product (<dY, W_hat x> = <dY W_hat, x> with the forward product computed by its own code
+    path), one-hot rows of dY return rows of W_hat exactly, and selected columns equal the full
+    result's columns."""
+    r = _rng(53)
+    cases = [(4, 64, 1, 16, 256), (4, 128, 0, 256, 96), (2, 16, 1, 12, 128), (3, 64, 1, 9, 192), (3, 16, 0, 48, 40)]
+    for nbits, g, axis, N, K in cases:
+        G = N * K // g
+        codes = r.integers(0, 2 ** nbits, (N, K)).astype(np.uint8)
+        delta = r.uniform(1e-3, 0.05, G).astype(np.float16).astype(np.float64)
+        zero = r.uniform(0, 2 ** nbits - 1, G).astype(np.float16).astype(np.float64)
+        pk = o.pack(codes, nbits)
+        dy = r.normal(0, 1, (3, N))
+        x = r.normal(0, 1, (1, K))
+        dx = o.gemv_t(pk, delta, zero, N, K, nbits, g, axis, dy)
+        y = o.gemv_fmt(pk, delta, zero, N, K, nbits, g, axis, x)  # [1, N]
+        lhs = dy @ y[0]
+        rhs = dx @ x[0]
+        assert np.allclose(lhs, rhs, rtol=1e-10, atol=1e-10), (nbits, g, axis)
+        w64, _ = o.dequant(pk, delta, zero, N, K, nbits, g, axis)
+        w64 = w64.reshape(N, K)
+        onehot = np.zeros((2, N))
+        onehot[0, 0] = onehot[1, N - 1] = 1.0
+        assert (o.gemv_t(pk, delta, zero, N, K, nbits, g, axis, onehot) == w64[[0, N - 1]]).all(), (nbits, g, axis)
+        sel = np.array([K - 1, 0, K // 2])
+        assert np.array_equal(o.gemv_t(pk, delta, zero, N, K, nbits, g, axis, dy, cols_sel=sel), dx[:, sel])
+
+
 def pin_mae_definition(o):
     """Round 0's MAE is the mean |W - W_hat| of the min-max start (the dequantisation of the
     iters=0 codes with fp64 metadata)."""

@@ -23,6 +23,7 @@ PLANTS = {
     15: "scale not limited to 2e4",
     16: "sums accumulated sequentially instead of pairwise",
     17: "product for all formats takes axis-0 groups as axis-1 runs",
+    18: "input gradient multiplies by the transposed weight (column index as row)",
 }
 
 
