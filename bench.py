@@ -8,7 +8,8 @@ three 11008x4096 fp16 weights, N(0, 0.02) with 0.1 % +/-10 sigma outliers):
   * hqq_dequantize of every layer back to fp16 (the round trip);
   * the fused product on an 8192x8192 4-bit g64 weight: hqq_gemv_w4a16 at batch 1 and 8 (GEMV),
     hqq_gemm_w4a16 (split-K MFMA GEMM, workspace preallocated) at batch 256.
-Beside the step (in "legs", not in `value`): the same layer shapes on Laplace weights at 3-bit
+Beside the step (in "legs", not in `value`): the input gradient dX = dY W_hat on the 8192x8192
+weight at batch 256 (hqq_gemm_w4a16_dx), the same layer shapes on Laplace weights at 3-bit
 g64 and 2-bit g16, the 28672x8192 weight with axis-0 groups of 128, and the fused products over
 the 3-bit, 2-bit and axis-0 formats.
 Inputs are resident in HBM before the timed region; the GEMV operands rotate over enough
@@ -326,6 +327,18 @@ def main():
         legs["gemv_b%d" % b] = {"us": tg * 1e6, "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM,
                                 "TFLOP/s": flops / tg / 1e12, "frac_mfma_f16": flops / tg / PEAK_FP16_MFMA,
                                 "bytes": byt}
+
+    # the input gradient dX = dY W_hat (training through the frozen weight) at batch 256
+    dx_ws = torch.empty(max(hq.hqq_gemm_dx_workspace_bytes(GN, GK, 256), 16), dtype=torch.uint8, device=dev)
+    DX = torch.empty((256, GK), dtype=torch.float16, device=dev)
+    DY = torch.from_numpy(synth.activations(256, GN, gspec["x_seed"] + 1)).to(dev)
+
+    def dxl(r):
+        pk, d, z = copies[r % ncopy]
+        hq.hqq_gemm_w4a16_dx(pk, d, z, GN, GK, gq.group_size, DY, out=DX, workspace=dx_ws)
+    tg = timed(dxl, 2 * ncopy)
+    flops = 2.0 * 256 * GN * GK
+    legs["dx_b256"] = {"us": tg * 1e6, "TFLOP/s": flops / tg / 1e12, "frac_mfma_f16": flops / tg / PEAK_FP16_MFMA}
 
     if not a.no_extra_legs:
         legs.update(config_legs(a, timed, stream, dev))

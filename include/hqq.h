@@ -179,6 +179,23 @@ int hqq_gemm_w4a16(const void* packed, const void* delta_fp16, const void* zero_
                    size_t workspace_bytes, void* stream);
 
 /*
+ * Input gradient of the fused product, for training through frozen quantised weights
+ * ("从压缩文件到一次前向": the forward is y = x @ W_hat^T, so dL/dx = dL/dy @ W_hat):
+ *   dX[b, k] = sum_n dY[b, n] * (q[n, k] - zero[n, k/g]) * delta[n, k/g].
+ *   packed, delta_fp16, zero_fp16, group_size  as hqq_gemm_w4a16 (W [N, K], 4-bit, axis 1).
+ *   dy_fp16     in  fp16 [batch, N] row-major.
+ *   dx          out [batch, K] row-major, dx_dtype HQQ_OUT_F16 or HQQ_OUT_F32.
+ *   workspace   at least hqq_gemm_dx_workspace_bytes(N, K, batch) bytes, as hqq_gemm_w4a16.
+ * The same split MFMA kernel with the weight tile transposed in LDS (the packed format is read
+ * as stored); fp32 accumulation, splits of N added in a fixed order.  K must be a multiple of
+ * 128 and N of 512; other shapes return HQQ_ERR_UNSUPPORTED.
+ */
+size_t hqq_gemm_dx_workspace_bytes(int64_t N, int64_t K, int64_t batch);
+int hqq_gemm_w4a16_dx(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K,
+                      int group_size, const void* dy_fp16, int64_t batch, void* dx, int dx_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
  * The same fused product for the other stored formats ("从压缩文件到一次前向";
  * "axis 不是一个无关紧要的开关" for axis 0; "为什么一定要分组" for the containers):
  *   y[b, n] = sum_k x[b, k] * (q[n, k] - zero[j]) * delta[j],  j the group of code (n, k)

@@ -291,3 +291,44 @@ def test_gemm_split_errors():
                                                                                   device="cuda"))
     with pytest.raises(hq.HQQError):  # N not a multiple of 128
         hq.hqq_gemm_w4a16(pk, md, md, 64, 512, 64, x)
+
+
+# ---------------------------------------------------------------------------- input gradient
+
+@pytest.mark.parametrize("g", [64, 128])
+@pytest.mark.parametrize("N,K,batch", [(512, 256, 9), (1024, 384, 100), (512, 1024, 256), (2048, 128, 300),
+                                       (1536, 512, 37)])
+def test_gemm_dx_parity(g, N, K, batch):
+    """dX = dY @ W_hat through the transposed split GEMM against the oracle's input gradient:
+    one to sixteen splits of N, ragged batches over one and two 256-row blocks."""
+    import weight_only_quantization_amd as hq
+    torch = torch_dev()
+    say("gemm dx", g, N, K, batch)
+    o = oracle.get()
+    packed, d16, z16 = gemv_inputs(N, K, g, seed=6000 + N + K)
+    dy = synth.activations(batch, N, seed=19)
+    ref = o.gemv_t(packed, d16, z16, N, K, 4, g, 1, dy.astype(np.float64))
+    scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref ** 2)))
+    for out_dtype in (torch.float32, torch.float16):
+        dx = hq.hqq_gemm_w4a16_dx(torch.from_numpy(packed).cuda(), torch.from_numpy(d16).cuda(),
+                                  torch.from_numpy(z16).cuda(), N, K, g, torch.from_numpy(dy).cuda(),
+                                  out_dtype=out_dtype).float().cpu().numpy().astype(np.float64)
+        err = float(np.max(np.abs(dx - ref) / scale))
+        assert err <= GEMV_TOL, "max rel err %.3g" % err
+
+
+def test_gemm_dx_adjoint():
+    """<dY, x W_hat^T> = <dY W_hat, x> between the GPU forward product and the GPU input gradient
+    (both fp32 outputs), to fp32 accumulation error."""
+    import weight_only_quantization_amd as hq
+    torch = torch_dev()
+    N, K, g = 1024, 512, 64
+    packed, d16, z16 = gemv_inputs(N, K, g, seed=77)
+    pk, dl, zr = (torch.from_numpy(a).cuda() for a in (packed, d16, z16))
+    x = torch.from_numpy(synth.activations(16, K, seed=21)).cuda()
+    dy = torch.from_numpy(synth.activations(16, N, seed=22)).cuda()
+    y = hq.hqq_gemm_w4a16(pk, dl, zr, N, K, g, x, out_dtype=torch.float32).double()
+    dx = hq.hqq_gemm_w4a16_dx(pk, dl, zr, N, K, g, dy, out_dtype=torch.float32).double()
+    lhs = (dy.double() * y).sum(dim=1)
+    rhs = (dx * x.double()).sum(dim=1)
+    assert torch.allclose(lhs, rhs, rtol=1e-4, atol=1e-3 * float(lhs.abs().max()))

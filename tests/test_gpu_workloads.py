@@ -142,3 +142,11 @@ def test_workload_gemv():
                 err = float(np.max(np.abs(y[:, sel] - yr) / scale))
                 say("    split GEMM %s max rel err %.3g" % (out_dtype, err))
                 assert err <= GEMV_TOL
+                # input gradient dX = dY W_hat with dY = the same activations (N = K here)
+                dx = hq.hqq_gemm_w4a16_dx(pk_d, d_d, z_d, N, K, q.group_size, torch.from_numpy(x).cuda(),
+                                          out_dtype=out_dtype).float().cpu().numpy().astype(np.float64)
+                dxr = o.gemv_t(packed, d16, z16, N, K, 4, q.group_size, 1, x.astype(np.float64), cols_sel=sel)
+                sc = np.maximum(np.abs(dxr), np.sqrt(np.mean(dxr ** 2)))
+                err = float(np.max(np.abs(dx[:, sel] - dxr) / sc))
+                say("    input gradient %s max rel err %.3g" % (out_dtype, err))
+                assert err <= GEMV_TOL

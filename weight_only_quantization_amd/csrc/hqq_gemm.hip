@@ -20,6 +20,9 @@
 //     other wave reads them), one chunk ahead;
 //   * the packed codes of chunk c + 2 are loaded while chunk c is multiplied.
 // One barrier per chunk.
+//
+// The same kernel, transposed, computes the input gradient dX = dY @ W_hat: output columns k of
+// the weight, contraction over its rows (the dequantised tile is stored transposed in LDS).
 
 #include "hqq_gemv_common.h"
 
@@ -51,7 +54,13 @@ __device__ __forceinline__ u32x4 wq8(unsigned w, float ds24, float ds20, float z
 // memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int GS, bool DIRECT>
+// TRANS = false: y [batch, N] = x [batch, K] @ W_hat^T (the forward product; output index n,
+//   contraction over k).  TRANS = true: dX [batch, K] = dY [batch, N] @ W_hat (its input
+//   gradient; output index k, contraction over the weight rows n).  W is [N, K] in both.
+// The LDS tile always holds W_hat as [output index][contraction index]; the transposed form
+// writes it with an XOR swizzle of 16-byte blocks (block ^ 4 (output >> 5)), which keeps both
+// its dword stores and the 16-byte fragment reads free of bank conflicts.
+template <int GS, bool DIRECT, bool TRANS>
 __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restrict__ packed, const __half* __restrict__ delta,
                                                  const __half* __restrict__ zero, int64_t N, int64_t K, int64_t ks,
                                                  const u32x4* __restrict__ xt, int64_t MG, int64_t batch,
@@ -59,12 +68,13 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
                                                  int xcd_map) {
   extern __shared__ _Float16 wt[];  // [2][kSkBN][kSkRow]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t NO = TRANS ? K : N, KC = TRANS ? N : K;  // output and contraction lengths
   // Block b of a row of the grid runs on XCD b mod 8 (round-robin dispatch).  With xcd_map,
   // the S splits get 8 / S XCDs each (S <= 8) or each XCD gets S / 8 splits, so one XCD's L2
   // holds only its splits' columns of x.
   int tile, split;
   {
-    const int b = blockIdx.x, nb = gridDim.x, S = (int)(K / ks);
+    const int b = blockIdx.x, nb = gridDim.x, S = (int)(KC / ks);
     if (xcd_map) {
       const int xcd = b & 7, r = b >> 3;
       if (S <= 8) {
@@ -84,16 +94,30 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
   const int64_t n0 = (int64_t)tile * kSkBN, m0 = (int64_t)blockIdx.y * kSkBM, k0 = (int64_t)split * ks;
   const int nch = (int)(ks / kSkBK);
 
-  // W staging: thread -> weight rows wr and 64 + wr, codes 32 wq .. 32 wq + 31 of each chunk
-  // (16 bytes each): one load instruction of a wave spans 16 rows (each row of a 4-bit weight
-  // with K = 8192 is its own 4 KB page, and an instruction's distinct pages are translated one
-  // after another)
+  // W staging.  Forward: thread -> weight rows wr and 64 + wr (output rows of the tile), codes
+  // 32 wq .. 32 wq + 31 of each chunk.  Transposed: thread -> weight rows 2 wr and 2 wr + 1 of
+  // the chunk (contraction), codes 32 wq .. +31 of the tile's output columns.  16 bytes per
+  // row: one load instruction of a wave spans 16 (32) rows (each row of a 4-bit weight with
+  // K = 8192 is its own 4 KB page, and an instruction's distinct pages are translated one after
+  // another)
   const int wr = tid >> 2, wq = tid & 3;
-  const uint8_t* wsrc = packed + (n0 + wr) * (K / 2) + k0 / 2 + 16 * wq;
-  const int64_t wstride = 64 * (K / 2);  // second row pass
-  const __half* dsrc = delta + (n0 + wr) * (K / GS);
-  const __half* zsrc = zero + (n0 + wr) * (K / GS);
-  const int64_t mstride = 64 * (K / GS);
+  const int64_t G_row = K / GS;  // groups per weight row
+  const uint8_t* wsrc;
+  const __half *dsrc, *zsrc;
+  int64_t wstride, mstride, wchunk, mchunk;
+  if constexpr (TRANS) {
+    wsrc = packed + (k0 + 2 * wr) * (K / 2) + (n0 + 32 * wq) / 2;
+    dsrc = delta + (k0 + 2 * wr) * G_row + (n0 + 32 * wq) / GS;
+    zsrc = zero + (k0 + 2 * wr) * G_row + (n0 + 32 * wq) / GS;
+    wstride = K / 2, mstride = G_row;                       // the second row
+    wchunk = (int64_t)kSkBK * (K / 2), mchunk = (int64_t)kSkBK * G_row;  // the next chunk of rows
+  } else {
+    wsrc = packed + (n0 + wr) * (K / 2) + k0 / 2 + 16 * wq;
+    dsrc = delta + (n0 + wr) * G_row + (k0 + 32 * wq) / GS;
+    zsrc = zero + (n0 + wr) * G_row + (k0 + 32 * wq) / GS;
+    wstride = 64 * (K / 2), mstride = 64 * G_row;           // the second row pass
+    wchunk = kSkBK / 2, mchunk = kSkBK / GS;                 // the next 128 codes
+  }
   _Float16* wdst = wt + wr * kSkRow + 32 * wq;
 
   // A operand from the tiled copy of x: the 16 x 32 fragment of row group mg and k-step q is
@@ -105,12 +129,11 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
 
   auto load_w = [&](int c, u32x4 (&wv)[2], unsigned (&dm)[2], unsigned (&zm)[2]) {
     const int cc = min(c, nch - 1);  // past the end: reload the last chunk (never used)
-    const int64_t gi = (k0 + (int64_t)kSkBK * cc + 32 * wq) / GS;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      wv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + p * wstride + 64 * cc));
-      dm[p] = __half_as_ushort(dsrc[p * mstride + gi]);
-      zm[p] = __half_as_ushort(zsrc[p * mstride + gi]);
+      wv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + p * wstride + cc * wchunk));
+      dm[p] = __half_as_ushort(dsrc[p * mstride + cc * mchunk]);
+      zm[p] = __half_as_ushort(zsrc[p * mstride + cc * mchunk]);
     }
   };
   // A operand of k-step q (32 codes) into one of four register slots
@@ -129,12 +152,28 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
     const float z = __half2float(__ushort_as_half((unsigned short)zm));
     return WConst{z * d, d * 16777216.0f, d * 1048576.0f};
   };
-  // words 2 h, 2 h + 1 of row pass p -> W_hat into LDS buffer `buf`
-  auto stage2 = [&](int buf, const u32x4 (&wv)[2], const WConst (&k)[2], int p, int h) {
-    _Float16* dst = wdst + buf * (kSkBN * kSkRow) + p * 64 * kSkRow;
+  // a quarter (k-step s) of the thread's staging for the next chunk -> LDS buffer `buf`.
+  // Forward: words 2h, 2h + 1 of row pass p = s / 2 (h = s mod 2), 16-byte stores.  Transposed:
+  // word s of both rows, the two rows' values of one output column paired into a dword.
+  auto stage_step = [&](int buf, const u32x4 (&wv)[2], const WConst (&k)[2], int s) {
+    if constexpr (TRANS) {
+      const u32x4 r0 = wq8(wv[0][s], k[0].ds24, k[0].ds20, k[0].zd);
+      const u32x4 r1 = wq8(wv[1][s], k[1].ds24, k[1].ds20, k[1].zd);
+      _Float16* base = wt + buf * (kSkBN * kSkRow);
 #pragma unroll
-    for (int i = 2 * h; i < 2 * h + 2; ++i)
-      *reinterpret_cast<u32x4*>(dst + 8 * i) = wq8(wv[p][i], k[p].ds24, k[p].ds20, k[p].zd);
+      for (int e = 0; e < 8; ++e) {
+        const int o = 32 * wq + 8 * s + e;  // output column in the tile; contraction 2 wr, 2 wr + 1
+        const unsigned v = __builtin_amdgcn_perm(r1[e >> 1], r0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+        const int blk = (wr >> 2) ^ (4 * (o >> 5));
+        *reinterpret_cast<unsigned*>(base + o * kSkRow + 8 * blk + 2 * (wr & 3)) = v;
+      }
+    } else {
+      const int p = s >> 1, h = s & 1;
+      _Float16* dst = wdst + buf * (kSkBN * kSkRow) + p * 64 * kSkRow;
+#pragma unroll
+      for (int i = 2 * h; i < 2 * h + 2; ++i)
+        *reinterpret_cast<u32x4*>(dst + 8 * i) = wq8(wv[p][i], k[p].ds24, k[p].ds20, k[p].zd);
+    }
   };
 
   f32x4 acc[4][8];
@@ -157,19 +196,24 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
     load_w(c + 2, wn, dmn, zmn);
     const WConst k[2] = {wconst(dmp[0], zmp[0]), wconst(dmp[1], zmp[1])};
     const _Float16* src = wt + buf * (kSkBN * kSkRow) + (lane & 15) * kSkRow + 8 * (lane >> 4);
+    // fragment j, k-step s: 16-byte block 4s + (lane >> 4) of its row (swizzled when TRANS)
+    auto bfrag = [&](int j, int s) {
+      const int sb = TRANS ? (s ^ (j >> 1)) : s;
+      return *reinterpret_cast<const f16x8*>(src + 16 * j * kSkRow + 32 * sb);
+    };
     f16x8 B[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) B[j] = *reinterpret_cast<const f16x8*>(src + 16 * j * kSkRow);
+    for (int j = 0; j < 8; ++j) B[j] = bfrag(j, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      stage2(buf ^ 1, wp, k, s >> 1, s & 1);
+      stage_step(buf ^ 1, wp, k, s);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, as[s][t]), B[j], acc[t][j], 0, 0, 0);
-        if (s < 3) B[j] = *reinterpret_cast<const f16x8*>(src + 16 * j * kSkRow + 32 * (s + 1));
+        if (s < 3) B[j] = bfrag(j, s + 1);
       }
       load_a(4 * c + s + 4, as[s]);  // into the registers just read: no copy at the loop edge
       __builtin_amdgcn_sched_barrier(0);
@@ -185,7 +229,7 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
   {
     const WConst k[2] = {wconst(dma[0], zma[0]), wconst(dma[1], zma[1])};
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) stage2(0, wa, k, s4 >> 1, s4 & 1);
+    for (int s4 = 0; s4 < 4; ++s4) stage_step(0, wa, k, s4);
   }
   load_w(1, wa, dma, zma);
 #pragma unroll
@@ -211,11 +255,11 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
         const int64_t n = n0 + 16 * j + (lane & 15);
         if constexpr (DIRECT) {
           if (out_dtype == HQQ_OUT_F16)
-            store_y<HQQ_OUT_F16>(y, m * N + n, acc[t][j][r]);
+            store_y<HQQ_OUT_F16>(y, m * NO + n, acc[t][j][r]);
           else
-            store_y<HQQ_OUT_F32>(y, m * N + n, acc[t][j][r]);
+            store_y<HQQ_OUT_F32>(y, m * NO + n, acc[t][j][r]);
         } else {
-          part[((int64_t)split * batch + m) * N + n] = acc[t][j][r];
+          part[((int64_t)split * batch + m) * NO + n] = acc[t][j][r];
         }
       }
     }
@@ -287,43 +331,59 @@ size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t batch) {
   return tiled_x_bytes(K, batch) + (S > 1 ? (size_t)S * (size_t)batch * (size_t)N * sizeof(float) : 0);
 }
 
-hipError_t launch_gemm_split(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
-                             int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
-                             hipStream_t st) {
-  const int S = gemm_splits(N, K, batch);
+namespace {
+// One split product: tile the A operand (x, or dY for the input gradient) into fragments, the
+// split GEMM, and the sum over splits.  NO = output length (N, or K), KC = contraction (K, or N).
+template <bool TRANS>
+hipError_t launch_split(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int gs,
+                        const __half* a, int64_t batch, void* y, int y_dtype, void* workspace, hipStream_t st) {
+  const int64_t NO = TRANS ? K : N, KC = TRANS ? N : K;
+  const int S = gemm_splits(NO, KC, batch);
   const int64_t MG = (batch + kSkBM - 1) / kSkBM * (kSkBM / 16);
   u32x4* xt = reinterpret_cast<u32x4*>(workspace);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + tiled_x_bytes(K, batch));
-  {
-    hipLaunchKernelGGL(k_tile_x, dim3((unsigned)(K / kTileCols), (unsigned)MG), dim3(256), 0, st, x, batch, K, MG, xt);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int64_t nb = (N / kSkBN) * S;  // blocks in a row of the grid: weight-row tiles x splits
-  const int xcd_map = nb % 8 == 0 && (S <= 8 ? (N / kSkBN) % (8 / S) == 0 : S % 8 == 0);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + tiled_x_bytes(KC, batch));
+  hipLaunchKernelGGL(k_tile_x, dim3((unsigned)(KC / kTileCols), (unsigned)MG), dim3(256), 0, st, a, batch, KC, MG, xt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nb = (NO / kSkBN) * S;  // blocks in a row of the grid: output tiles x splits
+  const int xcd_map = nb % 8 == 0 && (S <= 8 ? (NO / kSkBN) % (8 / S) == 0 : S % 8 == 0);
   const dim3 grid((unsigned)nb, (unsigned)((batch + kSkBM - 1) / kSkBM));
-  const int64_t ks = K / S;
+  const int64_t ks = KC / S;
+  void* out = S == 1 ? y : nullptr;
+  float* pw = S == 1 ? nullptr : part;
   if (S == 1) {
     if (gs == 64)
-      hipLaunchKernelGGL((k_gemm_sk<64, true>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks, xt, MG,
-                         batch, nullptr, y, y_dtype, xcd_map);
+      hipLaunchKernelGGL((k_gemm_sk<64, true, TRANS>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks,
+                         xt, MG, batch, pw, out, y_dtype, xcd_map);
     else
-      hipLaunchKernelGGL((k_gemm_sk<128, true>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks, xt, MG,
-                         batch, nullptr, y, y_dtype, xcd_map);
+      hipLaunchKernelGGL((k_gemm_sk<128, true, TRANS>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K,
+                         ks, xt, MG, batch, pw, out, y_dtype, xcd_map);
     return hipGetLastError();
   }
   if (gs == 64)
-    hipLaunchKernelGGL((k_gemm_sk<64, false>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks, xt, MG,
-                       batch, part, nullptr, y_dtype, xcd_map);
+    hipLaunchKernelGGL((k_gemm_sk<64, false, TRANS>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks,
+                       xt, MG, batch, pw, out, y_dtype, xcd_map);
   else
-    hipLaunchKernelGGL((k_gemm_sk<128, false>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks, xt, MG,
-                       batch, part, nullptr, y_dtype, xcd_map);
-  const hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL((k_gemm_sk<128, false, TRANS>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K,
+                       ks, xt, MG, batch, pw, out, y_dtype, xcd_map);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t MN = batch * N;
-  hipLaunchKernelGGL(k_splitk_sum, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, st, part, S, MN, y,
-                     y_dtype);
+  const int64_t MN = batch * NO;
+  hipLaunchKernelGGL(k_splitk_sum, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, st, part, S, MN, y, y_dtype);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_split(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                             int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
+                             hipStream_t st) {
+  return launch_split<false>(packed, delta, zero, N, K, gs, x, batch, y, y_dtype, workspace, st);
+}
+
+hipError_t launch_gemm_dx(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                          int gs, const __half* dy, int64_t batch, void* dx, int dx_dtype, void* workspace,
+                          hipStream_t st) {
+  return launch_split<true>(packed, delta, zero, N, K, gs, dy, batch, dx, dx_dtype, workspace, st);
 }
 
 }  // namespace hqq

@@ -49,13 +49,19 @@ hipError_t launch_gemv(const uint8_t* packed, const __half* delta, const __half*
 size_t gemv_lds_bytes(int64_t K, int group_size, int64_t batch);
 
 // Other stored formats (batch 1 or 2): 4-bit with axis-0 groups; 2-bit with axis-1 groups of 16.
-// Split-K fused GEMM (batched product): K splits for a shape (0 = not supported), the
-// workspace it needs (tiled x + fp32 partial sums), and the launch (tiling pass, GEMM, sum).
-int gemm_splits(int64_t N, int64_t K, int64_t batch);
-size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t batch);
+// Split-K fused GEMM (batched product): splits of the contraction for an output length NO and a
+// contraction length KC (0 = not supported), the workspace it needs (tiled A operand + fp32
+// partial sums), and the launch (tiling pass, GEMM, sum).
+int gemm_splits(int64_t NO, int64_t KC, int64_t batch);
+size_t gemm_workspace_bytes(int64_t NO, int64_t KC, int64_t batch);
 hipError_t launch_gemm_split(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                              int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
                              hipStream_t st);
+// Input gradient dX [batch, K] = dY [batch, N] @ W_hat with the same kernel transposed; its
+// workspace is gemm_workspace_bytes(K, N, batch) (output length first).
+hipError_t launch_gemm_dx(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                          int gs, const __half* dy, int64_t batch, void* dx, int dx_dtype, void* workspace,
+                          hipStream_t st);
 // Fused product with 3-bit codes (axis 1, batch 1-2): shapes it takes, LDS bytes, launch.
 bool gemv_3b_supported(int64_t K, int g);
 size_t gemv_3b_lds_bytes(int64_t K, int64_t batch);
