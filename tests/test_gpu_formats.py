@@ -68,7 +68,7 @@ def test_2bit_g16(N, K):
 # 3-bit: every supported g; K with every residue of a row's start inside a word (K mod 10),
 # one and two rows per wave (N mod 8), K up to the largest span
 CASES_3B = [(16, 12, 208), (32, 64, 800), (64, 40, 4096), (64, 20, 1216), (128, 48, 1152), (64, 16, 5056),
-            (16, 100, 96)]
+            (16, 100, 96), (256, 24, 8192), (64, 4, 640)]
 
 
 @pytest.mark.parametrize("g,N,K", CASES_3B, ids=lambda v: str(v))

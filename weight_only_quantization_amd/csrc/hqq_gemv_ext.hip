@@ -360,115 +360,99 @@ __global__ void __launch_bounds__(64 * k2Waves) k_gemv_2b(const uint8_t* __restr
 
 // ------------------------------------------------------------------------------------------
 // Axis 1, 3-bit (ten codes per 32-bit word over the flat index, so a row starts inside a word:
-// row n begins at code o = nK mod 10 of word nK / 10).  A wave takes one row at a time; lane l
-// takes the words l + 64j of the row's span, word i holding the codes of k = 10i - o .. +9.
-// x is staged in LDS with zero halves before and after the row, so codes of the neighbouring
-// rows in the two end words multiply zeros.  A word's ten codes span at most two groups
-// (g >= 16); for g dividing 640 the position where the second group starts is the same for a
-// lane in every word of the row, so its half masks are formed once per row.  Codes become fp16
-// subnormal pairs (c_2u, c_2u+1) = bits 6u.. and 6u+3.. of the word; per segment
-// acc += delta (P 2^24 - z S) with P = sum x c 2^-24 and S = sum x (v_dot2_f32_f16).
+// code (n, k) is slot f mod 10 of word f / 10, f = nK + k).  A wave takes one row at a time;
+// lane l takes the 8-code blocks m = l + 64j of the row (codes 8m .. 8m + 7, all in one group
+// since g >= 16).  Their 24 bits lie in words q = f / 10 and q + 1 (f = nK + 8m): the 30-bit
+// payloads concatenated into 64 bits and shifted right by 3 (f mod 10) put c0..c7 at bits
+// 0..23; (v & 0xFFF) | ((v << 4) & 0xFFF0000) then gives the fp16 subnormal pairs (c0, c4),
+// 8 (c1, c5), 64 (c2, c6) and, after >> 9, (c3, c7) with one AND each.  x is staged per block
+// in that pair order with 1, 1/8, 1/64, 1 on the four slots, and the block sums of x beside
+// it; per block acc += delta 2^24 (P - z 2^-24 S) (v_dot2_f32_f16, fp32 sums).
 // ------------------------------------------------------------------------------------------
 constexpr int k3Waves = 4;
-constexpr int k3Pad = 16;  // zero halves on each side of a staged x row
 
-template <int B, int GS, int J, int R>
+template <int B, int J, int R>
 __global__ void __launch_bounds__(64 * k3Waves) k_gemv_3b(const uint32_t* __restrict__ packed,
                                                          const __half* __restrict__ delta,
                                                          const __half* __restrict__ zero, int64_t N, int64_t K,
-                                                         int out_dtype, const __half* __restrict__ x,
+                                                         int gs_log2, int out_dtype, const __half* __restrict__ x,
                                                          void* __restrict__ y) {
-  static_assert(640 % GS == 0 && GS >= 16, "the in-word group split must repeat every 64 words");
-  constexpr int D = R < 2 ? R : 2;                 // rows in flight per wave
-  constexpr int GPL = (640 * J / GS + 2 + 63) / 64;  // a row's groups per lane (K <= 640 J - 20)
+  constexpr int D = R < 2 ? R : 2;  // rows in flight per wave
   extern __shared__ float lds3[];
-  unsigned* meta = reinterpret_cast<unsigned*>(lds3);  // [waves][64 GPL] (delta | zero << 16)
-  _Float16* xs = reinterpret_cast<_Float16*>(meta + k3Waves * 64 * GPL);  // [B][K + 2 pad], zero pads
+  const int nb8 = (int)(K / 8);                              // 8-code blocks per row
+  float* sxb = lds3;                                         // [B][nb8] block sums of x
+  uint4* xq = reinterpret_cast<uint4*>(sxb + ((B * nb8 + 3) & ~3));  // [B][nb8] staged x pairs
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t XS = K + 2 * k3Pad;
-  const int G = (int)(K / GS);  // groups per row
+  const int64_t G = K >> gs_log2;  // groups per row
   const int64_t TW = N / R;
   const int64_t gw = (int64_t)blockIdx.x * k3Waves + wave;
-  unsigned* wmeta = meta + wave * 64 * GPL;
 
-  // the first D rows' words, and their groups' steps and zeros (lane l: groups l + 64 m)
-  unsigned wv[D][J], dm[D][GPL], zm[D][GPL];
+  // the first D rows: two words per block, the block's step and zero
+  unsigned w0v[D][J], w1v[D][J], dmv[D][J], zmv[D][J];
+  const int64_t nwt = (N * K + 9) / 10;  // words of the tensor
   auto issue = [&](int s, int64_t n) {
-    const int64_t f0 = n * K;
-    const int o = (int)(f0 % 10);
-    const int64_t w0 = f0 / 10;
-    const int nw = (o + (int)K + 9) / 10;
+    const int64_t f0 = n * K, q0 = f0 / 10;
+    const int ph0 = (int)(f0 - 10 * q0);
 #pragma unroll
-    for (int j = 0; j < J; ++j) wv[s][j] = packed[w0 + min(lane + 64 * j, nw - 1)];
-#pragma unroll
-    for (int m = 0; m < GPL; ++m) {
-      const int64_t gi = n * G + min(lane + 64 * m, G - 1);
-      dm[s][m] = __half_as_ushort(delta[gi]);
-      zm[s][m] = __half_as_ushort(zero[gi]);
+    for (int j = 0; j < J; ++j) {
+      const int m = min(lane + 64 * j, nb8 - 1);
+      const int64_t q = q0 + (ph0 + 8 * m) / 10;
+      w0v[s][j] = packed[q];
+      // the second word only matters when the block runs past word q, and then it exists
+      w1v[s][j] = packed[min(q + 1, nwt - 1)];
+      const int64_t gi = n * G + ((8 * m) >> gs_log2);
+      dmv[s][j] = __half_as_ushort(delta[gi]);
+      zmv[s][j] = __half_as_ushort(zero[gi]);
     }
   };
 #pragma unroll
   for (int s = 0; s < D; ++s) issue(s, gw + s * TW);
 
-  for (int64_t i = tid; i < B * XS; i += 64 * k3Waves) {
-    const int64_t b = i / XS, kk = i % XS - k3Pad;
-    xs[i] = (kk >= 0 && kk < K) ? __half2float(x[b * K + kk]) : (_Float16)0.0f;
+  // stage x: block m of batch row b as [(x0, x4), (x1, x5)/8, (x2, x6)/64, (x3, x7)], and its sum
+  for (int i = tid; i < B * nb8; i += 64 * k3Waves) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(x + 8 * (int64_t)i);  // x is [B][K] contiguous
+    const unsigned r4[4] = {raw.x, raw.y, raw.z, raw.w};
+    sxb[i] = block_sum8(r4);
+    uint4 o;
+    o.x = __builtin_amdgcn_perm(raw.z, raw.x, 0x05040100u);  // x0 | x4 << 16
+    o.y = as_u(as_h2(__builtin_amdgcn_perm(raw.z, raw.x, 0x07060302u)) *
+               f16x2{(_Float16)0.125f, (_Float16)0.125f});   // (x1, x5) / 8
+    o.z = as_u(as_h2(__builtin_amdgcn_perm(raw.w, raw.y, 0x05040100u)) *
+               f16x2{(_Float16)0.015625f, (_Float16)0.015625f});  // (x2, x6) / 64
+    o.w = __builtin_amdgcn_perm(raw.w, raw.y, 0x07060302u);  // x3 | x7 << 16
+    xq[i] = o;
   }
   __syncthreads();
-  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
 
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int s = r % D;
     const int64_t n = gw + r * TW;
-    const int o = (int)((n * K) % 10);
-    const int nw = (o + (int)K + 9) / 10;
-    // this row's steps and zeros into the wave's LDS slot (the previous row's reads of it were
-    // issued earlier by this wave, and a wave's LDS operations complete in order)
-#pragma unroll
-    for (int m = 0; m < GPL; ++m) wmeta[lane + 64 * m] = dm[s][m] | (zm[s][m] << 16);
-    __builtin_amdgcn_wave_barrier();
-    // segment B (the word's second group) starts at code ts of every word of this lane
-    const int rem = (10 * lane - o) & (GS - 1);
-    const int ts = rem + 10 > GS ? GS - rem : 10;
-    unsigned mB[5];
-#pragma unroll
-    for (int u = 0; u < 5; ++u) mB[u] = (2 * u >= ts ? 0x0000FFFFu : 0u) | (2 * u + 1 >= ts ? 0xFFFF0000u : 0u);
+    const int ph0 = (int)((n * K) % 10);
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int i = lane + 64 * j;
-      const bool valid = i < nw;
-      const int k0 = 10 * min(i, nw - 1) - o;  // >= -9, and k0 + 9 < K + 10
-      const int gA = k0 >= 0 ? k0 / GS : -1;
-      const unsigned mA = wmeta[max(gA, 0)], mBm = wmeta[min(gA + 1, G - 1)];
-      const unsigned w = wv[s][j];
-      unsigned cp[5];
-#pragma unroll
-      for (int u = 0; u < 5; ++u)
-        cp[u] = __builtin_amdgcn_ubfe(w, 6 * u, 3) | (__builtin_amdgcn_ubfe(w, 6 * u + 3, 3) << 16);
-      const float da = valid ? (float)as_h2(mA)[0] * kSubScale : 0.f;
-      const float db = valid ? (float)as_h2(mBm)[0] * kSubScale : 0.f;
-      const float za = (float)as_h2(mA)[1] * kSubScaleInv;
-      const float zb = (float)as_h2(mBm)[1] * kSubScaleInv;
+      const int mr = lane + 64 * j;
+      const int m = min(mr, nb8 - 1);
+      const bool valid = mr < nb8;
+      const int ph = (ph0 + 8 * m) % 10;  // slot of code 0 in word q
+      const uint64_t win = (uint64_t)(w0v[s][j] & 0x3FFFFFFFu) | ((uint64_t)w1v[s][j] << 30);
+      const unsigned v = (unsigned)(win >> (3 * ph));
+      const unsigned x0 = (v & 0x00000FFFu) | ((v << 4) & 0x0FFF0000u);
+      const unsigned cp[4] = {x0 & 0x00070007u, x0 & 0x00380038u, x0 & 0x01C001C0u, (x0 >> 9) & 0x00070007u};
+      const float dl = valid ? __half2float(__ushort_as_half((unsigned short)dmv[s][j])) * kSubScale : 0.f;
+      const float zz = __half2float(__ushort_as_half((unsigned short)zmv[s][j])) * kSubScaleInv;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const unsigned* xr = reinterpret_cast<const unsigned*>(xs + b * XS + k3Pad + k0);  // k0 even
-        float PA = 0.f, PB = 0.f, SA = 0.f, SB = 0.f;
-#pragma unroll
-        for (int u = 0; u < 5; ++u) {
-          const unsigned xv = xr[u];
-          const f16x2 xa = as_h2(xv & ~mB[u]), xb = as_h2(xv & mB[u]);
-          PA = __builtin_amdgcn_fdot2(xa, as_h2(cp[u]), PA, false);
-          PB = __builtin_amdgcn_fdot2(xb, as_h2(cp[u]), PB, false);
-          SA = __builtin_amdgcn_fdot2(xa, one, SA, false);
-          SB = __builtin_amdgcn_fdot2(xb, one, SB, false);
-        }
-        acc[b] = fmaf(da, fmaf(-za, SA, PA), acc[b]);
-        acc[b] = fmaf(db, fmaf(-zb, SB, PB), acc[b]);
+        const uint4 xv = xq[b * nb8 + m];
+        float P = __builtin_amdgcn_fdot2(as_h2(xv.x), as_h2(cp[0]), 0.f, false);
+        P = __builtin_amdgcn_fdot2(as_h2(xv.y), as_h2(cp[1]), P, false);
+        P = __builtin_amdgcn_fdot2(as_h2(xv.z), as_h2(cp[2]), P, false);
+        P = __builtin_amdgcn_fdot2(as_h2(xv.w), as_h2(cp[3]), P, false);
+        acc[b] = fmaf(dl, fmaf(-zz, sxb[b * nb8 + m], P), acc[b]);
       }
     }
     if (r + D < R) issue(s, gw + (r + D) * TW);
@@ -482,7 +466,6 @@ __global__ void __launch_bounds__(64 * k3Waves) k_gemv_3b(const uint32_t* __rest
           store_y<HQQ_OUT_F32>(y, (int64_t)b * N + n, v);
       }
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -556,60 +539,56 @@ hipError_t b2_b(const uint8_t* packed, const __half* delta, const __half* zero, 
   }
 }
 
-template <int GS, int J>
-constexpr int gpl_3b() { return (640 * J / GS + 2 + 63) / 64; }
-template <int GS, int J>
-size_t lds_3b(int B, int64_t K) { return (size_t)k3Waves * 64 * gpl_3b<GS, J>() * 4 + (size_t)B * (K + 2 * k3Pad) * 2; }
+size_t lds_3b(int B, int64_t K) { return (size_t)((B * (K / 8) + 3) & ~int64_t(3)) * 4 + (size_t)B * K * 2; }
 
-template <int B, int GS, int J>
-hipError_t b3_r(const uint32_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+template <int B, int J>
+hipError_t b3_r(const uint32_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int gl,
                 const __half* x, void* y, int y_dtype, hipStream_t st) {
   const int R = N % (2 * k3Waves) == 0 ? 2 : 1;
   const dim3 grid((unsigned)(N / (R * k3Waves))), block(64 * k3Waves);
-  const size_t lds = lds_3b<GS, J>(B, K);
+  const size_t lds = lds_3b(B, K);
   if (R == 2)
-    hipLaunchKernelGGL((k_gemv_3b<B, GS, J, 2>), grid, block, lds, st, packed, delta, zero, N, K, y_dtype,
-                       x, y);
+    hipLaunchKernelGGL((k_gemv_3b<B, J, 2>), grid, block, lds, st, packed, delta, zero, N, K, gl, y_dtype, x, y);
   else
-    hipLaunchKernelGGL((k_gemv_3b<B, GS, J, 1>), grid, block, lds, st, packed, delta, zero, N, K, y_dtype,
-                       x, y);
+    hipLaunchKernelGGL((k_gemv_3b<B, J, 1>), grid, block, lds, st, packed, delta, zero, N, K, gl, y_dtype, x, y);
   return hipGetLastError();
 }
 
-template <int B, int GS>
-hipError_t b3_j(const uint32_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
-                const __half* x, void* y, int y_dtype, hipStream_t st) {
-  const int64_t words = (K + 9 + 9) / 10;  // a row's span, at most
-  if (words <= 128) return b3_r<B, GS, 2>(packed, delta, zero, N, K, x, y, y_dtype, st);
-  if (words <= 256) return b3_r<B, GS, 4>(packed, delta, zero, N, K, x, y, y_dtype, st);
-  if (words <= 448) return b3_r<B, GS, 7>(packed, delta, zero, N, K, x, y, y_dtype, st);
-  return b3_r<B, GS, 8>(packed, delta, zero, N, K, x, y, y_dtype, st);
-}
-
 template <int B>
-hipError_t b3_g(const uint32_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
+hipError_t b3_j(const uint32_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int gl,
                 const __half* x, void* y, int y_dtype, hipStream_t st) {
-  switch (g) {
-    case 16: return b3_j<B, 16>(packed, delta, zero, N, K, x, y, y_dtype, st);
-    case 32: return b3_j<B, 32>(packed, delta, zero, N, K, x, y, y_dtype, st);
-    case 64: return b3_j<B, 64>(packed, delta, zero, N, K, x, y, y_dtype, st);
-    default: return b3_j<B, 128>(packed, delta, zero, N, K, x, y, y_dtype, st);
+  switch ((K / 8 + 63) / 64) {
+    case 1: return b3_r<B, 1>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
+    case 2: return b3_r<B, 2>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
+    case 3:
+    case 4: return b3_r<B, 4>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
+    case 5:
+    case 6: return b3_r<B, 6>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
+    case 7:
+    case 8: return b3_r<B, 8>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
+    case 9:
+    case 10:
+    case 11:
+    case 12: return b3_r<B, 12>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
+    default: return b3_r<B, 16>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
   }
 }
 
 }  // namespace
 
-// a row of the 3-bit product spans at most 512 words (K <= 5100)
+// 3-bit product: rows of at most 8192 codes (16 blocks of 8 per lane), K a multiple of 8
 bool gemv_3b_supported(int64_t K, int g) {
-  return K % 2 == 0 && (K + 18) / 10 <= 512 && (g == 16 || g == 32 || g == 64 || g == 128);
+  return K % 8 == 0 && K <= 8192 && (g == 16 || g == 32 || g == 64 || g == 128 || g == 256);
 }
-size_t gemv_3b_lds_bytes(int64_t K, int64_t batch) { return lds_3b<16, 8>((int)batch, K); }  // the largest
+size_t gemv_3b_lds_bytes(int64_t K, int64_t batch) { return lds_3b((int)batch, K); }
 
 hipError_t launch_gemv_3b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
                           const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t st) {
   const uint32_t* pk = reinterpret_cast<const uint32_t*>(packed);
-  return batch == 1 ? b3_g<1>(pk, delta, zero, N, K, g, x, y, y_dtype, st)
-                    : b3_g<2>(pk, delta, zero, N, K, g, x, y, y_dtype, st);
+  int gl = 4;
+  while ((1 << gl) < g) ++gl;
+  return batch == 1 ? b3_j<1>(pk, delta, zero, N, K, gl, x, y, y_dtype, st)
+                    : b3_j<2>(pk, delta, zero, N, K, gl, x, y, y_dtype, st);
 }
 
 size_t gemv_ax0_lds_bytes(int64_t K, int64_t batch) { return ax0_lds_bytes((int)batch, K); }
