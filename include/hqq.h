@@ -207,7 +207,7 @@ int hqq_gemm_w4a16_dx(const void* packed, const void* delta_fp16, const void* ze
  * Supported: nbits=4 axis=1 (as hqq_gemv_w4a16); nbits=4 axis=0 with group_size 16..256,
  * K a multiple of 32, batch 1 or 2, K <= 16384; nbits=2 axis=1 group_size 16 with N a
  * multiple of 16, K a multiple of 64, batch 1 or 2, K <= 16384; nbits=3 axis=1 with
- * group_size 16..256, N a multiple of 4, K <= 8192, batch 1 or 2 (rows start inside the
+ * group_size 16..256, N a multiple of 4, 40 <= K <= 8192, batch 1 or 2 (rows start inside the
  * ten-code words).  Other combinations return HQQ_ERR_UNSUPPORTED.  Codes stay exact
  * (fp16 subnormals into v_dot2_f32_f16); fp32 sums.
  */

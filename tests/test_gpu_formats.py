@@ -65,10 +65,11 @@ def test_2bit_g16(N, K):
     _check(N, K, 2, 16, 1, (1, 2), seed=2000 + N + K)
 
 
-# 3-bit: every supported g; K with every residue of a row's start inside a word (K mod 10),
-# one and two rows per wave (N mod 8), K up to the largest span
+# 3-bit: every supported g; K with every residue of a row's start inside a word (K mod 10) and
+# inside a 40-code superblock (K mod 40); one and two rows per wave (N mod 8); the smallest K;
+# K at the largest span of one and of two superblocks per lane (2512, 2528)
 CASES_3B = [(16, 12, 208), (32, 64, 800), (64, 40, 4096), (64, 20, 1216), (128, 48, 1152), (64, 16, 5056),
-            (16, 100, 96), (256, 24, 8192), (64, 4, 640)]
+            (16, 100, 96), (256, 24, 8192), (64, 4, 640), (16, 4, 48), (16, 36, 2512), (32, 8, 2528)]
 
 
 @pytest.mark.parametrize("g,N,K", CASES_3B, ids=lambda v: str(v))
@@ -106,5 +107,7 @@ def test_unsupported_formats_rejected():
     for nbits, g, axis in ((3, 32, 0), (2, 32, 1), (2, 16, 0)):
         with pytest.raises(hq.HQQError):
             hq.hqq_gemv(pk, md, md, 64, 128, nbits, g, axis, x)
+    with pytest.raises(hq.HQQError):  # 3-bit rows shorter than 40 codes
+        hq.hqq_gemv(pk, md, md, 64, 32, 3, 16, 1, x[:, :32].contiguous())
     with pytest.raises(hq.HQQError):  # batch 3 is not fused for these formats
         hq.hqq_gemv(pk, md, md, 64, 128, 4, 16, 0, torch.zeros((3, 128), dtype=torch.float16, device="cuda"))

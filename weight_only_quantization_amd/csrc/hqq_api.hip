@@ -303,7 +303,7 @@ int hqq_gemv(const void* packed, const void* delta_fp16, const void* zero_fp16, 
     if (!hqq::gemv_3b_supported(K, group_size))
       return fail(HQQ_ERR_UNSUPPORTED, "3-bit: pow2 group_size 16..256 and K of at most 8192");
     if (N % 4 != 0) return fail(HQQ_ERR_UNSUPPORTED, "3-bit: N must be a multiple of 4");
-    if (hqq::gemv_3b_lds_bytes(K, batch) > 160 * 1024) return fail(HQQ_ERR_UNSUPPORTED, "LDS too large");
+    if (hqq::gemv_3b_lds_bytes(N, K, group_size, batch) > 160 * 1024) return fail(HQQ_ERR_UNSUPPORTED, "LDS too large");
     e = hqq::launch_gemv_3b(pk, dl, zr, N, K, group_size, xx, batch, y, y_dtype, st);
   } else if (nbits == 2 && axis == 1 && group_size == 16) {
     if (N % 16 != 0 || K % 64 != 0) return fail(HQQ_ERR_UNSUPPORTED, "N must be a multiple of 16 and K of 64");

@@ -49,10 +49,6 @@ __device__ __forceinline__ u32x4 wq8(unsigned w, float ds24, float ds20, float z
   return u32x4{as_u(p0), as_u(p1), as_u(p2), as_u(p3)};
 }
 
-// Workgroup barrier for LDS hand-over only: waits for this wave's LDS operations, not for its
-// global loads (the prefetched operands stay in flight; __syncthreads would drain them).  The
-// memory clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // TRANS = false: y [batch, N] = x [batch, K] @ W_hat^T (the forward product; output index n,
 //   contraction over k).  TRANS = true: dX [batch, K] = dY [batch, N] @ W_hat (its input

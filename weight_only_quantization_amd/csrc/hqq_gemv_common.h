@@ -94,4 +94,9 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Workgroup barrier for LDS hand-over only: waits for this wave's LDS operations, not for its
+// global loads (the prefetched operands stay in flight; __syncthreads would drain them).  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace hqq

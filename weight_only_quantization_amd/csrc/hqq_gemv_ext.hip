@@ -370,7 +370,18 @@ __global__ void __launch_bounds__(64 * k2Waves) k_gemv_2b(const uint8_t* __restr
 // it; per block acc += delta 2^24 (P - z 2^-24 S) (v_dot2_f32_f16, fp32 sums).
 // ------------------------------------------------------------------------------------------
 constexpr int k3Waves = 4;
+constexpr int k3PadB = 4;  // zero blocks staged before and after x (a row's first and last superblock overhang)
+constexpr int k3PadG = 2;  // zero groups before and after a row's metadata
+// 16-byte blocks of x each thread loads: J superblocks per lane cover rows of K < 40 (64 J - 1)
+// codes, i.e. fewer than 320 J blocks of 8, and K <= 8192 caps it at 1024 blocks
+constexpr int x_loads_3b(int B, int J) { return (B * (320 * J < 1024 ? 320 * J : 1024) + 64 * k3Waves - 1) / (64 * k3Waves); }
 
+// Four 16-byte aligned words hold 40 codes: five 8-code blocks whose bit positions are fixed
+// (block 1 straddles words 0-1, block 2 words 1-2, block 3 words 2-3).  A row starts at code
+// n*K, a multiple of 8, so every block lies inside one row and, with g >= 16 a multiple of 8,
+// inside one group.  Lane i of a wave takes superblock sb0 + i + 64 j of its row, with sb0 the
+// superblock holding the row's first code; blocks of a neighbouring row in the row's first and
+// last superblock meet zero x and zero metadata.
 template <int B, int J, int R>
 __global__ void __launch_bounds__(64 * k3Waves) k_gemv_3b(const uint32_t* __restrict__ packed,
                                                          const __half* __restrict__ delta,
@@ -379,80 +390,162 @@ __global__ void __launch_bounds__(64 * k3Waves) k_gemv_3b(const uint32_t* __rest
                                                          void* __restrict__ y) {
   constexpr int D = R < 2 ? R : 2;  // rows in flight per wave
   extern __shared__ float lds3[];
-  const int nb8 = (int)(K / 8);                              // 8-code blocks per row
-  float* sxb = lds3;                                         // [B][nb8] block sums of x
-  uint4* xq = reinterpret_cast<uint4*>(sxb + ((B * nb8 + 3) & ~3));  // [B][nb8] staged x pairs
+  const int nb8 = (int)(K / 8);      // 8-code blocks per row
+  const int xs = nb8 + 2 * k3PadB;   // staged blocks per batch row
+  const int G = (int)(K >> gs_log2);  // groups per row
+  const int gsr = G + 2 * k3PadG;
+  float* sxb = lds3;                                              // [B][xs] block sums of x
+  uint4* xq = reinterpret_cast<uint4*>(sxb + ((B * xs + 3) & ~3));  // [B][xs] staged x pairs
+  float2* meta = reinterpret_cast<float2*>(xq + B * xs);          // [waves][R][gsr] (step 2^24, -zero 2^-24)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t G = K >> gs_log2;  // groups per row
   const int64_t TW = N / R;
   const int64_t gw = (int64_t)blockIdx.x * k3Waves + wave;
-
-  // the first D rows: two words per block, the block's step and zero
-  unsigned w0v[D][J], w1v[D][J], dmv[D][J], zmv[D][J];
   const int64_t nwt = (N * K + 9) / 10;  // words of the tensor
-  auto issue = [&](int s, int64_t n) {
-    const int64_t f0 = n * K, q0 = f0 / 10;
-    const int ph0 = (int)(f0 - 10 * q0);
+
+  // 1. this thread's blocks of x and this wave's rows' metadata, ahead of the weight stream
+  constexpr int XR = x_loads_3b(B, J);
+  constexpr int MR = 3;  // metadata entries per lane and row loaded early: rows of up to 188 groups
+  const int nxb = B * nb8;
+  uint4 xr[XR];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int m = min(lane + 64 * j, nb8 - 1);
-      const int64_t q = q0 + (ph0 + 8 * m) / 10;
-      w0v[s][j] = packed[q];
-      // the second word only matters when the block runs past word q, and then it exists
-      w1v[s][j] = packed[min(q + 1, nwt - 1)];
-      const int64_t gi = n * G + ((8 * m) >> gs_log2);
-      dmv[s][j] = __half_as_ushort(delta[gi]);
-      zmv[s][j] = __half_as_ushort(zero[gi]);
+  for (int t = 0; t < XR; ++t) {
+    const int i = min(tid + 64 * k3Waves * t, nxb - 1);
+    xr[t] = *reinterpret_cast<const uint4*>(x + 8 * (int64_t)i);  // x is [B][K] contiguous
+  }
+  unsigned dm[R][MR], zm[R][MR];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t gb = (gw + r * TW) * G;
+#pragma unroll
+    for (int t = 0; t < MR; ++t) {
+      const int gi = min(max(lane + 64 * t - k3PadG, 0), G - 1);
+      dm[r][t] = __half_as_ushort(delta[gb + gi]);
+      zm[r][t] = __half_as_ushort(zero[gb + gi]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. the first D rows' words, in flight
+  uint4 wv[D][J];
+  auto issue = [&](int s, int64_t n) {
+    const int64_t f0 = n * K, sb0 = f0 / 40;
+    const int nsb = (int)((f0 + K - 1) / 40 - sb0) + 1;
+    const int lim = (int)min(nwt - 4 * sb0, (int64_t)INT_MAX);  // words from the row's first superblock on
+    const int nfull = min(lim / 4, nsb);  // superblocks wholly inside the tensor: >= 1 as K >= 40
+    const uint4* base = reinterpret_cast<const uint4*>(packed) + sb0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) wv[s][j] = base[(unsigned)min(lane + 64 * j, nfull - 1)];
+    if (nfull < nsb) {  // the tensor ends inside this row's last superblock: its words one by one
+      const uint32_t* wp = packed + 4 * sb0;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int i = lane + 64 * j;
+        if (i >= nfull && i < nsb) {
+          wv[s][j].x = wp[min(4 * i, lim - 1)];
+          wv[s][j].y = wp[min(4 * i + 1, lim - 1)];
+          wv[s][j].z = wp[min(4 * i + 2, lim - 1)];
+          wv[s][j].w = wp[min(4 * i + 3, lim - 1)];
+        }
+      }
     }
   };
 #pragma unroll
   for (int s = 0; s < D; ++s) issue(s, gw + s * TW);
 
-  // stage x: block m of batch row b as [(x0, x4), (x1, x5)/8, (x2, x6)/64, (x3, x7)], and its sum
-  for (int i = tid; i < B * nb8; i += 64 * k3Waves) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(x + 8 * (int64_t)i);  // x is [B][K] contiguous
-    const unsigned r4[4] = {raw.x, raw.y, raw.z, raw.w};
-    sxb[i] = block_sum8(r4);
-    uint4 o;
-    o.x = __builtin_amdgcn_perm(raw.z, raw.x, 0x05040100u);  // x0 | x4 << 16
-    o.y = as_u(as_h2(__builtin_amdgcn_perm(raw.z, raw.x, 0x07060302u)) *
-               f16x2{(_Float16)0.125f, (_Float16)0.125f});   // (x1, x5) / 8
-    o.z = as_u(as_h2(__builtin_amdgcn_perm(raw.w, raw.y, 0x05040100u)) *
-               f16x2{(_Float16)0.015625f, (_Float16)0.015625f});  // (x2, x6) / 64
-    o.w = __builtin_amdgcn_perm(raw.w, raw.y, 0x07060302u);  // x3 | x7 << 16
-    xq[i] = o;
+  // 3. metadata as floats (step 2^24, -zero 2^-24), zero-padded at both ends of each row
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float2* mr = meta + (wave * R + r) * gsr;
+#pragma unroll
+    for (int t = 0; t < MR; ++t) {
+      const int i = lane + 64 * t, gi = i - k3PadG;
+      float2 v = {0.f, 0.f};
+      if (gi >= 0 && gi < G) {
+        v.x = __half2float(__ushort_as_half((unsigned short)dm[r][t])) * kSubScale;
+        v.y = -__half2float(__ushort_as_half((unsigned short)zm[r][t])) * kSubScaleInv;
+      }
+      if (i < gsr) mr[i] = v;
+    }
+    if (gsr > 64 * MR) {  // longer rows: the rest after the words (waits for them)
+      const int64_t gb = (gw + r * TW) * G;
+      for (int i = lane + 64 * MR; i < gsr; i += 64) {
+        const int gi = i - k3PadG;
+        float2 v = {0.f, 0.f};
+        if (gi < G) {
+          v.x = __half2float(delta[gb + gi]) * kSubScale;
+          v.y = -__half2float(zero[gb + gi]) * kSubScaleInv;
+        }
+        mr[i] = v;
+      }
+    }
   }
-  __syncthreads();
+
+  // 4. stage x: block m of batch row b as [(x0, x4), (x1, x5)/8, (x2, x6)/64, (x3, x7)] at
+  //    b * xs + pad + m, and its sum; the pads are zero
+#pragma unroll
+  for (int t = 0; t < XR; ++t) {
+    const int i = tid + 64 * k3Waves * t;
+    if (i < nxb) {
+      const int b = i / nb8, m = i - b * nb8;
+      const uint4 raw = xr[t];
+      const unsigned r4[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint4 o;
+      o.x = __builtin_amdgcn_perm(raw.z, raw.x, 0x05040100u);  // x0 | x4 << 16
+      o.y = as_u(as_h2(__builtin_amdgcn_perm(raw.z, raw.x, 0x07060302u)) *
+                 f16x2{(_Float16)0.125f, (_Float16)0.125f});  // (x1, x5) / 8
+      o.z = as_u(as_h2(__builtin_amdgcn_perm(raw.w, raw.y, 0x05040100u)) *
+                 f16x2{(_Float16)0.015625f, (_Float16)0.015625f});  // (x2, x6) / 64
+      o.w = __builtin_amdgcn_perm(raw.w, raw.y, 0x07060302u);  // x3 | x7 << 16
+      sxb[b * xs + k3PadB + m] = block_sum8(r4);
+      xq[b * xs + k3PadB + m] = o;
+    }
+  }
+  if (tid < B * 2 * k3PadB) {
+    const int b = tid / (2 * k3PadB), p = tid % (2 * k3PadB);
+    const int m = p < k3PadB ? p : nb8 + p;  // pads before and after the row
+    sxb[b * xs + m] = 0.f;
+    xq[b * xs + m] = uint4{0u, 0u, 0u, 0u};
+  }
+  lds_barrier();
 
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int s = r % D;
     const int64_t n = gw + r * TW;
-    const int ph0 = (int)((n * K) % 10);
+    const int64_t f0 = n * K, sb0 = f0 / 40;
+    const int nsb = (int)((f0 + K - 1) / 40 - sb0) + 1;
+    const int crow = (int)(5 * sb0 - f0 / 8) + k3PadB;  // staged index of the first superblock's block 0
+    const float2* mr = meta + (wave * R + r) * gsr + k3PadG;
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int mr = lane + 64 * j;
-      const int m = min(mr, nb8 - 1);
-      const bool valid = mr < nb8;
-      const int ph = (ph0 + 8 * m) % 10;  // slot of code 0 in word q
-      const uint64_t win = (uint64_t)(w0v[s][j] & 0x3FFFFFFFu) | ((uint64_t)w1v[s][j] << 30);
-      const unsigned v = (unsigned)(win >> (3 * ph));
-      const unsigned x0 = (v & 0x00000FFFu) | ((v << 4) & 0x0FFF0000u);
-      const unsigned cp[4] = {x0 & 0x00070007u, x0 & 0x00380038u, x0 & 0x01C001C0u, (x0 >> 9) & 0x00070007u};
-      const float dl = valid ? __half2float(__ushort_as_half((unsigned short)dmv[s][j])) * kSubScale : 0.f;
-      const float zz = __half2float(__ushort_as_half((unsigned short)zmv[s][j])) * kSubScaleInv;
+      const int i = lane + 64 * j;
+      if (i < nsb) {
+        const uint4 w = wv[s][j];
+        const unsigned v[5] = {w.x, __builtin_amdgcn_ubfe(w.x, 24, 6) | (w.y << 6),
+                               __builtin_amdgcn_ubfe(w.y, 18, 12) | (w.z << 12),
+                               __builtin_amdgcn_ubfe(w.z, 12, 18) | (w.w << 18), w.w >> 6};
+        const int m0 = crow + 5 * i;  // staged block index, in [0, nb8 + 2 pads)
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const uint4 xv = xq[b * nb8 + m];
-        float P = __builtin_amdgcn_fdot2(as_h2(xv.x), as_h2(cp[0]), 0.f, false);
-        P = __builtin_amdgcn_fdot2(as_h2(xv.y), as_h2(cp[1]), P, false);
-        P = __builtin_amdgcn_fdot2(as_h2(xv.z), as_h2(cp[2]), P, false);
-        P = __builtin_amdgcn_fdot2(as_h2(xv.w), as_h2(cp[3]), P, false);
-        acc[b] = fmaf(dl, fmaf(-zz, sxb[b * nb8 + m], P), acc[b]);
+        for (int bb = 0; bb < 5; ++bb) {
+          const unsigned x0 = (v[bb] & 0x00000FFFu) | ((v[bb] << 4) & 0x0FFF0000u);
+          const unsigned cp[4] = {x0 & 0x00070007u, x0 & 0x00380038u, x0 & 0x01C001C0u,
+                                  (x0 >> 9) & 0x00070007u};
+          const int m = m0 + bb;
+          const float2 md = mr[(8 * (m - k3PadB)) >> gs_log2];
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const uint4 xv = xq[b * xs + m];
+            float P = __builtin_amdgcn_fdot2(as_h2(xv.x), as_h2(cp[0]), 0.f, false);
+            P = __builtin_amdgcn_fdot2(as_h2(xv.y), as_h2(cp[1]), P, false);
+            P = __builtin_amdgcn_fdot2(as_h2(xv.z), as_h2(cp[2]), P, false);
+            P = __builtin_amdgcn_fdot2(as_h2(xv.w), as_h2(cp[3]), P, false);
+            acc[b] = fmaf(md.x, fmaf(md.y, sxb[b * xs + m], P), acc[b]);
+          }
+        }
       }
     }
     if (r + D < R) issue(s, gw + (r + D) * TW);
@@ -539,14 +632,22 @@ hipError_t b2_b(const uint8_t* packed, const __half* delta, const __half* zero, 
   }
 }
 
-size_t lds_3b(int B, int64_t K) { return (size_t)((B * (K / 8) + 3) & ~int64_t(3)) * 4 + (size_t)B * K * 2; }
+// staged x (pairs and block sums, zero-padded) and the metadata of the block's rows
+size_t lds_3b(int B, int R, int64_t K, int g) {
+  const int64_t xs = K / 8 + 2 * k3PadB;
+  return (size_t)((B * xs + 3) & ~int64_t(3)) * 4 + (size_t)B * xs * 16 + (size_t)k3Waves * R * (K / g + 2 * k3PadG) * 8;
+}
+inline int rows_per_wave_3b(int64_t N) { return N % (2 * k3Waves) == 0 ? 2 : 1; }
 
 template <int B, int J>
 hipError_t b3_r(const uint32_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int gl,
                 const __half* x, void* y, int y_dtype, hipStream_t st) {
-  const int R = N % (2 * k3Waves) == 0 ? 2 : 1;
+  const int R = rows_per_wave_3b(N);
+  // every superblock of a row has a lane, every block of x a loading thread, every row a wave
+  if (K < 40 || (K / 40 + 2) > 64 * J || B * (K / 8) > x_loads_3b(B, J) * 64 * k3Waves || N % (R * k3Waves) != 0)
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)(N / (R * k3Waves))), block(64 * k3Waves);
-  const size_t lds = lds_3b(B, K);
+  const size_t lds = lds_3b(B, R, K, 1 << gl);
   if (R == 2)
     hipLaunchKernelGGL((k_gemv_3b<B, J, 2>), grid, block, lds, st, packed, delta, zero, N, K, gl, y_dtype, x, y);
   else
@@ -554,23 +655,15 @@ hipError_t b3_r(const uint32_t* packed, const __half* delta, const __half* zero,
   return hipGetLastError();
 }
 
+// superblocks per lane: a row of K codes touches at most K/40 + 2 superblocks
 template <int B>
 hipError_t b3_j(const uint32_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int gl,
                 const __half* x, void* y, int y_dtype, hipStream_t st) {
-  switch ((K / 8 + 63) / 64) {
+  switch ((K / 40 + 2 + 63) / 64) {
     case 1: return b3_r<B, 1>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
     case 2: return b3_r<B, 2>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
-    case 3:
-    case 4: return b3_r<B, 4>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
-    case 5:
-    case 6: return b3_r<B, 6>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
-    case 7:
-    case 8: return b3_r<B, 8>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
-    case 9:
-    case 10:
-    case 11:
-    case 12: return b3_r<B, 12>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
-    default: return b3_r<B, 16>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
+    case 3: return b3_r<B, 3>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
+    default: return b3_r<B, 4>(packed, delta, zero, N, K, gl, x, y, y_dtype, st);
   }
 }
 
@@ -578,9 +671,11 @@ hipError_t b3_j(const uint32_t* packed, const __half* delta, const __half* zero,
 
 // 3-bit product: rows of at most 8192 codes (16 blocks of 8 per lane), K a multiple of 8
 bool gemv_3b_supported(int64_t K, int g) {
-  return K % 8 == 0 && K <= 8192 && (g == 16 || g == 32 || g == 64 || g == 128 || g == 256);
+  return K % 8 == 0 && K >= 40 && K <= 8192 && (g == 16 || g == 32 || g == 64 || g == 128 || g == 256);
 }
-size_t gemv_3b_lds_bytes(int64_t K, int64_t batch) { return lds_3b((int)batch, K); }
+size_t gemv_3b_lds_bytes(int64_t N, int64_t K, int g, int64_t batch) {
+  return lds_3b((int)batch, rows_per_wave_3b(N), K, g);
+}
 
 hipError_t launch_gemv_3b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
                           const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t st) {

@@ -64,7 +64,7 @@ hipError_t launch_gemm_dx(const uint8_t* packed, const __half* delta, const __ha
                           hipStream_t st);
 // Fused product with 3-bit codes (axis 1, batch 1-2): shapes it takes, LDS bytes, launch.
 bool gemv_3b_supported(int64_t K, int g);
-size_t gemv_3b_lds_bytes(int64_t K, int64_t batch);
+size_t gemv_3b_lds_bytes(int64_t N, int64_t K, int g, int64_t batch);
 hipError_t launch_gemv_3b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
                           const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t st);
 hipError_t launch_gemv_ax0(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
