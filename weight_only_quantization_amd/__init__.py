@@ -261,7 +261,7 @@ def hqq_gemm_w4a16_dx(packed, delta, zero, N: int, K: int, group_size: int, dy, 
 def hqq_gemv(packed, delta, zero, N: int, K: int, nbits: int, group_size: int, axis: int, x, out_dtype=None,
              out=None, stream=None):
     """y [batch, N] = x [batch, K] @ W_hat^T for any stored format the library fuses
-    (4-bit axis 1 or 0, 2-bit axis 1 with groups of 16)."""
+    (4-bit axis 1 or 0, 3-bit axis 1, 2-bit axis 1 with groups of 16)."""
     import torch
     lib = load()
     out_dtype = out_dtype or torch.float16
