@@ -25,10 +25,15 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-ffp-contract=
 
 SOURCES = ["hqq_api.hip", "hqq_quant.hip", "hqq_dequant.hip", "hqq_gemv.hip", "hqq_gemv_ext.hip", "hqq_gemm.hip"]
 
+# The split GEMM keeps its 128 MFMA accumulators per lane in ordinary VGPRs: with the default
+# (accumulation-register) form the register allocator does not tie each MFMA's result to its
+# accumulator input and copies accumulators between register files around most MFMAs.
+EXTRA = {"hqq_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in (r.stderr or "").splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)

@@ -34,7 +34,8 @@ constexpr int kSkBN = 128;          // weight rows per block
 constexpr int kSkBK = 128;          // codes per chunk
 constexpr int kSkRow = kSkBK + 8;   // LDS row stride of the W_hat tile (halves)
 constexpr size_t kSkLds = 2 * kSkBN * kSkRow * sizeof(_Float16);
-constexpr int kSkThreads = 256;     // 4 waves, each 64 batch rows x all 128 weight rows
+constexpr int kSkMulWaves = 4;      // multiplying waves, each 64 batch rows x all 128 weight rows
+constexpr int kSkThreads = 512;     // and as many staging waves
 
 // Eight 4-bit codes of a word (natural order) -> fp16 W_hat pairs (c0,c1), (c2,c3), (c4,c5), (c6,c7).
 // t0 = (c0, c4), t1 = 16 (c1, c5), t2 = (c2, c6), t3 = 16 (c3, c7) as fp16 subnormals.
@@ -56,6 +57,13 @@ __device__ __forceinline__ u32x4 wq8(unsigned w, float ds24, float ds20, float z
 // The LDS tile always holds W_hat as [output index][contraction index]; the transposed form
 // writes it with an XOR swizzle of 16-byte blocks (block ^ 4 (output >> 5)), which keeps both
 // its dword stores and the 16-byte fragment reads free of bank conflicts.
+//
+// Two roles per block, two waves per SIMD: waves 0-3 multiply (A from the tiled activations,
+// B from the LDS tile), waves 4-7 stage the weight tile (codes and metadata two chunks ahead,
+// dequantisation, LDS stores).  A wave's memory counter completes in issue order, so a wave
+// that issued both would wait for the slow weight stream (HBM) whenever it needs its next
+// activations (L2); split by role, each waits only for its own stream.  Both roles pass the
+// same barriers: one after the first tile is staged and one per chunk.
 template <int GS, bool DIRECT, bool TRANS>
 __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restrict__ packed, const __half* __restrict__ delta,
                                                  const __half* __restrict__ zero, int64_t N, int64_t K, int64_t ks,
@@ -63,7 +71,7 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
                                                  float* __restrict__ part, void* __restrict__ y, int out_dtype,
                                                  int xcd_map) {
   extern __shared__ _Float16 wt[];  // [2][kSkBN][kSkRow]
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t NO = TRANS ? K : N, KC = TRANS ? N : K;  // output and contraction lengths
   // Block b of a row of the grid runs on XCD b mod 8 (round-robin dispatch).  With xcd_map,
   // the S splits get 8 / S XCDs each (S <= 8) or each XCD gets S / 8 splits, so one XCD's L2
@@ -88,88 +96,114 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
     }
   }
   const int64_t n0 = (int64_t)tile * kSkBN, m0 = (int64_t)blockIdx.y * kSkBM, k0 = (int64_t)split * ks;
-  const int nch = (int)(ks / kSkBK);
+  const int nch = (int)(ks / kSkBK);  // even, >= 2
 
-  // W staging.  Forward: thread -> weight rows wr and 64 + wr (output rows of the tile), codes
-  // 32 wq .. 32 wq + 31 of each chunk.  Transposed: thread -> weight rows 2 wr and 2 wr + 1 of
-  // the chunk (contraction), codes 32 wq .. +31 of the tile's output columns.  16 bytes per
-  // row: one load instruction of a wave spans 16 (32) rows (each row of a 4-bit weight with
-  // K = 8192 is its own 4 KB page, and an instruction's distinct pages are translated one after
-  // another)
-  const int wr = tid >> 2, wq = tid & 3;
-  const int64_t G_row = K / GS;  // groups per weight row
-  const uint8_t* wsrc;
-  const __half *dsrc, *zsrc;
-  int64_t wstride, mstride, wchunk, mchunk;
-  if constexpr (TRANS) {
-    wsrc = packed + (k0 + 2 * wr) * (K / 2) + (n0 + 32 * wq) / 2;
-    dsrc = delta + (k0 + 2 * wr) * G_row + (n0 + 32 * wq) / GS;
-    zsrc = zero + (k0 + 2 * wr) * G_row + (n0 + 32 * wq) / GS;
-    wstride = K / 2, mstride = G_row;                       // the second row
-    wchunk = (int64_t)kSkBK * (K / 2), mchunk = (int64_t)kSkBK * G_row;  // the next chunk of rows
-  } else {
-    wsrc = packed + (n0 + wr) * (K / 2) + k0 / 2 + 16 * wq;
-    dsrc = delta + (n0 + wr) * G_row + (k0 + 32 * wq) / GS;
-    zsrc = zero + (n0 + wr) * G_row + (k0 + 32 * wq) / GS;
-    wstride = 64 * (K / 2), mstride = 64 * G_row;           // the second row pass
-    wchunk = kSkBK / 2, mchunk = kSkBK / GS;                 // the next 128 codes
+  if (wave >= kSkMulWaves) {
+    // ---------------------------------------------------------------- staging waves
+    // Forward: thread -> weight rows wr and 64 + wr (output rows of the tile), codes
+    // 32 wq .. 32 wq + 31 of each chunk.  Transposed: thread -> weight rows 2 wr and 2 wr + 1 of
+    // the chunk (contraction), codes 32 wq .. +31 of the tile's output columns.  16 bytes per
+    // row: one load instruction of a wave spans 16 (32) rows (each row of a 4-bit weight with
+    // K = 8192 is its own 4 KB page, and an instruction's distinct pages are translated one
+    // after another)
+    const int st = tid - 64 * kSkMulWaves;
+    const int wr = st >> 2, wq = st & 3;
+    const int64_t G_row = K / GS;  // groups per weight row
+    const uint8_t* wsrc;
+    const __half *dsrc, *zsrc;
+    int64_t wstride, mstride, wchunk, mchunk;
+    if constexpr (TRANS) {
+      wsrc = packed + (k0 + 2 * wr) * (K / 2) + (n0 + 32 * wq) / 2;
+      dsrc = delta + (k0 + 2 * wr) * G_row + (n0 + 32 * wq) / GS;
+      zsrc = zero + (k0 + 2 * wr) * G_row + (n0 + 32 * wq) / GS;
+      wstride = K / 2, mstride = G_row;                                   // the second row
+      wchunk = (int64_t)kSkBK * (K / 2), mchunk = (int64_t)kSkBK * G_row;  // the next chunk of rows
+    } else {
+      wsrc = packed + (n0 + wr) * (K / 2) + k0 / 2 + 16 * wq;
+      dsrc = delta + (n0 + wr) * G_row + (k0 + 32 * wq) / GS;
+      zsrc = zero + (n0 + wr) * G_row + (k0 + 32 * wq) / GS;
+      wstride = 64 * (K / 2), mstride = 64 * G_row;  // the second row pass
+      wchunk = kSkBK / 2, mchunk = kSkBK / GS;        // the next 128 codes
+    }
+    _Float16* wdst = wt + wr * kSkRow + 32 * wq;
+
+    auto load_w = [&](int c, u32x4 (&wv)[2], unsigned (&dm)[2], unsigned (&zm)[2]) {
+      const int cc = min(c, nch - 1);  // past the end: reload the last chunk (never used)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        wv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + p * wstride + cc * wchunk));
+        dm[p] = __half_as_ushort(dsrc[p * mstride + cc * mchunk]);
+        zm[p] = __half_as_ushort(zsrc[p * mstride + cc * mchunk]);
+      }
+    };
+    // the thread's share of one chunk -> LDS buffer `buf`, with the dequantisation constants of
+    // its rows' groups: z d and d 2^24, d 2^20 (all exact).  Forward: 16-byte stores.
+    // Transposed: the two rows' values of one output column paired into a dword.
+    auto stage = [&](int buf, const u32x4 (&wv)[2], const unsigned (&dm)[2], const unsigned (&zm)[2]) {
+      float zd[2], ds24[2], ds20[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const float d = __half2float(__ushort_as_half((unsigned short)dm[p]));
+        const float z = __half2float(__ushort_as_half((unsigned short)zm[p]));
+        zd[p] = z * d, ds24[p] = d * 16777216.0f, ds20[p] = d * 1048576.0f;
+      }
+      _Float16* base = wt + buf * (kSkBN * kSkRow);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if constexpr (TRANS) {
+          const u32x4 r0 = wq8(wv[0][s], ds24[0], ds20[0], zd[0]);
+          const u32x4 r1 = wq8(wv[1][s], ds24[1], ds20[1], zd[1]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int o = 32 * wq + 8 * s + e;  // output column in the tile; contraction 2 wr, 2 wr + 1
+            const unsigned v = __builtin_amdgcn_perm(r1[e >> 1], r0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+            const int blk = (wr >> 2) ^ (4 * (o >> 5));
+            *reinterpret_cast<unsigned*>(base + o * kSkRow + 8 * blk + 2 * (wr & 3)) = v;
+          }
+        } else {
+          const int p = s >> 1, h = s & 1;
+          _Float16* dst = wdst + buf * (kSkBN * kSkRow) + p * 64 * kSkRow;
+#pragma unroll
+          for (int i = 2 * h; i < 2 * h + 2; ++i)
+            *reinterpret_cast<u32x4*>(dst + 8 * i) = wq8(wv[p][i], ds24[p], ds20[p], zd[p]);
+        }
+      }
+    };
+
+    // chunk c + 1 is staged while the multiplying waves use chunk c; the codes of chunk c + 3
+    // are requested right after, so each wait covers codes requested two chunks earlier
+    u32x4 wa[2], wb[2];
+    unsigned dma[2], zma[2], dmb[2], zmb[2];
+    load_w(0, wa, dma, zma);
+    load_w(1, wb, dmb, zmb);
+    stage(0, wa, dma, zma);
+    load_w(2, wa, dma, zma);
+    lds_barrier();
+    for (int c = 0; c < nch; c += 2) {
+      stage(1, wb, dmb, zmb);  // chunk c + 1 (always < nch: nch is even)
+      load_w(c + 3, wb, dmb, zmb);
+      lds_barrier();
+      if (c + 2 < nch) stage(0, wa, dma, zma);  // chunk c + 2
+      load_w(c + 4, wa, dma, zma);
+      lds_barrier();
+    }
+    return;
   }
-  _Float16* wdst = wt + wr * kSkRow + 32 * wq;
 
+  // ---------------------------------------------------------------- multiplying waves
   // A operand from the tiled copy of x: the 16 x 32 fragment of row group mg and k-step q is
   // 1 KB at xt[(q MG + mg) 64 ..], already in lane order (lane l: row l & 15, codes
   // 8 (l >> 4) .. +7), so every A load instruction reads one contiguous 1 KB
   const u32x4* xa[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) xa[t] = xt + ((k0 / 32) * MG + (m0 + 64 * wave + 16 * t) / 16) * 64 + lane;
-
-  auto load_w = [&](int c, u32x4 (&wv)[2], unsigned (&dm)[2], unsigned (&zm)[2]) {
-    const int cc = min(c, nch - 1);  // past the end: reload the last chunk (never used)
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      wv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + p * wstride + cc * wchunk));
-      dm[p] = __half_as_ushort(dsrc[p * mstride + cc * mchunk]);
-      zm[p] = __half_as_ushort(zsrc[p * mstride + cc * mchunk]);
-    }
-  };
-  // A operand of k-step q (32 codes) into one of four register slots
   const int nsteps = 4 * nch;
+  const int64_t astep = MG * 64;  // one k-step further in the tiled copy
+  // A operand of k-step q (32 codes) into one of four register slots
   auto load_a = [&](int q, u32x4 (&av)[4]) {
-    const int qq = min(q, nsteps - 1);
+    const int64_t off = (int64_t)min(q, nsteps - 1) * astep;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) av[t] = xa[t][(int64_t)qq * MG * 64];
-  };
-  // per-chunk dequantisation constants of a row's group: z d and d 2^24, d 2^20 (all exact)
-  struct WConst {
-    float zd, ds24, ds20;
-  };
-  auto wconst = [&](unsigned dm, unsigned zm) {
-    const float d = __half2float(__ushort_as_half((unsigned short)dm));
-    const float z = __half2float(__ushort_as_half((unsigned short)zm));
-    return WConst{z * d, d * 16777216.0f, d * 1048576.0f};
-  };
-  // a quarter (k-step s) of the thread's staging for the next chunk -> LDS buffer `buf`.
-  // Forward: words 2h, 2h + 1 of row pass p = s / 2 (h = s mod 2), 16-byte stores.  Transposed:
-  // word s of both rows, the two rows' values of one output column paired into a dword.
-  auto stage_step = [&](int buf, const u32x4 (&wv)[2], const WConst (&k)[2], int s) {
-    if constexpr (TRANS) {
-      const u32x4 r0 = wq8(wv[0][s], k[0].ds24, k[0].ds20, k[0].zd);
-      const u32x4 r1 = wq8(wv[1][s], k[1].ds24, k[1].ds20, k[1].zd);
-      _Float16* base = wt + buf * (kSkBN * kSkRow);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int o = 32 * wq + 8 * s + e;  // output column in the tile; contraction 2 wr, 2 wr + 1
-        const unsigned v = __builtin_amdgcn_perm(r1[e >> 1], r0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-        const int blk = (wr >> 2) ^ (4 * (o >> 5));
-        *reinterpret_cast<unsigned*>(base + o * kSkRow + 8 * blk + 2 * (wr & 3)) = v;
-      }
-    } else {
-      const int p = s >> 1, h = s & 1;
-      _Float16* dst = wdst + buf * (kSkBN * kSkRow) + p * 64 * kSkRow;
-#pragma unroll
-      for (int i = 2 * h; i < 2 * h + 2; ++i)
-        *reinterpret_cast<u32x4*>(dst + 8 * i) = wq8(wv[p][i], k[p].ds24, k[p].ds20, k[p].zd);
-    }
+    for (int t = 0; t < 4; ++t) av[t] = xa[t][off];
   };
 
   f32x4 acc[4][8];
@@ -178,20 +212,15 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One chunk c from LDS buffer `buf`, with the staging of chunk c + 1 (codes in wp, loaded one
-  // chunk ago) into the other buffer and the loads of chunk c + 2's codes into wq spread over
-  // its four k-steps.  k-step s: MFMAs in fragment order j (four batch tiles each); fragment j's
-  // registers are refilled from LDS with k-step s + 1 right after its four MFMAs; words 2s and
-  // 2s + 1 of the thread's next-chunk codes are dequantised and stored; A slot s is refilled
-  // with k-step s of chunk c + 1 after its last MFMA (A runs three k-steps ahead).  The group
-  // scheduling barriers keep the loads where they are written (the compiler would otherwise
-  // sink them to the loop end and wait for them there).
+  // One chunk from LDS buffer `buf`.  k-step s: MFMAs in fragment order j (four batch tiles
+  // each); fragment j's registers are refilled from LDS with k-step s + 1 right after its four
+  // MFMAs; A slot s is refilled with k-step s of the next chunk after its last MFMA (A runs a
+  // chunk ahead).  The scheduling barriers keep the loads where they are written (the
+  // compiler would otherwise sink them to the loop end and wait for them there).
   u32x4 as[4][4];
-  auto chunk = [&](int buf, int c, const u32x4 (&wp)[2], const unsigned (&dmp)[2], const unsigned (&zmp)[2],
-                   u32x4 (&wn)[2], unsigned (&dmn)[2], unsigned (&zmn)[2]) {
-    load_w(c + 2, wn, dmn, zmn);
-    const WConst k[2] = {wconst(dmp[0], zmp[0]), wconst(dmp[1], zmp[1])};
-    const _Float16* src = wt + buf * (kSkBN * kSkRow) + (lane & 15) * kSkRow + 8 * (lane >> 4);
+  const _Float16* src0 = wt + (lane & 15) * kSkRow + 8 * (lane >> 4);
+  auto chunk = [&](int buf, int c) {
+    const _Float16* src = src0 + buf * (kSkBN * kSkRow);
     // fragment j, k-step s: 16-byte block 4s + (lane >> 4) of its row (swizzled when TRANS)
     auto bfrag = [&](int j, int s) {
       const int sb = TRANS ? (s ^ (j >> 1)) : s;
@@ -203,7 +232,6 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      stage_step(buf ^ 1, wp, k, s);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
 #pragma unroll
@@ -216,25 +244,13 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
     }
   };
 
-  // two chunks per iteration, so that the two code register sets keep fixed names; the loads
-  // outstanding at the loop head are issued in the same order as in the loop (codes of the
-  // next chunk, then the A slots), so the head waits only for the former
-  u32x4 wa[2], wb[2];
-  unsigned dma[2], zma[2], dmb[2], zmb[2];
-  load_w(0, wa, dma, zma);
-  {
-    const WConst k[2] = {wconst(dma[0], zma[0]), wconst(dma[1], zma[1])};
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) stage_step(0, wa, k, s4);
-  }
-  load_w(1, wa, dma, zma);
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) load_a(s4, as[s4]);
-  lds_barrier();
+  lds_barrier();  // the first tile is staged
   for (int c = 0; c < nch; c += 2) {
-    chunk(0, c, wa, dma, zma, wb, dmb, zmb);
+    chunk(0, c);
     lds_barrier();
-    chunk(1, c + 1, wb, dmb, zmb, wa, dma, zma);
+    chunk(1, c + 1);
     lds_barrier();
   }
 
