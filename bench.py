@@ -94,7 +94,8 @@ def sleep_rate(stream):
 def config_legs(a, timed, stream, dev):
     """Legs outside the step, one per remaining configuration: the 7B-shaped layer set at 3-bit
     g64 and 2-bit g16 (Laplace weights), the 28672x8192 axis-0 g128 weight, and the fused
-    products over the 2-bit and axis-0 formats (batch 1 and 2, operands rotated over > 1 GB)."""
+    products over the 3-bit, 2-bit and axis-0 formats (batch 1 and 2; batch 256 through hqq_gemm for
+    the axis-1 formats; operands rotated over > 1 GB)."""
     import numpy as np
     import torch
 
@@ -149,6 +150,21 @@ def config_legs(a, timed, stream, dev):
             byt = byt_w + 2 * b * K + 2 * b * N
             legs["%s_b%d" % (name, b)] = {"us": tg * 1e6, "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM,
                                           "bytes": byt, "shape": [N, K], "copies_rotated": ncopy}
+        if axis == 1:  # the batched product over the same format at batch 256 (hqq_gemm)
+            B = 256
+            X2 = torch.from_numpy(synth.activations(B, K, 403)).to(dev)
+            Y = torch.empty((B, N), dtype=torch.float16, device=dev)
+            ws = torch.empty(hq.hqq_gemm_workspace_bytes(N, K, B), dtype=torch.uint8, device=dev)
+
+            def gm(r):
+                pk, d, z = copies[r % ncopy]
+                hq.hqq_gemm(pk, d, z, N, K, nbits, g, axis, X2, out=Y, workspace=ws)
+            tg = timed(gm, 2 * ncopy)
+            fl = 2.0 * B * N * K
+            legs["%s_b%d" % (name.replace("gemv", "gemm"), B)] = {
+                "us": tg * 1e6, "TFLOP/s": fl / tg / 1e12, "frac_mfma_f16": fl / tg / PEAK_FP16_MFMA, "shape": [N, K],
+                "copies_rotated": ncopy}
+            del X2, ws
         del copies
 
     log("config legs: 3-bit and 2-bit layer sets")

@@ -179,6 +179,23 @@ int hqq_gemm_w4a16(const void* packed, const void* delta_fp16, const void* zero_
                    size_t workspace_bytes, void* stream);
 
 /*
+ * The batched product for the other stored formats ("为什么一定要分组" for the containers,
+ * "从压缩文件到一次前向" for the product): y = x @ W_hat^T as hqq_gemm_w4a16, for codes of
+ * nbits = 2, 3 or 4 with axis-1 groups, stored as hqq_quantize wrote them.
+ *   packed, delta_fp16, zero_fp16, N, K, nbits, group_size, axis  as hqq_gemv.
+ *   x_fp16, batch, y, y_dtype  as hqq_gemm_w4a16.
+ *   workspace   at least hqq_gemm_workspace_bytes(N, K, batch) bytes, as hqq_gemm_w4a16.
+ * The same split MFMA kernel: only the weight tile's staging depends on the format (ten
+ * 3-bit codes per word, rows starting inside words; four 2-bit codes per byte).  N a multiple
+ * of 128, K of 512; group_size 64 or 128 for 4-bit codes (the hqq_gemm_w4a16 path), a power of
+ * two 16..256 for 2/3-bit codes; axis 0 and other shapes return HQQ_ERR_UNSUPPORTED.  Any
+ * batch >= 1 (batches 1 and 2 are cheaper through hqq_gemv).
+ */
+int hqq_gemm(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K, int nbits,
+             int group_size, int axis, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/*
  * Input gradient of the fused product, for training through frozen quantised weights
  * ("从压缩文件到一次前向": the forward is y = x @ W_hat^T, so dL/dx = dL/dy @ W_hat):
  *   dX[b, k] = sum_n dY[b, n] * (q[n, k] - zero[n, k/g]) * delta[n, k/g].

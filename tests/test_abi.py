@@ -103,6 +103,39 @@ def test_dequantize_and_gemv_reject(lib):
     assert gv(FAKE, FAKE, FAKE, 64, 256, 64, FAKE, 1, FAKE, 9, None) == hq.HQQ_ERR_INVALID_ARGUMENT
 
 
+def test_batched_products_reject(lib):
+    """hqq_gemm_w4a16, hqq_gemm (every stored format) and hqq_gemm_w4a16_dx check shapes, formats and
+    the workspace size before any launch."""
+    ws = lib.hqq_gemm_workspace_bytes(256, 1024, 32)
+    assert ws > 0 and lib.hqq_gemm_workspace_bytes(200, 1024, 32) == 0 and lib.hqq_gemm_workspace_bytes(256, 1000, 32) == 0
+    g = lib.hqq_gemm
+    ok = dict(N=256, K=1024, nbits=3, gs=64, axis=1, batch=32, ydt=0, wsb=ws)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return g(FAKE, FAKE, FAKE, a["N"], a["K"], a["nbits"], a["gs"], a["axis"], FAKE, a["batch"], FAKE, a["ydt"],
+                 FAKE, a["wsb"], None)
+    assert call(nbits=5) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(axis=2) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(gs=48) == hq.HQQ_ERR_INVALID_ARGUMENT          # does not divide K
+    assert call(axis=0) == hq.HQQ_ERR_UNSUPPORTED
+    assert call(nbits=4, gs=32) == hq.HQQ_ERR_UNSUPPORTED      # 4-bit: 64 or 128
+    assert call(nbits=2, gs=512) == hq.HQQ_ERR_UNSUPPORTED
+    assert call(N=192) == hq.HQQ_ERR_UNSUPPORTED               # N % 128
+    assert call(K=768) == hq.HQQ_ERR_UNSUPPORTED               # K % 512
+    assert call(ydt=7) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(wsb=ws - 16) == hq.HQQ_ERR_WORKSPACE
+    assert call(batch=0) == hq.HQQ_ERR_INVALID_ARGUMENT
+    w4 = lib.hqq_gemm_w4a16
+    assert w4(FAKE, FAKE, FAKE, 256, 1024, 32, FAKE, 32, FAKE, 0, FAKE, ws, None) == hq.HQQ_ERR_UNSUPPORTED
+    assert w4(FAKE, FAKE, FAKE, 256, 1024, 64, FAKE, 32, FAKE, 0, FAKE, ws - 16, None) == hq.HQQ_ERR_WORKSPACE
+    wdx = lib.hqq_gemm_dx_workspace_bytes(1024, 256, 32)
+    assert wdx > 0 and lib.hqq_gemm_dx_workspace_bytes(1000, 256, 32) == 0
+    dx = lib.hqq_gemm_w4a16_dx
+    assert dx(FAKE, FAKE, FAKE, 1024, 200, 64, FAKE, 32, FAKE, 0, FAKE, wdx, None) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert dx(FAKE, FAKE, FAKE, 1024, 256, 64, FAKE, 32, FAKE, 0, FAKE, wdx - 16, None) == hq.HQQ_ERR_WORKSPACE
+
+
 def test_status_strings(lib):
     assert hq.status_string(0) == "HQQ_OK"
     assert hq.status_string(3) == "HQQ_ERR_WORKSPACE"

@@ -111,3 +111,54 @@ def test_unsupported_formats_rejected():
         hq.hqq_gemv(pk, md, md, 64, 32, 3, 16, 1, x[:, :32].contiguous())
     with pytest.raises(hq.HQQError):  # batch 3 is not fused for these formats
         hq.hqq_gemv(pk, md, md, 64, 128, 4, 16, 0, torch.zeros((3, 128), dtype=torch.float16, device="cuda"))
+
+
+# ---------------------------------------------------------------- batched product (hqq_gemm)
+# 3-bit rows start at word slot n K mod 10: K = 512, 1024, 1536, 2048, 4096 give every even
+# residue; batches 3 .. 300 span one and two 256-row blocks; N from one to four 128-row tiles
+GEMM_CASES = [(3, 64, 128, 512, 3), (3, 16, 256, 1024, 9), (3, 32, 384, 2048, 100), (3, 128, 128, 1536, 256),
+              (3, 256, 512, 4096, 300), (2, 16, 128, 512, 5), (2, 32, 256, 1024, 64), (2, 16, 384, 4096, 257),
+              (2, 128, 128, 2048, 17), (2, 256, 256, 1536, 40), (4, 64, 256, 1024, 33), (4, 128, 128, 512, 3)]
+
+
+def _check_gemm(nbits, g, N, K, batch, seed, rows_sel=None):
+    torch = torch_dev()
+    import weight_only_quantization_amd as hq
+    o = oracle.get()
+    packed, delta, zero = _operands(seed, N, K, nbits, g, 1)
+    x = np.random.default_rng(seed + 1).normal(0, 1, (batch, K)).astype(np.float16)
+    yr = o.gemv_fmt(packed, delta.astype(np.float64), zero.astype(np.float64), N, K, nbits, g, 1,
+                    x.astype(np.float64), rows_sel=rows_sel)
+    scale = np.maximum(np.abs(yr), np.sqrt(np.mean(yr ** 2)))
+    pk, dl, zr = (torch.from_numpy(a).cuda() for a in (packed, delta, zero))
+    for out_dtype in (torch.float32, torch.float16):
+        y = hq.hqq_gemm(pk, dl, zr, N, K, nbits, g, 1, torch.from_numpy(x).cuda(),
+                        out_dtype=out_dtype).float().cpu().numpy().astype(np.float64)
+        yg = y if rows_sel is None else y[:, rows_sel]
+        err = float(np.max(np.abs(yg - yr) / scale))
+        say("  gemm N=%d K=%d b%d g%d batch=%d %s: max rel err %.3g" % (N, K, nbits, g, batch, out_dtype, err))
+        assert err <= GEMV_TOL
+
+
+@pytest.mark.parametrize("nbits,g,N,K,batch", GEMM_CASES, ids=lambda v: str(v))
+def test_gemm_formats(nbits, g, N, K, batch):
+    _check_gemm(nbits, g, N, K, batch, seed=4000 + 7 * nbits + g + N + K + batch)
+
+
+@pytest.mark.parametrize("nbits,g", [(3, 64), (2, 16)])
+def test_gemm_formats_full_shape(nbits, g):
+    """The 11008 x 4096 projection of the 3-bit and 2-bit layer sets at batch 256 (sampled rows)."""
+    sel = np.sort(np.random.default_rng(10 + nbits).choice(11008, 256, replace=False))
+    _check_gemm(nbits, g, 11008, 4096, 256, seed=4500 + nbits, rows_sel=sel)
+
+
+def test_gemm_formats_rejected():
+    torch = torch_dev()
+    import weight_only_quantization_amd as hq
+    pk = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    md = torch.zeros(1 << 14, dtype=torch.float16, device="cuda")
+    x = torch.zeros((4, 512), dtype=torch.float16, device="cuda")
+    for nbits, g, axis, N, K in ((3, 64, 0, 128, 512), (4, 32, 1, 128, 512), (2, 16, 1, 64, 512), (3, 16, 1, 128, 256),
+                                 (2, 512, 1, 128, 512), (5, 64, 1, 128, 512)):
+        with pytest.raises(hq.HQQError):
+            hq.hqq_gemm(pk, md, md, N, K, nbits, g, axis, x[:, :K].contiguous())

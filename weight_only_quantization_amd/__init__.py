@@ -29,7 +29,7 @@ HQQ_MAX_ITERS = 64
 # Every symbol the header declares.
 EXPORTS = ("hqq_packed_bytes", "hqq_num_groups", "hqq_quantize_workspace_bytes", "hqq_quantize",
            "hqq_dequantize", "hqq_gemv_w4a16", "hqq_gemm_workspace_bytes", "hqq_gemm_w4a16",
-           "hqq_gemm_dx_workspace_bytes", "hqq_gemm_w4a16_dx", "hqq_gemv",
+           "hqq_gemm_dx_workspace_bytes", "hqq_gemm_w4a16_dx", "hqq_gemv", "hqq_gemm",
            "hqq_status_string", "hqq_last_error")
 
 _lib = None
@@ -72,6 +72,8 @@ def load(path: str = LIB_PATH):
     lib.hqq_gemm_w4a16_dx.restype = i32
     lib.hqq_gemv.argtypes = [p, p, p, i64, i64, i32, i32, i32, p, i64, p, i32, p]
     lib.hqq_gemv.restype = i32
+    lib.hqq_gemm.argtypes = [p, p, p, i64, i64, i32, i32, i32, p, i64, p, i32, p, sz, p]
+    lib.hqq_gemm.restype = i32
     lib.hqq_status_string.argtypes = [i32]
     lib.hqq_status_string.restype = ctypes.c_char_p
     lib.hqq_last_error.argtypes = []
@@ -228,6 +230,28 @@ def hqq_gemm_w4a16(packed, delta, zero, N: int, K: int, group_size: int, x, out_
                             ctypes.c_void_p(zero.data_ptr()), N, K, group_size, ctypes.c_void_p(x.data_ptr()), batch,
                             ctypes.c_void_p(out.data_ptr()), code, ctypes.c_void_p(workspace.data_ptr()),
                             workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    _check(st)
+    return out
+
+
+def hqq_gemm(packed, delta, zero, N: int, K: int, nbits: int, group_size: int, axis: int, x, out_dtype=None,
+             out=None, workspace=None, stream=None):
+    """Batched y [batch, N] = x [batch, K] @ W_hat^T for 2-, 3- or 4-bit codes with axis-1 groups,
+    with a workspace as hqq_gemm_w4a16 (hqq_gemm_workspace_bytes(N, K, batch) bytes)."""
+    import torch
+    lib = load()
+    out_dtype = out_dtype or torch.float16
+    batch = x.shape[0]
+    if out is None:
+        out = torch.empty((batch, N), dtype=out_dtype, device=x.device)
+    need = lib.hqq_gemm_workspace_bytes(N, K, batch)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    code = HQQ_OUT_F16 if out.dtype == torch.float16 else HQQ_OUT_F32
+    st = lib.hqq_gemm(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                      ctypes.c_void_p(zero.data_ptr()), N, K, nbits, group_size, axis, ctypes.c_void_p(x.data_ptr()),
+                      batch, ctypes.c_void_p(out.data_ptr()), code, ctypes.c_void_p(workspace.data_ptr()),
+                      workspace.numel() * workspace.element_size(), _stream_ptr(stream))
     _check(st)
     return out
 

@@ -235,6 +235,41 @@ int hqq_gemm_w4a16(const void* packed, const void* delta_fp16, const void* zero_
   return HQQ_OK;
 }
 
+int hqq_gemm(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K, int nbits,
+             int group_size, int axis, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (N <= 0 || K <= 0 || batch <= 0) return fail(HQQ_ERR_INVALID_ARGUMENT, "N, K and batch must be positive");
+  if (N > (int64_t(1) << 31) || K > (int64_t(1) << 31) || batch > (int64_t(1) << 24))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "shape too large");
+  if (nbits != 2 && nbits != 3 && nbits != 4) return fail(HQQ_ERR_INVALID_ARGUMENT, "nbits must be 2, 3 or 4");
+  if (axis != 0 && axis != 1) return fail(HQQ_ERR_INVALID_ARGUMENT, "axis must be 0 or 1");
+  if (group_size <= 0 || (axis == 1 ? K : N) % group_size != 0)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "group_size must divide the grouped dimension");
+  if (axis != 1) return fail(HQQ_ERR_UNSUPPORTED, "the batched product takes axis-1 groups");
+  if (nbits == 4 ? (group_size != 64 && group_size != 128)
+                 : (group_size < 16 || group_size > 256 || (group_size & (group_size - 1)) != 0))
+    return fail(HQQ_ERR_UNSUPPORTED, "group_size 64 or 128 for 4-bit codes, a power of two 16..256 for 2/3-bit");
+  if (hqq::gemm_splits(N, K, batch) == 0)
+    return fail(HQQ_ERR_UNSUPPORTED, "N must be a multiple of 128 and K of 512");
+  if (y_dtype != HQQ_OUT_F16 && y_dtype != HQQ_OUT_F32)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "y_dtype must be HQQ_OUT_F16 or HQQ_OUT_F32");
+  if (!packed || !delta_fp16 || !zero_fp16 || !x_fp16 || !y || !workspace)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "null buffer");
+  if (!aligned16(packed) || !aligned16(delta_fp16) || !aligned16(zero_fp16) || !aligned16(x_fp16) || !aligned16(y) ||
+      !aligned16(workspace))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
+  const size_t need = hqq::gemm_workspace_bytes(N, K, batch);
+  if (workspace_bytes < need)
+    return fail(HQQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const hipError_t e = hqq::launch_gemm_fmt(
+      reinterpret_cast<const uint8_t*>(packed), reinterpret_cast<const __half*>(delta_fp16),
+      reinterpret_cast<const __half*>(zero_fp16), N, K, nbits, group_size, reinterpret_cast<const __half*>(x_fp16),
+      batch, y, y_dtype, workspace, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "hqq_gemm launch");
+  return HQQ_OK;
+}
+
 size_t hqq_gemm_dx_workspace_bytes(int64_t N, int64_t K, int64_t batch) {
   if (N <= 0 || K <= 0 || batch <= 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31) ||
       batch > (int64_t(1) << 24))

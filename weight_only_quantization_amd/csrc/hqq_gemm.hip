@@ -50,6 +50,41 @@ __device__ __forceinline__ u32x4 wq8(unsigned w, float ds24, float ds20, float z
   return u32x4{as_u(p0), as_u(p1), as_u(p2), as_u(p3)};
 }
 
+// Sixteen 2-bit codes of a word (natural order) -> fp16 W_hat pairs: lo = (c0,c1) .. (c6,c7),
+// hi = (c8,c9) .. (c14,c15).  The masks 3 << 2t on w and on w >> 8 give (c_t, c_t+8) and
+// (c_t+4, c_t+12) as fp16 subnormals at 4^t 2^-24; ds[t] = d 2^24 / 4^t.
+__device__ __forceinline__ void wq16_2b(unsigned w, const float (&ds)[4], float zd, u32x4& lo, u32x4& hi) {
+  const unsigned u = w >> 8;
+  f16x2 h[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    h[t] = as_h2(w & (0x00030003u << (2 * t)));
+    h[4 + t] = as_h2(u & (0x00030003u << (2 * t)));
+  }
+  auto pr = [&](int a, int b, int e) {  // codes of h[a] and h[b], element e (0 low, 1 high)
+    return as_u(f16x2{(_Float16)__builtin_fmaf((float)h[a][e], ds[a & 3], -zd),
+                      (_Float16)__builtin_fmaf((float)h[b][e], ds[b & 3], -zd)});
+  };
+  lo = u32x4{pr(0, 1, 0), pr(2, 3, 0), pr(4, 5, 0), pr(6, 7, 0)};
+  hi = u32x4{pr(0, 1, 1), pr(2, 3, 1), pr(4, 5, 1), pr(6, 7, 1)};
+}
+
+// Eight 3-bit codes in bits 0..23 of v (natural order) -> fp16 W_hat pairs (c0,c1) .. (c6,c7):
+// spread to two halves (codes 4..7 move up by 4 bits), the masks 7 << 3t give (c_t, c_t+4) at
+// 8^t 2^-24 for t < 3 and the fourth pair after a 9-bit shift.
+__device__ __forceinline__ u32x4 wq8_3b(unsigned v, float ds24, float ds21, float ds18, float zd) {
+  const unsigned x0 = (v & 0x00000FFFu) | ((v << 4) & 0x0FFF0000u);
+  const f16x2 h0 = as_h2(x0 & 0x00070007u), h1 = as_h2(x0 & 0x00380038u), h2 = as_h2(x0 & 0x01C001C0u),
+              h3 = as_h2((x0 >> 9) & 0x00070007u);
+  auto pr = [&](f16x2 a, float sa, f16x2 b, float sb, int e) {
+    return as_u(f16x2{(_Float16)__builtin_fmaf((float)a[e], sa, -zd), (_Float16)__builtin_fmaf((float)b[e], sb, -zd)});
+  };
+  return u32x4{pr(h0, ds24, h1, ds21, 0), pr(h2, ds18, h3, ds24, 0), pr(h0, ds24, h1, ds21, 1), pr(h2, ds18, h3, ds24, 1)};
+}
+
+// Stored formats the split GEMM stages (4-bit axis 1 has its group size as a template
+// parameter; the others take log2 of it at run time).
+constexpr int kFmt4 = 0, kFmt2 = 2, kFmt3 = 3;
 
 // TRANS = false: y [batch, N] = x [batch, K] @ W_hat^T (the forward product; output index n,
 //   contraction over k).  TRANS = true: dX [batch, K] = dY [batch, N] @ W_hat (its input
@@ -64,12 +99,13 @@ __device__ __forceinline__ u32x4 wq8(unsigned w, float ds24, float ds20, float z
 // that issued both would wait for the slow weight stream (HBM) whenever it needs its next
 // activations (L2); split by role, each waits only for its own stream.  Both roles pass the
 // same barriers: one after the first tile is staged and one per chunk.
-template <int GS, bool DIRECT, bool TRANS>
+template <int FMT, int GS, bool DIRECT, bool TRANS>
 __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restrict__ packed, const __half* __restrict__ delta,
                                                  const __half* __restrict__ zero, int64_t N, int64_t K, int64_t ks,
                                                  const u32x4* __restrict__ xt, int64_t MG, int64_t batch,
                                                  float* __restrict__ part, void* __restrict__ y, int out_dtype,
-                                                 int xcd_map) {
+                                                 int xcd_map, int gs_log2) {
+  static_assert(FMT == kFmt4 || !TRANS, "the input gradient is built for 4-bit codes");
   extern __shared__ _Float16 wt[];  // [2][kSkBN][kSkRow]
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t NO = TRANS ? K : N, KC = TRANS ? N : K;  // output and contraction lengths
@@ -98,96 +134,194 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
   const int64_t n0 = (int64_t)tile * kSkBN, m0 = (int64_t)blockIdx.y * kSkBM, k0 = (int64_t)split * ks;
   const int nch = (int)(ks / kSkBK);  // even, >= 2
 
-  if (wave >= kSkMulWaves) {
-    // ---------------------------------------------------------------- staging waves
-    // Forward: thread -> weight rows wr and 64 + wr (output rows of the tile), codes
-    // 32 wq .. 32 wq + 31 of each chunk.  Transposed: thread -> weight rows 2 wr and 2 wr + 1 of
-    // the chunk (contraction), codes 32 wq .. +31 of the tile's output columns.  16 bytes per
-    // row: one load instruction of a wave spans 16 (32) rows (each row of a 4-bit weight with
-    // K = 8192 is its own 4 KB page, and an instruction's distinct pages are translated one
-    // after another)
-    const int st = tid - 64 * kSkMulWaves;
-    const int wr = st >> 2, wq = st & 3;
-    const int64_t G_row = K / GS;  // groups per weight row
-    const uint8_t* wsrc;
-    const __half *dsrc, *zsrc;
-    int64_t wstride, mstride, wchunk, mchunk;
-    if constexpr (TRANS) {
-      wsrc = packed + (k0 + 2 * wr) * (K / 2) + (n0 + 32 * wq) / 2;
-      dsrc = delta + (k0 + 2 * wr) * G_row + (n0 + 32 * wq) / GS;
-      zsrc = zero + (k0 + 2 * wr) * G_row + (n0 + 32 * wq) / GS;
-      wstride = K / 2, mstride = G_row;                                   // the second row
-      wchunk = (int64_t)kSkBK * (K / 2), mchunk = (int64_t)kSkBK * G_row;  // the next chunk of rows
-    } else {
-      wsrc = packed + (n0 + wr) * (K / 2) + k0 / 2 + 16 * wq;
-      dsrc = delta + (n0 + wr) * G_row + (k0 + 32 * wq) / GS;
-      zsrc = zero + (n0 + wr) * G_row + (k0 + 32 * wq) / GS;
-      wstride = 64 * (K / 2), mstride = 64 * G_row;  // the second row pass
-      wchunk = kSkBK / 2, mchunk = kSkBK / GS;        // the next 128 codes
-    }
-    _Float16* wdst = wt + wr * kSkRow + 32 * wq;
-
-    auto load_w = [&](int c, u32x4 (&wv)[2], unsigned (&dm)[2], unsigned (&zm)[2]) {
-      const int cc = min(c, nch - 1);  // past the end: reload the last chunk (never used)
+  if constexpr (FMT != kFmt4) {
+    if (wave >= kSkMulWaves) {
+      // ---------------------------------------------------------------- staging waves, 2/3-bit
+      // thread -> weight rows wr and 64 + wr, codes 32 wq .. 32 wq + 31 of each chunk: flat code
+      // index f = n K + k, a multiple of 32 (K % 512 == 0).  2-bit: 8 bytes; 3-bit: ten codes per
+      // word, the 32 codes start at an even slot ph of word f / 10 and end inside the fourth word.
+      // With g = 16 codes 0..15 and 16..31 are two groups; otherwise one.
+      const int st = tid - 64 * kSkMulWaves;
+      const int wr = st >> 2, wq = st & 3;
+      _Float16* wdst = wt + wr * kSkRow + 32 * wq;
+      int64_t fr[2];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        wv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + p * wstride + cc * wchunk));
-        dm[p] = __half_as_ushort(dsrc[p * mstride + cc * mchunk]);
-        zm[p] = __half_as_ushort(zsrc[p * mstride + cc * mchunk]);
-      }
-    };
-    // the thread's share of one chunk -> LDS buffer `buf`, with the dequantisation constants of
-    // its rows' groups: z d and d 2^24, d 2^20 (all exact).  Forward: 16-byte stores.
-    // Transposed: the two rows' values of one output column paired into a dword.
-    auto stage = [&](int buf, const u32x4 (&wv)[2], const unsigned (&dm)[2], const unsigned (&zm)[2]) {
-      float zd[2], ds24[2], ds20[2];
+      for (int p = 0; p < 2; ++p) fr[p] = (n0 + wr + 64 * p) * K + k0 + 32 * wq;
+      struct Regs {
+        unsigned w[2][4], dm[2][2], zm[2][2];
+        int ph[2];
+      };
+      auto load_w = [&](int c, Regs& r) {
+        const int64_t cc = min(c, nch - 1);  // past the end: reload the last chunk (never used)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const float d = __half2float(__ushort_as_half((unsigned short)dm[p]));
-        const float z = __half2float(__ushort_as_half((unsigned short)zm[p]));
-        zd[p] = z * d, ds24[p] = d * 16777216.0f, ds20[p] = d * 1048576.0f;
-      }
-      _Float16* base = wt + buf * (kSkBN * kSkRow);
+        for (int p = 0; p < 2; ++p) {
+          const int64_t f0 = fr[p] + kSkBK * cc;
+          if constexpr (FMT == kFmt3) {
+            const int64_t q0 = f0 / 10;
+            r.ph[p] = (int)(f0 - 10 * q0);
+            const uint32_t* pw = reinterpret_cast<const uint32_t*>(packed) + q0;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if constexpr (TRANS) {
-          const u32x4 r0 = wq8(wv[0][s], ds24[0], ds20[0], zd[0]);
-          const u32x4 r1 = wq8(wv[1][s], ds24[1], ds20[1], zd[1]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int o = 32 * wq + 8 * s + e;  // output column in the tile; contraction 2 wr, 2 wr + 1
-            const unsigned v = __builtin_amdgcn_perm(r1[e >> 1], r0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-            const int blk = (wr >> 2) ^ (4 * (o >> 5));
-            *reinterpret_cast<unsigned*>(base + o * kSkRow + 8 * blk + 2 * (wr & 3)) = v;
+            for (int i = 0; i < 4; ++i) r.w[p][i] = pw[i];
+          } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(packed + f0 / 4);
+            r.w[p][0] = v.x, r.w[p][1] = v.y;
           }
-        } else {
-          const int p = s >> 1, h = s & 1;
-          _Float16* dst = wdst + buf * (kSkBN * kSkRow) + p * 64 * kSkRow;
 #pragma unroll
-          for (int i = 2 * h; i < 2 * h + 2; ++i)
-            *reinterpret_cast<u32x4*>(dst + 8 * i) = wq8(wv[p][i], ds24[p], ds20[p], zd[p]);
+          for (int h = 0; h < 2; ++h) {
+            const int64_t gi = (f0 + 16 * h) >> gs_log2;
+            r.dm[p][h] = __half_as_ushort(delta[gi]);
+            r.zm[p][h] = __half_as_ushort(zero[gi]);
+          }
         }
+      };
+      auto stage = [&](int buf, const Regs& r) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          float zd[2], d[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            d[h] = __half2float(__ushort_as_half((unsigned short)r.dm[p][h]));
+            zd[h] = __half2float(__ushort_as_half((unsigned short)r.zm[p][h])) * d[h];
+          }
+          _Float16* dst = wdst + buf * (kSkBN * kSkRow) + p * 64 * kSkRow;
+          if constexpr (FMT == kFmt2) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float ds[4] = {d[h] * 16777216.0f, d[h] * 4194304.0f, d[h] * 1048576.0f, d[h] * 262144.0f};
+              u32x4 lo, hi;
+              wq16_2b(r.w[p][h], ds, zd[h], lo, hi);
+              *reinterpret_cast<u32x4*>(dst + 16 * h) = lo;
+              *reinterpret_cast<u32x4*>(dst + 16 * h + 8) = hi;
+            }
+          } else {
+            // block b (codes 8b..8b+7) starts at slot o = ph + 8b of the window: in word o / 10,
+            // which is b - 1 or b (b >= 1) depending on ph; it ends in the next word or (o >= 30,
+            // then o / 10 = 3 and 3 (o - 30) + 24 <= 30) in the same one
+            const int ph = r.ph[p];
+            const unsigned* w = r.w[p];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const bool up = b > 0 && ph >= 2 * b;
+              const int i = up ? b : (b > 0 ? b - 1 : 0);
+              const unsigned lo = up ? w[b] : w[b > 0 ? b - 1 : 0];
+              const unsigned hi = up ? (b < 3 ? w[b + 1] : 0u) : w[b > 0 ? b : 1];
+              const int sh = 3 * (ph + 8 * b - 10 * i);
+              const unsigned v = (unsigned)((((uint64_t)hi << 30) | (lo & 0x3FFFFFFFu)) >> sh);
+              const int h = b >> 1;
+              *reinterpret_cast<u32x4*>(dst + 8 * b) =
+                  wq8_3b(v, d[h] * 16777216.0f, d[h] * 2097152.0f, d[h] * 262144.0f, zd[h]);
+            }
+          }
+        }
+      };
+      Regs ra, rb;
+      load_w(0, ra);
+      load_w(1, rb);
+      stage(0, ra);
+      load_w(2, ra);
+      lds_barrier();
+      for (int c = 0; c < nch; c += 2) {
+        stage(1, rb);  // chunk c + 1 (always < nch: nch is even)
+        load_w(c + 3, rb);
+        lds_barrier();
+        if (c + 2 < nch) stage(0, ra);  // chunk c + 2
+        load_w(c + 4, ra);
+        lds_barrier();
       }
-    };
-
-    // chunk c + 1 is staged while the multiplying waves use chunk c; the codes of chunk c + 3
-    // are requested right after, so each wait covers codes requested two chunks earlier
-    u32x4 wa[2], wb[2];
-    unsigned dma[2], zma[2], dmb[2], zmb[2];
-    load_w(0, wa, dma, zma);
-    load_w(1, wb, dmb, zmb);
-    stage(0, wa, dma, zma);
-    load_w(2, wa, dma, zma);
-    lds_barrier();
-    for (int c = 0; c < nch; c += 2) {
-      stage(1, wb, dmb, zmb);  // chunk c + 1 (always < nch: nch is even)
-      load_w(c + 3, wb, dmb, zmb);
-      lds_barrier();
-      if (c + 2 < nch) stage(0, wa, dma, zma);  // chunk c + 2
-      load_w(c + 4, wa, dma, zma);
-      lds_barrier();
+      return;
     }
-    return;
+  } else {
+    if (wave >= kSkMulWaves) {
+      // ---------------------------------------------------------------- staging waves, 4-bit
+      // Forward: thread -> weight rows wr and 64 + wr (output rows of the tile), codes
+      // 32 wq .. 32 wq + 31 of each chunk.  Transposed: thread -> weight rows 2 wr and 2 wr + 1 of
+      // the chunk (contraction), codes 32 wq .. +31 of the tile's output columns.  16 bytes per
+      // row: one load instruction of a wave spans 16 (32) rows (each row of a 4-bit weight with
+      // K = 8192 is its own 4 KB page, and an instruction's distinct pages are translated one
+      // after another)
+      const int st = tid - 64 * kSkMulWaves;
+      const int wr = st >> 2, wq = st & 3;
+      const int64_t G_row = K / GS;  // groups per weight row
+      const uint8_t* wsrc;
+      const __half *dsrc, *zsrc;
+      int64_t wstride, mstride, wchunk, mchunk;
+      if constexpr (TRANS) {
+        wsrc = packed + (k0 + 2 * wr) * (K / 2) + (n0 + 32 * wq) / 2;
+        dsrc = delta + (k0 + 2 * wr) * G_row + (n0 + 32 * wq) / GS;
+        zsrc = zero + (k0 + 2 * wr) * G_row + (n0 + 32 * wq) / GS;
+        wstride = K / 2, mstride = G_row;                                   // the second row
+        wchunk = (int64_t)kSkBK * (K / 2), mchunk = (int64_t)kSkBK * G_row;  // the next chunk of rows
+      } else {
+        wsrc = packed + (n0 + wr) * (K / 2) + k0 / 2 + 16 * wq;
+        dsrc = delta + (n0 + wr) * G_row + (k0 + 32 * wq) / GS;
+        zsrc = zero + (n0 + wr) * G_row + (k0 + 32 * wq) / GS;
+        wstride = 64 * (K / 2), mstride = 64 * G_row;  // the second row pass
+        wchunk = kSkBK / 2, mchunk = kSkBK / GS;        // the next 128 codes
+      }
+      _Float16* wdst = wt + wr * kSkRow + 32 * wq;
+
+      auto load_w = [&](int c, u32x4 (&wv)[2], unsigned (&dm)[2], unsigned (&zm)[2]) {
+        const int cc = min(c, nch - 1);  // past the end: reload the last chunk (never used)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          wv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + p * wstride + cc * wchunk));
+          dm[p] = __half_as_ushort(dsrc[p * mstride + cc * mchunk]);
+          zm[p] = __half_as_ushort(zsrc[p * mstride + cc * mchunk]);
+        }
+      };
+      // the thread's share of one chunk -> LDS buffer `buf`, with the dequantisation constants of
+      // its rows' groups: z d and d 2^24, d 2^20 (all exact).  Forward: 16-byte stores.
+      // Transposed: the two rows' values of one output column paired into a dword.
+      auto stage = [&](int buf, const u32x4 (&wv)[2], const unsigned (&dm)[2], const unsigned (&zm)[2]) {
+        float zd[2], ds24[2], ds20[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const float d = __half2float(__ushort_as_half((unsigned short)dm[p]));
+          const float z = __half2float(__ushort_as_half((unsigned short)zm[p]));
+          zd[p] = z * d, ds24[p] = d * 16777216.0f, ds20[p] = d * 1048576.0f;
+        }
+        _Float16* base = wt + buf * (kSkBN * kSkRow);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if constexpr (TRANS) {
+            const u32x4 r0 = wq8(wv[0][s], ds24[0], ds20[0], zd[0]);
+            const u32x4 r1 = wq8(wv[1][s], ds24[1], ds20[1], zd[1]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int o = 32 * wq + 8 * s + e;  // output column in the tile; contraction 2 wr, 2 wr + 1
+              const unsigned v = __builtin_amdgcn_perm(r1[e >> 1], r0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+              const int blk = (wr >> 2) ^ (4 * (o >> 5));
+              *reinterpret_cast<unsigned*>(base + o * kSkRow + 8 * blk + 2 * (wr & 3)) = v;
+            }
+          } else {
+            const int p = s >> 1, h = s & 1;
+            _Float16* dst = wdst + buf * (kSkBN * kSkRow) + p * 64 * kSkRow;
+#pragma unroll
+            for (int i = 2 * h; i < 2 * h + 2; ++i)
+              *reinterpret_cast<u32x4*>(dst + 8 * i) = wq8(wv[p][i], ds24[p], ds20[p], zd[p]);
+          }
+        }
+      };
+
+      // chunk c + 1 is staged while the multiplying waves use chunk c; the codes of chunk c + 3
+      // are requested right after, so each wait covers codes requested two chunks earlier
+      u32x4 wa[2], wb[2];
+      unsigned dma[2], zma[2], dmb[2], zmb[2];
+      load_w(0, wa, dma, zma);
+      load_w(1, wb, dmb, zmb);
+      stage(0, wa, dma, zma);
+      load_w(2, wa, dma, zma);
+      lds_barrier();
+      for (int c = 0; c < nch; c += 2) {
+        stage(1, wb, dmb, zmb);  // chunk c + 1 (always < nch: nch is even)
+        load_w(c + 3, wb, dmb, zmb);
+        lds_barrier();
+        if (c + 2 < nch) stage(0, wa, dma, zma);  // chunk c + 2
+        load_w(c + 4, wa, dma, zma);
+        lds_barrier();
+      }
+      return;
+    }
   }
 
   // ---------------------------------------------------------------- multiplying waves
@@ -346,9 +480,40 @@ size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t batch) {
 namespace {
 // One split product: tile the A operand (x, or dY for the input gradient) into fragments, the
 // split GEMM, and the sum over splits.  NO = output length (N, or K), KC = contraction (K, or N).
+template <int FMT, int GS, bool DIRECT, bool TRANS>
+void launch_sk(dim3 grid, hipStream_t st, const uint8_t* packed, const __half* delta, const __half* zero, int64_t N,
+               int64_t K, int64_t ks, const u32x4* xt, int64_t MG, int64_t batch, float* pw, void* out, int y_dtype,
+               int xcd_map, int gl) {
+  hipLaunchKernelGGL((k_gemm_sk<FMT, GS, DIRECT, TRANS>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K,
+                     ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+}
+
+template <bool DIRECT, bool TRANS>
+void launch_fmt(int fmt, int gs, dim3 grid, hipStream_t st, const uint8_t* packed, const __half* delta,
+                const __half* zero, int64_t N, int64_t K, int64_t ks, const u32x4* xt, int64_t MG, int64_t batch,
+                float* pw, void* out, int y_dtype, int xcd_map) {
+  int gl = 0;
+  while ((1 << gl) < gs) ++gl;
+  if constexpr (TRANS) {
+    if (gs == 64)
+      launch_sk<kFmt4, 64, DIRECT, true>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+    else
+      launch_sk<kFmt4, 128, DIRECT, true>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+  } else {
+    if (fmt == kFmt3)
+      launch_sk<kFmt3, 0, DIRECT, false>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+    else if (fmt == kFmt2)
+      launch_sk<kFmt2, 0, DIRECT, false>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+    else if (gs == 64)
+      launch_sk<kFmt4, 64, DIRECT, false>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+    else
+      launch_sk<kFmt4, 128, DIRECT, false>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+  }
+}
+
 template <bool TRANS>
-hipError_t launch_split(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int gs,
-                        const __half* a, int64_t batch, void* y, int y_dtype, void* workspace, hipStream_t st) {
+hipError_t launch_split(int fmt, const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                        int gs, const __half* a, int64_t batch, void* y, int y_dtype, void* workspace, hipStream_t st) {
   const int64_t NO = TRANS ? K : N, KC = TRANS ? N : K;
   const int S = gemm_splits(NO, KC, batch);
   const int64_t MG = (batch + kSkBM - 1) / kSkBM * (kSkBM / 16);
@@ -364,20 +529,10 @@ hipError_t launch_split(const uint8_t* packed, const __half* delta, const __half
   void* out = S == 1 ? y : nullptr;
   float* pw = S == 1 ? nullptr : part;
   if (S == 1) {
-    if (gs == 64)
-      hipLaunchKernelGGL((k_gemm_sk<64, true, TRANS>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks,
-                         xt, MG, batch, pw, out, y_dtype, xcd_map);
-    else
-      hipLaunchKernelGGL((k_gemm_sk<128, true, TRANS>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K,
-                         ks, xt, MG, batch, pw, out, y_dtype, xcd_map);
+    launch_fmt<true, TRANS>(fmt, gs, grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map);
     return hipGetLastError();
   }
-  if (gs == 64)
-    hipLaunchKernelGGL((k_gemm_sk<64, false, TRANS>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K, ks,
-                       xt, MG, batch, pw, out, y_dtype, xcd_map);
-  else
-    hipLaunchKernelGGL((k_gemm_sk<128, false, TRANS>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K,
-                       ks, xt, MG, batch, pw, out, y_dtype, xcd_map);
+  launch_fmt<false, TRANS>(fmt, gs, grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t MN = batch * NO;
@@ -389,13 +544,20 @@ hipError_t launch_split(const uint8_t* packed, const __half* delta, const __half
 hipError_t launch_gemm_split(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                              int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
                              hipStream_t st) {
-  return launch_split<false>(packed, delta, zero, N, K, gs, x, batch, y, y_dtype, workspace, st);
+  return launch_split<false>(kFmt4, packed, delta, zero, N, K, gs, x, batch, y, y_dtype, workspace, st);
+}
+
+hipError_t launch_gemm_fmt(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                           int nbits, int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
+                           hipStream_t st) {
+  const int fmt = nbits == 3 ? kFmt3 : nbits == 2 ? kFmt2 : kFmt4;
+  return launch_split<false>(fmt, packed, delta, zero, N, K, gs, x, batch, y, y_dtype, workspace, st);
 }
 
 hipError_t launch_gemm_dx(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                           int gs, const __half* dy, int64_t batch, void* dx, int dx_dtype, void* workspace,
                           hipStream_t st) {
-  return launch_split<true>(packed, delta, zero, N, K, gs, dy, batch, dx, dx_dtype, workspace, st);
+  return launch_split<true>(kFmt4, packed, delta, zero, N, K, gs, dy, batch, dx, dx_dtype, workspace, st);
 }
 
 }  // namespace hqq

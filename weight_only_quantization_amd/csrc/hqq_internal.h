@@ -57,6 +57,11 @@ size_t gemm_workspace_bytes(int64_t NO, int64_t KC, int64_t batch);
 hipError_t launch_gemm_split(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                              int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
                              hipStream_t st);
+// The same batched product for 2-, 3- and 4-bit codes with axis-1 groups (the staging waves
+// unpack the stored format; 4-bit takes group sizes 64 and 128, 2/3-bit 16..256).
+hipError_t launch_gemm_fmt(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                           int nbits, int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
+                           hipStream_t st);
 // Input gradient dX [batch, K] = dY [batch, N] @ W_hat with the same kernel transposed; its
 // workspace is gemm_workspace_bytes(K, N, batch) (output length first).
 hipError_t launch_gemm_dx(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
