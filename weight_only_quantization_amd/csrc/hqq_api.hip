@@ -145,7 +145,8 @@ int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int 
     m = fmin(m, a.thr[k]);
     a.thr_frozen[k] = m;
   }
-  hipError_t e = hqq::launch_quantize(a, nbits, group_size, axis, q.lds, rows * cols, mae_trace_dev, stop_iter_dev,
+  hipError_t e = hqq::launch_quantize(a, nbits, group_size, axis, q.threads, q.lds, rows * cols, mae_trace_dev,
+                                      stop_iter_dev,
                                       reinterpret_cast<double*>(ws + q.off_reduce),
                                       reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "hqq_quantize launch");

@@ -32,7 +32,8 @@ struct SolveArgs {
 
 // Quantizer: one solve pass (speculates that the loop runs all rounds), the device-side stop
 // decision, a fix-up pass that redoes the groups when the loop stopped early, 3-bit packing.
-hipError_t launch_quantize(const SolveArgs& a, int nbits, int group_size, int axis, size_t lds_bytes,
+// threads and lds_bytes are quant_geometry's for the configuration (the kernels assume them).
+hipError_t launch_quantize(const SolveArgs& a, int nbits, int group_size, int axis, int threads, size_t lds_bytes,
                            int64_t N, double* mae_trace, int32_t* stop_iter, double* reduce_ws, hipStream_t stream);
 // Per-round entries of the intermediate levels of the stop-decision reduction.
 int64_t reduce_scratch_entries(int64_t nblocks, int iters);

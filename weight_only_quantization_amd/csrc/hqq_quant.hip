@@ -358,18 +358,27 @@ __global__ void __launch_bounds__(256) k_quant_ax1(const SolveArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// axis = 0: group j = {i*M + j}, a column of the [g, M] view.  A block owns 64 adjacent
-// groups: it loads the g x 64 fp16 tile with 16-byte row loads into LDS, each lane then takes
+// axis = 0: group j = {i*M + j}, a column of the [g, M] view.  A block owns TW adjacent
+// groups: it loads the g x TW fp16 tile with 16-byte row loads into LDS, each lane then takes
 // E weights of one group from LDS; the codes go back through LDS for row-wise packed stores.
-// Block = L waves (64*L threads).
+// Block = 4 waves (TW = 4 GPW groups), as on axis 1: a lane's fp64 values and the round's
+// temporaries need more than 128 registers for g >= 32, and small blocks let three of them
+// share a compute unit at that size.
 // ------------------------------------------------------------------------------------------
+template <int G>
+constexpr int ax0_groups_per_block() { return 4 * Shape<G>::GPW; }
+template <int G>
+constexpr int ax0_threads() { return 64 * (ax0_groups_per_block<G>() / Shape<G>::GPW); }
+
 template <int NBITS, int G, bool FIX>
 __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int kmax, double* smem) {
   using S = Shape<G>;
   constexpr int E = S::E, L = S::L, GPW = S::GPW;
-  constexpr int TW = 64;          // groups per block
-  constexpr int ROW = TW + 8;     // LDS row stride in halves (16-byte aligned rows)
-  constexpr int NT = 64 * L;      // threads
+  constexpr int TW = ax0_groups_per_block<G>();  // groups per block
+  constexpr int CPR = TW / 8;                    // 8-column pieces per tile row
+  constexpr int ROW = TW + 8;                    // LDS row stride in halves (16-byte aligned rows)
+  constexpr int NT = ax0_threads<G>();           // threads
+  static_assert(NT == 256 && TW % 8 == 0 && (TW & (TW - 1)) == 0, "axis-0 block shape");
   double* meta_lds = smem;  // [2][TW]
   double* err_lds = smem + 2 * TW;  // [iters][TW]
   __half* wt = reinterpret_cast<__half*>(err_lds + (size_t)a.iters * TW);  // [G][ROW]
@@ -378,8 +387,8 @@ __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int k
   const int64_t M = a.G;
   const int64_t j0 = tile * TW;
   const int tid = threadIdx.x;
-  for (int task = tid; task < G * 8; task += NT) {
-    const int i = task >> 3, c = task & 7;
+  for (int task = tid; task < G * CPR; task += NT) {
+    const int i = task / CPR, c = task % CPR;
     const int64_t col = j0 + 8 * c;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (col < M) v = *reinterpret_cast<const uint4*>(a.W + (int64_t)i * M + col);
@@ -409,9 +418,9 @@ __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int k
     meta_lds[TW + acol] = z;
   }
   store_block_meta(a, meta_lds, TW, j0);  // its barrier also publishes the code tile
-  // Rows of 64 codes, 8 codes per task: flat index i*M + j0 + 8c (a multiple of 8).
-  for (int task = tid; task < G * 8; task += NT) {
-    const int i = task >> 3, cc = task & 7;
+  // Rows of TW codes, 8 codes per task: flat index i*M + j0 + 8c (a multiple of 8).
+  for (int task = tid; task < G * CPR; task += NT) {
+    const int i = task / CPR, cc = task % CPR;
     if (j0 + 8 * cc >= M) continue;
     const uint8_t* cr = ct + i * TW + 8 * cc;
     const int64_t f = (int64_t)i * M + j0 + 8 * cc;
@@ -433,7 +442,7 @@ __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int k
 }
 
 template <int NBITS, int G, bool FIX>
-__global__ void __launch_bounds__(1024) k_quant_ax0(const SolveArgs a) {
+__global__ void __launch_bounds__(ax0_threads<G>()) k_quant_ax0(const SolveArgs a) {
   extern __shared__ double smem[];
   int kmax = a.iters;
   if (FIX) {
@@ -550,6 +559,8 @@ __global__ void __launch_bounds__(256) k_pack3(const uint8_t* codes, int64_t N, 
 template <int NBITS, int G>
 hipError_t launch_cfg(const SolveArgs& a, int axis, int64_t nblocks, int threads, size_t lds, hipStream_t st,
                       bool fix) {
+  // the kernels index their tiles by a fixed block shape: refuse any other
+  if (threads != (axis == 1 ? 256 : ax0_threads<G>())) return hipErrorInvalidConfiguration;
   if (axis == 1) {
     if (fix)
       hipLaunchKernelGGL((k_quant_ax1<NBITS, G, true>), dim3(nblocks), dim3(threads), lds, st, a);
@@ -590,11 +601,12 @@ bool quant_geometry(int64_t G, int g, int axis, int iters, int64_t* nblocks, int
     *nblocks = (G + gpb - 1) / gpb;
     *threads = 256;
     *lds = (size_t)(iters + 2) * gpb * sizeof(double);
-  } else {
-    *nblocks = (G + 63) / 64;
-    *threads = 64 * L;
-    const size_t tile = (size_t)g * (64 + 8) * sizeof(__half);
-    *lds = (size_t)(iters + 2) * 64 * sizeof(double) + tile;
+  } else {  // the block shape of ax0_tile: tw groups, tw / gpw waves
+    const int tw = 4 * gpw;
+    *nblocks = (G + tw - 1) / tw;
+    *threads = 64 * (tw / gpw);
+    const size_t tile = (size_t)g * (tw + 8) * sizeof(__half);
+    *lds = (size_t)(iters + 2) * tw * sizeof(double) + tile;
   }
   return *lds <= 64 * 1024;
 }
@@ -610,10 +622,9 @@ int64_t reduce_scratch_entries(int64_t nblocks, int iters) {
   return total;
 }
 
-hipError_t launch_quantize(const SolveArgs& a, int nbits, int g, int axis, size_t lds, int64_t N, double* mae_trace,
-                           int32_t* stop_iter, double* reduce_ws, hipStream_t st) {
+hipError_t launch_quantize(const SolveArgs& a, int nbits, int g, int axis, int threads, size_t lds, int64_t N,
+                           double* mae_trace, int32_t* stop_iter, double* reduce_ws, hipStream_t st) {
   const int64_t nblocks = a.nblocks;
-  const int threads = axis == 1 ? 256 : 64 * lanes_per_group(g);
   hipError_t err = hipSuccess;
   auto solve = [&](bool fix, int64_t grid) {
     if (nbits == 4) return launch_bits<4>(a, g, axis, grid, threads, lds, st, fix);
