@@ -33,9 +33,12 @@ namespace {
 // GEMV, batch B <= 8.  Block = 8 waves on SPB 16-row strips; wave w takes the 128-code chunks
 // c = w, w + 8, ... of each K segment, for every strip of the block.  Per segment the
 // activations are staged in LDS in the operand order (x, with 1/16 on odd codes) together with
-// the per-group sums of x (staged once for all SPB strips); the next segment's loads are in
-// flight while the current one is multiplied.  The eight waves' partial results are added in a
-// fixed order at the end.
+// the per-group sums of x (staged once for all SPB strips), and so are the packed codes: wave w
+// loads whole row segments (rows w, w + 8, ...: one 1 KB run, one page, per load instruction;
+// the MFMA operand layout would put 16 rows, 16 pages, into every instruction) and each lane
+// then reads its 16-byte operand pieces from LDS.  The next segment's loads are in flight
+// while the current one is multiplied.  The eight waves' partial results are added in a fixed
+// order at the end.
 // ------------------------------------------------------------------------------------------
 template <int B>
 struct GemvCfg {
@@ -50,10 +53,14 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
   constexpr int CPW = GemvCfg<B>::CPW, KS = GemvCfg<B>::KS;
   constexpr int GPS = KS / GS;  // groups per segment
   constexpr int KSP = KS + 8;   // LDS row stride of x: padded so that rows fall in different banks
+  constexpr int WRB = KS / 2 + 16;  // LDS row stride of the packed codes (bytes; 16 rows, distinct banks)
+  constexpr int RPW = SPB * 2;      // weight rows each wave loads per segment
+  constexpr int PPL = KS / 32 / 64; // 16-byte pieces of a row segment per lane
   extern __shared__ float lds[];
   float* sx = lds;                                                     // [B][GPS]
   float* red = sx + B * GPS;                                           // [SPB][8][B][16]
   _Float16* xs = reinterpret_cast<_Float16*>(red + SPB * 8 * B * 16);  // [B][KSP]
+  uint8_t* wl = reinterpret_cast<uint8_t*>(xs + B * KSP);              // [16 SPB][WRB] packed codes
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -75,9 +82,9 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
   // are unconditional (clamped indexes): a load under a branch makes the compiler wait for it
   // before the branch joins; blocks and chunks past the end are never staged or never used.
   uint4 xr[XR];
-  uint4 v[SPB][CPW], vn[SPB][CPW];
+  uint4 wr[RPW][PPL];  // this wave's row segments of packed codes (PPL 16-byte pieces per lane and row)
   unsigned dm[SPB][CPW], zm[SPB][CPW], dmn[SPB][CPW], zmn[SPB][CPW];
-  auto load_segment = [&](int64_t kb0, uint4 (&w)[SPB][CPW], unsigned (&d)[SPB][CPW], unsigned (&z)[SPB][CPW]) {
+  auto load_segment = [&](int64_t kb0, unsigned (&d)[SPB][CPW], unsigned (&z)[SPB][CPW]) {
     const int nbs = (int)(((K - kb0 < KS) ? (K - kb0) : KS) / 8);
 #pragma unroll
     for (int j = 0; j < XR; ++j) {
@@ -91,7 +98,6 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
 #pragma unroll
       for (int i = 0; i < CPW; ++i) {
         const int64_t c = min(kb0 / 128 + wave + 8 * i, nchunks - 1);
-        w[sp][i] = ld_stream16(packed + n * (K / 2) + c * 64 + h * 16);
         if constexpr (GS == 64) {
           d[sp][i] = *reinterpret_cast<const unsigned*>(delta + n * gpr + 2 * c);
           z[sp][i] = *reinterpret_cast<const unsigned*>(zero + n * gpr + 2 * c);
@@ -101,8 +107,16 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
         }
       }
     }
+    {
+      const int pieces = (int)(((K - kb0 < KS) ? (K - kb0) : KS) / 32);  // 16-byte pieces of the segment's rows
+#pragma unroll
+      for (int j = 0; j < RPW; ++j)
+#pragma unroll
+        for (int q = 0; q < PPL; ++q)
+          wr[j][q] = ld_stream16(packed + (n0 + wave + 8 * j) * (K / 2) + kb0 / 2 + 16 * min(lane + 64 * q, pieces - 1));
+    }
   };
-  load_segment(0, v, dm, zm);
+  load_segment(0, dm, zm);
   for (int64_t kbase = 0; kbase < K; kbase += KS) {
     const int64_t cbase = kbase / 128;
     // 1. stage x in operand order (1/16 on the odd codes) with the per-group sums of x
@@ -122,10 +136,32 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
         if ((kb % (GS / 8)) == 0) sx[m * GPS + kb / (GS / 8)] = part;
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+#pragma unroll
+      for (int q = 0; q < PPL; ++q) *reinterpret_cast<uint4*>(wl + (wave + 8 * j) * WRB + 16 * (lane + 64 * q)) = wr[j][q];
+    // this segment's steps and zeros, requested with its codes (no earlier wait than the codes')
+    if (kbase > 0) {
+#pragma unroll
+      for (int sp = 0; sp < SPB; ++sp)
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+          dm[sp][i] = dmn[sp][i];
+          zm[sp][i] = zmn[sp][i];
+        }
+    }
+    lds_barrier();  // LDS hand-over
     // 2. the next segment's loads go out before this one is multiplied
     const bool more = kbase + KS < K;
-    if (more) load_segment(kbase + KS, vn, dmn, zmn);
+    if (more) load_segment(kbase + KS, dmn, zmn);
+    uint4 v[SPB][CPW];
+#pragma unroll
+    for (int sp = 0; sp < SPB; ++sp)
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const int cl = min(wave + 8 * i, KS / 128 - 1);  // chunk within the segment (unused when past the end)
+        v[sp][i] = *reinterpret_cast<const uint4*>(wl + (16 * sp + nl) * WRB + cl * 64 + h * 16);
+      }
 
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
@@ -190,17 +226,7 @@ __global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed
         }
       }
     }
-    __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int sp = 0; sp < SPB; ++sp)
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-          v[sp][i] = vn[sp][i];
-          dm[sp][i] = dmn[sp][i];
-          zm[sp][i] = zmn[sp][i];
-        }
-    }
+    lds_barrier();  // LDS hand-over; the next segment's loads stay in flight
   }
 #pragma unroll
   for (int sp = 0; sp < SPB; ++sp)
@@ -309,7 +335,7 @@ __global__ void __launch_bounds__(64 * W) k_gemv_valu(const uint8_t* __restrict_
     part = seg_sum_f<4>(part);  // the 4 lanes of a chunk are consecutive and active together
     if (t == 0) sxc[m * nch + c] = part;
   }
-  __syncthreads();
+  lds_barrier();  // LDS hand-over; the weight loads stay in flight
   f16x2 xq[XREG ? B : 1][XREG ? JMAX : 1][16];
   float sxr[B][JMAX];
 #pragma unroll
@@ -581,7 +607,8 @@ hipError_t gemv_valu(const uint8_t* packed, const __half* delta, const __half* z
 template <int B>
 size_t gemv_lds_b(int gs, int spb) {
   constexpr int KS = GemvCfg<B>::KS;
-  return (size_t)B * (KS / gs) * 4 + (size_t)spb * 8 * B * 16 * 4 + (size_t)B * (KS + 8) * 2;
+  return (size_t)B * (KS / gs) * 4 + (size_t)spb * 8 * B * 16 * 4 + (size_t)B * (KS + 8) * 2 +
+         (size_t)16 * spb * (KS / 2 + 16);
 }
 
 // Strips per block of the batched GEMV: two when that still leaves >= 256 blocks.

@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(64 * kAx0Waves) k_gemv_ax0(const uint8_t* __re
     const float v = wave_sum(zpart[b]);
     if (lane == 0) red[wave * B + b] = v;
   }
-  __syncthreads();
+  lds_barrier();  // LDS hand-over; the weight loads stay in flight
   float zb[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) {
@@ -288,7 +288,7 @@ __global__ void __launch_bounds__(64 * k2Waves) k_gemv_2b(const uint8_t* __restr
     xs[(m * 8 + 2 * t + 1) * nch + c] = o[1];
     sg[m * ngr + gi] = sum;
   }
-  __syncthreads();
+  lds_barrier();  // LDS hand-over; the weight loads stay in flight
   uint4 xq[XREG ? B : 1][XREG ? JMAX : 1][8];
   float sxr[B][JMAX][4];
 #pragma unroll
