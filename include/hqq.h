@@ -130,6 +130,52 @@ int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int 
                  void* workspace, size_t workspace_bytes, int32_t* stop_iter_dev, double* mae_trace_dev,
                  void* stream);
 
+/* Stop rules of hqq_quantize_ex: readings of "第二拍" (the loop stops at the first round k >= 1
+ * whose whole-tensor MAE is not below the best so far, and rolls back to the previous
+ * parameters; the page gives no result for a loop that never stops).  hqq_quantize uses 0. */
+#define HQQ_STOP_BEST 0         /* keep z_(k-1), the zero of the best round */
+#define HQQ_STOP_FAILED 1       /* keep z_k, the zero the failing round used */
+#define HQQ_STOP_NONE 2         /* keep z_(k+1), the update the failing round computed */
+#define HQQ_STOP_MEASURED_END 4 /* flag: a loop that never stops keeps z_(iters-1), the last zero
+                                   whose error was measured, instead of z_iters */
+/* Debug flags of hqq_quantize_ex.  The first two switch off exact shortcuts of the solver,
+ * so the results do not change; they exist to show that. */
+#define HQQ_DEBUG_NO_FROZEN_SKIP 1 /* run every round of every group (no fixed-point skip) */
+#define HQQ_DEBUG_SLOW_SHRINK 2    /* evaluate the shrink for every residual (no zero fast path) */
+#define HQQ_DEBUG_SYNC 4           /* wait for the stream after the launches and report a kernel
+                                      failure as HQQ_ERR_DEVICE (the call then blocks) */
+
+/* Arguments of hqq_quantize_ex: those of hqq_quantize, then the stop rule, the tiny-range
+ * threshold of the start (s = 1 when max - min <= tiny_range; >= 0, hqq_quantize uses
+ * HQQ_TINY_RANGE) and the debug flags. */
+typedef struct hqq_quant_args {
+  const void* W_fp16;
+  int64_t rows, cols;
+  int nbits, group_size, axis, iters;
+  double p, beta0, kappa;
+  void* packed;
+  void* delta;
+  void* zero;
+  int meta_dtype;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t* stop_iter_dev;
+  double* mae_trace_dev;
+  void* stream;
+  int stop_rule;
+  double tiny_range;
+  int debug_flags;
+} hqq_quant_args;
+
+/*
+ * hqq_quantize with the choices the page leaves open ("第一拍": the tiny-range threshold;
+ * "第二拍": which zero the stop keeps) and debug flags.  Same buffers, layout, ownership and
+ * asynchrony as hqq_quantize (except HQQ_DEBUG_SYNC); stop_iter_dev receives the index of
+ * the kept zero under the chosen rule.  Returns HQQ_ERR_INVALID_ARGUMENT for a NULL args, a
+ * stop_rule outside {0, 1, 2, 4, 5, 6}, a negative or non-finite tiny_range or unknown flags.
+ */
+int hqq_quantize_ex(const hqq_quant_args* args);
+
 /*
  * Standalone dequantisation ("量化公式", "从压缩文件到一次前向"):
  * W_out[i] = fp16((q_i - zero[j]) * delta[j]), j the group of flat element i.

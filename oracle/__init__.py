@@ -57,7 +57,10 @@ def _declare(lib):
         "hqq_oracle_round_group": (None, [p, i32, i32, dbl, dbl, dbl, dbl, dbl, p, p, p, p]),
         "hqq_oracle_stop_check": (i32, [i32, dbl, dbl]),
         "hqq_oracle_stop_iter": (i32, [p, i32, i32, p]),
+        "hqq_oracle_stop_iter_rule": (i32, [p, i32, i32, i32, p]),
         "hqq_oracle_quantize": (i32, [p, i64, i64, i32, i32, i32, i32, dbl, dbl, dbl, dbl, p, p, p, p, p, p, p]),
+        "hqq_oracle_quantize_rule": (i32, [p, i64, i64, i32, i32, i32, i32, dbl, dbl, dbl, dbl, i32, p, p, p, p, p,
+                                           p, p]),
         "hqq_oracle_quantize_groups": (i32, [p, i64, i32, i32, i32, dbl, dbl, dbl, dbl, p, p, p, p, p, p]),
         "hqq_oracle_packed_bytes": (i64, [i64, i32]),
         "hqq_oracle_pack": (i32, [p, i64, i32, p]),
@@ -120,15 +123,20 @@ class Oracle:
                                         ctypes.byref(zn), q.ctypes.data, e.ctypes.data)
         return err.value, zn.value, q, e
 
-    def stop_iter(self, mae, iters: int):
+    def stop_iter(self, mae, iters: int, rule: int = 0):
+        """(index of the kept zero, rounds evaluated) for a MAE sequence; rule as
+        hqq_oracle_stop_iter_rule (0: the page's rollback)."""
         mae = np.ascontiguousarray(mae, dtype=np.float64)
         r = ctypes.c_int()
-        k = self.lib.hqq_oracle_stop_iter(mae.ctypes.data, mae.size, iters, ctypes.byref(r))
+        if rule == 0:
+            k = self.lib.hqq_oracle_stop_iter(mae.ctypes.data, mae.size, iters, ctypes.byref(r))
+        else:
+            k = self.lib.hqq_oracle_stop_iter_rule(mae.ctypes.data, mae.size, iters, rule, ctypes.byref(r))
         return k, r.value
 
     # ---------------------------------------------------------------- quantizer
     def quantize(self, W, nbits=4, group_size=64, axis=1, iters=20, p=0.7, beta0=10.0, kappa=1.01,
-                 tiny=TINY_RANGE) -> dict:
+                 tiny=TINY_RANGE, stop_rule: int = 0) -> dict:
         """Whole-tensor HQQ.  W: 2-D array (fp16 or fp64 values).  Returns codes [rows, cols]
         (uint8), s / delta / z per group (fp64), the MAE of each evaluated round, the number
         of rounds evaluated and the index of the kept zero, plus the stored fp16 metadata."""
@@ -142,9 +150,15 @@ class Oracle:
         z = np.empty(G)
         mae = np.full(max(iters, 1), np.nan)
         rounds, kout = ctypes.c_int(), ctypes.c_int()
-        rc = self.lib.hqq_oracle_quantize(W64.ctypes.data, rows, cols, nbits, group_size, axis, iters, p, beta0,
-                                          kappa, tiny, codes.ctypes.data, s.ctypes.data, d.ctypes.data,
-                                          z.ctypes.data, mae.ctypes.data, ctypes.byref(rounds), ctypes.byref(kout))
+        if stop_rule == 0:
+            rc = self.lib.hqq_oracle_quantize(W64.ctypes.data, rows, cols, nbits, group_size, axis, iters, p, beta0,
+                                              kappa, tiny, codes.ctypes.data, s.ctypes.data, d.ctypes.data,
+                                              z.ctypes.data, mae.ctypes.data, ctypes.byref(rounds), ctypes.byref(kout))
+        else:
+            rc = self.lib.hqq_oracle_quantize_rule(W64.ctypes.data, rows, cols, nbits, group_size, axis, iters, p,
+                                                   beta0, kappa, tiny, stop_rule, codes.ctypes.data, s.ctypes.data,
+                                                   d.ctypes.data, z.ctypes.data, mae.ctypes.data,
+                                                   ctypes.byref(rounds), ctypes.byref(kout))
         if rc != 0:
             raise ValueError("oracle quantize rejected the arguments (rc=%d)" % rc)
         return {"codes": codes, "s": s, "delta": d, "z": z, "mae": mae[:rounds.value].copy(),

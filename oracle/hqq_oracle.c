@@ -178,20 +178,28 @@ void hqq_oracle_round_group(const double* w, int g, int nbits, double s, double 
 
 int hqq_oracle_stop_check(int k, double mae_k, double best) { return k >= 1 && !(mae_k < best); }
 
-/* Index of the kept zero for a given MAE sequence (n values available), and the number of
- * rounds the method evaluates. */
-int hqq_oracle_stop_iter(const double* mae, int n, int iters, int* rounds_out) {
+/* Index of the kept zero for a given MAE sequence (n values available) under a stop rule, and
+ * the number of rounds the method evaluates.  Rules (readings of "第二拍"; 0 is the page's
+ * "roll back to the previous parameters"): on a stop at round k, keep z_(k-1) (0), z_k, the
+ * zero the failing round used (1), or z_(k+1), the update it computed (2); flag 4: when the
+ * loop never stops, keep z_(iters-1), the last zero whose error was measured, not z_iters. */
+int hqq_oracle_stop_iter_rule(const double* mae, int n, int iters, int rule, int* rounds_out) {
   double best = INFINITY;
   int limit = n < iters ? n : iters;
   for (int k = 0; k < limit; k++) {
     if (hqq_oracle_stop_check(k, mae[k], best)) {
       if (rounds_out) *rounds_out = k + 1;
-      return PLANT(6) ? k : k - 1;
+      if ((rule & 3) == 0) return PLANT(6) ? k : k - 1;
+      return k - 1 + (rule & 3);
     }
     best = mae[k];
   }
   if (rounds_out) *rounds_out = limit;
-  return iters;
+  return ((rule & 4) && iters >= 1) ? iters - 1 : iters;
+}
+
+int hqq_oracle_stop_iter(const double* mae, int n, int iters, int* rounds_out) {
+  return hqq_oracle_stop_iter_rule(mae, n, iters, 0, rounds_out);
 }
 
 static int valid_shape(int64_t rows, int64_t cols, int nbits, int g, int axis) {
@@ -209,10 +217,13 @@ static int valid_shape(int64_t rows, int64_t cols, int nbits, int g, int axis) {
  * first *rounds_out entries are set), *kout_out = index of the kept zero.
  * ---------------------------------------------------------------------------------------- */
 
-int hqq_oracle_quantize(const double* W, int64_t rows, int64_t cols, int nbits, int g, int axis, int iters,
-                        double p, double beta0, double kappa, double tiny, uint8_t* codes, double* s_out,
-                        double* delta_out, double* z_out, double* mae_out, int* rounds_out, int* kout_out) {
-  if (!valid_shape(rows, cols, nbits, g, axis) || iters < 0) return -1;
+int hqq_oracle_quantize_rule(const double* W, int64_t rows, int64_t cols, int nbits, int g, int axis, int iters,
+                             double p, double beta0, double kappa, double tiny, int stop_rule, uint8_t* codes,
+                             double* s_out, double* delta_out, double* z_out, double* mae_out, int* rounds_out,
+                             int* kout_out) {
+  if (!valid_shape(rows, cols, nbits, g, axis) || iters < 0 || stop_rule < 0 || stop_rule > 6 ||
+      (stop_rule & 3) == 3)
+    return -1;
   const int64_t N = rows * cols;
   const int64_t G = N / g;
   /* The reshape of the group view, materialised group-major. */
@@ -240,6 +251,7 @@ int hqq_oracle_quantize(const double* W, int64_t rows, int64_t cols, int nbits, 
   double best = INFINITY;
   double beta = beta0;
   int kout = iters, rounds = 0, stopped = 0;
+  const double* zk = NULL;
   for (int k = 0; k < iters; k++) {
     for (int64_t j = 0; j < G; j++)
       hqq_oracle_round_group(Wg + j * g, g, nbits, s_out[j], delta_out[j], z_cur[j], beta, p, &gerr[j], &z_next[j],
@@ -248,7 +260,10 @@ int hqq_oracle_quantize(const double* W, int64_t rows, int64_t cols, int nbits, 
     mae_out[k] = mae;
     rounds = k + 1;
     if (hqq_oracle_stop_check(k, mae, best)) {
-      kout = PLANT(6) ? k : k - 1;
+      /* here z_prev = z_(k-1), z_cur = z_k (this round's zero), z_next = z_(k+1) (its update) */
+      const int shift = (stop_rule & 3) == 0 ? (PLANT(6) ? 1 : 0) : (stop_rule & 3);
+      kout = k - 1 + shift;
+      zk = shift == 0 ? z_prev : (shift == 1 ? z_cur : z_next);
       stopped = 1;
       break;
     }
@@ -259,8 +274,15 @@ int hqq_oracle_quantize(const double* W, int64_t rows, int64_t cols, int nbits, 
     z_next = t;
     if (!PLANT(11)) beta = beta * kappa;
   }
-  /* On a stop at round k, z_cur holds z_k and z_prev holds z_(k-1). */
-  const double* zk = (stopped && !PLANT(6)) ? z_prev : z_cur;
+  /* Ran to the end: z_cur = z_iters, z_prev = z_(iters-1). */
+  if (!stopped) {
+    if ((stop_rule & 4) && iters >= 1) {
+      kout = iters - 1;
+      zk = z_prev;
+    } else {
+      zk = z_cur;
+    }
+  }
 
   const double qmax = (double)((1 << nbits) - 1);
   for (int64_t j = 0; j < G; j++) {
@@ -280,6 +302,13 @@ int hqq_oracle_quantize(const double* W, int64_t rows, int64_t cols, int nbits, 
   free(zbuf);
   free(gerr);
   return 0;
+}
+
+int hqq_oracle_quantize(const double* W, int64_t rows, int64_t cols, int nbits, int g, int axis, int iters,
+                        double p, double beta0, double kappa, double tiny, uint8_t* codes, double* s_out,
+                        double* delta_out, double* z_out, double* mae_out, int* rounds_out, int* kout_out) {
+  return hqq_oracle_quantize_rule(W, rows, cols, nbits, g, axis, iters, p, beta0, kappa, tiny, 0, codes, s_out,
+                                  delta_out, z_out, mae_out, rounds_out, kout_out);
 }
 
 /* ------------------------------------------------------------------------------------------

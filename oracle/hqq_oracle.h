@@ -27,8 +27,9 @@
  * even; degenerate groups; the zero update as the least-squares minimiser (brute force);
  * L2 monotonicity without the shrink; pack/unpack exhaustively and the 4.5 bpw size;
  * dequantisation and the GEMV through one-hot and linearity checks; the input
- * gradient through the adjoint identity with the forward product and one-hot rows; binary16
- * conversions exhaustively against numpy.  Parity unpinned (readings, no value on the
+ * gradient through the adjoint identity with the forward product and one-hot rows; the stop
+ * rule's alternative readings on hand-built MAE sequences and against the per-group steps run
+ * for the kept number of rounds; binary16 conversions exhaustively against numpy.  Parity unpinned (readings, no value on the
  * page to check against): the shrink formula itself, the stop rule's rollback target
  * and tie handling, the summation order, and the solver's values on the full-size
  * synthetic tensors.
@@ -56,10 +57,17 @@ void hqq_oracle_round_group(const double* w, int g, int nbits, double s, double 
                             double p, double* err_sum, double* z_next, double* q_out, double* e_out);
 int hqq_oracle_stop_check(int k, double mae_k, double best);
 int hqq_oracle_stop_iter(const double* mae, int n, int iters, int* rounds_out);
+/* Stop rule: 0 keep z_(k-1) on a stop at round k (the page's rollback), 1 keep z_k, 2 keep
+ * z_(k+1); flag 4 keeps z_(iters-1) instead of z_iters when the loop never stops. */
+int hqq_oracle_stop_iter_rule(const double* mae, int n, int iters, int rule, int* rounds_out);
 
 int hqq_oracle_quantize(const double* W, int64_t rows, int64_t cols, int nbits, int g, int axis, int iters,
                         double p, double beta0, double kappa, double tiny, uint8_t* codes, double* s_out,
                         double* delta_out, double* z_out, double* mae_out, int* rounds_out, int* kout_out);
+int hqq_oracle_quantize_rule(const double* W, int64_t rows, int64_t cols, int nbits, int g, int axis, int iters,
+                             double p, double beta0, double kappa, double tiny, int stop_rule, uint8_t* codes,
+                             double* s_out, double* delta_out, double* z_out, double* mae_out, int* rounds_out,
+                             int* kout_out);
 int hqq_oracle_quantize_groups(const double* Wg, int64_t n, int g, int nbits, int kout, double p, double beta0,
                                double kappa, double tiny, uint8_t* codes, double* s_out, double* delta_out,
                                double* z_out, double* z_traj, double* err_traj);

@@ -49,13 +49,14 @@ def golden_for(workload, tensor, nbits, g, axis):
     raise KeyError((workload, tensor, nbits, g, axis))
 
 
-def gpu_quantize(W16: np.ndarray, nbits, g, axis, iters=20, p=0.7, beta0=10.0, kappa=1.01, meta="f64"):
-    """Quantize on the GPU; returns numpy copies of packed, delta, zero, stop index, MAE trace."""
+def gpu_quantize(W16: np.ndarray, nbits, g, axis, iters=20, p=0.7, beta0=10.0, kappa=1.01, meta="f64", **ex):
+    """Quantize on the GPU; returns numpy copies of packed, delta, zero, stop index, MAE trace.
+    `ex` (stop_rule, tiny_range, debug_flags) goes to hqq_quantize_ex."""
     torch = torch_dev()
     Wd = torch.from_numpy(np.ascontiguousarray(W16)).cuda()
     md = {"f16": torch.float16, "f32": torch.float32, "f64": torch.float64}[meta]
     q = hq.hqq_quantize(Wd, nbits=nbits, group_size=g, axis=axis, iters=iters, p=p, beta0=beta0, kappa=kappa,
-                        meta_dtype=md)
+                        meta_dtype=md, **ex)
     torch.cuda.synchronize()
     out = {"packed": q.packed.cpu().numpy(), "delta": q.delta.cpu().numpy(), "zero": q.zero.cpu().numpy(),
            "stop": int(q.stop_iter.cpu().numpy()[0]), "mae": q.mae_trace.cpu().numpy()}

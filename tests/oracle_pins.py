@@ -284,6 +284,44 @@ def pin_stop_in_solver(o):
     assert np.array_equal(g["codes"].reshape(W.shape), res["codes"])
 
 
+def pin_stop_rule_variants(o):
+    """The alternative readings of the rollback on hand-built MAE sequences: on a stop at round
+    k the kept zero is z_(k-1) (rule 0), z_k (1) or z_(k+1) (2); flag 4 changes only the result
+    of a loop that never stops (z_(iters-1) instead of z_iters); the rounds evaluated never
+    depend on the rule."""
+    cases = [([5, 4, 3, 3.5, 2], 5, 3), ([5, 4, 4], 3, 2), ([5, 6, 1], 3, 1)]
+    for mae, iters, kstar in cases:
+        for rule in (0, 1, 2, 4, 5, 6):
+            assert o.stop_iter(mae, iters, rule) == (kstar - 1 + (rule & 3), kstar + 1), (mae, rule)
+    for rule, expect in ((0, 4), (1, 4), (2, 4), (4, 3), (5, 3), (6, 3)):
+        assert o.stop_iter([5, 4, 3, 2], 4, rule) == (expect, 4)
+        assert o.stop_iter([], 0, rule) == (0, 0)
+
+
+def pin_stop_rule_zero_choice(o):
+    """Each rule keeps the zero it names: the codes and zeros equal those of the per-group steps
+    run for exactly that many rounds with no stop decision (k* - 1, k*, k* + 1 on a tensor that
+    stops at k*; iters - 1 under flag 4 on one that never stops)."""
+    r = _rng(23)
+    W = r.normal(0, 0.02, (8, 64)).astype(np.float16).astype(np.float64)
+    base = o.quantize(W, nbits=4, group_size=64, axis=1, iters=30)
+    kstar = base["rounds"] - 1
+    assert kstar + 1 <= 30 and base["kout"] == kstar - 1
+    for rule in (0, 1, 2):
+        res = o.quantize(W, nbits=4, group_size=64, axis=1, iters=30, stop_rule=rule)
+        assert res["kout"] == kstar - 1 + rule and res["rounds"] == base["rounds"]
+        assert np.array_equal(res["mae"], base["mae"])
+        g = o.quantize_groups(W.reshape(-1, 64), 4, kstar - 1 + rule)
+        assert np.array_equal(g["z"], res["z"]) and np.array_equal(g["codes"].reshape(W.shape), res["codes"])
+    W2 = r.normal(0, 0.02, (4, 128)).astype(np.float16).astype(np.float64)
+    full = o.quantize(W2, nbits=3, group_size=64, axis=1, iters=2)
+    assert full["rounds"] == 2 and full["kout"] == 2  # too few rounds to stop
+    res = o.quantize(W2, nbits=3, group_size=64, axis=1, iters=2, stop_rule=4)
+    g = o.quantize_groups(W2.reshape(-1, 64), 3, 1)
+    assert res["kout"] == 1 and np.array_equal(g["z"], res["z"])
+    assert np.array_equal(g["codes"].reshape(W2.shape), res["codes"])
+
+
 # ----------------------------------------------------------------------------- group view
 
 def pin_group_view(o):

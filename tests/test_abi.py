@@ -140,3 +140,27 @@ def test_status_strings(lib):
     assert hq.status_string(0) == "HQQ_OK"
     assert hq.status_string(3) == "HQQ_ERR_WORKSPACE"
     assert hq.status_string(99) == "HQQ_ERR_UNKNOWN"
+
+
+def test_quantize_ex_rejects_before_launch(lib):
+    """hqq_quantize_ex checks its own fields (stop rule, tiny range, flags) and then the same
+    arguments as hqq_quantize, before any launch."""
+    ws = lib.hqq_quantize_workspace_bytes(64, 128, 4, 64, 1, 20)
+
+    def call(**kw):
+        a = dict(W_fp16=FAKE.value, rows=64, cols=128, nbits=4, group_size=64, axis=1, iters=20, p=0.7, beta0=10.0,
+                 kappa=1.01, packed=FAKE.value, delta=FAKE.value, zero=FAKE.value, meta_dtype=0,
+                 workspace=FAKE.value, workspace_bytes=ws, stop_iter_dev=None, mae_trace_dev=None, stream=None,
+                 stop_rule=0, tiny_range=1e-4, debug_flags=0)
+        a.update(kw)
+        return lib.hqq_quantize_ex(ctypes.byref(hq.QuantArgs(**a)))
+    assert lib.hqq_quantize_ex(None) == hq.HQQ_ERR_INVALID_ARGUMENT
+    for rule in (-1, 3, 7, 8):
+        assert call(stop_rule=rule) == hq.HQQ_ERR_INVALID_ARGUMENT
+    for t in (-1e-4, float("inf"), float("nan")):
+        assert call(tiny_range=t) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(debug_flags=8) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(nbits=5) != hq.HQQ_OK                       # the shared checks of hqq_quantize follow
+    assert call(workspace_bytes=ws - 8) == hq.HQQ_ERR_WORKSPACE
+    assert call(p=0.0) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert hq.last_error() != ""

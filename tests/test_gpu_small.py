@@ -15,7 +15,7 @@ def weights(rows, cols, seed, sigma=0.02, frac=0.001, k=10.0):
 
 
 # shapes: several solve blocks and a partial last block (axis=1: 32 groups per block at g=64;
-# axis=0: 64 groups per block)
+# axis=0: 64 groups per block at g <= 32, 32 at g=64, 16 at g >= 128)
 CASES = [
     # nbits, g, axis, rows, cols
     (4, 64, 1, 37, 192),

@@ -25,9 +25,12 @@ HQQ_ERR_DEVICE = 4
 HQQ_META_F16, HQQ_META_F32, HQQ_META_F64 = 0, 1, 2
 HQQ_OUT_F16, HQQ_OUT_F32 = 0, 1
 HQQ_MAX_ITERS = 64
+HQQ_TINY_RANGE = 1e-4
+HQQ_STOP_BEST, HQQ_STOP_FAILED, HQQ_STOP_NONE, HQQ_STOP_MEASURED_END = 0, 1, 2, 4
+HQQ_DEBUG_NO_FROZEN_SKIP, HQQ_DEBUG_SLOW_SHRINK, HQQ_DEBUG_SYNC = 1, 2, 4
 
 # Every symbol the header declares.
-EXPORTS = ("hqq_packed_bytes", "hqq_num_groups", "hqq_quantize_workspace_bytes", "hqq_quantize",
+EXPORTS = ("hqq_packed_bytes", "hqq_num_groups", "hqq_quantize_workspace_bytes", "hqq_quantize", "hqq_quantize_ex",
            "hqq_dequantize", "hqq_gemv_w4a16", "hqq_gemm_workspace_bytes", "hqq_gemm_w4a16",
            "hqq_gemm_dx_workspace_bytes", "hqq_gemm_w4a16_dx", "hqq_gemv", "hqq_gemm",
            "hqq_status_string", "hqq_last_error")
@@ -58,6 +61,8 @@ def load(path: str = LIB_PATH):
     lib.hqq_quantize_workspace_bytes.restype = sz
     lib.hqq_quantize.argtypes = [p, i64, i64, i32, i32, i32, i32, dbl, dbl, dbl, p, p, p, i32, p, sz, p, p, p]
     lib.hqq_quantize.restype = i32
+    lib.hqq_quantize_ex.argtypes = [ctypes.POINTER(QuantArgs)]
+    lib.hqq_quantize_ex.restype = i32
     lib.hqq_dequantize.argtypes = [p, p, p, i32, i64, i64, i32, i32, i32, p, p]
     lib.hqq_dequantize.restype = i32
     lib.hqq_gemv_w4a16.argtypes = [p, p, p, i64, i64, i32, p, i64, p, i32, p]
@@ -143,11 +148,24 @@ class Quantized:
     mae_trace: "object"
 
 
+class QuantArgs(ctypes.Structure):
+    """hqq_quant_args of include/hqq.h (field order and C types as declared there)."""
+    _fields_ = [("W_fp16", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("nbits", ctypes.c_int), ("group_size", ctypes.c_int), ("axis", ctypes.c_int), ("iters", ctypes.c_int),
+                ("p", ctypes.c_double), ("beta0", ctypes.c_double), ("kappa", ctypes.c_double),
+                ("packed", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("zero", ctypes.c_void_p),
+                ("meta_dtype", ctypes.c_int), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("stop_iter_dev", ctypes.c_void_p), ("mae_trace_dev", ctypes.c_void_p), ("stream", ctypes.c_void_p),
+                ("stop_rule", ctypes.c_int), ("tiny_range", ctypes.c_double), ("debug_flags", ctypes.c_int)]
+
+
 def hqq_quantize(W, nbits: int = 4, group_size: int = 64, axis: int = 1, iters: int = 20, p: float = 0.7,
                  beta0: float = 10.0, kappa: float = 1.01, meta_dtype=None, workspace=None, out=None,
-                 stream=None) -> Quantized:
+                 stream=None, stop_rule: int = HQQ_STOP_BEST, tiny_range: float | None = None,
+                 debug_flags: int = 0) -> Quantized:
     """HQQ quantisation of a 2-D fp16 CUDA tensor.  Output buffers are torch tensors (or the
-    ones passed in `out` as (packed, delta, zero, stop_iter, mae_trace))."""
+    ones passed in `out` as (packed, delta, zero, stop_iter, mae_trace)).  A stop rule, tiny
+    range or debug flag other than the defaults goes through hqq_quantize_ex."""
     import torch
     lib = load()
     assert W.dtype == torch.float16 and W.is_cuda and W.dim() == 2 and W.is_contiguous()
@@ -166,12 +184,20 @@ def hqq_quantize(W, nbits: int = 4, group_size: int = 64, axis: int = 1, iters: 
     ws_bytes = lib.hqq_quantize_workspace_bytes(rows, cols, nbits, group_size, axis, iters)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    st = lib.hqq_quantize(ctypes.c_void_p(W.data_ptr()), rows, cols, nbits, group_size, axis, iters, p, beta0, kappa,
-                          ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
-                          ctypes.c_void_p(zero.data_ptr()), _meta_code(meta_dtype),
-                          ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
-                          ctypes.c_void_p(stop_iter.data_ptr()), ctypes.c_void_p(mae_trace.data_ptr()),
-                          _stream_ptr(stream))
+    if stop_rule == HQQ_STOP_BEST and tiny_range is None and debug_flags == 0:
+        st = lib.hqq_quantize(ctypes.c_void_p(W.data_ptr()), rows, cols, nbits, group_size, axis, iters, p, beta0,
+                              kappa, ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                              ctypes.c_void_p(zero.data_ptr()), _meta_code(meta_dtype),
+                              ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+                              ctypes.c_void_p(stop_iter.data_ptr()), ctypes.c_void_p(mae_trace.data_ptr()),
+                              _stream_ptr(stream))
+    else:
+        args = QuantArgs(W.data_ptr(), rows, cols, nbits, group_size, axis, iters, p, beta0, kappa, packed.data_ptr(),
+                         delta.data_ptr(), zero.data_ptr(), _meta_code(meta_dtype), workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), stop_iter.data_ptr(), mae_trace.data_ptr(),
+                         _stream_ptr(stream).value, stop_rule, HQQ_TINY_RANGE if tiny_range is None else tiny_range,
+                         debug_flags)
+        st = lib.hqq_quantize_ex(ctypes.byref(args))
     _check(st)
     return Quantized(packed, delta, zero, rows, cols, nbits, group_size, axis, stop_iter, mae_trace)
 

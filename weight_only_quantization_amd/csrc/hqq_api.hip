@@ -89,11 +89,20 @@ size_t hqq_quantize_workspace_bytes(int64_t rows, int64_t cols, int nbits, int g
   return q.total;
 }
 
-int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int group_size, int axis, int iters,
-                 double p, double beta0, double kappa, void* packed, void* delta, void* zero, int meta_dtype,
-                 void* workspace, size_t workspace_bytes, int32_t* stop_iter_dev, double* mae_trace_dev,
-                 void* stream) {
-  g_last_error[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// hqq_quantize and hqq_quantize_ex: validation, the solver's per-round constants, the launches.
+int quantize_impl(const hqq_quant_args& x) {
+  const void* W_fp16 = x.W_fp16;
+  const int64_t rows = x.rows, cols = x.cols;
+  const int nbits = x.nbits, group_size = x.group_size, axis = x.axis, iters = x.iters, meta_dtype = x.meta_dtype;
+  const double p = x.p, beta0 = x.beta0, kappa = x.kappa;
+  void *packed = x.packed, *delta = x.delta, *zero = x.zero, *workspace = x.workspace;
+  const size_t workspace_bytes = x.workspace_bytes;
+  int32_t* stop_iter_dev = x.stop_iter_dev;
+  double* mae_trace_dev = x.mae_trace_dev;
   int st = check_shape(rows, cols, nbits, group_size, axis);
   if (st != HQQ_OK) return st;
   if (iters < 0 || iters > HQQ_MAX_ITERS) return fail(HQQ_ERR_INVALID_ARGUMENT, "iters must be in [0, %d]", HQQ_MAX_ITERS);
@@ -129,7 +138,7 @@ int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int 
   a.iters = iters;
   a.meta_dtype = meta_dtype;
   a.qmax = (double)((1 << nbits) - 1);
-  a.tiny = HQQ_TINY_RANGE;
+  a.tiny = x.tiny_range;
   a.pm1 = p - 1.0;
   // beta_k by repeated products (beta grows by kappa after every round); thresholds of the
   // shrink: e = 0 exactly for |r| <= beta^(-1/(2-p)); a 1e-6 relative margin keeps the fast
@@ -143,14 +152,47 @@ int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int 
   double m = INFINITY;
   for (int k = iters - 1; k >= 0; --k) {
     m = fmin(m, a.thr[k]);
-    a.thr_frozen[k] = m;
+    a.thr_frozen[k] = (x.debug_flags & HQQ_DEBUG_NO_FROZEN_SKIP) ? -1.0 : m;  // -1: no group ever freezes
+    if (x.debug_flags & HQQ_DEBUG_SLOW_SHRINK) a.thr[k] = 0.0;               // every residual takes pow()
   }
-  hipError_t e = hqq::launch_quantize(a, nbits, group_size, axis, q.threads, q.lds, rows * cols, mae_trace_dev,
-                                      stop_iter_dev,
-                                      reinterpret_cast<double*>(ws + q.off_reduce),
-                                      reinterpret_cast<hipStream_t>(stream));
+  hipStream_t hs = reinterpret_cast<hipStream_t>(x.stream);
+  hipError_t e = hqq::launch_quantize(a, nbits, group_size, axis, q.threads, q.lds, rows * cols, x.stop_rule,
+                                      mae_trace_dev, stop_iter_dev, reinterpret_cast<double*>(ws + q.off_reduce),
+                                      hs);
   if (e != hipSuccess) return device_fail(e, "hqq_quantize launch");
+  if (x.debug_flags & HQQ_DEBUG_SYNC) {
+    e = hipStreamSynchronize(hs);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return device_fail(e, "hqq_quantize kernels");
+  }
   return HQQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int group_size, int axis, int iters,
+                 double p, double beta0, double kappa, void* packed, void* delta, void* zero, int meta_dtype,
+                 void* workspace, size_t workspace_bytes, int32_t* stop_iter_dev, double* mae_trace_dev,
+                 void* stream) {
+  g_last_error[0] = 0;
+  const hqq_quant_args x = {W_fp16, rows, cols, nbits, group_size, axis, iters, p, beta0, kappa, packed, delta,
+                            zero, meta_dtype, workspace, workspace_bytes, stop_iter_dev, mae_trace_dev, stream,
+                            HQQ_STOP_BEST, HQQ_TINY_RANGE, 0};
+  return quantize_impl(x);
+}
+
+int hqq_quantize_ex(const hqq_quant_args* args) {
+  g_last_error[0] = 0;
+  if (!args) return fail(HQQ_ERR_INVALID_ARGUMENT, "null args");
+  const int r = args->stop_rule;
+  if (r < 0 || r > 6 || (r & 3) == 3) return fail(HQQ_ERR_INVALID_ARGUMENT, "stop_rule must be 0, 1 or 2, optionally | 4");
+  if (!(args->tiny_range >= 0.0) || !isfinite(args->tiny_range))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "tiny_range must be finite and >= 0");
+  if (args->debug_flags & ~(HQQ_DEBUG_NO_FROZEN_SKIP | HQQ_DEBUG_SLOW_SHRINK | HQQ_DEBUG_SYNC))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "unknown debug flags");
+  return quantize_impl(*args);
 }
 
 int hqq_dequantize(const void* packed, const void* delta, const void* zero, int meta_dtype, int64_t rows,

@@ -34,7 +34,8 @@ struct SolveArgs {
 // decision, a fix-up pass that redoes the groups when the loop stopped early, 3-bit packing.
 // threads and lds_bytes are quant_geometry's for the configuration (the kernels assume them).
 hipError_t launch_quantize(const SolveArgs& a, int nbits, int group_size, int axis, int threads, size_t lds_bytes,
-                           int64_t N, double* mae_trace, int32_t* stop_iter, double* reduce_ws, hipStream_t stream);
+                           int64_t N, int stop_rule, double* mae_trace, int32_t* stop_iter, double* reduce_ws,
+                           hipStream_t stream);
 // Per-round entries of the intermediate levels of the stop-decision reduction.
 int64_t reduce_scratch_entries(int64_t nblocks, int iters);
 // Geometry of the solve kernel for a configuration: blocks, threads, dynamic LDS bytes.

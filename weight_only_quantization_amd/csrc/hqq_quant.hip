@@ -518,19 +518,21 @@ __global__ void __launch_bounds__(kRedThreads) k_reduce(const double* in, int64_
 }
 
 __global__ void __launch_bounds__(kRedThreads) k_decide(const double* partials, int64_t n, int iters, double N,
-                                                        int block_major, int32_t* ctrl, int32_t* stop_iter,
-                                                        double* mae_trace) {
+                                                        int block_major, int stop_rule, int32_t* ctrl,
+                                                        int32_t* stop_iter, double* mae_trace) {
   __shared__ double red[kRedLds];
   const int W = reduce_width(iters);
   load_level(red, partials, n, 0, iters, W, block_major != 0);
   lds_trees(red, iters, W);
   if (threadIdx.x == 0) {
     double best = __builtin_inf();
-    int kout = iters, rounds = iters;
+    // the rule (hqq_quantize_ex): on a stop at round k keep z_(k-1) (0), z_k (1) or z_(k+1) (2);
+    // flag 4 keeps z_(iters-1) instead of z_iters when the loop never stops
+    int kout = ((stop_rule & 4) && iters >= 1) ? iters - 1 : iters, rounds = iters;
     for (int k = 0; k < iters; ++k) {
       const double mae = red[k * W] / N;
       if (k >= 1 && !(mae < best)) {
-        kout = k - 1;
+        kout = k - 1 + (stop_rule & 3);
         rounds = k + 1;
         break;
       }
@@ -623,7 +625,8 @@ int64_t reduce_scratch_entries(int64_t nblocks, int iters) {
 }
 
 hipError_t launch_quantize(const SolveArgs& a, int nbits, int g, int axis, int threads, size_t lds, int64_t N,
-                           double* mae_trace, int32_t* stop_iter, double* reduce_ws, hipStream_t st) {
+                           int stop_rule, double* mae_trace, int32_t* stop_iter, double* reduce_ws,
+                           hipStream_t st) {
   const int64_t nblocks = a.nblocks;
   hipError_t err = hipSuccess;
   auto solve = [&](bool fix, int64_t grid) {
@@ -648,8 +651,8 @@ hipError_t launch_quantize(const SolveArgs& a, int nbits, int g, int axis, int t
     n = n_out;
     block_major = 0;
   }
-  hipLaunchKernelGGL(k_decide, dim3(1), dim3(kRedThreads), 0, st, level, n, a.iters, (double)N, block_major, a.ctrl,
-                     stop_iter, mae_trace);
+  hipLaunchKernelGGL(k_decide, dim3(1), dim3(kRedThreads), 0, st, level, n, a.iters, (double)N, block_major,
+                     stop_rule, a.ctrl, stop_iter, mae_trace);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // fix-up pass: a small grid (tiles in a loop), which returns at once when the loop ran to the end
   err = solve(true, nblocks < 1024 ? nblocks : 1024);
