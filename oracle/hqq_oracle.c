@@ -190,7 +190,7 @@ int hqq_oracle_stop_iter_rule(const double* mae, int n, int iters, int rule, int
     if (hqq_oracle_stop_check(k, mae[k], best)) {
       if (rounds_out) *rounds_out = k + 1;
       if ((rule & 3) == 0) return PLANT(6) ? k : k - 1;
-      return k - 1 + (rule & 3);
+      return k - 1 + (rule & 3) + (PLANT(19) && (rule & 3) == 1);
     }
     best = mae[k];
   }
@@ -261,7 +261,7 @@ int hqq_oracle_quantize_rule(const double* W, int64_t rows, int64_t cols, int nb
     rounds = k + 1;
     if (hqq_oracle_stop_check(k, mae, best)) {
       /* here z_prev = z_(k-1), z_cur = z_k (this round's zero), z_next = z_(k+1) (its update) */
-      const int shift = (stop_rule & 3) == 0 ? (PLANT(6) ? 1 : 0) : (stop_rule & 3);
+      const int shift = (stop_rule & 3) == 0 ? (PLANT(6) ? 1 : 0) : (stop_rule & 3) + (PLANT(19) && (stop_rule & 3) == 1);
       kout = k - 1 + shift;
       zk = shift == 0 ? z_prev : (shift == 1 ? z_cur : z_next);
       stopped = 1;
