@@ -63,20 +63,40 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(layer_tensor, q):
-    """The fp64 oracle as it stands, single-threaded on the host, on one 4096x4096 layer."""
+    """The fp64 oracle as it stands, single-threaded on the host (pinned to one core for the
+    call), on one 4096x4096 layer."""
     import numpy as np
 
     import oracle
     o = oracle.get()
     W = layer_tensor.make().astype(np.float64)
-    t0 = time.perf_counter()
-    r = o.quantize(W, nbits=q.nbits, group_size=q.group_size, axis=q.axis, iters=q.iters, p=q.p, beta0=q.beta0,
-                   kappa=q.kappa)
-    dt = time.perf_counter() - t0
+    allowed = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    if allowed:
+        os.sched_setaffinity(0, {min(allowed)})
+    try:
+        t0 = time.perf_counter()
+        r = o.quantize(W, nbits=q.nbits, group_size=q.group_size, axis=q.axis, iters=q.iters, p=q.p, beta0=q.beta0,
+                       kappa=q.kappa)
+        dt = time.perf_counter() - t0
+    finally:
+        if allowed:
+            os.sched_setaffinity(0, allowed)
     return {"value": W.size / dt / 1e9, "unit": "Gweights/s", "cores": 1, "kind": "oracle",
             "sample": "oracle quantize of one %dx%d layer (%s), 4-bit g64 axis=1, %d rounds evaluated, %.1f s"
-                      % (layer_tensor.rows, layer_tensor.cols, layer_tensor.name, r["rounds"], dt)}
+                      % (layer_tensor.rows, layer_tensor.cols, layer_tensor.name, r["rounds"], dt),
+            "cpu_model": _cpu_model(), "host_cores": os.cpu_count()}
 
 
 def sleep_rate(stream):
@@ -356,8 +376,21 @@ def main():
     flops = 2.0 * 256 * GN * GK
     legs["dx_b256"] = {"us": tg * 1e6, "TFLOP/s": flops / tg / 1e12, "frac_mfma_f16": flops / tg / PEAK_FP16_MFMA}
 
+    # a plain device copy on the same box: the HBM rate a kernel can reach in practice
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    tc = timed(lambda r: cdst.copy_(csrc), 20)
+    copy_bps = 2.0 * csrc.numel() / tc
+    legs["stream_copy_1GiB"] = {"us": tc * 1e6, "GB/s": copy_bps / 1e9, "frac_hbm": copy_bps / PEAK_HBM}
+    del csrc, cdst
+
     if not a.no_extra_legs:
         legs.update(config_legs(a, timed, stream, dev))
+    for leg in legs.values():  # every HBM fraction also against the measured copy rate
+        if "frac_hbm" in leg:
+            leg["frac_copy"] = leg["frac_hbm"] * PEAK_HBM / copy_bps
+        if "dequant_frac_hbm" in leg:
+            leg["dequant_frac_copy"] = leg["dequant_frac_hbm"] * PEAK_HBM / copy_bps
 
     if a.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
