@@ -521,7 +521,11 @@ __global__ void __launch_bounds__(kRedThreads) k_decide(const double* partials, 
                                                         int block_major, int stop_rule, int32_t* ctrl,
                                                         int32_t* stop_iter, double* mae_trace) {
   __shared__ double red[kRedLds];
-  const int W = reduce_width(iters);
+  __shared__ int s_rounds;
+  // the last tree spans the n <= reduce_width entries left, zero-padded to a power of two (the
+  // same sums as the full width: the padding adds zeros)
+  int W = 1;
+  while (W < n) W <<= 1;
   load_level(red, partials, n, 0, iters, W, block_major != 0);
   lds_trees(red, iters, W);
   if (threadIdx.x == 0) {
@@ -541,8 +545,12 @@ __global__ void __launch_bounds__(kRedThreads) k_decide(const double* partials, 
     ctrl[0] = kout;
     ctrl[1] = rounds;
     if (stop_iter) *stop_iter = kout;
-    if (mae_trace)
-      for (int k = 0; k < iters; ++k) mae_trace[k] = (k < rounds) ? red[k * W] / N : __builtin_nan("");
+    s_rounds = rounds;
+  }
+  __syncthreads();
+  if (mae_trace && (int)threadIdx.x < iters) {
+    const int k = threadIdx.x;
+    mae_trace[k] = (k < s_rounds) ? red[k * W] / N : __builtin_nan("");
   }
 }
 
