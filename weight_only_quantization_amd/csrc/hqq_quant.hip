@@ -46,9 +46,15 @@ constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8
 constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within 16
 
+// Every control used here names a valid source lane for every lane and all rows and banks are
+// enabled, so no lane keeps its old value: a plain DPP move of the two halves (no register
+// to pre-fill, unlike an update with an old operand).
 template <int CTRL>
 __device__ __forceinline__ double dpp(double v) {
-  return __builtin_amdgcn_update_dpp(0.0, v, CTRL, 0xF, 0xF, false);
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)b, CTRL, 0xF, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
 template <int L>
@@ -121,6 +127,14 @@ struct Shape {
   static constexpr int GPW = 64 / L;  // groups per wave
   static_assert(L >= 1 && L <= 16 && E * L == G, "group size");
 };
+
+// Waves per SIMD the axis-1 solve kernel is compiled for (the register budget is 512 / waves).
+// The solver is bound by fp64 latency rather than issue, so more resident waves pay: g <= 128
+// fits 4 (5 at g = 16) with a few spills outside the round loop; g = 256 (16 weights per lane)
+// keeps its natural 2.  The axis-0 kernel keeps its natural budget: its LDS staging would
+// spill some 24 registers at 128, which costs more than the fourth wave gains.
+template <int G>
+constexpr int solve_waves() { return G == 16 ? 5 : (G >= 256 ? 2 : 4); }
 
 // ------------------------------------------------------------------------------------------
 // One proximal round of one group (per lane: E weights).  Returns the group's sum of |r|,
@@ -195,9 +209,11 @@ __device__ __forceinline__ double solve_group(const SolveArgs& a, const double (
   for (int e = 0; e < E; ++e) ws[e] = w[e] * s;
 
   const double inv_g = 1.0 / (double)(E * L);
+  // canonicalised once here, not in every round's clip
+  const double qmax = __builtin_canonicalize(a.qmax);
   for (int k = 0; k < kmax; ++k) {
     double err, zn, maxr;
-    hqq_round<E, L>(w, ws, s, delta, z, a.qmax, a.beta[k], a.pm1, a.thr[k], inv_g, err, zn, maxr);
+    hqq_round<E, L>(w, ws, s, delta, z, qmax, a.beta[k], a.pm1, a.thr[k], inv_g, err, zn, maxr);
     if (write_err) err_lds[k * stride] = valid ? err : 0.0;
     const bool frozen = !valid || (zn == z && maxr <= a.thr_frozen[k]);
     z = zn;
@@ -342,7 +358,7 @@ __device__ __forceinline__ void ax1_tile(const SolveArgs& a, int64_t tile, int k
 }
 
 template <int NBITS, int G, bool FIX>
-__global__ void __launch_bounds__(256) k_quant_ax1(const SolveArgs a) {
+__global__ void __launch_bounds__(256, solve_waves<G>()) k_quant_ax1(const SolveArgs a) {
   extern __shared__ double err_lds[];  // [iters][groups per block], then [2][groups per block]
   constexpr int GPB = 4 * Shape<G>::GPW;
   double* meta_lds = err_lds + a.iters * GPB;
@@ -457,8 +473,9 @@ __global__ void __launch_bounds__(ax0_threads<G>()) k_quant_ax0(const SolveArgs 
 
 // ------------------------------------------------------------------------------------------
 // Stop decision ("第二拍"): MAE_k = (sum of the block sums, fixed order) / N; the loop stops
-// at the first k >= 1 with MAE_k not below the best so far and keeps z_(k-1); otherwise it
-// keeps z_iters.  One block of 256 threads.
+// at the first k >= 1 with MAE_k not below the best so far and keeps z_(k-1) (by default;
+// the rule argument picks z_(k-1), z_k or z_(k+1), and z_iters or z_(iters-1) when it never
+// stops).  k_reduce and k_decide run blocks of 1024 threads.
 // ------------------------------------------------------------------------------------------
 // Block sums of round k are combined as a balanced pairwise tree over the blocks in index
 // order, zero-padded to a power of two.  That tree splits into aligned subtrees of W leaves
@@ -598,7 +615,15 @@ hipError_t launch_bits(const SolveArgs& a, int g, int axis, int64_t nblocks, int
   }
 }
 
-int lanes_per_group(int g) { return g == 16 ? 4 : (g >= 256 ? 16 : g / 8); }
+int lanes_per_group(int g) {
+  switch (g) {
+    case 16: return Shape<16>::L;
+    case 32: return Shape<32>::L;
+    case 64: return Shape<64>::L;
+    case 128: return Shape<128>::L;
+    default: return Shape<256>::L;
+  }
+}
 
 }  // namespace
 
