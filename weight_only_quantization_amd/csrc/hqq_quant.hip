@@ -128,11 +128,12 @@ struct Shape {
   static_assert(L >= 1 && L <= 16 && E * L == G, "group size");
 };
 
-// Waves per SIMD the axis-1 solve kernel is compiled for (the register budget is 512 / waves).
+// Waves per SIMD the solve kernels are compiled for (the register budget is 512 / waves).
 // The solver is bound by fp64 latency rather than issue, so more resident waves pay: g <= 128
-// fits 4 (5 at g = 16) with a few spills outside the round loop; g = 256 (16 weights per lane)
-// keeps its natural 2.  The axis-0 kernel keeps its natural budget: its LDS staging would
-// spill some 24 registers at 128, which costs more than the fourth wave gains.
+// fits 4 (5 at g = 16); g = 256 (16 weights per lane) keeps its natural 2.  On axis 1 this
+// costs no spill; on axis 0 some ten registers of per-tile addresses spill outside the round
+// loop.  One wave more than that (5, or 6 at g = 16) spills inside the round loop and halves
+// the speed.
 template <int G>
 constexpr int solve_waves() { return G == 16 ? 5 : (G >= 256 ? 2 : 4); }
 
@@ -211,15 +212,18 @@ __device__ __forceinline__ double solve_group(const SolveArgs& a, const double (
   const double inv_g = 1.0 / (double)(E * L);
   // canonicalised once here, not in every round's clip
   const double qmax = __builtin_canonicalize(a.qmax);
+  double* slot = err_lds;  // round k's entry; the fill below continues from the same pointer
   for (int k = 0; k < kmax; ++k) {
     double err, zn, maxr;
     hqq_round<E, L>(w, ws, s, delta, z, qmax, a.beta[k], a.pm1, a.thr[k], inv_g, err, zn, maxr);
-    if (write_err) err_lds[k * stride] = valid ? err : 0.0;
+    const double ev = valid ? err : 0.0;
+    if (write_err) *slot = ev;
+    slot += stride;
     const bool frozen = !valid || (zn == z && maxr <= a.thr_frozen[k]);
     z = zn;
     if (__all(frozen)) {
       if (write_err)
-        for (int kk = k + 1; kk < a.iters; ++kk) err_lds[kk * stride] = valid ? err : 0.0;
+        for (int kk = k + 1; kk < a.iters; ++kk, slot += stride) *slot = ev;
       break;
     }
   }
@@ -258,13 +262,22 @@ __device__ __forceinline__ void write_partials(const SolveArgs& a, double* err_l
 
 // The block's step and zero, staged in LDS by one lane per group, go out as one contiguous
 // run per array (small scattered stores would each cost a whole memory burst).
+// The thread index through an empty asm statement: what is formed from it here is computed at
+// this point, not hoisted above the round loop where it would only hold registers.
+__device__ __forceinline__ int late_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// Wave 0 stores the steps and wave 1 the zeros (ng <= 64 groups per block), so the choice of
+// array is uniform per wave.
 __device__ __forceinline__ void store_block_meta(const SolveArgs& a, const double* meta_lds, int ng, int64_t g0) {
   __syncthreads();
-  const int t = threadIdx.x;
-  if (t < 2 * ng) {
-    const int i = t < ng ? t : t - ng;
-    if (g0 + i < a.G) store_meta(t < ng ? a.delta : a.zero, a.meta_dtype, g0 + i, meta_lds[t]);
-  }
+  const int t = late_tid();
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  if (wave < 2 && lane < ng && g0 + lane < a.G)
+    store_meta(wave == 0 ? a.delta : a.zero, a.meta_dtype, g0 + lane, meta_lds[wave * ng + lane]);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -276,7 +289,7 @@ __device__ __forceinline__ void ax1_tile(const SolveArgs& a, int64_t tile, int k
   using S = Shape<G>;
   constexpr int E = S::E, L = S::L, GPW = S::GPW;
   constexpr int GPB = 4 * GPW;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane / L, slot = lane % L;
   const int gblock = wave * GPW + sub;
   const int64_t gidx = tile * GPB + gblock;
@@ -412,7 +425,7 @@ __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int k
   }
   __syncthreads();
 
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sub = lane / L, slot = lane % L;
   const int acol = wave * GPW + sub;
   const int64_t gidx = j0 + acol;
@@ -427,15 +440,21 @@ __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int k
 
   unsigned c[E];
   final_codes<E>(ws, z, a.qmax, c);
+  {
+    // the same lane coordinates, formed again after the rounds (not held through them)
+    const int t = late_tid();
+    const int l2 = t & 63, w2 = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int slot2 = l2 % L, acol2 = w2 * GPW + l2 / L;
 #pragma unroll
-  for (int e = 0; e < E; ++e) ct[(slot * E + e) * TW + acol] = (uint8_t)c[e];
-  if (valid && slot == 0) {
-    meta_lds[acol] = delta;
-    meta_lds[TW + acol] = z;
+    for (int e = 0; e < E; ++e) ct[(slot2 * E + e) * TW + acol2] = (uint8_t)c[e];
+    if (valid && slot2 == 0) {
+      meta_lds[acol2] = delta;
+      meta_lds[TW + acol2] = z;
+    }
   }
   store_block_meta(a, meta_lds, TW, j0);  // its barrier also publishes the code tile
   // Rows of TW codes, 8 codes per task: flat index i*M + j0 + 8c (a multiple of 8).
-  for (int task = tid; task < G * CPR; task += NT) {
+  for (int task = late_tid(); task < G * CPR; task += NT) {
     const int i = task / CPR, cc = task % CPR;
     if (j0 + 8 * cc >= M) continue;
     const uint8_t* cr = ct + i * TW + 8 * cc;
@@ -458,7 +477,7 @@ __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int k
 }
 
 template <int NBITS, int G, bool FIX>
-__global__ void __launch_bounds__(ax0_threads<G>()) k_quant_ax0(const SolveArgs a) {
+__global__ void __launch_bounds__(ax0_threads<G>(), solve_waves<G>()) k_quant_ax0(const SolveArgs a) {
   extern __shared__ double smem[];
   int kmax = a.iters;
   if (FIX) {
