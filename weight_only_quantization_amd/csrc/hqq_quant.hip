@@ -634,6 +634,21 @@ hipError_t launch_bits(const SolveArgs& a, int g, int axis, int64_t nblocks, int
   }
 }
 
+// Blocks of the fix-up grid: one 4-wave block per compute unit for each wave per SIMD the
+// solve kernels are compiled for, so that a fix-up that has work runs at their occupancy.
+int64_t fix_grid(int g, int64_t nblocks) {
+  int waves;
+  switch (g) {
+    case 16: waves = solve_waves<16>(); break;
+    case 32: waves = solve_waves<32>(); break;
+    case 64: waves = solve_waves<64>(); break;
+    case 128: waves = solve_waves<128>(); break;
+    default: waves = solve_waves<256>(); break;
+  }
+  const int64_t full = 256 * (int64_t)waves;
+  return nblocks < full ? nblocks : full;
+}
+
 int lanes_per_group(int g) {
   switch (g) {
     case 16: return Shape<16>::L;
@@ -706,8 +721,9 @@ hipError_t launch_quantize(const SolveArgs& a, int nbits, int g, int axis, int t
   hipLaunchKernelGGL(k_decide, dim3(1), dim3(kRedThreads), 0, st, level, n, a.iters, (double)N, block_major,
                      stop_rule, a.ctrl, stop_iter, mae_trace);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  // fix-up pass: a small grid (tiles in a loop), which returns at once when the loop ran to the end
-  err = solve(true, nblocks < 1024 ? nblocks : 1024);
+  // fix-up pass: a grid of a few blocks per compute unit (tiles in a loop), which returns at once
+  // when the loop ran to the end
+  err = solve(true, fix_grid(g, nblocks));
   if (err != hipSuccess) return err;
   if (nbits == 3) {
     const int64_t nwords = (N + 9) / 10;
