@@ -243,25 +243,6 @@ __device__ __forceinline__ void final_codes(const double (&ws)[E], double z, dou
   }
 }
 
-// Sum of the per-group round errors of the block (pairwise, in group order, NG a power of
-// two) to the workspace.
-__device__ __forceinline__ void write_partials(const SolveArgs& a, double* err_lds, int ng, int64_t tile) {
-  for (int st = 1; st < ng; st <<= 1) {
-    __syncthreads();
-    const int pairs = ng / (2 * st);
-    for (int idx = threadIdx.x; idx < a.iters * pairs; idx += blockDim.x) {
-      const int k = idx / pairs, i = idx % pairs;
-      double* row = err_lds + k * ng;
-      row[2 * st * i] = row[2 * st * i] + row[2 * st * i + st];
-    }
-  }
-  __syncthreads();
-  // block-major [nblocks][iters]: one contiguous run per block
-  for (int k = threadIdx.x; k < a.iters; k += blockDim.x) a.partials[tile * a.iters + k] = err_lds[k * ng];
-}
-
-// The block's step and zero, staged in LDS by one lane per group, go out as one contiguous
-// run per array (small scattered stores would each cost a whole memory burst).
 // The thread index through an empty asm statement: what is formed from it here is computed at
 // this point, not hoisted above the round loop where it would only hold registers.
 __device__ __forceinline__ int late_tid() {
@@ -269,6 +250,53 @@ __device__ __forceinline__ int late_tid() {
   asm volatile("" : "+v"(t));
   return t;
 }
+
+// Sum of the two 16-lane rows of each 32-lane half (SWAP16 = true) or of the two 32-lane halves
+// of the wave, in every lane.  A swap of a register with itself gives the even (lower) and the
+// odd (upper) part broadcast over both, so their sum is left + right with no lane index.
+template <bool SWAP16>
+__device__ __forceinline__ double add_across(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned l = (unsigned)b, h = (unsigned)(b >> 32);
+  unsigned l0, l1, h0, h1;
+  if constexpr (SWAP16) {
+    const auto ls = __builtin_amdgcn_permlane16_swap(l, l, false, false);
+    const auto hs = __builtin_amdgcn_permlane16_swap(h, h, false, false);
+    l0 = ls[0]; l1 = ls[1]; h0 = hs[0]; h1 = hs[1];
+  } else {
+    const auto ls = __builtin_amdgcn_permlane32_swap(l, l, false, false);
+    const auto hs = __builtin_amdgcn_permlane32_swap(h, h, false, false);
+    l0 = ls[0]; l1 = ls[1]; h0 = hs[0]; h1 = hs[1];
+  }
+  return __longlong_as_double((long long)(((unsigned long long)h0 << 32) | l0)) +
+         __longlong_as_double((long long)(((unsigned long long)h1 << 32) | l1));
+}
+
+// Sum of the per-group round errors of the block (pairwise, in group order) to the
+// workspace, block-major [nblocks][iters].  One wave takes 64 / NG rounds at a time, lane
+// NG r + i holding group i of its round r: DPP steps inside rows of 16 lanes, then the sums of
+// row pairs and of wave halves (add_across).  After every step each lane of an aligned run holds that run's
+// sum (the adds are commutative), so this is the balanced pairwise tree over the NG groups;
+// no barrier after the first (a former LDS tree took one per level and an integer division
+// per element).
+template <int NG>
+__device__ __forceinline__ void write_partials(const SolveArgs& a, const double* err_lds, int64_t tile) {
+  static_assert(NG == 16 || NG == 32 || NG == 64, "groups per block");
+  constexpr int RPW = 64 / NG;  // rounds per wave and pass
+  __syncthreads();
+  const int t = late_tid();
+  const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int nw = blockDim.x >> 6, r = lane / NG, i = lane % NG;
+  for (int k0 = wave * RPW; k0 < a.iters; k0 += nw * RPW) {
+    const int k = k0 + r;
+    double v = (k < a.iters) ? err_lds[k * NG + i] : 0.0;
+    v = seg_sum<16>(v);
+    if constexpr (NG >= 32) v = add_across<true>(v);
+    if constexpr (NG >= 64) v = add_across<false>(v);
+    if (i == 0 && k < a.iters) a.partials[tile * a.iters + k] = v;
+  }
+}
+
 
 // Wave 0 stores the steps and wave 1 the zeros (ng <= 64 groups per block), so the choice of
 // array is uniform per wave.
@@ -367,7 +395,7 @@ __device__ __forceinline__ void ax1_tile(const SolveArgs& a, int64_t tile, int k
     }
   }
   store_block_meta(a, meta_lds, GPB, tile * GPB);
-  if (!FIX) write_partials(a, err_lds, GPB, tile);
+  if (!FIX) write_partials<GPB>(a, err_lds, tile);
 }
 
 template <int NBITS, int G, bool FIX>
@@ -473,7 +501,7 @@ __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int k
       *reinterpret_cast<uint2*>(a.codes_ws + f) = *reinterpret_cast<const uint2*>(cr);
     }
   }
-  if (!FIX) write_partials(a, err_lds, TW, tile);
+  if (!FIX) write_partials<TW>(a, err_lds, tile);
 }
 
 template <int NBITS, int G, bool FIX>
