@@ -525,80 +525,67 @@ __global__ void __launch_bounds__(ax0_threads<G>(), solve_waves<G>()) k_quant_ax
 // stops).  k_reduce and k_decide run blocks of 1024 threads.
 // ------------------------------------------------------------------------------------------
 // Block sums of round k are combined as a balanced pairwise tree over the blocks in index
-// order, zero-padded to a power of two.  That tree splits into aligned subtrees of W leaves
-// (W a power of two): k_reduce turns each run of W entries, for every round at once, into one
-// entry, until at most W remain; k_decide forms the last tree, MAE_k = sum / N, and applies
-// the stop rule.  All rounds share each tree level, so a level costs one barrier.
+// order, zero-padded to a power of two.  That tree splits into aligned subtrees of W = 256
+// leaves: k_reduce turns each run of W entries into one entry, until at most W remain;
+// k_decide forms the last tree, MAE_k = sum / N, and applies the stop rule.  Each tree is one
+// wave's register butterfly (no LDS, no barrier).
 constexpr int kRedThreads = 1024;
-constexpr int kRedLds = 6144;  // doubles of LDS for the trees (48 KiB)
+constexpr int kRedW = 256;  // entries per subtree: 64 lanes x 4
 
-// Width of the subtrees for `iters` rounds: the largest power of two <= 1024 with
-// iters * W doubles in LDS.
-__host__ __device__ inline int reduce_width(int iters) {
-  int w = 1024;
-  while (w > 1 && (int64_t)w * (iters > 0 ? iters : 1) > kRedLds) w >>= 1;
-  return w;
-}
+// Width of the subtrees (the same for every round count).
+__host__ __device__ inline int reduce_width(int) { return kRedW; }
 
-// red[k * W + i] for k < iters, i < W: pairwise tree over i, in place; result at red[k * W].
-__device__ __forceinline__ void lds_trees(double* red, int iters, int W) {
-  for (int st = 1; st < W; st <<= 1) {
-    __syncthreads();
-    const int pairs = W / (2 * st);
-    for (int idx = threadIdx.x; idx < iters * pairs; idx += blockDim.x) {
-      const int k = idx / pairs, j = idx % pairs;
-      red[k * W + 2 * st * j] = red[k * W + 2 * st * j] + red[k * W + 2 * st * j + st];
-    }
+// Balanced pairwise tree over entries base .. base + 255 of round k of a level (zero beyond
+// n_in): lane l holds entries 4l .. 4l + 3, adds them pairwise, then the DPP row steps and
+// the row-pair and half-wave sums complete the tree; every lane returns the total.  Entries:
+// block-major [n][iters] for the solver's per-block sums, round-major [iters][n] above.
+__device__ __forceinline__ double tree256(const double* in, int64_t n_in, int64_t base, int iters, int k,
+                                          bool block_major) {
+  const int lane = threadIdx.x & 63;
+  double v[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int64_t i = base + 4 * lane + c;
+    v[c] = 0.0;
+    if (i < n_in) v[c] = block_major ? in[i * iters + k] : in[(int64_t)k * n_in + i];
   }
-  __syncthreads();
+  double x = (v[0] + v[1]) + (v[2] + v[3]);
+  x = seg_sum<16>(x);
+  x = add_across<true>(x);
+  return add_across<false>(x);
 }
 
-// Entry i of round k of a level: block-major [n][iters] for the solver's per-block sums,
-// round-major [iters][n] for the intermediate levels.  Loads run along memory either way.
-__device__ __forceinline__ void load_level(double* red, const double* in, int64_t n_in, int64_t base, int iters,
-                                           int W, bool block_major) {
-  for (int idx = threadIdx.x; idx < iters * W; idx += blockDim.x) {
-    int k, i;
-    if (block_major) {
-      i = idx / iters;
-      k = idx % iters;
-    } else {
-      k = idx / W;
-      i = idx % W;
-    }
-    const int64_t e = block_major ? (base + i) * iters + k : (int64_t)k * n_in + base + i;
-    red[k * W + i] = (base + i < n_in) ? in[e] : 0.0;
-  }
-}
-
+// One block per run of kRedW entries; one wave per round.
 __global__ void __launch_bounds__(kRedThreads) k_reduce(const double* in, int64_t n_in, double* out, int64_t n_out,
                                                         int iters, int block_major) {
-  __shared__ double red[kRedLds];
-  const int W = reduce_width(iters);
-  const int64_t base = (int64_t)blockIdx.x * W;
-  load_level(red, in, n_in, base, iters, W, block_major != 0);
-  lds_trees(red, iters, W);
-  for (int k = threadIdx.x; k < iters; k += blockDim.x) out[(int64_t)k * n_out + blockIdx.x] = red[k * W];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
+  const int64_t base = (int64_t)blockIdx.x * kRedW;
+  for (int k = wave; k < iters; k += nw) {
+    const double x = tree256(in, n_in, base, iters, k, block_major != 0);
+    if ((threadIdx.x & 63) == 0) out[(int64_t)k * n_out + blockIdx.x] = x;
+  }
 }
 
+// The last tree over the n <= kRedW entries left (zero-padded: the padding adds zeros, so the
+// sums are those of the tree over next_pow2(n)), MAE_k = sum / N, and the stop rule.
 __global__ void __launch_bounds__(kRedThreads) k_decide(const double* partials, int64_t n, int iters, double N,
                                                         int block_major, int stop_rule, int32_t* ctrl,
                                                         int32_t* stop_iter, double* mae_trace) {
-  __shared__ double red[kRedLds];
+  __shared__ double sums[HQQ_MAX_ITERS];
   __shared__ int s_rounds;
-  // the last tree spans the n <= reduce_width entries left, zero-padded to a power of two (the
-  // same sums as the full width: the padding adds zeros)
-  int W = 1;
-  while (W < n) W <<= 1;
-  load_level(red, partials, n, 0, iters, W, block_major != 0);
-  lds_trees(red, iters, W);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
+  for (int k = wave; k < iters; k += nw) {
+    const double x = tree256(partials, n, 0, iters, k, block_major != 0);
+    if ((threadIdx.x & 63) == 0) sums[k] = x;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     double best = __builtin_inf();
     // the rule (hqq_quantize_ex): on a stop at round k keep z_(k-1) (0), z_k (1) or z_(k+1) (2);
     // flag 4 keeps z_(iters-1) instead of z_iters when the loop never stops
     int kout = ((stop_rule & 4) && iters >= 1) ? iters - 1 : iters, rounds = iters;
     for (int k = 0; k < iters; ++k) {
-      const double mae = red[k * W] / N;
+      const double mae = sums[k] / N;
       if (k >= 1 && !(mae < best)) {
         kout = k - 1 + (stop_rule & 3);
         rounds = k + 1;
@@ -612,10 +599,8 @@ __global__ void __launch_bounds__(kRedThreads) k_decide(const double* partials, 
     s_rounds = rounds;
   }
   __syncthreads();
-  if (mae_trace && (int)threadIdx.x < iters) {
-    const int k = threadIdx.x;
-    mae_trace[k] = (k < s_rounds) ? red[k * W] / N : __builtin_nan("");
-  }
+  if (mae_trace)
+    for (int k = threadIdx.x; k < iters; k += blockDim.x) mae_trace[k] = (k < s_rounds) ? sums[k] / N : __builtin_nan("");
 }
 
 // Ten 3-bit codes per 32-bit word, bits 3t, the last word padded with code 0.
