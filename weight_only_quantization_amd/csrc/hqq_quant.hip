@@ -31,7 +31,8 @@
 //
 // Shrink fast path: e = 0 exactly when |r| <= beta^(-1/(2-p)); the kernel takes e = 0 for
 // |r| below that threshold times (1 - 1e-6) (a margin far above the rounding of the
-// expression) and evaluates the shrink with pow() otherwise.
+// expression) and evaluates the shrink with pow() otherwise.  Both this and the freeze test
+// look at each lane's sum of |r|, an upper bound of every |r| of the lane.
 
 #include "hqq_internal.h"
 
@@ -139,14 +140,16 @@ constexpr int solve_waves() { return G == 16 ? 5 : (G >= 256 ? 2 : 4); }
 
 // ------------------------------------------------------------------------------------------
 // One proximal round of one group (per lane: E weights).  Returns the group's sum of |r|,
-// the next zero and this lane's largest |r|.
+// the next zero and a bound on this lane's largest |r|: the lane's own pairwise sum of |r|
+// (a rounded sum of non-negative terms is at least each term), which the shrink and freeze
+// tests use in place of the maximum (both stay sufficient; the maximum would cost an
+// instruction per weight and round).
 // ------------------------------------------------------------------------------------------
 template <int E, int L>
 __device__ __forceinline__ void hqq_round(const double (&w)[E], const double (&ws)[E], double s, double delta,
                                           double z, double qmax, double beta, double pm1, double thr,
                                           double inv_g, double& err_o, double& zn_o, double& maxr_o) {
   double ar[E], tm[E];
-  double maxr = 0.0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const double t = ws[e] + z;
@@ -156,10 +159,10 @@ __device__ __forceinline__ void hqq_round(const double (&w)[E], const double (&w
     const double wh = (qq - z) * delta;
     const double rr = w[e] - wh;
     ar[e] = fabs(rr);
-    maxr = fmax(maxr, ar[e]);
     tm[e] = qq - ws[e];  // e = 0: (W - e)*s is W*s
   }
-  if (__any(maxr >= thr)) {
+  const double err = tree_sum<0, E, E>(ar);
+  if (__any(err >= thr)) {
     // Some residual of the wave may pass the shrink: redo the terms with the shrink evaluated
     // wherever it can be non-zero (q and r recomputed identically).
 #pragma unroll
@@ -179,11 +182,10 @@ __device__ __forceinline__ void hqq_round(const double (&w)[E], const double (&w
       tm[e] = (ee == 0.0) ? (qq - ws[e]) : (qq - (w[e] - ee) * s);
     }
   }
-  const double err = tree_sum<0, E, E>(ar);
   const double acc = tree_sum<0, E, E>(tm);
   err_o = seg_sum<L>(err);
   zn_o = seg_sum<L>(acc) * inv_g;
-  maxr_o = maxr;
+  maxr_o = err;
 }
 
 // Start of a group from its weights (min-max), then the rounds.  Returns the final zero.
