@@ -353,6 +353,97 @@ int hqq_oracle_quantize_groups(const double* Wg, int64_t n, int g, int nbits, in
 }
 
 /* ------------------------------------------------------------------------------------------
+ * Scale search (the slower second solver the pages name next to the default one, "第二拍":
+ * it can grid-search the scale, while the default keeps the min-max scale and only refines
+ * the zero).  The pages give its name and purpose only; the reading here, PARITY UNPINNED as
+ * to what the reference project computes:
+ *   per group (axis 1), for each multiplier c_j of a caller-given grid: s = s0 * c_j with s0
+ *   the min-max start (then the same 2e4 limit), delta = 1/s, z0 = -min*s; the default
+ *   proximal rounds with the default rule applied to the group's own error sum (the first
+ *   k >= 1 whose sum is not below the previous one stops the loop and keeps z_(k-1); no stop
+ *   keeps z_iters); the candidate's error is the pairwise sum of |W - W_hat| of its final
+ *   codes.  Candidate 0 is taken first and a later one replaces it only with a strictly
+ *   smaller error.  Outputs as hqq_oracle_quantize, plus the chosen index per group.
+ * With one group and the grid {1} this is the default solver exactly (g is a power of two,
+ * so the MAE is the error sum divided exactly).
+ * ---------------------------------------------------------------------------------------- */
+
+static double candidate_error(const double* w, int g, int nbits, double s, double delta, double z) {
+  const double qmax = (double)((1 << nbits) - 1);
+  double absr[g];
+  for (int i = 0; i < g; i++) {
+    double t = w[i] * s;
+    t = t + z;
+    double q = rint(t);
+    if (q < 0.0) q = 0.0;
+    if (q > qmax) q = qmax;
+    absr[i] = fabs(w[i] - (q - z) * delta);
+  }
+  return hqq_oracle_sum(absr, g);
+}
+
+int hqq_oracle_quantize_v2(const double* W, int64_t rows, int64_t cols, int nbits, int g, int iters, double p,
+                           double beta0, double kappa, double tiny, const double* grid, int ncand, uint8_t* codes,
+                           double* s_out, double* delta_out, double* z_out, uint8_t* choice_out) {
+  if (!valid_shape(rows, cols, nbits, g, 1) || iters < 0 || ncand < 1 || ncand > 255) return -1;
+  const int64_t G = rows * cols / g;
+  const double qmax = (double)((1 << nbits) - 1);
+  for (int64_t j = 0; j < G; j++) {
+    const double* w = W + j * g; /* axis 1: group j is the run of g consecutive weights */
+    double mn = w[0], mx = w[0];
+    for (int i = 1; i < g; i++) {
+      if (w[i] < mn) mn = w[i];
+      if (w[i] > mx) mx = w[i];
+    }
+    /* the min-max start before its 2e4 limit: the multiplier scales it, then the limit */
+    const double d = mx - mn;
+    const double sb = (d <= tiny) ? 1.0 : qmax / d;
+    double best_e = 0.0, best_s = 0.0, best_delta = 0.0, best_z = 0.0;
+    int best_c = 0;
+    for (int c = 0; c < ncand; c++) {
+      double s = sb * grid[c];
+      if (s > 2.0e4) s = 2.0e4;
+      const double delta = 1.0 / s;
+      double z = -mn * s;
+      double zprev = z, best = INFINITY, beta = beta0;
+      for (int k = 0; k < iters; k++) {
+        double err, zn;
+        hqq_oracle_round_group(w, g, nbits, s, delta, z, beta, p, &err, &zn, NULL, NULL);
+        if (k >= 1 && !(err < best)) { /* stop: keep z_(k-1) */
+          z = zprev;
+          break;
+        }
+        best = err;
+        zprev = z;
+        z = zn;
+        beta = beta * kappa;
+      }
+      const double e = candidate_error(w, g, nbits, s, delta, z);
+      if (c == 0 || (PLANT(20) ? e > best_e : e < best_e)) {
+        best_e = e;
+        best_s = s;
+        best_delta = delta;
+        best_z = z;
+        best_c = c;
+      }
+    }
+    s_out[j] = best_s;
+    delta_out[j] = best_delta;
+    z_out[j] = best_z;
+    if (choice_out) choice_out[j] = (uint8_t)best_c;
+    for (int i = 0; i < g; i++) {
+      double t = w[i] * best_s;
+      t = t + best_z;
+      double q = rint(t);
+      if (q < 0.0) q = 0.0;
+      if (q > qmax) q = qmax;
+      codes[j * g + i] = (uint8_t)q;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------------
  * Bit-packing ("为什么一定要分组": two 4-bit codes per uint8, four 2-bit codes per byte, ten
  * 3-bit codes per 32-bit integer).  Reading of the layout: codes in flat row-major order,
  * little-endian within the container: 4-bit byte j = c[2j] + 16*c[2j+1]; 2-bit byte j =

@@ -556,4 +556,56 @@ def pin_group_steps_consistent(o):
         assert np.array_equal(cg.reshape(W.shape), res["codes"])
 
 
+# ----------------------------------------------------------------------------- scale search
+
+def _group_error(o, Wg, codes, z, delta):
+    """Pairwise sum of |W - W_hat| per group for given codes / zero / step."""
+    what = (codes.astype(np.float64) - z[:, None]) * delta[:, None]
+    return np.array([o.sum(np.abs(Wg[j] - what[j])) for j in range(Wg.shape[0])])
+
+
+def pin_scale_search_identity(o):
+    """With the single multiplier 1 the scale search is the default solver run on each group
+    alone: every group of a many-group tensor gets the codes, scale and zero that the default
+    whole-tensor solver gives a tensor made of that group only (its MAE is the group's error
+    sum divided exactly by g, a power of two, so the global stop is the group's own); iters = 0
+    is min-max round-to-nearest."""
+    r = _rng(31)
+    for nbits, g, iters in ((4, 64, 20), (2, 16, 20), (4, 128, 7), (2, 256, 20), (4, 32, 0)):
+        W = r.normal(0, 0.02, (4, 2 * g)).astype(np.float16).astype(np.float64)
+        W[1, :g] = r.laplace(0, 0.05, g)  # a heavier-tailed group, where the shrink acts
+        v2 = o.quantize_v2(W, [1.0], nbits=nbits, group_size=g, iters=iters)
+        Wg = W.reshape(-1, g)
+        assert np.all(v2["choice"] == 0)
+        for j in range(Wg.shape[0]):
+            one = o.quantize(Wg[j:j + 1], nbits=nbits, group_size=g, axis=1, iters=iters)
+            assert v2["s"][j] == one["s"][0] and v2["z"][j] == one["z"][0]
+            assert np.array_equal(v2["codes"].reshape(-1, g)[j], one["codes"][0])
+
+
+def pin_scale_search_argmin(o):
+    """A grid of several multipliers picks, per group, the candidate whose own single-multiplier
+    search has the smallest error sum (the first such one on a tie), and returns exactly that
+    candidate's codes, scale and zero; a repeated multiplier is never chosen over its first
+    copy."""
+    r = _rng(37)
+    W = r.normal(0, 0.02, (8, 256)).astype(np.float16).astype(np.float64)
+    W[3, 17] = 0.2  # an outlier
+    grid = [0.9, 1.0, 1.05, 1.1, 0.95, 1.05]
+    full = o.quantize_v2(W, grid, nbits=4, group_size=64)
+    Wg = W.reshape(-1, 64)
+    singles = [o.quantize_v2(W, [c], nbits=4, group_size=64) for c in grid]
+    errs = np.array([_group_error(o, Wg, sg["codes"].reshape(-1, 64), sg["z"], sg["delta"]) for sg in singles])
+    best = np.argmin(errs, axis=0)
+    assert np.array_equal(full["choice"], best) and np.all(full["choice"] != 5)
+    assert len(set(best.tolist())) >= 3  # the grid matters on these groups
+    for j, c in enumerate(best):
+        sg = singles[c]
+        assert full["s"][j] == sg["s"][j] and full["z"][j] == sg["z"][j]
+        assert np.array_equal(full["codes"].reshape(-1, 64)[j], sg["codes"].reshape(-1, 64)[j])
+    base = _group_error(o, Wg, singles[1]["codes"].reshape(-1, 64), singles[1]["z"], singles[1]["delta"])
+    mine = _group_error(o, Wg, full["codes"].reshape(-1, 64), full["z"], full["delta"])
+    assert np.all(mine <= base)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -25,6 +25,7 @@ PLANTS = {
     17: "product for all formats takes axis-0 groups as axis-1 runs",
     18: "input gradient multiplies by the transposed weight (column index as row)",
     19: "the stop rule that keeps the failing round's zero keeps its update instead",
+    20: "the scale search keeps the candidate with the larger error",
 }
 
 
