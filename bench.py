@@ -111,6 +111,53 @@ def sleep_rate(stream):
     return 2_000_000 / max(e0.elapsed_time(e1), 1e-3)
 
 
+SCALE_GRID = (0.85, 0.925, 1.0, 1.05, 1.1)
+
+
+def scale_search_leg(timed, dev):
+    """The second solver (hqq_quantize_v2) on the Llama-7B layer set, 4-bit g64, 20 rounds, over
+    five multipliers of the min-max scale: its rate and, next to the default solver's, the mean
+    |W - W_hat| it reaches (both dequantised by the library, averaged on the device)."""
+    import torch
+
+    import synth
+    import weight_only_quantization_amd as hq
+
+    spec = synth.WORKLOADS["llama7b_layers"]
+    qp = spec["quant"][0]
+    tensors = spec["tensors"]
+    Ws = [torch.from_numpy(t.make()).to(dev) for t in tensors]
+    outs = [hq.hqq_quantize_v2(W, SCALE_GRID, nbits=qp.nbits, group_size=qp.group_size, iters=qp.iters, p=qp.p,
+                               beta0=qp.beta0, kappa=qp.kappa) for W in Ws]
+
+    def vall(r):
+        for W, (q, ch) in zip(Ws, outs):
+            hq.hqq_quantize_v2(W, SCALE_GRID, nbits=qp.nbits, group_size=qp.group_size, iters=qp.iters, p=qp.p,
+                               beta0=qp.beta0, kappa=qp.kappa, out=(q.packed, q.delta, q.zero, ch))
+
+    tv = timed(vall, 3)
+    n = sum(t.rows * t.cols for t in tensors)
+
+    def mae(pk, d, z, t, W):
+        Wh = hq.hqq_dequantize(pk, d, z, t.rows, t.cols, qp.nbits, qp.group_size, 1)
+        return float((Wh.double() - W.double()).abs().sum())
+
+    e2 = sum(mae(q.packed, q.delta, q.zero, t, W) for (q, _), t, W in zip(outs, tensors, Ws)) / n
+    e1 = 0.0
+    for t, W in zip(tensors, Ws):
+        q = hq.hqq_quantize(W, nbits=qp.nbits, group_size=qp.group_size, axis=1, iters=qp.iters, p=qp.p,
+                            beta0=qp.beta0, kappa=qp.kappa)
+        e1 += mae(q.packed, q.delta, q.zero, t, W)
+    e1 /= n
+    counts = torch.zeros(len(SCALE_GRID), dtype=torch.int64, device=dev)
+    for _, ch in outs:
+        counts += torch.bincount(ch.long(), minlength=len(SCALE_GRID))
+    del Ws, outs
+    return {"grid": list(SCALE_GRID), "quantize_s": tv, "quantize_gweights_per_s": n / tv / 1e9,
+            "mae_fp16_dequant": e2, "mae_fp16_dequant_default_solver": e1,
+            "chosen_per_multiplier": counts.cpu().tolist()}
+
+
 def config_legs(a, timed, stream, dev):
     """Legs outside the step, one per remaining configuration: the 7B-shaped layer set at 3-bit
     g64 and 2-bit g16 (Laplace weights), the 28672x8192 axis-0 g128 weight, and the fused
@@ -200,6 +247,9 @@ def config_legs(a, timed, stream, dev):
                      4 * ((t.rows * t.cols + 9) // 10) + 4 * t.rows * t.cols / qp.group_size)
         del outs
         torch.cuda.empty_cache()
+    log("config legs: scale search over the 4-bit layer set")
+    legs["layers_scale_search_4bit_g64"] = scale_search_leg(timed, dev)
+    torch.cuda.empty_cache()
     log("config legs: 28672x8192 axis 0")
     m70 = synth.WORKLOADS["mlp70b"]
     qp = m70["quant"][0]

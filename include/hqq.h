@@ -88,6 +88,8 @@ extern "C" {
 #define HQQ_MAX_SCALE 2.0e4
 /* Largest accepted `iters`. */
 #define HQQ_MAX_ITERS 64
+/* Multipliers of the scale search (hqq_quantize_v2) at most. */
+#define HQQ_V2_MAX_CANDIDATES 16
 
 /* Bytes of the packed code buffer for rows*cols codes of `nbits` (2, 3 or 4), or 0
  * when the arguments are invalid. */
@@ -175,6 +177,41 @@ typedef struct hqq_quant_args {
  * stop_rule outside {0, 1, 2, 4, 5, 6}, a negative or non-finite tiny_range or unknown flags.
  */
 int hqq_quantize_ex(const hqq_quant_args* args);
+
+/*
+ * Scale search: the slower second solver of the method ("第二拍" names it next to the default
+ * one, which keeps the min-max scale and only refines the zero; this one can grid-search the
+ * scale).  The page gives its name and purpose only; the reading implemented (and its oracle)
+ * is: for each group and each multiplier c_j of scale_grid, s = min(s0 * c_j, 2e4) with s0 the
+ * min-max start before its limit, delta = 1/s, z0 = -min * s, up to `iters` proximal rounds
+ * (shrink p, beta_k = beta0 * kappa^k) stopped by the default rule applied to the group's own
+ * error sum (keep z_(k-1) at the first k >= 1 whose sum is not below the previous one, else
+ * z_iters), and the group's sum of |W - W_hat| over its final codes; the first candidate with
+ * the smallest sum wins.  There is no whole-tensor stop and no workspace.
+ *
+ * Arguments as hqq_quant_args where named alike, with these limits: axis must be 1 and nbits 2
+ * or 4 (else HQQ_ERR_UNSUPPORTED); scale_grid is a HOST array of n_candidates (1 ..
+ * HQQ_V2_MAX_CANDIDATES) finite positive multipliers, read before the call returns; choice_dev
+ * (device, may be NULL) receives the chosen index per group (G bytes).  Outputs: packed codes,
+ * delta and zero (meta_dtype) as hqq_quantize.  Validation errors return before any launch;
+ * the work is enqueued on `stream` and is asynchronous.
+ */
+typedef struct hqq_quant_v2_args {
+  const void* W_fp16;
+  int64_t rows, cols;
+  int nbits, group_size, axis, iters;
+  double p, beta0, kappa, tiny_range;
+  const double* scale_grid;
+  int n_candidates;
+  void* packed;
+  void* delta;
+  void* zero;
+  int meta_dtype;
+  uint8_t* choice_dev;
+  void* stream;
+} hqq_quant_v2_args;
+
+int hqq_quantize_v2(const hqq_quant_v2_args* args);
 
 /*
  * Standalone dequantisation ("量化公式", "从压缩文件到一次前向"):

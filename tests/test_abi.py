@@ -142,6 +142,39 @@ def test_status_strings(lib):
     assert hq.status_string(99) == "HQQ_ERR_UNKNOWN"
 
 
+def test_quantize_v2_rejects_before_launch(lib):
+    """hqq_quantize_v2 refuses what it does not take (axis 0, 3-bit), a grid of 0 or more than
+    HQQ_V2_MAX_CANDIDATES multipliers or one that is not finite and positive, and the shared
+    argument errors, all before any launch."""
+    grid = (ctypes.c_double * 17)(*([1.0] * 17))
+
+    def call(**kw):
+        a = dict(W_fp16=FAKE.value, rows=64, cols=128, nbits=4, group_size=64, axis=1, iters=20, p=0.7, beta0=10.0,
+                 kappa=1.01, tiny_range=1e-4, scale_grid=ctypes.addressof(grid), n_candidates=3, packed=FAKE.value,
+                 delta=FAKE.value, zero=FAKE.value, meta_dtype=0, choice_dev=None, stream=None)
+        a.update(kw)
+        return lib.hqq_quantize_v2(ctypes.byref(hq.QuantV2Args(**a)))
+    assert lib.hqq_quantize_v2(None) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(axis=0) == hq.HQQ_ERR_UNSUPPORTED
+    assert call(nbits=3) == hq.HQQ_ERR_UNSUPPORTED
+    assert call(nbits=5) == hq.HQQ_ERR_INVALID_ARGUMENT
+    for n in (0, 17):
+        assert call(n_candidates=n) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(scale_grid=None) == hq.HQQ_ERR_INVALID_ARGUMENT
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        grid[1] = bad
+        assert call() == hq.HQQ_ERR_INVALID_ARGUMENT
+    grid[1] = 1.0
+    assert call(iters=65) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(p=0.0) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(tiny_range=-1.0) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(meta_dtype=7) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(packed=None) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(packed=FAKE.value + 8) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(group_size=48) != hq.HQQ_OK
+    assert hq.last_error() != ""
+
+
 def test_quantize_ex_rejects_before_launch(lib):
     """hqq_quantize_ex checks its own fields (stop rule, tiny range, flags) and then the same
     arguments as hqq_quantize, before any launch."""

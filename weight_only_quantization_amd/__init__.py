@@ -31,6 +31,7 @@ HQQ_DEBUG_NO_FROZEN_SKIP, HQQ_DEBUG_SLOW_SHRINK, HQQ_DEBUG_SYNC = 1, 2, 4
 
 # Every symbol the header declares.
 EXPORTS = ("hqq_packed_bytes", "hqq_num_groups", "hqq_quantize_workspace_bytes", "hqq_quantize", "hqq_quantize_ex",
+           "hqq_quantize_v2",
            "hqq_dequantize", "hqq_gemv_w4a16", "hqq_gemm_workspace_bytes", "hqq_gemm_w4a16",
            "hqq_gemm_dx_workspace_bytes", "hqq_gemm_w4a16_dx", "hqq_gemv", "hqq_gemm",
            "hqq_status_string", "hqq_last_error")
@@ -63,6 +64,8 @@ def load(path: str = LIB_PATH):
     lib.hqq_quantize.restype = i32
     lib.hqq_quantize_ex.argtypes = [ctypes.POINTER(QuantArgs)]
     lib.hqq_quantize_ex.restype = i32
+    lib.hqq_quantize_v2.argtypes = [ctypes.POINTER(QuantV2Args)]
+    lib.hqq_quantize_v2.restype = i32
     lib.hqq_dequantize.argtypes = [p, p, p, i32, i64, i64, i32, i32, i32, p, p]
     lib.hqq_dequantize.restype = i32
     lib.hqq_gemv_w4a16.argtypes = [p, p, p, i64, i64, i32, p, i64, p, i32, p]
@@ -159,6 +162,16 @@ class QuantArgs(ctypes.Structure):
                 ("stop_rule", ctypes.c_int), ("tiny_range", ctypes.c_double), ("debug_flags", ctypes.c_int)]
 
 
+class QuantV2Args(ctypes.Structure):
+    """hqq_quant_v2_args of include/hqq.h (field order and C types as declared there)."""
+    _fields_ = [("W_fp16", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("nbits", ctypes.c_int), ("group_size", ctypes.c_int), ("axis", ctypes.c_int), ("iters", ctypes.c_int),
+                ("p", ctypes.c_double), ("beta0", ctypes.c_double), ("kappa", ctypes.c_double),
+                ("tiny_range", ctypes.c_double), ("scale_grid", ctypes.c_void_p), ("n_candidates", ctypes.c_int),
+                ("packed", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("zero", ctypes.c_void_p),
+                ("meta_dtype", ctypes.c_int), ("choice_dev", ctypes.c_void_p), ("stream", ctypes.c_void_p)]
+
+
 def hqq_quantize(W, nbits: int = 4, group_size: int = 64, axis: int = 1, iters: int = 20, p: float = 0.7,
                  beta0: float = 10.0, kappa: float = 1.01, meta_dtype=None, workspace=None, out=None,
                  stream=None, stop_rule: int = HQQ_STOP_BEST, tiny_range: float | None = None,
@@ -200,6 +213,37 @@ def hqq_quantize(W, nbits: int = 4, group_size: int = 64, axis: int = 1, iters: 
         st = lib.hqq_quantize_ex(ctypes.byref(args))
     _check(st)
     return Quantized(packed, delta, zero, rows, cols, nbits, group_size, axis, stop_iter, mae_trace)
+
+
+def hqq_quantize_v2(W, scale_grid, nbits: int = 4, group_size: int = 64, iters: int = 20, p: float = 0.7,
+                    beta0: float = 10.0, kappa: float = 1.01, tiny_range: float | None = None, meta_dtype=None,
+                    out=None, stream=None):
+    """Scale search (axis 1, 2- or 4-bit) over the multipliers `scale_grid` of the min-max scale.
+    Returns (Quantized, choice): the packed codes, delta and zero as hqq_quantize (no stop index
+    or MAE trace: the stop is per group) and the chosen multiplier's index per group (uint8).
+    `out` may give (packed, delta, zero, choice)."""
+    import numpy as np
+    import torch
+    lib = load()
+    assert W.dtype == torch.float16 and W.is_cuda and W.dim() == 2 and W.is_contiguous()
+    rows, cols = W.shape
+    meta_dtype = meta_dtype or torch.float16
+    G = lib.hqq_num_groups(rows, cols, group_size)
+    dev = W.device
+    if out is None:
+        packed = torch.empty(max(lib.hqq_packed_bytes(rows, cols, nbits), 1), dtype=torch.uint8, device=dev)
+        delta = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
+        zero = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
+        choice = torch.empty(max(G, 1), dtype=torch.uint8, device=dev)
+    else:
+        packed, delta, zero, choice = out
+    grid = np.ascontiguousarray(scale_grid, dtype=np.float64)
+    args = QuantV2Args(W.data_ptr(), rows, cols, nbits, group_size, 1, iters, p, beta0, kappa,
+                       HQQ_TINY_RANGE if tiny_range is None else tiny_range, grid.ctypes.data, grid.size,
+                       packed.data_ptr(), delta.data_ptr(), zero.data_ptr(), _meta_code(meta_dtype),
+                       choice.data_ptr() if choice is not None else None, _stream_ptr(stream).value)
+    _check(lib.hqq_quantize_v2(ctypes.byref(args)))
+    return Quantized(packed, delta, zero, rows, cols, nbits, group_size, 1, None, None), choice
 
 
 def hqq_dequantize(packed, delta, zero, rows: int, cols: int, nbits: int, group_size: int, axis: int, out=None,

@@ -94,6 +94,18 @@ size_t hqq_quantize_workspace_bytes(int64_t rows, int64_t cols, int nbits, int g
 namespace {
 
 // hqq_quantize and hqq_quantize_ex: validation, the solver's per-round constants, the launches.
+// beta_k by repeated products (beta grows by kappa after every round); thresholds of the
+// shrink: e = 0 exactly for |r| <= beta^(-1/(2-p)); a 1e-6 relative margin keeps the fast
+// path strictly inside that region.
+void fill_schedule(hqq::SolveArgs& a, int iters, double p, double beta0, double kappa) {
+  double beta = beta0;
+  for (int k = 0; k < iters; ++k) {
+    a.beta[k] = beta;
+    a.thr[k] = pow(beta, -1.0 / (2.0 - p)) * (1.0 - 1e-6);
+    beta = beta * kappa;
+  }
+}
+
 int quantize_impl(const hqq_quant_args& x) {
   const void* W_fp16 = x.W_fp16;
   const int64_t rows = x.rows, cols = x.cols;
@@ -140,15 +152,7 @@ int quantize_impl(const hqq_quant_args& x) {
   a.qmax = (double)((1 << nbits) - 1);
   a.tiny = x.tiny_range;
   a.pm1 = p - 1.0;
-  // beta_k by repeated products (beta grows by kappa after every round); thresholds of the
-  // shrink: e = 0 exactly for |r| <= beta^(-1/(2-p)); a 1e-6 relative margin keeps the fast
-  // path strictly inside that region.
-  double beta = beta0;
-  for (int k = 0; k < iters; ++k) {
-    a.beta[k] = beta;
-    a.thr[k] = pow(beta, -1.0 / (2.0 - p)) * (1.0 - 1e-6);
-    beta = beta * kappa;
-  }
+  fill_schedule(a, iters, p, beta0, kappa);
   double m = INFINITY;
   for (int k = iters - 1; k >= 0; --k) {
     m = fmin(m, a.thr[k]);
@@ -193,6 +197,56 @@ int hqq_quantize_ex(const hqq_quant_args* args) {
   if (args->debug_flags & ~(HQQ_DEBUG_NO_FROZEN_SKIP | HQQ_DEBUG_SLOW_SHRINK | HQQ_DEBUG_SYNC))
     return fail(HQQ_ERR_INVALID_ARGUMENT, "unknown debug flags");
   return quantize_impl(*args);
+}
+
+int hqq_quantize_v2(const hqq_quant_v2_args* args) {
+  g_last_error[0] = 0;
+  if (!args) return fail(HQQ_ERR_INVALID_ARGUMENT, "null args");
+  const hqq_quant_v2_args& x = *args;
+  int st = check_shape(x.rows, x.cols, x.nbits, x.group_size, x.axis);
+  if (st != HQQ_OK) return st;
+  if (x.axis != 1) return fail(HQQ_ERR_UNSUPPORTED, "the scale search takes axis 1 only");
+  if (x.nbits != 2 && x.nbits != 4) return fail(HQQ_ERR_UNSUPPORTED, "the scale search takes nbits 2 or 4");
+  if (x.iters < 0 || x.iters > HQQ_MAX_ITERS) return fail(HQQ_ERR_INVALID_ARGUMENT, "iters must be in [0, %d]", HQQ_MAX_ITERS);
+  if (!(x.p > 0.0 && x.p <= 1.0)) return fail(HQQ_ERR_INVALID_ARGUMENT, "p must be in (0, 1]");
+  if (!(x.beta0 > 0.0) || !isfinite(x.beta0)) return fail(HQQ_ERR_INVALID_ARGUMENT, "beta0 must be positive");
+  if (!(x.kappa > 0.0) || !isfinite(x.kappa)) return fail(HQQ_ERR_INVALID_ARGUMENT, "kappa must be positive");
+  if (!(x.tiny_range >= 0.0) || !isfinite(x.tiny_range))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "tiny_range must be finite and >= 0");
+  if (x.n_candidates < 1 || x.n_candidates > HQQ_V2_MAX_CANDIDATES || !x.scale_grid)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "n_candidates must be in [1, %d] with a scale_grid", HQQ_V2_MAX_CANDIDATES);
+  for (int c = 0; c < x.n_candidates; ++c)
+    if (!(x.scale_grid[c] > 0.0) || !isfinite(x.scale_grid[c]))
+      return fail(HQQ_ERR_INVALID_ARGUMENT, "scale_grid values must be finite and positive");
+  if (x.meta_dtype != HQQ_META_F16 && x.meta_dtype != HQQ_META_F32 && x.meta_dtype != HQQ_META_F64)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "meta_dtype must be HQQ_META_F16, _F32 or _F64");
+  if (!x.W_fp16 || !x.packed || !x.delta || !x.zero) return fail(HQQ_ERR_INVALID_ARGUMENT, "null buffer");
+  if (!aligned16(x.W_fp16) || !aligned16(x.packed) || !aligned16(x.delta) || !aligned16(x.zero))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
+  const int64_t G = x.rows * x.cols / x.group_size;  // >= 1: rows, cols > 0 and g divides cols
+
+  hqq::SolveArgs a;
+  memset(&a, 0, sizeof(a));
+  a.W = reinterpret_cast<const __half*>(x.W_fp16);
+  a.packed = reinterpret_cast<uint8_t*>(x.packed);
+  a.delta = x.delta;
+  a.zero = x.zero;
+  a.G = G;
+  a.nblocks = hqq::quant_v2_blocks(G, x.group_size);
+  a.iters = x.iters;
+  a.meta_dtype = x.meta_dtype;
+  a.qmax = (double)((1 << x.nbits) - 1);
+  a.tiny = x.tiny_range;
+  a.pm1 = x.p - 1.0;
+  fill_schedule(a, x.iters, x.p, x.beta0, x.kappa);
+  hqq::ScaleGrid sg;
+  memset(&sg, 0, sizeof(sg));
+  for (int c = 0; c < x.n_candidates; ++c) sg.c[c] = x.scale_grid[c];
+  sg.n = x.n_candidates;
+  sg.choice = x.choice_dev;
+  hipError_t e = hqq::launch_quantize_v2(a, sg, x.nbits, x.group_size, reinterpret_cast<hipStream_t>(x.stream));
+  if (e != hipSuccess) return device_fail(e, "hqq_quantize_v2 launch");
+  return HQQ_OK;
 }
 
 int hqq_dequantize(const void* packed, const void* delta, const void* zero, int meta_dtype, int64_t rows,

@@ -417,6 +417,135 @@ __global__ void __launch_bounds__(256, solve_waves<G>()) k_quant_ax1(const Solve
 }
 
 // ------------------------------------------------------------------------------------------
+// Scale search (the second, slower solver the method names: it can grid-search the scale while
+// the default keeps the min-max scale).  Reading: per group and multiplier c_j of the grid,
+// s = min(s0 c_j, 2e4) with s0 the min-max start before its limit, delta = 1/s, z0 = -min s,
+// the proximal rounds with the stop rule applied to the group's own error sum (keep z_(k-1) at
+// the first k >= 1 whose sum is not below the previous one, else z_iters), and the error sum of
+// the candidate's final codes; candidate 0 first, a later one only with a strictly smaller
+// error.  Axis 1, one tile of 4 GPW groups per block as in the solve pass; a wave runs the
+// rounds of a candidate until every one of its groups has stopped.  No global dependency.
+// ------------------------------------------------------------------------------------------
+template <int NBITS, int G>
+__global__ void __launch_bounds__(256) k_quant_v2(const SolveArgs a, const ScaleGrid sg) {
+  using S = Shape<G>;
+  constexpr int E = S::E, L = S::L, GPW = S::GPW;
+  constexpr int GPB = 4 * GPW;
+  extern __shared__ double meta_lds[];  // [2][groups per block]
+  const int64_t tile = blockIdx.x;
+  if (tile >= a.nblocks) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = lane / L, slot = lane % L;
+  const int gblock = wave * GPW + sub;
+  const int64_t gidx = tile * GPB + gblock;
+  const bool valid = gidx < a.G;
+  const int64_t e0 = (valid ? gidx : 0) * G + slot * E;
+
+  double w[E];
+#pragma unroll
+  for (int c = 0; c < E / 2; ++c) {
+    const unsigned u = reinterpret_cast<const unsigned*>(a.W + e0)[c];
+    w[2 * c] = valid ? (double)__half2float(__ushort_as_half((unsigned short)(u & 0xFFFFu))) : 0.0;
+    w[2 * c + 1] = valid ? (double)__half2float(__ushort_as_half((unsigned short)(u >> 16))) : 0.0;
+  }
+  double mn = w[0], mx = w[0];
+#pragma unroll
+  for (int e = 1; e < E; ++e) {
+    mn = fmin(mn, w[e]);
+    mx = fmax(mx, w[e]);
+  }
+  mn = seg_min<L>(mn);
+  mx = seg_max<L>(mx);
+  const double d = mx - mn;
+  const double sb = (d <= a.tiny) ? 1.0 : a.qmax / d;
+  const double qmax = __builtin_canonicalize(a.qmax);
+  const double inv_g = 1.0 / (double)G;
+
+  double best_e = 0.0, best_s = 0.0, best_delta = 0.0, best_z = 0.0;
+  int best_c = 0;
+  double ws[E];
+  for (int c = 0; c < sg.n; ++c) {
+    const double s = fmin(sb * sg.c[c], HQQ_MAX_SCALE);
+    const double delta = 1.0 / s;
+    double z = -mn * s;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ws[e] = w[e] * s;
+    double zprev = z, best = __builtin_inf();
+    bool done = !valid;
+    for (int k = 0; k < a.iters; ++k) {
+      if (__all(done)) break;
+      double err, zn, bound;
+      hqq_round<E, L>(w, ws, s, delta, z, qmax, a.beta[k], a.pm1, a.thr[k], inv_g, err, zn, bound);
+      if (!done) {
+        if (k >= 1 && !(err < best)) {
+          z = zprev;
+          done = true;
+        } else {
+          best = err;
+          zprev = z;
+          z = zn;
+        }
+      }
+    }
+    double ar[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      double qq = __builtin_rint(ws[e] + z);
+      qq = fmax(qq, 0.0);
+      qq = fmin(qq, qmax);
+      ar[e] = fabs(w[e] - (qq - z) * delta);
+    }
+    const double ce = seg_sum<L>(tree_sum<0, E, E>(ar));
+    if (c == 0 || ce < best_e) {
+      best_e = ce;
+      best_s = s;
+      best_delta = delta;
+      best_z = z;
+      best_c = c;
+    }
+  }
+
+#pragma unroll
+  for (int e = 0; e < E; ++e) ws[e] = w[e] * best_s;
+  unsigned cq[E];
+  final_codes<E>(ws, best_z, qmax, cq);
+  if (valid) {
+    if constexpr (NBITS == 4) {
+      if constexpr (E == 4) {
+        reinterpret_cast<unsigned short*>(a.packed)[e0 / 4] =
+            (unsigned short)(cq[0] | (cq[1] << 4) | (cq[2] << 8) | (cq[3] << 12));
+      } else {
+#pragma unroll
+        for (int h = 0; h < E / 8; ++h) {
+          unsigned word = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) word |= cq[8 * h + e] << (4 * e);
+          reinterpret_cast<unsigned*>(a.packed)[e0 / 8 + h] = word;
+        }
+      }
+    } else {
+      if constexpr (E == 4) {
+        a.packed[e0 / 4] = (uint8_t)(cq[0] | (cq[1] << 2) | (cq[2] << 4) | (cq[3] << 6));
+      } else {
+#pragma unroll
+        for (int h = 0; h < E / 8; ++h) {
+          unsigned v = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v |= cq[8 * h + e] << (2 * e);
+          reinterpret_cast<unsigned short*>(a.packed)[e0 / 8 + h] = (unsigned short)v;
+        }
+      }
+    }
+    if (slot == 0) {
+      meta_lds[gblock] = best_delta;
+      meta_lds[GPB + gblock] = best_z;
+      if (sg.choice) sg.choice[gidx] = (uint8_t)best_c;
+    }
+  }
+  store_block_meta(a, meta_lds, GPB, tile * GPB);
+}
+
+// ------------------------------------------------------------------------------------------
 // axis = 0: group j = {i*M + j}, a column of the [g, M] view.  A block owns TW adjacent
 // groups: it loads the g x TW fp16 tile with 16-byte row loads into LDS, each lane then takes
 // E weights of one group from LDS; the codes go back through LDS for row-wise packed stores.
@@ -747,6 +876,39 @@ hipError_t launch_quantize(const SolveArgs& a, int nbits, int g, int axis, int t
     err = hipGetLastError();
   }
   return err;
+}
+
+namespace {
+template <int NBITS, int G>
+hipError_t launch_v2_g(const SolveArgs& a, const ScaleGrid& sg, hipStream_t st) {
+  constexpr int GPB = 4 * Shape<G>::GPW;
+  hipLaunchKernelGGL((k_quant_v2<NBITS, G>), dim3((unsigned)a.nblocks), dim3(256), 2 * GPB * sizeof(double), st, a,
+                     sg);
+  return hipGetLastError();
+}
+template <int NBITS>
+hipError_t launch_v2_b(const SolveArgs& a, const ScaleGrid& sg, int g, hipStream_t st) {
+  switch (g) {
+    case 16: return launch_v2_g<NBITS, 16>(a, sg, st);
+    case 32: return launch_v2_g<NBITS, 32>(a, sg, st);
+    case 64: return launch_v2_g<NBITS, 64>(a, sg, st);
+    case 128: return launch_v2_g<NBITS, 128>(a, sg, st);
+    case 256: return launch_v2_g<NBITS, 256>(a, sg, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
+int64_t quant_v2_blocks(int64_t G, int g) {
+  const int gpb = 4 * (64 / lanes_per_group(g));
+  return (G + gpb - 1) / gpb;
+}
+
+hipError_t launch_quantize_v2(const SolveArgs& a, const ScaleGrid& sg, int nbits, int g, hipStream_t st) {
+  if (a.nblocks != quant_v2_blocks(a.G, g)) return hipErrorInvalidConfiguration;
+  if (nbits == 4) return launch_v2_b<4>(a, sg, g, st);
+  if (nbits == 2) return launch_v2_b<2>(a, sg, g, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace hqq
