@@ -189,12 +189,14 @@ int hqq_quantize_ex(const hqq_quant_args* args);
  * z_iters), and the group's sum of |W - W_hat| over its final codes; the first candidate with
  * the smallest sum wins.  There is no whole-tensor stop and no workspace.
  *
- * Arguments as hqq_quant_args where named alike, with these limits: axis must be 1 and nbits 2
- * or 4 (else HQQ_ERR_UNSUPPORTED); scale_grid is a HOST array of n_candidates (1 ..
- * HQQ_V2_MAX_CANDIDATES) finite positive multipliers, read before the call returns; choice_dev
- * (device, may be NULL) receives the chosen index per group (G bytes).  Outputs: packed codes,
- * delta and zero (meta_dtype) as hqq_quantize.  Validation errors return before any launch;
- * the work is enqueued on `stream` and is asynchronous.
+ * Arguments as hqq_quant_args where named alike, with these limits: axis must be 1 (else
+ * HQQ_ERR_UNSUPPORTED); scale_grid is a HOST array of n_candidates (1 .. HQQ_V2_MAX_CANDIDATES)
+ * finite positive multipliers, read before the call returns; choice_dev (device, may be NULL)
+ * receives the chosen index per group (G bytes); workspace (device, 16-byte aligned) holds
+ * hqq_quantize_v2_workspace_bytes(rows, cols, nbits) bytes (the 3-bit codes before packing; 0
+ * for 2 and 4 bits, when it may be NULL; HQQ_ERR_WORKSPACE if smaller).  Outputs: packed
+ * codes, delta and zero (meta_dtype) as hqq_quantize.  Validation errors return before any
+ * launch; the work is enqueued on `stream` and is asynchronous.
  */
 typedef struct hqq_quant_v2_args {
   const void* W_fp16;
@@ -209,8 +211,11 @@ typedef struct hqq_quant_v2_args {
   int meta_dtype;
   uint8_t* choice_dev;
   void* stream;
+  void* workspace;
+  size_t workspace_bytes;
 } hqq_quant_v2_args;
 
+size_t hqq_quantize_v2_workspace_bytes(int64_t rows, int64_t cols, int nbits);
 int hqq_quantize_v2(const hqq_quant_v2_args* args);
 
 /*

@@ -143,20 +143,25 @@ def test_status_strings(lib):
 
 
 def test_quantize_v2_rejects_before_launch(lib):
-    """hqq_quantize_v2 refuses what it does not take (axis 0, 3-bit), a grid of 0 or more than
-    HQQ_V2_MAX_CANDIDATES multipliers or one that is not finite and positive, and the shared
-    argument errors, all before any launch."""
+    """hqq_quantize_v2 refuses what it does not take (axis 0), a grid of 0 or more than
+    HQQ_V2_MAX_CANDIDATES multipliers or one that is not finite and positive, a missing or
+    small 3-bit workspace, and the shared argument errors, all before any launch."""
     grid = (ctypes.c_double * 17)(*([1.0] * 17))
 
     def call(**kw):
         a = dict(W_fp16=FAKE.value, rows=64, cols=128, nbits=4, group_size=64, axis=1, iters=20, p=0.7, beta0=10.0,
                  kappa=1.01, tiny_range=1e-4, scale_grid=ctypes.addressof(grid), n_candidates=3, packed=FAKE.value,
-                 delta=FAKE.value, zero=FAKE.value, meta_dtype=0, choice_dev=None, stream=None)
+                 delta=FAKE.value, zero=FAKE.value, meta_dtype=0, choice_dev=None, stream=None, workspace=None,
+                 workspace_bytes=0)
         a.update(kw)
         return lib.hqq_quantize_v2(ctypes.byref(hq.QuantV2Args(**a)))
     assert lib.hqq_quantize_v2(None) == hq.HQQ_ERR_INVALID_ARGUMENT
     assert call(axis=0) == hq.HQQ_ERR_UNSUPPORTED
-    assert call(nbits=3) == hq.HQQ_ERR_UNSUPPORTED
+    ws3 = lib.hqq_quantize_v2_workspace_bytes(64, 128, 3)
+    assert ws3 >= 64 * 128 and lib.hqq_quantize_v2_workspace_bytes(64, 128, 4) == 0
+    assert call(nbits=3) == hq.HQQ_ERR_WORKSPACE
+    assert call(nbits=3, workspace=FAKE.value, workspace_bytes=ws3 - 1) == hq.HQQ_ERR_WORKSPACE
+    assert call(nbits=3, workspace=FAKE.value + 8, workspace_bytes=ws3) == hq.HQQ_ERR_INVALID_ARGUMENT
     assert call(nbits=5) == hq.HQQ_ERR_INVALID_ARGUMENT
     for n in (0, 17):
         assert call(n_candidates=n) == hq.HQQ_ERR_INVALID_ARGUMENT

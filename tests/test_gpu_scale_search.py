@@ -61,7 +61,7 @@ def check(W16, grid, nbits, g, iters=20, exact=True, meta="f64", **kw):
 
 # several tiles of groups and a ragged last one (rows chosen so the group count is odd)
 CASES = [(4, 64, 37, 128), (2, 16, 29, 192), (4, 32, 33, 256), (4, 128, 21, 512), (2, 256, 11, 512),
-         (2, 64, 45, 320), (4, 16, 17, 64)]
+         (2, 64, 45, 320), (4, 16, 17, 64), (3, 64, 37, 128), (3, 32, 19, 160), (3, 16, 23, 48)]
 
 
 @pytest.mark.parametrize("nbits,g,rows,cols", CASES)
@@ -82,7 +82,7 @@ def test_scale_search_stored_metadata(meta):
 
 
 @pytest.mark.parametrize("iters", [0, 1, 2, 20])
-@pytest.mark.parametrize("nbits", [2, 4])
+@pytest.mark.parametrize("nbits", [2, 3, 4])
 def test_scale_search_edge_cases(nbits, iters):
     """Constant and zero groups, a tiny range, the 2e4 limit (multipliers above 1 push more
     groups against it), sigma-1 rows where the shrink is active, outliers, exact ties."""

@@ -31,7 +31,7 @@ HQQ_DEBUG_NO_FROZEN_SKIP, HQQ_DEBUG_SLOW_SHRINK, HQQ_DEBUG_SYNC = 1, 2, 4
 
 # Every symbol the header declares.
 EXPORTS = ("hqq_packed_bytes", "hqq_num_groups", "hqq_quantize_workspace_bytes", "hqq_quantize", "hqq_quantize_ex",
-           "hqq_quantize_v2",
+           "hqq_quantize_v2", "hqq_quantize_v2_workspace_bytes",
            "hqq_dequantize", "hqq_gemv_w4a16", "hqq_gemm_workspace_bytes", "hqq_gemm_w4a16",
            "hqq_gemm_dx_workspace_bytes", "hqq_gemm_w4a16_dx", "hqq_gemv", "hqq_gemm",
            "hqq_status_string", "hqq_last_error")
@@ -66,6 +66,8 @@ def load(path: str = LIB_PATH):
     lib.hqq_quantize_ex.restype = i32
     lib.hqq_quantize_v2.argtypes = [ctypes.POINTER(QuantV2Args)]
     lib.hqq_quantize_v2.restype = i32
+    lib.hqq_quantize_v2_workspace_bytes.argtypes = [i64, i64, i32]
+    lib.hqq_quantize_v2_workspace_bytes.restype = sz
     lib.hqq_dequantize.argtypes = [p, p, p, i32, i64, i64, i32, i32, i32, p, p]
     lib.hqq_dequantize.restype = i32
     lib.hqq_gemv_w4a16.argtypes = [p, p, p, i64, i64, i32, p, i64, p, i32, p]
@@ -169,7 +171,8 @@ class QuantV2Args(ctypes.Structure):
                 ("p", ctypes.c_double), ("beta0", ctypes.c_double), ("kappa", ctypes.c_double),
                 ("tiny_range", ctypes.c_double), ("scale_grid", ctypes.c_void_p), ("n_candidates", ctypes.c_int),
                 ("packed", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("zero", ctypes.c_void_p),
-                ("meta_dtype", ctypes.c_int), ("choice_dev", ctypes.c_void_p), ("stream", ctypes.c_void_p)]
+                ("meta_dtype", ctypes.c_int), ("choice_dev", ctypes.c_void_p), ("stream", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 def hqq_quantize(W, nbits: int = 4, group_size: int = 64, axis: int = 1, iters: int = 20, p: float = 0.7,
@@ -217,8 +220,8 @@ def hqq_quantize(W, nbits: int = 4, group_size: int = 64, axis: int = 1, iters: 
 
 def hqq_quantize_v2(W, scale_grid, nbits: int = 4, group_size: int = 64, iters: int = 20, p: float = 0.7,
                     beta0: float = 10.0, kappa: float = 1.01, tiny_range: float | None = None, meta_dtype=None,
-                    out=None, stream=None):
-    """Scale search (axis 1, 2- or 4-bit) over the multipliers `scale_grid` of the min-max scale.
+                    out=None, workspace=None, stream=None):
+    """Scale search (axis 1, 2/3/4-bit) over the multipliers `scale_grid` of the min-max scale.
     Returns (Quantized, choice): the packed codes, delta and zero as hqq_quantize (no stop index
     or MAE trace: the stop is per group) and the chosen multiplier's index per group (uint8).
     `out` may give (packed, delta, zero, choice)."""
@@ -238,10 +241,15 @@ def hqq_quantize_v2(W, scale_grid, nbits: int = 4, group_size: int = 64, iters: 
     else:
         packed, delta, zero, choice = out
     grid = np.ascontiguousarray(scale_grid, dtype=np.float64)
+    ws_bytes = lib.hqq_quantize_v2_workspace_bytes(rows, cols, nbits)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     args = QuantV2Args(W.data_ptr(), rows, cols, nbits, group_size, 1, iters, p, beta0, kappa,
                        HQQ_TINY_RANGE if tiny_range is None else tiny_range, grid.ctypes.data, grid.size,
                        packed.data_ptr(), delta.data_ptr(), zero.data_ptr(), _meta_code(meta_dtype),
-                       choice.data_ptr() if choice is not None else None, _stream_ptr(stream).value)
+                       choice.data_ptr() if choice is not None else None, _stream_ptr(stream).value,
+                       workspace.data_ptr() if workspace is not None else None,
+                       workspace.numel() * workspace.element_size() if workspace is not None else 0)
     _check(lib.hqq_quantize_v2(ctypes.byref(args)))
     return Quantized(packed, delta, zero, rows, cols, nbits, group_size, 1, None, None), choice
 

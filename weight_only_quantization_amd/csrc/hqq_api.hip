@@ -199,6 +199,11 @@ int hqq_quantize_ex(const hqq_quant_args* args) {
   return quantize_impl(*args);
 }
 
+size_t hqq_quantize_v2_workspace_bytes(int64_t rows, int64_t cols, int nbits) {
+  if (nbits != 3 || rows <= 0 || cols <= 0) return 0;
+  return ((size_t)rows * (size_t)cols + 255) & ~size_t(255);  // one byte per code before packing
+}
+
 int hqq_quantize_v2(const hqq_quant_v2_args* args) {
   g_last_error[0] = 0;
   if (!args) return fail(HQQ_ERR_INVALID_ARGUMENT, "null args");
@@ -206,7 +211,6 @@ int hqq_quantize_v2(const hqq_quant_v2_args* args) {
   int st = check_shape(x.rows, x.cols, x.nbits, x.group_size, x.axis);
   if (st != HQQ_OK) return st;
   if (x.axis != 1) return fail(HQQ_ERR_UNSUPPORTED, "the scale search takes axis 1 only");
-  if (x.nbits != 2 && x.nbits != 4) return fail(HQQ_ERR_UNSUPPORTED, "the scale search takes nbits 2 or 4");
   if (x.iters < 0 || x.iters > HQQ_MAX_ITERS) return fail(HQQ_ERR_INVALID_ARGUMENT, "iters must be in [0, %d]", HQQ_MAX_ITERS);
   if (!(x.p > 0.0 && x.p <= 1.0)) return fail(HQQ_ERR_INVALID_ARGUMENT, "p must be in (0, 1]");
   if (!(x.beta0 > 0.0) || !isfinite(x.beta0)) return fail(HQQ_ERR_INVALID_ARGUMENT, "beta0 must be positive");
@@ -223,6 +227,10 @@ int hqq_quantize_v2(const hqq_quant_v2_args* args) {
   if (!x.W_fp16 || !x.packed || !x.delta || !x.zero) return fail(HQQ_ERR_INVALID_ARGUMENT, "null buffer");
   if (!aligned16(x.W_fp16) || !aligned16(x.packed) || !aligned16(x.delta) || !aligned16(x.zero))
     return fail(HQQ_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
+  const size_t wsb = hqq_quantize_v2_workspace_bytes(x.rows, x.cols, x.nbits);
+  if (wsb && (!x.workspace || x.workspace_bytes < wsb))
+    return fail(HQQ_ERR_WORKSPACE, "workspace of %zu bytes needed", wsb);
+  if (wsb && !aligned16(x.workspace)) return fail(HQQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   const int64_t G = x.rows * x.cols / x.group_size;  // >= 1: rows, cols > 0 and g divides cols
 
   hqq::SolveArgs a;
@@ -231,6 +239,7 @@ int hqq_quantize_v2(const hqq_quant_v2_args* args) {
   a.packed = reinterpret_cast<uint8_t*>(x.packed);
   a.delta = x.delta;
   a.zero = x.zero;
+  a.codes_ws = x.nbits == 3 ? reinterpret_cast<uint8_t*>(x.workspace) : nullptr;
   a.G = G;
   a.nblocks = hqq::quant_v2_blocks(G, x.group_size);
   a.iters = x.iters;

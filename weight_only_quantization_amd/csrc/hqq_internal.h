@@ -36,7 +36,7 @@ struct SolveArgs {
 hipError_t launch_quantize(const SolveArgs& a, int nbits, int group_size, int axis, int threads, size_t lds_bytes,
                            int64_t N, int stop_rule, double* mae_trace, int32_t* stop_iter, double* reduce_ws,
                            hipStream_t stream);
-// Scale search (second solver, axis 1, 2- and 4-bit): the grid of multipliers of the min-max
+// Scale search (second solver, axis 1, 2/3/4-bit): the grid of multipliers of the min-max
 // scale, passed by value; choice (device, optional) receives the chosen index per group.
 struct ScaleGrid {
   double c[HQQ_V2_MAX_CANDIDATES];

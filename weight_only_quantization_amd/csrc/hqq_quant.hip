@@ -424,7 +424,8 @@ __global__ void __launch_bounds__(256, solve_waves<G>()) k_quant_ax1(const Solve
 // the first k >= 1 whose sum is not below the previous one, else z_iters), and the error sum of
 // the candidate's final codes; candidate 0 first, a later one only with a strictly smaller
 // error.  Axis 1, one tile of 4 GPW groups per block as in the solve pass; a wave runs the
-// rounds of a candidate until every one of its groups has stopped.  No global dependency.
+// rounds of a candidate until every one of its groups has stopped.  No global dependency (the
+// 3-bit codes go through a byte per code and k_pack3, as in the default path).
 // ------------------------------------------------------------------------------------------
 template <int NBITS, int G>
 __global__ void __launch_bounds__(256) k_quant_v2(const SolveArgs a, const ScaleGrid sg) {
@@ -523,7 +524,7 @@ __global__ void __launch_bounds__(256) k_quant_v2(const SolveArgs a, const Scale
           reinterpret_cast<unsigned*>(a.packed)[e0 / 8 + h] = word;
         }
       }
-    } else {
+    } else if constexpr (NBITS == 2) {
       if constexpr (E == 4) {
         a.packed[e0 / 4] = (uint8_t)(cq[0] | (cq[1] << 2) | (cq[2] << 4) | (cq[3] << 6));
       } else {
@@ -535,6 +536,11 @@ __global__ void __launch_bounds__(256) k_quant_v2(const SolveArgs a, const Scale
           reinterpret_cast<unsigned short*>(a.packed)[e0 / 8 + h] = (unsigned short)v;
         }
       }
+    } else {  // 3-bit: one byte per code, packed by k_pack3
+#pragma unroll
+      for (int h = 0; h < E / 4; ++h)
+        reinterpret_cast<unsigned*>(a.codes_ws + e0)[h] =
+            cq[4 * h] | (cq[4 * h + 1] << 8) | (cq[4 * h + 2] << 16) | (cq[4 * h + 3] << 24);
     }
     if (slot == 0) {
       meta_lds[gblock] = best_delta;
@@ -908,7 +914,13 @@ hipError_t launch_quantize_v2(const SolveArgs& a, const ScaleGrid& sg, int nbits
   if (a.nblocks != quant_v2_blocks(a.G, g)) return hipErrorInvalidConfiguration;
   if (nbits == 4) return launch_v2_b<4>(a, sg, g, st);
   if (nbits == 2) return launch_v2_b<2>(a, sg, g, st);
-  return hipErrorInvalidValue;
+  if (nbits != 3 || !a.codes_ws) return hipErrorInvalidValue;
+  hipError_t err = launch_v2_b<3>(a, sg, g, st);
+  if (err != hipSuccess) return err;
+  const int64_t N = a.G * g, nwords = (N + 9) / 10;
+  hipLaunchKernelGGL(k_pack3, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, st, a.codes_ws, N,
+                     reinterpret_cast<uint32_t*>(a.packed), nwords);
+  return hipGetLastError();
 }
 
 }  // namespace hqq
