@@ -62,7 +62,8 @@ def _declare(lib):
         "hqq_oracle_quantize_rule": (i32, [p, i64, i64, i32, i32, i32, i32, dbl, dbl, dbl, dbl, i32, p, p, p, p, p,
                                            p, p]),
         "hqq_oracle_quantize_groups": (i32, [p, i64, i32, i32, i32, dbl, dbl, dbl, dbl, p, p, p, p, p, p]),
-        "hqq_oracle_quantize_v2": (i32, [p, i64, i64, i32, i32, i32, dbl, dbl, dbl, dbl, p, i32, p, p, p, p, p]),
+        "hqq_oracle_quantize_v2": (i32, [p, i64, i64, i32, i32, i32, i32, dbl, dbl, dbl, dbl, p, i32, p, p, p, p,
+                                         p]),
         "hqq_oracle_packed_bytes": (i64, [i64, i32]),
         "hqq_oracle_pack": (i32, [p, i64, i32, p]),
         "hqq_oracle_unpack": (i32, [p, i64, i32, p]),
@@ -167,8 +168,8 @@ class Oracle:
                 "delta16": self.to_half_bits(d), "zero16": self.to_half_bits(z)}
 
     def quantize_v2(self, W, grid, nbits=4, group_size=64, iters=20, p=0.7, beta0=10.0, kappa=1.01,
-                    tiny=TINY_RANGE) -> dict:
-        """Scale search per group (axis 1) over multipliers `grid` of the min-max scale; the reading
+                    tiny=TINY_RANGE, axis=1) -> dict:
+        """Scale search per group over multipliers `grid` of the min-max scale; the reading
         is in hqq_oracle.c (parity unpinned as to the reference project).  Returns codes, s /
         delta / z per group, the chosen multiplier's index per group and the fp16 metadata."""
         rows, cols = W.shape
@@ -178,8 +179,8 @@ class Oracle:
         codes = np.empty((rows, cols), dtype=np.uint8)
         s, d, z = np.empty(G), np.empty(G), np.empty(G)
         choice = np.empty(G, dtype=np.uint8)
-        rc = self.lib.hqq_oracle_quantize_v2(W64.ctypes.data, rows, cols, nbits, group_size, iters, p, beta0, kappa,
-                                             tiny, gr.ctypes.data, gr.size, codes.ctypes.data, s.ctypes.data,
+        rc = self.lib.hqq_oracle_quantize_v2(W64.ctypes.data, rows, cols, nbits, group_size, axis, iters, p, beta0,
+                                             kappa, tiny, gr.ctypes.data, gr.size, codes.ctypes.data, s.ctypes.data,
                                              d.ctypes.data, z.ctypes.data, choice.ctypes.data)
         if rc != 0:
             raise ValueError("oracle quantize_v2 rejected the arguments (rc=%d)" % rc)

@@ -382,14 +382,15 @@ static double candidate_error(const double* w, int g, int nbits, double s, doubl
   return hqq_oracle_sum(absr, g);
 }
 
-int hqq_oracle_quantize_v2(const double* W, int64_t rows, int64_t cols, int nbits, int g, int iters, double p,
-                           double beta0, double kappa, double tiny, const double* grid, int ncand, uint8_t* codes,
-                           double* s_out, double* delta_out, double* z_out, uint8_t* choice_out) {
-  if (!valid_shape(rows, cols, nbits, g, 1) || iters < 0 || ncand < 1 || ncand > 255) return -1;
+int hqq_oracle_quantize_v2(const double* W, int64_t rows, int64_t cols, int nbits, int g, int axis, int iters,
+                           double p, double beta0, double kappa, double tiny, const double* grid, int ncand,
+                           uint8_t* codes, double* s_out, double* delta_out, double* z_out, uint8_t* choice_out) {
+  if (!valid_shape(rows, cols, nbits, g, axis) || iters < 0 || ncand < 1 || ncand > 255) return -1;
   const int64_t G = rows * cols / g;
   const double qmax = (double)((1 << nbits) - 1);
+  double w[g];
   for (int64_t j = 0; j < G; j++) {
-    const double* w = W + j * g; /* axis 1: group j is the run of g consecutive weights */
+    for (int i = 0; i < g; i++) w[i] = W[hqq_oracle_group_elem(rows, cols, g, axis, j, i)];
     double mn = w[0], mx = w[0];
     for (int i = 1; i < g; i++) {
       if (w[i] < mn) mn = w[i];
@@ -437,7 +438,7 @@ int hqq_oracle_quantize_v2(const double* W, int64_t rows, int64_t cols, int nbit
       double q = rint(t);
       if (q < 0.0) q = 0.0;
       if (q > qmax) q = qmax;
-      codes[j * g + i] = (uint8_t)q;
+      codes[hqq_oracle_group_elem(rows, cols, g, axis, j, i)] = (uint8_t)q;
     }
   }
   return 0;

@@ -68,12 +68,12 @@ int hqq_oracle_quantize_rule(const double* W, int64_t rows, int64_t cols, int nb
                              double p, double beta0, double kappa, double tiny, int stop_rule, uint8_t* codes,
                              double* s_out, double* delta_out, double* z_out, double* mae_out, int* rounds_out,
                              int* kout_out);
-/* Scale search per group over a grid of multipliers of the min-max scale (axis 1; reading in
+/* Scale search per group over a grid of multipliers of the min-max scale (reading in
  * hqq_oracle.c, parity unpinned as to the reference project).  choice_out (may be NULL): the
  * index of the chosen multiplier per group. */
-int hqq_oracle_quantize_v2(const double* W, int64_t rows, int64_t cols, int nbits, int g, int iters, double p,
-                           double beta0, double kappa, double tiny, const double* grid, int ncand, uint8_t* codes,
-                           double* s_out, double* delta_out, double* z_out, uint8_t* choice_out);
+int hqq_oracle_quantize_v2(const double* W, int64_t rows, int64_t cols, int nbits, int g, int axis, int iters,
+                           double p, double beta0, double kappa, double tiny, const double* grid, int ncand,
+                           uint8_t* codes, double* s_out, double* delta_out, double* z_out, uint8_t* choice_out);
 int hqq_oracle_quantize_groups(const double* Wg, int64_t n, int g, int nbits, int kout, double p, double beta0,
                                double kappa, double tiny, uint8_t* codes, double* s_out, double* delta_out,
                                double* z_out, double* z_traj, double* err_traj);

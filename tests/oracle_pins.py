@@ -608,4 +608,23 @@ def pin_scale_search_argmin(o):
     assert np.all(mine <= base)
 
 
+def pin_scale_search_axis0(o):
+    """Axis-0 groups of a [g, M] tensor are its columns, which are the axis-1 groups of its
+    transpose: the scale search gives the same steps, zeros and choices, and the transposed
+    codes; for a taller tensor the groups follow reshape([g, -1])."""
+    r = _rng(43)
+    for nbits, g in ((4, 64), (3, 32), (2, 16)):
+        W = r.normal(0, 0.02, (g, 24)).astype(np.float16).astype(np.float64)
+        a0 = o.quantize_v2(W, [0.9, 1.0, 1.1], nbits=nbits, group_size=g, axis=0)
+        a1 = o.quantize_v2(np.ascontiguousarray(W.T), [0.9, 1.0, 1.1], nbits=nbits, group_size=g, axis=1)
+        assert np.array_equal(a0["z"], a1["z"]) and np.array_equal(a0["s"], a1["s"])
+        assert np.array_equal(a0["choice"], a1["choice"]) and np.array_equal(a0["codes"], a1["codes"].T)
+    W = r.normal(0, 0.02, (128, 16)).astype(np.float16).astype(np.float64)
+    a0 = o.quantize_v2(W, [1.0, 1.05], nbits=4, group_size=64, axis=0)
+    view = W.reshape(64, -1)
+    a1 = o.quantize_v2(np.ascontiguousarray(view.T), [1.0, 1.05], nbits=4, group_size=64, axis=1)
+    assert np.array_equal(a0["z"], a1["z"])
+    assert np.array_equal(a0["codes"].reshape(64, -1), a1["codes"].T)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
