@@ -189,8 +189,8 @@ int hqq_quantize_ex(const hqq_quant_args* args);
  * z_iters), and the group's sum of |W - W_hat| over its final codes; the first candidate with
  * the smallest sum wins.  There is no whole-tensor stop and no workspace.
  *
- * Arguments as hqq_quant_args where named alike, with these limits: axis must be 1 (else
- * HQQ_ERR_UNSUPPORTED); scale_grid is a HOST array of n_candidates (1 .. HQQ_V2_MAX_CANDIDATES)
+ * Arguments as hqq_quant_args where named alike (either axis, with hqq_quantize's shape
+ * rules); scale_grid is a HOST array of n_candidates (1 .. HQQ_V2_MAX_CANDIDATES)
  * finite positive multipliers, read before the call returns; choice_dev (device, may be NULL)
  * receives the chosen index per group (G bytes); workspace (device, 16-byte aligned) holds
  * hqq_quantize_v2_workspace_bytes(rows, cols, nbits) bytes (the 3-bit codes before packing; 0

@@ -143,7 +143,7 @@ def test_status_strings(lib):
 
 
 def test_quantize_v2_rejects_before_launch(lib):
-    """hqq_quantize_v2 refuses what it does not take (axis 0), a grid of 0 or more than
+    """hqq_quantize_v2 refuses an unknown axis or a shape its axis does not divide, a grid of 0 or more than
     HQQ_V2_MAX_CANDIDATES multipliers or one that is not finite and positive, a missing or
     small 3-bit workspace, and the shared argument errors, all before any launch."""
     grid = (ctypes.c_double * 17)(*([1.0] * 17))
@@ -156,7 +156,8 @@ def test_quantize_v2_rejects_before_launch(lib):
         a.update(kw)
         return lib.hqq_quantize_v2(ctypes.byref(hq.QuantV2Args(**a)))
     assert lib.hqq_quantize_v2(None) == hq.HQQ_ERR_INVALID_ARGUMENT
-    assert call(axis=0) == hq.HQQ_ERR_UNSUPPORTED
+    assert call(axis=2) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(axis=0, group_size=128) == hq.HQQ_ERR_INVALID_ARGUMENT  # 128 does not divide the 64 rows
     ws3 = lib.hqq_quantize_v2_workspace_bytes(64, 128, 3)
     assert ws3 >= 64 * 128 and lib.hqq_quantize_v2_workspace_bytes(64, 128, 4) == 0
     assert call(nbits=3) == hq.HQQ_ERR_WORKSPACE

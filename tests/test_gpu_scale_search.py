@@ -16,12 +16,12 @@ GRID5 = [0.85, 0.925, 1.0, 1.05, 1.1]
 GRID16 = list(np.linspace(0.8, 1.2, 16))
 
 
-def gpu_v2(W16, grid, nbits, g, iters=20, meta="f64", **kw):
+def gpu_v2(W16, grid, nbits, g, iters=20, meta="f64", axis=1, **kw):
     import weight_only_quantization_amd as hq
     torch = torch_dev()
     Wd = torch.from_numpy(np.ascontiguousarray(W16)).cuda()
     md = {"f16": torch.float16, "f32": torch.float32, "f64": torch.float64}[meta]
-    q, choice = hq.hqq_quantize_v2(Wd, grid, nbits=nbits, group_size=g, iters=iters, meta_dtype=md, **kw)
+    q, choice = hq.hqq_quantize_v2(Wd, grid, nbits=nbits, group_size=g, iters=iters, meta_dtype=md, axis=axis, **kw)
     torch.cuda.synchronize()
     out = {"packed": q.packed.cpu().numpy(), "delta": q.delta.cpu().numpy(), "zero": q.zero.cpu().numpy(),
            "choice": choice.cpu().numpy()}
@@ -29,10 +29,10 @@ def gpu_v2(W16, grid, nbits, g, iters=20, meta="f64", **kw):
     return out
 
 
-def check(W16, grid, nbits, g, iters=20, exact=True, meta="f64", **kw):
+def check(W16, grid, nbits, g, iters=20, exact=True, meta="f64", axis=1, **kw):
     o = oracle.get()
-    ref = o.quantize_v2(W16.astype(np.float64), grid, nbits=nbits, group_size=g, iters=iters, **kw)
-    gq = gpu_v2(W16, grid, nbits, g, iters, meta=meta, **kw)
+    ref = o.quantize_v2(W16.astype(np.float64), grid, nbits=nbits, group_size=g, iters=iters, axis=axis, **kw)
+    gq = gpu_v2(W16, grid, nbits, g, iters, meta=meta, axis=axis, **kw)
     N = W16.size
     G = N // g
     codes = o.unpack(gq["packed"], N, nbits)
@@ -72,6 +72,18 @@ def test_scale_search_parity(nbits, g, rows, cols, grid):
     ref, _ = check(W, grid, nbits, g)
     if len(grid) > 1:
         assert len(set(ref["choice"].tolist())) > 1  # the inputs make the grid matter
+
+
+# axis 0: (rows / g) * cols groups, a multiple of 8, with a ragged last tile of columns
+CASES_AX0 = [(4, 64, 128, 40), (2, 16, 48, 56), (3, 32, 96, 24), (4, 128, 256, 24), (4, 256, 256, 40)]
+
+
+@pytest.mark.parametrize("nbits,g,rows,cols", CASES_AX0)
+@pytest.mark.parametrize("grid", [[1.0], GRID5], ids=["c1", "c5"])
+def test_scale_search_axis0_parity(nbits, g, rows, cols, grid):
+    say("scale search axis 0", nbits, g, rows, cols, len(grid))
+    W = synth.weight_normal(rows, cols, 0.02, seed=rows * cols + g, outlier_frac=0.002, outlier_k=10.0)
+    check(W, grid, nbits, g, axis=0)
 
 
 @pytest.mark.parametrize("meta", ["f16", "f32"])

@@ -220,8 +220,8 @@ def hqq_quantize(W, nbits: int = 4, group_size: int = 64, axis: int = 1, iters: 
 
 def hqq_quantize_v2(W, scale_grid, nbits: int = 4, group_size: int = 64, iters: int = 20, p: float = 0.7,
                     beta0: float = 10.0, kappa: float = 1.01, tiny_range: float | None = None, meta_dtype=None,
-                    out=None, workspace=None, stream=None):
-    """Scale search (axis 1, 2/3/4-bit) over the multipliers `scale_grid` of the min-max scale.
+                    out=None, workspace=None, stream=None, axis: int = 1):
+    """Scale search (either axis, 2/3/4-bit) over the multipliers `scale_grid` of the min-max scale.
     Returns (Quantized, choice): the packed codes, delta and zero as hqq_quantize (no stop index
     or MAE trace: the stop is per group) and the chosen multiplier's index per group (uint8).
     `out` may give (packed, delta, zero, choice)."""
@@ -244,14 +244,14 @@ def hqq_quantize_v2(W, scale_grid, nbits: int = 4, group_size: int = 64, iters: 
     ws_bytes = lib.hqq_quantize_v2_workspace_bytes(rows, cols, nbits)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    args = QuantV2Args(W.data_ptr(), rows, cols, nbits, group_size, 1, iters, p, beta0, kappa,
+    args = QuantV2Args(W.data_ptr(), rows, cols, nbits, group_size, axis, iters, p, beta0, kappa,
                        HQQ_TINY_RANGE if tiny_range is None else tiny_range, grid.ctypes.data, grid.size,
                        packed.data_ptr(), delta.data_ptr(), zero.data_ptr(), _meta_code(meta_dtype),
                        choice.data_ptr() if choice is not None else None, _stream_ptr(stream).value,
                        workspace.data_ptr() if workspace is not None else None,
                        workspace.numel() * workspace.element_size() if workspace is not None else 0)
     _check(lib.hqq_quantize_v2(ctypes.byref(args)))
-    return Quantized(packed, delta, zero, rows, cols, nbits, group_size, 1, None, None), choice
+    return Quantized(packed, delta, zero, rows, cols, nbits, group_size, axis, None, None), choice
 
 
 def hqq_dequantize(packed, delta, zero, rows: int, cols: int, nbits: int, group_size: int, axis: int, out=None,

@@ -210,7 +210,6 @@ int hqq_quantize_v2(const hqq_quant_v2_args* args) {
   const hqq_quant_v2_args& x = *args;
   int st = check_shape(x.rows, x.cols, x.nbits, x.group_size, x.axis);
   if (st != HQQ_OK) return st;
-  if (x.axis != 1) return fail(HQQ_ERR_UNSUPPORTED, "the scale search takes axis 1 only");
   if (x.iters < 0 || x.iters > HQQ_MAX_ITERS) return fail(HQQ_ERR_INVALID_ARGUMENT, "iters must be in [0, %d]", HQQ_MAX_ITERS);
   if (!(x.p > 0.0 && x.p <= 1.0)) return fail(HQQ_ERR_INVALID_ARGUMENT, "p must be in (0, 1]");
   if (!(x.beta0 > 0.0) || !isfinite(x.beta0)) return fail(HQQ_ERR_INVALID_ARGUMENT, "beta0 must be positive");
@@ -253,7 +252,8 @@ int hqq_quantize_v2(const hqq_quant_v2_args* args) {
   for (int c = 0; c < x.n_candidates; ++c) sg.c[c] = x.scale_grid[c];
   sg.n = x.n_candidates;
   sg.choice = x.choice_dev;
-  hipError_t e = hqq::launch_quantize_v2(a, sg, x.nbits, x.group_size, reinterpret_cast<hipStream_t>(x.stream));
+  hipError_t e =
+      hqq::launch_quantize_v2(a, sg, x.nbits, x.group_size, x.axis, reinterpret_cast<hipStream_t>(x.stream));
   if (e != hipSuccess) return device_fail(e, "hqq_quantize_v2 launch");
   return HQQ_OK;
 }

@@ -36,7 +36,7 @@ struct SolveArgs {
 hipError_t launch_quantize(const SolveArgs& a, int nbits, int group_size, int axis, int threads, size_t lds_bytes,
                            int64_t N, int stop_rule, double* mae_trace, int32_t* stop_iter, double* reduce_ws,
                            hipStream_t stream);
-// Scale search (second solver, axis 1, 2/3/4-bit): the grid of multipliers of the min-max
+// Scale search (second solver, either axis, 2/3/4-bit): the grid of multipliers of the min-max
 // scale, passed by value; choice (device, optional) receives the chosen index per group.
 struct ScaleGrid {
   double c[HQQ_V2_MAX_CANDIDATES];
@@ -45,7 +45,7 @@ struct ScaleGrid {
 };
 // Blocks of the scale-search kernel for G groups of size g; launch (a.nblocks must be that).
 int64_t quant_v2_blocks(int64_t G, int g);
-hipError_t launch_quantize_v2(const SolveArgs& a, const ScaleGrid& sg, int nbits, int g, hipStream_t stream);
+hipError_t launch_quantize_v2(const SolveArgs& a, const ScaleGrid& sg, int nbits, int g, int axis, hipStream_t stream);
 // Per-round entries of the intermediate levels of the stop-decision reduction.
 int64_t reduce_scratch_entries(int64_t nblocks, int iters);
 // Geometry of the solve kernel for a configuration: blocks, threads, dynamic LDS bytes.

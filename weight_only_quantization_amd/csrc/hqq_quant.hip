@@ -423,32 +423,17 @@ __global__ void __launch_bounds__(256, solve_waves<G>()) k_quant_ax1(const Solve
 // the proximal rounds with the stop rule applied to the group's own error sum (keep z_(k-1) at
 // the first k >= 1 whose sum is not below the previous one, else z_iters), and the error sum of
 // the candidate's final codes; candidate 0 first, a later one only with a strictly smaller
-// error.  Axis 1, one tile of 4 GPW groups per block as in the solve pass; a wave runs the
-// rounds of a candidate until every one of its groups has stopped.  No global dependency (the
-// 3-bit codes go through a byte per code and k_pack3, as in the default path).
+// error.  One tile of 4 GPW groups per block as in the solve pass (axis 0: a column tile staged
+// through LDS); a wave runs the rounds of a candidate until every one of its groups has
+// stopped.  No global dependency (the 3-bit codes go through a byte per code and k_pack3, as in
+// the default path).
 // ------------------------------------------------------------------------------------------
-template <int NBITS, int G>
-__global__ void __launch_bounds__(256) k_quant_v2(const SolveArgs a, const ScaleGrid sg) {
-  using S = Shape<G>;
-  constexpr int E = S::E, L = S::L, GPW = S::GPW;
-  constexpr int GPB = 4 * GPW;
-  extern __shared__ double meta_lds[];  // [2][groups per block]
-  const int64_t tile = blockIdx.x;
-  if (tile >= a.nblocks) return;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int sub = lane / L, slot = lane % L;
-  const int gblock = wave * GPW + sub;
-  const int64_t gidx = tile * GPB + gblock;
-  const bool valid = gidx < a.G;
-  const int64_t e0 = (valid ? gidx : 0) * G + slot * E;
-
-  double w[E];
-#pragma unroll
-  for (int c = 0; c < E / 2; ++c) {
-    const unsigned u = reinterpret_cast<const unsigned*>(a.W + e0)[c];
-    w[2 * c] = valid ? (double)__half2float(__ushort_as_half((unsigned short)(u & 0xFFFFu))) : 0.0;
-    w[2 * c + 1] = valid ? (double)__half2float(__ushort_as_half((unsigned short)(u >> 16))) : 0.0;
-  }
+// The search for one group from a lane's E weights (L lanes per group): the chosen scale, step,
+// zero and index.  Every lane of the group ends with the same values (the DPP sums and maxima
+// give each lane the bit-identical result).
+template <int E, int L>
+__device__ __forceinline__ void v2_search(const SolveArgs& a, const ScaleGrid& sg, const double (&w)[E], bool valid,
+                                          double& best_s, double& best_delta, double& best_z, int& best_c) {
   double mn = w[0], mx = w[0];
 #pragma unroll
   for (int e = 1; e < E; ++e) {
@@ -460,10 +445,11 @@ __global__ void __launch_bounds__(256) k_quant_v2(const SolveArgs a, const Scale
   const double d = mx - mn;
   const double sb = (d <= a.tiny) ? 1.0 : a.qmax / d;
   const double qmax = __builtin_canonicalize(a.qmax);
-  const double inv_g = 1.0 / (double)G;
+  const double inv_g = 1.0 / (double)(E * L);
 
-  double best_e = 0.0, best_s = 0.0, best_delta = 0.0, best_z = 0.0;
-  int best_c = 0;
+  double best_e = 0.0;
+  best_s = best_delta = best_z = 0.0;
+  best_c = 0;
   double ws[E];
   for (int c = 0; c < sg.n; ++c) {
     const double s = fmin(sb * sg.c[c], HQQ_MAX_SCALE);
@@ -505,11 +491,39 @@ __global__ void __launch_bounds__(256) k_quant_v2(const SolveArgs a, const Scale
       best_c = c;
     }
   }
+}
 
+template <int NBITS, int G>
+__global__ void __launch_bounds__(256) k_quant_v2(const SolveArgs a, const ScaleGrid sg) {
+  using S = Shape<G>;
+  constexpr int E = S::E, L = S::L, GPW = S::GPW;
+  constexpr int GPB = 4 * GPW;
+  extern __shared__ double meta_lds[];  // [2][groups per block]
+  const int64_t tile = blockIdx.x;
+  if (tile >= a.nblocks) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = lane / L, slot = lane % L;
+  const int gblock = wave * GPW + sub;
+  const int64_t gidx = tile * GPB + gblock;
+  const bool valid = gidx < a.G;
+  const int64_t e0 = (valid ? gidx : 0) * G + slot * E;
+
+  double w[E];
+#pragma unroll
+  for (int c = 0; c < E / 2; ++c) {
+    const unsigned u = reinterpret_cast<const unsigned*>(a.W + e0)[c];
+    w[2 * c] = valid ? (double)__half2float(__ushort_as_half((unsigned short)(u & 0xFFFFu))) : 0.0;
+    w[2 * c + 1] = valid ? (double)__half2float(__ushort_as_half((unsigned short)(u >> 16))) : 0.0;
+  }
+  double best_s, best_delta, best_z;
+  int best_c;
+  v2_search<E, L>(a, sg, w, valid, best_s, best_delta, best_z, best_c);
+
+  double ws[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) ws[e] = w[e] * best_s;
   unsigned cq[E];
-  final_codes<E>(ws, best_z, qmax, cq);
+  final_codes<E>(ws, best_z, __builtin_canonicalize(a.qmax), cq);
   if (valid) {
     if constexpr (NBITS == 4) {
       if constexpr (E == 4) {
@@ -549,6 +563,78 @@ __global__ void __launch_bounds__(256) k_quant_v2(const SolveArgs a, const Scale
     }
   }
   store_block_meta(a, meta_lds, GPB, tile * GPB);
+}
+
+// Axis 0: the block stages its g x TW column tile through LDS as the axis-0 solve does, each
+// lane takes E weights of one column, the search runs as on axis 1, and the codes go back
+// through LDS for row-wise packed stores.
+template <int NBITS, int G>
+__global__ void __launch_bounds__(256) k_quant_v2_ax0(const SolveArgs a, const ScaleGrid sg) {
+  using S = Shape<G>;
+  constexpr int E = S::E, L = S::L, GPW = S::GPW;
+  constexpr int TW = 4 * GPW;  // groups per block, as in the axis-0 solve
+  constexpr int CPR = TW / 8, ROW = TW + 8, NT = 256;
+  extern __shared__ double smem[];
+  double* meta_lds = smem;                                   // [2][TW]
+  __half* wt = reinterpret_cast<__half*>(smem + 2 * TW);     // [G][ROW]
+  uint8_t* ct = reinterpret_cast<uint8_t*>(wt);              // [G][TW] after the loads
+  const int64_t tile = blockIdx.x;
+  if (tile >= a.nblocks) return;
+  const int64_t M = a.G, j0 = tile * TW;
+  const int tid = threadIdx.x;
+  for (int task = tid; task < G * CPR; task += NT) {
+    const int i = task / CPR, c = task % CPR;
+    const int64_t col = j0 + 8 * c;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (col < M) v = *reinterpret_cast<const uint4*>(a.W + (int64_t)i * M + col);
+    *reinterpret_cast<uint4*>(wt + i * ROW + 8 * c) = v;
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = lane % L, acol = wave * GPW + lane / L;
+  const int64_t gidx = j0 + acol;
+  const bool valid = gidx < M;
+  double w[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) w[e] = valid ? (double)__half2float(wt[(slot * E + e) * ROW + acol]) : 0.0;
+  __syncthreads();  // the tile is reused for the codes below
+
+  double best_s, best_delta, best_z;
+  int best_c;
+  v2_search<E, L>(a, sg, w, valid, best_s, best_delta, best_z, best_c);
+
+  double ws[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) ws[e] = w[e] * best_s;
+  unsigned cq[E];
+  final_codes<E>(ws, best_z, __builtin_canonicalize(a.qmax), cq);
+#pragma unroll
+  for (int e = 0; e < E; ++e) ct[(slot * E + e) * TW + acol] = (uint8_t)cq[e];
+  if (valid && slot == 0) {
+    meta_lds[acol] = best_delta;
+    meta_lds[TW + acol] = best_z;
+    if (sg.choice) sg.choice[gidx] = (uint8_t)best_c;
+  }
+  store_block_meta(a, meta_lds, TW, j0);  // its barrier also publishes the code tile
+  for (int task = tid; task < G * CPR; task += NT) {  // rows of TW codes, 8 per task
+    const int i = task / CPR, cc = task % CPR;
+    if (j0 + 8 * cc >= M) continue;
+    const uint8_t* cr = ct + i * TW + 8 * cc;
+    const int64_t f = (int64_t)i * M + j0 + 8 * cc;
+    if constexpr (NBITS == 4) {
+      unsigned word = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) word |= (unsigned)cr[e] << (4 * e);
+      reinterpret_cast<unsigned*>(a.packed)[f / 8] = word;
+    } else if constexpr (NBITS == 2) {
+      unsigned v = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v |= (unsigned)cr[e] << (2 * e);
+      reinterpret_cast<unsigned short*>(a.packed)[f / 8] = (unsigned short)v;
+    } else {
+      *reinterpret_cast<uint2*>(a.codes_ws + f) = *reinterpret_cast<const uint2*>(cr);
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -886,20 +972,25 @@ hipError_t launch_quantize(const SolveArgs& a, int nbits, int g, int axis, int t
 
 namespace {
 template <int NBITS, int G>
-hipError_t launch_v2_g(const SolveArgs& a, const ScaleGrid& sg, hipStream_t st) {
-  constexpr int GPB = 4 * Shape<G>::GPW;
-  hipLaunchKernelGGL((k_quant_v2<NBITS, G>), dim3((unsigned)a.nblocks), dim3(256), 2 * GPB * sizeof(double), st, a,
-                     sg);
+hipError_t launch_v2_g(const SolveArgs& a, const ScaleGrid& sg, int axis, hipStream_t st) {
+  constexpr int GPB = 4 * Shape<G>::GPW;  // groups per block on either axis
+  if (axis == 1) {
+    hipLaunchKernelGGL((k_quant_v2<NBITS, G>), dim3((unsigned)a.nblocks), dim3(256), 2 * GPB * sizeof(double), st,
+                       a, sg);
+  } else {
+    const size_t lds = 2 * GPB * sizeof(double) + (size_t)G * (GPB + 8) * sizeof(__half);
+    hipLaunchKernelGGL((k_quant_v2_ax0<NBITS, G>), dim3((unsigned)a.nblocks), dim3(256), lds, st, a, sg);
+  }
   return hipGetLastError();
 }
 template <int NBITS>
-hipError_t launch_v2_b(const SolveArgs& a, const ScaleGrid& sg, int g, hipStream_t st) {
+hipError_t launch_v2_b(const SolveArgs& a, const ScaleGrid& sg, int g, int axis, hipStream_t st) {
   switch (g) {
-    case 16: return launch_v2_g<NBITS, 16>(a, sg, st);
-    case 32: return launch_v2_g<NBITS, 32>(a, sg, st);
-    case 64: return launch_v2_g<NBITS, 64>(a, sg, st);
-    case 128: return launch_v2_g<NBITS, 128>(a, sg, st);
-    case 256: return launch_v2_g<NBITS, 256>(a, sg, st);
+    case 16: return launch_v2_g<NBITS, 16>(a, sg, axis, st);
+    case 32: return launch_v2_g<NBITS, 32>(a, sg, axis, st);
+    case 64: return launch_v2_g<NBITS, 64>(a, sg, axis, st);
+    case 128: return launch_v2_g<NBITS, 128>(a, sg, axis, st);
+    case 256: return launch_v2_g<NBITS, 256>(a, sg, axis, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -910,12 +1001,12 @@ int64_t quant_v2_blocks(int64_t G, int g) {
   return (G + gpb - 1) / gpb;
 }
 
-hipError_t launch_quantize_v2(const SolveArgs& a, const ScaleGrid& sg, int nbits, int g, hipStream_t st) {
-  if (a.nblocks != quant_v2_blocks(a.G, g)) return hipErrorInvalidConfiguration;
-  if (nbits == 4) return launch_v2_b<4>(a, sg, g, st);
-  if (nbits == 2) return launch_v2_b<2>(a, sg, g, st);
+hipError_t launch_quantize_v2(const SolveArgs& a, const ScaleGrid& sg, int nbits, int g, int axis, hipStream_t st) {
+  if (a.nblocks != quant_v2_blocks(a.G, g) || (axis != 0 && axis != 1)) return hipErrorInvalidConfiguration;
+  if (nbits == 4) return launch_v2_b<4>(a, sg, g, axis, st);
+  if (nbits == 2) return launch_v2_b<2>(a, sg, g, axis, st);
   if (nbits != 3 || !a.codes_ws) return hipErrorInvalidValue;
-  hipError_t err = launch_v2_b<3>(a, sg, g, st);
+  hipError_t err = launch_v2_b<3>(a, sg, g, axis, st);
   if (err != hipSuccess) return err;
   const int64_t N = a.G * g, nwords = (N + 9) / 10;
   hipLaunchKernelGGL(k_pack3, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, st, a.codes_ws, N,
