@@ -274,7 +274,7 @@ def main():
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+        print("bench.py measures one GPU only: there is no multi-GPU path (run with --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -68,7 +68,7 @@ extern "C" {
 /* Status codes. */
 #define HQQ_OK 0
 #define HQQ_ERR_INVALID_ARGUMENT 1 /* a pointer, size or parameter is outside the contract */
-#define HQQ_ERR_UNSUPPORTED 2      /* valid HQQ, but a shape/format this build has no kernel for */
+#define HQQ_ERR_UNSUPPORTED 2      /* valid HQQ, but a shape/format the library has no kernel for */
 #define HQQ_ERR_WORKSPACE 3        /* workspace missing or smaller than hqq_quantize_workspace_bytes */
 #define HQQ_ERR_DEVICE 4           /* a HIP call or kernel launch failed */
 

@@ -23,7 +23,7 @@ _SRC = os.path.join(_HERE, "hqq_oracle.c")
 _HDR = os.path.join(_HERE, "hqq_oracle.h")
 _LIB = os.path.join(_HERE, "libhqq_oracle.so")
 
-# The range at or below which s = 1 (the page names no number; this build uses 1e-4).
+# The range at or below which s = 1 (the page names no number; 1e-4 is used here).
 TINY_RANGE = 1e-4
 
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
