@@ -49,7 +49,7 @@ struct QuantLayout {
   int64_t G, nblocks;
   int threads;
   size_t lds;
-  size_t off_partials, off_reduce, off_codes, total;
+  size_t off_partials, off_reduce, off_rounds, off_codes, total;
 };
 
 bool quant_layout(int64_t rows, int64_t cols, int nbits, int g, int axis, int iters, QuantLayout* q) {
@@ -58,7 +58,8 @@ bool quant_layout(int64_t rows, int64_t cols, int nbits, int g, int axis, int it
   auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
   q->off_partials = 256;
   q->off_reduce = up(q->off_partials + (size_t)iters * q->nblocks * sizeof(double));
-  q->off_codes = up(q->off_reduce + (size_t)iters * hqq::reduce_scratch_entries(q->nblocks, iters) * sizeof(double));
+  q->off_rounds = up(q->off_reduce + (size_t)iters * hqq::reduce_scratch_entries(q->nblocks, iters) * sizeof(double));
+  q->off_codes = up(q->off_rounds + (size_t)q->nblocks * sizeof(int32_t));
   q->total = q->off_codes + (nbits == 3 ? up((size_t)(rows * cols)) : 0);
   return true;
 }
@@ -144,6 +145,7 @@ int quantize_impl(const hqq_quant_args& x) {
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   a.ctrl = reinterpret_cast<int32_t*>(ws);
   a.partials = reinterpret_cast<double*>(ws + q.off_partials);
+  a.tile_round = reinterpret_cast<int32_t*>(ws + q.off_rounds);
   a.codes_ws = nbits == 3 ? ws + q.off_codes : nullptr;
   a.G = q.G;
   a.nblocks = q.nblocks;

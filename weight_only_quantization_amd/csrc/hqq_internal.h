@@ -18,6 +18,7 @@ struct SolveArgs {
   uint8_t* codes_ws;   // 3-bit: one byte per code, packed afterwards; else nullptr
   double* partials;    // [iters][nblocks] per-block sums of |W - W_hat| per round
   int32_t* ctrl;       // [0] = index of the kept zero, [1] = rounds evaluated
+  int32_t* tile_round; // [nblocks] latest round at which a wave of the tile froze (iters: one never did)
   int64_t G;           // number of groups (= M for axis 0)
   int64_t nblocks;     // blocks of the solve kernel
   int iters;

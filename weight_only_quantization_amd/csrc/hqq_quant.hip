@@ -194,7 +194,7 @@ __device__ __forceinline__ void hqq_round(const double (&w)[E], const double (&w
 template <int E, int L>
 __device__ __forceinline__ double solve_group(const SolveArgs& a, const double (&w)[E], double (&ws)[E],
                                               bool valid, int kmax, double* err_lds, int stride, bool write_err,
-                                              double& s_o, double& delta_o) {
+                                              double& s_o, double& delta_o, int& kfrozen) {
   double mn = w[0], mx = w[0];
 #pragma unroll
   for (int e = 1; e < E; ++e) {
@@ -214,6 +214,7 @@ __device__ __forceinline__ double solve_group(const SolveArgs& a, const double (
   const double inv_g = 1.0 / (double)(E * L);
   // canonicalised once here, not in every round's clip
   const double qmax = __builtin_canonicalize(a.qmax);
+  kfrozen = kmax;  // the round at which every group of the wave froze (kmax: not before the end)
   double* slot = err_lds;  // round k's entry; the fill below continues from the same pointer
   for (int k = 0; k < kmax; ++k) {
     double err, zn, maxr;
@@ -226,6 +227,7 @@ __device__ __forceinline__ double solve_group(const SolveArgs& a, const double (
     if (__all(frozen)) {
       if (write_err)
         for (int kk = k + 1; kk < a.iters; ++kk, slot += stride) *slot = ev;
+      kfrozen = k;
       break;
     }
   }
@@ -310,6 +312,14 @@ __device__ __forceinline__ void store_block_meta(const SolveArgs& a, const doubl
     store_meta(wave == 0 ? a.delta : a.zero, a.meta_dtype, g0 + lane, meta_lds[wave * ng + lane]);
 }
 
+// Whether the solve records, per tile, the round by which all its waves froze, so that the
+// fix-up can skip tiles that an early stop does not change.  Only for 2-bit codes: their groups
+// converge within a few rounds and the loop stops early, which makes the fix-up redo every
+// group; at 3 and 4 bits the loop usually runs to the end, and the recording cost the solve 9 %
+// (a different schedule of its round loop), so those widths keep the plain fix-up.
+template <int NBITS>
+constexpr bool kRecordFreeze = (NBITS == 2);
+
 // ------------------------------------------------------------------------------------------
 // axis = 1: group j = 64-bit-aligned run of g consecutive weights.  Block = 4 waves.
 // ------------------------------------------------------------------------------------------
@@ -351,7 +361,11 @@ __device__ __forceinline__ void ax1_tile(const SolveArgs& a, int64_t tile, int k
   }
 
   double s, delta;
-  const double z = solve_group<E, L>(a, w, ws, valid, kmax, err_lds + gblock, GPB, !FIX && slot == 0, s, delta);
+  int kfrozen;
+  const double z =
+      solve_group<E, L>(a, w, ws, valid, kmax, err_lds + gblock, GPB, !FIX && slot == 0, s, delta, kfrozen);
+  __shared__ int s_kfrozen[4];
+  if (kRecordFreeze<NBITS> && !FIX && lane == 0) s_kfrozen[wave] = kfrozen;  // published by store_block_meta
 
   unsigned c[E];
   final_codes<E>(ws, z, a.qmax, c);
@@ -397,6 +411,8 @@ __device__ __forceinline__ void ax1_tile(const SolveArgs& a, int64_t tile, int k
     }
   }
   store_block_meta(a, meta_lds, GPB, tile * GPB);
+  if (kRecordFreeze<NBITS> && !FIX && threadIdx.x == 0)
+    a.tile_round[tile] = max(max(s_kfrozen[0], s_kfrozen[1]), max(s_kfrozen[2], s_kfrozen[3]));
   if (!FIX) write_partials<GPB>(a, err_lds, tile);
 }
 
@@ -411,6 +427,9 @@ __global__ void __launch_bounds__(256, solve_waves<G>()) k_quant_ax1(const Solve
     if (kmax >= a.iters) return;  // the loop ran to the end: the solve pass wrote the result
   }
   for (int64_t tile = blockIdx.x; tile < a.nblocks; tile += gridDim.x) {
+    // fix-up: every wave of this tile froze by round kmax, after which its zeros no longer
+    // change, so the solve pass already wrote the codes and zeros of z_kmax
+    if (kRecordFreeze<NBITS> && FIX && a.tile_round[tile] <= kmax) continue;
     ax1_tile<NBITS, G, FIX>(a, tile, kmax, err_lds, meta_lds);
     if (FIX) __syncthreads();
   }
@@ -687,7 +706,10 @@ __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int k
   __syncthreads();  // the tile is reused for the codes below
 
   double s, delta;
-  const double z = solve_group<E, L>(a, w, ws, valid, kmax, err_lds + acol, TW, !FIX && slot == 0, s, delta);
+  int kfrozen;
+  const double z = solve_group<E, L>(a, w, ws, valid, kmax, err_lds + acol, TW, !FIX && slot == 0, s, delta, kfrozen);
+  __shared__ int s_kfrozen[4];
+  if (kRecordFreeze<NBITS> && !FIX && lane == 0) s_kfrozen[wave] = kfrozen;  // published by store_block_meta
 
   unsigned c[E];
   final_codes<E>(ws, z, a.qmax, c);
@@ -704,6 +726,8 @@ __device__ __forceinline__ void ax0_tile(const SolveArgs& a, int64_t tile, int k
     }
   }
   store_block_meta(a, meta_lds, TW, j0);  // its barrier also publishes the code tile
+  if (kRecordFreeze<NBITS> && !FIX && threadIdx.x == 0)
+    a.tile_round[tile] = max(max(s_kfrozen[0], s_kfrozen[1]), max(s_kfrozen[2], s_kfrozen[3]));
   // Rows of TW codes, 8 codes per task: flat index i*M + j0 + 8c (a multiple of 8).
   for (int task = late_tid(); task < G * CPR; task += NT) {
     const int i = task / CPR, cc = task % CPR;
@@ -736,6 +760,7 @@ __global__ void __launch_bounds__(ax0_threads<G>(), solve_waves<G>()) k_quant_ax
     if (kmax >= a.iters) return;
   }
   for (int64_t tile = blockIdx.x; tile < a.nblocks; tile += gridDim.x) {
+    if (kRecordFreeze<NBITS> && FIX && a.tile_round[tile] <= kmax) continue;  // frozen by round kmax
     ax0_tile<NBITS, G, FIX>(a, tile, kmax, smem);
     __syncthreads();
   }
