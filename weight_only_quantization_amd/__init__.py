@@ -16,6 +16,7 @@ from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhqq.so")
+PROBE_LIB_PATH = os.path.join(HERE, "libhqq_probe.so")
 
 HQQ_OK = 0
 HQQ_ERR_INVALID_ARGUMENT = 1
@@ -127,6 +128,63 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context for the tensors a call allocates: the caching allocator ties a block to the stream
+    that is current when it is allocated, so temporaries (workspaces) and outputs are allocated
+    on the stream the kernels run on; a block freed on return is then reused only by work
+    ordered after those kernels."""
+    import contextlib
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _need(t, name, dtype=None, numel=None, min_bytes=None, shape=None, device=True):
+    """Check a tensor operand before its pointer crosses the ABI (the C side reads raw memory of
+    the type the format implies, so a wrong dtype or size would be read silently).  With
+    device=False only the values are checked (the caller checks placement after all operands)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if numel is not None and t.numel() < numel:
+        raise ValueError("%s holds %d elements, %d needed" % (name, t.numel(), numel))
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError("%s holds %d bytes, %d needed" % (name, t.numel() * t.element_size(), min_bytes))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if device:
+        _placed(t, name)
+
+
+def _placed(t, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a CUDA (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _product_operands(packed, delta, zero, N, K, nbits, group_size, x, xname="x", out=None, out_cols=None):
+    """Checks shared by the fused products: codes and fp16 metadata of W [N, K] and fp16 x [batch, *]."""
+    import torch
+    lib = load()
+    if group_size <= 0 or (N * K) % group_size:
+        raise ValueError("group_size must divide N*K")
+    _need(packed, "packed", torch.uint8, min_bytes=lib.hqq_packed_bytes(N, K, nbits), device=False)
+    _need(delta, "delta", torch.float16, numel=N * K // group_size, device=False)
+    _need(zero, "zero", torch.float16, numel=N * K // group_size, device=False)
+    _need(x, xname, torch.float16, device=False)
+    if x.dim() != 2:
+        raise ValueError("%s must be 2-D [batch, K]" % xname)
+    if x.shape[1] != (K if xname == "x" else N):
+        raise ValueError("%s must be [batch, %d], got %s" % (xname, K if xname == "x" else N, tuple(x.shape)))
+    if out is not None:
+        _need(out, "out", (torch.float16, torch.float32), shape=(x.shape[0], out_cols), device=False)
+    for t, name in ((packed, "packed"), (delta, "delta"), (zero, "zero"), (x, xname), (out, "out")):
+        if t is not None:
+            _placed(t, name)
+
+
 _META = {}
 
 
@@ -184,22 +242,32 @@ def hqq_quantize(W, nbits: int = 4, group_size: int = 64, axis: int = 1, iters: 
     range or debug flag other than the defaults goes through hqq_quantize_ex."""
     import torch
     lib = load()
-    assert W.dtype == torch.float16 and W.is_cuda and W.dim() == 2 and W.is_contiguous()
+    _need(W, "W", torch.float16)
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [rows, cols]")
     rows, cols = W.shape
     meta_dtype = meta_dtype or torch.float16
     G = lib.hqq_num_groups(rows, cols, group_size)
     dev = W.device
-    if out is None:
-        packed = torch.empty(max(lib.hqq_packed_bytes(rows, cols, nbits), 1), dtype=torch.uint8, device=dev)
-        delta = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
-        zero = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
-        stop_iter = torch.empty(1, dtype=torch.int32, device=dev)
-        mae_trace = torch.empty(max(iters, 1), dtype=torch.float64, device=dev)
-    else:
-        packed, delta, zero, stop_iter, mae_trace = out
-    ws_bytes = lib.hqq_quantize_workspace_bytes(rows, cols, nbits, group_size, axis, iters)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    with _on(stream):
+        if out is None:
+            packed = torch.empty(max(lib.hqq_packed_bytes(rows, cols, nbits), 1), dtype=torch.uint8, device=dev)
+            delta = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
+            zero = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
+            stop_iter = torch.empty(1, dtype=torch.int32, device=dev)
+            mae_trace = torch.empty(max(iters, 1), dtype=torch.float64, device=dev)
+        else:
+            packed, delta, zero, stop_iter, mae_trace = out
+            _need(packed, "packed", torch.uint8, min_bytes=lib.hqq_packed_bytes(rows, cols, nbits))
+            for t, n in ((delta, "delta"), (zero, "zero")):
+                _need(t, n, meta_dtype, numel=max(G, 1))
+            _need(stop_iter, "stop_iter", torch.int32, numel=1)
+            _need(mae_trace, "mae_trace", torch.float64, numel=iters)
+        ws_bytes = lib.hqq_quantize_workspace_bytes(rows, cols, nbits, group_size, axis, iters)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        else:
+            _need(workspace, "workspace", torch.uint8)
     if stop_rule == HQQ_STOP_BEST and tiny_range is None and debug_flags == 0:
         st = lib.hqq_quantize(ctypes.c_void_p(W.data_ptr()), rows, cols, nbits, group_size, axis, iters, p, beta0,
                               kappa, ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
@@ -228,22 +296,30 @@ def hqq_quantize_v2(W, scale_grid, nbits: int = 4, group_size: int = 64, iters: 
     import numpy as np
     import torch
     lib = load()
-    assert W.dtype == torch.float16 and W.is_cuda and W.dim() == 2 and W.is_contiguous()
+    _need(W, "W", torch.float16)
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [rows, cols]")
     rows, cols = W.shape
     meta_dtype = meta_dtype or torch.float16
     G = lib.hqq_num_groups(rows, cols, group_size)
     dev = W.device
-    if out is None:
-        packed = torch.empty(max(lib.hqq_packed_bytes(rows, cols, nbits), 1), dtype=torch.uint8, device=dev)
-        delta = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
-        zero = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
-        choice = torch.empty(max(G, 1), dtype=torch.uint8, device=dev)
-    else:
-        packed, delta, zero, choice = out
     grid = np.ascontiguousarray(scale_grid, dtype=np.float64)
-    ws_bytes = lib.hqq_quantize_v2_workspace_bytes(rows, cols, nbits)
-    if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    with _on(stream):
+        if out is None:
+            packed = torch.empty(max(lib.hqq_packed_bytes(rows, cols, nbits), 1), dtype=torch.uint8, device=dev)
+            delta = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
+            zero = torch.empty(max(G, 1), dtype=meta_dtype, device=dev)
+            choice = torch.empty(max(G, 1), dtype=torch.uint8, device=dev)
+        else:
+            packed, delta, zero, choice = out
+            _need(packed, "packed", torch.uint8, min_bytes=lib.hqq_packed_bytes(rows, cols, nbits))
+            for t, n in ((delta, "delta"), (zero, "zero")):
+                _need(t, n, meta_dtype, numel=max(G, 1))
+            if choice is not None:
+                _need(choice, "choice", torch.uint8, numel=max(G, 1))
+        ws_bytes = lib.hqq_quantize_v2_workspace_bytes(rows, cols, nbits)
+        if workspace is None and ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     args = QuantV2Args(W.data_ptr(), rows, cols, nbits, group_size, axis, iters, p, beta0, kappa,
                        HQQ_TINY_RANGE if tiny_range is None else tiny_range, grid.ctypes.data, grid.size,
                        packed.data_ptr(), delta.data_ptr(), zero.data_ptr(), _meta_code(meta_dtype),
@@ -259,8 +335,17 @@ def hqq_dequantize(packed, delta, zero, rows: int, cols: int, nbits: int, group_
     """fp16 [rows, cols] W_hat = (q - zero) * delta."""
     import torch
     lib = load()
-    if out is None:
-        out = torch.empty((rows, cols), dtype=torch.float16, device=packed.device)
+    if group_size <= 0 or (rows * cols) % group_size:
+        raise ValueError("group_size must divide rows*cols")
+    _need(packed, "packed", torch.uint8, min_bytes=lib.hqq_packed_bytes(rows, cols, nbits), device=False)
+    _need(delta, "delta", (torch.float16, torch.float32), numel=rows * cols // group_size, device=False)
+    _need(zero, "zero", delta.dtype, numel=rows * cols // group_size, device=False)
+    for t, name in ((packed, "packed"), (delta, "delta"), (zero, "zero")):
+        _placed(t, name)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((rows, cols), dtype=torch.float16, device=packed.device)
+    _need(out, "out", torch.float16, numel=rows * cols)
     st = lib.hqq_dequantize(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
                             ctypes.c_void_p(zero.data_ptr()), _meta_code(delta.dtype), rows, cols, nbits, group_size,
                             axis, ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream))
@@ -274,9 +359,11 @@ def hqq_gemv_w4a16(packed, delta, zero, N: int, K: int, group_size: int, x, out_
     import torch
     lib = load()
     out_dtype = out_dtype or torch.float16
+    _product_operands(packed, delta, zero, N, K, 4, group_size, x, out=out, out_cols=N)
     batch = x.shape[0]
-    if out is None:
-        out = torch.empty((batch, N), dtype=out_dtype, device=x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((batch, N), dtype=out_dtype, device=x.device)
     code = HQQ_OUT_F16 if out.dtype == torch.float16 else HQQ_OUT_F32
     st = lib.hqq_gemv_w4a16(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
                             ctypes.c_void_p(zero.data_ptr()), N, K, group_size, ctypes.c_void_p(x.data_ptr()), batch,
@@ -297,12 +384,15 @@ def hqq_gemm_w4a16(packed, delta, zero, N: int, K: int, group_size: int, x, out_
     import torch
     lib = load()
     out_dtype = out_dtype or torch.float16
+    _product_operands(packed, delta, zero, N, K, 4, group_size, x, out=out, out_cols=N)
     batch = x.shape[0]
-    if out is None:
-        out = torch.empty((batch, N), dtype=out_dtype, device=x.device)
     need = lib.hqq_gemm_workspace_bytes(N, K, batch)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((batch, N), dtype=out_dtype, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8)
     code = HQQ_OUT_F16 if out.dtype == torch.float16 else HQQ_OUT_F32
     st = lib.hqq_gemm_w4a16(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
                             ctypes.c_void_p(zero.data_ptr()), N, K, group_size, ctypes.c_void_p(x.data_ptr()), batch,
@@ -319,12 +409,15 @@ def hqq_gemm(packed, delta, zero, N: int, K: int, nbits: int, group_size: int, a
     import torch
     lib = load()
     out_dtype = out_dtype or torch.float16
+    _product_operands(packed, delta, zero, N, K, nbits, group_size, x, out=out, out_cols=N)
     batch = x.shape[0]
-    if out is None:
-        out = torch.empty((batch, N), dtype=out_dtype, device=x.device)
     need = lib.hqq_gemm_workspace_bytes(N, K, batch)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((batch, N), dtype=out_dtype, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8)
     code = HQQ_OUT_F16 if out.dtype == torch.float16 else HQQ_OUT_F32
     st = lib.hqq_gemm(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
                       ctypes.c_void_p(zero.data_ptr()), N, K, nbits, group_size, axis, ctypes.c_void_p(x.data_ptr()),
@@ -345,12 +438,15 @@ def hqq_gemm_w4a16_dx(packed, delta, zero, N: int, K: int, group_size: int, dy, 
     import torch
     lib = load()
     out_dtype = out_dtype or torch.float16
+    _product_operands(packed, delta, zero, N, K, 4, group_size, dy, xname="dy", out=out, out_cols=K)
     batch = dy.shape[0]
-    if out is None:
-        out = torch.empty((batch, K), dtype=out_dtype, device=dy.device)
     need = lib.hqq_gemm_dx_workspace_bytes(N, K, batch)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dy.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((batch, K), dtype=out_dtype, device=dy.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dy.device)
+    _need(workspace, "workspace", torch.uint8)
     code = HQQ_OUT_F16 if out.dtype == torch.float16 else HQQ_OUT_F32
     st = lib.hqq_gemm_w4a16_dx(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
                                ctypes.c_void_p(zero.data_ptr()), N, K, group_size, ctypes.c_void_p(dy.data_ptr()),
@@ -367,12 +463,61 @@ def hqq_gemv(packed, delta, zero, N: int, K: int, nbits: int, group_size: int, a
     import torch
     lib = load()
     out_dtype = out_dtype or torch.float16
+    _product_operands(packed, delta, zero, N, K, nbits, group_size, x, out=out, out_cols=N)
     batch = x.shape[0]
-    if out is None:
-        out = torch.empty((batch, N), dtype=out_dtype, device=x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((batch, N), dtype=out_dtype, device=x.device)
     code = HQQ_OUT_F16 if out.dtype == torch.float16 else HQQ_OUT_F32
     st = lib.hqq_gemv(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
                       ctypes.c_void_p(zero.data_ptr()), N, K, nbits, group_size, axis, ctypes.c_void_p(x.data_ptr()),
                       batch, ctypes.c_void_p(out.data_ptr()), code, _stream_ptr(stream))
     _check(st)
     return out
+
+
+# ------------------------------------------------------------------------------ HBM probes
+
+PROBE_EXPORTS = ("hqq_probe_copy", "hqq_probe_read")
+_probe = None
+
+
+def load_probe(path: str = PROBE_LIB_PATH):
+    """Load libhqq_probe.so (include/hqq_probe.h): a streaming copy and read of known byte counts,
+    used by the measurements; no part of the method."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(path):
+            raise OSError("libhqq_probe.so not built (run `python -m weight_only_quantization_amd.build`): %s" % path)
+        lib = ctypes.CDLL(path)
+        p, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        lib.hqq_probe_copy.argtypes = [p, p, sz, i32, p]
+        lib.hqq_probe_copy.restype = i32
+        lib.hqq_probe_read.argtypes = [ctypes.POINTER(p), ctypes.POINTER(sz), i32, p, i32, p]
+        lib.hqq_probe_read.restype = i32
+        _probe = lib
+    return _probe
+
+
+def probe_copy(src, dst, unroll: int = 4, stream=None):
+    """dst[:] = src[:] (same byte count) with the streaming copy kernel."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    if load_probe().hqq_probe_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, unroll,
+                                   _stream_ptr(stream)) != 0:
+        raise RuntimeError("hqq_probe_copy failed")
+
+
+def probe_read(bufs, sink, unroll: int = 4, stream=None) -> int:
+    """Stream the tensors in `bufs` (1-3) once; `sink` is a 16-byte device tensor.  Each buffer is
+    read up to the last whole 16-byte block (a packed 3-bit buffer may end inside one); returns
+    the bytes read."""
+    n = len(bufs)
+    ptrs = (ctypes.c_void_p * n)(*[b.data_ptr() for b in bufs])
+    nb = [(b.numel() * b.element_size()) & ~15 for b in bufs]
+    sizes = (ctypes.c_size_t * n)(*nb)
+    if load_probe().hqq_probe_read(ptrs, sizes, n, ctypes.c_void_p(sink.data_ptr()), unroll,
+                                   _stream_ptr(stream)) != 0:
+        raise RuntimeError("hqq_probe_read failed")
+    return sum(nb)
