@@ -63,6 +63,28 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
+GEMV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+GEMV_SOURCES = ("hqq_gemv.hip", "hqq_gemv_common.h", "hqq_internal.h")
+
+
+def gemv_traffic():
+    """HBM bytes per call of the batch-1 GEMV from the committed counter runs, if they were taken
+    on the current kernel sources (else null)."""
+    if not os.path.exists(GEMV_TRAFFIC_FILE):
+        return None
+    with open(GEMV_TRAFFIC_FILE) as f:
+        tr = json.load(f)
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_only_quantization_amd", "csrc")
+    for fn in GEMV_SOURCES:
+        with open(os.path.join(csrc, fn), "rb") as fh:
+            h.update(fn.encode() + fh.read())
+    k = tr.get("kernels", {}).get("gemv_b1")
+    if not k or k.get("source_sha") != h.hexdigest():
+        return None
+    return k.get("bytes_per_call")
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -158,7 +180,7 @@ def scale_search_leg(timed, dev):
             "chosen_per_multiplier": counts.cpu().tolist()}
 
 
-def config_legs(a, timed, stream, dev):
+def config_legs(a, timed, stream, dev, rotated, read_floor):
     """Legs outside the step, one per remaining configuration: the 7B-shaped layer set at 3-bit
     g64 and 2-bit g16 (Laplace weights), the 28672x8192 axis-0 g128 weight, and the fused
     products over the 3-bit, 2-bit and axis-0 formats (batch 1 and 2; batch 256 through hqq_gemm for
@@ -185,28 +207,32 @@ def config_legs(a, timed, stream, dev):
                                 beta0=qp.beta0, kappa=qp.kappa, workspace=ws,
                                 out=(q.packed, q.delta, q.zero, q.stop_iter, q.mae_trace))
 
-        Wh = [torch.empty_like(W) for W in Ws]
-
-        def dqall(r):
-            for t, q, o in zip(tensors, outs, Wh):
-                hq.hqq_dequantize(q.packed, q.delta, q.zero, t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=o)
-
         tq = timed(qall, reps)
-        td = timed(dqall, reps)
+        del wss
+        Wh = [torch.empty_like(W) for W in Ws]
+        del Ws
         n = sum(t.rows * t.cols for t in tensors)
         wb = 3.2 if qp.nbits == 3 else qp.nbits
         byt = sum(t.rows * t.cols * (wb / 8 + 4 / qp.group_size) for t in tensors)
+        dcopies = rotated([(q.packed, q.delta, q.zero) for q in outs], byt)
+
+        def dqall(r):
+            for t, (pk, d, z), o in zip(tensors, dcopies[r % len(dcopies)], Wh):
+                hq.hqq_dequantize(pk, d, z, t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=o)
+
+        td = timed(dqall, 2 * len(dcopies))
         leg = {"quantize_s": tq, "quantize_gweights_per_s": n / tq / 1e9,
                "stop_index_per_layer": [int(q.stop_iter.item()) for q in outs],
                "dequant_s": td, "dequant_GB/s": (byt + 2 * n) / td / 1e9,
-               "dequant_frac_hbm": (byt + 2 * n) / td / PEAK_HBM}
-        del Ws, wss, Wh
+               "dequant_frac_hbm": (byt + 2 * n) / td / PEAK_HBM, "dequant_copies_rotated": len(dcopies)}
+        del Wh, dcopies
         return leg, outs
 
     def gemv_leg(name, q, N, K, nbits, g, axis, byt_w):
         ncopy = max(4, int(np.ceil(1.1e9 / byt_w)))
         copies = [(q.packed.clone(), q.delta.clone(), q.zero.clone()) for _ in range(ncopy)]
         X = torch.from_numpy(synth.activations(2, K, 402)).to(dev)
+        legs["%s_read_floor" % name] = read_floor(copies)
         for b in (1, 2):
             Y = torch.empty((b, N), dtype=torch.float16, device=dev)
 
@@ -216,7 +242,8 @@ def config_legs(a, timed, stream, dev):
             tg = timed(gv, 2 * ncopy)
             byt = byt_w + 2 * b * K + 2 * b * N
             legs["%s_b%d" % (name, b)] = {"us": tg * 1e6, "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM,
-                                          "bytes": byt, "shape": [N, K], "copies_rotated": ncopy}
+                                          "bytes": byt, "shape": [N, K], "copies_rotated": ncopy,
+                                          "frac_of_read_floor": legs["%s_read_floor" % name]["us"] / (tg * 1e6)}
         if axis == 1:  # the batched product over the same format at batch 256 (hqq_gemm)
             B = 256
             X2 = torch.from_numpy(synth.activations(B, K, 403)).to(dev)
@@ -272,6 +299,8 @@ def main():
                     help="skip the 3-/2-bit, axis-0 and other-format legs outside the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="each leg's kernels run a few times without timing loops (for rocprofv3 --pmc runs)")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (run with --gpus 1).",
@@ -376,7 +405,13 @@ def main():
     def timed(fn, reps):
         """Mean GPU time of one call over `reps` back-to-back calls on the launch stream.  A spin
         kernel holds the stream while the host enqueues the calls (so that host launch overhead
-        never leaves the GPU idle between them); one event pair brackets the calls."""
+        never leaves the GPU idle between them); one event pair brackets the calls.  In a counter
+        pass the calls run a few times, untimed (rocprofv3 serialises and samples each dispatch)."""
+        if a.counter_pass:
+            for r in range(min(reps, 3)):
+                fn(r)
+            torch.cuda.synchronize()
+            return float("nan")
         fn(0)
         torch.cuda.synchronize()
         h0 = time.perf_counter()
@@ -393,16 +428,44 @@ def main():
         torch.cuda.synchronize()
         return t0_ev.elapsed_time(t1_ev) * 1e-3 / reps  # s per call
 
-    def dq_all(r):
-        for t, W, ws, out, What in layers:
-            hq.hqq_dequantize(out[0], out[1], out[2], t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=What)
+    def rotated(bufs, nbytes):
+        """Copies of `bufs` (a list of tensors or of tuples of tensors) totalling >= 1.1 GB of
+        operands (`nbytes` per set), so that a timing loop over them reads HBM, not the 256 MB
+        last-level cache."""
+        n = max(4, int(np.ceil(1.1e9 / nbytes)))
+        cl = lambda b: tuple(t.clone() for t in b) if isinstance(b, tuple) else b.clone()
+        return [[cl(b) for b in bufs] for _ in range(n)]
+
+    probe_sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def read_floor(copies):
+        """The HBM floor of a kernel that must stream these operands once: the probe's streaming
+        read of one copy's buffers in one launch, timed back to back over the rotated copies
+        (best of 4 and 8 loads in flight per thread)."""
+        nb = sum((t.numel() * t.element_size()) & ~15 for t in copies[0])  # whole 16-byte blocks
+        best = None
+        for u in (4, 8):
+            tr = timed(lambda r, u=u: hq.probe_read(copies[r % len(copies)], probe_sink, unroll=u), 2 * len(copies))
+            if best is None or tr < best[0]:
+                best = (tr, u)
+        return {"us": best[0] * 1e6, "GB/s": nb / best[0] / 1e9, "frac_hbm": nb / best[0] / PEAK_HBM, "bytes": nb,
+                "loads_in_flight": best[1], "copies_rotated": len(copies)}
 
     legs = {}
-    t_dq = timed(dq_all, 10)
     dq_bytes = sum(t.rows * t.cols * (qp.nbits / 8 + 2) + 4 * t.rows * t.cols / qp.group_size
                    for t, *_ in layers)
+    dq_in = sum(t.rows * t.cols * qp.nbits / 8 + 4 * t.rows * t.cols / qp.group_size for t, *_ in layers)
+    dq_copies = rotated([(out[0], out[1], out[2]) for _, _, _, out, _ in layers], dq_in)
+
+    def dq_all(r):
+        for (t, W, ws, out, What), (pk, d, z) in zip(layers, dq_copies[r % len(dq_copies)]):
+            hq.hqq_dequantize(pk, d, z, t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=What)
+
+    t_dq = timed(dq_all, 2 * len(dq_copies))
     legs["dequant"] = {"s_per_layer_set": t_dq, "GB/s": dq_bytes / t_dq / 1e9,
-                       "frac_hbm": dq_bytes / t_dq / PEAK_HBM, "bytes": dq_bytes}
+                       "frac_hbm": dq_bytes / t_dq / PEAK_HBM, "bytes": dq_bytes, "copies_rotated": len(dq_copies)}
+    del dq_copies
+    legs["gemv_read_floor"] = read_floor(copies)
     for b in (1, 8, 256):
         def gv(r, b=b):
             pk, d, z = copies[r % ncopy]
@@ -412,7 +475,7 @@ def main():
         flops = 2.0 * b * GN * GK
         legs["gemv_b%d" % b] = {"us": tg * 1e6, "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM,
                                 "TFLOP/s": flops / tg / 1e12, "frac_mfma_f16": flops / tg / PEAK_FP16_MFMA,
-                                "bytes": byt}
+                                "bytes": byt, "frac_of_read_floor": legs["gemv_read_floor"]["us"] / (tg * 1e6)}
 
     # the input gradient dX = dY W_hat (training through the frozen weight) at batch 256
     dx_ws = torch.empty(max(hq.hqq_gemm_dx_workspace_bytes(GN, GK, 256), 16), dtype=torch.uint8, device=dev)
@@ -426,26 +489,27 @@ def main():
     flops = 2.0 * 256 * GN * GK
     legs["dx_b256"] = {"us": tg * 1e6, "TFLOP/s": flops / tg / 1e12, "frac_mfma_f16": flops / tg / PEAK_FP16_MFMA}
 
-    # a plain device copy on the same box: the HBM rate a kernel can reach in practice
+    # a streaming device copy on the same box (the probe's 16-byte non-temporal loads and stores,
+    # best of 4 and 8 loads in flight): the HBM rate a read + write kernel reaches in practice
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
-    tc = timed(lambda r: cdst.copy_(csrc), 20)
+    tc = min(timed(lambda r, u=u: hq.probe_copy(csrc, cdst, unroll=u), 20) for u in (4, 8))
     copy_bps = 2.0 * csrc.numel() / tc
-    legs["stream_copy_1GiB"] = {"us": tc * 1e6, "GB/s": copy_bps / 1e9, "frac_hbm": copy_bps / PEAK_HBM}
+    legs["probe_copy_1GiB"] = {"us": tc * 1e6, "GB/s": copy_bps / 1e9, "frac_hbm": copy_bps / PEAK_HBM}
     del csrc, cdst
 
     if not a.no_extra_legs:
-        legs.update(config_legs(a, timed, stream, dev))
+        legs.update(config_legs(a, timed, stream, dev, rotated, read_floor))
     for leg in legs.values():  # every HBM fraction also against the measured copy rate
         if "frac_hbm" in leg:
             leg["frac_copy"] = leg["frac_hbm"] * PEAK_HBM / copy_bps
         if "dequant_frac_hbm" in leg:
             leg["dequant_frac_copy"] = leg["dequant_frac_hbm"] * PEAK_HBM / copy_bps
 
-    if a.copy_probe:
+    if a.copy_probe:  # one 1 GiB probe copy: the counter calibration of known size
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        hq.probe_copy(src, dst, unroll=4)
         torch.cuda.synchronize()
         del src, dst
 
@@ -465,6 +529,13 @@ def main():
             "kernel": "hqq_quantize (solve + stop decision + fix-up), 7 layers",
             "ops_per_weight": "%d per evaluated round + %d" % (OPS_PER_ROUND, OPS_FIXED),
             "rounds_evaluated": rounds, "seconds_per_layer_set": q_s_total}
+    g1 = legs["gemv_b1"]
+    roof_gemv = {"bound": "hbm", "achieved": g1["GB/s"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                 "frac": g1["frac_hbm"], "traffic": gemv_traffic(),
+                 "kernel": "hqq_gemv_w4a16 batch 1 (k_gemv_valu), 8192x8192 4-bit g64, fp16 step and zero",
+                 "us": g1["us"], "bytes": g1["bytes"],
+                 "read_floor_us": legs["gemv_read_floor"]["us"],
+                 "frac_of_read_floor": g1["frac_of_read_floor"]}
     alg_bytes_q = sum(t.rows * t.cols * (2 + qp.nbits / 8) + 4 * t.rows * t.cols / qp.group_size
                       for t, *_ in layers)
 
@@ -490,6 +561,7 @@ def main():
         "stop_index_per_layer": stops,
         "legs": legs,
         "roofline": roof,
+        "roofline_gemv_b1": roof_gemv,
         "wall_s": wall,
     }
     if not a.no_cpu_baseline:

@@ -203,3 +203,25 @@ def test_quantize_ex_rejects_before_launch(lib):
     assert call(workspace_bytes=ws - 8) == hq.HQQ_ERR_WORKSPACE
     assert call(p=0.0) == hq.HQQ_ERR_INVALID_ARGUMENT
     assert hq.last_error() != ""
+
+
+def test_probe_library_exports_and_checks():
+    """libhqq_probe.so (include/hqq_probe.h) loads, exports what its header declares and refuses
+    invalid arguments before any launch."""
+    if not os.path.exists(hq.PROBE_LIB_PATH):
+        from weight_only_quantization_amd import build
+        build.build()
+    plib = hq.load_probe()
+    src = open(os.path.join(ROOT, "include", "hqq_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(hqq_probe_[a-z0-9_]+)\s*\(", src)))
+    assert set(names) == set(hq.PROBE_EXPORTS), names
+    for n in names:
+        assert hasattr(plib, n), n
+    assert plib.hqq_probe_copy(FAKE, FAKE, 24, 4, None) == 1          # not a multiple of 16
+    assert plib.hqq_probe_copy(FAKE, FAKE, 4096, 5, None) == 1        # unroll
+    assert plib.hqq_probe_copy(None, FAKE, 4096, 4, None) == 1
+    p3 = (ctypes.c_void_p * 1)(FAKE.value)
+    assert plib.hqq_probe_read(p3, (ctypes.c_size_t * 1)(4096), 0, FAKE, 4, None) == 1    # nbuf
+    assert plib.hqq_probe_read(p3, (ctypes.c_size_t * 1)(4100), 1, FAKE, 4, None) == 1    # size
+    assert plib.hqq_probe_read(p3, (ctypes.c_size_t * 1)(4096), 1, None, 4, None) == 1    # sink

@@ -13,6 +13,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhqq.so")
+PROBE_LIB = os.path.join(HERE, "libhqq_probe.so")
 OBJDIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -24,6 +25,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-ffp-contract=
          "-Wall", "-Wno-unused-function", "-I" + os.path.join(HERE, "..", "include")]
 
 SOURCES = ["hqq_api.hip", "hqq_quant.hip", "hqq_dequant.hip", "hqq_gemv.hip", "hqq_gemv_ext.hip", "hqq_gemm.hip"]
+# HBM probes of known byte counts (measurement only), a library of their own
+PROBE_SOURCES = ["hqq_probe.hip"]
 
 # The split GEMM keeps its 128 MFMA accumulators per lane in ordinary VGPRs: with the default
 # (accumulation-register) form the register allocator does not tie each MFMA's result to its
@@ -44,13 +47,18 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs])
+    os.replace(tmp, lib)
+
+
 def build(jobs: int = 4) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    subprocess.check_call([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     return LIB
 
 
