@@ -41,7 +41,8 @@
  *
  * Conventions:
  *   - Ownership: every pointer is caller-owned device memory (workspace
- *     included).  The library allocates, frees and retains nothing.
+ *     included).  The library allocates, frees and retains nothing (its only device
+ *     memory is the static scratch array of hqq_quantize_noalloc).
  *   - Asynchrony: every compute call only enqueues work on `stream` (a
  *     hipStream_t, NULL = the default stream) and returns; nothing is
  *     synchronised.  Outputs are valid once the stream has reached that point.
@@ -53,7 +54,8 @@
  *     status means nothing was launched (HQQ_ERR_DEVICE: a launch failed; the
  *     message is in hqq_last_error()).  No exception crosses the ABI.
  *   - State: the library keeps no mutable global state, so calls on different
- *     streams may run concurrently (with distinct workspaces).
+ *     streams may run concurrently (with distinct workspaces); the one exception is
+ *     hqq_quantize_noalloc, whose calls on one GPU share that GPU's scratch array.
  */
 #ifndef HQQ_H
 #define HQQ_H
@@ -131,6 +133,25 @@ int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int 
                  double p, double beta0, double kappa, void* packed, void* delta, void* zero, int meta_dtype,
                  void* workspace, size_t workspace_bytes, int32_t* stop_iter_dev, double* mae_trace_dev,
                  void* stream);
+
+/*
+ * Allocation-free variant of hqq_quantize, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * operation, arguments (without the workspace), layout, ownership of the caller's buffers and
+ * asynchrony as hqq_quantize; its workspace is a device array owned by the library, one copy per
+ * GPU of HQQ_NOALLOC_SCRATCH_BYTES, set up on the first call on that device (with the device
+ * current) and held until the process ends.  It calls no hipMalloc, hipFree or allocating
+ * library routine.  Limit: tensors whose hqq_quantize_workspace_bytes(...) exceeds
+ * HQQ_NOALLOC_SCRATCH_BYTES are refused with HQQ_ERR_WORKSPACE before anything is enqueued
+ * (e.g. the per-round error sums of 20 rounds over a 28672x8192 tensor take 19 MB; 3-bit codes
+ * take one more byte per weight).  Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be serialised by the caller;
+ * the array needs no clearing between calls (no part of it has to start at zero).
+ */
+#define HQQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+int hqq_quantize_noalloc(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int group_size, int axis,
+                         int iters, double p, double beta0, double kappa, void* packed, void* delta, void* zero,
+                         int meta_dtype, int32_t* stop_iter_dev, double* mae_trace_dev, void* stream);
 
 /* Stop rules of hqq_quantize_ex: readings of "第二拍" (the loop stops at the first round k >= 1
  * whose whole-tensor MAE is not below the best so far, and rolls back to the previous

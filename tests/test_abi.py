@@ -225,3 +225,20 @@ def test_probe_library_exports_and_checks():
     assert plib.hqq_probe_read(p3, (ctypes.c_size_t * 1)(4096), 0, FAKE, 4, None) == 1    # nbuf
     assert plib.hqq_probe_read(p3, (ctypes.c_size_t * 1)(4100), 1, FAKE, 4, None) == 1    # size
     assert plib.hqq_probe_read(p3, (ctypes.c_size_t * 1)(4096), 1, None, 4, None) == 1    # sink
+
+
+def test_noalloc_rejects_before_any_device_call(lib):
+    """hqq_quantize_noalloc checks the shape and its scratch need before it touches the device."""
+    i64 = ctypes.c_int64
+    def call(rows, cols, nbits, g, axis, iters):
+        return lib.hqq_quantize_noalloc(FAKE, rows, cols, nbits, g, axis, iters, 0.7, 10.0, 1.01, FAKE, FAKE, FAKE,
+                                        hq.HQQ_META_F16, None, None, None)
+    # 4-bit g64 at 20 rounds over 65536x8192: 42 MB of per-round sums, beyond the array
+    need = hq.hqq_quantize_workspace_bytes(65536, 8192, 4, 64, 1, 20)
+    assert need > hq.HQQ_NOALLOC_SCRATCH_BYTES
+    assert call(65536, 8192, 4, 64, 1, 20) == hq.HQQ_ERR_WORKSPACE
+    assert "scratch" in hq.last_error()
+    assert call(8192, 8192, 3, 64, 1, 20) == hq.HQQ_ERR_WORKSPACE      # 3-bit: a byte per code
+    assert call(64, 64, 5, 64, 1, 20) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(64, 64, 4, 64, 1, 65) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call(64, 96, 4, 64, 1, 20) == hq.HQQ_ERR_INVALID_ARGUMENT    # 64 does not divide 96

@@ -29,9 +29,11 @@ HQQ_MAX_ITERS = 64
 HQQ_TINY_RANGE = 1e-4
 HQQ_STOP_BEST, HQQ_STOP_FAILED, HQQ_STOP_NONE, HQQ_STOP_MEASURED_END = 0, 1, 2, 4
 HQQ_DEBUG_NO_FROZEN_SKIP, HQQ_DEBUG_SLOW_SHRINK, HQQ_DEBUG_SYNC = 1, 2, 4
+HQQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol the header declares.
 EXPORTS = ("hqq_packed_bytes", "hqq_num_groups", "hqq_quantize_workspace_bytes", "hqq_quantize", "hqq_quantize_ex",
+           "hqq_quantize_noalloc",
            "hqq_quantize_v2", "hqq_quantize_v2_workspace_bytes",
            "hqq_dequantize", "hqq_gemv_w4a16", "hqq_gemm_workspace_bytes", "hqq_gemm_w4a16",
            "hqq_gemm_dx_workspace_bytes", "hqq_gemm_w4a16_dx", "hqq_gemv", "hqq_gemm",
@@ -63,6 +65,8 @@ def load(path: str = LIB_PATH):
     lib.hqq_quantize_workspace_bytes.restype = sz
     lib.hqq_quantize.argtypes = [p, i64, i64, i32, i32, i32, i32, dbl, dbl, dbl, p, p, p, i32, p, sz, p, p, p]
     lib.hqq_quantize.restype = i32
+    lib.hqq_quantize_noalloc.argtypes = [p, i64, i64, i32, i32, i32, i32, dbl, dbl, dbl, p, p, p, i32, p, p, p]
+    lib.hqq_quantize_noalloc.restype = i32
     lib.hqq_quantize_ex.argtypes = [ctypes.POINTER(QuantArgs)]
     lib.hqq_quantize_ex.restype = i32
     lib.hqq_quantize_v2.argtypes = [ctypes.POINTER(QuantV2Args)]
@@ -282,6 +286,34 @@ def hqq_quantize(W, nbits: int = 4, group_size: int = 64, axis: int = 1, iters: 
                          _stream_ptr(stream).value, stop_rule, HQQ_TINY_RANGE if tiny_range is None else tiny_range,
                          debug_flags)
         st = lib.hqq_quantize_ex(ctypes.byref(args))
+    _check(st)
+    return Quantized(packed, delta, zero, rows, cols, nbits, group_size, axis, stop_iter, mae_trace)
+
+
+def hqq_quantize_noalloc(W, out, nbits: int = 4, group_size: int = 64, axis: int = 1, iters: int = 20,
+                         p: float = 0.7, beta0: float = 10.0, kappa: float = 1.01, stream=None) -> Quantized:
+    """hqq_quantize into caller-given outputs `out` = (packed, delta, zero, stop_iter, mae_trace)
+    with the library's own scratch array: the call allocates nothing (no torch allocation either),
+    so it may run where allocation is not allowed.  Calls on one GPU share its scratch array and
+    must not overlap."""
+    import torch
+    lib = load()
+    _need(W, "W", torch.float16)
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [rows, cols]")
+    rows, cols = W.shape
+    packed, delta, zero, stop_iter, mae_trace = out
+    G = lib.hqq_num_groups(rows, cols, group_size)
+    _need(packed, "packed", torch.uint8, min_bytes=lib.hqq_packed_bytes(rows, cols, nbits))
+    _need(delta, "delta", (torch.float16, torch.float32, torch.float64), numel=max(G, 1))
+    _need(zero, "zero", delta.dtype, numel=max(G, 1))
+    _need(stop_iter, "stop_iter", torch.int32, numel=1)
+    _need(mae_trace, "mae_trace", torch.float64, numel=iters)
+    st = lib.hqq_quantize_noalloc(ctypes.c_void_p(W.data_ptr()), rows, cols, nbits, group_size, axis, iters, p, beta0,
+                                  kappa, ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                                  ctypes.c_void_p(zero.data_ptr()), _meta_code(delta.dtype),
+                                  ctypes.c_void_p(stop_iter.data_ptr()), ctypes.c_void_p(mae_trace.data_ptr()),
+                                  _stream_ptr(stream))
     _check(st)
     return Quantized(packed, delta, zero, rows, cols, nbits, group_size, axis, stop_iter, mae_trace)
 

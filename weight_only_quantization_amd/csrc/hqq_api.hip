@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "hqq_internal.h"
 
 namespace {
@@ -186,6 +188,67 @@ int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int 
   const hqq_quant_args x = {W_fp16, rows, cols, nbits, group_size, axis, iters, p, beta0, kappa, packed, delta,
                             zero, meta_dtype, workspace, workspace_bytes, stop_iter_dev, mae_trace_dev, stream,
                             HQQ_STOP_BEST, HQQ_TINY_RANGE, 0};
+  return quantize_impl(x);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------------
+// Allocation-free quantisation: the workspace of hqq_quantize in a library-owned device array
+// (one copy per GPU, held until the process ends).  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is taken per device with
+// hipGetSymbolAddress on the first call there and only that address is handed to kernels.
+// ------------------------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[HQQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (set up once per device, with it current).
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HQQ_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned16(ptr)) return fail(HQQ_ERR_DEVICE, "scratch array has no usable device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HQQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hqq_quantize_noalloc(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int group_size, int axis,
+                         int iters, double p, double beta0, double kappa, void* packed, void* delta, void* zero,
+                         int meta_dtype, int32_t* stop_iter_dev, double* mae_trace_dev, void* stream) {
+  g_last_error[0] = 0;
+  // everything that can be checked without the device first: the shape, then the scratch need
+  int st = check_shape(rows, cols, nbits, group_size, axis);
+  if (st != HQQ_OK) return st;
+  if (iters < 0 || iters > HQQ_MAX_ITERS) return fail(HQQ_ERR_INVALID_ARGUMENT, "iters must be in [0, %d]", HQQ_MAX_ITERS);
+  QuantLayout q;
+  if (!quant_layout(rows, cols, nbits, group_size, axis, iters, &q))
+    return fail(HQQ_ERR_UNSUPPORTED, "configuration needs more LDS than one block may use");
+  if (q.total > (size_t)HQQ_NOALLOC_SCRATCH_BYTES)
+    return fail(HQQ_ERR_WORKSPACE, "this tensor needs %zu bytes of scratch, beyond the %zu of the allocation-free entry point",
+                q.total, (size_t)HQQ_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != HQQ_OK) return st;
+  const hqq_quant_args x = {W_fp16, rows, cols, nbits, group_size, axis, iters, p, beta0, kappa, packed, delta,
+                            zero, meta_dtype, ws, (size_t)HQQ_NOALLOC_SCRATCH_BYTES, stop_iter_dev, mae_trace_dev,
+                            stream, HQQ_STOP_BEST, HQQ_TINY_RANGE, 0};
   return quantize_impl(x);
 }
 
