@@ -226,6 +226,19 @@ def test_gemv_parity_long_rows(K, batch):
     check_gemv(packed, d16, z16, N, K, 64, x, out_f32=True)
 
 
+@pytest.mark.parametrize("g", [64, 128])
+@pytest.mark.parametrize("N,K,batch", [(8192, 256, 6), (8192, 640, 3), (32, 20480, 1), (32, 18432, 2),
+                                       (48, 2176, 5)])
+def test_gemv_parity_mfma_blocks(g, N, K, batch):
+    """The batched MFMA GEMV: two 16-row strips per block (N = 8192), one segment shorter than
+    2048 codes, a partial last segment, and batch 1-2 rows longer than the streaming kernel takes."""
+    say("gemv mfma", g, N, K, batch)
+    packed, d16, z16 = gemv_inputs(N, K, g, seed=4100 + N + K)
+    x = synth.activations(batch, K, seed=19)
+    check_gemv(packed, d16, z16, N, K, g, x, out_f32=True)
+    check_gemv(packed, d16, z16, N, K, g, x, out_f32=False)
+
+
 def test_gemv_onehot_columns():
     """A one-hot activation row returns one column of W_hat (to fp32 rounding)."""
     import weight_only_quantization_amd as hq

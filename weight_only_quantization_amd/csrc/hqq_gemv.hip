@@ -1,28 +1,33 @@
 // Fused dequantise + product, 4-bit weights, fp16 activations, fp32 accumulation (page
 // "HQQ 算法解读", section "从压缩文件到一次前向": unpack, (q - zero) * scale, x @ W_hat^T).
 //
-// Both kernels run on the MFMA unit (v_mfma_f32_16x16x32_f16): the weight tile is the B
-// operand (16 output rows n per tile, n = lane % 16), the activations are the A operand
-// (16 batch rows m per tile, m = lane % 16), and lane (h = lane / 16, r) of the result holds
-// y[m = 4h + r][n].
+// Three kernels:
+//   k_gemv_valu  batch 1-2: each wave streams whole rows (1 KB of one row per load instruction)
+//                and forms the group sums with v_dot2_f32_f16 on exact codes;
+//   k_gemv_mf    batch 3-8 (and 1-2 with rows longer than 16384 codes): v_mfma_f32_16x16x32_f16,
+//                the packed rows staged through LDS so that the global loads stay row-contiguous;
+//   k_gemm       batch > 8 without a workspace: an MFMA GEMM on fp16 W_hat tiles.
 //
-// Weight streaming: lane (h, n) loads 16 bytes (32 codes) of row n per 128-code chunk, so a
-// wave reads 16 rows x 64 contiguous bytes per load instruction.  One v_permlane32_swap per
-// dword pair regroups the chunk so that the four lane groups hold the four 16-code quarters of
-// one 64-code group (lane group h holds quarter pi(h), pi = [0, 2, 1, 3]): every MFMA then sums
-// codes of a single group, which lets the group's delta and zero be applied once per group.
+// MFMA operand layout: the weight tile is the B operand (16 output rows n per tile,
+// n = lane % 16), the activations are the A operand (16 batch rows m, m = lane % 16), and lane
+// (h = lane / 16, r) of the result holds y[m = 4h + r][n].  A load instruction whose lanes span
+// 16 rows reads the weight stream at half the rate of one that reads 1 KB of one row (the rows
+// are pages apart), hence the LDS staging.  One v_permlane32_swap per dword pair regroups a
+// 128-code chunk so that the four lane groups hold the four 16-code quarters of one 64-code
+// group (lane group h holds quarter pi(h), pi = [0, 2, 1, 3]): every MFMA then sums codes of a
+// single group, which lets the group's delta and zero be applied once per group.
 //
-// Code unpack ("magic" fp16): for a dword of eight 4-bit codes c0..c7,
-//   (d & 0x000F000F) | 0x64006400 = fp16 (1024 + c0, 1024 + c4),
-//   (d & 0x00F000F0) | 0x64006400 = fp16 (1024 + 16 c1, 1024 + 16 c5), and the same on d >> 8;
-// one packed fp16 add of -1024 leaves exact small integers.  The operand order within the
-// lane's eight k slots is therefore [0, 4, 1, 5, 2, 6, 3, 7] with a factor 16 on the odd codes;
-// the activations are staged in the same order (and, in the GEMV, with 1/16 on the odd codes).
-//
-// GEMV (batch <= 8): q stays exact; the MFMA forms P = sum_k x_k q_k per group and the group's
-// metadata is applied on the fp32 partial: acc += delta * (P - z * sum_k x_k).
-// GEMM (batch > 8): the tile is dequantised to fp16 W_hat = (q - z) * delta first (the plain
+// Code unpack (fp16 subnormals): for a dword of eight 4-bit codes c0..c7, (d & 0x000F000F) is
+// the fp16 pair (c0, c4) * 2^-24 and (d & 0x00F000F0) the pair (16 c1, 16 c5) * 2^-24, the same
+// on d >> 8; the dot-product units and the MFMA keep subnormal inputs.  The operand order within
+// a lane's eight k slots is therefore [0, 4, 1, 5, 2, 6, 3, 7] with a factor 16 on the odd
+// codes; the activations are staged in the same order with 1/16 on the odd codes.  q stays
+// exact; the group's metadata is applied on the fp32 partial: acc += delta * (P - z * sum_k x_k),
+// with the 2^24 folded into the step and the zero.
+// The batch > 8 GEMM dequantises its tile to fp16 W_hat = (q - z) * delta first (the plain
 // "dequantise then matmul" of the page, with fp32 accumulation).
+
+#include <type_traits>
 
 #include "hqq_gemv_common.h"
 
@@ -30,218 +35,258 @@ namespace hqq {
 namespace {
 
 // ------------------------------------------------------------------------------------------
-// GEMV, batch B <= 8.  Block = 8 waves on SPB 16-row strips; wave w takes the 128-code chunks
-// c = w, w + 8, ... of each K segment, for every strip of the block.  Per segment the
-// activations are staged in LDS in the operand order (x, with 1/16 on odd codes) together with
-// the per-group sums of x (staged once for all SPB strips), and so are the packed codes: wave w
-// loads whole row segments (rows w, w + 8, ...: one 1 KB run, one page, per load instruction;
-// the MFMA operand layout would put 16 rows, 16 pages, into every instruction) and each lane
-// then reads its 16-byte operand pieces from LDS.  The next segment's loads are in flight
-// while the current one is multiplied.  The eight waves' partial results are added in a fixed
-// order at the end.
+// GEMV, batch 3..8, on the MFMA unit with the whole pipeline in one block per compute unit.
+// Block = 16 waves on RB = 16 SPB weight rows; K is walked in segments of 2048 codes and wave w
+// always takes the 128-code chunk w of a segment, for every strip of the block (the A
+// fragments it reads from LDS serve all strips).  Per segment the block stages, double
+// buffered in LDS: x in the MFMA operand order (1/16 on the odd codes) with the per-group sums
+// of x, the packed rows (each load instruction reads 1 KB of one row: one page; the operand
+// layout would put 16 rows, 16 pages, into each), and the rows' steps and zeros.  The loads
+// run two segments ahead in registers; one LDS-only barrier per segment.  At the end the 16
+// waves' partial sums of each output are added in wave order (deterministic).
 // ------------------------------------------------------------------------------------------
-template <int B>
-struct GemvCfg {
-  static constexpr int CPW = (B <= 2) ? 8 : (B <= 4 ? 4 : 2);  // chunks per wave per segment
-  static constexpr int KS = 128 * 8 * CPW;                       // K per segment
-};
+constexpr int kMfWaves = 16;            // waves per block: one per 128-code chunk of a segment
+constexpr int kMfKS = 128 * kMfWaves;   // codes per segment
+constexpr int kMfKSP = kMfKS + 8;       // LDS row stride of x (halves): rows in different banks
+constexpr int kMfWRB = kMfKS / 2 + 16;  // LDS row stride of the packed codes (bytes)
 
-template <int B, int GS, int OUT, int SPB>
-__global__ void __launch_bounds__(512) k_gemv(const uint8_t* __restrict__ packed, const __half* __restrict__ delta,
-                                              const __half* __restrict__ zero, int64_t N, int64_t K,
-                                              const __half* __restrict__ x, void* __restrict__ y) {
-  constexpr int CPW = GemvCfg<B>::CPW, KS = GemvCfg<B>::KS;
-  constexpr int GPS = KS / GS;  // groups per segment
-  constexpr int KSP = KS + 8;   // LDS row stride of x: padded so that rows fall in different banks
-  constexpr int WRB = KS / 2 + 16;  // LDS row stride of the packed codes (bytes; 16 rows, distinct banks)
-  constexpr int RPW = SPB * 2;      // weight rows each wave loads per segment
-  constexpr int PPL = KS / 32 / 64; // 16-byte pieces of a row segment per lane
-  extern __shared__ float lds[];
-  float* sx = lds;                                                     // [B][GPS]
-  float* red = sx + B * GPS;                                           // [SPB][8][B][16]
-  _Float16* xs = reinterpret_cast<_Float16*>(red + SPB * 8 * B * 16);  // [B][KSP]
-  uint8_t* wl = reinterpret_cast<uint8_t*>(xs + B * KSP);              // [16 SPB][WRB] packed codes
+// LDS bytes of one stage (x, sums of x, codes, metadata) and of the kernel (two stages).
+__host__ __device__ constexpr int mf_stage_bytes(int B, int GS, int SPB) {
+  return B * kMfKSP * 2 + (kMfKS / GS) * ((B + 3) & ~3) * 4 + 16 * SPB * kMfWRB + 16 * SPB * (2 * (kMfKS / GS) + 4) * 4;
+}
+
+template <int B, int GS, int SPB, int NSEG>
+__global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __restrict__ packed,
+                                                          const __half* __restrict__ delta,
+                                                          const __half* __restrict__ zero, int64_t N, int64_t K,
+                                                          const __half* __restrict__ x, void* __restrict__ y,
+                                                          int out_dtype) {
+  static_assert(B >= 1 && B <= 8 && (GS == 64 || GS == 128) && (SPB == 1 || SPB == 2), "shape");
+  constexpr int NT = 64 * kMfWaves, RB = 16 * SPB;
+  constexpr int GPS = kMfKS / GS;          // groups per segment and row
+  constexpr int XB = B * (kMfKS / 8);      // 16-byte blocks of x per segment
+  constexpr int XR = (XB + NT - 1) / NT;   // of them per thread
+  constexpr int MW = GS == 64 ? 2 : 1;     // groups per metadata load (4 or 2 bytes)
+  constexpr int ML = RB * GPS / MW;        // metadata loads per array and segment
+  constexpr int BP = (B + 3) & ~3;         // batch rows of the x sums, padded with zeros to a multiple of 4
+  constexpr int MLR = 2 * GPS + 4;         // LDS row stride of the metadata (floats): 16-byte reads of 8
+                                           // consecutive rows fall in distinct banks
+  static_assert(ML <= NT, "one step and one zero load per thread");
+  constexpr int STAGE = mf_stage_bytes(B, GS, SPB);
+  extern __shared__ __align__(16) uint8_t lds_raw[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 4, nl = lane & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * 16 * SPB;
-  const int64_t gpr = K / GS;  // groups per row
-  const int qh = quarter_of(h);
-  // A-operand row of this lane: batch rows >= B read row 0; they only feed output rows >= B,
-  // which are never stored.
-  const int arow = nl < B ? nl : 0;
-
-  f32x4 acc[SPB];
-#pragma unroll
-  for (int sp = 0; sp < SPB; ++sp) acc[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int h = lane >> 4, nl = lane & 15, qh = quarter_of(h);
+  const int arow = nl < B ? nl : 0;  // A rows >= B only feed outputs that are never stored
+  const int64_t n0 = (int64_t)blockIdx.x * RB;
+  const int64_t gpr = K / GS;
   const int64_t nchunks = K / 128;
-  constexpr int XR = (B * (KS / 8) + 511) / 512;  // 8-element blocks of x staged per thread
-  // Loads of one segment: this thread's blocks of x (small, cache-resident) first, so that
-  // staging them does not wait for the weight stream, then the wave's weight chunks.  All loads
-  // are unconditional (clamped indexes): a load under a branch makes the compiler wait for it
-  // before the branch joins; blocks and chunks past the end are never staged or never used.
-  uint4 xr[XR];
-  uint4 wr[RPW][PPL];  // this wave's row segments of packed codes (PPL 16-byte pieces per lane and row)
-  unsigned dm[SPB][CPW], zm[SPB][CPW], dmn[SPB][CPW], zmn[SPB][CPW];
-  auto load_segment = [&](int64_t kb0, unsigned (&d)[SPB][CPW], unsigned (&z)[SPB][CPW]) {
-    const int nbs = (int)(((K - kb0 < KS) ? (K - kb0) : KS) / 8);
+  // segments: a compile-time count (1..8) makes the pipeline straight-line code, so the memory
+  // counter waits name exactly the loads about to be staged; 0 = a run-time loop (longer rows)
+  const int nseg = NSEG > 0 ? NSEG : (int)((K + kMfKS - 1) / kMfKS);
+
+  // stage layout
+  auto xs_of = [&](int buf) { return reinterpret_cast<_Float16*>(lds_raw + buf * STAGE); };
+  // per group of the segment the sums of x over its codes, [GPS][BP]; per row and group the
+  // step times 2^24 and minus the zero times 2^-24 (fp32, converted once at staging), [RB][MLR]
+  auto sx_of = [&](int buf) { return reinterpret_cast<float*>(lds_raw + buf * STAGE + B * kMfKSP * 2); };
+  auto wl_of = [&](int buf) { return lds_raw + buf * STAGE + B * kMfKSP * 2 + GPS * BP * 4; };
+  auto ml_of = [&](int buf) {
+    return reinterpret_cast<float*>(lds_raw + buf * STAGE + B * kMfKSP * 2 + GPS * BP * 4 + RB * kMfWRB);
+  };
+
+  // ---- loads of one segment into a register set (unconditional, clamped indexes: a load under
+  //      a branch makes the compiler wait for it at the join)
+  struct Regs {
+    uint4 xr[XR];
+    uint4 wr[SPB];
+    unsigned md, mz;  // steps and zeros of one to two groups (fp16)
+  };
+  auto load_seg = [&](int sg, Regs& r) {
+    const int64_t kb0 = (int64_t)sg * kMfKS;
+    const int valid = (int)((K - kb0 < kMfKS) ? (K - kb0) : kMfKS);  // codes of the segment (a multiple of 128)
 #pragma unroll
     for (int j = 0; j < XR; ++j) {
-      const int idx = tid + 512 * j;
-      const int m = min(idx / (KS / 8), B - 1), kb = min(idx % (KS / 8), nbs - 1);
-      xr[j] = *reinterpret_cast<const uint4*>(x + m * K + kb0 + 8 * kb);
+      const int idx = min(tid + NT * j, XB - 1);
+      const int m = idx / (kMfKS / 8), kb = min(idx % (kMfKS / 8), valid / 8 - 1);
+      r.xr[j] = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + kb0 + 8 * kb);
     }
 #pragma unroll
-    for (int sp = 0; sp < SPB; ++sp) {
-      const int64_t n = n0 + 16 * sp + nl;
-#pragma unroll
-      for (int i = 0; i < CPW; ++i) {
-        const int64_t c = min(kb0 / 128 + wave + 8 * i, nchunks - 1);
-        if constexpr (GS == 64) {
-          d[sp][i] = *reinterpret_cast<const unsigned*>(delta + n * gpr + 2 * c);
-          z[sp][i] = *reinterpret_cast<const unsigned*>(zero + n * gpr + 2 * c);
-        } else {
-          d[sp][i] = __half_as_ushort(delta[n * gpr + c]);
-          z[sp][i] = __half_as_ushort(zero[n * gpr + c]);
-        }
-      }
+    for (int j = 0; j < SPB; ++j) {
+      const int row = wave + kMfWaves * j;
+      const int piece = min(lane, valid / 32 - 1);  // 16-byte pieces of the row's segment
+      r.wr[j] = ld_stream16(packed + (n0 + row) * (K / 2) + kb0 / 2 + 16 * piece);
     }
     {
-      const int pieces = (int)(((K - kb0 < KS) ? (K - kb0) : KS) / 32);  // 16-byte pieces of the segment's rows
-#pragma unroll
-      for (int j = 0; j < RPW; ++j)
-#pragma unroll
-        for (int q = 0; q < PPL; ++q)
-          wr[j][q] = ld_stream16(packed + (n0 + wave + 8 * j) * (K / 2) + kb0 / 2 + 16 * min(lane + 64 * q, pieces - 1));
+      const int i = min(tid, ML - 1);
+      const int row = i / (GPS / MW), pc = min(i % (GPS / MW), valid / (GS * MW) - 1);  // valid % 128 == 0
+      const int64_t gi = (n0 + row) * gpr + kb0 / GS + (int64_t)MW * pc;
+      r.md = MW == 2 ? *reinterpret_cast<const unsigned*>(delta + gi) : (unsigned)__half_as_ushort(delta[gi]);
+      r.mz = MW == 2 ? *reinterpret_cast<const unsigned*>(zero + gi) : (unsigned)__half_as_ushort(zero[gi]);
     }
   };
-  load_segment(0, dm, zm);
-  for (int64_t kbase = 0; kbase < K; kbase += KS) {
-    const int64_t cbase = kbase / 128;
-    // 1. stage x in operand order (1/16 on the odd codes) with the per-group sums of x
+  // ---- a register set -> LDS stage `buf`
+  auto stage_seg = [&](int sg, int buf, const Regs& r) {
+    const int64_t kb0 = (int64_t)sg * kMfKS;
+    const int valid = (int)((K - kb0 < kMfKS) ? (K - kb0) : kMfKS);
+    _Float16* xs = xs_of(buf);
+    float* sx = sx_of(buf);
 #pragma unroll
     for (int j = 0; j < XR; ++j) {
-      const int idx = tid + 512 * j;
-      if (idx < B * (KS / 8)) {  // uniform per 256-lane run: segments of GS/8 lanes stay whole
-        const int m = idx / (KS / 8), kb = idx % (KS / 8);
-        const uint4 raw = xr[j];
+      const int idx = tid + NT * j;
+      if (idx < XB) {  // uniform per 64-lane run: a group's GS/8 blocks stay in one run
+        const int m = idx / (kMfKS / 8), kb = idx % (kMfKS / 8);
+        const uint4 raw = r.xr[j];
         const unsigned r4[4] = {raw.x, raw.y, raw.z, raw.w};
         float part = block_sum8(r4);
         uint4 o = perm_slots(raw);
         o.y = as_u(as_h2(o.y) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
         o.w = as_u(as_h2(o.w) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
-        *reinterpret_cast<uint4*>(xs + m * KSP + 8 * kb) = o;
+        *reinterpret_cast<uint4*>(xs + m * kMfKSP + 8 * kb) = o;
         part = seg_sum_f<GS / 8>(part);
-        if ((kb % (GS / 8)) == 0) sx[m * GPS + kb / (GS / 8)] = part;
+        if ((kb % (GS / 8)) == 0 && 8 * kb < valid) sx[(kb / (GS / 8)) * BP + m] = part;
       }
     }
+    uint8_t* wl = wl_of(buf);
 #pragma unroll
-    for (int j = 0; j < RPW; ++j)
-#pragma unroll
-      for (int q = 0; q < PPL; ++q) *reinterpret_cast<uint4*>(wl + (wave + 8 * j) * WRB + 16 * (lane + 64 * q)) = wr[j][q];
-    // this segment's steps and zeros, requested with its codes (no earlier wait than the codes')
-    if (kbase > 0) {
-#pragma unroll
-      for (int sp = 0; sp < SPB; ++sp)
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-          dm[sp][i] = dmn[sp][i];
-          zm[sp][i] = zmn[sp][i];
-        }
-    }
-    lds_barrier();  // LDS hand-over
-    // 2. the next segment's loads go out before this one is multiplied
-    const bool more = kbase + KS < K;
-    if (more) load_segment(kbase + KS, dmn, zmn);
-    uint4 v[SPB][CPW];
-#pragma unroll
-    for (int sp = 0; sp < SPB; ++sp)
-#pragma unroll
-      for (int i = 0; i < CPW; ++i) {
-        const int cl = min(wave + 8 * i, KS / 128 - 1);  // chunk within the segment (unused when past the end)
-        v[sp][i] = *reinterpret_cast<const uint4*>(wl + (16 * sp + nl) * WRB + cl * 64 + h * 16);
+    for (int j = 0; j < SPB; ++j)
+      *reinterpret_cast<uint4*>(wl + (wave + kMfWaves * j) * kMfWRB + 16 * lane) = r.wr[j];
+    if (tid < ML) {
+      // P = 2^-24 sum x q (subnormal codes): the step is scaled up and the zero down by 2^24 (exact)
+      const int row = tid / (GPS / MW), pc = tid % (GPS / MW);
+      float* ml = ml_of(buf) + row * MLR + 2 * MW * pc;
+      const float d0 = __half2float(__ushort_as_half((unsigned short)r.md)) * kSubScale;
+      const float z0 = __half2float(__ushort_as_half((unsigned short)r.mz)) * -kSubScaleInv;
+      if (MW == 2) {
+        const float d1 = __half2float(__ushort_as_half((unsigned short)(r.md >> 16))) * kSubScale;
+        const float z1 = __half2float(__ushort_as_half((unsigned short)(r.mz >> 16))) * -kSubScaleInv;
+        *reinterpret_cast<f32x4*>(ml) = f32x4{d0, z0, d1, z1};
+      } else {
+        *reinterpret_cast<float2*>(ml) = make_float2(d0, z0);
       }
+    }
+  };
 
+  f32x4 acc[SPB];
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int64_t c = cbase + wave + 8 * i;
-      if (c >= nchunks) break;
-      const int cl = (int)(c - cbase);  // chunk within the segment
+  for (int sp = 0; sp < SPB; ++sp) acc[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Two register sets, each always holding a segment in flight: iteration `cur` first stages
+  // segment cur + 1 (requested two iterations earlier) into the stage the block finished
+  // reading an iteration ago, refills that register set with segment cur + 3, then multiplies
+  // segment cur; one LDS-only barrier per iteration.
+  if constexpr (BP > B) {  // padded batch rows of the x sums stay zero (staging never writes them)
+    for (int i = tid; i < 2 * GPS * (BP - B); i += NT) {
+      const int b = i / (GPS * (BP - B)), rem = i % (GPS * (BP - B));
+      sx_of(b)[(rem / (BP - B)) * BP + B + rem % (BP - B)] = 0.f;
+    }
+  }
+  Regs rs[2];
+  load_seg(0, rs[0]);
+  if (NSEG != 1) load_seg(min(1, nseg - 1), rs[1]);
+  stage_seg(0, 0, rs[0]);
+  if (NSEG == 0 || NSEG > 2) load_seg(min(2, nseg - 1), rs[0]);
+  lds_barrier();
+  // one segment: stage `cur` + 1 (requested two segments earlier) into the other stage, refill
+  // that register set with `cur` + 3, multiply `cur`; one LDS-only barrier
+  auto segment = [&](const int cur, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;  // segment cur lives in stage cur % 2
+    if (cur + 1 < nseg) stage_seg(cur + 1, buf ^ 1, rs[buf ^ 1]);  // waits only for those loads
+    if (NSEG == 0 || cur + 3 < NSEG) load_seg(min(cur + 3, nseg - 1), rs[buf ^ 1]);
+    const int64_t c = (int64_t)cur * kMfWaves + wave;  // this wave's chunk
+    if (c < nchunks) {
+      const _Float16* xs = xs_of(buf);
+      const float* sx = sx_of(buf);
+      const uint8_t* wl = wl_of(buf);
+      const float* ml = ml_of(buf);
       if constexpr (GS == 64) {
-        const int kl = cl * 128 + qh * 16;
-        const f16x8 a00 = *reinterpret_cast<const f16x8*>(xs + arow * KSP + kl);
-        const f16x8 a01 = *reinterpret_cast<const f16x8*>(xs + arow * KSP + kl + 8);
-        const f16x8 a10 = *reinterpret_cast<const f16x8*>(xs + arow * KSP + kl + 64);
-        const f16x8 a11 = *reinterpret_cast<const f16x8*>(xs + arow * KSP + kl + 72);
-        float sx0[4], sx1[4];
-#pragma unroll
-        for (int r = 0; r < (B < 4 ? B : 4); ++r) {
-          const int m = 4 * h + r;
-          sx0[r] = (m < B) ? sx[m * GPS + cl * 2] : 0.f;
-          sx1[r] = (m < B) ? sx[m * GPS + cl * 2 + 1] : 0.f;
-        }
+        const int kl = wave * 128 + qh * 16;
+        const f16x8 a00 = *reinterpret_cast<const f16x8*>(xs + arow * kMfKSP + kl);
+        const f16x8 a01 = *reinterpret_cast<const f16x8*>(xs + arow * kMfKSP + kl + 8);
+        const f16x8 a10 = *reinterpret_cast<const f16x8*>(xs + arow * kMfKSP + kl + 64);
+        const f16x8 a11 = *reinterpret_cast<const f16x8*>(xs + arow * kMfKSP + kl + 72);
+        // sums of x of this lane's four batch rows 4h .. 4h + 3 (zeros past the batch)
+        const int hq = 4 * h < BP ? 4 * h : 0;
+        f32x4 sx0 = *reinterpret_cast<const f32x4*>(sx + (2 * wave) * BP + hq);
+        f32x4 sx1 = *reinterpret_cast<const f32x4*>(sx + (2 * wave + 1) * BP + hq);
+        if (4 * h >= BP) sx0 = sx1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sp = 0; sp < SPB; ++sp) {
+          const int row = 16 * sp + nl;
+          const uint4 v = *reinterpret_cast<const uint4*>(wl + row * kMfWRB + wave * 64 + h * 16);
           // regroup: lane group h then holds quarter pi(h) of both 64-code groups of the chunk
-          const auto s0 = __builtin_amdgcn_permlane32_swap(v[sp][i].x, v[sp][i].z, false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(v[sp][i].y, v[sp][i].w, false, false);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
           const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-          // the two groups' products interleaved (no back-to-back dependent MFMA)
           f32x4 P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a00, unpack8_sub(s0[0]), zero4, 0, 0, 0);
           f32x4 P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a10, unpack8_sub(s0[1]), zero4, 0, 0, 0);
           P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a01, unpack8_sub(s1[0]), P0, 0, 0, 0);
           P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a11, unpack8_sub(s1[1]), P1, 0, 0, 0);
-          // P = 2^-24 sum x q: scale the step up and the zero down by 2^24 (exact)
-          const float dl0 = __half2float(__ushort_as_half((unsigned short)dm[sp][i])) * kSubScale;
-          const float dl1 = __half2float(__ushort_as_half((unsigned short)(dm[sp][i] >> 16))) * kSubScale;
-          const float zz0 = __half2float(__ushort_as_half((unsigned short)zm[sp][i])) * kSubScaleInv;
-          const float zz1 = __half2float(__ushort_as_half((unsigned short)(zm[sp][i] >> 16))) * kSubScaleInv;
+          const f32x4 md = *reinterpret_cast<const f32x4*>(ml + row * MLR + 4 * wave);  // d0, -z0, d1, -z1
 #pragma unroll
           for (int r = 0; r < (B < 4 ? B : 4); ++r) {
-            acc[sp][r] = fmaf(dl0, fmaf(-zz0, sx0[r], P0[r]), acc[sp][r]);
-            acc[sp][r] = fmaf(dl1, fmaf(-zz1, sx1[r], P1[r]), acc[sp][r]);
+            acc[sp][r] = fmaf(md[0], fmaf(md[1], sx0[r], P0[r]), acc[sp][r]);
+            acc[sp][r] = fmaf(md[2], fmaf(md[3], sx1[r], P1[r]), acc[sp][r]);
           }
         }
-      } else {  // GS == 128: the 128-code chunk is one group; lane group h holds codes 32h..32h+31
+      } else {  // GS == 128: the chunk is one group; lane group h holds codes 32 h .. 32 h + 31
         f16x8 A[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) A[t] = *reinterpret_cast<const f16x8*>(xs + arow * KSP + cl * 128 + h * 32 + t * 8);
-        float sxv[4];
-#pragma unroll
-        for (int r = 0; r < (B < 4 ? B : 4); ++r) {
-          const int m = 4 * h + r;
-          sxv[r] = (m < B) ? sx[m * GPS + cl] : 0.f;
-        }
+        for (int t = 0; t < 4; ++t)
+          A[t] = *reinterpret_cast<const f16x8*>(xs + arow * kMfKSP + wave * 128 + h * 32 + t * 8);
+        const int hq = 4 * h < BP ? 4 * h : 0;
+        f32x4 sxv = *reinterpret_cast<const f32x4*>(sx + wave * BP + hq);
+        if (4 * h >= BP) sxv = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sp = 0; sp < SPB; ++sp) {
-          const unsigned dd[4] = {v[sp][i].x, v[sp][i].y, v[sp][i].z, v[sp][i].w};
+          const int row = 16 * sp + nl;
+          const uint4 v = *reinterpret_cast<const uint4*>(wl + row * kMfWRB + wave * 64 + h * 16);
+          const unsigned dd[4] = {v.x, v.y, v.z, v.w};
           f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int t = 0; t < 4; ++t) P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t], unpack8_sub(dd[t]), P, 0, 0, 0);
-          const float dl = __half2float(__ushort_as_half((unsigned short)dm[sp][i])) * kSubScale;
-          const float zz = __half2float(__ushort_as_half((unsigned short)zm[sp][i])) * kSubScaleInv;
+          const float2 md = *reinterpret_cast<const float2*>(ml + row * MLR + 2 * wave);  // d, -z
 #pragma unroll
-          for (int r = 0; r < (B < 4 ? B : 4); ++r) acc[sp][r] = fmaf(dl, fmaf(-zz, sxv[r], P[r]), acc[sp][r]);
+          for (int r = 0; r < (B < 4 ? B : 4); ++r) acc[sp][r] = fmaf(md.x, fmaf(md.y, sxv[r], P[r]), acc[sp][r]);
         }
       }
     }
-    lds_barrier();  // LDS hand-over; the next segment's loads stay in flight
+    lds_barrier();
+  };
+  if constexpr (NSEG > 0) {
+#pragma unroll
+    for (int cur = 0; cur < NSEG; ++cur) {
+      if (cur % 2 == 0)
+        segment(cur, std::integral_constant<int, 0>{});
+      else
+        segment(cur, std::integral_constant<int, 1>{});
+    }
+  } else {
+    for (int cur = 0; cur < nseg; cur += 2) {
+      segment(cur, std::integral_constant<int, 0>{});
+      if (cur + 1 < nseg) segment(cur + 1, std::integral_constant<int, 1>{});
+    }
   }
+  // ---- the 16 waves' partial sums of each output, added in wave order (stage memory reused)
+  float* red = reinterpret_cast<float*>(lds_raw);  // [SPB][16 waves][B][16]
 #pragma unroll
   for (int sp = 0; sp < SPB; ++sp)
 #pragma unroll
     for (int r = 0; r < (B < 4 ? B : 4); ++r) {
       const int m = 4 * h + r;
-      if (m < B) red[((sp * 8 + wave) * B + m) * 16 + nl] = acc[sp][r];
+      if (m < B) red[((sp * kMfWaves + wave) * B + m) * 16 + nl] = acc[sp][r];
     }
-  __syncthreads();
+  lds_barrier();
   if (tid < SPB * B * 16) {
     const int sp = tid / (B * 16), m = (tid / 16) % B, col = tid % 16;
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) sum += red[((sp * 8 + w) * B + m) * 16 + col];
-    store_y<OUT>(y, (int64_t)m * N + n0 + 16 * sp + col, sum);
+    for (int w = 0; w < kMfWaves; ++w) sum += red[((sp * kMfWaves + w) * B + m) * 16 + col];
+    if (out_dtype == HQQ_OUT_F16)
+      store_y<HQQ_OUT_F16>(y, (int64_t)m * N + n0 + 16 * sp + col, sum);
+    else
+      store_y<HQQ_OUT_F32>(y, (int64_t)m * N + n0 + 16 * sp + col, sum);
   }
 }
 
@@ -604,44 +649,44 @@ hipError_t gemv_valu(const uint8_t* packed, const __half* delta, const __half* z
   }
 }
 
-template <int B>
-size_t gemv_lds_b(int gs, int spb) {
-  constexpr int KS = GemvCfg<B>::KS;
-  return (size_t)B * (KS / gs) * 4 + (size_t)spb * 8 * B * 16 * 4 + (size_t)B * (KS + 8) * 2 +
-         (size_t)16 * spb * (KS / 2 + 16);
+// Batch 1-2 with rows of at most 16384 codes run on the vector ALUs.
+inline bool gemv_uses_valu(int64_t K, int64_t batch) { return batch <= 2 && K <= 64 * 32 * 8; }
+
+// Strips per block of the batched MFMA GEMV: two when that still leaves >= 256 blocks.
+inline int mf_strips_per_block(int64_t N) { return (N % 32 == 0 && N / 32 >= 256) ? 2 : 1; }
+
+template <int B, int GS, int SPB, int NSEG>
+void gemv_mf_launch(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                    const __half* x, void* y, int y_dtype, hipStream_t st) {
+  hipLaunchKernelGGL((k_gemv_mf<B, GS, SPB, NSEG>), dim3((unsigned)(N / (16 * SPB))), dim3(64 * kMfWaves),
+                     2 * mf_stage_bytes(B, GS, SPB), st, packed, delta, zero, N, K, x, y, y_dtype);
 }
 
-// Strips per block of the batched GEMV: two when that still leaves >= 256 blocks.
-inline int gemv_strips_per_block(int64_t N, int64_t batch) {
-  return (batch >= 3 && N % 32 == 0 && N / 32 >= 256) ? 2 : 1;  // batch <= 2 holds 8 chunks per strip
+template <int B, int GS, int SPB>
+void gemv_mf_seg(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                 const __half* x, void* y, int y_dtype, hipStream_t st) {
+  // batch 1-2 come here only for rows longer than the streaming kernel takes: the run-time loop
+  if constexpr (B >= 3) {
+    switch ((K + kMfKS - 1) / kMfKS) {
+      case 1: return gemv_mf_launch<B, GS, SPB, 1>(packed, delta, zero, N, K, x, y, y_dtype, st);
+      case 2: return gemv_mf_launch<B, GS, SPB, 2>(packed, delta, zero, N, K, x, y, y_dtype, st);
+      case 3: return gemv_mf_launch<B, GS, SPB, 3>(packed, delta, zero, N, K, x, y, y_dtype, st);
+      case 4: return gemv_mf_launch<B, GS, SPB, 4>(packed, delta, zero, N, K, x, y, y_dtype, st);
+      default: break;
+    }
+  }
+  gemv_mf_launch<B, GS, SPB, 0>(packed, delta, zero, N, K, x, y, y_dtype, st);
 }
 
 template <int B, int GS>
-hipError_t gemv_b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
-                  const __half* x, void* y, int y_dtype, hipStream_t st) {
-  const int spb = gemv_strips_per_block(N, B);
-  const size_t lds = gemv_lds_b<B>(GS, spb);
-  const dim3 grid((unsigned)(N / (16 * spb)));
-  if constexpr (B >= 3) {
-    if (spb == 2) {
-      if (y_dtype == HQQ_OUT_F16)
-        hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F16, 2>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
-      else
-        hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F32, 2>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
-      return hipGetLastError();
-    }
-  }
-  {
-    if (y_dtype == HQQ_OUT_F16)
-      hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F16, 1>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
-    else
-      hipLaunchKernelGGL((k_gemv<B, GS, HQQ_OUT_F32, 1>), grid, dim3(512), lds, st, packed, delta, zero, N, K, x, y);
-  }
+hipError_t gemv_mf(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                   const __half* x, void* y, int y_dtype, hipStream_t st) {
+  if (mf_strips_per_block(N) == 2)
+    gemv_mf_seg<B, GS, 2>(packed, delta, zero, N, K, x, y, y_dtype, st);
+  else
+    gemv_mf_seg<B, GS, 1>(packed, delta, zero, N, K, x, y, y_dtype, st);
   return hipGetLastError();
 }
-
-// Batch 1-2 with rows of at most 16384 codes run on the vector ALUs.
-inline bool gemv_uses_valu(int64_t K, int64_t batch) { return batch <= 2 && K <= 64 * 32 * 8; }
 
 template <int GS>
 hipError_t gemv_gs(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
@@ -650,16 +695,16 @@ hipError_t gemv_gs(const uint8_t* packed, const __half* delta, const __half* zer
   switch (batch) {
     case 1:
       return valu ? gemv_valu<1>(packed, delta, zero, N, K, GS, x, y, y_dtype, st)
-                  : gemv_b<1, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
+                  : gemv_mf<1, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
     case 2:
       return valu ? gemv_valu<2>(packed, delta, zero, N, K, GS, x, y, y_dtype, st)
-                  : gemv_b<2, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
-    case 3: return gemv_b<3, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
-    case 4: return gemv_b<4, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
-    case 5: return gemv_b<5, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
-    case 6: return gemv_b<6, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
-    case 7: return gemv_b<7, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
-    case 8: return gemv_b<8, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
+                  : gemv_mf<2, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    case 3: return gemv_mf<3, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    case 4: return gemv_mf<4, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    case 5: return gemv_mf<5, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    case 6: return gemv_mf<6, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    case 7: return gemv_mf<7, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    case 8: return gemv_mf<8, GS>(packed, delta, zero, N, K, x, y, y_dtype, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -668,17 +713,8 @@ hipError_t gemv_gs(const uint8_t* packed, const __half* delta, const __half* zer
 
 size_t gemv_lds_bytes(int64_t K, int gs, int64_t batch) {
   if (gemv_uses_valu(K, batch)) return (size_t)valu_lds_bytes((int)batch, K);
-  switch (batch) {  // the larger of the one- and two-strip layouts
-    case 1: return gemv_lds_b<1>(gs, 2);
-    case 2: return gemv_lds_b<2>(gs, 2);
-    case 3: return gemv_lds_b<3>(gs, 2);
-    case 4: return gemv_lds_b<4>(gs, 2);
-    case 5: return gemv_lds_b<5>(gs, 2);
-    case 6: return gemv_lds_b<6>(gs, 2);
-    case 7: return gemv_lds_b<7>(gs, 2);
-    case 8: return gemv_lds_b<8>(gs, 2);
-    default: return 0;
-  }
+  if (batch < 1 || batch > 8) return 0;
+  return 2 * (size_t)mf_stage_bytes((int)batch, gs, 2);  // the two-strip layout is the larger
 }
 
 hipError_t launch_gemv(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int gs,
