@@ -144,7 +144,7 @@ int hqq_quantize(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int 
  * library routine.  Limit: tensors whose hqq_quantize_workspace_bytes(...) exceeds
  * HQQ_NOALLOC_SCRATCH_BYTES are refused with HQQ_ERR_WORKSPACE before anything is enqueued
  * (e.g. the per-round error sums of 20 rounds over a 28672x8192 tensor take 19 MB; 3-bit codes
- * take one more byte per weight).  Every call on a GPU shares that GPU's array: calls that
+ * with axis-0 groups take one more byte per weight).  Every call on a GPU shares that GPU's array: calls that
  * overlap on one GPU (other streams, other threads) race and must be serialised by the caller;
  * the array needs no clearing between calls (no part of it has to start at zero).
  */

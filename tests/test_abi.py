@@ -49,8 +49,9 @@ def test_num_groups(lib):
 
 def test_workspace_bytes(lib):
     assert hq.hqq_quantize_workspace_bytes(1024, 1024, 4, 64, 1, 20) > 0
-    # 3-bit keeps one byte per code in the workspace
-    assert hq.hqq_quantize_workspace_bytes(64, 640, 3, 64, 1, 20) >= 64 * 640
+    # 3-bit: axis 1 packs in the solve (two partial words per tile); axis 0 keeps one byte per code
+    assert hq.hqq_quantize_workspace_bytes(64, 640, 3, 64, 1, 20) < hq.hqq_quantize_workspace_bytes(64, 640, 4, 64, 1, 20) + 4096
+    assert hq.hqq_quantize_workspace_bytes(640, 64, 3, 64, 0, 20) >= 64 * 640
     assert hq.hqq_quantize_workspace_bytes(1024, 1024, 4, 48, 1, 20) == 0      # g does not divide
     assert hq.hqq_quantize_workspace_bytes(1024, 1024, 4, 64, 1, 65) == 0      # iters too large
     assert hq.hqq_quantize_workspace_bytes(1024, 1024, 5, 64, 1, 20) == 0      # nbits
@@ -238,7 +239,7 @@ def test_noalloc_rejects_before_any_device_call(lib):
     assert need > hq.HQQ_NOALLOC_SCRATCH_BYTES
     assert call(65536, 8192, 4, 64, 1, 20) == hq.HQQ_ERR_WORKSPACE
     assert "scratch" in hq.last_error()
-    assert call(8192, 8192, 3, 64, 1, 20) == hq.HQQ_ERR_WORKSPACE      # 3-bit: a byte per code
+    assert call(8192, 8192, 3, 64, 0, 20) == hq.HQQ_ERR_WORKSPACE      # 3-bit axis 0: a byte per code
     assert call(64, 64, 5, 64, 1, 20) == hq.HQQ_ERR_INVALID_ARGUMENT
     assert call(64, 64, 4, 64, 1, 65) == hq.HQQ_ERR_INVALID_ARGUMENT
     assert call(64, 96, 4, 64, 1, 20) == hq.HQQ_ERR_INVALID_ARGUMENT    # 64 does not divide 96

@@ -56,13 +56,17 @@ struct QuantLayout {
 
 bool quant_layout(int64_t rows, int64_t cols, int nbits, int g, int axis, int iters, QuantLayout* q) {
   q->G = rows * cols / g;
-  if (!hqq::quant_geometry(q->G, g, axis, iters, &q->nblocks, &q->threads, &q->lds)) return false;
+  if (!hqq::quant_geometry(q->G, g, axis, iters, nbits, &q->nblocks, &q->threads, &q->lds)) return false;
   auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
   q->off_partials = 256;
   q->off_reduce = up(q->off_partials + (size_t)iters * q->nblocks * sizeof(double));
   q->off_rounds = up(q->off_reduce + (size_t)iters * hqq::reduce_scratch_entries(q->nblocks, iters) * sizeof(double));
   q->off_codes = up(q->off_rounds + (size_t)q->nblocks * sizeof(int32_t));
-  q->total = q->off_codes + (nbits == 3 ? up((size_t)(rows * cols)) : 0);
+  // 3-bit codes: axis 1 packs them in the solve (two partial words per tile for the words shared
+  // with a neighbouring tile); axis 0 keeps one byte per code for the packing pass
+  q->total = q->off_codes + (nbits == 3 ? (axis == 1 ? up((size_t)q->nblocks * 2 * sizeof(uint32_t))
+                                                     : up((size_t)(rows * cols)))
+                                        : 0);
   return true;
 }
 
@@ -148,7 +152,8 @@ int quantize_impl(const hqq_quant_args& x) {
   a.ctrl = reinterpret_cast<int32_t*>(ws);
   a.partials = reinterpret_cast<double*>(ws + q.off_partials);
   a.tile_round = reinterpret_cast<int32_t*>(ws + q.off_rounds);
-  a.codes_ws = nbits == 3 ? ws + q.off_codes : nullptr;
+  a.codes_ws = (nbits == 3 && axis == 0) ? ws + q.off_codes : nullptr;
+  a.edges3 = (nbits == 3 && axis == 1) ? reinterpret_cast<uint32_t*>(ws + q.off_codes) : nullptr;
   a.G = q.G;
   a.nblocks = q.nblocks;
   a.iters = iters;

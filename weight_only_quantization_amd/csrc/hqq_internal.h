@@ -15,7 +15,9 @@ struct SolveArgs {
   uint8_t* packed;     // packed output (2/4-bit written directly)
   void* delta;         // [G] meta_dtype
   void* zero;          // [G] meta_dtype
-  uint8_t* codes_ws;   // 3-bit: one byte per code, packed afterwards; else nullptr
+  uint8_t* codes_ws;   // 3-bit axis 0 (and the scale search): one byte per code, packed afterwards; else nullptr
+  uint32_t* edges3;    // 3-bit axis 1: per solve tile its part of the word it starts inside and of the word it
+                       // ends inside ([nblocks][2]); a merge pass joins neighbours' parts
   double* partials;    // [iters][nblocks] per-block sums of |W - W_hat| per round
   int32_t* ctrl;       // [0] = index of the kept zero, [1] = rounds evaluated
   int32_t* tile_round; // [nblocks] latest round at which a wave of the tile froze (iters: one never did)
@@ -50,7 +52,7 @@ hipError_t launch_quantize_v2(const SolveArgs& a, const ScaleGrid& sg, int nbits
 // Per-round entries of the intermediate levels of the stop-decision reduction.
 int64_t reduce_scratch_entries(int64_t nblocks, int iters);
 // Geometry of the solve kernel for a configuration: blocks, threads, dynamic LDS bytes.
-bool quant_geometry(int64_t G, int group_size, int axis, int iters, int64_t* nblocks, int* threads,
+bool quant_geometry(int64_t G, int group_size, int axis, int iters, int nbits, int64_t* nblocks, int* threads,
                     size_t* lds_bytes);
 
 hipError_t launch_dequant(const uint8_t* packed, const void* delta, const void* zero, int meta_dtype,

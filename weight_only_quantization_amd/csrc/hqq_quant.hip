@@ -312,6 +312,42 @@ __device__ __forceinline__ void store_block_meta(const SolveArgs& a, const doubl
     store_meta(wave == 0 ? a.delta : a.zero, a.meta_dtype, g0 + lane, meta_lds[wave * ng + lane]);
 }
 
+// 3-bit codes of one axis-1 tile (flat codes [T0, T1), T1 = T0 + TC or the tensor's end) from
+// LDS, ten per 32-bit word at bits 3t: the words inside the tile are stored directly; the word
+// the tile starts inside (T0 not a multiple of 10) and the word it ends inside get only this
+// tile's codes, kept in a.edges3[2 tile] and [2 tile + 1] for k_merge3 (the tensor's last word,
+// padded with code 0, is whole).
+template <int TC>
+__device__ __forceinline__ void pack3_tile(const SolveArgs& a, const uint8_t* ct, int64_t tile, int64_t N) {
+  const int64_t T0 = tile * TC;
+  const int64_t T1 = T0 + TC < N ? T0 + TC : N;
+  const int n = (int)(T1 - T0);                            // >= 16: a tile holds at least one group
+  const int64_t jf = (T0 + 9) / 10;                        // first word that starts inside the tile
+  const int64_t je = T1 == N ? (T1 + 9) / 10 : T1 / 10;    // words [jf, je) lie inside (the last one padded)
+  uint32_t* out = reinterpret_cast<uint32_t*>(a.packed);
+  const int tid = late_tid();
+  for (int64_t j = jf + tid; j < je; j += blockDim.x) {
+    const int b = (int)(10 * j - T0);
+    uint32_t w = 0;
+#pragma unroll
+    for (int t = 0; t < 10; ++t)
+      if (b + t < n) w |= (uint32_t)ct[b + t] << (3 * t);
+    out[j] = w;
+  }
+  if (tid == 0) {
+    uint32_t head = 0, tail = 0;
+    const int hs = (int)(T0 % 10);  // slot of code T0 in its word
+    if (hs)
+      for (int t = hs; t < 10; ++t) head |= (uint32_t)ct[t - hs] << (3 * t);
+    if (T1 < N) {
+      const int ts = (int)(T1 % 10);  // codes of the tile in the word it ends inside
+      for (int t = 0; t < ts; ++t) tail |= (uint32_t)ct[n - ts + t] << (3 * t);
+    }
+    a.edges3[2 * tile] = head;
+    a.edges3[2 * tile + 1] = tail;
+  }
+}
+
 // Whether the solve records, per tile, the round by which all its waves froze, so that the
 // fix-up can skip tiles that an early stop does not change.  Only for 2-bit codes: their groups
 // converge within a few rounds and the loop stops early, which makes the fix-up redo every
@@ -395,22 +431,21 @@ __device__ __forceinline__ void ax1_tile(const SolveArgs& a, int64_t tile, int k
           reinterpret_cast<unsigned short*>(a.packed)[e0 / 8 + h] = (unsigned short)v;
         }
       }
-    } else {  // 3-bit: one byte per code, packed by k_pack3
-      if constexpr (E == 4) {
-        reinterpret_cast<unsigned*>(a.codes_ws + e0)[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-      } else {
-#pragma unroll
-        for (int h = 0; h < E / 4; ++h)
-          reinterpret_cast<unsigned*>(a.codes_ws + e0)[h] =
-              c[4 * h] | (c[4 * h + 1] << 8) | (c[4 * h + 2] << 16) | (c[4 * h + 3] << 24);
-      }
     }
     if (slot == 0) {
       meta_lds[gblock] = delta;
       meta_lds[GPB + gblock] = z;
     }
   }
-  store_block_meta(a, meta_lds, GPB, tile * GPB);
+  uint8_t* ct = reinterpret_cast<uint8_t*>(meta_lds + 2 * GPB);  // 3-bit: the tile's codes, one byte each
+  if constexpr (NBITS == 3) {
+    const int o = gblock * G + slot * E;  // codes of groups past the tensor's end are never read
+#pragma unroll
+    for (int e = 0; e < E; e += 4)
+      *reinterpret_cast<unsigned*>(ct + o + e) = c[e] | (c[e + 1] << 8) | (c[e + 2] << 16) | (c[e + 3] << 24);
+  }
+  store_block_meta(a, meta_lds, GPB, tile * GPB);  // its barrier also publishes the code tile
+  if constexpr (NBITS == 3) pack3_tile<GPB * G>(a, ct, tile, a.G * (int64_t)G);
   if (kRecordFreeze<NBITS> && !FIX && threadIdx.x == 0)
     a.tile_round[tile] = max(max(s_kfrozen[0], s_kfrozen[1]), max(s_kfrozen[2], s_kfrozen[3]));
   if (!FIX) write_partials<GPB>(a, err_lds, tile);
@@ -863,6 +898,15 @@ __global__ void __launch_bounds__(256) k_pack3(const uint8_t* codes, int64_t N, 
   out[j] = word;
 }
 
+// The words shared by neighbouring axis-1 tiles (3-bit): word T0 / 10 of tile t (T0 = t * TC not a
+// multiple of 10) = the end part of tile t - 1 | the start part of tile t.
+__global__ void __launch_bounds__(256) k_merge3(const uint32_t* edges, int64_t nblocks, int64_t TC, uint32_t* out) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x + 1;
+  if (t >= nblocks) return;
+  const int64_t T0 = t * TC;
+  if (T0 % 10) out[T0 / 10] = edges[2 * (t - 1) + 1] | edges[2 * t];
+}
+
 template <int NBITS, int G>
 hipError_t launch_cfg(const SolveArgs& a, int axis, int64_t nblocks, int threads, size_t lds, hipStream_t st,
                       bool fix) {
@@ -922,7 +966,7 @@ int lanes_per_group(int g) {
 
 }  // namespace
 
-bool quant_geometry(int64_t G, int g, int axis, int iters, int64_t* nblocks, int* threads, size_t* lds) {
+bool quant_geometry(int64_t G, int g, int axis, int iters, int nbits, int64_t* nblocks, int* threads, size_t* lds) {
   if (g != 16 && g != 32 && g != 64 && g != 128 && g != 256) return false;
   const int L = lanes_per_group(g);
   const int gpw = 64 / L;
@@ -930,7 +974,8 @@ bool quant_geometry(int64_t G, int g, int axis, int iters, int64_t* nblocks, int
     const int gpb = 4 * gpw;
     *nblocks = (G + gpb - 1) / gpb;
     *threads = 256;
-    *lds = (size_t)(iters + 2) * gpb * sizeof(double);
+    // per-round sums, steps and zeros; 3-bit: the tile's codes before packing
+    *lds = (size_t)(iters + 2) * gpb * sizeof(double) + (nbits == 3 ? (size_t)gpb * g : 0);
   } else {  // the block shape of ax0_tile: tw groups, tw / gpw waves
     const int tw = 4 * gpw;
     *nblocks = (G + tw - 1) / tw;
@@ -986,7 +1031,13 @@ hipError_t launch_quantize(const SolveArgs& a, int nbits, int g, int axis, int t
   // when the loop ran to the end
   err = solve(true, fix_grid(g, nblocks));
   if (err != hipSuccess) return err;
-  if (nbits == 3) {
+  if (nbits == 3 && axis == 1) {
+    const int64_t TC = (int64_t)g * (4 * (64 / lanes_per_group(g)));  // codes per tile: g x groups per block
+    if (a.nblocks > 1)
+      hipLaunchKernelGGL(k_merge3, dim3((unsigned)((a.nblocks - 1 + 255) / 256)), dim3(256), 0, st, a.edges3,
+                         a.nblocks, TC, reinterpret_cast<uint32_t*>(a.packed));
+    err = hipGetLastError();
+  } else if (nbits == 3) {
     const int64_t nwords = (N + 9) / 10;
     hipLaunchKernelGGL(k_pack3, dim3((nwords + 255) / 256), dim3(256), 0, st, a.codes_ws, N,
                        reinterpret_cast<uint32_t*>(a.packed), nwords);
