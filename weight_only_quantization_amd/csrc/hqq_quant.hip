@@ -320,31 +320,26 @@ __device__ __forceinline__ void store_block_meta(const SolveArgs& a, const doubl
 template <int TC>
 __device__ __forceinline__ void pack3_tile(const SolveArgs& a, const uint8_t* ct, int64_t tile, int64_t N) {
   const int64_t T0 = tile * TC;
-  const int64_t T1 = T0 + TC < N ? T0 + TC : N;
-  const int n = (int)(T1 - T0);                            // >= 16: a tile holds at least one group
-  const int64_t jf = (T0 + 9) / 10;                        // first word that starts inside the tile
-  const int64_t je = T1 == N ? (T1 + 9) / 10 : T1 / 10;    // words [jf, je) lie inside (the last one padded)
+  const int64_t T1 = T0 + TC < N ? T0 + TC : N;  // T1 - T0 >= 16: a tile holds at least one group
   uint32_t* out = reinterpret_cast<uint32_t*>(a.packed);
-  const int tid = late_tid();
-  for (int64_t j = jf + tid; j < je; j += blockDim.x) {
-    const int b = (int)(10 * j - T0);
+  // every word holding a code of the tile, one per thread: whole words (and the tensor's padded
+  // last word) to the output, the word the tile starts inside and the one it ends inside to edges3
+  for (int64_t j = T0 / 10 + late_tid(); j <= (T1 - 1) / 10; j += blockDim.x) {
+    const int64_t lo = 10 * j > T0 ? 10 * j : T0, hi = 10 * j + 10 < T1 ? 10 * j + 10 : T1;
     uint32_t w = 0;
 #pragma unroll
-    for (int t = 0; t < 10; ++t)
-      if (b + t < n) w |= (uint32_t)ct[b + t] << (3 * t);
-    out[j] = w;
-  }
-  if (tid == 0) {
-    uint32_t head = 0, tail = 0;
-    const int hs = (int)(T0 % 10);  // slot of code T0 in its word
-    if (hs)
-      for (int t = hs; t < 10; ++t) head |= (uint32_t)ct[t - hs] << (3 * t);
-    if (T1 < N) {
-      const int ts = (int)(T1 % 10);  // codes of the tile in the word it ends inside
-      for (int t = 0; t < ts; ++t) tail |= (uint32_t)ct[n - ts + t] << (3 * t);
+    for (int t = 0; t < 10; ++t) {
+      const int64_t i = 10 * j + t;
+      const bool in = i >= lo && i < hi;
+      const uint32_t c = ct[in ? i - T0 : 0];
+      w |= in ? c << (3 * t) : 0u;
     }
-    a.edges3[2 * tile] = head;
-    a.edges3[2 * tile + 1] = tail;
+    if (lo > 10 * j)
+      a.edges3[2 * tile] = w;
+    else if (hi < 10 * j + 10 && T1 < N)
+      a.edges3[2 * tile + 1] = w;
+    else
+      out[j] = w;
   }
 }
 
