@@ -12,8 +12,10 @@ Beside the step (in "legs", not in `value`): the input gradient dX = dY W_hat on
 weight at batch 256 (hqq_gemm_w4a16_dx), the same layer shapes on Laplace weights at 3-bit
 g64 and 2-bit g16, the 28672x8192 weight with axis-0 groups of 128, and the fused products over
 the 3-bit, 2-bit and axis-0 formats.
-Inputs are resident in HBM before the timed region; the GEMV operands rotate over enough
-copies (> 1 GB) that the 256 MB last-level cache cannot hold them.
+The seven layers are independent tensors: their quantize and dequantize calls are spread over four
+streams (joined before the products).  Inputs are resident in HBM before the timed region; the
+product and dequant operands rotate over enough copies (> 1 GB) that the 256 MB last-level cache
+cannot hold them.
 
 Prints one JSON line.  `value` is the step's throughput in quantized weights per second
 (all legs inside the step time); the per-leg rates and the roofline of the dominant kernel
@@ -44,6 +46,11 @@ PEAK_FP64_ALU = 256 * 4 * 16 * 2.4e9
 OPS_PER_ROUND = 6
 OPS_FIXED = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_traffic.json")
+# The layers are independent tensors: their hqq_quantize (and hqq_dequantize) calls go to this many
+# streams (default priority), so one layer's solve fills the GPU while another's stop decision and
+# fix-up (small, latency-bound launches) run.  Measured on the 7-layer set: 1 stream 199, 2 streams
+# 208, 3 streams 210, 4 streams 212 Gweights/s for the quantize phase.
+QSTREAMS = 4
 
 
 def log(*a):
@@ -299,6 +306,8 @@ def main():
                     help="skip the 3-/2-bit, axis-0 and other-format legs outside the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--qstreams", type=int, default=QSTREAMS,
+                    help="streams the layers' hqq_quantize calls are spread over (independent tensors)")
     ap.add_argument("--counter-pass", action="store_true",
                     help="each leg's kernels run a few times without timing loops (for rocprofv3 --pmc runs)")
     a = ap.parse_args()
@@ -359,16 +368,56 @@ def main():
         else:
             hq.hqq_gemm_w4a16(pk, d, z, GN, GK, gq.group_size, X[:b], out=Y[b], workspace=gemm_ws)
 
-    def step(i, ev=None):
+    # layers to streams: largest first, each to the stream with the least work so far
+    nqs = max(1, a.qstreams)
+    qstreams = [stream] if nqs == 1 else [torch.cuda.Stream(device=dev) for _ in range(nqs)]
+    load = [0] * nqs
+    qstream_of = [0] * len(layers)
+    for li in sorted(range(len(layers)), key=lambda k: -layers[k][0].rows * layers[k][0].cols):
+        sidx = min(range(nqs), key=lambda k: load[k])
+        qstream_of[li] = sidx
+        load[sidx] += layers[li][0].rows * layers[li][0].cols
+
+    def quantize_all(ev=None):
+        """The layers' hqq_quantize calls; ev = (start, end) events on the launch stream around them."""
+        if ev is not None:
+            ev[0].record(stream)
+        if nqs > 1:
+            fork = torch.cuda.Event()
+            fork.record(stream)
+            for qs in qstreams:
+                qs.wait_event(fork)
         for li, (t, W, ws, out, What) in enumerate(layers):
-            if ev is not None:
-                ev["q"][li][0].record(stream)
             hq.hqq_quantize(W, nbits=qp.nbits, group_size=qp.group_size, axis=qp.axis, iters=qp.iters, p=qp.p,
-                            beta0=qp.beta0, kappa=qp.kappa, workspace=ws, out=out)
-            if ev is not None:
-                ev["q"][li][1].record(stream)
+                            beta0=qp.beta0, kappa=qp.kappa, workspace=ws, out=out,
+                            stream=None if nqs == 1 else qstreams[qstream_of[li]])
+        if nqs > 1:
+            for qs in qstreams:
+                j = torch.cuda.Event()
+                j.record(qs)
+                stream.wait_event(j)
+        if ev is not None:
+            ev[1].record(stream)
+
+    def dequantize_all():
+        """The layers' hqq_dequantize calls, on the same streams as their quantize calls."""
+        if nqs > 1:
+            fork = torch.cuda.Event()
+            fork.record(stream)
+            for qs in qstreams:
+                qs.wait_event(fork)
         for li, (t, W, ws, out, What) in enumerate(layers):
-            hq.hqq_dequantize(out[0], out[1], out[2], t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=What)
+            hq.hqq_dequantize(out[0], out[1], out[2], t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=What,
+                              stream=None if nqs == 1 else qstreams[qstream_of[li]])
+        if nqs > 1:
+            for qs in qstreams:
+                j = torch.cuda.Event()
+                j.record(qs)
+                stream.wait_event(j)
+
+    def step(i, ev=None):
+        quantize_all(ev)
+        dequantize_all()
         for j, b in enumerate((1, 8, 256)):
             pk, d, z = copies[(3 * i + j) % ncopy]
             product(pk, d, z, b)
@@ -377,24 +426,18 @@ def main():
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
-    ev = {"q": [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in layers] for _ in range(a.steps)]}
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    qtimes = []
     for i in range(a.steps):
-        evs = {"q": ev["q"][i]}
-        step(i, evs)
+        step(i, ev[i])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = start.elapsed_time(end) / a.steps
-    for i in range(a.steps):
-        qtimes.append([s.elapsed_time(e) for s, e in ev["q"][i]])
-    qtimes = np.array(qtimes)  # [steps, layers] ms per hqq_quantize call
-    q_ms_step = float(qtimes.sum(axis=1).mean())
+    qtimes = np.array([s.elapsed_time(e) for s, e in ev])  # ms per step of the layers' hqq_quantize calls
 
     stops = [int(out[3].item()) for _, _, _, out, _ in layers]
     rounds = [min(s + 2, qp.iters) if s < qp.iters else qp.iters for s in stops]
@@ -514,9 +557,8 @@ def main():
         del src, dst
 
     # ---------------------------------------------------------------- roofline of the quantizer
-    q_s_per_call = qtimes.mean(axis=0) * 1e-3  # per layer
     ops = sum((OPS_PER_ROUND * r + OPS_FIXED) * t.rows * t.cols for (t, *_), r in zip(layers, rounds))
-    q_s_total = float(q_s_per_call.sum())
+    q_s_total = float(qtimes.mean()) * 1e-3  # the layer set's quantize phase per step
     achieved = ops / q_s_total
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -526,7 +568,7 @@ def main():
             traffic = tr.get("bytes_per_layer_set")
     roof = {"bound": "alu", "achieved": achieved / 1e12, "peak": PEAK_FP64_ALU / 1e12, "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP64_ALU, "traffic": traffic,
-            "kernel": "hqq_quantize (solve + stop decision + fix-up), 7 layers",
+            "kernel": "hqq_quantize (solve + stop decision + fix-up), 7 layers on %d stream(s)" % nqs,
             "ops_per_weight": "%d per evaluated round + %d" % (OPS_PER_ROUND, OPS_FIXED),
             "rounds_evaluated": rounds, "seconds_per_layer_set": q_s_total}
     g1 = legs["gemv_b1"]
