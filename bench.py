@@ -12,8 +12,8 @@ Beside the step (in "legs", not in `value`): the input gradient dX = dY W_hat on
 weight at batch 256 (hqq_gemm_w4a16_dx), the same layer shapes on Laplace weights at 3-bit
 g64 and 2-bit g16, the 28672x8192 weight with axis-0 groups of 128, and the fused products over
 the 3-bit, 2-bit and axis-0 formats.
-The seven layers are independent tensors: their quantize and dequantize calls are spread over four
-streams (joined before the products).  Inputs are resident in HBM before the timed region; the
+The seven layers are independent tensors: their quantize calls are spread over two streams (joined
+before the dequantisation).  Inputs are resident in HBM before the timed region; the
 product and dequant operands rotate over enough copies (> 1 GB) that the 256 MB last-level cache
 cannot hold them.
 
@@ -46,11 +46,11 @@ PEAK_FP64_ALU = 256 * 4 * 16 * 2.4e9
 OPS_PER_ROUND = 6
 OPS_FIXED = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_traffic.json")
-# The layers are independent tensors: their hqq_quantize (and hqq_dequantize) calls go to this many
-# streams (default priority), so one layer's solve fills the GPU while another's stop decision and
-# fix-up (small, latency-bound launches) run.  Measured on the 7-layer set: 1 stream 199, 2 streams
-# 208, 3 streams 210, 4 streams 212 Gweights/s for the quantize phase.
-QSTREAMS = 4
+# The layers are independent tensors: their hqq_quantize calls go to this many streams (default
+# priority), so one layer's solve fills the GPU while another's stop decision and fix-up (small,
+# latency-bound launches) run.  Measured on the 7-layer set (quantize phase / whole step,
+# Gweights/s): 1 stream 202 / 172, 2 streams 213 / 177, 3 streams 213 / 175, 4 streams 212 / 174.
+QSTREAMS = 2
 
 
 def log(*a):
@@ -143,7 +143,7 @@ def sleep_rate(stream):
 SCALE_GRID = (0.85, 0.925, 1.0, 1.05, 1.1)
 
 
-def scale_search_leg(timed, dev):
+def scale_search_leg(timed, dev, fan, assign):
     """The second solver (hqq_quantize_v2) on the Llama-7B layer set, 4-bit g64, 20 rounds, over
     five multipliers of the min-max scale: its rate and, next to the default solver's, the mean
     |W - W_hat| it reaches (both dequantised by the library, averaged on the device)."""
@@ -159,10 +159,12 @@ def scale_search_leg(timed, dev):
     outs = [hq.hqq_quantize_v2(W, SCALE_GRID, nbits=qp.nbits, group_size=qp.group_size, iters=qp.iters, p=qp.p,
                                beta0=qp.beta0, kappa=qp.kappa) for W in Ws]
 
-    def vall(r):
-        for W, (q, ch) in zip(Ws, outs):
-            hq.hqq_quantize_v2(W, SCALE_GRID, nbits=qp.nbits, group_size=qp.group_size, iters=qp.iters, p=qp.p,
-                               beta0=qp.beta0, kappa=qp.kappa, out=(q.packed, q.delta, q.zero, ch))
+    where = assign([t.rows * t.cols for t in tensors])
+
+    def vall(r):  # the layers spread over the streams, as in the step
+        fan([lambda W=W, q=q, ch=ch: hq.hqq_quantize_v2(
+            W, SCALE_GRID, nbits=qp.nbits, group_size=qp.group_size, iters=qp.iters, p=qp.p, beta0=qp.beta0,
+            kappa=qp.kappa, out=(q.packed, q.delta, q.zero, ch)) for W, (q, ch) in zip(Ws, outs)], where)
 
     tv = timed(vall, 3)
     n = sum(t.rows * t.cols for t in tensors)
@@ -187,7 +189,7 @@ def scale_search_leg(timed, dev):
             "chosen_per_multiplier": counts.cpu().tolist()}
 
 
-def config_legs(a, timed, stream, dev, rotated, read_floor):
+def config_legs(a, timed, stream, dev, rotated, read_floor, fan, assign):
     """Legs outside the step, one per remaining configuration: the 7B-shaped layer set at 3-bit
     g64 and 2-bit g16 (Laplace weights), the 28672x8192 axis-0 g128 weight, and the fused
     products over the 3-bit, 2-bit and axis-0 formats (batch 1 and 2; batch 256 through hqq_gemm for
@@ -208,11 +210,13 @@ def config_legs(a, timed, stream, dev, rotated, read_floor):
         outs = [hq.hqq_quantize(W, nbits=qp.nbits, group_size=qp.group_size, axis=qp.axis, iters=qp.iters, p=qp.p,
                                 beta0=qp.beta0, kappa=qp.kappa, workspace=ws) for W, ws in zip(Ws, wss)]
 
-        def qall(r):
-            for W, ws, q in zip(Ws, wss, outs):
-                hq.hqq_quantize(W, nbits=qp.nbits, group_size=qp.group_size, axis=qp.axis, iters=qp.iters, p=qp.p,
-                                beta0=qp.beta0, kappa=qp.kappa, workspace=ws,
-                                out=(q.packed, q.delta, q.zero, q.stop_iter, q.mae_trace))
+        where = assign([t.rows * t.cols for t in tensors])
+
+        def qall(r):  # the layers spread over the streams, as in the step
+            fan([lambda W=W, ws=ws, q=q: hq.hqq_quantize(
+                W, nbits=qp.nbits, group_size=qp.group_size, axis=qp.axis, iters=qp.iters, p=qp.p, beta0=qp.beta0,
+                kappa=qp.kappa, workspace=ws, out=(q.packed, q.delta, q.zero, q.stop_iter, q.mae_trace))
+                for W, ws, q in zip(Ws, wss, outs)], where)
 
         tq = timed(qall, reps)
         del wss
@@ -223,7 +227,7 @@ def config_legs(a, timed, stream, dev, rotated, read_floor):
         byt = sum(t.rows * t.cols * (wb / 8 + 4 / qp.group_size) for t in tensors)
         dcopies = rotated([(q.packed, q.delta, q.zero) for q in outs], byt)
 
-        def dqall(r):
+        def dqall(r):  # one stream: concurrent write streams measured slower (0.49 against 0.64 of peak)
             for t, (pk, d, z), o in zip(tensors, dcopies[r % len(dcopies)], Wh):
                 hq.hqq_dequantize(pk, d, z, t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=o)
 
@@ -251,21 +255,22 @@ def config_legs(a, timed, stream, dev, rotated, read_floor):
             legs["%s_b%d" % (name, b)] = {"us": tg * 1e6, "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM,
                                           "bytes": byt, "shape": [N, K], "copies_rotated": ncopy,
                                           "frac_of_read_floor": legs["%s_read_floor" % name]["us"] / (tg * 1e6)}
-        if axis == 1:  # the batched product over the same format at batch 256 (hqq_gemm)
-            B = 256
-            X2 = torch.from_numpy(synth.activations(B, K, 403)).to(dev)
-            Y = torch.empty((B, N), dtype=torch.float16, device=dev)
-            ws = torch.empty(hq.hqq_gemm_workspace_bytes(N, K, B), dtype=torch.uint8, device=dev)
+        if axis == 1:  # the batched product over the same format at batch 8 and 256 (hqq_gemm)
+            for B in (8, 256):
+                X2 = torch.from_numpy(synth.activations(B, K, 403)).to(dev)
+                Y = torch.empty((B, N), dtype=torch.float16, device=dev)
+                ws = torch.empty(hq.hqq_gemm_workspace_bytes(N, K, B), dtype=torch.uint8, device=dev)
 
-            def gm(r):
-                pk, d, z = copies[r % ncopy]
-                hq.hqq_gemm(pk, d, z, N, K, nbits, g, axis, X2, out=Y, workspace=ws)
-            tg = timed(gm, 2 * ncopy)
-            fl = 2.0 * B * N * K
-            legs["%s_b%d" % (name.replace("gemv", "gemm"), B)] = {
-                "us": tg * 1e6, "TFLOP/s": fl / tg / 1e12, "frac_mfma_f16": fl / tg / PEAK_FP16_MFMA, "shape": [N, K],
-                "copies_rotated": ncopy}
-            del X2, ws
+                def gm(r, X2=X2, Y=Y, ws=ws):
+                    pk, d, z = copies[r % ncopy]
+                    hq.hqq_gemm(pk, d, z, N, K, nbits, g, axis, X2, out=Y, workspace=ws)
+                tg = timed(gm, 2 * ncopy)
+                fl = 2.0 * B * N * K
+                byt = byt_w + 2 * B * K + 2 * B * N
+                legs["%s_b%d" % (name.replace("gemv", "gemm"), B)] = {
+                    "us": tg * 1e6, "TFLOP/s": fl / tg / 1e12, "frac_mfma_f16": fl / tg / PEAK_FP16_MFMA,
+                    "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM, "shape": [N, K], "copies_rotated": ncopy}
+                del X2, ws
         del copies
 
     log("config legs: 3-bit and 2-bit layer sets")
@@ -282,7 +287,7 @@ def config_legs(a, timed, stream, dev, rotated, read_floor):
         del outs
         torch.cuda.empty_cache()
     log("config legs: scale search over the 4-bit layer set")
-    legs["layers_scale_search_4bit_g64"] = scale_search_leg(timed, dev)
+    legs["layers_scale_search_4bit_g64"] = scale_search_leg(timed, dev, fan, assign)
     torch.cuda.empty_cache()
     log("config legs: 28672x8192 axis 0")
     m70 = synth.WORKLOADS["mlp70b"]
@@ -371,49 +376,49 @@ def main():
     # layers to streams: largest first, each to the stream with the least work so far
     nqs = max(1, a.qstreams)
     qstreams = [stream] if nqs == 1 else [torch.cuda.Stream(device=dev) for _ in range(nqs)]
-    load = [0] * nqs
-    qstream_of = [0] * len(layers)
-    for li in sorted(range(len(layers)), key=lambda k: -layers[k][0].rows * layers[k][0].cols):
-        sidx = min(range(nqs), key=lambda k: load[k])
-        qstream_of[li] = sidx
-        load[sidx] += layers[li][0].rows * layers[li][0].cols
+
+    def assign(sizes):
+        load, where = [0] * nqs, [0] * len(sizes)
+        for li in sorted(range(len(sizes)), key=lambda k: -sizes[k]):
+            where[li] = min(range(nqs), key=lambda k: load[k])
+            load[where[li]] += sizes[li]
+        return where
+
+    qstream_of = assign([t.rows * t.cols for t, *_ in layers])
+
+    def fan(fns, where):
+        """Run fns[i] on stream qstreams[where[i]], forked from and joined back to the launch stream."""
+        if nqs == 1:
+            for f in fns:
+                f()
+            return
+        fork = torch.cuda.Event()
+        fork.record(stream)
+        for qs in qstreams:
+            qs.wait_event(fork)
+        for f, w in zip(fns, where):
+            with torch.cuda.stream(qstreams[w]):
+                f()
+        for qs in qstreams:
+            j = torch.cuda.Event()
+            j.record(qs)
+            stream.wait_event(j)
 
     def quantize_all(ev=None):
         """The layers' hqq_quantize calls; ev = (start, end) events on the launch stream around them."""
         if ev is not None:
             ev[0].record(stream)
-        if nqs > 1:
-            fork = torch.cuda.Event()
-            fork.record(stream)
-            for qs in qstreams:
-                qs.wait_event(fork)
-        for li, (t, W, ws, out, What) in enumerate(layers):
-            hq.hqq_quantize(W, nbits=qp.nbits, group_size=qp.group_size, axis=qp.axis, iters=qp.iters, p=qp.p,
-                            beta0=qp.beta0, kappa=qp.kappa, workspace=ws, out=out,
-                            stream=None if nqs == 1 else qstreams[qstream_of[li]])
-        if nqs > 1:
-            for qs in qstreams:
-                j = torch.cuda.Event()
-                j.record(qs)
-                stream.wait_event(j)
+        fan([lambda W=W, ws=ws, out=out: hq.hqq_quantize(
+            W, nbits=qp.nbits, group_size=qp.group_size, axis=qp.axis, iters=qp.iters, p=qp.p, beta0=qp.beta0,
+            kappa=qp.kappa, workspace=ws, out=out) for t, W, ws, out, What in layers], qstream_of)
         if ev is not None:
             ev[1].record(stream)
 
     def dequantize_all():
-        """The layers' hqq_dequantize calls, on the same streams as their quantize calls."""
-        if nqs > 1:
-            fork = torch.cuda.Event()
-            fork.record(stream)
-            for qs in qstreams:
-                qs.wait_event(fork)
-        for li, (t, W, ws, out, What) in enumerate(layers):
-            hq.hqq_dequantize(out[0], out[1], out[2], t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=What,
-                              stream=None if nqs == 1 else qstreams[qstream_of[li]])
-        if nqs > 1:
-            for qs in qstreams:
-                j = torch.cuda.Event()
-                j.record(qs)
-                stream.wait_event(j)
+        """The layers' hqq_dequantize calls on the launch stream (write-heavy kernels on several streams at
+        once measured slower than one after another)."""
+        for t, W, ws, out, What in layers:
+            hq.hqq_dequantize(out[0], out[1], out[2], t.rows, t.cols, qp.nbits, qp.group_size, qp.axis, out=What)
 
     def step(i, ev=None):
         quantize_all(ev)
@@ -542,7 +547,7 @@ def main():
     del csrc, cdst
 
     if not a.no_extra_legs:
-        legs.update(config_legs(a, timed, stream, dev, rotated, read_floor))
+        legs.update(config_legs(a, timed, stream, dev, rotated, read_floor, fan, assign))
     for leg in legs.values():  # every HBM fraction also against the measured copy rate
         if "frac_hbm" in leg:
             leg["frac_copy"] = leg["frac_hbm"] * PEAK_HBM / copy_bps
