@@ -11,7 +11,7 @@ three 11008x4096 fp16 weights, N(0, 0.02) with 0.1 % +/-10 sigma outliers):
 Beside the step (in "legs", not in `value`): the input gradient dX = dY W_hat on the 8192x8192
 weight at batch 256 (hqq_gemm_w4a16_dx), the same layer shapes on Laplace weights at 3-bit
 g64 and 2-bit g16, the 28672x8192 weight with axis-0 groups of 128, and the fused products over
-the 3-bit, 2-bit and axis-0 formats.
+the 3-bit, 2-bit and axis-0 formats (with the 3-/2-bit input gradients, hqq_gemm_dx).
 The seven layers are independent tensors: their quantize calls are spread over two streams (joined
 before the dequantisation).  Inputs are resident in HBM before the timed region; the
 product and dequant operands rotate over enough copies (> 1 GB) that the 256 MB last-level cache
@@ -271,6 +271,20 @@ def config_legs(a, timed, stream, dev, rotated, read_floor, fan, assign):
                     "us": tg * 1e6, "TFLOP/s": fl / tg / 1e12, "frac_mfma_f16": fl / tg / PEAK_FP16_MFMA,
                     "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM, "shape": [N, K], "copies_rotated": ncopy}
                 del X2, ws
+            # the input gradient dX = dY W_hat at batch 256 (hqq_gemm_dx)
+            DY = torch.from_numpy(synth.activations(256, N, 404)).to(dev)
+            DX = torch.empty((256, K), dtype=torch.float16, device=dev)
+            ws = torch.empty(hq.hqq_gemm_dx_workspace_bytes(N, K, 256), dtype=torch.uint8, device=dev)
+
+            def gdx(r):
+                pk, d, z = copies[r % ncopy]
+                hq.hqq_gemm_dx(pk, d, z, N, K, nbits, g, axis, DY, out=DX, workspace=ws)
+            tg = timed(gdx, 2 * ncopy)
+            fl = 2.0 * 256 * N * K
+            legs["%s_b256" % name.replace("gemv", "dx")] = {
+                "us": tg * 1e6, "TFLOP/s": fl / tg / 1e12, "frac_mfma_f16": fl / tg / PEAK_FP16_MFMA,
+                "shape": [N, K], "copies_rotated": ncopy}
+            del DY, DX, ws
         del copies
 
     log("config legs: 3-bit and 2-bit layer sets")

@@ -278,7 +278,7 @@ int hqq_gemv_w4a16(const void* packed, const void* delta_fp16, const void* zero_
  *   workspace        device memory of at least hqq_gemm_workspace_bytes(N, K, batch) bytes,
  *                    16-byte aligned, owned by the caller; overwritten (a tiled copy of x and
  *                    the partial sums); calls that share a workspace must not overlap.
- * N must be a multiple of 128 and K of 512; group_size 64 or 128; any batch >= 1 (rows are
+ * N must be a multiple of 128 and K of 256; group_size 64 or 128; any batch >= 1 (rows are
  * processed in blocks of 256).  Returns HQQ_ERR_UNSUPPORTED for other shapes and
  * HQQ_ERR_WORKSPACE when the workspace is too small.
  */
@@ -296,7 +296,7 @@ int hqq_gemm_w4a16(const void* packed, const void* delta_fp16, const void* zero_
  *   workspace   at least hqq_gemm_workspace_bytes(N, K, batch) bytes, as hqq_gemm_w4a16.
  * The same split MFMA kernel: only the weight tile's staging depends on the format (ten
  * 3-bit codes per word, rows starting inside words; four 2-bit codes per byte).  N a multiple
- * of 128, K of 512; group_size 64 or 128 for 4-bit codes (the hqq_gemm_w4a16 path), a power of
+ * of 128, K of 256; group_size 64 or 128 for 4-bit codes (the hqq_gemm_w4a16 path), a power of
  * two 16..256 for 2/3-bit codes; axis 0 and other shapes return HQQ_ERR_UNSUPPORTED.  Any
  * batch >= 1 (batches 1 and 2 are cheaper through hqq_gemv).
  */
@@ -314,12 +314,28 @@ int hqq_gemm(const void* packed, const void* delta_fp16, const void* zero_fp16, 
  *   workspace   at least hqq_gemm_dx_workspace_bytes(N, K, batch) bytes, as hqq_gemm_w4a16.
  * The same split MFMA kernel with the weight tile transposed in LDS (the packed format is read
  * as stored); fp32 accumulation, splits of N added in a fixed order.  K must be a multiple of
- * 128 and N of 512; other shapes return HQQ_ERR_UNSUPPORTED.
+ * 128 and N of 256; other shapes return HQQ_ERR_UNSUPPORTED.
  */
 size_t hqq_gemm_dx_workspace_bytes(int64_t N, int64_t K, int64_t batch);
 int hqq_gemm_w4a16_dx(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K,
                       int group_size, const void* dy_fp16, int64_t batch, void* dx, int dx_dtype, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * The input gradient for the other stored formats ("从压缩文件到一次前向" for the product,
+ * "为什么一定要分组" for the containers): dX = dY @ W_hat as hqq_gemm_w4a16_dx, for codes of
+ * nbits = 2, 3 or 4 with axis-1 groups, stored as hqq_quantize wrote them.
+ *   packed, delta_fp16, zero_fp16, N, K, nbits, group_size, axis  as hqq_gemm.
+ *   dy_fp16, batch, dx, dx_dtype  as hqq_gemm_w4a16_dx.
+ *   workspace   at least hqq_gemm_dx_workspace_bytes(N, K, batch) bytes, as hqq_gemm_w4a16.
+ * The transposed split kernel: each staging thread unpacks 32 codes of two weight rows (ten
+ * 3-bit codes per word, four 2-bit codes per byte) and writes them column-major into the LDS
+ * tile.  K a multiple of 128, N of 256; group_size 64 or 128 for 4-bit codes, a power of two
+ * 16..256 for 2/3-bit codes; axis 0 and other shapes return HQQ_ERR_UNSUPPORTED.
+ */
+int hqq_gemm_dx(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K, int nbits,
+                int group_size, int axis, const void* dy_fp16, int64_t batch, void* dx, int dx_dtype, void* workspace,
+                size_t workspace_bytes, void* stream);
 
 /*
  * The same fused product for the other stored formats ("从压缩文件到一次前向";

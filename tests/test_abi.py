@@ -123,7 +123,7 @@ def test_batched_products_reject(lib):
     assert call(nbits=4, gs=32) == hq.HQQ_ERR_UNSUPPORTED      # 4-bit: 64 or 128
     assert call(nbits=2, gs=512) == hq.HQQ_ERR_UNSUPPORTED
     assert call(N=192) == hq.HQQ_ERR_UNSUPPORTED               # N % 128
-    assert call(K=768) == hq.HQQ_ERR_UNSUPPORTED               # K % 512
+    assert call(K=640) == hq.HQQ_ERR_UNSUPPORTED               # K % 256
     assert call(ydt=7) == hq.HQQ_ERR_INVALID_ARGUMENT
     assert call(wsb=ws - 16) == hq.HQQ_ERR_WORKSPACE
     assert call(batch=0) == hq.HQQ_ERR_INVALID_ARGUMENT
@@ -135,6 +135,23 @@ def test_batched_products_reject(lib):
     dx = lib.hqq_gemm_w4a16_dx
     assert dx(FAKE, FAKE, FAKE, 1024, 200, 64, FAKE, 32, FAKE, 0, FAKE, wdx, None) == hq.HQQ_ERR_INVALID_ARGUMENT
     assert dx(FAKE, FAKE, FAKE, 1024, 256, 64, FAKE, 32, FAKE, 0, FAKE, wdx - 16, None) == hq.HQQ_ERR_WORKSPACE
+    gdx = lib.hqq_gemm_dx
+    okd = dict(N=1024, K=256, nbits=3, gs=64, axis=1, batch=32, ydt=0, wsb=wdx)
+
+    def call_dx(**kw):
+        a = dict(okd, **kw)
+        return gdx(FAKE, FAKE, FAKE, a["N"], a["K"], a["nbits"], a["gs"], a["axis"], FAKE, a["batch"], FAKE,
+                   a["ydt"], FAKE, a["wsb"], None)
+    assert call_dx(nbits=1) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call_dx(axis=0) == hq.HQQ_ERR_UNSUPPORTED
+    assert call_dx(gs=48) == hq.HQQ_ERR_INVALID_ARGUMENT      # does not divide K
+    assert call_dx(nbits=4, gs=32) == hq.HQQ_ERR_UNSUPPORTED
+    assert call_dx(nbits=2, gs=8) == hq.HQQ_ERR_UNSUPPORTED
+    assert call_dx(K=192) == hq.HQQ_ERR_UNSUPPORTED           # K % 128
+    assert call_dx(N=640) == hq.HQQ_ERR_UNSUPPORTED           # N % 256
+    assert call_dx(ydt=5) == hq.HQQ_ERR_INVALID_ARGUMENT
+    assert call_dx(wsb=wdx - 16) == hq.HQQ_ERR_WORKSPACE
+    assert call_dx(batch=-1) == hq.HQQ_ERR_INVALID_ARGUMENT
 
 
 def test_status_strings(lib):

@@ -118,7 +118,9 @@ def test_unsupported_formats_rejected():
 # residue; batches 3 .. 300 span one and two 256-row blocks; N from one to four 128-row tiles
 GEMM_CASES = [(3, 64, 128, 512, 3), (3, 16, 256, 1024, 9), (3, 32, 384, 2048, 100), (3, 128, 128, 1536, 256),
               (3, 256, 512, 4096, 300), (2, 16, 128, 512, 5), (2, 32, 256, 1024, 64), (2, 16, 384, 4096, 257),
-              (2, 128, 128, 2048, 17), (2, 256, 256, 1536, 40), (4, 64, 256, 1024, 33), (4, 128, 128, 512, 3)]
+              (2, 128, 128, 2048, 17), (2, 256, 256, 1536, 40), (4, 64, 256, 1024, 33), (4, 128, 128, 512, 3),
+              # K / 256 pairs of chunks not a power of two: splits of unequal length
+              (3, 64, 128, 1280, 20), (2, 16, 256, 768, 70), (4, 64, 256, 768, 40), (4, 128, 128, 256, 9)]
 
 
 def _check_gemm(nbits, g, N, K, batch, seed, rows_sel=None):
@@ -145,11 +147,13 @@ def test_gemm_formats(nbits, g, N, K, batch):
     _check_gemm(nbits, g, N, K, batch, seed=4000 + 7 * nbits + g + N + K + batch)
 
 
-@pytest.mark.parametrize("nbits,g", [(3, 64), (2, 16)])
-def test_gemm_formats_full_shape(nbits, g):
-    """The 11008 x 4096 projection of the 3-bit and 2-bit layer sets at batch 256 (sampled rows)."""
-    sel = np.sort(np.random.default_rng(10 + nbits).choice(11008, 256, replace=False))
-    _check_gemm(nbits, g, 11008, 4096, 256, seed=4500 + nbits, rows_sel=sel)
+@pytest.mark.parametrize("nbits,g,N,K", [(3, 64, 11008, 4096), (2, 16, 11008, 4096), (3, 64, 4096, 11008),
+                                          (2, 16, 4096, 11008)], ids=lambda v: str(v))
+def test_gemm_formats_full_shape(nbits, g, N, K):
+    """The 11008 x 4096 and 4096 x 11008 projections of the 3-bit and 2-bit layer sets at batch
+    256 (sampled rows); the second contracts over 43 pairs of chunks in 8 unequal splits."""
+    sel = np.sort(np.random.default_rng(10 + nbits).choice(N, 256, replace=False))
+    _check_gemm(nbits, g, N, K, 256, seed=4500 + nbits + K, rows_sel=sel)
 
 
 def test_gemm_formats_rejected():
@@ -158,7 +162,77 @@ def test_gemm_formats_rejected():
     pk = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
     md = torch.zeros(1 << 14, dtype=torch.float16, device="cuda")
     x = torch.zeros((4, 512), dtype=torch.float16, device="cuda")
-    for nbits, g, axis, N, K in ((3, 64, 0, 128, 512), (4, 32, 1, 128, 512), (2, 16, 1, 64, 512), (3, 16, 1, 128, 256),
+    for nbits, g, axis, N, K in ((3, 64, 0, 128, 512), (4, 32, 1, 128, 512), (2, 16, 1, 64, 512), (3, 16, 1, 128, 384),
                                  (2, 512, 1, 128, 512), (5, 64, 1, 128, 512)):
         with pytest.raises(hq.HQQError):
             hq.hqq_gemm(pk, md, md, N, K, nbits, g, axis, x[:, :K].contiguous())
+
+
+# ------------------------------------------------------------ input gradient (hqq_gemm_dx)
+# dX [batch, K] = dY [batch, N] @ W_hat, W [N, K]: the contraction N in pairs of 128-row chunks
+# (one to eight, also counts that do not split evenly), output columns K in 128-column tiles
+# whose 32-code pieces start at every even slot of a 3-bit word
+DX_CASES = [(3, 64, 512, 128, 3), (3, 16, 256, 384, 9), (3, 32, 768, 256, 100), (3, 128, 1024, 640, 256),
+            (3, 256, 2048, 512, 300), (2, 16, 512, 128, 5), (2, 32, 768, 384, 64), (2, 128, 1280, 256, 257),
+            (2, 256, 256, 512, 17), (4, 64, 768, 256, 33), (4, 128, 512, 384, 3)]
+
+
+def _check_dx(nbits, g, N, K, batch, seed, cols_sel=None):
+    torch = torch_dev()
+    import weight_only_quantization_amd as hq
+    o = oracle.get()
+    packed, delta, zero = _operands(seed, N, K, nbits, g, 1)
+    dy = np.random.default_rng(seed + 1).normal(0, 1, (batch, N)).astype(np.float16)
+    ref = o.gemv_t(packed, delta, zero, N, K, nbits, g, 1, dy.astype(np.float64), cols_sel=cols_sel)
+    scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref ** 2)))
+    pk, dl, zr = (torch.from_numpy(a).cuda() for a in (packed, delta, zero))
+    for out_dtype in (torch.float32, torch.float16):
+        dx = hq.hqq_gemm_dx(pk, dl, zr, N, K, nbits, g, 1, torch.from_numpy(dy).cuda(),
+                            out_dtype=out_dtype).float().cpu().numpy().astype(np.float64)
+        dxg = dx if cols_sel is None else dx[:, cols_sel]
+        err = float(np.max(np.abs(dxg - ref) / scale))
+        say("  dx N=%d K=%d b%d g%d batch=%d %s: max rel err %.3g" % (N, K, nbits, g, batch, out_dtype, err))
+        assert err <= GEMV_TOL
+
+
+@pytest.mark.parametrize("nbits,g,N,K,batch", DX_CASES, ids=lambda v: str(v))
+def test_gemm_dx_formats(nbits, g, N, K, batch):
+    _check_dx(nbits, g, N, K, batch, seed=7000 + 7 * nbits + g + N + K + batch)
+
+
+@pytest.mark.parametrize("nbits,g,N,K", [(3, 64, 11008, 4096), (2, 16, 11008, 4096), (3, 64, 4096, 11008),
+                                          (4, 64, 11008, 4096)], ids=lambda v: str(v))
+def test_gemm_dx_formats_full_shape(nbits, g, N, K):
+    """Input gradients of the layer sets' projections at batch 256 (sampled columns); the
+    11008-row weights contract over 43 pairs of chunks in unequal splits."""
+    sel = np.sort(np.random.default_rng(20 + nbits).choice(K, 256, replace=False))
+    _check_dx(nbits, g, N, K, 256, seed=7500 + nbits + N, cols_sel=sel)
+
+
+@pytest.mark.parametrize("nbits,g", [(3, 32), (2, 16)])
+def test_gemm_dx_formats_adjoint(nbits, g):
+    """<dY, x W_hat^T> = <dY W_hat, x> between hqq_gemm and hqq_gemm_dx (fp32 outputs)."""
+    torch = torch_dev()
+    import weight_only_quantization_amd as hq
+    N, K, B = 768, 512, 24
+    packed, delta, zero = _operands(90 + nbits, N, K, nbits, g, 1)
+    pk, dl, zr = (torch.from_numpy(a).cuda() for a in (packed, delta, zero))
+    r = np.random.default_rng(91)
+    x = torch.from_numpy(r.normal(0, 1, (B, K)).astype(np.float16)).cuda()
+    dy = torch.from_numpy(r.normal(0, 1, (B, N)).astype(np.float16)).cuda()
+    y = hq.hqq_gemm(pk, dl, zr, N, K, nbits, g, 1, x, out_dtype=torch.float32).double()
+    dx = hq.hqq_gemm_dx(pk, dl, zr, N, K, nbits, g, 1, dy, out_dtype=torch.float32).double()
+    lhs = (dy.double() * y).sum(dim=1)
+    rhs = (dx * x.double()).sum(dim=1)
+    assert torch.allclose(lhs, rhs, rtol=1e-4, atol=1e-4 * float(lhs.abs().max()))
+
+
+def test_gemm_dx_formats_rejected():
+    torch = torch_dev()
+    import weight_only_quantization_amd as hq
+    pk = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    md = torch.zeros(1 << 14, dtype=torch.float16, device="cuda")
+    for nbits, g, axis, N, K in ((3, 64, 0, 512, 128), (4, 32, 1, 512, 128), (2, 16, 1, 384, 128),
+                                 (3, 16, 1, 512, 64), (2, 512, 1, 512, 512)):
+        with pytest.raises(hq.HQQError):
+            hq.hqq_gemm_dx(pk, md, md, N, K, nbits, g, axis, torch.zeros((4, N), dtype=torch.float16, device="cuda"))

@@ -36,7 +36,7 @@ EXPORTS = ("hqq_packed_bytes", "hqq_num_groups", "hqq_quantize_workspace_bytes",
            "hqq_quantize_noalloc",
            "hqq_quantize_v2", "hqq_quantize_v2_workspace_bytes",
            "hqq_dequantize", "hqq_gemv_w4a16", "hqq_gemm_workspace_bytes", "hqq_gemm_w4a16",
-           "hqq_gemm_dx_workspace_bytes", "hqq_gemm_w4a16_dx", "hqq_gemv", "hqq_gemm",
+           "hqq_gemm_dx_workspace_bytes", "hqq_gemm_w4a16_dx", "hqq_gemm_dx", "hqq_gemv", "hqq_gemm",
            "hqq_status_string", "hqq_last_error")
 
 _lib = None
@@ -85,6 +85,8 @@ def load(path: str = LIB_PATH):
     lib.hqq_gemm_dx_workspace_bytes.restype = sz
     lib.hqq_gemm_w4a16_dx.argtypes = [p, p, p, i64, i64, i32, p, i64, p, i32, p, sz, p]
     lib.hqq_gemm_w4a16_dx.restype = i32
+    lib.hqq_gemm_dx.argtypes = [p, p, p, i64, i64, i32, i32, i32, p, i64, p, i32, p, sz, p]
+    lib.hqq_gemm_dx.restype = i32
     lib.hqq_gemv.argtypes = [p, p, p, i64, i64, i32, i32, i32, p, i64, p, i32, p]
     lib.hqq_gemv.restype = i32
     lib.hqq_gemm.argtypes = [p, p, p, i64, i64, i32, i32, i32, p, i64, p, i32, p, sz, p]
@@ -484,6 +486,32 @@ def hqq_gemm_w4a16_dx(packed, delta, zero, N: int, K: int, group_size: int, dy, 
                                ctypes.c_void_p(zero.data_ptr()), N, K, group_size, ctypes.c_void_p(dy.data_ptr()),
                                batch, ctypes.c_void_p(out.data_ptr()), code, ctypes.c_void_p(workspace.data_ptr()),
                                workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    _check(st)
+    return out
+
+
+def hqq_gemm_dx(packed, delta, zero, N: int, K: int, nbits: int, group_size: int, axis: int, dy, out_dtype=None,
+                out=None, workspace=None, stream=None):
+    """Input gradient dX [batch, K] = dY [batch, N] @ W_hat for 2-, 3- or 4-bit codes of W [N, K]
+    with axis-1 groups (workspace as hqq_gemm_w4a16, sized by hqq_gemm_dx_workspace_bytes)."""
+    import torch
+    lib = load()
+    out_dtype = out_dtype or torch.float16
+    _product_operands(packed, delta, zero, N, K, nbits, group_size, dy, xname="dy", out=out, out_cols=K)
+    batch = dy.shape[0]
+    need = lib.hqq_gemm_dx_workspace_bytes(N, K, batch)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((batch, K), dtype=out_dtype, device=dy.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dy.device)
+    _need(workspace, "workspace", torch.uint8)
+    code = HQQ_OUT_F16 if out.dtype == torch.float16 else HQQ_OUT_F32
+    st = lib.hqq_gemm_dx(ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(delta.data_ptr()),
+                         ctypes.c_void_p(zero.data_ptr()), N, K, nbits, group_size, axis,
+                         ctypes.c_void_p(dy.data_ptr()), batch, ctypes.c_void_p(out.data_ptr()), code,
+                         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+                         _stream_ptr(stream))
     _check(st)
     return out
 

@@ -392,7 +392,7 @@ int hqq_gemm_w4a16(const void* packed, const void* delta_fp16, const void* zero_
   if (group_size <= 0 || K % group_size != 0) return fail(HQQ_ERR_INVALID_ARGUMENT, "group_size must divide K");
   if (group_size != 64 && group_size != 128) return fail(HQQ_ERR_UNSUPPORTED, "group_size must be 64 or 128");
   if (hqq::gemm_splits(N, K, batch) == 0)
-    return fail(HQQ_ERR_UNSUPPORTED, "N must be a multiple of 128 and K of 512");
+    return fail(HQQ_ERR_UNSUPPORTED, "N must be a multiple of 128 and K of 256");
   if (y_dtype != HQQ_OUT_F16 && y_dtype != HQQ_OUT_F32)
     return fail(HQQ_ERR_INVALID_ARGUMENT, "y_dtype must be HQQ_OUT_F16 or HQQ_OUT_F32");
   if (!packed || !delta_fp16 || !zero_fp16 || !x_fp16 || !y || !workspace)
@@ -427,7 +427,7 @@ int hqq_gemm(const void* packed, const void* delta_fp16, const void* zero_fp16, 
                  : (group_size < 16 || group_size > 256 || (group_size & (group_size - 1)) != 0))
     return fail(HQQ_ERR_UNSUPPORTED, "group_size 64 or 128 for 4-bit codes, a power of two 16..256 for 2/3-bit");
   if (hqq::gemm_splits(N, K, batch) == 0)
-    return fail(HQQ_ERR_UNSUPPORTED, "N must be a multiple of 128 and K of 512");
+    return fail(HQQ_ERR_UNSUPPORTED, "N must be a multiple of 128 and K of 256");
   if (y_dtype != HQQ_OUT_F16 && y_dtype != HQQ_OUT_F32)
     return fail(HQQ_ERR_INVALID_ARGUMENT, "y_dtype must be HQQ_OUT_F16 or HQQ_OUT_F32");
   if (!packed || !delta_fp16 || !zero_fp16 || !x_fp16 || !y || !workspace)
@@ -463,7 +463,7 @@ int hqq_gemm_w4a16_dx(const void* packed, const void* delta_fp16, const void* ze
   if (group_size <= 0 || K % group_size != 0) return fail(HQQ_ERR_INVALID_ARGUMENT, "group_size must divide K");
   if (group_size != 64 && group_size != 128) return fail(HQQ_ERR_UNSUPPORTED, "group_size must be 64 or 128");
   if (hqq::gemm_splits(K, N, batch) == 0)
-    return fail(HQQ_ERR_UNSUPPORTED, "K must be a multiple of 128 and N of 512");
+    return fail(HQQ_ERR_UNSUPPORTED, "K must be a multiple of 128 and N of 256");
   if (dx_dtype != HQQ_OUT_F16 && dx_dtype != HQQ_OUT_F32)
     return fail(HQQ_ERR_INVALID_ARGUMENT, "dx_dtype must be HQQ_OUT_F16 or HQQ_OUT_F32");
   if (!packed || !delta_fp16 || !zero_fp16 || !dy_fp16 || !dx || !workspace)
@@ -476,9 +476,44 @@ int hqq_gemm_w4a16_dx(const void* packed, const void* delta_fp16, const void* ze
     return fail(HQQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   const hipError_t e = hqq::launch_gemm_dx(
       reinterpret_cast<const uint8_t*>(packed), reinterpret_cast<const __half*>(delta_fp16),
-      reinterpret_cast<const __half*>(zero_fp16), N, K, group_size, reinterpret_cast<const __half*>(dy_fp16), batch,
+      reinterpret_cast<const __half*>(zero_fp16), N, K, 4, group_size, reinterpret_cast<const __half*>(dy_fp16), batch,
       dx, dx_dtype, workspace, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "hqq_gemm_w4a16_dx launch");
+  return HQQ_OK;
+}
+
+int hqq_gemm_dx(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K, int nbits,
+                int group_size, int axis, const void* dy_fp16, int64_t batch, void* dx, int dx_dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (N <= 0 || K <= 0 || batch <= 0) return fail(HQQ_ERR_INVALID_ARGUMENT, "N, K and batch must be positive");
+  if (N > (int64_t(1) << 31) || K > (int64_t(1) << 31) || batch > (int64_t(1) << 24))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "shape too large");
+  if (nbits != 2 && nbits != 3 && nbits != 4) return fail(HQQ_ERR_INVALID_ARGUMENT, "nbits must be 2, 3 or 4");
+  if (axis != 0 && axis != 1) return fail(HQQ_ERR_INVALID_ARGUMENT, "axis must be 0 or 1");
+  if (group_size <= 0 || (axis == 1 ? K : N) % group_size != 0)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "group_size must divide the grouped dimension");
+  if (axis != 1) return fail(HQQ_ERR_UNSUPPORTED, "the input gradient takes axis-1 groups");
+  if (nbits == 4 ? (group_size != 64 && group_size != 128)
+                 : (group_size < 16 || group_size > 256 || (group_size & (group_size - 1)) != 0))
+    return fail(HQQ_ERR_UNSUPPORTED, "group_size 64 or 128 for 4-bit codes, a power of two 16..256 for 2/3-bit");
+  if (hqq::gemm_splits(K, N, batch) == 0)
+    return fail(HQQ_ERR_UNSUPPORTED, "K must be a multiple of 128 and N of 256");
+  if (dx_dtype != HQQ_OUT_F16 && dx_dtype != HQQ_OUT_F32)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "dx_dtype must be HQQ_OUT_F16 or HQQ_OUT_F32");
+  if (!packed || !delta_fp16 || !zero_fp16 || !dy_fp16 || !dx || !workspace)
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "null buffer");
+  if (!aligned16(packed) || !aligned16(delta_fp16) || !aligned16(zero_fp16) || !aligned16(dy_fp16) || !aligned16(dx) ||
+      !aligned16(workspace))
+    return fail(HQQ_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
+  const size_t need = hqq::gemm_workspace_bytes(K, N, batch);
+  if (workspace_bytes < need)
+    return fail(HQQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const hipError_t e = hqq::launch_gemm_dx(
+      reinterpret_cast<const uint8_t*>(packed), reinterpret_cast<const __half*>(delta_fp16),
+      reinterpret_cast<const __half*>(zero_fp16), N, K, nbits, group_size, reinterpret_cast<const __half*>(dy_fp16),
+      batch, dx, dx_dtype, workspace, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "hqq_gemm_dx launch");
   return HQQ_OK;
 }
 

@@ -101,11 +101,10 @@ constexpr int kFmt4 = 0, kFmt2 = 2, kFmt3 = 3;
 // same barriers: one after the first tile is staged and one per chunk.
 template <int FMT, int GS, bool DIRECT, bool TRANS>
 __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restrict__ packed, const __half* __restrict__ delta,
-                                                 const __half* __restrict__ zero, int64_t N, int64_t K, int64_t ks,
+                                                 const __half* __restrict__ zero, int64_t N, int64_t K, int S,
                                                  const u32x4* __restrict__ xt, int64_t MG, int64_t batch,
                                                  float* __restrict__ part, void* __restrict__ y, int out_dtype,
                                                  int xcd_map, int gs_log2) {
-  static_assert(FMT == kFmt4 || !TRANS, "the input gradient is built for 4-bit codes");
   extern __shared__ _Float16 wt[];  // [2][kSkBN][kSkRow]
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t NO = TRANS ? K : N, KC = TRANS ? N : K;  // output and contraction lengths
@@ -114,7 +113,7 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
   // holds only its splits' columns of x.
   int tile, split;
   {
-    const int b = blockIdx.x, nb = gridDim.x, S = (int)(KC / ks);
+    const int b = blockIdx.x, nb = gridDim.x;
     if (xcd_map) {
       const int xcd = b & 7, r = b >> 3;
       if (S <= 8) {
@@ -131,22 +130,28 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
       split = b / (nb / S);
     }
   }
-  const int64_t n0 = (int64_t)tile * kSkBN, m0 = (int64_t)blockIdx.y * kSkBM, k0 = (int64_t)split * ks;
-  const int nch = (int)(ks / kSkBK);  // even, >= 2
+  // split s takes pairs of chunks [s C2 / S, (s + 1) C2 / S) of the C2 = KC / 256 pairs (S <= C2)
+  const int64_t C2 = KC / (2 * kSkBK), p_lo = split * C2 / S, p_hi = (split + 1) * C2 / S;
+  const int64_t n0 = (int64_t)tile * kSkBN, m0 = (int64_t)blockIdx.y * kSkBM, k0 = p_lo * 2 * kSkBK;
+  const int nch = (int)(2 * (p_hi - p_lo));  // even, >= 2
 
   if constexpr (FMT != kFmt4) {
     if (wave >= kSkMulWaves) {
       // ---------------------------------------------------------------- staging waves, 2/3-bit
-      // thread -> weight rows wr and 64 + wr, codes 32 wq .. 32 wq + 31 of each chunk: flat code
-      // index f = n K + k, a multiple of 32 (K % 512 == 0).  2-bit: 8 bytes; 3-bit: ten codes per
-      // word, the 32 codes start at an even slot ph of word f / 10 and end inside the fourth word.
-      // With g = 16 codes 0..15 and 16..31 are two groups; otherwise one.
+      // Forward: thread -> weight rows wr and 64 + wr, codes 32 wq .. 32 wq + 31 of each chunk.
+      // Transposed: thread -> weight rows 2 wr and 2 wr + 1 of the chunk (contraction), codes
+      // 32 wq .. +31 of the tile's output columns.  Either way 32 codes of one row from flat code
+      // index f = n K + k, an even number (K % 128 == 0): 2-bit: 8 bytes; 3-bit: ten codes per
+      // word, the 32 codes start at an even slot ph <= 8 of word f / 10 and end inside the fourth
+      // word.  With g = 16 codes 0..15 and 16..31 are two groups; otherwise one.
       const int st = tid - 64 * kSkMulWaves;
       const int wr = st >> 2, wq = st & 3;
       _Float16* wdst = wt + wr * kSkRow + 32 * wq;
       int64_t fr[2];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) fr[p] = (n0 + wr + 64 * p) * K + k0 + 32 * wq;
+      for (int p = 0; p < 2; ++p)
+        fr[p] = TRANS ? (k0 + 2 * wr + p) * K + n0 + 32 * wq : (n0 + wr + 64 * p) * K + k0 + 32 * wq;
+      const int64_t fstep = TRANS ? (int64_t)kSkBK * K : kSkBK;  // the next chunk
       struct Regs {
         unsigned w[2][4], dm[2][2], zm[2][2];
         int ph[2];
@@ -155,7 +160,7 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
         const int64_t cc = min(c, nch - 1);  // past the end: reload the last chunk (never used)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const int64_t f0 = fr[p] + kSkBK * cc;
+          const int64_t f0 = fr[p] + fstep * cc;
           if constexpr (FMT == kFmt3) {
             const int64_t q0 = f0 / 10;
             r.ph[p] = (int)(f0 - 10 * q0);
@@ -174,26 +179,21 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
           }
         }
       };
-      auto stage = [&](int buf, const Regs& r) {
+      // W_hat of the thread's 32 codes of row p, natural order: blocks of 8 codes (4 dwords of pairs)
+      auto decode = [&](const Regs& r, int p, u32x4 (&o)[4]) {
+        float zd[2], d[2];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          float zd[2], d[2];
+        for (int h = 0; h < 2; ++h) {
+          d[h] = __half2float(__ushort_as_half((unsigned short)r.dm[p][h]));
+          zd[h] = __half2float(__ushort_as_half((unsigned short)r.zm[p][h])) * d[h];
+        }
+        if constexpr (FMT == kFmt2) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            d[h] = __half2float(__ushort_as_half((unsigned short)r.dm[p][h]));
-            zd[h] = __half2float(__ushort_as_half((unsigned short)r.zm[p][h])) * d[h];
+            const float ds[4] = {d[h] * 16777216.0f, d[h] * 4194304.0f, d[h] * 1048576.0f, d[h] * 262144.0f};
+            wq16_2b(r.w[p][h], ds, zd[h], o[2 * h], o[2 * h + 1]);
           }
-          _Float16* dst = wdst + buf * (kSkBN * kSkRow) + p * 64 * kSkRow;
-          if constexpr (FMT == kFmt2) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const float ds[4] = {d[h] * 16777216.0f, d[h] * 4194304.0f, d[h] * 1048576.0f, d[h] * 262144.0f};
-              u32x4 lo, hi;
-              wq16_2b(r.w[p][h], ds, zd[h], lo, hi);
-              *reinterpret_cast<u32x4*>(dst + 16 * h) = lo;
-              *reinterpret_cast<u32x4*>(dst + 16 * h + 8) = hi;
-            }
-          } else {
+        } else {
             // block b (codes 8b..8b+7) starts at slot o = ph + 8b of the window: in word o / 10,
             // which is b - 1 or b (b >= 1) depending on ph; it ends in the next word or (o >= 30,
             // then o / 10 = 3 and 3 (o - 30) + 24 <= 30) in the same one
@@ -208,9 +208,36 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
               const int sh = 3 * (ph + 8 * b - 10 * i);
               const unsigned v = (unsigned)((((uint64_t)hi << 30) | (lo & 0x3FFFFFFFu)) >> sh);
               const int h = b >> 1;
-              *reinterpret_cast<u32x4*>(dst + 8 * b) =
-                  wq8_3b(v, d[h] * 16777216.0f, d[h] * 2097152.0f, d[h] * 262144.0f, zd[h]);
+              o[b] = wq8_3b(v, d[h] * 16777216.0f, d[h] * 2097152.0f, d[h] * 262144.0f, zd[h]);
             }
+        }
+      };
+      auto stage = [&](int buf, const Regs& r) {
+        if constexpr (TRANS) {
+          // the two rows' values of one output column paired into a dword (contraction 2 wr, 2 wr + 1),
+          // 16-byte blocks swizzled as in the 4-bit path
+          u32x4 r0[4], r1[4];
+          decode(r, 0, r0);
+          decode(r, 1, r1);
+          _Float16* base = wt + buf * (kSkBN * kSkRow);
+#pragma unroll
+          for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int o = 32 * wq + 8 * sb + e;
+              const unsigned v =
+                  __builtin_amdgcn_perm(r1[sb][e >> 1], r0[sb][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+              const int blk = (wr >> 2) ^ (4 * (o >> 5));
+              *reinterpret_cast<unsigned*>(base + o * kSkRow + 8 * blk + 2 * (wr & 3)) = v;
+            }
+        } else {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            u32x4 o[4];
+            decode(r, p, o);
+            _Float16* dst = wdst + buf * (kSkBN * kSkRow) + p * 64 * kSkRow;
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) *reinterpret_cast<u32x4*>(dst + 8 * sb) = o[sb];
           }
         }
       };
@@ -430,37 +457,41 @@ __global__ void __launch_bounds__(256) k_splitk_sum(const float* __restrict__ pa
 // x [batch, K] -> xt: for k-step q (32 codes) and row group mg (16 rows), 64 lanes x 16 bytes,
 // lane l holding row 16 mg + (l & 15) (rows past the batch repeat the last row), codes
 // 32 q + 8 (l >> 4) .. +7.  A block moves a 16-row x 512-code tile through LDS: it reads
-// 1 KB row pieces and writes sixteen whole 1 KB fragments.
+// 1 KB row pieces and writes sixteen whole 1 KB fragments (the last tile of a row may hold
+// 256 codes: eight fragments).
 constexpr int kTileCols = 512;
 __global__ void __launch_bounds__(256) k_tile_x(const __half* __restrict__ x, int64_t batch, int64_t K, int64_t MG,
                                                 u32x4* __restrict__ xt) {
   __shared__ u32x4 tile[16][kTileCols / 8 + 1];
   const int tid = threadIdx.x;
   const int64_t mg = blockIdx.y, c0 = (int64_t)blockIdx.x * kTileCols;
+  const int pieces = (int)min<int64_t>(kTileCols, K - c0) / 8;  // 16-byte pieces of a row in the tile
   {
     const int r = tid >> 4, cp = (tid & 15) * 4;  // row, first 16-byte piece of four
     const int64_t src_row = min(16 * mg + r, batch - 1);
     const u32x4* src = reinterpret_cast<const u32x4*>(x + src_row * K + c0) + cp;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tile[r][cp + i] = src[i];
+    for (int i = 0; i < 4; ++i)
+      if (cp + i < pieces) tile[r][cp + i] = src[i];
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid + 256 * i, qb = e >> 6, l = e & 63;
-    xt[((c0 / 32 + qb) * MG + mg) * 64 + l] = tile[l & 15][4 * qb + (l >> 4)];
+    if (4 * qb < pieces) xt[((c0 / 32 + qb) * MG + mg) * 64 + l] = tile[l & 15][4 * qb + (l >> 4)];
   }
 }
 
 }  // namespace
 
 // Splits of K for the split GEMM: the smallest power of two that brings the grid to >= 256
-// blocks, keeping >= 2 chunks of 128 codes (an even number) per split.  0 = not applicable.
+// blocks while every split keeps >= 1 pair of 128-code chunks (the K / 256 pairs are dealt out
+// as evenly as they go: K = 11008 in 8 splits gives splits of 5 and 6 pairs).  0 = not applicable.
 int gemm_splits(int64_t N, int64_t K, int64_t batch) {
-  if (N % kSkBN != 0 || K % kTileCols != 0 || batch <= 0) return 0;
-  const int64_t tiles = (N / kSkBN) * ((batch + kSkBM - 1) / kSkBM);
+  if (N % kSkBN != 0 || K % (2 * kSkBK) != 0 || batch <= 0) return 0;
+  const int64_t tiles = (N / kSkBN) * ((batch + kSkBM - 1) / kSkBM), C2 = K / (2 * kSkBK);
   int S = 1;
-  while (tiles * S < 256 && K % (2 * kSkBK * 2 * S) == 0) S *= 2;
+  while (tiles * S < 256 && 2 * S <= C2) S *= 2;
   return S;
 }
 
@@ -482,32 +513,36 @@ namespace {
 // split GEMM, and the sum over splits.  NO = output length (N, or K), KC = contraction (K, or N).
 template <int FMT, int GS, bool DIRECT, bool TRANS>
 void launch_sk(dim3 grid, hipStream_t st, const uint8_t* packed, const __half* delta, const __half* zero, int64_t N,
-               int64_t K, int64_t ks, const u32x4* xt, int64_t MG, int64_t batch, float* pw, void* out, int y_dtype,
+               int64_t K, int S, const u32x4* xt, int64_t MG, int64_t batch, float* pw, void* out, int y_dtype,
                int xcd_map, int gl) {
   hipLaunchKernelGGL((k_gemm_sk<FMT, GS, DIRECT, TRANS>), grid, dim3(kSkThreads), kSkLds, st, packed, delta, zero, N, K,
-                     ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+                     S, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
 }
 
 template <bool DIRECT, bool TRANS>
 void launch_fmt(int fmt, int gs, dim3 grid, hipStream_t st, const uint8_t* packed, const __half* delta,
-                const __half* zero, int64_t N, int64_t K, int64_t ks, const u32x4* xt, int64_t MG, int64_t batch,
+                const __half* zero, int64_t N, int64_t K, int S, const u32x4* xt, int64_t MG, int64_t batch,
                 float* pw, void* out, int y_dtype, int xcd_map) {
   int gl = 0;
   while ((1 << gl) < gs) ++gl;
   if constexpr (TRANS) {
-    if (gs == 64)
-      launch_sk<kFmt4, 64, DIRECT, true>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+    if (fmt == kFmt3)
+      launch_sk<kFmt3, 0, DIRECT, true>(grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+    else if (fmt == kFmt2)
+      launch_sk<kFmt2, 0, DIRECT, true>(grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+    else if (gs == 64)
+      launch_sk<kFmt4, 64, DIRECT, true>(grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
     else
-      launch_sk<kFmt4, 128, DIRECT, true>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+      launch_sk<kFmt4, 128, DIRECT, true>(grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
   } else {
     if (fmt == kFmt3)
-      launch_sk<kFmt3, 0, DIRECT, false>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+      launch_sk<kFmt3, 0, DIRECT, false>(grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
     else if (fmt == kFmt2)
-      launch_sk<kFmt2, 0, DIRECT, false>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+      launch_sk<kFmt2, 0, DIRECT, false>(grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
     else if (gs == 64)
-      launch_sk<kFmt4, 64, DIRECT, false>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+      launch_sk<kFmt4, 64, DIRECT, false>(grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
     else
-      launch_sk<kFmt4, 128, DIRECT, false>(grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+      launch_sk<kFmt4, 128, DIRECT, false>(grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
   }
 }
 
@@ -519,20 +554,20 @@ hipError_t launch_split(int fmt, const uint8_t* packed, const __half* delta, con
   const int64_t MG = (batch + kSkBM - 1) / kSkBM * (kSkBM / 16);
   u32x4* xt = reinterpret_cast<u32x4*>(workspace);
   float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + tiled_x_bytes(KC, batch));
-  hipLaunchKernelGGL(k_tile_x, dim3((unsigned)(KC / kTileCols), (unsigned)MG), dim3(256), 0, st, a, batch, KC, MG, xt);
+  hipLaunchKernelGGL(k_tile_x, dim3((unsigned)((KC + kTileCols - 1) / kTileCols), (unsigned)MG), dim3(256), 0, st, a,
+                     batch, KC, MG, xt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nb = (NO / kSkBN) * S;  // blocks in a row of the grid: output tiles x splits
   const int xcd_map = nb % 8 == 0 && (S <= 8 ? (NO / kSkBN) % (8 / S) == 0 : S % 8 == 0);
   const dim3 grid((unsigned)nb, (unsigned)((batch + kSkBM - 1) / kSkBM));
-  const int64_t ks = KC / S;
   void* out = S == 1 ? y : nullptr;
   float* pw = S == 1 ? nullptr : part;
   if (S == 1) {
-    launch_fmt<true, TRANS>(fmt, gs, grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map);
+    launch_fmt<true, TRANS>(fmt, gs, grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map);
     return hipGetLastError();
   }
-  launch_fmt<false, TRANS>(fmt, gs, grid, st, packed, delta, zero, N, K, ks, xt, MG, batch, pw, out, y_dtype, xcd_map);
+  launch_fmt<false, TRANS>(fmt, gs, grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t MN = batch * NO;
@@ -555,9 +590,10 @@ hipError_t launch_gemm_fmt(const uint8_t* packed, const __half* delta, const __h
 }
 
 hipError_t launch_gemm_dx(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
-                          int gs, const __half* dy, int64_t batch, void* dx, int dx_dtype, void* workspace,
+                          int nbits, int gs, const __half* dy, int64_t batch, void* dx, int dx_dtype, void* workspace,
                           hipStream_t st) {
-  return launch_split<true>(kFmt4, packed, delta, zero, N, K, gs, dy, batch, dx, dx_dtype, workspace, st);
+  const int fmt = nbits == 3 ? kFmt3 : nbits == 2 ? kFmt2 : kFmt4;
+  return launch_split<true>(fmt, packed, delta, zero, N, K, gs, dy, batch, dx, dx_dtype, workspace, st);
 }
 
 }  // namespace hqq

@@ -77,10 +77,11 @@ hipError_t launch_gemm_split(const uint8_t* packed, const __half* delta, const _
 hipError_t launch_gemm_fmt(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                            int nbits, int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
                            hipStream_t st);
-// Input gradient dX [batch, K] = dY [batch, N] @ W_hat with the same kernel transposed; its
-// workspace is gemm_workspace_bytes(K, N, batch) (output length first).
+// Input gradient dX [batch, K] = dY [batch, N] @ W_hat with the same kernel transposed (2-, 3-
+// and 4-bit codes, axis-1 groups, group sizes as launch_gemm_fmt); its workspace is
+// gemm_workspace_bytes(K, N, batch) (output length first).
 hipError_t launch_gemm_dx(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
-                          int gs, const __half* dy, int64_t batch, void* dx, int dx_dtype, void* workspace,
+                          int nbits, int gs, const __half* dy, int64_t batch, void* dx, int dx_dtype, void* workspace,
                           hipStream_t st);
 // Fused product with 3-bit codes (axis 1, batch 1-2): shapes it takes, LDS bytes, launch.
 bool gemv_3b_supported(int64_t K, int g);
