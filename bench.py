@@ -242,9 +242,9 @@ def config_legs(a, timed, stream, dev, rotated, read_floor, fan, assign):
     def gemv_leg(name, q, N, K, nbits, g, axis, byt_w):
         ncopy = max(4, int(np.ceil(1.1e9 / byt_w)))
         copies = [(q.packed.clone(), q.delta.clone(), q.zero.clone()) for _ in range(ncopy)]
-        X = torch.from_numpy(synth.activations(2, K, 402)).to(dev)
+        X = torch.from_numpy(synth.activations(8, K, 402)).to(dev)
         legs["%s_read_floor" % name] = read_floor(copies)
-        for b in (1, 2):
+        for b in ((1, 2, 8) if axis == 0 else (1, 2)):
             Y = torch.empty((b, N), dtype=torch.float16, device=dev)
 
             def gv(r, b=b, Y=Y):

@@ -347,11 +347,13 @@ int hqq_gemm_dx(const void* packed, const void* delta_fp16, const void* zero_fp1
  *   delta_fp16, zero_fp16  in  fp16, one per group in group-view order.
  *   x_fp16      in  fp16 [batch, K];  y out [batch, N], y_dtype HQQ_OUT_F16 or HQQ_OUT_F32.
  * Supported: nbits=4 axis=1 (as hqq_gemv_w4a16); nbits=4 axis=0 with group_size 16..256,
- * K a multiple of 32, batch 1 or 2, K <= 16384; nbits=2 axis=1 group_size 16 with N a
- * multiple of 16, K a multiple of 64, batch 1 or 2, K <= 16384; nbits=3 axis=1 with
- * group_size 16..256, N a multiple of 4, 40 <= K <= 8192, batch 1 or 2 (rows start inside the
- * ten-code words).  Other combinations return HQQ_ERR_UNSUPPORTED.  Codes stay exact
- * (fp16 subnormals into v_dot2_f32_f16); fp32 sums.
+ * K a multiple of 32, batch 1 or 2, K <= 16384, or batch 3..8 with K a multiple of 128 (the
+ * MFMA unit; any K); nbits=2 axis=1 group_size 16 with N a multiple of 16, K a multiple of
+ * 64, batch 1 or 2, K <= 16384; nbits=3 axis=1 with group_size 16..256, N a multiple of 4,
+ * 40 <= K <= 8192, batch 1 or 2 (rows start inside the ten-code words).  Other combinations
+ * return HQQ_ERR_UNSUPPORTED.  Codes stay exact (fp16 subnormals into v_dot2_f32_f16 or
+ * v_mfma_f32_16x16x32_f16); fp32 sums.  Axis 0 forms a = x * delta of the weight's
+ * metadata row in fp16 (one rounding) and subtracts sum_k a z.
  */
 int hqq_gemv(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K, int nbits,
              int group_size, int axis, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* stream);

@@ -57,6 +57,17 @@ def test_axis0_4bit(g, N, K):
     _check(N, K, 4, g, 0, (1, 2), seed=1000 + g + K)
 
 
+# batch 3..8 (MFMA): one and two 16-row strips per block, one to five 2048-code segments and a
+# ragged last segment (K = 1152, 10240)
+AX0_MF_CASES = [(16, 64, 128), (32, 128, 1152), (64, 256, 2048), (128, 512, 4096), (256, 512, 8192),
+                (128, 256, 10240)]
+
+
+@pytest.mark.parametrize("g,N,K", AX0_MF_CASES, ids=lambda v: str(v))
+def test_axis0_4bit_batched(g, N, K):
+    _check(N, K, 4, g, 0, (3, 4, 5, 6, 7, 8), seed=1100 + g + K)
+
+
 SHAPES_2B = [(16, 64), (48, 192), (64, 4160), (256, 4096), (32, 16384)]
 
 
@@ -85,10 +96,10 @@ def test_3bit_full_shape():
 
 
 def test_axis0_full_shape():
-    """The 70B-MLP shape of the axis-0 quantizer workload: 28672 x 8192, g = 128."""
+    """The 70B-MLP shape of the axis-0 quantizer workload: 28672 x 8192, g = 128, batch 1 and 8."""
     N, K = 28672, 8192
     sel = np.sort(np.random.default_rng(7).choice(N, 384, replace=False))
-    _check(N, K, 4, 128, 0, (1,), seed=3001, rows_sel=sel)
+    _check(N, K, 4, 128, 0, (1, 8), seed=3001, rows_sel=sel)
 
 
 def test_2bit_full_shape():
@@ -109,8 +120,12 @@ def test_unsupported_formats_rejected():
             hq.hqq_gemv(pk, md, md, 64, 128, nbits, g, axis, x)
     with pytest.raises(hq.HQQError):  # 3-bit rows shorter than 40 codes
         hq.hqq_gemv(pk, md, md, 64, 32, 3, 16, 1, x[:, :32].contiguous())
-    with pytest.raises(hq.HQQError):  # batch 3 is not fused for these formats
-        hq.hqq_gemv(pk, md, md, 64, 128, 4, 16, 0, torch.zeros((3, 128), dtype=torch.float16, device="cuda"))
+    with pytest.raises(hq.HQQError):  # batch 3 is not fused for 3-bit codes
+        hq.hqq_gemv(pk, md, md, 64, 128, 3, 16, 1, torch.zeros((3, 128), dtype=torch.float16, device="cuda"))
+    with pytest.raises(hq.HQQError):  # nor batch 9 for axis-0 codes
+        hq.hqq_gemv(pk, md, md, 64, 128, 4, 16, 0, torch.zeros((9, 128), dtype=torch.float16, device="cuda"))
+    with pytest.raises(hq.HQQError):  # axis 0, batch 3..8: K a multiple of 128
+        hq.hqq_gemv(pk, md, md, 64, 96, 4, 16, 0, torch.zeros((4, 96), dtype=torch.float16, device="cuda"))
 
 
 # ---------------------------------------------------------------- batched product (hqq_gemm)

@@ -533,8 +533,9 @@ int hqq_gemv(const void* packed, const void* delta_fp16, const void* zero_fp16, 
   if (!packed || !delta_fp16 || !zero_fp16 || !x_fp16 || !y) return fail(HQQ_ERR_INVALID_ARGUMENT, "null buffer");
   if (!aligned16(packed) || !aligned16(delta_fp16) || !aligned16(zero_fp16) || !aligned16(x_fp16) || !aligned16(y))
     return fail(HQQ_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
-  if (batch > 2) return fail(HQQ_ERR_UNSUPPORTED, "batch must be 1 or 2 for this format");
-  if (K > 16384) return fail(HQQ_ERR_UNSUPPORTED, "K must be at most 16384 for this format");
+  if (batch > (nbits == 4 ? 8 : 2))
+    return fail(HQQ_ERR_UNSUPPORTED, "batch must be at most 8 for axis-0 4-bit codes and 1 or 2 for 3/2-bit codes");
+  if (batch <= 2 && K > 16384) return fail(HQQ_ERR_UNSUPPORTED, "K must be at most 16384 for this format");
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint8_t* pk = reinterpret_cast<const uint8_t*>(packed);
   const __half* dl = reinterpret_cast<const __half*>(delta_fp16);
@@ -544,6 +545,8 @@ int hqq_gemv(const void* packed, const void* delta_fp16, const void* zero_fp16, 
   if (nbits == 4 && axis == 0) {
     if (!pow2_group(group_size)) return fail(HQQ_ERR_UNSUPPORTED, "group_size must be 16, 32, 64, 128 or 256");
     if (K % 32 != 0) return fail(HQQ_ERR_UNSUPPORTED, "K must be a multiple of 32");
+    if (batch > 2 && K % 128 != 0) return fail(HQQ_ERR_UNSUPPORTED, "batch 3-8: K must be a multiple of 128");
+    if (hqq::gemv_ax0_lds_bytes(K, batch) > 160 * 1024) return fail(HQQ_ERR_UNSUPPORTED, "LDS too large");
     e = hqq::launch_gemv_ax0(pk, dl, zr, N, K, group_size, xx, batch, y, y_dtype, st);
   } else if (nbits == 3 && axis == 1) {
     if (!hqq::gemv_3b_supported(K, group_size))

@@ -7,6 +7,8 @@
 // Both run on the vector ALUs with v_dot2_f32_f16 on exact codes (fp16 subnormals, as in the
 // 4-bit kernels) and stream whole weight rows, 1 KB per load instruction.
 
+#include <type_traits>
+
 #include "hqq_gemv_common.h"
 
 namespace hqq {
@@ -183,6 +185,202 @@ __global__ void __launch_bounds__(64 * kAx0Waves) k_gemv_ax0(const uint8_t* __re
           store_y<HQQ_OUT_F32>(y, (int64_t)b * N + n, v);
       }
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Axis 0, 4-bit, batch 3..8, on the MFMA unit.  The same factorisation as k_gemv_ax0 (a block
+// takes RB = 16 SPB of the g weight rows of one metadata row r0, a = x delta[r0] in fp16, the
+// zero term sum_k a z[r0, k] from the same staged values), with the segment pipeline of the
+// 4-bit batch 3-8 kernel: 16 waves, K in segments of 2048 codes, wave w always takes the
+// 128-code chunk w of a segment; per segment the block stages a (unpack slot order, 1/16 on
+// the odd codes) and the packed rows (1 KB of one row per load instruction) in LDS, double
+// buffered, the loads two segments ahead in registers, one LDS-only barrier per segment.
+// The codes stay exact (fp16 subnormals into v_mfma_f32_16x16x32_f16) and there is no
+// per-group step inside a row, so each wave's MFMAs chain over the whole row:
+//   y[b, n] = 2^24 sum_w P_w[b, n] - sum_k a[b, k] z[r0, k],
+// the 16 waves' sums added in wave order, the zero term in a fixed tree (deterministic).
+// ------------------------------------------------------------------------------------------
+constexpr int kM0Waves = 16;
+constexpr int kM0KS = 128 * kM0Waves;   // codes per segment
+constexpr int kM0KSP = kM0KS + 8;       // LDS row stride of a (halves)
+constexpr int kM0WRB = kM0KS / 2 + 16;  // LDS row stride of the packed codes (bytes)
+
+__host__ __device__ constexpr int mf0_stage_bytes(int B, int SPB) { return B * kM0KSP * 2 + 16 * SPB * kM0WRB; }
+
+template <int B, int SPB, int NSEG>
+__global__ void __launch_bounds__(64 * kM0Waves) k_gemv_mf0(const uint8_t* __restrict__ packed,
+                                                           const __half* __restrict__ delta,
+                                                           const __half* __restrict__ zero, int64_t N, int64_t K,
+                                                           int g, int subsets, int out_dtype,
+                                                           const __half* __restrict__ x, void* __restrict__ y) {
+  static_assert(B >= 1 && B <= 8 && (SPB == 1 || SPB == 2), "shape");
+  constexpr int NT = 64 * kM0Waves, RB = 16 * SPB;
+  constexpr int XB = B * (kM0KS / 8);      // 16-byte blocks of x (and of a) per segment
+  constexpr int XR = (XB + NT - 1) / NT;   // of them per thread
+  constexpr int STAGE = mf0_stage_bytes(B, SPB);
+  extern __shared__ __align__(16) uint8_t lds_raw[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 4, nl = lane & 15;
+  const int arow = nl < B ? nl : 0;  // A rows >= B only feed outputs that are never stored
+  const int64_t R0 = N / g, r0 = blockIdx.x / subsets;
+  const int64_t i0 = (int64_t)(blockIdx.x % subsets) * RB;  // rows n = r0 + R0 (i0 + row)
+  const __half* drow = delta + r0 * K;
+  const __half* zrow = zero + r0 * K;
+  const int64_t nchunks = K / 128;
+  const int nseg = NSEG > 0 ? NSEG : (int)((K + kM0KS - 1) / kM0KS);
+
+  auto as_of = [&](int buf) { return reinterpret_cast<_Float16*>(lds_raw + buf * STAGE); };
+  auto wl_of = [&](int buf) { return lds_raw + buf * STAGE + B * kM0KSP * 2; };
+
+  struct Regs {
+    uint4 xr[XR], dr[XR], zr[XR];
+    uint4 wr[SPB];
+  };
+  auto load_seg = [&](int sg, Regs& r) {
+    const int64_t kb0 = (int64_t)sg * kM0KS;
+    const int valid = (int)((K - kb0 < kM0KS) ? (K - kb0) : kM0KS);  // a multiple of 128
+#pragma unroll
+    for (int j = 0; j < XR; ++j) {
+      const int idx = min(tid + NT * j, XB - 1);
+      const int m = idx / (kM0KS / 8), kb = min(idx % (kM0KS / 8), valid / 8 - 1);
+      r.xr[j] = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + kb0 + 8 * kb);
+      r.dr[j] = *reinterpret_cast<const uint4*>(drow + kb0 + 8 * kb);
+      r.zr[j] = *reinterpret_cast<const uint4*>(zrow + kb0 + 8 * kb);
+    }
+#pragma unroll
+    for (int j = 0; j < SPB; ++j) {
+      const int row = wave + kM0Waves * j;
+      const int piece = min(lane, valid / 32 - 1);
+      r.wr[j] = ld_stream16(packed + (r0 + R0 * (i0 + row)) * (K / 2) + kb0 / 2 + 16 * piece);
+    }
+  };
+  // a = x delta -> LDS stage `buf`; the zero term of the thread's blocks into zacc
+  float zacc[XR];
+#pragma unroll
+  for (int j = 0; j < XR; ++j) zacc[j] = 0.f;
+  auto stage_seg = [&](int sg, int buf, const Regs& r) {
+    const int64_t kb0 = (int64_t)sg * kM0KS;
+    const int valid = (int)((K - kb0 < kM0KS) ? (K - kb0) : kM0KS);
+    _Float16* as = as_of(buf);
+#pragma unroll
+    for (int j = 0; j < XR; ++j) {
+      const int idx = tid + NT * j;
+      if (idx < XB) {  // uniform per wave (XB is a multiple of 256)
+        const int m = idx / (kM0KS / 8), kb = idx % (kM0KS / 8);
+        const unsigned xu[4] = {r.xr[j].x, r.xr[j].y, r.xr[j].z, r.xr[j].w};
+        const unsigned du[4] = {r.dr[j].x, r.dr[j].y, r.dr[j].z, r.dr[j].w};
+        unsigned au[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f16x2 xv = as_h2(xu[q]), dv = as_h2(du[q]);
+          au[q] = as_u(f16x2{(_Float16)((float)xv[0] * (float)dv[0]), (_Float16)((float)xv[1] * (float)dv[1])});
+        }
+        uint4 o = perm_slots(make_uint4(au[0], au[1], au[2], au[3]));
+        o.y = as_u(as_h2(o.y) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
+        o.w = as_u(as_h2(o.w) * f16x2{(_Float16)0.0625f, (_Float16)0.0625f});
+        *reinterpret_cast<uint4*>(as + m * kM0KSP + 8 * kb) = o;
+        // zero term from the staged values: slot order [k0, k4, k1, k5, k2, k6, k3, k7], odd x 16
+        const uint4 zp = perm_slots(r.zr[j]);
+        const unsigned ou[4] = {o.x, o.y, o.z, o.w}, zq[4] = {zp.x, zp.y, zp.z, zp.w};
+        float zt = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sc = (q & 1) ? 16.f : 1.f;
+          zt = fmaf((float)as_h2(ou[q])[0] * sc, (float)as_h2(zq[q])[0], zt);
+          zt = fmaf((float)as_h2(ou[q])[1] * sc, (float)as_h2(zq[q])[1], zt);
+        }
+        if (8 * kb < valid) zacc[j] += zt;
+      }
+    }
+    uint8_t* wl = wl_of(buf);
+#pragma unroll
+    for (int j = 0; j < SPB; ++j)
+      *reinterpret_cast<uint4*>(wl + (wave + kM0Waves * j) * kM0WRB + 16 * lane) = r.wr[j];
+  };
+
+  f32x4 acc[SPB];
+#pragma unroll
+  for (int sp = 0; sp < SPB; ++sp) acc[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Regs rs[2];
+  load_seg(0, rs[0]);
+  if (NSEG != 1) load_seg(min(1, nseg - 1), rs[1]);
+  stage_seg(0, 0, rs[0]);
+  if (NSEG == 0 || NSEG > 2) load_seg(min(2, nseg - 1), rs[0]);
+  lds_barrier();
+  // one segment: stage `cur` + 1 (requested two segments earlier) into the other stage, refill
+  // that register set with `cur` + 3, multiply `cur`; one LDS-only barrier
+  auto segment = [&](const int cur, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    if (cur + 1 < nseg) stage_seg(cur + 1, buf ^ 1, rs[buf ^ 1]);
+    if (NSEG == 0 || cur + 3 < NSEG) load_seg(min(cur + 3, nseg - 1), rs[buf ^ 1]);
+    const int64_t c = (int64_t)cur * kM0Waves + wave;  // this wave's chunk
+    if (c < nchunks) {
+      const _Float16* as = as_of(buf);
+      const uint8_t* wl = wl_of(buf);
+      // lane group h holds codes 32 h .. 32 h + 31 of the chunk, dword t codes 8 t .. 8 t + 7
+      f16x8 A[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        A[t] = *reinterpret_cast<const f16x8*>(as + arow * kM0KSP + wave * 128 + h * 32 + t * 8);
+#pragma unroll
+      for (int sp = 0; sp < SPB; ++sp) {
+        const uint4 v = *reinterpret_cast<const uint4*>(wl + (16 * sp + nl) * kM0WRB + wave * 64 + h * 16);
+        const unsigned dd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[sp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t], unpack8_sub(dd[t]), acc[sp], 0, 0, 0);
+      }
+    }
+    lds_barrier();
+  };
+  if constexpr (NSEG > 0) {
+#pragma unroll
+    for (int cur = 0; cur < NSEG; ++cur) {
+      if (cur % 2 == 0)
+        segment(cur, std::integral_constant<int, 0>{});
+      else
+        segment(cur, std::integral_constant<int, 1>{});
+    }
+  } else {
+    for (int cur = 0; cur < nseg; cur += 2) {
+      segment(cur, std::integral_constant<int, 0>{});
+      if (cur + 1 < nseg) segment(cur + 1, std::integral_constant<int, 1>{});
+    }
+  }
+  // ---- the 16 waves' sums of each output in wave order, the zero term in a fixed tree (the
+  //      wave's 64 lanes, then the four waves of a batch row); stage memory reused
+  float* red = reinterpret_cast<float*>(lds_raw);  // [SPB][16 waves][B][16]
+  float* redz = red + SPB * kM0Waves * B * 16;      // [XR][16 waves]
+#pragma unroll
+  for (int sp = 0; sp < SPB; ++sp)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * h + r;
+      if (m < B) red[((sp * kM0Waves + wave) * B + m) * 16 + nl] = acc[sp][r];
+    }
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const float v = wave_sum(zacc[j]);
+    if (lane == 0) redz[j * kM0Waves + wave] = v;
+  }
+  lds_barrier();
+  if (tid < SPB * B * 16) {
+    const int sp = tid / (B * 16), m = (tid / 16) % B, col = tid % 16;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kM0Waves; ++w) sum += red[((sp * kM0Waves + w) * B + m) * 16 + col];
+    // batch row m: blocks idx = tid + NT j with idx / 256 = m, i.e. j = m / 4, waves 4 (m % 4) + 0..3
+    const float* zw = redz + (m / 4) * kM0Waves + 4 * (m % 4);
+    const float zb = (zw[0] + zw[1]) + (zw[2] + zw[3]);
+    const float v = sum * kSubScale - zb;
+    const int64_t n = r0 + R0 * (i0 + 16 * sp + col);
+    if (out_dtype == HQQ_OUT_F16)
+      store_y<HQQ_OUT_F16>(y, (int64_t)m * N + n, v);
+    else
+      store_y<HQQ_OUT_F32>(y, (int64_t)m * N + n, v);
   }
 }
 
@@ -686,13 +884,55 @@ hipError_t launch_gemv_3b(const uint8_t* packed, const __half* delta, const __ha
                     : b3_j<2>(pk, delta, zero, N, K, gl, x, y, y_dtype, st);
 }
 
-size_t gemv_ax0_lds_bytes(int64_t K, int64_t batch) { return ax0_lds_bytes((int)batch, K); }
+// axis 0, batch 3..8: two strips per block where g and the block count allow
+inline int mf0_strips(int64_t N, int g) { return (g % 32 == 0 && (N / g) * (g / 32) >= 256) ? 2 : 1; }
+
+template <int B, int SPB, int NSEG>
+hipError_t mf0_launch(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
+                      const __half* x, void* y, int y_dtype, hipStream_t st) {
+  const int subsets = g / (16 * SPB);
+  hipLaunchKernelGGL((k_gemv_mf0<B, SPB, NSEG>), dim3((unsigned)((N / g) * subsets)), dim3(64 * kM0Waves),
+                     2 * mf0_stage_bytes(B, SPB), st, packed, delta, zero, N, K, g, subsets, y_dtype, x, y);
+  return hipGetLastError();
+}
+
+template <int B, int SPB>
+hipError_t mf0_seg(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
+                   const __half* x, void* y, int y_dtype, hipStream_t st) {
+  switch ((K + kM0KS - 1) / kM0KS) {
+    case 1: return mf0_launch<B, SPB, 1>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 2: return mf0_launch<B, SPB, 2>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 3: return mf0_launch<B, SPB, 3>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 4: return mf0_launch<B, SPB, 4>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    default: return mf0_launch<B, SPB, 0>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+  }
+}
+
+template <int B>
+hipError_t mf0_b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
+                 const __half* x, void* y, int y_dtype, hipStream_t st) {
+  return mf0_strips(N, g) == 2 ? mf0_seg<B, 2>(packed, delta, zero, N, K, g, x, y, y_dtype, st)
+                               : mf0_seg<B, 1>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+}
+
+size_t gemv_ax0_lds_bytes(int64_t K, int64_t batch) {
+  return batch <= 2 ? ax0_lds_bytes((int)batch, K) : 2 * (size_t)mf0_stage_bytes((int)batch, 2);
+}
 size_t gemv_2b_lds_bytes(int64_t K, int64_t batch) { return lds_2b((int)batch, K); }
 
 hipError_t launch_gemv_ax0(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                            int g, const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t st) {
-  return batch == 1 ? ax0_b<1>(packed, delta, zero, N, K, g, x, y, y_dtype, st)
-                    : ax0_b<2>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+  switch (batch) {
+    case 1: return ax0_b<1>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 2: return ax0_b<2>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 3: return mf0_b<3>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 4: return mf0_b<4>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 5: return mf0_b<5>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 6: return mf0_b<6>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 7: return mf0_b<7>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 8: return mf0_b<8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gemv_2b(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
