@@ -255,36 +255,36 @@ def config_legs(a, timed, stream, dev, rotated, read_floor, fan, assign):
             legs["%s_b%d" % (name, b)] = {"us": tg * 1e6, "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM,
                                           "bytes": byt, "shape": [N, K], "copies_rotated": ncopy,
                                           "frac_of_read_floor": legs["%s_read_floor" % name]["us"] / (tg * 1e6)}
-        if axis == 1:  # the batched product over the same format at batch 8 and 256 (hqq_gemm)
-            for B in (8, 256):
-                X2 = torch.from_numpy(synth.activations(B, K, 403)).to(dev)
-                Y = torch.empty((B, N), dtype=torch.float16, device=dev)
-                ws = torch.empty(hq.hqq_gemm_workspace_bytes(N, K, B), dtype=torch.uint8, device=dev)
+        # the batched product over the same format at batch 8 and 256 (hqq_gemm)
+        for B in (8, 256):
+            X2 = torch.from_numpy(synth.activations(B, K, 403)).to(dev)
+            Y = torch.empty((B, N), dtype=torch.float16, device=dev)
+            ws = torch.empty(hq.hqq_gemm_workspace_bytes(N, K, B), dtype=torch.uint8, device=dev)
 
-                def gm(r, X2=X2, Y=Y, ws=ws):
-                    pk, d, z = copies[r % ncopy]
-                    hq.hqq_gemm(pk, d, z, N, K, nbits, g, axis, X2, out=Y, workspace=ws)
-                tg = timed(gm, 2 * ncopy)
-                fl = 2.0 * B * N * K
-                byt = byt_w + 2 * B * K + 2 * B * N
-                legs["%s_b%d" % (name.replace("gemv", "gemm"), B)] = {
-                    "us": tg * 1e6, "TFLOP/s": fl / tg / 1e12, "frac_mfma_f16": fl / tg / PEAK_FP16_MFMA,
-                    "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM, "shape": [N, K], "copies_rotated": ncopy}
-                del X2, ws
-            # the input gradient dX = dY W_hat at batch 256 (hqq_gemm_dx)
-            DY = torch.from_numpy(synth.activations(256, N, 404)).to(dev)
-            DX = torch.empty((256, K), dtype=torch.float16, device=dev)
-            ws = torch.empty(hq.hqq_gemm_dx_workspace_bytes(N, K, 256), dtype=torch.uint8, device=dev)
-
-            def gdx(r):
+            def gm(r, X2=X2, Y=Y, ws=ws):
                 pk, d, z = copies[r % ncopy]
-                hq.hqq_gemm_dx(pk, d, z, N, K, nbits, g, axis, DY, out=DX, workspace=ws)
-            tg = timed(gdx, 2 * ncopy)
-            fl = 2.0 * 256 * N * K
-            legs["%s_b256" % name.replace("gemv", "dx")] = {
+                hq.hqq_gemm(pk, d, z, N, K, nbits, g, axis, X2, out=Y, workspace=ws)
+            tg = timed(gm, 2 * ncopy)
+            fl = 2.0 * B * N * K
+            byt = byt_w + 2 * B * K + 2 * B * N
+            legs["%s_b%d" % (name.replace("gemv", "gemm"), B)] = {
                 "us": tg * 1e6, "TFLOP/s": fl / tg / 1e12, "frac_mfma_f16": fl / tg / PEAK_FP16_MFMA,
-                "shape": [N, K], "copies_rotated": ncopy}
-            del DY, DX, ws
+                "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM, "shape": [N, K], "copies_rotated": ncopy}
+            del X2, ws
+        # the input gradient dX = dY W_hat at batch 256 (hqq_gemm_dx)
+        DY = torch.from_numpy(synth.activations(256, N, 404)).to(dev)
+        DX = torch.empty((256, K), dtype=torch.float16, device=dev)
+        ws = torch.empty(hq.hqq_gemm_dx_workspace_bytes(N, K, 256), dtype=torch.uint8, device=dev)
+
+        def gdx(r):
+            pk, d, z = copies[r % ncopy]
+            hq.hqq_gemm_dx(pk, d, z, N, K, nbits, g, axis, DY, out=DX, workspace=ws)
+        tg = timed(gdx, 2 * ncopy)
+        fl = 2.0 * 256 * N * K
+        legs["%s_b256" % name.replace("gemv", "dx")] = {
+            "us": tg * 1e6, "TFLOP/s": fl / tg / 1e12, "frac_mfma_f16": fl / tg / PEAK_FP16_MFMA,
+            "shape": [N, K], "copies_rotated": ncopy}
+        del DY, DX, ws
         del copies
 
     log("config legs: 3-bit and 2-bit layer sets")

@@ -289,16 +289,19 @@ int hqq_gemm_w4a16(const void* packed, const void* delta_fp16, const void* zero_
 
 /*
  * The batched product for the other stored formats ("为什么一定要分组" for the containers,
- * "从压缩文件到一次前向" for the product): y = x @ W_hat^T as hqq_gemm_w4a16, for codes of
- * nbits = 2, 3 or 4 with axis-1 groups, stored as hqq_quantize wrote them.
+ * "从压缩文件到一次前向" for the product, "`axis` 不是一个无关紧要的开关" for axis 0):
+ * y = x @ W_hat^T as hqq_gemm_w4a16, for codes of nbits = 2, 3 or 4 with axis-1 groups and
+ * 4-bit codes with axis-0 groups, stored as hqq_quantize wrote them.
  *   packed, delta_fp16, zero_fp16, N, K, nbits, group_size, axis  as hqq_gemv.
  *   x_fp16, batch, y, y_dtype  as hqq_gemm_w4a16.
  *   workspace   at least hqq_gemm_workspace_bytes(N, K, batch) bytes, as hqq_gemm_w4a16.
  * The same split MFMA kernel: only the weight tile's staging depends on the format (ten
- * 3-bit codes per word, rows starting inside words; four 2-bit codes per byte).  N a multiple
- * of 128, K of 256; group_size 64 or 128 for 4-bit codes (the hqq_gemm_w4a16 path), a power of
- * two 16..256 for 2/3-bit codes; axis 0 and other shapes return HQQ_ERR_UNSUPPORTED.  Any
- * batch >= 1 (batches 1 and 2 are cheaper through hqq_gemv).
+ * 3-bit codes per word, rows starting inside words; four 2-bit codes per byte; axis 0: each
+ * code with the step and zero of metadata row n mod (N/g) at its column).  N a multiple of
+ * 128, K of 256; group_size 64 or 128 for 4-bit axis-1 codes (the hqq_gemm_w4a16 path), a
+ * power of two 16..256 for 2/3-bit and axis-0 codes; 2/3-bit codes with axis 0 and other
+ * shapes return HQQ_ERR_UNSUPPORTED.  Any batch >= 1 (batches up to 2, or 8 for axis-0 codes,
+ * are cheaper through hqq_gemv).
  */
 int hqq_gemm(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K, int nbits,
              int group_size, int axis, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* workspace,
@@ -323,15 +326,15 @@ int hqq_gemm_w4a16_dx(const void* packed, const void* delta_fp16, const void* ze
 
 /*
  * The input gradient for the other stored formats ("从压缩文件到一次前向" for the product,
- * "为什么一定要分组" for the containers): dX = dY @ W_hat as hqq_gemm_w4a16_dx, for codes of
- * nbits = 2, 3 or 4 with axis-1 groups, stored as hqq_quantize wrote them.
+ * "为什么一定要分组" for the containers): dX = dY @ W_hat as hqq_gemm_w4a16_dx, for the formats
+ * of hqq_gemm (2-, 3- and 4-bit codes with axis-1 groups, 4-bit codes with axis-0 groups).
  *   packed, delta_fp16, zero_fp16, N, K, nbits, group_size, axis  as hqq_gemm.
  *   dy_fp16, batch, dx, dx_dtype  as hqq_gemm_w4a16_dx.
  *   workspace   at least hqq_gemm_dx_workspace_bytes(N, K, batch) bytes, as hqq_gemm_w4a16.
  * The transposed split kernel: each staging thread unpacks 32 codes of two weight rows (ten
  * 3-bit codes per word, four 2-bit codes per byte) and writes them column-major into the LDS
- * tile.  K a multiple of 128, N of 256; group_size 64 or 128 for 4-bit codes, a power of two
- * 16..256 for 2/3-bit codes; axis 0 and other shapes return HQQ_ERR_UNSUPPORTED.
+ * tile.  K a multiple of 128, N of 256; group sizes as hqq_gemm; 2/3-bit codes with axis 0
+ * and other shapes return HQQ_ERR_UNSUPPORTED.
  */
 int hqq_gemm_dx(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K, int nbits,
                 int group_size, int axis, const void* dy_fp16, int64_t batch, void* dx, int dx_dtype, void* workspace,

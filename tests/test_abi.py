@@ -119,8 +119,10 @@ def test_batched_products_reject(lib):
     assert call(nbits=5) == hq.HQQ_ERR_INVALID_ARGUMENT
     assert call(axis=2) == hq.HQQ_ERR_INVALID_ARGUMENT
     assert call(gs=48) == hq.HQQ_ERR_INVALID_ARGUMENT          # does not divide K
-    assert call(axis=0) == hq.HQQ_ERR_UNSUPPORTED
-    assert call(nbits=4, gs=32) == hq.HQQ_ERR_UNSUPPORTED      # 4-bit: 64 or 128
+    assert call(axis=0) == hq.HQQ_ERR_UNSUPPORTED              # axis 0 only at 4 bits
+    assert call(nbits=4, gs=32) == hq.HQQ_ERR_UNSUPPORTED      # 4-bit axis 1: 64 or 128
+    assert call(nbits=4, axis=0, gs=8, N=256) == hq.HQQ_ERR_UNSUPPORTED   # axis 0: 16..256
+    assert call(nbits=4, axis=0, gs=64, N=96) == hq.HQQ_ERR_INVALID_ARGUMENT  # g must divide N
     assert call(nbits=2, gs=512) == hq.HQQ_ERR_UNSUPPORTED
     assert call(N=192) == hq.HQQ_ERR_UNSUPPORTED               # N % 128
     assert call(K=640) == hq.HQQ_ERR_UNSUPPORTED               # K % 256
@@ -143,7 +145,8 @@ def test_batched_products_reject(lib):
         return gdx(FAKE, FAKE, FAKE, a["N"], a["K"], a["nbits"], a["gs"], a["axis"], FAKE, a["batch"], FAKE,
                    a["ydt"], FAKE, a["wsb"], None)
     assert call_dx(nbits=1) == hq.HQQ_ERR_INVALID_ARGUMENT
-    assert call_dx(axis=0) == hq.HQQ_ERR_UNSUPPORTED
+    assert call_dx(axis=0) == hq.HQQ_ERR_UNSUPPORTED           # axis 0 only at 4 bits
+    assert call_dx(nbits=4, axis=0, gs=512) == hq.HQQ_ERR_UNSUPPORTED
     assert call_dx(gs=48) == hq.HQQ_ERR_INVALID_ARGUMENT      # does not divide K
     assert call_dx(nbits=4, gs=32) == hq.HQQ_ERR_UNSUPPORTED
     assert call_dx(nbits=2, gs=8) == hq.HQQ_ERR_UNSUPPORTED

@@ -138,22 +138,23 @@ GEMM_CASES = [(3, 64, 128, 512, 3), (3, 16, 256, 1024, 9), (3, 32, 384, 2048, 10
               (3, 64, 128, 1280, 20), (2, 16, 256, 768, 70), (4, 64, 256, 768, 40), (4, 128, 128, 256, 9)]
 
 
-def _check_gemm(nbits, g, N, K, batch, seed, rows_sel=None):
+def _check_gemm(nbits, g, N, K, batch, seed, rows_sel=None, axis=1):
     torch = torch_dev()
     import weight_only_quantization_amd as hq
     o = oracle.get()
-    packed, delta, zero = _operands(seed, N, K, nbits, g, 1)
+    packed, delta, zero = _operands(seed, N, K, nbits, g, axis)
     x = np.random.default_rng(seed + 1).normal(0, 1, (batch, K)).astype(np.float16)
-    yr = o.gemv_fmt(packed, delta.astype(np.float64), zero.astype(np.float64), N, K, nbits, g, 1,
+    yr = o.gemv_fmt(packed, delta.astype(np.float64), zero.astype(np.float64), N, K, nbits, g, axis,
                     x.astype(np.float64), rows_sel=rows_sel)
     scale = np.maximum(np.abs(yr), np.sqrt(np.mean(yr ** 2)))
     pk, dl, zr = (torch.from_numpy(a).cuda() for a in (packed, delta, zero))
     for out_dtype in (torch.float32, torch.float16):
-        y = hq.hqq_gemm(pk, dl, zr, N, K, nbits, g, 1, torch.from_numpy(x).cuda(),
+        y = hq.hqq_gemm(pk, dl, zr, N, K, nbits, g, axis, torch.from_numpy(x).cuda(),
                         out_dtype=out_dtype).float().cpu().numpy().astype(np.float64)
         yg = y if rows_sel is None else y[:, rows_sel]
         err = float(np.max(np.abs(yg - yr) / scale))
-        say("  gemm N=%d K=%d b%d g%d batch=%d %s: max rel err %.3g" % (N, K, nbits, g, batch, out_dtype, err))
+        say("  gemm N=%d K=%d b%d g%d axis%d batch=%d %s: max rel err %.3g" % (N, K, nbits, g, axis, batch, out_dtype,
+                                                                             err))
         assert err <= GEMV_TOL
 
 
@@ -178,6 +179,7 @@ def test_gemm_formats_rejected():
     md = torch.zeros(1 << 14, dtype=torch.float16, device="cuda")
     x = torch.zeros((4, 512), dtype=torch.float16, device="cuda")
     for nbits, g, axis, N, K in ((3, 64, 0, 128, 512), (4, 32, 1, 128, 512), (2, 16, 1, 64, 512), (3, 16, 1, 128, 384),
+                                 (4, 512, 0, 512, 256), (4, 8, 0, 128, 512), (4, 64, 0, 64, 512),
                                  (2, 512, 1, 128, 512), (5, 64, 1, 128, 512)):
         with pytest.raises(hq.HQQError):
             hq.hqq_gemm(pk, md, md, N, K, nbits, g, axis, x[:, :K].contiguous())
@@ -192,21 +194,22 @@ DX_CASES = [(3, 64, 512, 128, 3), (3, 16, 256, 384, 9), (3, 32, 768, 256, 100), 
             (2, 256, 256, 512, 17), (4, 64, 768, 256, 33), (4, 128, 512, 384, 3)]
 
 
-def _check_dx(nbits, g, N, K, batch, seed, cols_sel=None):
+def _check_dx(nbits, g, N, K, batch, seed, cols_sel=None, axis=1):
     torch = torch_dev()
     import weight_only_quantization_amd as hq
     o = oracle.get()
-    packed, delta, zero = _operands(seed, N, K, nbits, g, 1)
+    packed, delta, zero = _operands(seed, N, K, nbits, g, axis)
     dy = np.random.default_rng(seed + 1).normal(0, 1, (batch, N)).astype(np.float16)
-    ref = o.gemv_t(packed, delta, zero, N, K, nbits, g, 1, dy.astype(np.float64), cols_sel=cols_sel)
+    ref = o.gemv_t(packed, delta, zero, N, K, nbits, g, axis, dy.astype(np.float64), cols_sel=cols_sel)
     scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref ** 2)))
     pk, dl, zr = (torch.from_numpy(a).cuda() for a in (packed, delta, zero))
     for out_dtype in (torch.float32, torch.float16):
-        dx = hq.hqq_gemm_dx(pk, dl, zr, N, K, nbits, g, 1, torch.from_numpy(dy).cuda(),
+        dx = hq.hqq_gemm_dx(pk, dl, zr, N, K, nbits, g, axis, torch.from_numpy(dy).cuda(),
                             out_dtype=out_dtype).float().cpu().numpy().astype(np.float64)
         dxg = dx if cols_sel is None else dx[:, cols_sel]
         err = float(np.max(np.abs(dxg - ref) / scale))
-        say("  dx N=%d K=%d b%d g%d batch=%d %s: max rel err %.3g" % (N, K, nbits, g, batch, out_dtype, err))
+        say("  dx N=%d K=%d b%d g%d axis%d batch=%d %s: max rel err %.3g" % (N, K, nbits, g, axis, batch, out_dtype,
+                                                                           err))
         assert err <= GEMV_TOL
 
 
@@ -248,6 +251,49 @@ def test_gemm_dx_formats_rejected():
     pk = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
     md = torch.zeros(1 << 14, dtype=torch.float16, device="cuda")
     for nbits, g, axis, N, K in ((3, 64, 0, 512, 128), (4, 32, 1, 512, 128), (2, 16, 1, 384, 128),
-                                 (3, 16, 1, 512, 64), (2, 512, 1, 512, 512)):
+                                 (3, 16, 1, 512, 64), (2, 512, 1, 512, 512), (4, 512, 0, 512, 128), (2, 16, 0, 512, 128)):
         with pytest.raises(hq.HQQError):
             hq.hqq_gemm_dx(pk, md, md, N, K, nbits, g, axis, torch.zeros((4, N), dtype=torch.float16, device="cuda"))
+
+
+# ------------------------------------- 4-bit axis-0 codes through the split GEMM (any batch)
+# every group size; one to four row tiles; the metadata row n mod (N / g) cycles inside a tile
+# (N / g < 128) or spans several tiles; batches over one and two 256-row blocks
+AX0_GEMM_CASES = [(16, 128, 256, 9), (32, 256, 768, 40), (64, 384, 1024, 100), (128, 512, 2048, 256),
+                  (256, 256, 512, 300), (128, 1024, 256, 17)]
+AX0_DX_CASES = [(16, 256, 128, 5), (32, 768, 384, 64), (64, 512, 256, 257), (128, 1024, 640, 33), (256, 512, 128, 3)]
+
+
+@pytest.mark.parametrize("g,N,K,batch", AX0_GEMM_CASES, ids=lambda v: str(v))
+def test_gemm_axis0(g, N, K, batch):
+    _check_gemm(4, g, N, K, batch, seed=8000 + g + N + K + batch, axis=0)
+
+
+@pytest.mark.parametrize("g,N,K,batch", AX0_DX_CASES, ids=lambda v: str(v))
+def test_gemm_dx_axis0(g, N, K, batch):
+    _check_dx(4, g, N, K, batch, seed=8500 + g + N + K + batch, axis=0)
+
+
+def test_gemm_axis0_full_shape():
+    """The 28672 x 8192 g128 axis-0 weight at batch 256: the product on sampled rows and the
+    input gradient on sampled columns."""
+    r = np.random.default_rng(30)
+    _check_gemm(4, 128, 28672, 8192, 256, seed=8900, rows_sel=np.sort(r.choice(28672, 256, replace=False)), axis=0)
+    _check_dx(4, 128, 28672, 8192, 256, seed=8901, cols_sel=np.sort(r.choice(8192, 256, replace=False)), axis=0)
+
+
+def test_gemm_axis0_adjoint():
+    """<dY, x W_hat^T> = <dY W_hat, x> between hqq_gemm and hqq_gemm_dx on axis-0 codes."""
+    torch = torch_dev()
+    import weight_only_quantization_amd as hq
+    N, K, B, g = 768, 512, 24, 32
+    packed, delta, zero = _operands(95, N, K, 4, g, 0)
+    pk, dl, zr = (torch.from_numpy(a).cuda() for a in (packed, delta, zero))
+    r = np.random.default_rng(96)
+    x = torch.from_numpy(r.normal(0, 1, (B, K)).astype(np.float16)).cuda()
+    dy = torch.from_numpy(r.normal(0, 1, (B, N)).astype(np.float16)).cuda()
+    y = hq.hqq_gemm(pk, dl, zr, N, K, 4, g, 0, x, out_dtype=torch.float32).double()
+    dx = hq.hqq_gemm_dx(pk, dl, zr, N, K, 4, g, 0, dy, out_dtype=torch.float32).double()
+    lhs = (dy.double() * y).sum(dim=1)
+    rhs = (dx * x.double()).sum(dim=1)
+    assert torch.allclose(lhs, rhs, rtol=1e-4, atol=1e-4 * float(lhs.abs().max()))

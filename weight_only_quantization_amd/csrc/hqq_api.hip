@@ -422,10 +422,10 @@ int hqq_gemm(const void* packed, const void* delta_fp16, const void* zero_fp16, 
   if (axis != 0 && axis != 1) return fail(HQQ_ERR_INVALID_ARGUMENT, "axis must be 0 or 1");
   if (group_size <= 0 || (axis == 1 ? K : N) % group_size != 0)
     return fail(HQQ_ERR_INVALID_ARGUMENT, "group_size must divide the grouped dimension");
-  if (axis != 1) return fail(HQQ_ERR_UNSUPPORTED, "the batched product takes axis-1 groups");
-  if (nbits == 4 ? (group_size != 64 && group_size != 128)
-                 : (group_size < 16 || group_size > 256 || (group_size & (group_size - 1)) != 0))
-    return fail(HQQ_ERR_UNSUPPORTED, "group_size 64 or 128 for 4-bit codes, a power of two 16..256 for 2/3-bit");
+  if (axis == 0 && nbits != 4) return fail(HQQ_ERR_UNSUPPORTED, "the batched product takes axis-0 groups at 4 bits");
+  if (nbits == 4 && axis == 1 ? (group_size != 64 && group_size != 128) : !pow2_group(group_size))
+    return fail(HQQ_ERR_UNSUPPORTED,
+                "group_size 64 or 128 for 4-bit axis-1 codes, a power of two 16..256 for 2/3-bit or axis-0 codes");
   if (hqq::gemm_splits(N, K, batch) == 0)
     return fail(HQQ_ERR_UNSUPPORTED, "N must be a multiple of 128 and K of 256");
   if (y_dtype != HQQ_OUT_F16 && y_dtype != HQQ_OUT_F32)
@@ -440,8 +440,8 @@ int hqq_gemm(const void* packed, const void* delta_fp16, const void* zero_fp16, 
     return fail(HQQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   const hipError_t e = hqq::launch_gemm_fmt(
       reinterpret_cast<const uint8_t*>(packed), reinterpret_cast<const __half*>(delta_fp16),
-      reinterpret_cast<const __half*>(zero_fp16), N, K, nbits, group_size, reinterpret_cast<const __half*>(x_fp16),
-      batch, y, y_dtype, workspace, reinterpret_cast<hipStream_t>(stream));
+      reinterpret_cast<const __half*>(zero_fp16), N, K, nbits, group_size, axis,
+      reinterpret_cast<const __half*>(x_fp16), batch, y, y_dtype, workspace, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "hqq_gemm launch");
   return HQQ_OK;
 }
@@ -476,8 +476,8 @@ int hqq_gemm_w4a16_dx(const void* packed, const void* delta_fp16, const void* ze
     return fail(HQQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   const hipError_t e = hqq::launch_gemm_dx(
       reinterpret_cast<const uint8_t*>(packed), reinterpret_cast<const __half*>(delta_fp16),
-      reinterpret_cast<const __half*>(zero_fp16), N, K, 4, group_size, reinterpret_cast<const __half*>(dy_fp16), batch,
-      dx, dx_dtype, workspace, reinterpret_cast<hipStream_t>(stream));
+      reinterpret_cast<const __half*>(zero_fp16), N, K, 4, group_size, 1, reinterpret_cast<const __half*>(dy_fp16),
+      batch, dx, dx_dtype, workspace, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "hqq_gemm_w4a16_dx launch");
   return HQQ_OK;
 }
@@ -493,10 +493,10 @@ int hqq_gemm_dx(const void* packed, const void* delta_fp16, const void* zero_fp1
   if (axis != 0 && axis != 1) return fail(HQQ_ERR_INVALID_ARGUMENT, "axis must be 0 or 1");
   if (group_size <= 0 || (axis == 1 ? K : N) % group_size != 0)
     return fail(HQQ_ERR_INVALID_ARGUMENT, "group_size must divide the grouped dimension");
-  if (axis != 1) return fail(HQQ_ERR_UNSUPPORTED, "the input gradient takes axis-1 groups");
-  if (nbits == 4 ? (group_size != 64 && group_size != 128)
-                 : (group_size < 16 || group_size > 256 || (group_size & (group_size - 1)) != 0))
-    return fail(HQQ_ERR_UNSUPPORTED, "group_size 64 or 128 for 4-bit codes, a power of two 16..256 for 2/3-bit");
+  if (axis == 0 && nbits != 4) return fail(HQQ_ERR_UNSUPPORTED, "the input gradient takes axis-0 groups at 4 bits");
+  if (nbits == 4 && axis == 1 ? (group_size != 64 && group_size != 128) : !pow2_group(group_size))
+    return fail(HQQ_ERR_UNSUPPORTED,
+                "group_size 64 or 128 for 4-bit axis-1 codes, a power of two 16..256 for 2/3-bit or axis-0 codes");
   if (hqq::gemm_splits(K, N, batch) == 0)
     return fail(HQQ_ERR_UNSUPPORTED, "K must be a multiple of 128 and N of 256");
   if (dx_dtype != HQQ_OUT_F16 && dx_dtype != HQQ_OUT_F32)
@@ -511,8 +511,8 @@ int hqq_gemm_dx(const void* packed, const void* delta_fp16, const void* zero_fp1
     return fail(HQQ_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   const hipError_t e = hqq::launch_gemm_dx(
       reinterpret_cast<const uint8_t*>(packed), reinterpret_cast<const __half*>(delta_fp16),
-      reinterpret_cast<const __half*>(zero_fp16), N, K, nbits, group_size, reinterpret_cast<const __half*>(dy_fp16),
-      batch, dx, dx_dtype, workspace, reinterpret_cast<hipStream_t>(stream));
+      reinterpret_cast<const __half*>(zero_fp16), N, K, nbits, group_size, axis,
+      reinterpret_cast<const __half*>(dy_fp16), batch, dx, dx_dtype, workspace, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "hqq_gemm_dx launch");
   return HQQ_OK;
 }

@@ -83,8 +83,9 @@ __device__ __forceinline__ u32x4 wq8_3b(unsigned v, float ds24, float ds21, floa
 }
 
 // Stored formats the split GEMM stages (4-bit axis 1 has its group size as a template
-// parameter; the others take log2 of it at run time).
-constexpr int kFmt4 = 0, kFmt2 = 2, kFmt3 = 3;
+// parameter; the others take log2 of it at run time).  kFmt4A0: 4-bit codes with axis-0 groups
+// (weight row n uses metadata row n mod (N/g), one step and zero per column).
+constexpr int kFmt4 = 0, kFmt2 = 2, kFmt3 = 3, kFmt4A0 = 4;
 
 // TRANS = false: y [batch, N] = x [batch, K] @ W_hat^T (the forward product; output index n,
 //   contraction over k).  TRANS = true: dX [batch, K] = dY [batch, N] @ W_hat (its input
@@ -143,7 +144,9 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
       // 32 wq .. +31 of the tile's output columns.  Either way 32 codes of one row from flat code
       // index f = n K + k, an even number (K % 128 == 0): 2-bit: 8 bytes; 3-bit: ten codes per
       // word, the 32 codes start at an even slot ph <= 8 of word f / 10 and end inside the fourth
-      // word.  With g = 16 codes 0..15 and 16..31 are two groups; otherwise one.
+      // word; 4-bit axis 0: 16 bytes, with the 32 steps and zeros of metadata row n mod (N / g)
+      // at the same columns (64 bytes each).  Axis 1 with g = 16: codes 0..15 and 16..31 are two
+      // groups; otherwise one.
       const int st = tid - 64 * kSkMulWaves;
       const int wr = st >> 2, wq = st & 3;
       _Float16* wdst = wt + wr * kSkRow + 32 * wq;
@@ -152,16 +155,39 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
       for (int p = 0; p < 2; ++p)
         fr[p] = TRANS ? (k0 + 2 * wr + p) * K + n0 + 32 * wq : (n0 + wr + 64 * p) * K + k0 + 32 * wq;
       const int64_t fstep = TRANS ? (int64_t)kSkBK * K : kSkBK;  // the next chunk
+      constexpr int MD = FMT == kFmt4A0 ? 16 : 2;  // metadata dwords per row (axis 0: 32 fp16 each)
       struct Regs {
-        unsigned w[2][4], dm[2][2], zm[2][2];
+        unsigned w[2][4], dm[2][MD], zm[2][MD];
         int ph[2];
       };
+      // axis 0: the thread's rows and first column; metadata index (n mod R0) K + k, R0 = N / g
+      const unsigned R0 = (unsigned)(N >> gs_log2);
+      unsigned mrow[2], mcol[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        mrow[p] = (unsigned)(TRANS ? k0 + 2 * wr + p : n0 + wr + 64 * p);
+        mcol[p] = (unsigned)(TRANS ? n0 + 32 * wq : k0 + 32 * wq);
+      }
       auto load_w = [&](int c, Regs& r) {
         const int64_t cc = min(c, nch - 1);  // past the end: reload the last chunk (never used)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const int64_t f0 = fr[p] + fstep * cc;
-          if constexpr (FMT == kFmt3) {
+          if constexpr (FMT == kFmt4A0) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(packed + f0 / 2);
+            const unsigned row = mrow[p] + (TRANS ? (unsigned)(kSkBK * cc) : 0u);
+            const unsigned col = mcol[p] + (TRANS ? 0u : (unsigned)(kSkBK * cc));
+            const int64_t mi = (int64_t)(row % R0) * K + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              r.w[p][i] = v[i];
+              const u32x4 dv = *reinterpret_cast<const u32x4*>(delta + mi + 8 * i);
+              const u32x4 zv = *reinterpret_cast<const u32x4*>(zero + mi + 8 * i);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) r.dm[p][4 * i + e] = dv[e], r.zm[p][4 * i + e] = zv[e];
+            }
+            continue;
+          } else if constexpr (FMT == kFmt3) {
             const int64_t q0 = f0 / 10;
             r.ph[p] = (int)(f0 - 10 * q0);
             const uint32_t* pw = reinterpret_cast<const uint32_t*>(packed) + q0;
@@ -181,6 +207,28 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
       };
       // W_hat of the thread's 32 codes of row p, natural order: blocks of 8 codes (4 dwords of pairs)
       auto decode = [&](const Regs& r, int p, u32x4 (&o)[4]) {
+        if constexpr (FMT == kFmt4A0) {
+          // dword t: codes 8t..8t+7 as fp16 subnormals (c0, c4), (16 c1, 16 c5), (c2, c6),
+          // (16 c3, 16 c7); each code with its own step and zero: fp16(c 2^-24 (d S) - z d),
+          // S = 2^24 (2^20 for the odd codes), z d exact in fp32
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const unsigned dw = r.w[p][t];
+            const f16x2 P[4] = {as_h2(dw & 0x000F000Fu), as_h2(dw & 0x00F000F0u), as_h2((dw >> 8) & 0x000F000Fu),
+                                as_h2((dw >> 8) & 0x00F000F0u)};
+            float w[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float c = (float)P[e & 3][e >> 2];
+              const f16x2 dp = as_h2(r.dm[p][4 * t + (e >> 1)]), zp = as_h2(r.zm[p][4 * t + (e >> 1)]);
+              const float d = (float)dp[e & 1], z = (float)zp[e & 1];
+              w[e] = __builtin_fmaf(c, d * ((e & 1) ? 1048576.0f : 16777216.0f), -(z * d));
+            }
+            o[t] = u32x4{as_u(f16x2{(_Float16)w[0], (_Float16)w[1]}), as_u(f16x2{(_Float16)w[2], (_Float16)w[3]}),
+                         as_u(f16x2{(_Float16)w[4], (_Float16)w[5]}), as_u(f16x2{(_Float16)w[6], (_Float16)w[7]})};
+          }
+          return;
+        }
         float zd[2], d[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -525,6 +573,10 @@ void launch_fmt(int fmt, int gs, dim3 grid, hipStream_t st, const uint8_t* packe
                 float* pw, void* out, int y_dtype, int xcd_map) {
   int gl = 0;
   while ((1 << gl) < gs) ++gl;
+  if (fmt == kFmt4A0) {
+    launch_sk<kFmt4A0, 0, DIRECT, TRANS>(grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
+    return;
+  }
   if constexpr (TRANS) {
     if (fmt == kFmt3)
       launch_sk<kFmt3, 0, DIRECT, true>(grid, st, packed, delta, zero, N, K, S, xt, MG, batch, pw, out, y_dtype, xcd_map, gl);
@@ -583,16 +635,16 @@ hipError_t launch_gemm_split(const uint8_t* packed, const __half* delta, const _
 }
 
 hipError_t launch_gemm_fmt(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
-                           int nbits, int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
-                           hipStream_t st) {
-  const int fmt = nbits == 3 ? kFmt3 : nbits == 2 ? kFmt2 : kFmt4;
+                           int nbits, int gs, int axis, const __half* x, int64_t batch, void* y, int y_dtype,
+                           void* workspace, hipStream_t st) {
+  const int fmt = axis == 0 ? kFmt4A0 : nbits == 3 ? kFmt3 : nbits == 2 ? kFmt2 : kFmt4;
   return launch_split<false>(fmt, packed, delta, zero, N, K, gs, x, batch, y, y_dtype, workspace, st);
 }
 
 hipError_t launch_gemm_dx(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
-                          int nbits, int gs, const __half* dy, int64_t batch, void* dx, int dx_dtype, void* workspace,
-                          hipStream_t st) {
-  const int fmt = nbits == 3 ? kFmt3 : nbits == 2 ? kFmt2 : kFmt4;
+                          int nbits, int gs, int axis, const __half* dy, int64_t batch, void* dx, int dx_dtype,
+                          void* workspace, hipStream_t st) {
+  const int fmt = axis == 0 ? kFmt4A0 : nbits == 3 ? kFmt3 : nbits == 2 ? kFmt2 : kFmt4;
   return launch_split<true>(fmt, packed, delta, zero, N, K, gs, dy, batch, dx, dx_dtype, workspace, st);
 }
 

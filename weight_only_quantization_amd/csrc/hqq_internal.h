@@ -73,16 +73,17 @@ hipError_t launch_gemm_split(const uint8_t* packed, const __half* delta, const _
                              int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
                              hipStream_t st);
 // The same batched product for 2-, 3- and 4-bit codes with axis-1 groups (the staging waves
-// unpack the stored format; 4-bit takes group sizes 64 and 128, 2/3-bit 16..256).
+// unpack the stored format; 4-bit takes group sizes 64 and 128, 2/3-bit 16..256) and for 4-bit
+// codes with axis-0 groups (axis = 0: g a power of two 16..256 dividing N).
 hipError_t launch_gemm_fmt(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
-                           int nbits, int gs, const __half* x, int64_t batch, void* y, int y_dtype, void* workspace,
-                           hipStream_t st);
-// Input gradient dX [batch, K] = dY [batch, N] @ W_hat with the same kernel transposed (2-, 3-
-// and 4-bit codes, axis-1 groups, group sizes as launch_gemm_fmt); its workspace is
-// gemm_workspace_bytes(K, N, batch) (output length first).
+                           int nbits, int gs, int axis, const __half* x, int64_t batch, void* y, int y_dtype,
+                           void* workspace, hipStream_t st);
+// Input gradient dX [batch, K] = dY [batch, N] @ W_hat with the same kernel transposed (the
+// formats of launch_gemm_fmt); its workspace is gemm_workspace_bytes(K, N, batch) (output
+// length first).
 hipError_t launch_gemm_dx(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
-                          int nbits, int gs, const __half* dy, int64_t batch, void* dx, int dx_dtype, void* workspace,
-                          hipStream_t st);
+                          int nbits, int gs, int axis, const __half* dy, int64_t batch, void* dx, int dx_dtype,
+                          void* workspace, hipStream_t st);
 // Fused product with 3-bit codes (axis 1, batch 1-2): shapes it takes, LDS bytes, launch.
 bool gemv_3b_supported(int64_t K, int g);
 size_t gemv_3b_lds_bytes(int64_t N, int64_t K, int g, int64_t batch);
