@@ -24,6 +24,8 @@
 // The same kernel, transposed, computes the input gradient dX = dY @ W_hat: output columns k of
 // the weight, contraction over its rows (the dequantised tile is stored transposed in LDS).
 
+#include <type_traits>
+
 #include "hqq_gemv_common.h"
 
 namespace hqq {
@@ -408,11 +410,15 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
   for (int t = 0; t < 4; ++t) xa[t] = xt + ((k0 / 32) * MG + (m0 + 64 * wave + 16 * t) / 16) * 64 + lane;
   const int nsteps = 4 * nch;
   const int64_t astep = MG * 64;  // one k-step further in the tiled copy
+  // 16-row batch tiles of this wave that hold rows of the batch (wave-uniform), rounded up to
+  // 0, 1 or 4: the MFMAs and A loads of the others are skipped (small batches: the tile's rows
+  // are mostly padding); the count is a compile-time constant, so the loops stay straight-line
+  const int tmax = (int)max<int64_t>(0, min<int64_t>(4, (batch - (m0 + 64 * wave) + 15) / 16));
   // A operand of k-step q (32 codes) into one of four register slots
-  auto load_a = [&](int q, u32x4 (&av)[4]) {
+  auto load_a = [&](int q, u32x4 (&av)[4], auto tm) {
     const int64_t off = (int64_t)min(q, nsteps - 1) * astep;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) av[t] = xa[t][off];
+    for (int t = 0; t < decltype(tm)::value; ++t) av[t] = xa[t][off];
   };
 
   f32x4 acc[4][8];
@@ -428,7 +434,7 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
   // compiler would otherwise sink them to the loop end and wait for them there).
   u32x4 as[4][4];
   const _Float16* src0 = wt + (lane & 15) * kSkRow + 8 * (lane >> 4);
-  auto chunk = [&](int buf, int c) {
+  auto chunk = [&](int buf, int c, auto tm) {
     const _Float16* src = src0 + buf * (kSkBN * kSkRow);
     // fragment j, k-step s: 16-byte block 4s + (lane >> 4) of its row (swizzled when TRANS)
     auto bfrag = [&](int j, int s) {
@@ -444,24 +450,31 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < decltype(tm)::value; ++t)
           acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, as[s][t]), B[j], acc[t][j], 0, 0, 0);
         if (s < 3) B[j] = bfrag(j, s + 1);
       }
-      load_a(4 * c + s + 4, as[s]);  // into the registers just read: no copy at the loop edge
+      load_a(4 * c + s + 4, as[s], tm);  // into the registers just read: no copy at the loop edge
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-
+  auto run = [&](auto tm) {
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) load_a(s4, as[s4]);
-  lds_barrier();  // the first tile is staged
-  for (int c = 0; c < nch; c += 2) {
-    chunk(0, c);
-    lds_barrier();
-    chunk(1, c + 1);
-    lds_barrier();
-  }
+    for (int s4 = 0; s4 < 4; ++s4) load_a(s4, as[s4], tm);
+    lds_barrier();  // the first tile is staged
+    for (int c = 0; c < nch; c += 2) {
+      if constexpr (decltype(tm)::value > 0) chunk(0, c, tm);
+      lds_barrier();
+      if constexpr (decltype(tm)::value > 0) chunk(1, c + 1, tm);
+      lds_barrier();
+    }
+  };
+  if (tmax > 1)
+    run(std::integral_constant<int, 4>{});
+  else if (tmax == 1)
+    run(std::integral_constant<int, 1>{});
+  else
+    run(std::integral_constant<int, 0>{});
 
   // D layout: acc[t][j][r] is batch row 64 wave + 16 t + 4 (lane >> 4) + r, weight row
   // 16 j + (lane & 15)
