@@ -47,15 +47,28 @@ def test_product_operand_checks(fn):
         call(pk, d, z, x)
 
 
-def test_gradient_operand_checks():
+@pytest.mark.parametrize("fn", ["gemm_w4a16_dx", "gemm_dx"])
+def test_gradient_operand_checks(fn):
     hq.load()
     pk, d, z, _ = ops()
+
+    def call(dy, pk=pk, d=d, z=z, out=None):
+        if fn == "gemm_w4a16_dx":
+            return hq.hqq_gemm_w4a16_dx(pk, d, z, N, K, G, dy, out=out)
+        return hq.hqq_gemm_dx(pk, d, z, N, K, 4, G, 1, dy, out=out)
+
     with pytest.raises(ValueError, match="dy must be torch.float16"):
-        hq.hqq_gemm_w4a16_dx(pk, d, z, N, K, G, torch.zeros((4, N), dtype=torch.float32))
-    with pytest.raises(ValueError, match="dy must be"):
-        hq.hqq_gemm_w4a16_dx(pk, d, z, N, K, G, torch.zeros((4, K), dtype=torch.float16))
+        call(torch.zeros((4, N), dtype=torch.float32))
+    with pytest.raises(ValueError, match="dy must be"):  # [batch, N], not [batch, K]
+        call(torch.zeros((4, K), dtype=torch.float16))
+    with pytest.raises(ValueError, match="delta must be torch.float16"):
+        call(torch.zeros((4, N), dtype=torch.float16), d=d.float())
+    with pytest.raises(ValueError, match="packed holds"):
+        call(torch.zeros((4, N), dtype=torch.float16), pk=pk[:-1])
+    with pytest.raises(ValueError, match="out must have shape"):  # dX is [batch, K]
+        call(torch.zeros((4, N), dtype=torch.float16), out=torch.zeros((4, N), dtype=torch.float16))
     with pytest.raises(ValueError, match="CUDA"):
-        hq.hqq_gemm_w4a16_dx(pk, d, z, N, K, G, torch.zeros((4, N), dtype=torch.float16))
+        call(torch.zeros((4, N), dtype=torch.float16))
 
 
 def test_quantize_and_dequantize_checks():
