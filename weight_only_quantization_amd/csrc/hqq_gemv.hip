@@ -297,8 +297,10 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __rest
 // group's step and zero on the fp32 partial, acc += delta * (P - z * sum_k x_k); row results
 // are reduced over the wave's lanes with a fixed tree.
 //
-// Pipelining: wave gw of the grid takes exactly R rows, n = gw + k * (N / R), so at any time
-// the waves of the chip stream one contiguous band of rows.  D rows are in flight per wave:
+// Pipelining: wave gw of the grid takes exactly R consecutive rows, n = gw R + k, so each wave
+// streams one contiguous run of R rows (measured at 8192 x 8192, batch 1: 7.77 us, against 8.00
+// with the rows of a wave N / R apart and 8.04 with a block's waves on neighbouring rows at each
+// step).  D rows are in flight per wave:
 // row k + D is requested as soon as row k has been multiplied.  Everything a wave does is
 // straight-line code: loads are unconditional (a chunk index past the row's end is clamped
 // and its contribution selected away), so the compiler's memory-counter waits only ever wait
@@ -332,8 +334,8 @@ __global__ void __launch_bounds__(64 * W) k_gemv_valu(const uint8_t* __restrict_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t gpr = K >> gs_log2;            // groups per row
   const int cshift = gs_log2 - 5;              // chunk -> group within the row
-  const int64_t TW = N / R;                    // waves in the grid
-  const int64_t gw = (int64_t)blockIdx.x * W + wave;
+  const int64_t TW = 1;                                 // row step within a wave
+  const int64_t gw = ((int64_t)blockIdx.x * W + wave) * R;  // the wave's first row
 
   // 1. this thread's 16-byte blocks of x (a block past the end re-reads the last one)
   constexpr int XR = (B * 64 * JMAX * 4 + NT - 1) / NT;

@@ -391,7 +391,7 @@ __global__ void __launch_bounds__(64 * kM0Waves) k_gemv_mf0(const uint8_t* __res
 // d & 0x00300030 = (16c2, 16c10), d & 0x00C000C0 = (64c3, 64c11), and the same on d >> 8 for
 // c4..c7 / c12..c15; x is staged in that pair order with 1, 1/4, 1/16, 1/64 on the four
 // positions.  Per group: acc += delta * (P - z * sum_k x_k), the 2^24 folded into delta and z.
-// Waves take R rows n = gw + k N / R with two rows in flight, as the 4-bit kernel.
+// Waves take R consecutive rows with two rows in flight, as the 4-bit kernel.
 // ------------------------------------------------------------------------------------------
 constexpr int k2Waves = 4;
 
@@ -443,8 +443,8 @@ __global__ void __launch_bounds__(64 * k2Waves) k_gemv_2b(const uint8_t* __restr
   uint4* xs = reinterpret_cast<uint4*>(sg + ((B * ngr + 3) & ~3));  // [B][8][nch] staged x
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t TW = N / R;
-  const int64_t gw = (int64_t)blockIdx.x * k2Waves + wave;
+  const int64_t TW = 1;                                       // a wave's R rows are consecutive
+  const int64_t gw = ((int64_t)blockIdx.x * k2Waves + wave) * R;  // its first row
 
   // 1. x: one group (32 bytes) per task
   constexpr int XR = (B * 64 * JMAX * 4 + NT - 1) / NT;
@@ -597,8 +597,8 @@ __global__ void __launch_bounds__(64 * k3Waves) k_gemv_3b(const uint32_t* __rest
   float2* meta = reinterpret_cast<float2*>(xq + B * xs);          // [waves][R][gsr] (step 2^24, -zero 2^-24)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t TW = N / R;
-  const int64_t gw = (int64_t)blockIdx.x * k3Waves + wave;
+  const int64_t TW = 1;                                       // a wave's R rows are consecutive
+  const int64_t gw = ((int64_t)blockIdx.x * k3Waves + wave) * R;  // its first row
   const int64_t nwt = (N * K + 9) / 10;  // words of the tensor
 
   // 1. this thread's blocks of x and this wave's rows' metadata, ahead of the weight stream
