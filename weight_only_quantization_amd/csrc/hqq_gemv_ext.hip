@@ -212,7 +212,7 @@ template <int B, int SPB, int NSEG>
 __global__ void __launch_bounds__(64 * kM0Waves) k_gemv_mf0(const uint8_t* __restrict__ packed,
                                                            const __half* __restrict__ delta,
                                                            const __half* __restrict__ zero, int64_t N, int64_t K,
-                                                           int g, int subsets, int out_dtype,
+                                                           int g, int subsets, int xcd_map, int out_dtype,
                                                            const __half* __restrict__ x, void* __restrict__ y) {
   static_assert(B >= 1 && B <= 8 && (SPB == 1 || SPB == 2), "shape");
   constexpr int NT = 64 * kM0Waves, RB = 16 * SPB;
@@ -225,8 +225,19 @@ __global__ void __launch_bounds__(64 * kM0Waves) k_gemv_mf0(const uint8_t* __res
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 4, nl = lane & 15;
   const int arow = nl < B ? nl : 0;  // A rows >= B only feed outputs that are never stored
-  const int64_t R0 = N / g, r0 = blockIdx.x / subsets;
-  const int64_t i0 = (int64_t)(blockIdx.x % subsets) * RB;  // rows n = r0 + R0 (i0 + row)
+  // Block b runs on XCD b mod 8 (round-robin dispatch).  With xcd_map (N / g a multiple of 8) the
+  // `subsets` blocks of one metadata row share an XCD, so its steps and zeros come from that L2.
+  const int64_t R0 = N / g;
+  int64_t r0, sub;
+  if (xcd_map) {
+    const int64_t xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    r0 = 8 * (q / subsets) + xcd;
+    sub = q % subsets;
+  } else {
+    r0 = blockIdx.x / subsets;
+    sub = blockIdx.x % subsets;
+  }
+  const int64_t i0 = sub * RB;  // rows n = r0 + R0 (i0 + row)
   const __half* drow = delta + r0 * K;
   const __half* zrow = zero + r0 * K;
   const int64_t nchunks = K / 128;
@@ -891,8 +902,9 @@ template <int B, int SPB, int NSEG>
 hipError_t mf0_launch(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
                       const __half* x, void* y, int y_dtype, hipStream_t st) {
   const int subsets = g / (16 * SPB);
+  const int xcd_map = (N / g) % 8 == 0;
   hipLaunchKernelGGL((k_gemv_mf0<B, SPB, NSEG>), dim3((unsigned)((N / g) * subsets)), dim3(64 * kM0Waves),
-                     2 * mf0_stage_bytes(B, SPB), st, packed, delta, zero, N, K, g, subsets, y_dtype, x, y);
+                     2 * mf0_stage_bytes(B, SPB), st, packed, delta, zero, N, K, g, subsets, xcd_map, y_dtype, x, y);
   return hipGetLastError();
 }
 
