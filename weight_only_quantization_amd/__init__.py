@@ -438,8 +438,9 @@ def hqq_gemm_w4a16(packed, delta, zero, N: int, K: int, group_size: int, x, out_
 
 def hqq_gemm(packed, delta, zero, N: int, K: int, nbits: int, group_size: int, axis: int, x, out_dtype=None,
              out=None, workspace=None, stream=None):
-    """Batched y [batch, N] = x [batch, K] @ W_hat^T for 2-, 3- or 4-bit codes with axis-1 groups,
-    with a workspace as hqq_gemm_w4a16 (hqq_gemm_workspace_bytes(N, K, batch) bytes)."""
+    """Batched y [batch, N] = x [batch, K] @ W_hat^T for 2-, 3- or 4-bit codes with axis-1 groups
+    and 4-bit codes with axis-0 groups, with a workspace as hqq_gemm_w4a16
+    (hqq_gemm_workspace_bytes(N, K, batch) bytes)."""
     import torch
     lib = load()
     out_dtype = out_dtype or torch.float16
@@ -492,8 +493,9 @@ def hqq_gemm_w4a16_dx(packed, delta, zero, N: int, K: int, group_size: int, dy, 
 
 def hqq_gemm_dx(packed, delta, zero, N: int, K: int, nbits: int, group_size: int, axis: int, dy, out_dtype=None,
                 out=None, workspace=None, stream=None):
-    """Input gradient dX [batch, K] = dY [batch, N] @ W_hat for 2-, 3- or 4-bit codes of W [N, K]
-    with axis-1 groups (workspace as hqq_gemm_w4a16, sized by hqq_gemm_dx_workspace_bytes)."""
+    """Input gradient dX [batch, K] = dY [batch, N] @ W_hat for the formats of hqq_gemm (2-, 3- or
+    4-bit codes of W [N, K] with axis-1 groups, 4-bit with axis-0 groups); workspace as
+    hqq_gemm_w4a16, sized by hqq_gemm_dx_workspace_bytes."""
     import torch
     lib = load()
     out_dtype = out_dtype or torch.float16
@@ -519,7 +521,8 @@ def hqq_gemm_dx(packed, delta, zero, N: int, K: int, nbits: int, group_size: int
 def hqq_gemv(packed, delta, zero, N: int, K: int, nbits: int, group_size: int, axis: int, x, out_dtype=None,
              out=None, stream=None):
     """y [batch, N] = x [batch, K] @ W_hat^T for any stored format the library fuses
-    (4-bit axis 1 or 0, 3-bit axis 1, 2-bit axis 1 with groups of 16)."""
+    (4-bit axis 1 or 0 at batch 1-8, 3-bit axis 1 and 2-bit axis 1 with groups of 16 at batch 1-2;
+    larger batches: hqq_gemm)."""
     import torch
     lib = load()
     out_dtype = out_dtype or torch.float16
