@@ -226,6 +226,17 @@ def test_gemv_parity_long_rows(K, batch):
     check_gemv(packed, d16, z16, N, K, 64, x, out_f32=True)
 
 
+@pytest.mark.parametrize("N,K,batch", [(8224, 256, 1), (8208, 384, 1), (4112, 512, 1), (4096, 256, 2),
+                                       (8192, 128, 2), (1040, 640, 1)])
+def test_gemv_parity_rows_per_wave(N, K, batch):
+    """The row-streaming GEMV's wave shapes: 8 consecutive rows per wave (N a multiple of 32 with
+    at least 256 blocks), 4 (N / 16 >= 256), 2 otherwise; every row of every wave checked."""
+    say("gemv rows per wave", N, K, batch)
+    packed, d16, z16 = gemv_inputs(N, K, 64, seed=4200 + N + K)
+    x = synth.activations(batch, K, seed=23)
+    check_gemv(packed, d16, z16, N, K, 64, x, out_f32=True)
+
+
 @pytest.mark.parametrize("g", [64, 128])
 @pytest.mark.parametrize("N,K,batch", [(8192, 256, 6), (8192, 640, 3), (32, 20480, 1), (32, 18432, 2),
                                        (48, 2176, 5)])
