@@ -34,8 +34,12 @@ namespace {
 constexpr int kSkBM = 256;          // batch rows per block
 constexpr int kSkBN = 128;          // weight rows per block
 constexpr int kSkBK = 128;          // codes per chunk
-constexpr int kSkRow = kSkBK + 8;   // LDS row stride of the W_hat tile (halves)
-constexpr size_t kSkLds = 2 * kSkBN * kSkRow * sizeof(_Float16);
+// LDS row stride of the W_hat tile (halves): 16 halves of padding for the forward product and 8
+// for the transposed tile (measured at 8192 x 8192, batch 256: forward 56.0-56.8 us against
+// 57.7-58.2 with 8; the transposed stores and their swizzle prefer 8: 58.9-59.4 against 59.5-60.7)
+template <bool TRANS>
+constexpr int sk_row() { return kSkBK + (TRANS ? 8 : 16); }
+constexpr size_t kSkLds = 2 * kSkBN * (kSkBK + 16) * sizeof(_Float16);  // the larger of the two
 constexpr int kSkMulWaves = 4;      // multiplying waves, each 64 batch rows x all 128 weight rows
 constexpr int kSkThreads = 512;     // and as many staging waves
 
@@ -109,6 +113,7 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
                                                  float* __restrict__ part, void* __restrict__ y, int out_dtype,
                                                  int xcd_map, int gs_log2) {
   extern __shared__ _Float16 wt[];  // [2][kSkBN][kSkRow]
+  constexpr int kSkRow = sk_row<TRANS>();
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t NO = TRANS ? K : N, KC = TRANS ? N : K;  // output and contraction lengths
   // Block b of a row of the grid runs on XCD b mod 8 (round-robin dispatch).  With xcd_map,
