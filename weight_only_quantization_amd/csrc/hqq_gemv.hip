@@ -9,13 +9,16 @@
 //   k_gemm       batch > 8 without a workspace: an MFMA GEMM on fp16 W_hat tiles.
 //
 // MFMA operand layout: the weight tile is the B operand (16 output rows n per tile,
-// n = lane % 16), the activations are the A operand (16 batch rows m, m = lane % 16), and lane
-// (h = lane / 16, r) of the result holds y[m = 4h + r][n].  A load instruction whose lanes span
-// 16 rows reads the weight stream at half the rate of one that reads 1 KB of one row (the rows
-// are pages apart), hence the LDS staging.  One v_permlane32_swap per dword pair regroups a
-// 128-code chunk so that the four lane groups hold the four 16-code quarters of one 64-code
-// group (lane group h holds quarter pi(h), pi = [0, 2, 1, 3]): every MFMA then sums codes of a
-// single group, which lets the group's delta and zero be applied once per group.
+// n = lane % 16), the activations are the A operand (16 rows m, m = lane % 16), and lane
+// (h = lane / 16, r) of the result holds row m = 4h + r, column n.  A load instruction whose
+// lanes span 16 rows reads the weight stream at half the rate of one that reads 1 KB of one row
+// (the rows are pages apart), hence the LDS staging.  Lane group h of the B operand holds codes
+// 32h .. 32h + 31 of a 128-code chunk.  With groups of 128 the chunk is one group and m is the
+// batch row.  With groups of 64 each MFMA sums 16 codes of each of the chunk's two groups, so A
+// row m < 8 carries batch row m against the first group's k slots (zeros against the second's)
+// and row 8 + m batch row m against the second's: result rows 0-7 are the first group's
+// partial sums, rows 8-15 the second's, and each group's delta and zero are applied once on
+// them, with no result row left for padding at batch 8.
 //
 // Code unpack (fp16 subnormals): for a dword of eight 4-bit codes c0..c7, (d & 0x000F000F) is
 // the fp16 pair (c0, c4) * 2^-24 and (d & 0x00F000F0) the pair (16 c1, 16 c5) * 2^-24, the same
@@ -50,9 +53,16 @@ constexpr int kMfKS = 128 * kMfWaves;   // codes per segment
 constexpr int kMfKSP = kMfKS + 8;       // LDS row stride of x (halves): rows in different banks
 constexpr int kMfWRB = kMfKS / 2 + 16;  // LDS row stride of the packed codes (bytes)
 
-// LDS bytes of one stage (x, sums of x, codes, metadata) and of the kernel (two stages).
+// Batch rows of the per-group sums of x, padded with zeros (8 with groups of 64: a lane reads the
+// sums of batch rows 0-3 or 4-7).
+__host__ __device__ constexpr int mf_bp(int B, int GS) { return GS == 64 ? 8 : (B + 3) & ~3; }
+// LDS bytes of one stage (x, sums of x, codes, metadata) and of the kernel (two stages, and with
+// groups of 64 a row of zeros that the A rows read against the other group's codes).
 __host__ __device__ constexpr int mf_stage_bytes(int B, int GS, int SPB) {
-  return B * kMfKSP * 2 + (kMfKS / GS) * ((B + 3) & ~3) * 4 + 16 * SPB * kMfWRB + 16 * SPB * (2 * (kMfKS / GS) + 4) * 4;
+  return B * kMfKSP * 2 + (kMfKS / GS) * mf_bp(B, GS) * 4 + 16 * SPB * kMfWRB + 16 * SPB * (2 * (kMfKS / GS) + 4) * 4;
+}
+__host__ __device__ constexpr int mf_lds_bytes(int B, int GS, int SPB) {
+  return 2 * mf_stage_bytes(B, GS, SPB) + (GS == 64 ? kMfKS * 2 : 0);
 }
 
 template <int B, int GS, int SPB, int NSEG>
@@ -68,7 +78,7 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __rest
   constexpr int XR = (XB + NT - 1) / NT;   // of them per thread
   constexpr int MW = GS == 64 ? 2 : 1;     // groups per metadata load (4 or 2 bytes)
   constexpr int ML = RB * GPS / MW;        // metadata loads per array and segment
-  constexpr int BP = (B + 3) & ~3;         // batch rows of the x sums, padded with zeros to a multiple of 4
+  constexpr int BP = mf_bp(B, GS);         // batch rows of the x sums, padded with zeros
   constexpr int MLR = 2 * GPS + 4;         // LDS row stride of the metadata (floats): 16-byte reads of 8
                                            // consecutive rows fall in distinct banks
   static_assert(ML <= NT, "one step and one zero load per thread");
@@ -77,7 +87,7 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __rest
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 4, nl = lane & 15, qh = quarter_of(h);
+  const int h = lane >> 4, nl = lane & 15;
   const int arow = nl < B ? nl : 0;  // A rows >= B only feed outputs that are never stored
   const int64_t n0 = (int64_t)blockIdx.x * RB;
   const int64_t gpr = K / GS;
@@ -182,6 +192,15 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __rest
       sx_of(b)[(rem / (BP - B)) * BP + B + rem % (BP - B)] = 0.f;
     }
   }
+  const _Float16* zrow = reinterpret_cast<const _Float16*>(lds_raw + 2 * STAGE);  // GS == 64: kMfKS zeros
+  if constexpr (GS == 64) {
+    static_assert(kMfKS / 2 == NT, "one dword of the zero row per thread");
+    reinterpret_cast<unsigned*>(lds_raw + 2 * STAGE)[tid] = 0u;
+  }
+  // GS == 64: A row m < 8 is batch row m against the first group of a chunk, row 8 + m batch row m
+  // against the second; the lane supplies x where its k slots hold codes of that row's group and
+  // zeros (the zero row) elsewhere and past the batch
+  const bool xact = ((nl < 8) == (h < 2)) && (nl & 7) < B;
   Regs rs[2];
   load_seg(0, rs[0]);
   if (NSEG != 1) load_seg(min(1, nseg - 1), rs[1]);
@@ -201,34 +220,27 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __rest
       const uint8_t* wl = wl_of(buf);
       const float* ml = ml_of(buf);
       if constexpr (GS == 64) {
-        const int kl = wave * 128 + qh * 16;
-        const f16x8 a00 = *reinterpret_cast<const f16x8*>(xs + arow * kMfKSP + kl);
-        const f16x8 a01 = *reinterpret_cast<const f16x8*>(xs + arow * kMfKSP + kl + 8);
-        const f16x8 a10 = *reinterpret_cast<const f16x8*>(xs + arow * kMfKSP + kl + 64);
-        const f16x8 a11 = *reinterpret_cast<const f16x8*>(xs + arow * kMfKSP + kl + 72);
-        // sums of x of this lane's four batch rows 4h .. 4h + 3 (zeros past the batch)
-        const int hq = 4 * h < BP ? 4 * h : 0;
-        f32x4 sx0 = *reinterpret_cast<const f32x4*>(sx + (2 * wave) * BP + hq);
-        f32x4 sx1 = *reinterpret_cast<const f32x4*>(sx + (2 * wave + 1) * BP + hq);
-        if (4 * h >= BP) sx0 = sx1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        // lane group h holds codes 32 h .. 32 h + 31 of the chunk: lane groups 0-1 the first group
+        // (64 codes), 2-3 the second, so each MFMA sums 16 codes of each group, and result rows
+        // 0-7 (lane groups 0-1) are the first group's partial sums for batch rows 0-7, rows 8-15
+        // (lane groups 2-3) the second group's
+        const _Float16* xa = (xact ? xs + (nl & 7) * kMfKSP : zrow) + wave * 128 + 32 * h;
+        f16x8 A[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) A[t] = *reinterpret_cast<const f16x8*>(xa + 8 * t);
+        // sums of x of this lane's group and batch rows 4 (h & 1) .. + 3
+        const f32x4 sxv = *reinterpret_cast<const f32x4*>(sx + (2 * wave + (h >> 1)) * BP + 4 * (h & 1));
 #pragma unroll
         for (int sp = 0; sp < SPB; ++sp) {
           const int row = 16 * sp + nl;
           const uint4 v = *reinterpret_cast<const uint4*>(wl + row * kMfWRB + wave * 64 + h * 16);
-          // regroup: lane group h then holds quarter pi(h) of both 64-code groups of the chunk
-          const auto s0 = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
-          const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-          f32x4 P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a00, unpack8_sub(s0[0]), zero4, 0, 0, 0);
-          f32x4 P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a10, unpack8_sub(s0[1]), zero4, 0, 0, 0);
-          P0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a01, unpack8_sub(s1[0]), P0, 0, 0, 0);
-          P1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a11, unpack8_sub(s1[1]), P1, 0, 0, 0);
-          const f32x4 md = *reinterpret_cast<const f32x4*>(ml + row * MLR + 4 * wave);  // d0, -z0, d1, -z1
+          const unsigned dd[4] = {v.x, v.y, v.z, v.w};
+          f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int r = 0; r < (B < 4 ? B : 4); ++r) {
-            acc[sp][r] = fmaf(md[0], fmaf(md[1], sx0[r], P0[r]), acc[sp][r]);
-            acc[sp][r] = fmaf(md[2], fmaf(md[3], sx1[r], P1[r]), acc[sp][r]);
-          }
+          for (int t = 0; t < 4; ++t) P = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t], unpack8_sub(dd[t]), P, 0, 0, 0);
+          const float2 md = *reinterpret_cast<const float2*>(ml + row * MLR + 4 * wave + 2 * (h >> 1));  // d, -z
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[sp][r] = fmaf(md.x, fmaf(md.y, sxv[r], P[r]), acc[sp][r]);
         }
       } else {  // GS == 128: the chunk is one group; lane group h holds codes 32 h .. 32 h + 31
         f16x8 A[4];
@@ -270,13 +282,31 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __rest
   }
   // ---- the 16 waves' partial sums of each output, added in wave order (stage memory reused)
   float* red = reinterpret_cast<float*>(lds_raw);  // [SPB][16 waves][B][16]
+  if constexpr (GS == 64) {
+    // first groups' sums (lanes 0-31) plus second groups' (lanes 32-63): one swap of the pair
+    // (r, r + 1) leaves row r's total in lanes 0-31 and row r + 1's in lanes 32-63, so lane
+    // (h, n) holds batch row 4 (h & 1) + r + (h >> 1)
 #pragma unroll
-  for (int sp = 0; sp < SPB; ++sp)
+    for (int sp = 0; sp < SPB; ++sp)
 #pragma unroll
-    for (int r = 0; r < (B < 4 ? B : 4); ++r) {
-      const int m = 4 * h + r;
-      if (m < B) red[((sp * kMfWaves + wave) * B + m) * 16 + nl] = acc[sp][r];
-    }
+      for (int r = 0; r < 4; r += 2) {
+        // (__float_as_uint on the element values: a bit cast of a vector element lvalue reads
+        // element 0 with this compiler)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[sp][r]), __float_as_uint(acc[sp][r + 1]),
+                                                         false, false);
+        const float t = __uint_as_float((unsigned)sw[0]) + __uint_as_float((unsigned)sw[1]);
+        const int m = 4 * (h & 1) + r + (h >> 1);
+        if (m < B) red[((sp * kMfWaves + wave) * B + m) * 16 + nl] = t;
+      }
+  } else {
+#pragma unroll
+    for (int sp = 0; sp < SPB; ++sp)
+#pragma unroll
+      for (int r = 0; r < (B < 4 ? B : 4); ++r) {
+        const int m = 4 * h + r;
+        if (m < B) red[((sp * kMfWaves + wave) * B + m) * 16 + nl] = acc[sp][r];
+      }
+  }
   lds_barrier();
   if (tid < SPB * B * 16) {
     const int sp = tid / (B * 16), m = (tid / 16) % B, col = tid % 16;
@@ -661,7 +691,7 @@ template <int B, int GS, int SPB, int NSEG>
 void gemv_mf_launch(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                     const __half* x, void* y, int y_dtype, hipStream_t st) {
   hipLaunchKernelGGL((k_gemv_mf<B, GS, SPB, NSEG>), dim3((unsigned)(N / (16 * SPB))), dim3(64 * kMfWaves),
-                     2 * mf_stage_bytes(B, GS, SPB), st, packed, delta, zero, N, K, x, y, y_dtype);
+                     mf_lds_bytes(B, GS, SPB), st, packed, delta, zero, N, K, x, y, y_dtype);
 }
 
 template <int B, int GS, int SPB>
@@ -716,7 +746,7 @@ hipError_t gemv_gs(const uint8_t* packed, const __half* delta, const __half* zer
 size_t gemv_lds_bytes(int64_t K, int gs, int64_t batch) {
   if (gemv_uses_valu(K, batch)) return (size_t)valu_lds_bytes((int)batch, K);
   if (batch < 1 || batch > 8) return 0;
-  return 2 * (size_t)mf_stage_bytes((int)batch, gs, 2);  // the two-strip layout is the larger
+  return (size_t)mf_lds_bytes((int)batch, gs, 2);  // the two-strip layout is the larger
 }
 
 hipError_t launch_gemv(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int gs,
