@@ -265,9 +265,24 @@ int hqq_dequantize(const void* packed, const void* delta, const void* zero, int 
  * N must be a multiple of 16 and K of 128.  batch <= 8 uses a streaming kernel that
  * keeps q exact and applies delta and zero per group on fp32 partial sums; larger
  * batches use an MFMA GEMM on fp16 W_hat tiles.  Accumulation is fp32 in both.
+ * Above batch 8, with N a multiple of 128 and K of 256, the call runs the split GEMM of
+ * hqq_gemm_w4a16 on a workspace the library owns: one device buffer per (device, stream),
+ * allocated (hipMalloc, after synchronising that stream when an older, smaller one is
+ * replaced) on the first call that needs more than the stream's buffer holds, and kept until
+ * hqq_release_workspaces or the end of the process.  Calls on different streams never share
+ * a buffer.  Callers that must not allocate (inside graph capture, say) make one call of the
+ * largest batch on the stream first, or call hqq_gemm_w4a16 with their own workspace.  Other
+ * shapes above batch 8 run a single-pass MFMA GEMM with no workspace.
  */
 int hqq_gemv_w4a16(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K,
                    int group_size, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* stream);
+
+/*
+ * Frees the workspaces hqq_gemv_w4a16 keeps per (device, stream) (waits for each device's
+ * work).  The next call above batch 8 allocates again.  No call of hqq_gemv_w4a16 may run
+ * concurrently on another host thread.  Returns HQQ_OK or HQQ_ERR_DEVICE.
+ */
+int hqq_release_workspaces(void);
 
 /*
  * Batched fused product with a caller-provided workspace (same operation, operands and

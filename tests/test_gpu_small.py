@@ -317,6 +317,54 @@ def test_gemm_split_errors():
         hq.hqq_gemm_w4a16(pk, md, md, 64, 512, 64, x)
 
 
+@pytest.mark.parametrize("g", [64, 128])
+@pytest.mark.parametrize("N,K,batch", [(384, 1280, 9), (128, 512, 64), (256, 2048, 300)])
+def test_gemv_w4a16_split_path(g, N, K, batch):
+    """Above batch 8, with N a multiple of 128 and K of 256, hqq_gemv_w4a16 runs the split GEMM on
+    the workspace the library keeps for the stream: the oracle's values, and bit for bit the
+    result of hqq_gemm_w4a16 with a caller's workspace."""
+    import weight_only_quantization_amd as hq
+    say("gemv_w4a16 split path", g, N, K, batch)
+    torch = torch_dev()
+    packed, d16, z16 = gemv_inputs(N, K, g, seed=5200 + N + K)
+    x = synth.activations(batch, K, seed=19)
+    check_gemv(packed, d16, z16, N, K, g, x, out_f32=True)
+    args = (torch.from_numpy(packed).cuda(), torch.from_numpy(d16).cuda(), torch.from_numpy(z16).cuda(), N, K, g,
+            torch.from_numpy(x).cuda())
+    for dt in (torch.float32, torch.float16):
+        a = hq.hqq_gemv_w4a16(*args, out_dtype=dt)
+        b = hq.hqq_gemm_w4a16(*args, out_dtype=dt)
+        assert torch.equal(a, b)
+
+
+def test_gemv_w4a16_workspace_streams():
+    """The library's workspaces: calls of different batches interleaved on two streams (one buffer
+    each), a batch that outgrows a stream's buffer, then a release and a call that allocates
+    again; every result equals the same call's result on the default stream."""
+    import weight_only_quantization_amd as hq
+    say("gemv_w4a16 workspaces on two streams")
+    torch = torch_dev()
+    N, K, g = 256, 1024, 64
+    packed, d16, z16 = gemv_inputs(N, K, g, seed=5300)
+    w = (torch.from_numpy(packed).cuda(), torch.from_numpy(d16).cuda(), torch.from_numpy(z16).cuda())
+    xs = {b: torch.from_numpy(synth.activations(b, K, seed=23 + b)).cuda() for b in (16, 200, 700)}
+    ref = {b: hq.hqq_gemv_w4a16(*w, N, K, g, xs[b], out_dtype=torch.float32) for b in xs}
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for rep in range(3):
+        for b, st in ((16, s1), (200, s2), (200, s1), (16, s2), (700, s1 if rep else s2)):
+            with torch.cuda.stream(st):
+                outs.append((b, hq.hqq_gemv_w4a16(*w, N, K, g, xs[b], out_dtype=torch.float32, stream=st)))
+    torch.cuda.synchronize()
+    for b, y in outs:
+        assert torch.equal(y, ref[b]), b
+    hq.hqq_release_workspaces()
+    y = hq.hqq_gemv_w4a16(*w, N, K, g, xs[200], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref[200])
+
+
 # ---------------------------------------------------------------------------- input gradient
 
 @pytest.mark.parametrize("g", [64, 128])

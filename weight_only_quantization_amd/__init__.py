@@ -37,7 +37,7 @@ EXPORTS = ("hqq_packed_bytes", "hqq_num_groups", "hqq_quantize_workspace_bytes",
            "hqq_quantize_v2", "hqq_quantize_v2_workspace_bytes",
            "hqq_dequantize", "hqq_gemv_w4a16", "hqq_gemm_workspace_bytes", "hqq_gemm_w4a16",
            "hqq_gemm_dx_workspace_bytes", "hqq_gemm_w4a16_dx", "hqq_gemm_dx", "hqq_gemv", "hqq_gemm",
-           "hqq_status_string", "hqq_last_error")
+           "hqq_release_workspaces", "hqq_status_string", "hqq_last_error")
 
 _lib = None
 
@@ -93,6 +93,8 @@ def load(path: str = LIB_PATH):
     lib.hqq_gemm.restype = i32
     lib.hqq_status_string.argtypes = [i32]
     lib.hqq_status_string.restype = ctypes.c_char_p
+    lib.hqq_release_workspaces.argtypes = []
+    lib.hqq_release_workspaces.restype = i32
     lib.hqq_last_error.argtypes = []
     lib.hqq_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -389,7 +391,9 @@ def hqq_dequantize(packed, delta, zero, rows: int, cols: int, nbits: int, group_
 
 def hqq_gemv_w4a16(packed, delta, zero, N: int, K: int, group_size: int, x, out_dtype=None, out=None,
                    stream=None):
-    """y [batch, N] = x [batch, K] @ W_hat^T for a 4-bit axis=1 weight W [N, K]."""
+    """y [batch, N] = x [batch, K] @ W_hat^T for a 4-bit axis=1 weight W [N, K].  Above batch 8
+    the library runs its split GEMM on a workspace it keeps per stream (hqq_release_workspaces
+    frees them)."""
     import torch
     lib = load()
     out_dtype = out_dtype or torch.float16
@@ -404,6 +408,11 @@ def hqq_gemv_w4a16(packed, delta, zero, N: int, K: int, group_size: int, x, out_
                             ctypes.c_void_p(out.data_ptr()), code, _stream_ptr(stream))
     _check(st)
     return out
+
+
+def hqq_release_workspaces():
+    """Frees the workspaces hqq_gemv_w4a16 keeps per stream above batch 8."""
+    _check(load().hqq_release_workspaces())
 
 
 def hqq_gemm_workspace_bytes(N: int, K: int, batch: int) -> int:

@@ -7,6 +7,8 @@
 #include <string.h>
 
 #include <mutex>
+#include <thread>
+#include <vector>
 
 #include "hqq_internal.h"
 
@@ -232,6 +234,67 @@ int scratch_for_current_device(void** out) {
 
 }  // namespace
 
+// ------------------------------------------------------------------------------------------
+// Library-owned workspaces of hqq_gemv_w4a16 above batch 8 (the split GEMM needs a tiled copy
+// of x and the splits' partial sums): one buffer per (device, stream), grown on demand and kept
+// until hqq_release_workspaces or the end of the process.  Calls on one stream run in order and
+// share its buffer; calls on different streams never share one (hipStreamPerThread is a
+// different stream on every host thread, so its entries are per thread).  g_ws_mutex is held
+// while a call enqueues its kernels, so calls from several host threads on one stream do not
+// interleave on the buffer.
+// ------------------------------------------------------------------------------------------
+namespace {
+
+struct StreamWs {
+  int dev;
+  hipStream_t st;
+  std::thread::id thread;  // hipStreamPerThread only
+  void* ptr;
+  size_t bytes;
+};
+std::mutex g_ws_mutex;
+std::vector<StreamWs> g_ws;  // a handful of entries: searched linearly
+
+// The buffer of (current device, st) with at least `need` bytes; g_ws_mutex held by the caller.
+int stream_workspace(hipStream_t st, size_t need, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  const std::thread::id tid = st == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
+  StreamWs* w = nullptr;
+  for (auto& c : g_ws)
+    if (c.dev == dev && c.st == st && c.thread == tid) w = &c;
+  if (!w) {
+    try {
+      g_ws.push_back(StreamWs{dev, st, tid, nullptr, 0});
+    } catch (...) {
+      return fail(HQQ_ERR_WORKSPACE, "no host memory for the workspace table");
+    }
+    w = &g_ws.back();
+  }
+  if (w->bytes < need) {
+    if (w->ptr) {
+      e = hipStreamSynchronize(st);  // the stream's earlier calls may still use the old buffer
+      if (e != hipSuccess) return device_fail(e, "hipStreamSynchronize");
+      e = hipFree(w->ptr);
+      w->ptr = nullptr;
+      w->bytes = 0;
+      if (e != hipSuccess) return device_fail(e, "hipFree");
+    }
+    const size_t bytes = (need + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);  // whole MiB
+    e = hipMalloc(&w->ptr, bytes);
+    if (e != hipSuccess) {
+      w->ptr = nullptr;
+      return device_fail(e, "hipMalloc of the batched product's workspace");
+    }
+    w->bytes = bytes;
+  }
+  *out = w->ptr;
+  return HQQ_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int hqq_quantize_noalloc(const void* W_fp16, int64_t rows, int64_t cols, int nbits, int group_size, int axis,
@@ -368,11 +431,36 @@ int hqq_gemv_w4a16(const void* packed, const void* delta_fp16, const void* zero_
   if (batch <= 8) {
     if (hqq::gemv_lds_bytes(K, group_size, batch) > 160 * 1024) return fail(HQQ_ERR_UNSUPPORTED, "LDS too large");  // 160 KB per workgroup on gfx950
     e = hqq::launch_gemv(pk, dl, zr, N, K, group_size, xx, batch, y, y_dtype, st);
+  } else if (hqq::gemm_splits(N, K, batch) != 0) {  // the split GEMM on the stream's workspace
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    void* ws = nullptr;
+    const int s = stream_workspace(st, hqq::gemm_workspace_bytes(N, K, batch), &ws);
+    if (s != HQQ_OK) return s;
+    e = hqq::launch_gemm_split(pk, dl, zr, N, K, group_size, xx, batch, y, y_dtype, ws, st);
   } else {
     e = hqq::launch_gemm(pk, dl, zr, N, K, group_size, xx, batch, y, y_dtype, st);
   }
   if (e != hipSuccess) return device_fail(e, "hqq_gemv_w4a16 launch");
   return HQQ_OK;
+}
+
+int hqq_release_workspaces(void) {
+  g_last_error[0] = 0;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  int status = HQQ_OK;
+  for (auto& c : g_ws) {
+    if (!c.ptr) continue;
+    e = hipSetDevice(c.dev);
+    if (e == hipSuccess) e = hipFree(c.ptr);  // waits for the device's work
+    if (e != hipSuccess && status == HQQ_OK) status = device_fail(e, "hipFree of a workspace");
+  }
+  g_ws.clear();
+  e = hipSetDevice(cur);
+  if (e != hipSuccess && status == HQQ_OK) status = device_fail(e, "hipSetDevice");
+  return status;
 }
 
 size_t hqq_gemm_workspace_bytes(int64_t N, int64_t K, int64_t batch) {
