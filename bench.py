@@ -242,9 +242,9 @@ def config_legs(a, timed, stream, dev, rotated, read_floor, fan, assign):
     def gemv_leg(name, q, N, K, nbits, g, axis, byt_w):
         ncopy = max(4, int(np.ceil(1.1e9 / byt_w)))
         copies = [(q.packed.clone(), q.delta.clone(), q.zero.clone()) for _ in range(ncopy)]
-        X = torch.from_numpy(synth.activations(8, K, 402)).to(dev)
+        X = torch.from_numpy(synth.activations(16, K, 402)).to(dev)
         legs["%s_read_floor" % name] = read_floor(copies)
-        for b in ((1, 2, 8) if axis == 0 else (1, 2)):
+        for b in ((1, 2, 8) if axis == 0 else (1, 2, 8, 16)):
             Y = torch.empty((b, N), dtype=torch.float16, device=dev)
 
             def gv(r, b=b, Y=Y):
@@ -255,8 +255,8 @@ def config_legs(a, timed, stream, dev, rotated, read_floor, fan, assign):
             legs["%s_b%d" % (name, b)] = {"us": tg * 1e6, "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM,
                                           "bytes": byt, "shape": [N, K], "copies_rotated": ncopy,
                                           "frac_of_read_floor": legs["%s_read_floor" % name]["us"] / (tg * 1e6)}
-        # the batched product over the same format at batch 8 and 256 (hqq_gemm)
-        for B in (8, 256):
+        # the batched product over the same format at batch 256 (hqq_gemm)
+        for B in (256,):
             X2 = torch.from_numpy(synth.activations(B, K, 403)).to(dev)
             Y = torch.empty((B, N), dtype=torch.float16, device=dev)
             ws = torch.empty(hq.hqq_gemm_workspace_bytes(N, K, B), dtype=torch.uint8, device=dev)

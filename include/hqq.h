@@ -368,10 +368,15 @@ int hqq_gemm_dx(const void* packed, const void* delta_fp16, const void* zero_fp1
  * K a multiple of 32, batch 1 or 2, K <= 16384, or batch 3..8 with K a multiple of 128 (the
  * MFMA unit; any K); nbits=2 axis=1 group_size 16 with N a multiple of 16, K a multiple of
  * 64, batch 1 or 2, K <= 16384; nbits=3 axis=1 with group_size 16..256, N a multiple of 4,
- * 40 <= K <= 8192, batch 1 or 2 (rows start inside the ten-code words).  Other combinations
- * return HQQ_ERR_UNSUPPORTED.  Codes stay exact (fp16 subnormals into v_dot2_f32_f16 or
- * v_mfma_f32_16x16x32_f16); fp32 sums.  Axis 0 forms a = x * delta of the weight's
- * metadata row in fp16 (one rounding) and subtracts sum_k a z.
+ * 40 <= K <= 8192, batch 1 or 2 (rows start inside the ten-code words); nbits=3 (group_size
+ * 16..256) and nbits=2 (group_size 16) axis=1 at batch 3..16 with any N and K a multiple of
+ * 128, K <= 12288 (3-bit) or 16384 (2-bit), twice that with at most 8160 rows.  Other
+ * combinations return HQQ_ERR_UNSUPPORTED.  Batches 1-2 and axis-0 codes keep the codes exact
+ * (fp16 subnormals into v_dot2_f32_f16 or v_mfma_f32_16x16x32_f16; axis 0 forms
+ * a = x * delta of the weight's metadata row in fp16, one rounding, and subtracts sum_k a z);
+ * 3/2-bit batches 3..16 dequantise each code to fp16 W_hat = fp16(q delta - z delta) (one
+ * rounding of the exact value) in registers and multiply on v_mfma_f32_16x16x32_f16.  fp32
+ * sums throughout; the waves' partial sums are added in a fixed order (deterministic).
  */
 int hqq_gemv(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K, int nbits,
              int group_size, int axis, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* stream);

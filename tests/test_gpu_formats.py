@@ -1,7 +1,7 @@
 """GPU parity of the fused product for the other stored formats (hqq_gemv): 4-bit with
 axis-0 groups, 3-bit (ten codes per 32-bit word, rows starting inside words) and 2-bit with
-axis-1 groups of 16, against the oracle's fp64 product of the same stored codes and fp16
-metadata.
+axis-1 groups of 16 (batch 1-2 on the dot-product units, 3-16 on the matrix units), against the
+oracle's fp64 product of the same stored codes and fp16 metadata.
 
 Inputs are seeded synthetic codes and metadata (steps U(1e-3, 5e-2), zeros U(0, 2^b - 1),
 activations N(0, 1), all fp16), packed by the oracle; sizes span several lanes' chunks, a
@@ -95,6 +95,39 @@ def test_3bit_full_shape():
     _check(N, K, 3, 64, 1, (1, 2), seed=3003, rows_sel=sel)
 
 
+# batch 3..16 (3/2-bit, the tile dequantised in registers into the MFMA): a block of 32 rows splits
+# the K / 128 chunks among 8 waves (4 from 8192 rows on).  Cases: one chunk for 8 waves (seven
+# empty runs), ragged strips (N = 40, 100, 8 rows), runs of unequal length (C = 5, 9, 86), every
+# row-start slot of the 3-bit words (K mod 10 = 8, 6, 4, 2, 0 for K = 128 .. 640), every group
+# size, and the longest rows the chunk counts take (3-bit 12288 codes, 2-bit 32768).
+DQ_BATCHES = (3, 4, 5, 8, 9, 16)
+CASES_DQ_3B = [(16, 16, 128), (32, 40, 256), (64, 100, 384), (128, 24, 512), (128, 48, 640), (64, 64, 1152),
+               (16, 32, 4096), (256, 8, 8192), (64, 8, 12288)]
+
+
+@pytest.mark.parametrize("g,N,K", CASES_DQ_3B, ids=lambda v: str(v))
+def test_3bit_batched(g, N, K):
+    _check(N, K, 3, g, 1, DQ_BATCHES, seed=2700 + g + N + K)
+
+
+CASES_DQ_2B = [(16, 128), (40, 640), (100, 1152), (64, 4096), (48, 16384), (8, 32768)]
+
+
+@pytest.mark.parametrize("N,K", CASES_DQ_2B, ids=lambda v: str(v))
+def test_2bit_batched(N, K):
+    _check(N, K, 2, 16, 1, DQ_BATCHES, seed=2800 + N + K)
+
+
+@pytest.mark.parametrize("nbits,g", [(3, 64), (2, 16)], ids=["3bit_g64", "2bit_g16"])
+def test_batched_full_shapes(nbits, g):
+    """The 11008 x 4096 projection (4 waves per block) at batch 3, 8 and 16 and the 4096 x 11008 one
+    (8 waves, runs of 10 and 11 chunks) at batch 8, sampled rows."""
+    sel = np.sort(np.random.default_rng(10).choice(11008, 512, replace=False))
+    _check(11008, 4096, nbits, g, 1, (3, 8, 16), seed=3010 + nbits, rows_sel=sel)
+    sel = np.sort(np.random.default_rng(11).choice(4096, 384, replace=False))
+    _check(4096, 11008, nbits, g, 1, (8,), seed=3020 + nbits, rows_sel=sel)
+
+
 def test_axis0_full_shape():
     """The 70B-MLP shape of the axis-0 quantizer workload: 28672 x 8192, g = 128, batch 1 and 8."""
     N, K = 28672, 8192
@@ -120,8 +153,14 @@ def test_unsupported_formats_rejected():
             hq.hqq_gemv(pk, md, md, 64, 128, nbits, g, axis, x)
     with pytest.raises(hq.HQQError):  # 3-bit rows shorter than 40 codes
         hq.hqq_gemv(pk, md, md, 64, 32, 3, 16, 1, x[:, :32].contiguous())
-    with pytest.raises(hq.HQQError):  # batch 3 is not fused for 3-bit codes
-        hq.hqq_gemv(pk, md, md, 64, 128, 3, 16, 1, torch.zeros((3, 128), dtype=torch.float16, device="cuda"))
+    with pytest.raises(hq.HQQError):  # batch 17 is not fused for 3-bit codes
+        hq.hqq_gemv(pk, md, md, 64, 128, 3, 16, 1, torch.zeros((17, 128), dtype=torch.float16, device="cuda"))
+    with pytest.raises(hq.HQQError):  # batch 3..16: K a multiple of 128
+        hq.hqq_gemv(pk, md, md, 16, 192, 2, 16, 1, torch.zeros((3, 192), dtype=torch.float16, device="cuda"))
+    pk3 = torch.zeros(hq.load().hqq_packed_bytes(1, 24704, 3), dtype=torch.uint8, device="cuda")
+    md3 = torch.zeros(24704 // 16, dtype=torch.float16, device="cuda")
+    with pytest.raises(hq.HQQError):  # batch 3..16, 3-bit: rows past 24576 codes
+        hq.hqq_gemv(pk3, md3, md3, 1, 24704, 3, 16, 1, torch.zeros((3, 24704), dtype=torch.float16, device="cuda"))
     with pytest.raises(hq.HQQError):  # nor batch 9 for axis-0 codes
         hq.hqq_gemv(pk, md, md, 64, 128, 4, 16, 0, torch.zeros((9, 128), dtype=torch.float16, device="cuda"))
     with pytest.raises(hq.HQQError):  # axis 0, batch 3..8: K a multiple of 128

@@ -530,7 +530,7 @@ def hqq_gemm_dx(packed, delta, zero, N: int, K: int, nbits: int, group_size: int
 def hqq_gemv(packed, delta, zero, N: int, K: int, nbits: int, group_size: int, axis: int, x, out_dtype=None,
              out=None, stream=None):
     """y [batch, N] = x [batch, K] @ W_hat^T for any stored format the library fuses
-    (4-bit axis 1 or 0 at batch 1-8, 3-bit axis 1 and 2-bit axis 1 with groups of 16 at batch 1-2;
+    (4-bit axis 1 or 0 at batch 1-8, 3-bit axis 1 and 2-bit axis 1 with groups of 16 at batch 1-16;
     larger batches: hqq_gemm)."""
     import torch
     lib = load()

@@ -24,7 +24,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-ffp-contract=
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-I" + os.path.join(HERE, "..", "include")]
 
-SOURCES = ["hqq_api.hip", "hqq_quant.hip", "hqq_dequant.hip", "hqq_gemv.hip", "hqq_gemv_ext.hip", "hqq_gemm.hip"]
+SOURCES = ["hqq_api.hip", "hqq_quant.hip", "hqq_dequant.hip", "hqq_gemv.hip", "hqq_gemv_ext.hip", "hqq_gemv_dq.hip", "hqq_gemm.hip"]
 # HBM probes of known byte counts (measurement only), a library of their own
 PROBE_SOURCES = ["hqq_probe.hip"]
 

@@ -621,8 +621,8 @@ int hqq_gemv(const void* packed, const void* delta_fp16, const void* zero_fp16, 
   if (!packed || !delta_fp16 || !zero_fp16 || !x_fp16 || !y) return fail(HQQ_ERR_INVALID_ARGUMENT, "null buffer");
   if (!aligned16(packed) || !aligned16(delta_fp16) || !aligned16(zero_fp16) || !aligned16(x_fp16) || !aligned16(y))
     return fail(HQQ_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
-  if (batch > (nbits == 4 ? 8 : 2))
-    return fail(HQQ_ERR_UNSUPPORTED, "batch must be at most 8 for axis-0 4-bit codes and 1 or 2 for 3/2-bit codes");
+  if (batch > (nbits == 4 ? 8 : 16))
+    return fail(HQQ_ERR_UNSUPPORTED, "batch must be at most 8 for axis-0 4-bit codes and 16 for 3/2-bit codes");
   if (batch <= 2 && K > 16384) return fail(HQQ_ERR_UNSUPPORTED, "K must be at most 16384 for this format");
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint8_t* pk = reinterpret_cast<const uint8_t*>(packed);
@@ -630,7 +630,14 @@ int hqq_gemv(const void* packed, const void* delta_fp16, const void* zero_fp16, 
   const __half* zr = reinterpret_cast<const __half*>(zero_fp16);
   const __half* xx = reinterpret_cast<const __half*>(x_fp16);
   hipError_t e;
-  if (nbits == 4 && axis == 0) {
+  if (batch > 2 && axis == 1) {  // 3/2-bit codes, batch 3-16: the tile dequantised in registers into the MFMA
+    if (nbits == 2 && group_size != 16)
+      return fail(HQQ_ERR_UNSUPPORTED, "no fused product for nbits=2 group_size=%d", group_size);
+    if (!hqq::gemv_dq_supported(N, K, nbits, group_size, batch))
+      return fail(HQQ_ERR_UNSUPPORTED, "batch 3-16: K must be a multiple of 128 and at most %s, group_size 16..256",
+                  nbits == 3 ? "12288 (24576 with at most 8160 rows)" : "16384 (32768 with at most 8160 rows)");
+    e = hqq::launch_gemv_dq(pk, dl, zr, N, K, nbits, group_size, xx, batch, y, y_dtype, st);
+  } else if (nbits == 4 && axis == 0) {
     if (!pow2_group(group_size)) return fail(HQQ_ERR_UNSUPPORTED, "group_size must be 16, 32, 64, 128 or 256");
     if (K % 32 != 0) return fail(HQQ_ERR_UNSUPPORTED, "K must be a multiple of 32");
     if (batch > 2 && K % 128 != 0) return fail(HQQ_ERR_UNSUPPORTED, "batch 3-8: K must be a multiple of 128");

@@ -43,51 +43,6 @@ constexpr size_t kSkLds = 2 * kSkBN * (kSkBK + 16) * sizeof(_Float16);  // the l
 constexpr int kSkMulWaves = 4;      // multiplying waves, each 64 batch rows x all 128 weight rows
 constexpr int kSkThreads = 512;     // and as many staging waves
 
-// Eight 4-bit codes of a word (natural order) -> fp16 W_hat pairs (c0,c1), (c2,c3), (c4,c5), (c6,c7).
-// t0 = (c0, c4), t1 = 16 (c1, c5), t2 = (c2, c6), t3 = 16 (c3, c7) as fp16 subnormals.
-__device__ __forceinline__ u32x4 wq8(unsigned w, float ds24, float ds20, float zd) {
-  const unsigned u = w >> 8;
-  const f16x2 h0 = as_h2(w & 0x000F000Fu), h1 = as_h2(w & 0x00F000F0u);
-  const f16x2 h2 = as_h2(u & 0x000F000Fu), h3 = as_h2(u & 0x00F000F0u);
-  const f16x2 p0 = {(_Float16)__builtin_fmaf((float)h0[0], ds24, -zd), (_Float16)__builtin_fmaf((float)h1[0], ds20, -zd)};
-  const f16x2 p1 = {(_Float16)__builtin_fmaf((float)h2[0], ds24, -zd), (_Float16)__builtin_fmaf((float)h3[0], ds20, -zd)};
-  const f16x2 p2 = {(_Float16)__builtin_fmaf((float)h0[1], ds24, -zd), (_Float16)__builtin_fmaf((float)h1[1], ds20, -zd)};
-  const f16x2 p3 = {(_Float16)__builtin_fmaf((float)h2[1], ds24, -zd), (_Float16)__builtin_fmaf((float)h3[1], ds20, -zd)};
-  return u32x4{as_u(p0), as_u(p1), as_u(p2), as_u(p3)};
-}
-
-// Sixteen 2-bit codes of a word (natural order) -> fp16 W_hat pairs: lo = (c0,c1) .. (c6,c7),
-// hi = (c8,c9) .. (c14,c15).  The masks 3 << 2t on w and on w >> 8 give (c_t, c_t+8) and
-// (c_t+4, c_t+12) as fp16 subnormals at 4^t 2^-24; ds[t] = d 2^24 / 4^t.
-__device__ __forceinline__ void wq16_2b(unsigned w, const float (&ds)[4], float zd, u32x4& lo, u32x4& hi) {
-  const unsigned u = w >> 8;
-  f16x2 h[8];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    h[t] = as_h2(w & (0x00030003u << (2 * t)));
-    h[4 + t] = as_h2(u & (0x00030003u << (2 * t)));
-  }
-  auto pr = [&](int a, int b, int e) {  // codes of h[a] and h[b], element e (0 low, 1 high)
-    return as_u(f16x2{(_Float16)__builtin_fmaf((float)h[a][e], ds[a & 3], -zd),
-                      (_Float16)__builtin_fmaf((float)h[b][e], ds[b & 3], -zd)});
-  };
-  lo = u32x4{pr(0, 1, 0), pr(2, 3, 0), pr(4, 5, 0), pr(6, 7, 0)};
-  hi = u32x4{pr(0, 1, 1), pr(2, 3, 1), pr(4, 5, 1), pr(6, 7, 1)};
-}
-
-// Eight 3-bit codes in bits 0..23 of v (natural order) -> fp16 W_hat pairs (c0,c1) .. (c6,c7):
-// spread to two halves (codes 4..7 move up by 4 bits), the masks 7 << 3t give (c_t, c_t+4) at
-// 8^t 2^-24 for t < 3 and the fourth pair after a 9-bit shift.
-__device__ __forceinline__ u32x4 wq8_3b(unsigned v, float ds24, float ds21, float ds18, float zd) {
-  const unsigned x0 = (v & 0x00000FFFu) | ((v << 4) & 0x0FFF0000u);
-  const f16x2 h0 = as_h2(x0 & 0x00070007u), h1 = as_h2(x0 & 0x00380038u), h2 = as_h2(x0 & 0x01C001C0u),
-              h3 = as_h2((x0 >> 9) & 0x00070007u);
-  auto pr = [&](f16x2 a, float sa, f16x2 b, float sb, int e) {
-    return as_u(f16x2{(_Float16)__builtin_fmaf((float)a[e], sa, -zd), (_Float16)__builtin_fmaf((float)b[e], sb, -zd)});
-  };
-  return u32x4{pr(h0, ds24, h1, ds21, 0), pr(h2, ds18, h3, ds24, 0), pr(h0, ds24, h1, ds21, 1), pr(h2, ds18, h3, ds24, 1)};
-}
-
 // Stored formats the split GEMM stages (4-bit axis 1 has its group size as a template
 // parameter; the others take log2 of it at run time).  kFmt4A0: 4-bit codes with axis-0 groups
 // (weight row n uses metadata row n mod (N/g), one step and zero per column).
@@ -249,22 +204,7 @@ __global__ void __launch_bounds__(kSkThreads) k_gemm_sk(const uint8_t* __restric
             wq16_2b(r.w[p][h], ds, zd[h], o[2 * h], o[2 * h + 1]);
           }
         } else {
-            // block b (codes 8b..8b+7) starts at slot o = ph + 8b of the window: in word o / 10,
-            // which is b - 1 or b (b >= 1) depending on ph; it ends in the next word or (o >= 30,
-            // then o / 10 = 3 and 3 (o - 30) + 24 <= 30) in the same one
-            const int ph = r.ph[p];
-            const unsigned* w = r.w[p];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const bool up = b > 0 && ph >= 2 * b;
-              const int i = up ? b : (b > 0 ? b - 1 : 0);
-              const unsigned lo = up ? w[b] : w[b > 0 ? b - 1 : 0];
-              const unsigned hi = up ? (b < 3 ? w[b + 1] : 0u) : w[b > 0 ? b : 1];
-              const int sh = 3 * (ph + 8 * b - 10 * i);
-              const unsigned v = (unsigned)((((uint64_t)hi << 30) | (lo & 0x3FFFFFFFu)) >> sh);
-              const int h = b >> 1;
-              o[b] = wq8_3b(v, d[h] * 16777216.0f, d[h] * 2097152.0f, d[h] * 262144.0f, zd[h]);
-            }
+          decode32_3b(r.w[p], r.ph[p], d, zd, o);
         }
       };
       auto stage = [&](int buf, const Regs& r) {

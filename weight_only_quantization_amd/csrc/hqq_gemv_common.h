@@ -76,6 +76,83 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
     reinterpret_cast<float*>(y)[idx] = v;
 }
 
+// ---- Codes -> fp16 W_hat = fp16(c 2^-24 (d 2^24) - z d) in natural order (the mixed fp16/fp32
+// FMA: the code is a masked fp16 subnormal, z d is exact in fp32; one rounding to fp32 and one
+// to fp16).  Used where the weight tile is dequantised before the matrix units.
+// Eight 4-bit codes of a word (natural order) -> fp16 W_hat pairs (c0,c1), (c2,c3), (c4,c5), (c6,c7).
+// t0 = (c0, c4), t1 = 16 (c1, c5), t2 = (c2, c6), t3 = 16 (c3, c7) as fp16 subnormals.
+__device__ __forceinline__ u32x4 wq8(unsigned w, float ds24, float ds20, float zd) {
+  const unsigned u = w >> 8;
+  const f16x2 h0 = as_h2(w & 0x000F000Fu), h1 = as_h2(w & 0x00F000F0u);
+  const f16x2 h2 = as_h2(u & 0x000F000Fu), h3 = as_h2(u & 0x00F000F0u);
+  const f16x2 p0 = {(_Float16)__builtin_fmaf((float)h0[0], ds24, -zd), (_Float16)__builtin_fmaf((float)h1[0], ds20, -zd)};
+  const f16x2 p1 = {(_Float16)__builtin_fmaf((float)h2[0], ds24, -zd), (_Float16)__builtin_fmaf((float)h3[0], ds20, -zd)};
+  const f16x2 p2 = {(_Float16)__builtin_fmaf((float)h0[1], ds24, -zd), (_Float16)__builtin_fmaf((float)h1[1], ds20, -zd)};
+  const f16x2 p3 = {(_Float16)__builtin_fmaf((float)h2[1], ds24, -zd), (_Float16)__builtin_fmaf((float)h3[1], ds20, -zd)};
+  return u32x4{as_u(p0), as_u(p1), as_u(p2), as_u(p3)};
+}
+
+// Sixteen 2-bit codes of a word (natural order) -> fp16 W_hat pairs: lo = (c0,c1) .. (c6,c7),
+// hi = (c8,c9) .. (c14,c15).  The masks 3 << 2t on w and on w >> 8 give (c_t, c_t+8) and
+// (c_t+4, c_t+12) as fp16 subnormals at 4^t 2^-24; ds[t] = d 2^24 / 4^t.
+__device__ __forceinline__ void wq16_2b(unsigned w, const float (&ds)[4], float zd, u32x4& lo, u32x4& hi) {
+  const unsigned u = w >> 8;
+  f16x2 h[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    h[t] = as_h2(w & (0x00030003u << (2 * t)));
+    h[4 + t] = as_h2(u & (0x00030003u << (2 * t)));
+  }
+  // pair q: element q >> 2 of h[a] and h[a + 1], a = 2 (q & 3).  Each half is written on its own,
+  // which the compiler selects as one v_fma_mixlo/mixhi_f16 each (a two-element vector built at
+  // once became v_fma_mix_f32 pairs and a v_cvt_pk_f16_f32)
+  unsigned r[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int a = 2 * (q & 3), e = q >> 2;
+    f16x2 p;
+    p[0] = (_Float16)__builtin_fmaf((float)h[a][e], ds[a & 3], -zd);
+    p[1] = (_Float16)__builtin_fmaf((float)h[a + 1][e], ds[(a + 1) & 3], -zd);
+    r[q] = as_u(p);
+  }
+  lo = u32x4{r[0], r[1], r[2], r[3]};
+  hi = u32x4{r[4], r[5], r[6], r[7]};
+}
+
+// Eight 3-bit codes in bits 0..23 of v (natural order) -> fp16 W_hat pairs (c0,c1) .. (c6,c7):
+// spread to two halves (codes 4..7 move up by 4 bits), the masks 7 << 3t give (c_t, c_t+4) at
+// 8^t 2^-24 for t < 3 and the fourth pair after a 9-bit shift.
+__device__ __forceinline__ u32x4 wq8_3b(unsigned v, float ds24, float ds21, float ds18, float zd) {
+  const unsigned x0 = (v & 0x00000FFFu) | ((v << 4) & 0x0FFF0000u);
+  const f16x2 h0 = as_h2(x0 & 0x00070007u), h1 = as_h2(x0 & 0x00380038u), h2 = as_h2(x0 & 0x01C001C0u),
+              h3 = as_h2((x0 >> 9) & 0x00070007u);
+  auto pr = [&](f16x2 a, float sa, f16x2 b, float sb, int e) {
+    return as_u(f16x2{(_Float16)__builtin_fmaf((float)a[e], sa, -zd), (_Float16)__builtin_fmaf((float)b[e], sb, -zd)});
+  };
+  return u32x4{pr(h0, ds24, h1, ds21, 0), pr(h2, ds18, h3, ds24, 0), pr(h0, ds24, h1, ds21, 1), pr(h2, ds18, h3, ds24, 1)};
+}
+
+// Thirty-two 3-bit codes starting at an even slot ph (<= 8) of w[0] and ending in w[3] -> fp16
+// W_hat in natural order, o[b] = codes 8b .. 8b + 7; codes 0..15 take step d[0] and zero-step
+// product zd[0], codes 16..31 d[1], zd[1].  Block b starts at slot o = ph + 8b: in word o / 10,
+// which is b - 1 or b (b >= 1) depending on ph; it ends in the next word or (o >= 30, then
+// o / 10 = 3 and 3 (o - 30) + 24 <= 30) in the same one.  A 64-bit window of two words (30-bit
+// payloads) shifted by 3 (o mod 10) puts the block's 24 bits at bits 0..23.
+__device__ __forceinline__ void decode32_3b(const unsigned (&w)[4], int ph, const float (&d)[2], const float (&zd)[2],
+                                            u32x4 (&o)[4]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const bool up = b > 0 && ph >= 2 * b;
+    const int i = up ? b : (b > 0 ? b - 1 : 0);
+    const unsigned lo = up ? w[b] : w[b > 0 ? b - 1 : 0];
+    const unsigned hi = up ? (b < 3 ? w[b + 1] : 0u) : w[b > 0 ? b : 1];
+    const int sh = 3 * (ph + 8 * b - 10 * i);
+    const unsigned v = (unsigned)((((uint64_t)hi << 30) | (lo & 0x3FFFFFFFu)) >> sh);
+    const int h = b >> 1;
+    o[b] = wq8_3b(v, d[h] * 16777216.0f, d[h] * 2097152.0f, d[h] * 262144.0f, zd[h]);
+  }
+}
+
 // Sum of the eight fp16 values of a 16-byte block (fp32 accumulation of x * 1).
 __device__ __forceinline__ float block_sum8(const unsigned (&r4)[4]) {
   const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};

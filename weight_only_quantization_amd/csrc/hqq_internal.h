@@ -84,6 +84,11 @@ hipError_t launch_gemm_fmt(const uint8_t* packed, const __half* delta, const __h
 hipError_t launch_gemm_dx(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                           int nbits, int gs, int axis, const __half* dy, int64_t batch, void* dx, int dx_dtype,
                           void* workspace, hipStream_t st);
+// Fused product at batch 1-16 on the matrix units with the tile dequantised in registers
+// (2-, 3- and 4-bit codes, axis-1 groups): shapes it takes, launch.
+bool gemv_dq_supported(int64_t N, int64_t K, int nbits, int g, int64_t batch);
+hipError_t launch_gemv_dq(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
+                          int nbits, int g, const __half* x, int64_t batch, void* y, int y_dtype, hipStream_t st);
 // Fused product with 3-bit codes (axis 1, batch 1-2): shapes it takes, LDS bytes, launch.
 bool gemv_3b_supported(int64_t K, int g);
 size_t gemv_3b_lds_bytes(int64_t N, int64_t K, int g, int64_t batch);
