@@ -33,29 +33,47 @@ constexpr int kDqRows = 16 * kDqStrips;    // weight rows per block
 constexpr int kDqMaxWaves = 8;             // waves per block
 constexpr int kDqAhead = 3;                // chunks of codes and activations in flight ahead of their use
 
-template <int FMT, int NCW>
+template <int FMT, int NCW, bool EXACT>
 __global__ void __launch_bounds__(64 * kDqMaxWaves) k_gemv_dq(const uint8_t* __restrict__ packed,
                                                               const __half* __restrict__ delta,
                                                               const __half* __restrict__ zero, int64_t N, int64_t K,
                                                               int gs_log2, const __half* __restrict__ x, int64_t batch,
                                                               void* __restrict__ y, int out_dtype) {
-  static_assert(FMT == 2 || FMT == 3 || FMT == 4, "2-, 3- or 4-bit codes");
+  static_assert(FMT == 2 || FMT == 3, "2- or 3-bit codes");
   constexpr int RING = kDqAhead + 1;
   constexpr int SP = kDqStrips;
   __shared__ f32x4 red[kDqMaxWaves * SP * 64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nw = (int)(blockDim.x >> 6);
   const int nl = lane & 15, h = lane >> 4;
-  const int64_t C = K / 128;                                       // chunks per row
-  const int64_t c_lo = wave * C / nw, c_hi = (wave + 1) * C / nw;  // this wave's run (<= NCW chunks)
+  const int64_t C = K / 128;  // chunks per row
+  // this wave's run of chunks: EXACT, every run is NCW chunks (C = NCW nw); otherwise at most NCW,
+  // and chunk i of the run reads chunk max(0, min(i, nrun - 1)) past its end (c_lo < C, so a
+  // valid one even for an empty run)
+  const int64_t c_lo = EXACT ? (int64_t)wave * NCW : wave * C / nw;
+  const int nrun = EXACT ? NCW : (int)((wave + 1) * C / nw - c_lo);
   const int64_t r0 = (int64_t)blockIdx.x * kDqRows;
-  int64_t f_row[SP];  // flat index of the lane's first code in chunk 0 of its row, per strip
+  // per strip: flat index of the lane's first code in the run's first chunk (rows past N: the
+  // last row), and the pointers the run's loads step from
+  int64_t f_first[SP];
+  const uint8_t* pc[SP];      // 2-bit: byte of the lane's first code
+  const uint32_t* pq[SP];     // 3-bit: word of the lane's first code
+  int ph_first[SP];           // 3-bit: its slot in that word
+  const __half *pd[SP], *pz[SP];  // step and zero of its group
 #pragma unroll
-  for (int p = 0; p < SP; ++p) f_row[p] = min(r0 + 16 * p + nl, N - 1) * K + 32 * h;  // rows past N: the last row
-  const __half* xrow = x + min<int64_t>(nl, batch - 1) * K + 32 * h;
+  for (int p = 0; p < SP; ++p) {
+    f_first[p] = min(r0 + 16 * p + nl, N - 1) * K + 32 * h + 128 * c_lo;
+    pc[p] = packed + f_first[p] / 4;
+    const int64_t q = f_first[p] / 10;
+    pq[p] = reinterpret_cast<const uint32_t*>(packed) + q;
+    ph_first[p] = (int)(f_first[p] - 10 * q);
+    pd[p] = delta + (f_first[p] >> gs_log2);
+    pz[p] = zero + (f_first[p] >> gs_log2);
+  }
+  const __half* xrow = x + min<int64_t>(nl, batch - 1) * K + 32 * h + 128 * c_lo;
 
-  // ---- one chunk's loads for both strips: codes, and the step and zero of the lane's group (with
-  //      groups of 16, of its two groups)
+  // ---- one chunk's loads: codes, and the step and zero of the lane's group (with groups of 16,
+  //      of its two groups)
   struct WRegs {
     unsigned w[SP][4];
     unsigned dm[SP], zm[SP];
@@ -63,41 +81,41 @@ __global__ void __launch_bounds__(64 * kDqMaxWaves) k_gemv_dq(const uint8_t* __r
     bool valid;  // the chunk is in this wave's run
   };
   auto load_w = [&](int i, WRegs& r) {
-    const int64_t cc = c_lo + i;
-    r.valid = cc < c_hi;
-    const int64_t c = min(cc, C - 1);
+    r.valid = EXACT || i < nrun;
+    const int ci = EXACT ? i : max(0, min(i, nrun - 1));  // chunk of the run (an empty run: its first)
 #pragma unroll
     for (int p = 0; p < SP; ++p) {
-      const int64_t f0 = f_row[p] + 128 * c;
-      if constexpr (FMT == 4) {
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + f0 / 2));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r.w[p][e] = v[e];
-      } else if constexpr (FMT == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(packed + f0 / 4);
+      if constexpr (FMT == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(pc[p] + 32 * ci);
         r.w[p][0] = v.x, r.w[p][1] = v.y, r.w[p][2] = 0u, r.w[p][3] = 0u;
       } else {
-        const int64_t q0 = f0 / 10;
-        r.ph[p] = (int)(f0 - 10 * q0);
-        const uint32_t* pw = reinterpret_cast<const uint32_t*>(packed) + q0;
+        // 128 codes = 12 words and 8 slots: chunk ci starts at slot ph_first + 8 ci of word
+        // q_first + 12 ci (carried into the word index past slot 9)
+        int slot = ph_first[p] + (EXACT ? (8 * i) % 10 : 8 * ci);
+        int carry = EXACT ? (slot >= 10) : slot / 10;
+        slot -= 10 * carry;
+        r.ph[p] = slot;
+        const uint32_t* pw = pq[p] + (EXACT ? 12 * i + (8 * i) / 10 : 12 * ci) + carry;
 #pragma unroll
         for (int e = 0; e < 4; ++e) r.w[p][e] = pw[e];
       }
-      const int64_t gi = f0 >> gs_log2;
-      if (gs_log2 == 4) {  // groups of 16: the lane's two groups gi (even) and gi + 1 in one dword
-        r.dm[p] = *reinterpret_cast<const unsigned*>(delta + gi);
-        r.zm[p] = *reinterpret_cast<const unsigned*>(zero + gi);
+      // group entry: groups of <= 128 codes advance by 128 / g per chunk; 256 from the flat index
+      const int64_t go = gs_log2 <= 7 ? (int64_t)(128 >> gs_log2) * ci
+                                      : ((f_first[p] + 128 * ci) >> gs_log2) - (f_first[p] >> gs_log2);
+      if (gs_log2 == 4) {  // groups of 16: the lane's two groups (the first even) in one dword
+        r.dm[p] = *reinterpret_cast<const unsigned*>(pd[p] + go);
+        r.zm[p] = *reinterpret_cast<const unsigned*>(pz[p] + go);
       } else {  // one group: its entry in the low half
-        r.dm[p] = __half_as_ushort(delta[gi]);
-        r.zm[p] = __half_as_ushort(zero[gi]);
+        r.dm[p] = __half_as_ushort(pd[p][go]);
+        r.zm[p] = __half_as_ushort(pz[p][go]);
       }
     }
   };
   // A operand of one chunk: the four 16-byte pieces x[m][128 c + 32 h + 8 s .. +7]
   auto load_x = [&](int i, u32x4 (&a)[4]) {
-    const int64_t c = min(c_lo + i, C - 1);
+    const int ci = EXACT ? i : max(0, min(i, nrun - 1));
 #pragma unroll
-    for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const u32x4*>(xrow + 128 * c + 8 * s);
+    for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const u32x4*>(xrow + 128 * ci + 8 * s);
   };
   // W_hat of one strip's 32 codes: o[s] is the B operand of k-step s (codes 8s .. 8s + 7)
   auto decode = [&](const WRegs& r, int p, u32x4 (&o)[4]) {
@@ -111,10 +129,7 @@ __global__ void __launch_bounds__(64 * kDqMaxWaves) k_gemv_dq(const uint8_t* __r
       d[hh] = dv;
       zd[hh] = r.valid ? zv * dv : 0.f;
     }
-    if constexpr (FMT == 4) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) o[s] = wq8(r.w[p][s], d[s >> 1] * 16777216.0f, d[s >> 1] * 1048576.0f, zd[s >> 1]);
-    } else if constexpr (FMT == 2) {
+    if constexpr (FMT == 2) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const float ds[4] = {d[hh] * 16777216.0f, d[hh] * 4194304.0f, d[hh] * 1048576.0f, d[hh] * 262144.0f};
@@ -186,17 +201,19 @@ __global__ void __launch_bounds__(64 * kDqMaxWaves) k_gemv_dq(const uint8_t* __r
 constexpr int kDqNcw[] = {1, 2, 4, 6, 8, 12, 16, 24, 32};
 constexpr int dq_ncw_count(int fmt) { return fmt == 3 ? 8 : 9; }
 
-template <int FMT, int I = 0>
+// EXACT: the waves' runs are all `need` chunks long and `need` is one of the counts.
+template <int FMT, bool EXACT, int I = 0>
 hipError_t launch_dq_ncw(int need, dim3 grid, dim3 block, hipStream_t st, const uint8_t* packed, const __half* delta,
                          const __half* zero, int64_t N, int64_t K, int gl, const __half* x, int64_t batch, void* y,
                          int y_dtype) {
   if constexpr (I < dq_ncw_count(FMT)) {
-    if (need <= kDqNcw[I]) {
-      hipLaunchKernelGGL((k_gemv_dq<FMT, kDqNcw[I]>), grid, block, 0, st, packed, delta, zero, N, K, gl, x, batch, y,
-                         y_dtype);
+    if (EXACT ? need == kDqNcw[I] : need <= kDqNcw[I]) {
+      hipLaunchKernelGGL((k_gemv_dq<FMT, kDqNcw[I], EXACT>), grid, block, 0, st, packed, delta, zero, N, K, gl, x,
+                         batch, y, y_dtype);
       return hipGetLastError();
     }
-    return launch_dq_ncw<FMT, I + 1>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype);
+    return launch_dq_ncw<FMT, EXACT, I + 1>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y,
+                                            y_dtype);
   } else {
     return hipErrorInvalidValue;
   }
@@ -208,7 +225,7 @@ int dq_waves(int64_t) { return kDqMaxWaves; }
 }  // namespace
 
 bool gemv_dq_supported(int64_t N, int64_t K, int nbits, int g, int64_t batch) {
-  if (nbits < 2 || nbits > 4 || batch < 1 || batch > 16 || K % 128 != 0 || N < 1) return false;
+  if (nbits < 2 || nbits > 3 || batch < 1 || batch > 16 || K % 128 != 0 || N < 1) return false;
   if (g != 16 && g != 32 && g != 64 && g != 128 && g != 256) return false;
   if (nbits == 2 && g != 16) return false;
   const int64_t need = (K / 128 + dq_waves(N) - 1) / dq_waves(N);
@@ -220,14 +237,21 @@ hipError_t launch_gemv_dq(const uint8_t* packed, const __half* delta, const __ha
   int gl = 0;
   while ((1 << gl) < g) ++gl;
   const int nw = dq_waves(N);
-  const int need = (int)((K / 128 + nw - 1) / nw);
-  const dim3 grid((unsigned)((N + kDqRows - 1) / kDqRows)), block(64 * nw);
-  switch (nbits) {
-    case 4: return launch_dq_ncw<4>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype);
-    case 3: return launch_dq_ncw<3>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype);
-    case 2: return launch_dq_ncw<2>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype);
-    default: return hipErrorInvalidValue;
+  const int64_t C = K / 128;
+  const int need = (int)((C + nw - 1) / nw);
+  bool exact = C % nw == 0;
+  if (exact) {
+    exact = false;
+    for (int i = 0; i < dq_ncw_count(nbits); ++i) exact = exact || kDqNcw[i] == need;
   }
+  const dim3 grid((unsigned)((N + kDqRows - 1) / kDqRows)), block(64 * nw);
+  if (nbits == 3)
+    return exact ? launch_dq_ncw<3, true>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype)
+                 : launch_dq_ncw<3, false>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype);
+  if (nbits == 2)
+    return exact ? launch_dq_ncw<2, true>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype)
+                 : launch_dq_ncw<2, false>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace hqq
