@@ -262,14 +262,20 @@ int hqq_dequantize(const void* packed, const void* delta, const void* zero, int 
  *   group_size  64 or 128.
  *   x_fp16      in  fp16 [batch, K] row-major.
  *   y           out [batch, N] row-major, y_dtype HQQ_OUT_F16 or HQQ_OUT_F32.
- * N must be a multiple of 16 and K of 128.  batch <= 8 uses a streaming kernel that
- * keeps q exact and applies delta and zero per group on fp32 partial sums; larger
- * batches use an MFMA GEMM on fp16 W_hat tiles.  Accumulation is fp32 in both.
- * Above batch 8, with N a multiple of 128 and K of 256, the call runs the split GEMM of
- * hqq_gemm_w4a16 on a workspace the library owns: one device buffer per (device, stream),
- * allocated (hipMalloc, after synchronising that stream when an older, smaller one is
- * replaced) on the first call that needs more than the stream's buffer holds, and kept until
- * hqq_release_workspaces or the end of the process.  Calls on different streams never share
+ * N must be a multiple of 16 and K of 128.  Kernels by batch and size (fp32 accumulation in
+ * all; each deterministic):
+ *   batch 1-2: a streaming kernel that keeps q exact and applies delta and zero per group on
+ *     fp32 partial sums (the MFMA GEMV below for rows longer than 16384 codes);
+ *   batch 3-8 with N * K <= 2^24, and batch 9-16 with N * K <= 2^26 (K <= 32768): codes
+ *     dequantised to fp16 W_hat = fp16(q delta - z delta) (exact value, rounded once) in
+ *     registers, multiplied on the MFMA unit, K split over a block's waves;
+ *   batch 3-8 otherwise: an MFMA GEMV that keeps q exact, the packed rows staged in LDS;
+ *   above that, MFMA GEMMs on fp16 W_hat tiles.
+ * Above batch 8 (past the sizes above), with N a multiple of 128 and K of 256, the call runs
+ * the split GEMM of hqq_gemm_w4a16 on a workspace the library owns: one device buffer per
+ * (device, stream), allocated (hipMalloc, after synchronising that stream when an older,
+ * smaller one is replaced) on the first call that needs more than the stream's buffer holds,
+ * and kept until hqq_release_workspaces or the end of the process.  Calls on different streams never share
  * a buffer.  Callers that must not allocate (inside graph capture, say) make one call of the
  * largest batch on the stream first, or call hqq_gemm_w4a16 with their own workspace.  Other
  * shapes above batch 8 run a single-pass MFMA GEMM with no workspace.
@@ -279,8 +285,8 @@ int hqq_gemv_w4a16(const void* packed, const void* delta_fp16, const void* zero_
 
 /*
  * Frees the workspaces hqq_gemv_w4a16 keeps per (device, stream) (waits for each device's
- * work).  The next call above batch 8 allocates again.  No call of hqq_gemv_w4a16 may run
- * concurrently on another host thread.  Returns HQQ_OK or HQQ_ERR_DEVICE.
+ * work).  The next call that runs the split GEMM allocates again.  No call of hqq_gemv_w4a16
+ * may run concurrently on another host thread.  Returns HQQ_OK or HQQ_ERR_DEVICE.
  */
 int hqq_release_workspaces(void);
 

@@ -237,17 +237,53 @@ def test_gemv_parity_rows_per_wave(N, K, batch):
     check_gemv(packed, d16, z16, N, K, 64, x, out_f32=True)
 
 
+def random_w4(N, K, g, seed):
+    """Stored 4-bit operands drawn directly (codes U{0..15}, steps U(1e-3, 5e-2), zeros U(0, 15),
+    fp16), packed by the oracle: sizes past what the oracle quantizer finishes in seconds."""
+    r = np.random.default_rng(seed)
+    codes = r.integers(0, 16, N * K).astype(np.uint8)
+    d16 = r.uniform(1e-3, 5e-2, N * K // g).astype(np.float16)
+    z16 = r.uniform(0, 15, N * K // g).astype(np.float16)
+    return oracle.get().pack(codes, 4), d16, z16
+
+
+def sampled_rows(N, seed, n=384):
+    """The first and last 32 rows, and n random ones."""
+    r = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(32), np.arange(N - 32, N), r.choice(N, n, replace=False)]))
+
+
 @pytest.mark.parametrize("g", [64, 128])
-@pytest.mark.parametrize("N,K,batch", [(8192, 256, 6), (8192, 640, 3), (32, 20480, 1), (32, 18432, 2),
-                                       (48, 2176, 5)])
+@pytest.mark.parametrize("N,K,batch", [(8192, 2176, 6), (8192, 2304, 3), (4112, 4224, 5), (16384, 1152, 8),
+                                       (32, 20480, 1), (32, 18432, 2)])
 def test_gemv_parity_mfma_blocks(g, N, K, batch):
-    """The batched MFMA GEMV: two 16-row strips per block (N = 8192), one segment shorter than
-    2048 codes, a partial last segment, and batch 1-2 rows longer than the streaming kernel takes."""
+    """The batched MFMA GEMV that keeps codes exact (batch 3-8 past 2^24 weights): two 16-row
+    strips per block (N = 8192), one strip (N = 4112), one segment shorter than 2048 codes, a
+    partial last segment; and batch 1-2 rows longer than the streaming kernel takes."""
     say("gemv mfma", g, N, K, batch)
-    packed, d16, z16 = gemv_inputs(N, K, g, seed=4100 + N + K)
+    if N * K > (1 << 24):
+        packed, d16, z16 = random_w4(N, K, g, seed=4100 + N + K)
+        sel = sampled_rows(N, seed=N + K)
+    else:
+        packed, d16, z16 = gemv_inputs(N, K, g, seed=4100 + N + K)
+        sel = None
     x = synth.activations(batch, K, seed=19)
-    check_gemv(packed, d16, z16, N, K, g, x, out_f32=True)
-    check_gemv(packed, d16, z16, N, K, g, x, out_f32=False)
+    check_gemv(packed, d16, z16, N, K, g, x, out_f32=True, rows_sel=sel)
+    check_gemv(packed, d16, z16, N, K, g, x, out_f32=False, rows_sel=sel)
+
+
+@pytest.mark.parametrize("N,K,batch", [(4096, 4096, 8), (4112, 4096, 8), (2048, 8192, 3), (8192, 8192, 16),
+                                       (8192, 8192, 9), (8320, 8192, 9), (11008, 4096, 12), (4096, 11008, 16)])
+def test_gemv_w4a16_size_paths(N, K, batch):
+    """hqq_gemv_w4a16 on both sides of its size thresholds: batch 3-8 up to 2^24 weights and batch
+    9-16 up to 2^26 dequantise in registers into the MFMA; 4112 x 4096 at batch 8 keeps the exact-code
+    GEMV, 8320 x 8192 at batch 9 the split GEMM; the 7B projections at batch 12 and 16."""
+    say("gemv_w4a16 size paths", N, K, batch)
+    packed, d16, z16 = random_w4(N, K, 64, seed=4300 + N + K + batch)
+    x = synth.activations(batch, K, seed=29)
+    sel = sampled_rows(N, seed=K + batch, n=256)
+    check_gemv(packed, d16, z16, N, K, 64, x, out_f32=True, rows_sel=sel)
+    check_gemv(packed, d16, z16, N, K, 64, x, out_f32=False, rows_sel=sel)
 
 
 def test_gemv_onehot_columns():
@@ -318,9 +354,9 @@ def test_gemm_split_errors():
 
 
 @pytest.mark.parametrize("g", [64, 128])
-@pytest.mark.parametrize("N,K,batch", [(384, 1280, 9), (128, 512, 64), (256, 2048, 300)])
+@pytest.mark.parametrize("N,K,batch", [(384, 1280, 17), (128, 512, 64), (256, 2048, 300)])
 def test_gemv_w4a16_split_path(g, N, K, batch):
-    """Above batch 8, with N a multiple of 128 and K of 256, hqq_gemv_w4a16 runs the split GEMM on
+    """Above batch 16, with N a multiple of 128 and K of 256, hqq_gemv_w4a16 runs the split GEMM on
     the workspace the library keeps for the stream: the oracle's values, and bit for bit the
     result of hqq_gemm_w4a16 with a caller's workspace."""
     import weight_only_quantization_amd as hq

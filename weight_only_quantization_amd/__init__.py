@@ -392,8 +392,8 @@ def hqq_dequantize(packed, delta, zero, rows: int, cols: int, nbits: int, group_
 def hqq_gemv_w4a16(packed, delta, zero, N: int, K: int, group_size: int, x, out_dtype=None, out=None,
                    stream=None):
     """y [batch, N] = x [batch, K] @ W_hat^T for a 4-bit axis=1 weight W [N, K].  Above batch 8
-    the library runs its split GEMM on a workspace it keeps per stream (hqq_release_workspaces
-    frees them)."""
+    (past 2^26 weights up to batch 16) the library runs its split GEMM on a workspace it keeps per
+    stream (hqq_release_workspaces frees them)."""
     import torch
     lib = load()
     out_dtype = out_dtype or torch.float16

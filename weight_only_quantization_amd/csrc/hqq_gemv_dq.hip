@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(64 * kDqMaxWaves) k_gemv_dq(const uint8_t* __r
                                                               const __half* __restrict__ zero, int64_t N, int64_t K,
                                                               int gs_log2, const __half* __restrict__ x, int64_t batch,
                                                               void* __restrict__ y, int out_dtype) {
-  static_assert(FMT == 2 || FMT == 3, "2- or 3-bit codes");
+  static_assert(FMT == 2 || FMT == 3 || FMT == 4, "2-, 3- or 4-bit codes");
   constexpr int RING = kDqAhead + 1;
   constexpr int SP = kDqStrips;
   __shared__ f32x4 red[kDqMaxWaves * SP * 64];
@@ -56,14 +56,14 @@ __global__ void __launch_bounds__(64 * kDqMaxWaves) k_gemv_dq(const uint8_t* __r
   // per strip: flat index of the lane's first code in the run's first chunk (rows past N: the
   // last row), and the pointers the run's loads step from
   int64_t f_first[SP];
-  const uint8_t* pc[SP];      // 2-bit: byte of the lane's first code
+  const uint8_t* pc[SP];      // 2-/4-bit: byte of the lane's first code
   const uint32_t* pq[SP];     // 3-bit: word of the lane's first code
   int ph_first[SP];           // 3-bit: its slot in that word
   const __half *pd[SP], *pz[SP];  // step and zero of its group
 #pragma unroll
   for (int p = 0; p < SP; ++p) {
     f_first[p] = min(r0 + 16 * p + nl, N - 1) * K + 32 * h + 128 * c_lo;
-    pc[p] = packed + f_first[p] / 4;
+    pc[p] = packed + f_first[p] * FMT / 8;
     const int64_t q = f_first[p] / 10;
     pq[p] = reinterpret_cast<const uint32_t*>(packed) + q;
     ph_first[p] = (int)(f_first[p] - 10 * q);
@@ -85,7 +85,11 @@ __global__ void __launch_bounds__(64 * kDqMaxWaves) k_gemv_dq(const uint8_t* __r
     const int ci = EXACT ? i : max(0, min(i, nrun - 1));  // chunk of the run (an empty run: its first)
 #pragma unroll
     for (int p = 0; p < SP; ++p) {
-      if constexpr (FMT == 2) {
+      if constexpr (FMT == 4) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pc[p] + 64 * ci));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.w[p][e] = v[e];
+      } else if constexpr (FMT == 2) {
         const uint2 v = *reinterpret_cast<const uint2*>(pc[p] + 32 * ci);
         r.w[p][0] = v.x, r.w[p][1] = v.y, r.w[p][2] = 0u, r.w[p][3] = 0u;
       } else {
@@ -129,7 +133,10 @@ __global__ void __launch_bounds__(64 * kDqMaxWaves) k_gemv_dq(const uint8_t* __r
       d[hh] = dv;
       zd[hh] = r.valid ? zv * dv : 0.f;
     }
-    if constexpr (FMT == 2) {
+    if constexpr (FMT == 4) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) o[s] = wq8(r.w[p][s], d[s >> 1] * 16777216.0f, d[s >> 1] * 1048576.0f, zd[s >> 1]);
+    } else if constexpr (FMT == 2) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const float ds[4] = {d[hh] * 16777216.0f, d[hh] * 4194304.0f, d[hh] * 1048576.0f, d[hh] * 262144.0f};
@@ -225,7 +232,7 @@ int dq_waves(int64_t) { return kDqMaxWaves; }
 }  // namespace
 
 bool gemv_dq_supported(int64_t N, int64_t K, int nbits, int g, int64_t batch) {
-  if (nbits < 2 || nbits > 3 || batch < 1 || batch > 16 || K % 128 != 0 || N < 1) return false;
+  if (nbits < 2 || nbits > 4 || batch < 1 || batch > 16 || K % 128 != 0 || N < 1) return false;
   if (g != 16 && g != 32 && g != 64 && g != 128 && g != 256) return false;
   if (nbits == 2 && g != 16) return false;
   const int64_t need = (K / 128 + dq_waves(N) - 1) / dq_waves(N);
@@ -248,6 +255,9 @@ hipError_t launch_gemv_dq(const uint8_t* packed, const __half* delta, const __ha
   if (nbits == 3)
     return exact ? launch_dq_ncw<3, true>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype)
                  : launch_dq_ncw<3, false>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype);
+  if (nbits == 4)
+    return exact ? launch_dq_ncw<4, true>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype)
+                 : launch_dq_ncw<4, false>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype);
   if (nbits == 2)
     return exact ? launch_dq_ncw<2, true>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype)
                  : launch_dq_ncw<2, false>(need, grid, block, st, packed, delta, zero, N, K, gl, x, batch, y, y_dtype);
