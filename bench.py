@@ -551,6 +551,27 @@ def main():
     flops = 2.0 * 256 * GN * GK
     legs["dx_b256"] = {"us": tg * 1e6, "TFLOP/s": flops / tg / 1e12, "frac_mfma_f16": flops / tg / PEAK_FP16_MFMA}
 
+    # the layer set's 4096 x 4096 projection at batch 8 and 16: weights of up to 2^24 codes take the
+    # register-dequant MFMA kernel at batch 3-16 (32 rotated copies, ~300 MB: past the 256 MB
+    # last-level cache, and few enough calls for the spin kernel to cover their enqueue)
+    t0l, _, _, out0, _ = layers[0]
+    pq_bytes = out0[0].numel() + 4 * out0[1].numel()
+    pcop = [(out0[0].clone(), out0[1].clone(), out0[2].clone()) for _ in range(max(4, int(np.ceil(0.3e9 / pq_bytes))))]
+    XS = torch.from_numpy(synth.activations(16, t0l.cols, 405)).to(dev)
+    legs["gemv_4096x4096_read_floor"] = read_floor(pcop)
+    for b in (8, 16):
+        Yp = torch.empty((b, t0l.rows), dtype=torch.float16, device=dev)
+
+        def gp(r, b=b, Yp=Yp):
+            pk, d, z = pcop[r % len(pcop)]
+            hq.hqq_gemv_w4a16(pk, d, z, t0l.rows, t0l.cols, qp.group_size, XS[:b], out=Yp)
+        tg = timed(gp, 2 * len(pcop))
+        byt = pq_bytes + 2 * b * (t0l.rows + t0l.cols)
+        legs["gemv_4096x4096_b%d" % b] = {"us": tg * 1e6, "GB/s": byt / tg / 1e9, "frac_hbm": byt / tg / PEAK_HBM,
+                                          "bytes": byt, "copies_rotated": len(pcop),
+                                          "frac_of_read_floor": legs["gemv_4096x4096_read_floor"]["us"] / (tg * 1e6)}
+    del pcop, XS
+
     # a streaming device copy on the same box (the probe's 16-byte non-temporal loads and stores,
     # best of 4 and 8 loads in flight): the HBM rate a read + write kernel reaches in practice
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -321,8 +321,8 @@ int hqq_gemm_w4a16(const void* packed, const void* delta_fp16, const void* zero_
  * code with the step and zero of metadata row n mod (N/g) at its column).  N a multiple of
  * 128, K of 256; group_size 64 or 128 for 4-bit axis-1 codes (the hqq_gemm_w4a16 path), a
  * power of two 16..256 for 2/3-bit and axis-0 codes; 2/3-bit codes with axis 0 and other
- * shapes return HQQ_ERR_UNSUPPORTED.  Any batch >= 1 (batches up to 2, or 8 for axis-0 codes,
- * are cheaper through hqq_gemv).
+ * shapes return HQQ_ERR_UNSUPPORTED.  Any batch >= 1 (batches up to 16 for 3/2-bit codes, or 8
+ * for axis-0 codes, are cheaper through hqq_gemv).
  */
 int hqq_gemm(const void* packed, const void* delta_fp16, const void* zero_fp16, int64_t N, int64_t K, int nbits,
              int group_size, int axis, const void* x_fp16, int64_t batch, void* y, int y_dtype, void* workspace,
