@@ -38,40 +38,49 @@ namespace hqq {
 namespace {
 
 // ------------------------------------------------------------------------------------------
-// GEMV, batch 3..8, on the MFMA unit with the whole pipeline in one block per compute unit.
-// Block = 16 waves on RB = 16 SPB weight rows; K is walked in segments of 2048 codes and wave w
-// always takes the 128-code chunk w of a segment, for every strip of the block (the A
-// fragments it reads from LDS serve all strips).  Per segment the block stages, double
-// buffered in LDS: x in the MFMA operand order (1/16 on the odd codes) with the per-group sums
-// of x, the packed rows (each load instruction reads 1 KB of one row: one page; the operand
-// layout would put 16 rows, 16 pages, into each), and the rows' steps and zeros.  The loads
-// run two segments ahead in registers; one LDS-only barrier per segment.  At the end the 16
-// waves' partial sums of each output are added in wave order (deterministic).
+// GEMV, batch 3..8, on the MFMA unit with the whole pipeline in one block.
+// Block = W waves (8, or 16 for rows past 8192 codes) on RB = 16 SPB weight rows; K is walked in
+// segments of 128 W codes and wave w always takes the 128-code chunk w of a segment, for every
+// strip of the block (the A fragments it reads from LDS serve all strips).  Per segment the
+// block stages, double buffered in LDS: x in the MFMA operand order (1/16 on the odd codes)
+// with the per-group sums of x, the packed rows (each load instruction reads 1 KB of one or two
+// rows; the operand layout would put 16 rows, 16 pages, into each), and the rows' steps and
+// zeros.  The loads run two segments ahead in registers; one LDS-only barrier per segment.  At
+// the end the W waves' partial sums of each output are added in wave order (deterministic).
 // ------------------------------------------------------------------------------------------
-constexpr int kMfWaves = 16;            // waves per block: one per 128-code chunk of a segment
-constexpr int kMfKS = 128 * kMfWaves;   // codes per segment
-constexpr int kMfKSP = kMfKS + 8;       // LDS row stride of x (halves): rows in different banks
-constexpr int kMfWRB = kMfKS / 2 + 16;  // LDS row stride of the packed codes (bytes)
+// Block geometry for W waves: one 128-code chunk of a segment per wave.
+template <int W>
+struct MfGeom {
+  static constexpr int ks = 128 * W;            // codes per segment
+  static constexpr int ksp = ks + 8;            // LDS row stride of x (halves): rows in different banks
+  static constexpr int wrb = ks / 2 + 16;       // LDS row stride of the packed codes (bytes)
+  static constexpr int pieces = ks / 32;        // 16-byte pieces of one row's segment of codes
+  static constexpr int rows_per_wave = 16 / W;  // rows of a strip each wave loads per segment
+  static_assert(pieces * rows_per_wave == 64 && 16 % W == 0, "a wave loads whole row segments");
+};
 
 // Batch rows of the per-group sums of x, padded with zeros (8 with groups of 64: a lane reads the
 // sums of batch rows 0-3 or 4-7).
 __host__ __device__ constexpr int mf_bp(int B, int GS) { return GS == 64 ? 8 : (B + 3) & ~3; }
 // LDS bytes of one stage (x, sums of x, codes, metadata) and of the kernel (two stages, and with
 // groups of 64 a row of zeros that the A rows read against the other group's codes).
-__host__ __device__ constexpr int mf_stage_bytes(int B, int GS, int SPB) {
-  return B * kMfKSP * 2 + (kMfKS / GS) * mf_bp(B, GS) * 4 + 16 * SPB * kMfWRB + 16 * SPB * (2 * (kMfKS / GS) + 4) * 4;
+__host__ __device__ constexpr int mf_stage_bytes(int B, int GS, int SPB, int W) {
+  return B * (128 * W + 8) * 2 + (128 * W / GS) * mf_bp(B, GS) * 4 + 16 * SPB * (64 * W + 16) +
+         16 * SPB * (2 * (128 * W / GS) + 4) * 4;
 }
-__host__ __device__ constexpr int mf_lds_bytes(int B, int GS, int SPB) {
-  return 2 * mf_stage_bytes(B, GS, SPB) + (GS == 64 ? kMfKS * 2 : 0);
+__host__ __device__ constexpr int mf_lds_bytes(int B, int GS, int SPB, int W) {
+  return 2 * mf_stage_bytes(B, GS, SPB, W) + (GS == 64 ? 128 * W * 2 : 0);
 }
 
-template <int B, int GS, int SPB, int NSEG>
-__global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __restrict__ packed,
-                                                          const __half* __restrict__ delta,
-                                                          const __half* __restrict__ zero, int64_t N, int64_t K,
-                                                          const __half* __restrict__ x, void* __restrict__ y,
-                                                          int out_dtype) {
+template <int B, int GS, int SPB, int NSEG, int W>
+__global__ void __launch_bounds__(64 * W) k_gemv_mf(const uint8_t* __restrict__ packed,
+                                                   const __half* __restrict__ delta,
+                                                   const __half* __restrict__ zero, int64_t N, int64_t K,
+                                                   const __half* __restrict__ x, void* __restrict__ y,
+                                                   int out_dtype) {
   static_assert(B >= 1 && B <= 8 && (GS == 64 || GS == 128) && (SPB == 1 || SPB == 2), "shape");
+  constexpr int kMfWaves = W, kMfKS = MfGeom<W>::ks, kMfKSP = MfGeom<W>::ksp, kMfWRB = MfGeom<W>::wrb;
+  constexpr int kMfPieces = MfGeom<W>::pieces, kMfRowsPerWave = MfGeom<W>::rows_per_wave;
   constexpr int NT = 64 * kMfWaves, RB = 16 * SPB;
   constexpr int GPS = kMfKS / GS;          // groups per segment and row
   constexpr int XB = B * (kMfKS / 8);      // 16-byte blocks of x per segment
@@ -82,7 +91,7 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __rest
   constexpr int MLR = 2 * GPS + 4;         // LDS row stride of the metadata (floats): 16-byte reads of 8
                                            // consecutive rows fall in distinct banks
   static_assert(ML <= NT, "one step and one zero load per thread");
-  constexpr int STAGE = mf_stage_bytes(B, GS, SPB);
+  constexpr int STAGE = mf_stage_bytes(B, GS, SPB, W);
   extern __shared__ __align__(16) uint8_t lds_raw[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -123,9 +132,9 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __rest
       r.xr[j] = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + kb0 + 8 * kb);
     }
 #pragma unroll
-    for (int j = 0; j < SPB; ++j) {
-      const int row = wave + kMfWaves * j;
-      const int piece = min(lane, valid / 32 - 1);  // 16-byte pieces of the row's segment
+    for (int j = 0; j < SPB; ++j) {  // each wave takes 16 / kMfWaves rows of the strip
+      const int row = kMfRowsPerWave * wave + lane / kMfPieces + 16 * j;
+      const int piece = min(lane % kMfPieces, valid / 32 - 1);  // 16-byte pieces of the row's segment
       r.wr[j] = ld_stream16(packed + (n0 + row) * (K / 2) + kb0 / 2 + 16 * piece);
     }
     {
@@ -161,7 +170,8 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __rest
     uint8_t* wl = wl_of(buf);
 #pragma unroll
     for (int j = 0; j < SPB; ++j)
-      *reinterpret_cast<uint4*>(wl + (wave + kMfWaves * j) * kMfWRB + 16 * lane) = r.wr[j];
+      *reinterpret_cast<uint4*>(wl + (kMfRowsPerWave * wave + lane / kMfPieces + 16 * j) * kMfWRB +
+                                16 * (lane % kMfPieces)) = r.wr[j];
     if (tid < ML) {
       // P = 2^-24 sum x q (subnormal codes): the step is scaled up and the zero down by 2^24 (exact)
       const int row = tid / (GPS / MW), pc = tid % (GPS / MW);
@@ -280,8 +290,8 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gemv_mf(const uint8_t* __rest
       if (cur + 1 < nseg) segment(cur + 1, std::integral_constant<int, 1>{});
     }
   }
-  // ---- the 16 waves' partial sums of each output, added in wave order (stage memory reused)
-  float* red = reinterpret_cast<float*>(lds_raw);  // [SPB][16 waves][B][16]
+  // ---- the W waves' partial sums of each output, added in wave order (stage memory reused)
+  float* red = reinterpret_cast<float*>(lds_raw);  // [SPB][W waves][B][16]
   if constexpr (GS == 64) {
     // first groups' sums (lanes 0-31) plus second groups' (lanes 32-63): one swap of the pair
     // (r, r + 1) leaves row r's total in lanes 0-31 and row r + 1's in lanes 32-63, so lane
@@ -687,27 +697,37 @@ inline bool gemv_uses_valu(int64_t K, int64_t batch) { return batch <= 2 && K <=
 // Strips per block of the batched MFMA GEMV: two when that still leaves >= 256 blocks.
 inline int mf_strips_per_block(int64_t N) { return (N % 32 == 0 && N / 32 >= 256) ? 2 : 1; }
 
-template <int B, int GS, int SPB, int NSEG>
+template <int B, int GS, int SPB, int NSEG, int W>
 void gemv_mf_launch(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                     const __half* x, void* y, int y_dtype, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemv_mf<B, GS, SPB, NSEG>), dim3((unsigned)(N / (16 * SPB))), dim3(64 * kMfWaves),
-                     mf_lds_bytes(B, GS, SPB), st, packed, delta, zero, N, K, x, y, y_dtype);
+  hipLaunchKernelGGL((k_gemv_mf<B, GS, SPB, NSEG, W>), dim3((unsigned)(N / (16 * SPB))), dim3(64 * W),
+                     mf_lds_bytes(B, GS, SPB, W), st, packed, delta, zero, N, K, x, y, y_dtype);
 }
 
+// Rows of up to 8192 codes: 8 waves, up to 8 segments of 1024 codes as a compile-time count
+// (measured at batch 8 against 16 waves and 2048-code segments: 11008 x 4096 11.2 against 13.1 us,
+// 14336 x 4096 11.6 against 13.6, 28672 x 8192 37.1 against 43.3, 8192 x 8192 12.6 against 12.7;
+// the shorter segments double the pipeline's stages on short rows, and 8-wave blocks of half the
+// LDS).  Longer rows (and batch 1-2, which come here only for rows past 16384 codes): 16 waves,
+// 2048-code segments in a run-time loop (at 4096 x 14336 the 8-wave loop measured 15.8 against
+// 14.4 us).
 template <int B, int GS, int SPB>
 void gemv_mf_seg(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
                  const __half* x, void* y, int y_dtype, hipStream_t st) {
-  // batch 1-2 come here only for rows longer than the streaming kernel takes: the run-time loop
   if constexpr (B >= 3) {
-    switch ((K + kMfKS - 1) / kMfKS) {
-      case 1: return gemv_mf_launch<B, GS, SPB, 1>(packed, delta, zero, N, K, x, y, y_dtype, st);
-      case 2: return gemv_mf_launch<B, GS, SPB, 2>(packed, delta, zero, N, K, x, y, y_dtype, st);
-      case 3: return gemv_mf_launch<B, GS, SPB, 3>(packed, delta, zero, N, K, x, y, y_dtype, st);
-      case 4: return gemv_mf_launch<B, GS, SPB, 4>(packed, delta, zero, N, K, x, y, y_dtype, st);
+    switch ((K + MfGeom<8>::ks - 1) / MfGeom<8>::ks) {
+      case 1: return gemv_mf_launch<B, GS, SPB, 1, 8>(packed, delta, zero, N, K, x, y, y_dtype, st);
+      case 2: return gemv_mf_launch<B, GS, SPB, 2, 8>(packed, delta, zero, N, K, x, y, y_dtype, st);
+      case 3: return gemv_mf_launch<B, GS, SPB, 3, 8>(packed, delta, zero, N, K, x, y, y_dtype, st);
+      case 4: return gemv_mf_launch<B, GS, SPB, 4, 8>(packed, delta, zero, N, K, x, y, y_dtype, st);
+      case 5: return gemv_mf_launch<B, GS, SPB, 5, 8>(packed, delta, zero, N, K, x, y, y_dtype, st);
+      case 6: return gemv_mf_launch<B, GS, SPB, 6, 8>(packed, delta, zero, N, K, x, y, y_dtype, st);
+      case 7: return gemv_mf_launch<B, GS, SPB, 7, 8>(packed, delta, zero, N, K, x, y, y_dtype, st);
+      case 8: return gemv_mf_launch<B, GS, SPB, 8, 8>(packed, delta, zero, N, K, x, y, y_dtype, st);
       default: break;
     }
   }
-  gemv_mf_launch<B, GS, SPB, 0>(packed, delta, zero, N, K, x, y, y_dtype, st);
+  gemv_mf_launch<B, GS, SPB, 0, 16>(packed, delta, zero, N, K, x, y, y_dtype, st);
 }
 
 template <int B, int GS>
@@ -746,7 +766,7 @@ hipError_t gemv_gs(const uint8_t* packed, const __half* delta, const __half* zer
 size_t gemv_lds_bytes(int64_t K, int gs, int64_t batch) {
   if (gemv_uses_valu(K, batch)) return (size_t)valu_lds_bytes((int)batch, K);
   if (batch < 1 || batch > 8) return 0;
-  return (size_t)mf_lds_bytes((int)batch, gs, 2);  // the two-strip layout is the larger
+  return (size_t)mf_lds_bytes((int)batch, gs, 2, 16);  // the two-strip 16-wave layout is the largest
 }
 
 hipError_t launch_gemv(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int gs,
