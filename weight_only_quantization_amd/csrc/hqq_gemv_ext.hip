@@ -192,33 +192,38 @@ __global__ void __launch_bounds__(64 * kAx0Waves) k_gemv_ax0(const uint8_t* __re
 // Axis 0, 4-bit, batch 3..8, on the MFMA unit.  The same factorisation as k_gemv_ax0 (a block
 // takes RB = 16 SPB of the g weight rows of one metadata row r0, a = x delta[r0] in fp16, the
 // zero term sum_k a z[r0, k] from the same staged values), with the segment pipeline of the
-// 4-bit batch 3-8 kernel: 16 waves, K in segments of 2048 codes, wave w always takes the
-// 128-code chunk w of a segment; per segment the block stages a (unpack slot order, 1/16 on
-// the odd codes) and the packed rows (1 KB of one row per load instruction) in LDS, double
-// buffered, the loads two segments ahead in registers, one LDS-only barrier per segment.
+// 4-bit batch 3-8 kernel: W waves (8 for rows of up to 8192 codes, 16 beyond), K in segments
+// of 128 W codes, wave w always takes the 128-code chunk w of a segment; per segment the block
+// stages a (unpack slot order, 1/16 on the odd codes) and the packed rows (1 KB of one or two
+// rows per load instruction) in LDS, double buffered, the loads two segments ahead in
+// registers, one LDS-only barrier per segment.
 // The codes stay exact (fp16 subnormals into v_mfma_f32_16x16x32_f16) and there is no
 // per-group step inside a row, so each wave's MFMAs chain over the whole row:
 //   y[b, n] = 2^24 sum_w P_w[b, n] - sum_k a[b, k] z[r0, k],
-// the 16 waves' sums added in wave order, the zero term in a fixed tree (deterministic).
+// the W waves' sums added in wave order, the zero term in a fixed tree (deterministic).
 // ------------------------------------------------------------------------------------------
-constexpr int kM0Waves = 16;
-constexpr int kM0KS = 128 * kM0Waves;   // codes per segment
-constexpr int kM0KSP = kM0KS + 8;       // LDS row stride of a (halves)
-constexpr int kM0WRB = kM0KS / 2 + 16;  // LDS row stride of the packed codes (bytes)
+// LDS bytes of one stage of W waves (a, then the packed rows).
+__host__ __device__ constexpr int mf0_stage_bytes(int B, int SPB, int W) {
+  return B * (128 * W + 8) * 2 + 16 * SPB * (64 * W + 16);
+}
 
-__host__ __device__ constexpr int mf0_stage_bytes(int B, int SPB) { return B * kM0KSP * 2 + 16 * SPB * kM0WRB; }
-
-template <int B, int SPB, int NSEG>
-__global__ void __launch_bounds__(64 * kM0Waves) k_gemv_mf0(const uint8_t* __restrict__ packed,
-                                                           const __half* __restrict__ delta,
-                                                           const __half* __restrict__ zero, int64_t N, int64_t K,
-                                                           int g, int subsets, int xcd_map, int out_dtype,
-                                                           const __half* __restrict__ x, void* __restrict__ y) {
-  static_assert(B >= 1 && B <= 8 && (SPB == 1 || SPB == 2), "shape");
+template <int B, int SPB, int NSEG, int W>
+__global__ void __launch_bounds__(64 * W) k_gemv_mf0(const uint8_t* __restrict__ packed,
+                                                    const __half* __restrict__ delta,
+                                                    const __half* __restrict__ zero, int64_t N, int64_t K,
+                                                    int g, int subsets, int xcd_map, int out_dtype,
+                                                    const __half* __restrict__ x, void* __restrict__ y) {
+  static_assert(B >= 1 && B <= 8 && (SPB == 1 || SPB == 2) && (W == 8 || W == 16), "shape");
+  constexpr int kM0Waves = W;
+  constexpr int kM0KS = 128 * W;        // codes per segment
+  constexpr int kM0KSP = kM0KS + 8;     // LDS row stride of a (halves)
+  constexpr int kM0WRB = kM0KS / 2 + 16;  // LDS row stride of the packed codes (bytes)
+  constexpr int kPieces = kM0KS / 32;   // 16-byte pieces of one row's segment of codes
+  constexpr int kRowsPerWave = 16 / W;  // rows of a strip each wave loads per segment
   constexpr int NT = 64 * kM0Waves, RB = 16 * SPB;
   constexpr int XB = B * (kM0KS / 8);      // 16-byte blocks of x (and of a) per segment
   constexpr int XR = (XB + NT - 1) / NT;   // of them per thread
-  constexpr int STAGE = mf0_stage_bytes(B, SPB);
+  constexpr int STAGE = mf0_stage_bytes(B, SPB, W);
   extern __shared__ __align__(16) uint8_t lds_raw[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -262,9 +267,9 @@ __global__ void __launch_bounds__(64 * kM0Waves) k_gemv_mf0(const uint8_t* __res
       r.zr[j] = *reinterpret_cast<const uint4*>(zrow + kb0 + 8 * kb);
     }
 #pragma unroll
-    for (int j = 0; j < SPB; ++j) {
-      const int row = wave + kM0Waves * j;
-      const int piece = min(lane, valid / 32 - 1);
+    for (int j = 0; j < SPB; ++j) {  // each wave takes 16 / W rows of the strip
+      const int row = kRowsPerWave * wave + lane / kPieces + 16 * j;
+      const int piece = min(lane % kPieces, valid / 32 - 1);
       r.wr[j] = ld_stream16(packed + (r0 + R0 * (i0 + row)) * (K / 2) + kb0 / 2 + 16 * piece);
     }
   };
@@ -279,7 +284,7 @@ __global__ void __launch_bounds__(64 * kM0Waves) k_gemv_mf0(const uint8_t* __res
 #pragma unroll
     for (int j = 0; j < XR; ++j) {
       const int idx = tid + NT * j;
-      if (idx < XB) {  // uniform per wave (XB is a multiple of 256)
+      if (idx < XB) {  // uniform per wave (XB is a multiple of 128 W / 8 >= 128)
         const int m = idx / (kM0KS / 8), kb = idx % (kM0KS / 8);
         const unsigned xu[4] = {r.xr[j].x, r.xr[j].y, r.xr[j].z, r.xr[j].w};
         const unsigned du[4] = {r.dr[j].x, r.dr[j].y, r.dr[j].z, r.dr[j].w};
@@ -309,7 +314,8 @@ __global__ void __launch_bounds__(64 * kM0Waves) k_gemv_mf0(const uint8_t* __res
     uint8_t* wl = wl_of(buf);
 #pragma unroll
     for (int j = 0; j < SPB; ++j)
-      *reinterpret_cast<uint4*>(wl + (wave + kM0Waves * j) * kM0WRB + 16 * lane) = r.wr[j];
+      *reinterpret_cast<uint4*>(wl + (kRowsPerWave * wave + lane / kPieces + 16 * j) * kM0WRB + 16 * (lane % kPieces)) =
+          r.wr[j];
   };
 
   f32x4 acc[SPB];
@@ -361,10 +367,10 @@ __global__ void __launch_bounds__(64 * kM0Waves) k_gemv_mf0(const uint8_t* __res
       if (cur + 1 < nseg) segment(cur + 1, std::integral_constant<int, 1>{});
     }
   }
-  // ---- the 16 waves' sums of each output in wave order, the zero term in a fixed tree (the
-  //      wave's 64 lanes, then the four waves of a batch row); stage memory reused
-  float* red = reinterpret_cast<float*>(lds_raw);  // [SPB][16 waves][B][16]
-  float* redz = red + SPB * kM0Waves * B * 16;      // [XR][16 waves]
+  // ---- the W waves' sums of each output in wave order, the zero term in a fixed tree (the
+  //      wave's 64 lanes, then the W / 4 waves of a batch row); stage memory reused
+  float* red = reinterpret_cast<float*>(lds_raw);  // [SPB][W waves][B][16]
+  float* redz = red + SPB * kM0Waves * B * 16;      // [XR][W waves]
 #pragma unroll
   for (int sp = 0; sp < SPB; ++sp)
 #pragma unroll
@@ -383,9 +389,10 @@ __global__ void __launch_bounds__(64 * kM0Waves) k_gemv_mf0(const uint8_t* __res
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < kM0Waves; ++w) sum += red[((sp * kM0Waves + w) * B + m) * 16 + col];
-    // batch row m: blocks idx = tid + NT j with idx / 256 = m, i.e. j = m / 4, waves 4 (m % 4) + 0..3
-    const float* zw = redz + (m / 4) * kM0Waves + 4 * (m % 4);
-    const float zb = (zw[0] + zw[1]) + (zw[2] + zw[3]);
+    // batch row m: blocks idx = tid + NT j with idx / (16 W) = m, i.e. j = m / 4, waves
+    // (W / 4) (m % 4) + 0 .. W / 4 - 1
+    const float* zw = redz + (m / 4) * kM0Waves + (W / 4) * (m % 4);
+    const float zb = W == 16 ? (zw[0] + zw[1]) + (zw[2] + zw[3]) : zw[0] + zw[1];
     const float v = sum * kSubScale - zb;
     const int64_t n = r0 + R0 * (i0 + 16 * sp + col);
     if (out_dtype == HQQ_OUT_F16)
@@ -898,25 +905,32 @@ hipError_t launch_gemv_3b(const uint8_t* packed, const __half* delta, const __ha
 // axis 0, batch 3..8: two strips per block where g and the block count allow
 inline int mf0_strips(int64_t N, int g) { return (g % 32 == 0 && (N / g) * (g / 32) >= 256) ? 2 : 1; }
 
-template <int B, int SPB, int NSEG>
+template <int B, int SPB, int NSEG, int W>
 hipError_t mf0_launch(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
                       const __half* x, void* y, int y_dtype, hipStream_t st) {
   const int subsets = g / (16 * SPB);
   const int xcd_map = (N / g) % 8 == 0;
-  hipLaunchKernelGGL((k_gemv_mf0<B, SPB, NSEG>), dim3((unsigned)((N / g) * subsets)), dim3(64 * kM0Waves),
-                     2 * mf0_stage_bytes(B, SPB), st, packed, delta, zero, N, K, g, subsets, xcd_map, y_dtype, x, y);
+  hipLaunchKernelGGL((k_gemv_mf0<B, SPB, NSEG, W>), dim3((unsigned)((N / g) * subsets)), dim3(64 * W),
+                     2 * mf0_stage_bytes(B, SPB, W), st, packed, delta, zero, N, K, g, subsets, xcd_map, y_dtype, x, y);
   return hipGetLastError();
 }
 
+// Rows of up to 8192 codes: 8 waves, up to 8 segments of 1024 codes as a compile-time count (the
+// axis-1 kernel's choice; 28672 x 8192 at batch 8 measured below); longer rows: 16 waves and
+// 2048-code segments in a run-time loop.
 template <int B, int SPB>
 hipError_t mf0_seg(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K, int g,
                    const __half* x, void* y, int y_dtype, hipStream_t st) {
-  switch ((K + kM0KS - 1) / kM0KS) {
-    case 1: return mf0_launch<B, SPB, 1>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
-    case 2: return mf0_launch<B, SPB, 2>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
-    case 3: return mf0_launch<B, SPB, 3>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
-    case 4: return mf0_launch<B, SPB, 4>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
-    default: return mf0_launch<B, SPB, 0>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+  switch ((K + 1023) / 1024) {
+    case 1: return mf0_launch<B, SPB, 1, 8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 2: return mf0_launch<B, SPB, 2, 8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 3: return mf0_launch<B, SPB, 3, 8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 4: return mf0_launch<B, SPB, 4, 8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 5: return mf0_launch<B, SPB, 5, 8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 6: return mf0_launch<B, SPB, 6, 8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 7: return mf0_launch<B, SPB, 7, 8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    case 8: return mf0_launch<B, SPB, 8, 8>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
+    default: return mf0_launch<B, SPB, 0, 16>(packed, delta, zero, N, K, g, x, y, y_dtype, st);
   }
 }
 
@@ -928,7 +942,7 @@ hipError_t mf0_b(const uint8_t* packed, const __half* delta, const __half* zero,
 }
 
 size_t gemv_ax0_lds_bytes(int64_t K, int64_t batch) {
-  return batch <= 2 ? ax0_lds_bytes((int)batch, K) : 2 * (size_t)mf0_stage_bytes((int)batch, 2);
+  return batch <= 2 ? ax0_lds_bytes((int)batch, K) : 2 * (size_t)mf0_stage_bytes((int)batch, 2, 16);
 }
 size_t gemv_2b_lds_bytes(int64_t K, int64_t batch) { return lds_2b((int)batch, K); }
 
