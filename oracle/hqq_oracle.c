@@ -142,30 +142,33 @@ double hqq_oracle_shrink(double r, double beta, double p) {
  * One proximal round of one group ("第二拍", "为什么 zero 是这个均值"):
  *   q = clip(round(W*s + z), 0, 2^b-1);  W_hat = (q - z)*delta;  r = W - W_hat;
  *   err = sum |r|;  e = shrink(r);  z_next = mean(q - (W - e)*s).
+ * Reading (the pages fix no evaluation order): r = W - (q - z)*delta is formed with a single
+ * rounding of the product and the difference (a fused multiply-add), and the mean as
+ * (sum q - sum (W - e)*s) / g, both sums pairwise in index order; the sum of the integer
+ * codes is exact in any order.
  * q_out / e_out (may be NULL) receive q and e per element.
  * ---------------------------------------------------------------------------------------- */
 
 void hqq_oracle_round_group(const double* w, int g, int nbits, double s, double delta, double z, double beta,
                             double p, double* err_sum, double* z_next, double* q_out, double* e_out) {
   double qmax = (double)((1 << nbits) - 1);
-  double absr[g], term[g];
+  double absr[g], qv[g], uv[g];
   for (int i = 0; i < g; i++) {
     double t = w[i] * s;
     t = t + z;
     double q = PLANT(7) ? floor(t + 0.5) : rint(t); /* rint: ties to even */
     if (q < 0.0) q = 0.0;
     if (q > qmax && !PLANT(8)) q = qmax;
-    double what = (q - z) * delta;
-    double r = w[i] - what;
+    double r = fma(-(q - z), delta, w[i]); /* W - W_hat, W_hat = (q - z)*delta */
     absr[i] = fabs(r);
     double e = hqq_oracle_shrink(r, beta, p);
-    double u = PLANT(3) ? w[i] * s : (w[i] - e) * s;
-    term[i] = q - u;
+    uv[i] = PLANT(3) ? w[i] * s : (w[i] - e) * s;
+    qv[i] = q;
     if (q_out) q_out[i] = q;
     if (e_out) e_out[i] = e;
   }
   *err_sum = hqq_oracle_sum(absr, g);
-  *z_next = hqq_oracle_sum(term, g) / (double)(PLANT(12) ? g - 1 : g);
+  *z_next = (hqq_oracle_sum(qv, g) - hqq_oracle_sum(uv, g)) / (double)(PLANT(12) ? g - 1 : g);
 }
 
 /* ------------------------------------------------------------------------------------------

@@ -148,43 +148,45 @@ constexpr int solve_waves() { return G == 16 ? 5 : (G >= 256 ? 2 : 4); }
 template <int E, int L>
 __device__ __forceinline__ void hqq_round(const double (&w)[E], const double (&ws)[E], double s, double delta,
                                           double z, double qmax, double beta, double pm1, double thr,
-                                          double inv_g, double& err_o, double& zn_o, double& maxr_o) {
-  double ar[E], tm[E];
+                                          double inv_g, double sws, double& err_o, double& zn_o, double& maxr_o) {
+  double ar[E], qv[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const double t = ws[e] + z;
     double qq = __builtin_rint(t);
     qq = fmax(qq, 0.0);
     qq = fmin(qq, qmax);
-    const double wh = (qq - z) * delta;
-    const double rr = w[e] - wh;
+    const double rr = __builtin_fma(-(qq - z), delta, w[e]);  // W - (q - z) delta, one rounding
     ar[e] = fabs(rr);
-    tm[e] = qq - ws[e];  // e = 0: (W - e)*s is W*s
+    qv[e] = qq;
   }
   const double err = tree_sum<0, E, E>(ar);
+  double su = sws;  // the group's sum of (W - e) s: sum W s while the shrink is zero
   if (__any(err >= thr)) {
     // Some residual of the wave may pass the shrink: redo the terms with the shrink evaluated
     // wherever it can be non-zero (q and r recomputed identically).
+    double u[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const double t = ws[e] + z;
       double qq = __builtin_rint(t);
       qq = fmax(qq, 0.0);
       qq = fmin(qq, qmax);
-      const double wh = (qq - z) * delta;
-      const double rr = w[e] - wh;
+      const double rr = __builtin_fma(-(qq - z), delta, w[e]);
       const double a = fabs(rr);
       double ee = 0.0;
       if (a >= thr) {
         const double v = shrink_mag(a, pm1, beta);
         if (v > 0.0) ee = (rr < 0.0) ? -v : v;
       }
-      tm[e] = (ee == 0.0) ? (qq - ws[e]) : (qq - (w[e] - ee) * s);
+      u[e] = (ee == 0.0) ? ws[e] : (w[e] - ee) * s;
     }
+    su = seg_sum<L>(tree_sum<0, E, E>(u));
   }
-  const double acc = tree_sum<0, E, E>(tm);
+  // the codes are integers: their sum is exact in any order
+  const double sq = seg_sum<L>(tree_sum<0, E, E>(qv));
   err_o = seg_sum<L>(err);
-  zn_o = seg_sum<L>(acc) * inv_g;
+  zn_o = (sq - su) * inv_g;
   maxr_o = err;
 }
 
@@ -210,6 +212,7 @@ __device__ __forceinline__ double solve_group(const SolveArgs& a, const double (
   double z = -mn * s;
 #pragma unroll
   for (int e = 0; e < E; ++e) ws[e] = w[e] * s;
+  const double sws = seg_sum<L>(tree_sum<0, E, E>(ws));  // the group's sum of W s (pairwise)
 
   const double inv_g = 1.0 / (double)(E * L);
   // canonicalised once here, not in every round's clip
@@ -218,7 +221,7 @@ __device__ __forceinline__ double solve_group(const SolveArgs& a, const double (
   double* slot = err_lds;  // round k's entry; the fill below continues from the same pointer
   for (int k = 0; k < kmax; ++k) {
     double err, zn, maxr;
-    hqq_round<E, L>(w, ws, s, delta, z, qmax, a.beta[k], a.pm1, a.thr[k], inv_g, err, zn, maxr);
+    hqq_round<E, L>(w, ws, s, delta, z, qmax, a.beta[k], a.pm1, a.thr[k], inv_g, sws, err, zn, maxr);
     const double ev = valid ? err : 0.0;
     if (write_err) *slot = ev;
     slot += stride;
@@ -506,12 +509,13 @@ __device__ __forceinline__ void v2_search(const SolveArgs& a, const ScaleGrid& s
     double z = -mn * s;
 #pragma unroll
     for (int e = 0; e < E; ++e) ws[e] = w[e] * s;
+    const double sws = seg_sum<L>(tree_sum<0, E, E>(ws));  // the group's sum of W s (pairwise)
     double zprev = z, best = __builtin_inf();
     bool done = !valid;
     for (int k = 0; k < a.iters; ++k) {
       if (__all(done)) break;
       double err, zn, bound;
-      hqq_round<E, L>(w, ws, s, delta, z, qmax, a.beta[k], a.pm1, a.thr[k], inv_g, err, zn, bound);
+      hqq_round<E, L>(w, ws, s, delta, z, qmax, a.beta[k], a.pm1, a.thr[k], inv_g, sws, err, zn, bound);
       if (!done) {
         if (k >= 1 && !(err < best)) {
           z = zprev;
