@@ -219,13 +219,20 @@ __device__ __forceinline__ double solve_group(const SolveArgs& a, const double (
   const double qmax = __builtin_canonicalize(a.qmax);
   kfrozen = kmax;  // the round at which every group of the wave froze (kmax: not before the end)
   double* slot = err_lds;  // round k's entry; the fill below continues from the same pointer
+  // each round's two thresholds are requested a round ahead: a scalar load waited for at its
+  // use would sit in the middle of every round
+  double thr_k = a.thr[0], thf_k = a.thr_frozen[0];
   for (int k = 0; k < kmax; ++k) {
+    const int kn = k + 1 < kmax ? k + 1 : k;
+    const double thr_n = a.thr[kn], thf_n = a.thr_frozen[kn];
     double err, zn, maxr;
-    hqq_round<E, L>(w, ws, s, delta, z, qmax, a.beta[k], a.pm1, a.thr[k], inv_g, sws, err, zn, maxr);
+    hqq_round<E, L>(w, ws, s, delta, z, qmax, a.beta[k], a.pm1, thr_k, inv_g, sws, err, zn, maxr);
     const double ev = valid ? err : 0.0;
     if (write_err) *slot = ev;
     slot += stride;
-    const bool frozen = !valid || (zn == z && maxr <= a.thr_frozen[k]);
+    const bool frozen = !valid || (zn == z && maxr <= thf_k);
+    thr_k = thr_n;
+    thf_k = thf_n;
     z = zn;
     if (__all(frozen)) {
       if (write_err)
@@ -512,10 +519,13 @@ __device__ __forceinline__ void v2_search(const SolveArgs& a, const ScaleGrid& s
     const double sws = seg_sum<L>(tree_sum<0, E, E>(ws));  // the group's sum of W s (pairwise)
     double zprev = z, best = __builtin_inf();
     bool done = !valid;
+    double thr_k = a.thr[0];  // requested a round ahead, as in the solve
     for (int k = 0; k < a.iters; ++k) {
       if (__all(done)) break;
+      const double thr_n = a.thr[k + 1 < a.iters ? k + 1 : k];
       double err, zn, bound;
-      hqq_round<E, L>(w, ws, s, delta, z, qmax, a.beta[k], a.pm1, a.thr[k], inv_g, sws, err, zn, bound);
+      hqq_round<E, L>(w, ws, s, delta, z, qmax, a.beta[k], a.pm1, thr_k, inv_g, sws, err, zn, bound);
+      thr_k = thr_n;
       if (!done) {
         if (k >= 1 && !(err < best)) {
           z = zprev;
