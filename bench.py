@@ -49,7 +49,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_traffic.json")
 # The layers are independent tensors: their hqq_quantize calls go to this many streams (default
 # priority), so one layer's solve fills the GPU while another's stop decision and fix-up (small,
 # latency-bound launches) run.  Measured on the 7-layer set (quantize phase / whole step,
-# Gweights/s): 1 stream 202 / 172, 2 streams 213 / 177, 3 streams 213 / 175, 4 streams 212 / 174.
+# Gweights/s, two runs each): 1 stream 215-216 / 181-182, 2 streams 222-226 / 184-187,
+# 3 streams 227 / 184-185, 4 streams 228-229 / 185-186.
 QSTREAMS = 2
 
 
