@@ -17,7 +17,8 @@ def weights(rows, cols, seed, sigma=0.02, frac=0.001, k=10.0):
 # shapes: several solve blocks and a partial last block (axis=1: 32 groups per block at g=64;
 # axis=0: 64 groups per block at g <= 32, 32 at g=64, 16 at g >= 128).  Axis-0 tile counts of 25,
 # 13 and 13 (g = 128, 64 and the 3-bit 128) take both branches of the XCD tile order (eight
-# contiguous ranges, then the remainder in place); 6 and 5 tiles keep every tile in place.
+# contiguous ranges, then the remainder in place); the other axis-0 shapes (4 to 6 tiles) keep
+# every tile in place.
 CASES = [
     # nbits, g, axis, rows, cols
     (4, 64, 1, 37, 192),
