@@ -258,10 +258,11 @@ def sampled_rows(N, seed, n=384):
 
 @pytest.mark.parametrize("g", [64, 128])
 @pytest.mark.parametrize("N,K,batch", [(8192, 2176, 6), (8192, 2304, 3), (4112, 4224, 5), (16384, 1152, 8),
-                                       (4096, 10240, 5), (32, 20480, 1), (32, 18432, 2)])
+                                       (11008, 4096, 4), (4096, 10240, 5), (32, 20480, 1), (32, 18432, 2)])
 def test_gemv_parity_mfma_blocks(g, N, K, batch):
     """The batched MFMA GEMV that keeps codes exact (batch 3-8 past 2^24 weights): two 16-row
-    strips per block (N = 8192), one strip (N = 4112), 8-wave blocks with two to five 1024-code
+    strips per block (N = 8192, 16384), one strip (N = 4112, and N = 11008, where a two-strip grid
+    would leave its last round of 256 blocks at 88), 8-wave blocks with two to five 1024-code
     segments and a partial last one, 16-wave blocks in the run-time segment loop (K = 10240); and
     batch 1-2 rows longer than the streaming kernel takes."""
     say("gemv mfma", g, N, K, batch)

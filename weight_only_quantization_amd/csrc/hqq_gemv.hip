@@ -694,8 +694,17 @@ hipError_t gemv_valu(const uint8_t* packed, const __half* delta, const __half* z
 // Batch 1-2 with rows of at most 16384 codes run on the vector ALUs.
 inline bool gemv_uses_valu(int64_t K, int64_t batch) { return batch <= 2 && K <= 64 * 32 * 8; }
 
-// Strips per block of the batched MFMA GEMV: two when that still leaves >= 256 blocks.
-inline int mf_strips_per_block(int64_t N) { return (N % 32 == 0 && N / 32 >= 256) ? 2 : 1; }
+// Strips per block of the batched MFMA GEMV: two when that still leaves >= 256 blocks, unless
+// the two-strip grid's last round of 256 blocks would be at most 3/8 full.  Then one-strip
+// blocks (half the work each) even out the compute units' shares, which outweighs the x staging
+// they repeat: at 11008 x 4096 (344 two-strip blocks) batch 3-6 took 8.9-10.7 us against
+// 9.8-11.1 with two strips, batch 8 the same; where the last round is fuller or whole
+// (14336 x 4096: 448 blocks; 28672 x 8192: 896; 8192 x 8192: 256) two strips were 2-19 % faster.
+inline int mf_strips_per_block(int64_t N) {
+  if (N % 32 != 0 || N / 32 < 256) return 1;
+  const int64_t last = (N / 32) % 256;  // blocks in the last round of a two-strip grid
+  return (last > 0 && last <= 96) ? 1 : 2;
+}
 
 template <int B, int GS, int SPB, int NSEG, int W>
 void gemv_mf_launch(const uint8_t* packed, const __half* delta, const __half* zero, int64_t N, int64_t K,
