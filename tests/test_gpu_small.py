@@ -229,11 +229,13 @@ def test_gemv_parity_long_rows(K, batch):
     check_gemv(packed, d16, z16, N, K, 64, x, out_f32=True)
 
 
-@pytest.mark.parametrize("N,K,batch", [(8224, 256, 1), (8208, 384, 1), (4112, 512, 1), (4096, 256, 2),
-                                       (8192, 128, 2), (1040, 640, 1)])
+@pytest.mark.parametrize("N,K,batch", [(12320, 256, 1), (8224, 256, 1), (8208, 384, 1), (4112, 512, 1),
+                                       (4096, 256, 2), (8192, 128, 2), (1040, 640, 1)])
 def test_gemv_parity_rows_per_wave(N, K, batch):
     """The row-streaming GEMV's wave shapes: 8 consecutive rows per wave (N a multiple of 32 with
-    at least 256 blocks), 4 (N / 16 >= 256), 2 otherwise; every row of every wave checked."""
+    at least 256 blocks whose last round of 256 holds more than 96: N = 12320, 385 blocks), 4
+    (N / 16 >= 256, and N = 8224, whose 8-row grid would leave 1 block in its last round), 2
+    otherwise; every row of every wave checked."""
     say("gemv rows per wave", N, K, batch)
     packed, d16, z16 = gemv_inputs(N, K, 64, seed=4200 + N + K)
     x = synth.activations(batch, K, seed=23)

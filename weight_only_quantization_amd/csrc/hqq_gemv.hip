@@ -654,8 +654,16 @@ __global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ packed
 
 // Rows per wave of the VALU GEMV: batch 1 as many as keep >= 256 blocks (one per compute
 // unit); batch 2 at most 4 (measured: twice the VALU work per row wants more waves).
+// Rows per wave of the streaming GEMV: 8 at batch 1 when that leaves >= 256 blocks, unless the
+// last round of 256 such blocks would be at most 3/8 full; then 4 rows (blocks of half the work
+// even out the compute units' shares: 11008 x 4096 took 6.66 us against 7.20 with 8 rows, while
+// 8192 x 8192 and 14336 x 4096, whose last rounds are whole or 3/4 full, were 5-14 % slower
+// with 4).
 inline int valu_rows_per_wave(int64_t N, int B) {
-  if (B == 1 && N % (8 * kVWaves) == 0 && N / (8 * kVWaves) >= 256) return 8;
+  if (B == 1 && N % (8 * kVWaves) == 0 && N / (8 * kVWaves) >= 256) {
+    const int64_t last = (N / (8 * kVWaves)) % 256;  // blocks in the last round of the 8-row grid
+    if (!(last > 0 && last <= 96)) return 8;
+  }
   if (N / (4 * kVWaves) >= 256) return 4;  // N % 16 == 0
   return 2;
 }
